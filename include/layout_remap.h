@@ -1,0 +1,268 @@
+/*
+ * layout_remap.h -- C ABI of the MI355X (gfx950) layout-evaluation and
+ * layout-remapping-copy library (liblayout_remap.so).
+ *
+ * The operations are those of hierarchical "shape:stride" layouts as three web
+ * pages describe them; citations name the page and its section:
+ *   [ThreadMap page]     CUTLASS 2.x PitchLinearStripminedThreadMap article,
+ *                        hotelren.com/news/5252042
+ *   [CuTe algebra page]  "CUTE布局代数：GPU张量计算的内存优化革命", jsqmd.com/news/768714
+ *   [print_layout page]  "CUTLASS Layout可视化：从print_layout理解GPU内存映射与性能优化",
+ *                        codechina.net/article/weixin_30702441/411096
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative lr_status.  No C++ exception crosses.
+ *   - Descriptors (lr_layout) are plain structs owned by the caller; results are
+ *     written to caller-provided structs.  The library never allocates device
+ *     memory and keeps no global mutable state (the last HIP error text is kept
+ *     per calling thread).
+ *   - Device pointers are HIP device memory owned by the caller.  Launches are
+ *     asynchronous on the caller's stream (a hipStream_t passed as void*; NULL is
+ *     the null stream).  Errors found on the host are returned before any launch.
+ *   - Element data are moved as opaque bytes: NaN payloads and any bit pattern
+ *     survive unchanged.
+ *   - Offsets, strides and capacities are in elements, not bytes.
+ */
+#ifndef LAYOUT_REMAP_H
+#define LAYOUT_REMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the lr_* entry points are exported from the shared library (it is built
+ * with -fvisibility=hidden). */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
+#define LR_MAX_LEAVES 16
+
+/* Status codes (negative). */
+typedef enum {
+  LR_OK = 0,
+  LR_ERR_INVALID = -1,           /* bad argument: NULL, rank, extent < 1, negative stride, bad text */
+  LR_ERR_SIZE_MISMATCH = -2,     /* size(src layout) != size(dst layout) */
+  LR_ERR_BOUNDS = -3,            /* a layout reaches beyond its buffer capacity */
+  LR_ERR_OVERFLOW = -4,          /* a size or offset does not fit in int64 */
+  LR_ERR_ALIAS = -5,             /* dst layout not injective and LR_COPY_ORDERED_ALIAS not set,
+                                    or the ordered aliased copy is beyond its limits */
+  LR_ERR_NOT_REPRESENTABLE = -6, /* result of an algebra operation is not a layout */
+  LR_ERR_SWIZZLE = -7,           /* swizzle parameters invalid (need B >= 0, M >= 0, S >= B, B+M+S <= 62) */
+  LR_ERR_ELEM_BYTES = -8,        /* elem_bytes not one of 1, 2, 4, 8, 16 */
+  LR_ERR_HIP = -9,               /* a HIP call failed; lr_last_hip_error() gives its text */
+  LR_ERR_PATH = -10,             /* a forced copy path does not apply to these layouts */
+  LR_ERR_OVERLAP = -11,          /* source and destination storage overlap */
+  LR_ERR_CAPACITY = -12          /* text buffer too small (lr_layout_format) */
+} lr_status;
+
+/*
+ * Layout descriptor.  [CuTe algebra page, section 2.1] and [print_layout page,
+ * sections 2.1 and 3.2]: a layout is a function from logical coordinates to
+ * offsets given by a (possibly nested) shape and a congruent stride.  The
+ * descriptor keeps the leaves of the nested shape in depth-first order and the
+ * bounds of the top-level modes; nesting below the top level only groups leaves
+ * and does not change the function, so it is flattened.
+ *
+ * A 1-D index k is split colexicographically over the leaves (leaf 0 fastest):
+ * c_i = (k / prod_{j<i} shape_j) % shape_i, and offset = sum_i c_i * stride_i.
+ * [ThreadMap page, sections 1.2 and 2.2] split a thread id the same way, the
+ * contiguous part first.
+ *
+ * Optional Swizzle<B,M,S> [print_layout page, section 4.3] is applied to the
+ * final offset o:  o ^ ((o >> S) & (((1 << B) - 1) << M)).  swz_b == 0 means no
+ * swizzle.  With S >= B it is a bijection and its own inverse.
+ */
+typedef struct {
+  int32_t nleaves;                 /* 1 .. LR_MAX_LEAVES */
+  int32_t nmodes;                  /* 1 .. nleaves: top-level modes */
+  int64_t shape[LR_MAX_LEAVES];    /* each >= 1 */
+  int64_t stride[LR_MAX_LEAVES];   /* each >= 0 */
+  int32_t mode_end[LR_MAX_LEAVES]; /* leaf index one past the end of each top-level mode;
+                                      strictly increasing, mode_end[nmodes-1] == nleaves */
+  int32_t swz_b, swz_m, swz_s;     /* Swizzle<B,M,S> on the final offset; swz_b == 0: none */
+} lr_layout;
+
+/* ---------------------------------------------------------------- text form */
+
+/* Parse "(4,2):(_2,_1)", "((4,2),(2,4)):((2,16),(1,8))", "8:1" or
+ * "Sw<3,3,3> o ((128,32),(64,64)):((64,524288),(1,8192))" ([print_layout page,
+ * section 3.2] for the printed form; "_" marks a compile-time constant there and
+ * is accepted and ignored).  Returns LR_ERR_INVALID on malformed text,
+ * LR_ERR_SWIZZLE on bad swizzle parameters. */
+int lr_layout_parse(const char* text, lr_layout* out);
+
+/* Write the text form of L into buf (NUL-terminated).  LR_ERR_CAPACITY if cap is
+ * too small. */
+int lr_layout_format(const lr_layout* L, char* buf, size_t cap);
+
+/* Check a descriptor: ranks, extents >= 1, strides >= 0, mode bounds, swizzle,
+ * and that size and the largest linear offset fit in int64 (LR_ERR_OVERFLOW). */
+int lr_layout_validate(const lr_layout* L);
+
+/* --------------------------------------------------------------- properties */
+
+/* Number of logical elements: product of the extents. */
+int lr_size(const lr_layout* L, int64_t* n);
+
+/* Buffer length the layout needs.  Unswizzled: exact, 1 + sum (shape_i-1)*stride_i.
+ * Swizzled: an upper bound, 1 + (m | (2^(M+B) - 1)) where m is the unswizzled
+ * largest offset (the swizzle only rewrites bits below M+B). */
+int lr_cosize(const lr_layout* L, int64_t* n);
+
+/* --------------------------------------------------------------- algebra */
+
+/* Coalesce: the same function of the 1-D index on [0, size) with extent-1 leaves
+ * dropped and neighbours merged when stride[i+1] == shape[i]*stride[i]; each
+ * remaining leaf becomes a top-level mode.  The swizzle is kept. */
+int lr_coalesce(const lr_layout* in, lr_layout* out);
+
+/* Composition R = A o B, R(c) = A(B(c)) with B's integer offset used as a 1-D
+ * index into A ([CuTe algebra page, section 2.2]; a padded A is skipped over as
+ * that section describes).  A is coalesced and its last leaf extended without
+ * bound.  Each leaf (n:s) of B becomes the leaves of A met by skipping s then
+ * taking n, which needs divisibility at every leaf boundary; when A has more
+ * than one leaf, B's leaves with n > 1 and s > 0, sorted by stride, must cover
+ * disjoint ranges (s_j*n_j <= s_{j+1}) so that no carry crosses between them.
+ * The result has B's top-level modes and A's swizzle.  A swizzled B is accepted
+ * only when A is the identity n:1.  Otherwise LR_ERR_NOT_REPRESENTABLE. */
+int lr_composition(const lr_layout* a, const lr_layout* b, lr_layout* out);
+
+/* Right inverse L' with L(L'(i)) == i for i < size(L') ([CuTe algebra page,
+ * section 2.3]: which logical index sits at a given offset).  Built greedily:
+ * starting from stride 1, take the leaf whose stride equals the product so far
+ * and append (its extent : its colex weight in L).  Extent-1 and stride-0 leaves
+ * are ignored.  A swizzled L gives LR_ERR_NOT_REPRESENTABLE (its inverse applies
+ * the swizzle first, which a descriptor cannot express). */
+int lr_right_inverse(const lr_layout* in, lr_layout* out);
+
+/* zipped_divide by a tiler ([CuTe algebra page, section 3.2]): each top-level
+ * mode m of extent n_m splits into a tile part (first tiler[m] elements, in colex
+ * order) and a rest part (n_m/tiler[m] tiles); the result has two top-level
+ * modes, all tile parts then all rest parts.  ntiler <= nmodes; modes past the
+ * tiler are not split (they go whole into the rest part).  tiler[m] must divide
+ * n_m, else LR_ERR_NOT_REPRESENTABLE. */
+int lr_zipped_divide(const lr_layout* in, const int64_t* tiler, int32_t ntiler, lr_layout* out);
+
+/* Injectivity of L as a function of the 1-D index: exact (a bitmap over the
+ * offsets) when size <= 2^20; above that the sufficient test "sorted by stride,
+ * each stride exceeds the largest offset of the smaller ones" (*result 0 then
+ * means not proven injective).  A swizzle never changes the answer. */
+int lr_is_injective(const lr_layout* L, int32_t* result);
+
+/* Widest vector (in elements, a power of two with elems*elem_bytes <= 16) that a
+ * copy from src to dst can move as one unit, assuming 16-byte-aligned buffers
+ * ([CuTe algebra page, section 2.3]: the common part of the two inverse layouts
+ * gives the widest contiguous copy).  Computed from the joint flat form: the
+ * extent of the leading mode with stride 1 on both sides, limited so that every
+ * other stride and each swizzle's M keep the vectors aligned.  1 when dst is not
+ * injective or no joint form exists. */
+int lr_max_common_vector(const lr_layout* src, const lr_layout* dst, size_t elem_bytes, int64_t* elems);
+
+/* Thread maps as layouts over the thread id.  [ThreadMap page, section 2.2]:
+ * strip-mined offset(tid) = tid%P + ((tid/P)%S)*kRow + (tid/(P*S))*(P*S*kRow),
+ * i.e. the layout (P, S, ceil(T/(P*S))):(1, kRow, P*S*kRow).  strips == 0 gives
+ * the base pitch-linear map of [ThreadMap page, section 1.2], offset =
+ * tid%P + (tid/P)*kRow, i.e. (P, ceil(T/P)):(1, kRow). */
+int lr_thread_map(int64_t pitch, int64_t strips, int64_t krow, int64_t threads, lr_layout* out);
+
+/* --------------------------------------------------------------- copy plan */
+
+/* Copy paths (what lr_copy_plan chose). */
+typedef enum {
+  LR_PATH_GENERIC = 0,    /* one unit (vec_elems elements) per lane over the joint modes */
+  LR_PATH_VECTOR = 1,     /* same kernel, 16-byte units along the common contiguous mode */
+  LR_PATH_TRANSPOSE = 2,  /* register-blocked tile transpose, tiles staged in LDS */
+  LR_PATH_INTERLEAVE = 3, /* narrow dst-contiguous mode (<= 16 bytes) interleaved in registers */
+  LR_PATH_STAGED = 4,     /* compact source footprint per tile staged in LDS, gathered */
+  LR_PATH_DUAL = 5,       /* no joint refinement: each side evaluated from the index */
+  LR_PATH_ALIAS = 6,      /* non-injective dst, sequential last-writer semantics */
+  LR_PATH_TRANSPOSE_DIRECT = 7 /* register-blocked transpose storing straight to global */
+} lr_path;
+
+/* Copy flags. */
+#define LR_COPY_ORDERED_ALIAS 0x1u   /* allow a non-injective dst: result equals the sequential
+                                        loop over k = 0..N-1, so the greatest k wins */
+#define LR_COPY_WIDE_INDEX 0x2u      /* force 64-bit index arithmetic (generic/dual paths only) */
+#define LR_COPY_FORCE_PATH(p) ((((uint32_t)(p)) + 1u) << 8) /* force an lr_path; LR_ERR_PATH if it
+                                                              does not apply */
+
+typedef struct {
+  int32_t path;        /* lr_path */
+  int32_t elem_bytes;  /* bytes per element after fusing the common contiguous prefix */
+  int32_t vec_elems;   /* elements (of elem_bytes) per lane unit or per register-block row */
+  int32_t wide;        /* 1 if 64-bit index arithmetic is used */
+  int32_t joint_rank;  /* number of joint modes (0 for the dual/alias paths) */
+  int32_t a_mode;      /* joint mode contiguous in src (transpose/interleave), else -1 */
+  int32_t b_mode;      /* joint mode contiguous in dst (transpose/interleave), else -1 */
+  int32_t block;       /* threads per workgroup */
+  int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
+  int64_t grid;        /* workgroups launched */
+  int64_t n_elems;     /* logical elements of the original layouts */
+  int64_t ext[2 * LR_MAX_LEAVES];   /* joint modes, sorted by dst stride, in fused elements */
+  int64_t s_src[2 * LR_MAX_LEAVES];
+  int64_t s_dst[2 * LR_MAX_LEAVES];
+} lr_plan;
+
+/* Plan a copy without launching anything (host only).  Checks everything
+ * lr_layout_copy checks.  src_align/dst_align are the byte alignments of the
+ * buffers (pass 16 for "aligned"). */
+int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align,
+                 const lr_layout* Ld, int64_t dst_capacity_elems, size_t dst_align,
+                 size_t elem_bytes, uint32_t flags, lr_plan* out);
+
+/* --------------------------------------------------------------- device */
+
+/* Evaluate L at n 1-D indices on the GPU ([print_layout page, sections 2.3 and
+ * 3.1]: the layout called on each coordinate gives its offset).  idx: device
+ * int64[n], or NULL for 0..n-1.  offsets: device int64[n].  An index outside
+ * [0, size) yields offset -1.  Division by the extents uses precomputed
+ * multiply-high constants when size < 2^31. */
+int lr_layout_eval(const lr_layout* L, const int64_t* idx, int64_t n, int64_t* offsets, void* stream);
+
+/* Evaluate L at n coordinates on the GPU.  coords: device int64[n][ncols],
+ * row-major.  ncols == nmodes: one integer per top-level mode, split
+ * colexicographically inside that mode ([print_layout page, section 6.3]: a
+ * layout takes integers or coordinate objects); ncols == nleaves: the natural
+ * coordinate, one per leaf.  A coordinate out of range yields -1. */
+int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, int32_t ncols,
+                          int64_t* offsets, void* stream);
+
+/* The layout-remapping copy: for every logical index k of [0, N),
+ *   dst[Ld(k)] = src[Ls(k)]      (elem_bytes bytes each, bitwise)
+ * ([CuTe algebra page, sections 2.3 and 5.1]: a copy between two layouts that
+ * differ only in arrangement).  Elements of dst outside the image of Ld are not
+ * written.  src/dst: device pointers; capacities in elements bound cosize of each
+ * layout (LR_ERR_BOUNDS).  size(Ls) must equal size(Ld) (LR_ERR_SIZE_MISMATCH,
+ * the runtime form of [CuTe algebra page, section 3.3]'s compatibility check).
+ * The byte ranges [src, src+cap*eb) and [dst, dst+cap*eb) must not overlap
+ * (LR_ERR_OVERLAP).  A non-injective Ld needs LR_COPY_ORDERED_ALIAS
+ * (LR_ERR_ALIAS otherwise); the ordered copy then handles destination cosize up
+ * to 2^26 elements with N * ceil(cosize/16384) <= 2^36. */
+int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
+                   void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
+                   size_t elem_bytes, uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/* Static text for a status code. */
+const char* lr_strerror(int code);
+
+/* Text of the last HIP error seen by an lr_* call on this thread ("" if none). */
+const char* lr_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* lr_version(void);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAYOUT_REMAP_H */

@@ -1,0 +1,925 @@
+// HIP kernels for gfx950 (MI355X) and the device-side C ABI entry points:
+// lr_layout_eval, lr_layout_eval_coords, lr_layout_copy.
+//
+// Pages cited (title, address):
+//   [ThreadMap page]     CUTLASS 2.x PitchLinearStripminedThreadMap article, hotelren.com/news/5252042
+//   [CuTe algebra page]  "CUTE布局代数：GPU张量计算的内存优化革命", jsqmd.com/news/768714
+//   [print_layout page]  "CUTLASS Layout可视化：从print_layout理解GPU内存映射与性能优化",
+//                        codechina.net/article/weixin_30702441/411096
+//
+// All work here is integer index arithmetic and byte movement: elements are moved
+// as opaque bit patterns in units of 1, 2, 4, 8 or 16 bytes.  Divisions by layout
+// extents use multiply-high constants computed on the host (make_fastdiv), exact
+// for dividends below 2^31; problems that do not fit 31-bit indices and offsets
+// take the 64-bit ("wide") kernels with ordinary division.
+//
+// Wavefronts are 64 lanes; every kernel runs 256-lane workgroups (4 waves, one
+// per SIMD) except the ordered-alias kernel (1024 lanes, one window per group).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "lr_internal.h"
+
+namespace lr {
+
+// ------------------------------------------------------------------ helpers
+
+static thread_local char g_hip_err[256];
+
+void set_hip_error(const char* text) {
+  std::snprintf(g_hip_err, sizeof(g_hip_err), "%s", text ? text : "");
+}
+
+struct FD {  // device copy of FastDiv
+  uint32_t m, s;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, FD f) { return f.m ? (__umulhi(x, f.m) >> f.s) : x; }
+
+struct SwzArg {  // o ^ ((o >> shift) & mask); mask == 0: none
+  uint32_t mask, shift;
+};
+
+__device__ __forceinline__ uint32_t swz32(uint32_t o, SwzArg z) { return o ^ ((o >> z.shift) & z.mask); }
+__device__ __forceinline__ uint64_t swz64(uint64_t o, uint64_t mask, uint32_t shift) {
+  return o ^ ((o >> shift) & mask);
+}
+
+static SwzArg swz_arg(const Swz& z) {
+  SwzArg a{0, 0};
+  if (z.b > 0) {
+    a.mask = ((1u << z.b) - 1u) << z.m;
+    a.shift = (uint32_t)z.s;
+  }
+  return a;
+}
+
+static FD fd_of(int64_t d) {
+  FastDiv f = make_fastdiv((uint32_t)d);
+  return FD{f.m, f.s};
+}
+
+// element and chunk types, moved as raw bits
+template <int B> struct Raw;
+template <> struct Raw<1> { using T = uint8_t; };
+template <> struct Raw<2> { using T = uint16_t; };
+template <> struct Raw<4> { using T = uint32_t; };
+template <> struct Raw<8> { using T = uint2; };
+template <> struct Raw<16> { using T = uint4; };
+
+template <typename T, int V>
+struct alignas(V * sizeof(T) >= 16 ? 16 : V * sizeof(T)) Chunk {
+  T e[V];
+};
+
+// ------------------------------------------------------------------ eval
+
+struct EvalArgs {
+  int32_t nleaves, nmodes;
+  int64_t shape[LR_MAX_LEAVES];
+  int64_t stride[LR_MAX_LEAVES];
+  int32_t mode_end[LR_MAX_LEAVES];
+  FD fd[LR_MAX_LEAVES];
+  uint64_t swz_mask;
+  uint32_t swz_shift;
+  int32_t small;  // size < 2^31: fast division
+  int64_t size;
+  int64_t mode_size[LR_MAX_LEAVES];
+  const int64_t* idx;
+  const int64_t* coords;
+  int32_t ncols;
+  int64_t n;
+  int64_t* out;
+};
+
+// 1-D index -> offset: colex digits over the leaves, sum of digit*stride, swizzle
+// ([print_layout page, section 2.1]: offset = sum of coordinate * stride;
+//  [print_layout page, section 4.3]: the XOR swizzle on the offset).
+__device__ __forceinline__ int64_t eval_leaves(const EvalArgs& a, int lo, int hi, int64_t k) {
+  int64_t off = 0;
+  if (a.small) {
+    uint32_t r = (uint32_t)k;
+    for (int i = lo; i < hi; ++i) {
+      uint32_t q = (i == hi - 1) ? 0u : fdiv(r, a.fd[i]);
+      uint32_t dgt = (i == hi - 1) ? r : r - q * (uint32_t)a.shape[i];
+      off += (int64_t)dgt * a.stride[i];
+      r = q;
+    }
+  } else {
+    uint64_t r = (uint64_t)k;
+    for (int i = lo; i < hi; ++i) {
+      uint64_t n = (uint64_t)a.shape[i];
+      uint64_t q = (i == hi - 1) ? 0 : r / n;
+      off += (int64_t)(r - q * n) * a.stride[i];
+      r = q;
+    }
+  }
+  return off;
+}
+
+__global__ void __launch_bounds__(256) k_eval_index(EvalArgs a) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (int64_t)gridDim.x * 256) {
+    int64_t k = a.idx ? a.idx[i] : i;
+    int64_t off = -1;
+    if (k >= 0 && k < a.size) off = (int64_t)swz64((uint64_t)eval_leaves(a, 0, a.nleaves, k), a.swz_mask, a.swz_shift);
+    a.out[i] = off;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_eval_coords(EvalArgs a) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (int64_t)gridDim.x * 256) {
+    const int64_t* c = a.coords + i * a.ncols;
+    int64_t off = 0;
+    bool ok = true;
+    if (a.ncols == a.nleaves) {  // natural coordinate: one integer per leaf
+      for (int l = 0; l < a.nleaves; ++l) {
+        int64_t x = c[l];
+        ok = ok && x >= 0 && x < a.shape[l];
+        off += x * a.stride[l];
+      }
+    } else {  // one integer per top-level mode, colex inside the mode
+      int lo = 0;
+      for (int m = 0; m < a.nmodes; ++m) {
+        int64_t x = c[m];
+        ok = ok && x >= 0 && x < a.mode_size[m];
+        if (ok) off += eval_leaves(a, lo, a.mode_end[m], x);
+        lo = a.mode_end[m];
+      }
+    }
+    a.out[i] = ok ? (int64_t)swz64((uint64_t)off, a.swz_mask, a.swz_shift) : -1;
+  }
+}
+
+// ------------------------------------------------------------------ generic / vector copy
+
+struct ModeArg {
+  uint32_t ext;
+  FD fd;
+  uint32_t ss, sd;
+};
+
+struct ModeArg64 {
+  int64_t ext, ss, sd;
+};
+
+struct GenericArgs {
+  const void* src;
+  void* dst;
+  int32_t rank;
+  ModeArg m[kMaxKernelModes];
+  ModeArg64 w[kMaxKernelModes];
+  SwzArg sws, swd;
+  uint64_t sws_mask64, swd_mask64;
+  int64_t n_units;
+  int64_t n_chunks;  // groups of 1024 units
+};
+
+// One unit (UB bytes) per lane and step; four independent units per lane so each
+// lane keeps four loads in flight before its stores.  Lanes of a wave take
+// consecutive units, i.e. consecutive positions of the fastest joint mode.
+template <int UB, bool WIDE>
+__global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
+  using T = typename Raw<UB>::T;
+  const T* __restrict__ src = (const T*)a.src;
+  T* __restrict__ dst = (T*)a.dst;
+  constexpr int U = 4;
+  for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
+    T val[U];
+    uint64_t dof[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t idx = ch * (256 * U) + u * 256 + threadIdx.x;
+      ok[u] = idx < a.n_units;
+      dof[u] = 0;
+      if (ok[u]) {
+        uint64_t so = 0, d = 0;
+        if (WIDE) {
+          uint64_t r = (uint64_t)idx;
+          for (int k = 0; k < a.rank; ++k) {
+            uint64_t e = (uint64_t)a.w[k].ext;
+            uint64_t q = r / e;
+            uint64_t g = r - q * e;
+            so += g * (uint64_t)a.w[k].ss;
+            d += g * (uint64_t)a.w[k].sd;
+            r = q;
+          }
+          so = swz64(so, a.sws_mask64, a.sws.shift);
+          d = swz64(d, a.swd_mask64, a.swd.shift);
+        } else {
+          uint32_t r = (uint32_t)idx, s32 = 0, d32 = 0;
+          for (int k = 0; k < a.rank; ++k) {
+            uint32_t q = (k == a.rank - 1) ? 0u : fdiv(r, a.m[k].fd);
+            uint32_t g = r - q * a.m[k].ext;
+            s32 += g * a.m[k].ss;
+            d32 += g * a.m[k].sd;
+            r = q;
+          }
+          so = swz32(s32, a.sws);
+          d = swz32(d32, a.swd);
+        }
+        val[u] = src[so];
+        dof[u] = d;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) dst[dof[u]] = val[u];
+  }
+}
+
+// ------------------------------------------------------------------ dual evaluation
+
+struct SideArg {
+  int32_t nleaves;
+  uint32_t ext[LR_MAX_LEAVES];
+  FD fd[LR_MAX_LEAVES];
+  uint32_t stride[LR_MAX_LEAVES];
+  int64_t ext64[LR_MAX_LEAVES];
+  int64_t stride64[LR_MAX_LEAVES];
+  SwzArg sw;
+  uint64_t mask64;
+};
+
+template <bool WIDE>
+__device__ __forceinline__ uint64_t side_eval(const SideArg& s, int64_t k) {
+  if (WIDE) {
+    uint64_t r = (uint64_t)k, o = 0;
+    for (int i = 0; i < s.nleaves; ++i) {
+      uint64_t n = (uint64_t)s.ext64[i];
+      uint64_t q = r / n;
+      o += (r - q * n) * (uint64_t)s.stride64[i];
+      r = q;
+    }
+    return swz64(o, s.mask64, s.sw.shift);
+  }
+  uint32_t r = (uint32_t)k, o = 0;
+  for (int i = 0; i < s.nleaves; ++i) {
+    uint32_t q = (i == s.nleaves - 1) ? 0u : fdiv(r, s.fd[i]);
+    o += (r - q * s.ext[i]) * s.stride[i];
+    r = q;
+  }
+  return swz32(o, s.sw);
+}
+
+struct DualArgs {
+  const void* src;
+  void* dst;
+  SideArg s, d;
+  int64_t n;
+  int64_t n_chunks;
+};
+
+// Each lane evaluates both layouts from the index (used when the two layouts have
+// no common refinement into joint modes).
+template <int EB, bool WIDE>
+__global__ void __launch_bounds__(256) k_dual(DualArgs a) {
+  using T = typename Raw<EB>::T;
+  const T* __restrict__ src = (const T*)a.src;
+  T* __restrict__ dst = (T*)a.dst;
+  constexpr int U = 4;
+  for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
+    T val[U];
+    uint64_t dof[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t k = ch * (256 * U) + u * 256 + threadIdx.x;
+      ok[u] = k < a.n;
+      dof[u] = 0;
+      if (ok[u]) {
+        val[u] = src[side_eval<WIDE>(a.s, k)];
+        dof[u] = side_eval<WIDE>(a.d, k);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) dst[dof[u]] = val[u];
+  }
+}
+
+// ------------------------------------------------------------------ ordered aliased copy
+
+constexpr int kAliasWindow = 8192;
+
+// Non-injective destination with sequential semantics: for every dst offset the
+// greatest index k that writes it wins.  Workgroup w owns dst offsets
+// [w*8192, (w+1)*8192): it records the greatest writer of each offset in an LDS
+// table (atomic max), then lets only that writer store.  Deterministic; no
+// device scratch memory.
+template <int EB>
+__global__ void __launch_bounds__(1024) k_alias(DualArgs a) {
+  using T = typename Raw<EB>::T;
+  __shared__ int owner[kAliasWindow];
+  const T* __restrict__ src = (const T*)a.src;
+  T* __restrict__ dst = (T*)a.dst;
+  const int64_t w0 = (int64_t)blockIdx.x * kAliasWindow;
+  for (int i = threadIdx.x; i < kAliasWindow; i += 1024) owner[i] = -1;
+  __syncthreads();
+  for (int64_t k = threadIdx.x; k < a.n; k += 1024) {
+    int64_t o = (int64_t)side_eval<false>(a.d, k) - w0;
+    if (o >= 0 && o < kAliasWindow) atomicMax(&owner[o], (int)k);
+  }
+  __syncthreads();
+  for (int64_t k = threadIdx.x; k < a.n; k += 1024) {
+    int64_t o = (int64_t)side_eval<false>(a.d, k) - w0;
+    if (o >= 0 && o < kAliasWindow && owner[o] == (int)k) dst[w0 + o] = src[side_eval<false>(a.s, k)];
+  }
+}
+
+// ------------------------------------------------------------------ batch modes
+
+struct BatchArg {
+  int32_t rank;
+  uint32_t ext[kMaxKernelModes];
+  FD fd[kMaxKernelModes];
+  uint32_t ss[kMaxKernelModes], sd[kMaxKernelModes];
+};
+
+__device__ __forceinline__ void batch_offsets(const BatchArg& b, uint32_t r, uint32_t* so, uint32_t* sd) {
+  uint32_t s = 0, d = 0;
+  for (int k = 0; k < b.rank; ++k) {
+    uint32_t q = (k == b.rank - 1) ? 0u : fdiv(r, b.fd[k]);
+    uint32_t g = r - q * b.ext[k];
+    s += g * b.ss[k];
+    d += g * b.sd[k];
+    r = q;
+  }
+  *so = s;
+  *sd = d;
+}
+
+// ------------------------------------------------------------------ tile transpose
+
+struct TransposeArgs {
+  const void* src;
+  void* dst;
+  uint32_t ext_a, ext_b;  // a: src-contiguous mode, b: dst-contiguous mode
+  uint32_t ss_b, sd_a;    // the other stride of each
+  uint32_t tiles_a, tiles_b;
+  FD fd_ta, fd_tb;
+  BatchArg batch;
+  SwzArg sws, swd;
+};
+
+// Tile of 16V x 16V elements per workgroup; each lane owns a V x V register block:
+// V chunk loads of V elements along a (one per b row), an in-register transpose,
+// V chunk stores of V elements along b (one per a row).  V*EB == 16 normally, so
+// every global access is a 16-byte vector.
+//
+// LDS == true: the transposed chunks go through LDS so that a wave's stores run
+// along 16 consecutive chunks of one dst row (256 contiguous bytes per row for 16-B
+// chunks).  The LDS tile is addressed [row][chunk ^ (row / V)], an XOR swizzle of
+// the 16-byte chunk index ([print_layout page, sections 4.3 and 5.2]: XOR spreads
+// a column across banks, where padding would also do), so both the chunk writes
+// (16 lanes of one chunk column) and the row reads (16 lanes of one row) touch 16
+// distinct chunk slots of a 256-byte bank window.
+// LDS == false: lanes are arranged 8 x 8 per wave so each load and store
+// instruction covers eight full 128-byte lines, with no LDS at all.
+template <int EB, int V, bool LDS>
+__global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
+  using T = typename Raw<EB>::T;
+  using C = Chunk<T, V>;
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  uint32_t blk = blockIdx.x;
+  uint32_t r1 = fdiv(blk, t.fd_ta);
+  uint32_t ta = blk - r1 * t.tiles_a;
+  uint32_t r2 = fdiv(r1, t.fd_tb);
+  uint32_t tb = r1 - r2 * t.tiles_b;
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+
+  const int tid = threadIdx.x;
+  int alpha, beta;
+  if (LDS) {
+    alpha = tid & 15;
+    beta = tid >> 4;
+  } else {
+    const int lane = tid & 63, w = tid >> 6;
+    alpha = (lane & 7) + 8 * (w & 1);
+    beta = (lane >> 3) + 8 * (w >> 1);
+  }
+  const uint32_t a0 = ta * (16 * V), b0 = tb * (16 * V);
+  const uint32_t a_blk = a0 + V * alpha, b_blk = b0 + V * beta;
+  const bool valid = a_blk < t.ext_a && b_blk < t.ext_b;
+
+  C in[V];
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      uint32_t so = swz32(a_blk + (b_blk + j) * t.ss_b + bs, t.sws);
+      in[j] = *(const C*)(src + (size_t)so * EB);
+    }
+  }
+  C out[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+#pragma unroll
+    for (int j = 0; j < V; ++j) out[i].e[j] = in[j].e[i];
+
+  if (!LDS) {
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        uint32_t dof = swz32((a_blk + i) * t.sd_a + b_blk + bd, t.swd);
+        *(C*)(dst + (size_t)dof * EB) = out[i];
+      }
+    }
+    return;
+  }
+
+  __shared__ C tile[16 * V][16];
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) tile[V * alpha + i][beta ^ alpha] = out[i];
+  }
+  __syncthreads();
+  const int c = tid & 15;
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const int row = (tid >> 4) + 16 * k;
+    const uint32_t a = a0 + row, b = b0 + V * c;
+    if (a < t.ext_a && b < t.ext_b) {
+      C v = tile[row][c ^ ((row / V) & 15)];
+      uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+      *(C*)(dst + (size_t)dof * EB) = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ interleave
+
+struct InterleaveArgs {
+  const void* src;
+  void* dst;
+  uint32_t ext_a;        // src-contiguous mode; dst stride of a == NB
+  uint32_t ss_b;         // src stride of the short dst-contiguous mode b (extent NB)
+  uint32_t tiles_a;
+  FD fd_ta;
+  BatchArg batch;
+  SwzArg sws, swd;
+};
+
+// The dst-contiguous mode b is short (NB * EB <= 16 bytes) and a follows it in
+// dst, so V consecutive a positions times NB form NB contiguous dst chunks.  Each
+// lane loads NB 16-byte chunks (one per b) and writes them interleaved.  This is
+// the pairing of [print_layout page, section 4.2] (two heads side by side so one
+// wide load brings both), done in registers.
+template <int EB, int NB>
+__global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
+  using T = typename Raw<EB>::T;
+  constexpr int V = 16 / EB;
+  using C = Chunk<T, V>;
+  constexpr int U = 4;
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  uint32_t blk = blockIdx.x;
+  uint32_t r1 = fdiv(blk, t.fd_ta);
+  uint32_t ta = blk - r1 * t.tiles_a;
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r1, &bs, &bd);
+
+  C in[U][NB];
+  bool ok[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t a0 = (ta * (256 * U) + u * 256 + threadIdx.x) * V;
+    ok[u] = a0 < t.ext_a;
+    if (ok[u]) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
+        in[u][b] = *(const C*)(src + (size_t)so * EB);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!ok[u]) continue;
+    uint32_t a0 = (ta * (256 * U) + u * 256 + threadIdx.x) * V;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      C o;
+#pragma unroll
+      for (int x = 0; x < V; ++x) {
+        const int e = c * V + x;  // element a0*NB + e: a = a0 + e / NB, b = e % NB
+        o.e[x] = in[u][e % NB].e[e / NB];
+      }
+      uint32_t dof = swz32(a0 * NB + c * V + bd, t.swd);
+      *(C*)(dst + (size_t)dof * EB) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ staged footprint gather
+
+struct StagedArgs {
+  const void* src;
+  void* dst;
+  int32_t inner;                       // inner modes (compact in dst, in dst order)
+  uint32_t in_ext[kMaxKernelModes];
+  FD in_fd[kMaxKernelModes];
+  uint32_t in_ss[kMaxKernelModes];
+  uint32_t T;                          // tiles along the tile mode
+  uint32_t Ts, Td;                     // tile strides (elements)
+  uint32_t Fc;                         // 16-byte chunks of one tile's source footprint
+  FD fd_Fc;
+  uint32_t K;                          // tiles per workgroup
+  uint32_t cpt;                        // 16-byte dst chunks per tile (power of two <= 256)
+  uint32_t cpt_shift;                  // log2(cpt)
+  uint32_t tgroups;
+  FD fd_tg;
+  BatchArg batch;
+  SwzArg swd;
+};
+
+// Padded or gathered tiles ([CuTe algebra page, section 2.2]: composing a padded
+// layout skips the pad).  A workgroup stages the whole 16-byte-aligned source
+// footprint of K tiles in LDS with 16-byte loads (pad words included: DRAM
+// fetches them with their lines anyway), then each lane builds 16-byte dst chunks
+// by gathering elements from LDS and stores them contiguously.
+template <int EB>
+__global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
+  using T = typename Raw<EB>::T;
+  constexpr int V = 16 / EB;
+  using C = Chunk<T, V>;
+  extern __shared__ uint4 lds[];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  uint32_t blk = blockIdx.x;
+  uint32_t r1 = fdiv(blk, t.fd_tg);
+  uint32_t tg = blk - r1 * t.tgroups;
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r1, &bs, &bd);
+  const uint32_t t0 = tg * t.K;
+
+  const uint32_t nload = t.K * t.Fc;
+  for (uint32_t idx = threadIdx.x; idx < nload; idx += 256) {
+    uint32_t kk = fdiv(idx, t.fd_Fc);
+    uint32_t c = idx - kk * t.Fc;
+    uint32_t tile = t0 + kk;
+    if (tile < t.T) {
+      size_t byte = (size_t)(tile * t.Ts + bs) * EB + (size_t)c * 16;
+      lds[idx] = *(const uint4*)(src + byte);
+    }
+  }
+  __syncthreads();
+
+  // this lane's chunk position inside a tile is fixed (cpt divides 256)
+  const uint32_t c = threadIdx.x & (t.cpt - 1);
+  uint32_t g[V];
+#pragma unroll
+  for (int x = 0; x < V; ++x) {
+    uint32_t e = c * V + x, off = 0;
+    for (int k = 0; k < t.inner; ++k) {
+      uint32_t q = (k == t.inner - 1) ? 0u : fdiv(e, t.in_fd[k]);
+      off += (e - q * t.in_ext[k]) * t.in_ss[k];
+      e = q;
+    }
+    g[x] = off;
+  }
+  const T* ldsT = (const T*)lds;
+  const uint32_t nstore = t.K * t.cpt;
+  for (uint32_t idx = threadIdx.x; idx < nstore; idx += 256) {
+    uint32_t kk = idx >> t.cpt_shift;
+    uint32_t tile = t0 + kk;
+    if (tile >= t.T) continue;
+    C o;
+    const uint32_t base = kk * t.Fc * V;  // tile's first element in LDS
+#pragma unroll
+    for (int x = 0; x < V; ++x) o.e[x] = ldsT[base + g[x]];
+    uint32_t dof = swz32(tile * t.Td + bd + c * V, t.swd);
+    *(C*)(dst + (size_t)dof * EB) = o;
+  }
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+static int check_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_hip_error(hipGetErrorString(e));
+    return LR_ERR_HIP;
+  }
+  return LR_OK;
+}
+
+static unsigned grid_cap(int64_t g) {
+  if (g < 1) g = 1;
+  return (unsigned)(g > 0x7FFFFFFF ? 0x7FFFFFFF : g);
+}
+
+static void fill_side(SideArg* s, const lr_layout* L, bool wide) {
+  std::memset(s, 0, sizeof(*s));
+  s->nleaves = L->nleaves;
+  for (int i = 0; i < L->nleaves; ++i) {
+    s->ext64[i] = L->shape[i];
+    s->stride64[i] = L->stride[i];
+    if (!wide) {
+      s->ext[i] = (uint32_t)L->shape[i];
+      s->fd[i] = fd_of(L->shape[i]);
+      s->stride[i] = (uint32_t)L->stride[i];
+    }
+  }
+  Swz z{L->swz_b, L->swz_m, L->swz_s};
+  s->sw = swz_arg(z);
+  s->mask64 = L->swz_b > 0 ? (((uint64_t(1) << L->swz_b) - 1) << L->swz_m) : 0;
+}
+
+static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1) {
+  std::memset(b, 0, sizeof(*b));
+  for (int k = 0; k < p.rank; ++k) {
+    if (k == skip0 || k == skip1) continue;
+    int r = b->rank++;
+    b->ext[r] = (uint32_t)p.m[k].ext;
+    b->fd[r] = fd_of(p.m[k].ext);
+    b->ss[r] = (uint32_t)p.m[k].ss;
+    b->sd[r] = (uint32_t)p.m[k].sd;
+  }
+}
+
+template <int UB>
+static void launch_generic(const GenericArgs& a, bool wide, unsigned grid, hipStream_t st) {
+  if (wide)
+    hipLaunchKernelGGL((k_generic<UB, true>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_generic<UB, false>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int EB>
+static void launch_dual(const DualArgs& a, bool wide, unsigned grid, hipStream_t st) {
+  if (wide)
+    hipLaunchKernelGGL((k_dual<EB, true>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_dual<EB, false>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int EB, int V>
+static void launch_transpose_v(const TransposeArgs& a, bool lds, unsigned grid, hipStream_t st) {
+  if (lds)
+    hipLaunchKernelGGL((k_transpose<EB, V, true>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_transpose<EB, V, false>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int EB>
+static bool launch_transpose(const TransposeArgs& a, int v, bool lds, unsigned grid, hipStream_t st) {
+  switch (v) {
+    case 1: launch_transpose_v<EB, 1>(a, lds, grid, st); return true;
+    case 2: if constexpr (EB <= 8) { launch_transpose_v<EB, 2>(a, lds, grid, st); return true; } break;
+    case 4: if constexpr (EB <= 4) { launch_transpose_v<EB, 4>(a, lds, grid, st); return true; } break;
+    case 8: if constexpr (EB <= 2) { launch_transpose_v<EB, 8>(a, lds, grid, st); return true; } break;
+    case 16: if constexpr (EB == 1) { launch_transpose_v<EB, 16>(a, lds, grid, st); return true; } break;
+  }
+  return false;
+}
+
+template <int EB>
+static bool launch_interleave(const InterleaveArgs& a, int nb, unsigned grid, hipStream_t st) {
+  switch (nb) {
+    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+  }
+  return false;
+}
+
+#define LR_DISPATCH_EB(eb, CALL)          \
+  switch (eb) {                            \
+    case 1: { constexpr int EBV = 1; CALL; } break;   \
+    case 2: { constexpr int EBV = 2; CALL; } break;   \
+    case 4: { constexpr int EBV = 4; CALL; } break;   \
+    case 8: { constexpr int EBV = 8; CALL; } break;   \
+    case 16: { constexpr int EBV = 16; CALL; } break; \
+    default: return LR_ERR_ELEM_BYTES;     \
+  }
+
+static size_t ptr_align(const void* p) {
+  uintptr_t a = (uintptr_t)p;
+  if (a == 0) return 16;
+  size_t al = (size_t)(a & (~a + 1));
+  return al > 16 ? 16 : al;
+}
+
+static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_layout* Ld, const Plan& p,
+                    hipStream_t st) {
+  const unsigned grid = grid_cap(p.grid);
+  switch (p.path) {
+    case LR_PATH_GENERIC:
+    case LR_PATH_VECTOR: {
+      GenericArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.src = src;
+      a.dst = dst;
+      a.rank = p.rank;
+      const int64_t v = p.v;
+      for (int k = 0; k < p.rank; ++k) {
+        // mode 0 is the common contiguous mode when v > 1: it is counted in units
+        int64_t ext = (k == 0) ? p.m[0].ext / v : p.m[k].ext;
+        int64_t ss = (k == 0 && v > 1) ? 1 : p.m[k].ss / v;
+        int64_t sd = (k == 0 && v > 1) ? 1 : p.m[k].sd / v;
+        a.w[k] = {ext, ss, sd};
+        if (!p.wide) a.m[k] = {(uint32_t)ext, fd_of(ext), (uint32_t)ss, (uint32_t)sd};
+      }
+      const int sh = (v == 1) ? 0 : (v == 2 ? 1 : v == 4 ? 2 : v == 8 ? 3 : 4);
+      Swz zs = p.sw_s, zd = p.sw_d;
+      if (zs.b) zs.m -= sh;
+      if (zd.b) zd.m -= sh;
+      a.sws = swz_arg(zs);
+      a.swd = swz_arg(zd);
+      a.sws_mask64 = zs.b ? (((uint64_t(1) << zs.b) - 1) << zs.m) : 0;
+      a.swd_mask64 = zd.b ? (((uint64_t(1) << zd.b) - 1) << zd.m) : 0;
+      a.n_units = p.n_units;
+      a.n_chunks = (p.n_units + 1023) / 1024;
+      const int ub = p.v * p.eb;
+      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, grid, st));
+      return check_launch();
+    }
+    case LR_PATH_DUAL:
+    case LR_PATH_ALIAS: {
+      DualArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.src = src;
+      a.dst = dst;
+      fill_side(&a.s, Ls, p.wide);
+      fill_side(&a.d, Ld, p.wide);
+      a.n = p.n;
+      a.n_chunks = (p.n + 1023) / 1024;
+      if (p.path == LR_PATH_ALIAS) {
+        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_alias<EBV>), dim3(grid), dim3(1024), 0, st, a));
+      } else {
+        LR_DISPATCH_EB(p.eb, launch_dual<EBV>(a, p.wide, grid, st));
+      }
+      return check_launch();
+    }
+    case LR_PATH_TRANSPOSE:
+    case LR_PATH_TRANSPOSE_DIRECT: {
+      TransposeArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.src = src;
+      a.dst = dst;
+      a.ext_a = (uint32_t)p.m[p.a].ext;
+      a.ext_b = (uint32_t)p.m[p.b].ext;
+      a.ss_b = (uint32_t)p.m[p.b].ss;
+      a.sd_a = (uint32_t)p.m[p.a].sd;
+      a.tiles_a = (uint32_t)((p.m[p.a].ext + p.tile_a - 1) / p.tile_a);
+      a.tiles_b = (uint32_t)((p.m[p.b].ext + p.tile_b - 1) / p.tile_b);
+      a.fd_ta = fd_of(a.tiles_a);
+      a.fd_tb = fd_of(a.tiles_b);
+      fill_batch(&a.batch, p, p.a, p.b);
+      a.sws = swz_arg(p.sw_s);
+      a.swd = swz_arg(p.sw_d);
+      const bool lds = p.path == LR_PATH_TRANSPOSE;
+      bool ok = false;
+      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, grid, st));
+      if (!ok) return LR_ERR_PATH;
+      return check_launch();
+    }
+    case LR_PATH_INTERLEAVE: {
+      InterleaveArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.src = src;
+      a.dst = dst;
+      a.ext_a = (uint32_t)p.m[p.a].ext;
+      a.ss_b = (uint32_t)p.m[p.b].ss;
+      a.tiles_a = (uint32_t)((p.m[p.a].ext + p.tile_a - 1) / p.tile_a);
+      a.fd_ta = fd_of(a.tiles_a);
+      fill_batch(&a.batch, p, p.a, p.b);
+      a.sws = swz_arg(p.sw_s);
+      a.swd = swz_arg(p.sw_d);
+      bool ok = false;
+      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, grid, st));
+      if (!ok) return LR_ERR_PATH;
+      return check_launch();
+    }
+    case LR_PATH_STAGED: {
+      StagedArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.src = src;
+      a.dst = dst;
+      a.inner = p.staged_inner;
+      for (int k = 0; k < p.staged_inner; ++k) {
+        a.in_ext[k] = (uint32_t)p.m[k].ext;
+        a.in_fd[k] = fd_of(p.m[k].ext);
+        a.in_ss[k] = (uint32_t)p.m[k].ss;
+      }
+      const JMode& tm = p.m[p.staged_inner];
+      a.T = (uint32_t)tm.ext;
+      a.Ts = (uint32_t)tm.ss;
+      a.Td = (uint32_t)tm.sd;
+      a.Fc = (uint32_t)p.staged_Fc;
+      a.fd_Fc = fd_of(p.staged_Fc);
+      a.K = (uint32_t)p.staged_K;
+      a.cpt = (uint32_t)p.staged_cpt;
+      while ((1u << a.cpt_shift) < a.cpt) ++a.cpt_shift;
+      a.tgroups = (uint32_t)((tm.ext + p.staged_K - 1) / p.staged_K);
+      a.fd_tg = fd_of(a.tgroups);
+      std::memset(&a.batch, 0, sizeof(a.batch));
+      for (int k = p.staged_inner + 1; k < p.rank; ++k) {
+        int r = a.batch.rank++;
+        a.batch.ext[r] = (uint32_t)p.m[k].ext;
+        a.batch.fd[r] = fd_of(p.m[k].ext);
+        a.batch.ss[r] = (uint32_t)p.m[k].ss;
+        a.batch.sd[r] = (uint32_t)p.m[k].sd;
+      }
+      a.swd = swz_arg(p.sw_d);
+      const size_t shm = (size_t)p.staged_K * (size_t)p.staged_Fc * 16;
+      LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV>), dim3(grid), dim3(256), shm, st, a));
+      return check_launch();
+    }
+  }
+  return LR_ERR_PATH;
+}
+
+static int fill_eval(EvalArgs* a, const lr_layout* L) {
+  std::memset(a, 0, sizeof(*a));
+  a->nleaves = L->nleaves;
+  a->nmodes = L->nmodes;
+  a->size = size_of(L);
+  a->small = a->size < (int64_t(1) << 31);
+  for (int i = 0; i < L->nleaves; ++i) {
+    a->shape[i] = L->shape[i];
+    a->stride[i] = L->stride[i];
+    if (a->small) a->fd[i] = fd_of(L->shape[i]);
+  }
+  int lo = 0;
+  for (int m = 0; m < L->nmodes; ++m) {
+    a->mode_end[m] = L->mode_end[m];
+    int64_t s = 1;
+    for (int i = lo; i < L->mode_end[m]; ++i) s *= L->shape[i];
+    a->mode_size[m] = s;
+    lo = L->mode_end[m];
+  }
+  if (L->swz_b > 0) {
+    a->swz_mask = ((uint64_t(1) << L->swz_b) - 1) << L->swz_m;
+    a->swz_shift = (uint32_t)L->swz_s;
+  }
+  return LR_OK;
+}
+
+}  // namespace lr
+
+using namespace lr;
+
+extern "C" {
+
+const char* lr_last_hip_error(void) { return g_hip_err; }
+
+int lr_layout_eval(const lr_layout* L, const int64_t* idx, int64_t n, int64_t* offsets, void* stream) {
+  int rc = validate(L);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && !offsets)) return LR_ERR_INVALID;
+  if (n == 0) return LR_OK;
+  EvalArgs a;
+  if ((rc = fill_eval(&a, L))) return rc;
+  a.idx = idx;
+  a.n = n;
+  a.out = offsets;
+  hipLaunchKernelGGL(k_eval_index, dim3(grid_cap(std::min<int64_t>((n + 255) / 256, 65536))), dim3(256), 0,
+                     (hipStream_t)stream, a);
+  return check_launch();
+}
+
+int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, int32_t ncols, int64_t* offsets,
+                          void* stream) {
+  int rc = validate(L);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!offsets || !coords))) return LR_ERR_INVALID;
+  if (ncols != L->nmodes && ncols != L->nleaves) return LR_ERR_INVALID;
+  if (n == 0) return LR_OK;
+  EvalArgs a;
+  if ((rc = fill_eval(&a, L))) return rc;
+  a.coords = coords;
+  a.ncols = ncols;
+  a.n = n;
+  a.out = offsets;
+  hipLaunchKernelGGL(k_eval_coords, dim3(grid_cap(std::min<int64_t>((n + 255) / 256, 65536))), dim3(256), 0,
+                     (hipStream_t)stream, a);
+  return check_launch();
+}
+
+int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst, const lr_layout* Ld,
+                   int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags, void* stream) {
+  if (!src || !dst) return LR_ERR_INVALID;
+  Plan p;
+  int rc = plan_copy(Ls, src_capacity_elems, ptr_align(src), Ld, dst_capacity_elems, ptr_align(dst), elem_bytes,
+                     flags, &p);
+  if (rc) return rc;
+  // storage overlap: [src, src + cap*eb) vs [dst, dst + cap*eb)
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  const uintptr_t s1 = s0 + (uintptr_t)src_capacity_elems * elem_bytes;
+  const uintptr_t d1 = d0 + (uintptr_t)dst_capacity_elems * elem_bytes;
+  if (s0 < d1 && d0 < s1) return LR_ERR_OVERLAP;
+  return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
+}
+
+}  // extern "C"

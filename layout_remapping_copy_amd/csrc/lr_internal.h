@@ -1,0 +1,79 @@
+// Internal (non-ABI) declarations shared by the host algebra, the copy planner
+// and the HIP launch code.  Nothing here crosses the C ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "layout_remap.h"
+
+namespace lr {
+
+constexpr int kMaxJoint = 2 * LR_MAX_LEAVES;  // a joint refinement has < 2*16 modes
+constexpr int kMaxKernelModes = 16;           // modes a kernel argument block carries
+
+struct Leaf {
+  int64_t n, d;
+};
+
+// Checked int64 arithmetic.
+inline bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+inline bool add_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_add_overflow(a, b, r); }
+
+int validate(const lr_layout* L);
+int64_t size_of(const lr_layout* L);            // valid L only
+int64_t max_linear_offset(const lr_layout* L);  // valid L only, unswizzled
+int64_t cosize_bound(const lr_layout* L);       // valid L only
+bool injective(const lr_layout* L);             // valid L only
+
+// Multiply-high division by an invariant divisor d (1 <= d < 2^31), exact for
+// dividends x < 2^31 (Granlund & Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, the round-up variant):  with l = ceil(log2 d) and
+// m = ceil(2^(31+l) / d) < 2^32,  x / d == (x * m) >> (31 + l).  On the device this
+// is umulhi(x, m) >> (l - 1).  d == 1 is encoded as m == 0 (quotient = x).
+struct FastDiv {
+  uint32_t m, s;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+struct JMode {
+  int64_t ext, ss, sd;
+};
+
+// Joint flat form of a pair of layouts (unswizzled parts) over one index space;
+// false when the two prefix-product sequences do not form one divisibility chain.
+bool joint_flat(const lr_layout* s, const lr_layout* d, JMode* out, int* rank, bool sort_by_dst);
+
+struct Swz {
+  int32_t b, m, s;  // b == 0: none
+};
+
+// Everything the launch code needs.
+struct Plan {
+  int path;           // lr_path
+  int eb;             // bytes per (fused) element
+  int v;              // elements per unit (generic/vector) or per chunk (transpose/interleave)
+  bool wide;
+  int rank;           // joint modes (after fusion)
+  JMode m[kMaxJoint];
+  int a, b;           // src-contiguous / dst-contiguous modes, -1 if none
+  Swz sw_s, sw_d;     // swizzles in units of (fused) elements
+  int block;
+  int64_t tile_a, tile_b;
+  int64_t grid;
+  int64_t n;          // logical elements (original)
+  int64_t n_units;    // generic/vector: units to move
+  // staged path
+  int staged_inner;   // number of inner modes [0, staged_inner)
+  int64_t staged_P, staged_F, staged_Fc, staged_K, staged_cpt;
+  // alias path
+  int64_t alias_windows;
+};
+
+// Plans a copy; fills `p`.  Returns 0 or an lr_status.
+int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld,
+              int64_t dst_cap, size_t dst_align, size_t elem_bytes, uint32_t flags, Plan* p);
+
+void set_hip_error(const char* text);
+
+}  // namespace lr

@@ -1,0 +1,429 @@
+// Copy planner: joint flat form of the two layouts, the common vector width,
+// path selection and launch shapes.  Host only.
+//
+// The copy is dst[Ld(k)] = src[Ls(k)] for every index k ([CuTe algebra page,
+// jsqmd.com/news/768714, sections 2.3 and 5.1]).  For an injective Ld the order of
+// k is free, so the planner rewrites the pair of layouts as one list of joint
+// modes (extent, src stride, dst stride), sorted by dst stride, and picks a
+// kernel from the shape of that list:
+//   * the first mode contiguous on both sides  -> 16-byte vectors along it;
+//   * contiguous modes differ, the dst one short -> in-register interleave;
+//   * contiguous modes differ                    -> register-blocked tile transpose;
+//   * small compact source footprints per tile   -> footprint staged in LDS;
+//   * anything else                               -> one unit per lane.
+// [CuTe algebra page, section 2.3] motivates the first rule (the common part of
+// the inverse layouts gives the widest copy); [print_layout page, sections 5.1
+// and 5.2] the other two (adjacent lanes on adjacent addresses, bank-spread
+// staging).
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
+#include "lr_internal.h"
+
+namespace lr {
+
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{0, 0};
+  if (d <= 1) return f;
+  int l = 0;
+  while ((uint64_t(1) << l) < d) ++l;  // l = ceil(log2 d), 1..31
+  uint64_t p = uint64_t(1) << (31 + l);
+  uint64_t m = (p + d - 1) / d;  // ceil(2^(31+l)/d) < 2^32
+  f.m = (uint32_t)m;
+  f.s = (uint32_t)(l - 1);
+  return f;
+}
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+static int log2i(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+
+bool joint_flat(const lr_layout* s, const lr_layout* d, JMode* out, int* rank, bool sort_by_dst) {
+  Leaf a[LR_MAX_LEAVES], b[LR_MAX_LEAVES];
+  int na = 0, nb = 0;
+  for (int i = 0; i < s->nleaves; ++i)
+    if (s->shape[i] > 1) a[na++] = {s->shape[i], s->stride[i]};
+  for (int i = 0; i < d->nleaves; ++i)
+    if (d->shape[i] > 1) b[nb++] = {d->shape[i], d->stride[i]};
+  int r = 0;
+  int i = 0, j = 0;
+  int64_t pa = 1, pb = 1, pos = 1;  // pa/pb: start of current leaf; pos: current cut
+  while (i < na && j < nb) {
+    int64_t ea = pa * a[i].n, eb = pb * b[j].n;
+    int64_t nxt = std::min(ea, eb);
+    if (nxt % pos) return false;
+    out[r].ext = nxt / pos;
+    out[r].ss = a[i].d * (pos / pa);
+    out[r].sd = b[j].d * (pos / pb);
+    ++r;
+    pos = nxt;
+    if (nxt == ea) {
+      pa = ea;
+      ++i;
+    }
+    if (nxt == eb) {
+      pb = eb;
+      ++j;
+    }
+  }
+  if (i != na || j != nb) return false;  // sizes differ (checked by the caller)
+  auto merge = [](JMode* m, int n) {
+    int w = 0;
+    for (int k = 0; k < n; ++k) {
+      if (m[k].ext == 1) continue;
+      if (w > 0 && m[k].ss == m[w - 1].ext * m[w - 1].ss && m[k].sd == m[w - 1].ext * m[w - 1].sd) {
+        m[w - 1].ext *= m[k].ext;
+        continue;
+      }
+      m[w++] = m[k];
+    }
+    return w;
+  };
+  r = merge(out, r);
+  if (sort_by_dst) {
+    while (true) {
+      JMode tmp[kMaxJoint];
+      std::memcpy(tmp, out, sizeof(JMode) * r);
+      std::stable_sort(tmp, tmp + r, [](const JMode& x, const JMode& y) {
+        return x.sd < y.sd || (x.sd == y.sd && x.ss < y.ss);
+      });
+      int r2 = merge(tmp, r);
+      bool same = r2 == r && std::memcmp(tmp, out, sizeof(JMode) * r) == 0;
+      std::memcpy(out, tmp, sizeof(JMode) * r2);
+      r = r2;
+      if (same) break;
+    }
+  }
+  *rank = r;
+  return true;
+}
+
+// largest power of two v with v | x (x > 0)
+static int64_t pow2_divisor(int64_t x) { return x & (-x); }
+
+static bool swz_keeps(const Swz& z, int64_t v) { return z.b == 0 || (int64_t(1) << z.m) >= v; }
+
+// Largest unit (power of two elements, unit*eb <= 16) for the generic/vector kernel.
+static int64_t unit_width(const Plan& p, size_t align_s, size_t align_d) {
+  if (p.rank == 0 || p.m[0].ss != 1 || p.m[0].sd != 1) return 1;
+  int64_t v = std::min<int64_t>(16 / p.eb, pow2_divisor(p.m[0].ext));
+  for (int k = 1; k < p.rank; ++k) {
+    if (p.m[k].ss) v = std::min(v, pow2_divisor(p.m[k].ss));
+    if (p.m[k].sd) v = std::min(v, pow2_divisor(p.m[k].sd));
+  }
+  while (v > 1 && (!swz_keeps(p.sw_s, v) || !swz_keeps(p.sw_d, v) || (align_s % (size_t)(v * p.eb)) ||
+                   (align_d % (size_t)(v * p.eb))))
+    v >>= 1;
+  return v;
+}
+
+static bool env_flag(const char* name) {
+  const char* e = std::getenv(name);
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+static int plan_alias(Plan* p, int64_t n, int64_t cos_s, int64_t cos_d) {
+  const int64_t win = 8192;  // dst offsets owned by one workgroup (LDS owner table)
+  int64_t windows = (cos_d + win - 1) / win;
+  if (cos_d > (int64_t(1) << 26) || n >= (int64_t(1) << 31) || cos_s >= (int64_t(1) << 31)) return LR_ERR_ALIAS;
+  if ((double)n * (double)windows > (double)(int64_t(1) << 36)) return LR_ERR_ALIAS;
+  p->path = LR_PATH_ALIAS;
+  p->alias_windows = windows;
+  p->block = 1024;
+  p->grid = windows;
+  return LR_OK;
+}
+
+int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
+              size_t dst_align, size_t elem_bytes, uint32_t flags, Plan* p) {
+  int rc;
+  if ((rc = validate(Ls))) return rc;
+  if ((rc = validate(Ld))) return rc;
+  if (!p) return LR_ERR_INVALID;
+  if (!(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4 || elem_bytes == 8 || elem_bytes == 16))
+    return LR_ERR_ELEM_BYTES;
+  if (src_cap < 0 || dst_cap < 0) return LR_ERR_INVALID;
+  std::memset(p, 0, sizeof(*p));
+  p->a = p->b = -1;
+  const int64_t n = size_of(Ls);
+  if (size_of(Ld) != n) return LR_ERR_SIZE_MISMATCH;
+  const int64_t cos_s = cosize_bound(Ls), cos_d = cosize_bound(Ld);
+  if (cos_s > src_cap || cos_d > dst_cap) return LR_ERR_BOUNDS;
+  int64_t t;
+  if (!mul_ok(src_cap, (int64_t)elem_bytes, &t) || !mul_ok(dst_cap, (int64_t)elem_bytes, &t)) return LR_ERR_OVERFLOW;
+  p->n = n;
+  p->eb = (int)elem_bytes;
+  p->sw_s = {Ls->swz_b, Ls->swz_m, Ls->swz_s};
+  p->sw_d = {Ld->swz_b, Ld->swz_m, Ld->swz_s};
+  if (src_align == 0) src_align = 1;
+  if (dst_align == 0) dst_align = 1;
+  src_align = std::min<size_t>(src_align & (~src_align + 1), 16);
+  dst_align = std::min<size_t>(dst_align & (~dst_align + 1), 16);
+
+  const uint32_t forced_raw = (flags >> 8) & 0xFFu;
+  const int forced = forced_raw ? (int)forced_raw - 1 : -1;
+  if (forced > LR_PATH_TRANSPOSE_DIRECT) return LR_ERR_INVALID;
+  const int64_t lim32 = int64_t(1) << 31;
+  p->wide = (flags & LR_COPY_WIDE_INDEX) || n >= lim32 || cos_s >= lim32 || cos_d >= lim32;
+  p->block = 256;
+
+  // --- non-injective destination: sequential semantics
+  const bool inj = injective(Ld);
+  if (!inj || forced == LR_PATH_ALIAS) {
+    if (!inj && !(flags & LR_COPY_ORDERED_ALIAS)) return LR_ERR_ALIAS;
+    if (forced >= 0 && forced != LR_PATH_ALIAS) return LR_ERR_PATH;
+    p->wide = false;
+    return plan_alias(p, n, cos_s, cos_d);
+  }
+
+  // --- joint flat form
+  int rank = 0;
+  const bool have_joint = joint_flat(Ls, Ld, p->m, &rank, true);
+  p->rank = have_joint ? rank : 0;
+  if (!have_joint || forced == LR_PATH_DUAL || (have_joint && rank > kMaxKernelModes)) {
+    if (forced >= 0 && forced != LR_PATH_DUAL) return LR_ERR_PATH;
+    p->path = LR_PATH_DUAL;
+    p->rank = 0;
+    p->v = 1;
+    p->n_units = n;
+    p->grid = (n + 1023) / 1024;
+    return LR_OK;
+  }
+  if (p->wide) {
+    if (forced >= 0 && forced != LR_PATH_GENERIC) return LR_ERR_PATH;
+    p->path = LR_PATH_GENERIC;
+    p->v = 1;
+    p->n_units = n;
+    p->grid = (n + 1023) / 1024;
+    return LR_OK;
+  }
+
+  // --- long common contiguous mode: 16-byte vectors straight through
+  const bool common0 = p->rank > 0 && p->m[0].ss == 1 && p->m[0].sd == 1;
+  const int64_t v0 = unit_width(*p, src_align, dst_align);
+  const bool want_vector = common0 && p->m[0].ext * p->eb >= 64 && v0 * p->eb >= 4;
+  if (forced == LR_PATH_VECTOR && !(common0 && v0 > 1)) return LR_ERR_PATH;
+  if (forced == LR_PATH_VECTOR || forced == LR_PATH_GENERIC || (forced < 0 && want_vector)) {
+    p->path = forced == LR_PATH_GENERIC ? LR_PATH_GENERIC : (v0 > 1 ? LR_PATH_VECTOR : LR_PATH_GENERIC);
+    p->v = (int)v0;
+    p->n_units = n / v0;
+    p->grid = (p->n_units + 1023) / 1024;
+    return LR_OK;
+  }
+
+  // --- fuse a short common contiguous prefix into a wider element
+  if (common0) {
+    const int64_t e = p->m[0].ext;
+    bool ok = is_pow2(e) && e * p->eb <= 16 && swz_keeps(p->sw_s, e) && swz_keeps(p->sw_d, e) &&
+              src_align % (size_t)(e * p->eb) == 0 && dst_align % (size_t)(e * p->eb) == 0;
+    for (int k = 1; ok && k < p->rank; ++k) ok = (p->m[k].ss % e == 0) && (p->m[k].sd % e == 0);
+    if (ok) {
+      const int sh = log2i(e);
+      for (int k = 1; k < p->rank; ++k) p->m[k - 1] = {p->m[k].ext, p->m[k].ss / e, p->m[k].sd / e};
+      p->rank -= 1;
+      p->eb *= (int)e;
+      if (p->sw_s.b) p->sw_s.m -= sh;
+      if (p->sw_d.b) p->sw_d.m -= sh;
+      if (p->rank == 0) {  // the whole copy was one contiguous run
+        p->m[0] = {1, 1, 1};
+        p->rank = 1;
+      }
+    }
+  }
+
+  // --- a: contiguous in src, b: contiguous in dst
+  int a = -1, b = -1;
+  for (int k = 0; k < p->rank; ++k) {
+    if (b < 0 && p->m[k].sd == 1) b = k;
+    if (a < 0 && p->m[k].ss == 1) a = k;
+  }
+  const int V16 = 16 / p->eb;
+  auto batch_ok = [&](int64_t vs, int64_t vd, int ka, int kb) {
+    for (int k = 0; k < p->rank; ++k) {
+      if (k != ka && p->m[k].ss % vs) return false;
+      if (k != kb && p->m[k].sd % vd) return false;
+    }
+    return true;
+  };
+
+  // interleave: the dst-contiguous mode b is short and a follows it in dst
+  if (a >= 0 && b >= 0 && a != b && (forced < 0 || forced == LR_PATH_INTERLEAVE)) {
+    const int64_t nb = p->m[b].ext, V = V16;
+    bool ok = is_pow2(nb) && nb >= 2 && nb * p->eb <= 16 && p->m[a].sd == nb && p->m[a].ext % V == 0 &&
+              swz_keeps(p->sw_s, V) && swz_keeps(p->sw_d, V) && src_align >= 16 && dst_align >= 16;
+    if (ok) {
+      for (int k = 0; k < p->rank && ok; ++k) {
+        if (k != a && p->m[k].ss % V) ok = false;
+        if (k != a && k != b && p->m[k].sd % V) ok = false;
+      }
+    }
+    if (ok) {
+      p->path = LR_PATH_INTERLEAVE;
+      p->a = a;
+      p->b = b;
+      p->v = (int)V;
+      p->tile_a = 4 * 256 * V;  // a-elements per workgroup: 4 chunks per lane
+      p->tile_b = nb;
+      int64_t batch = 1;
+      for (int k = 0; k < p->rank; ++k)
+        if (k != a && k != b) batch *= p->m[k].ext;
+      p->grid = ((p->m[a].ext + p->tile_a - 1) / p->tile_a) * batch;
+      return LR_OK;
+    }
+    if (forced == LR_PATH_INTERLEAVE) return LR_ERR_PATH;
+  }
+
+  // transpose: register blocks of V x V elements, tiles of 16V x 16V
+  const bool want_t = forced < 0 || forced == LR_PATH_TRANSPOSE || forced == LR_PATH_TRANSPOSE_DIRECT;
+  if (a >= 0 && b >= 0 && a != b && want_t) {
+    int64_t V = V16;
+    while (V > 1) {
+      bool ok = p->m[a].ext % V == 0 && p->m[b].ext % V == 0 && batch_ok(V, V, a, b) && swz_keeps(p->sw_s, V) &&
+                swz_keeps(p->sw_d, V) && src_align % (size_t)(V * p->eb) == 0 &&
+                dst_align % (size_t)(V * p->eb) == 0;
+      if (ok) break;
+      V >>= 1;
+    }
+    const bool long_b = p->m[b].ext * p->eb > 16 && p->m[a].ext * p->eb > 16;
+    if (long_b || forced >= 0) {
+      p->path = forced == LR_PATH_TRANSPOSE_DIRECT ? LR_PATH_TRANSPOSE_DIRECT : LR_PATH_TRANSPOSE;
+      if (forced < 0 && env_flag("LR_TRANSPOSE_DIRECT")) p->path = LR_PATH_TRANSPOSE_DIRECT;
+      p->a = a;
+      p->b = b;
+      p->v = (int)V;
+      p->tile_a = 16 * V;
+      p->tile_b = 16 * V;
+      int64_t batch = 1;
+      for (int k = 0; k < p->rank; ++k)
+        if (k != a && k != b) batch *= p->m[k].ext;
+      p->grid = ((p->m[a].ext + p->tile_a - 1) / p->tile_a) * ((p->m[b].ext + p->tile_b - 1) / p->tile_b) * batch;
+      return LR_OK;
+    }
+  }
+  if (forced == LR_PATH_TRANSPOSE || forced == LR_PATH_TRANSPOSE_DIRECT) return LR_ERR_PATH;
+
+  // staged: a compact dst block of inner modes whose source footprint is small
+  if (forced < 0 || forced == LR_PATH_STAGED) {
+    bool ok = b == 0 && p->sw_s.b == 0 && src_align >= 16 && dst_align >= 16;
+    int inner = 0;
+    int64_t P = 1, F = 1;
+    if (ok) {
+      // grow the compact dst prefix while the source footprint stays small
+      int64_t want = 1;
+      while (inner < p->rank - 1 && p->m[inner].sd == want) {
+        int64_t P2 = P * p->m[inner].ext;
+        int64_t F2 = F + (p->m[inner].ext - 1) * p->m[inner].ss;
+        if (P2 * p->eb > 4096 || F2 > 2 * P2 + 64) break;
+        P = P2;
+        F = F2;
+        want = P;
+        ++inner;
+      }
+      ok = inner >= 1 && inner < p->rank && p->m[inner].sd == P && (P * p->eb) % 16 == 0 &&
+           is_pow2(P * p->eb / 16) && swz_keeps(p->sw_d, V16);
+      for (int k = inner; ok && k < p->rank; ++k) {
+        if ((p->m[k].ss * p->eb) % 16) ok = false;
+        if ((p->m[k].sd * p->eb) % 16) ok = false;
+      }
+      if (ok) {
+        const int64_t Fc = (F * p->eb + 15) / 16;
+        // the padded footprint of the last tile must stay inside the buffer
+        int64_t maxbase = 0;
+        for (int k = inner; k < p->rank; ++k) maxbase += (p->m[k].ext - 1) * p->m[k].ss;
+        ok = (maxbase + Fc * 16 / p->eb) <= src_cap;
+        if (ok) {
+          const int64_t cpt = P * p->eb / 16;  // 16-byte dst chunks per tile
+          // about four dst chunks per lane, and at most 40 KiB of LDS per workgroup
+          const int64_t K = std::max<int64_t>(1, std::min<int64_t>(1024 / cpt, 2560 / Fc));
+          p->path = LR_PATH_STAGED;
+          p->staged_inner = inner;
+          p->staged_P = P;
+          p->staged_F = F;
+          p->staged_Fc = Fc;
+          p->staged_cpt = cpt;
+          p->staged_K = K;
+          p->v = V16;
+          p->tile_a = K;
+          int64_t batch = 1;
+          for (int k = inner + 1; k < p->rank; ++k) batch *= p->m[k].ext;
+          p->grid = ((p->m[inner].ext + K - 1) / K) * batch;
+          return LR_OK;
+        }
+      }
+    }
+    if (forced == LR_PATH_STAGED) return LR_ERR_PATH;
+  }
+
+  // generic: one unit per lane over the (fused) joint modes
+  p->path = LR_PATH_GENERIC;
+  p->a = p->b = -1;
+  int64_t v = unit_width(*p, src_align, dst_align);
+  p->v = (int)v;
+  int64_t ne = 1;
+  for (int k = 0; k < p->rank; ++k) ne *= p->m[k].ext;
+  p->n_units = ne / v;
+  p->grid = (p->n_units + 1023) / 1024;
+  return LR_OK;
+}
+
+}  // namespace lr
+
+using namespace lr;
+
+extern "C" {
+
+int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align, const lr_layout* Ld,
+                 int64_t dst_capacity_elems, size_t dst_align, size_t elem_bytes, uint32_t flags, lr_plan* out) {
+  if (!out) return LR_ERR_INVALID;
+  Plan p;
+  int rc = plan_copy(Ls, src_capacity_elems, src_align, Ld, dst_capacity_elems, dst_align, elem_bytes, flags, &p);
+  if (rc) return rc;
+  std::memset(out, 0, sizeof(*out));
+  out->path = p.path;
+  out->elem_bytes = p.eb;
+  out->vec_elems = p.v;
+  out->wide = p.wide ? 1 : 0;
+  out->joint_rank = p.rank;
+  out->a_mode = p.a;
+  out->b_mode = p.b;
+  out->block = p.block;
+  out->tile_a = p.tile_a;
+  out->tile_b = p.tile_b;
+  out->grid = p.grid;
+  out->n_elems = p.n;
+  for (int k = 0; k < p.rank && k < 2 * LR_MAX_LEAVES; ++k) {
+    out->ext[k] = p.m[k].ext;
+    out->s_src[k] = p.m[k].ss;
+    out->s_dst[k] = p.m[k].sd;
+  }
+  return LR_OK;
+}
+
+int lr_max_common_vector(const lr_layout* src, const lr_layout* dst, size_t elem_bytes, int64_t* elems) {
+  int rc;
+  if ((rc = validate(src))) return rc;
+  if ((rc = validate(dst))) return rc;
+  if (!elems) return LR_ERR_INVALID;
+  if (!(elem_bytes == 1 || elem_bytes == 2 || elem_bytes == 4 || elem_bytes == 8 || elem_bytes == 16))
+    return LR_ERR_ELEM_BYTES;
+  if (size_of(src) != size_of(dst)) return LR_ERR_SIZE_MISMATCH;
+  *elems = 1;
+  if (!injective(dst)) return LR_OK;
+  Plan p;
+  std::memset(&p, 0, sizeof(p));
+  p.eb = (int)elem_bytes;
+  p.sw_s = {src->swz_b, src->swz_m, src->swz_s};
+  p.sw_d = {dst->swz_b, dst->swz_m, dst->swz_s};
+  int rank = 0;
+  if (!joint_flat(src, dst, p.m, &rank, true)) return LR_OK;
+  p.rank = rank;
+  *elems = unit_width(p, 16, 16);
+  return LR_OK;
+}
+
+}  // extern "C"

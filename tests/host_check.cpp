@@ -1,0 +1,173 @@
+// Host-only checks of the library's C++ sources (built with g++, no HIP):
+//   host_check fastdiv  -- the multiply-high division constants are exact
+//   host_check fuzz     -- random walk through the host algebra (run under
+//                          AddressSanitizer/UBSan by the test suite)
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "layout_remap.h"
+#include "lr_internal.h"
+
+static inline uint32_t qdiv(uint32_t x, lr::FastDiv f) {
+  if (f.m == 0) return x;
+  uint32_t hi = (uint32_t)(((uint64_t)x * f.m) >> 32);
+  return hi >> f.s;
+}
+
+static int check_div(uint32_t d, uint32_t x, lr::FastDiv f) {
+  if (qdiv(x, f) != x / d) {
+    std::printf("fastdiv mismatch d=%u x=%u got=%u want=%u\n", d, x, qdiv(x, f), x / d);
+    return 1;
+  }
+  return 0;
+}
+
+static int run_fastdiv() {
+  const uint32_t lim = 0x80000000u;  // dividends below 2^31
+  // exhaustive for a few divisors
+  for (uint32_t d : {3u, 7u, 3136u, 0x7FFFFFFFu}) {
+    lr::FastDiv f = lr::make_fastdiv(d);
+    for (uint32_t x = 0; x < lim; ++x)
+      if (qdiv(x, f) != x / d) return check_div(d, x, f);
+  }
+  // every quotient boundary (up to 2^17 quotients), the top of the range and
+  // random dividends for many more divisors
+  std::vector<uint32_t> ds;
+  for (uint32_t d = 1; d <= 4096; ++d) ds.push_back(d);
+  for (int k = 12; k < 31; ++k) {
+    ds.push_back(1u << k);
+    ds.push_back((1u << k) - 1);
+    ds.push_back((1u << k) + 1);
+  }
+  for (uint32_t d : {3136u, 802816u, 524288u, 1048576u, 16777216u, 14336u, 100352u, 65535u, 65537u}) ds.push_back(d);
+  std::mt19937_64 rng(12345);
+  for (int i = 0; i < 2000; ++i) ds.push_back(1 + (uint32_t)(rng() % 0x7FFFFFFFu));
+  for (uint32_t d : ds) {
+    lr::FastDiv f = lr::make_fastdiv(d);
+    uint64_t qmax = (lim - 1) / d;
+    uint64_t step = qmax > 131072 ? qmax / 131072 : 1;
+    for (uint64_t q = 0; q <= qmax; q += step) {
+      uint64_t x0 = q * d;
+      for (uint64_t x : {x0, x0 + d - 1, x0 ? x0 - 1 : 0})
+        if (x < lim && check_div(d, (uint32_t)x, f)) return 1;
+    }
+    for (uint32_t x = lim - 4096; x < lim; ++x)
+      if (check_div(d, x, f)) return 1;
+    for (int r = 0; r < 2000; ++r)
+      if (check_div(d, (uint32_t)(rng() % lim), f)) return 1;
+  }
+  std::printf("fastdiv ok (%zu divisors)\n", ds.size());
+  return 0;
+}
+
+static std::string rand_layout(std::mt19937_64& rng, bool swz) {
+  int nl = 1 + (int)(rng() % 6);
+  std::vector<int> ext(nl), st(nl);
+  for (int i = 0; i < nl; ++i) {
+    ext[i] = 1 + (int)(rng() % 6);
+    st[i] = (int)(rng() % 40);
+  }
+  std::string s = "(", d = "(";
+  int i = 0;
+  bool first = true;
+  while (i < nl) {
+    int j = i + 1 + (int)(rng() % (nl - i));
+    if (!first) {
+      s += ",";
+      d += ",";
+    }
+    first = false;
+    if (j - i == 1) {
+      s += std::to_string(ext[i]);
+      d += std::to_string(st[i]);
+    } else {
+      s += "(";
+      d += "(";
+      for (int k = i; k < j; ++k) {
+        if (k > i) {
+          s += ",";
+          d += ",";
+        }
+        s += std::to_string(ext[k]);
+        d += std::to_string(st[k]);
+      }
+      s += ")";
+      d += ")";
+    }
+    i = j;
+  }
+  std::string out = s + "):" + d + ")";
+  if (swz && rng() % 3 == 0) {
+    int b = 1 + (int)(rng() % 3);
+    out = "Sw<" + std::to_string(b) + "," + std::to_string(rng() % 4) + "," + std::to_string(b + rng() % 3) + "> o " +
+          out;
+  }
+  return out;
+}
+
+static int run_fuzz() {
+  std::mt19937_64 rng(777);
+  char buf[1024];
+  int n_ok = 0;
+  for (int it = 0; it < 20000; ++it) {
+    std::string ta = rand_layout(rng, true), tb = rand_layout(rng, true);
+    lr_layout a, b, r;
+    if (lr_layout_parse(ta.c_str(), &a) || lr_layout_parse(tb.c_str(), &b)) {
+      std::printf("parse failed: %s / %s\n", ta.c_str(), tb.c_str());
+      return 1;
+    }
+    if (lr_layout_format(&a, buf, sizeof(buf))) return 1;
+    lr_layout a2;
+    if (lr_layout_parse(buf, &a2) || std::memcmp(&a, &a2, sizeof(a)) != 0) {
+      std::printf("round trip failed: %s -> %s\n", ta.c_str(), buf);
+      return 1;
+    }
+    int64_t n;
+    lr_size(&a, &n);
+    lr_cosize(&a, &n);
+    lr_coalesce(&a, &r);
+    lr_composition(&a, &b, &r);
+    lr_right_inverse(&a, &r);
+    int64_t tiler[2] = {1 + (int64_t)(rng() % 4), 1 + (int64_t)(rng() % 4)};
+    lr_zipped_divide(&a, tiler, a.nmodes < 2 ? a.nmodes : 2, &r);
+    int32_t inj;
+    lr_is_injective(&a, &inj);
+    int64_t v;
+    lr_max_common_vector(&a, &b, 4, &v);
+    lr_plan p;
+    for (uint32_t fl : {0u, 1u, 2u}) {
+      lr_copy_plan(&a, 1 << 20, 16, &b, 1 << 20, 16, 2, fl, &p);
+      lr_copy_plan(&a, 1 << 20, 4, &a, 1 << 20, 8, 4, fl, &p);
+    }
+    for (int path = 0; path < 8; ++path) lr_copy_plan(&a, 1 << 20, 16, &a, 1 << 20, 16, 1, LR_COPY_FORCE_PATH(path), &p);
+    ++n_ok;
+  }
+  // malformed and adversarial descriptors
+  const char* bad[] = {"", "(", "()", "(1,2):(3)", "Sw<1,2> o 4:1", "((((((((((((((((((((((((((((((((((4))))))))))"
+                       "))))))))))))))))))))))):1", "99999999999999999999:1", "(4,2):(1,2) trailing", "Sw<70,0,80> o 4:1"};
+  lr_layout x;
+  for (const char* t : bad) lr_layout_parse(t, &x);
+  std::memset(&x, 0, sizeof(x));
+  x.nleaves = 17;
+  lr_layout_validate(&x);
+  x.nleaves = 2;
+  x.nmodes = 1;
+  x.mode_end[0] = 2;
+  x.shape[0] = x.shape[1] = int64_t(1) << 40;
+  x.stride[0] = 1;
+  x.stride[1] = int64_t(1) << 40;
+  if (lr_layout_validate(&x) != LR_ERR_OVERFLOW) return 1;
+  std::printf("fuzz ok (%d)\n", n_ok);
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc > 1 && std::strcmp(argv[1], "fastdiv") == 0) return run_fastdiv();
+  if (argc > 1 && std::strcmp(argv[1], "fuzz") == 0) return run_fuzz();
+  std::printf("usage: host_check fastdiv|fuzz\n");
+  return 2;
+}

@@ -1,0 +1,317 @@
+"""Host side of the C ABI (no GPU): the library loads and exports what the header
+declares, and its layout algebra and copy planner agree with the CPU oracle."""
+
+import os
+import random
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import layout as OL
+import workloads as W
+
+lr = pytest.importorskip("layout_remapping_copy_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(lr.LIB_PATH):
+        pytest.skip("library not built")
+
+
+def _same(Lc, Lo):
+    """C descriptor equals oracle layout: same leaves, same swizzle."""
+    return Lc.leaves == O.flatten(Lo) and Lc.swizzle == Lo.swz
+
+
+def _rand_layout(rng, max_leaves=4, max_ext=4, max_stride=16, swz_p=0.0, allow_zero=True):
+    nl = rng.randint(1, max_leaves)
+    ext = [rng.randint(1, max_ext) for _ in range(nl)]
+    st = [rng.randint(0 if allow_zero else 1, max_stride) for _ in range(nl)]
+    modes, i = [], 0
+    while i < nl:
+        j = rng.randint(i + 1, nl)
+        modes.append((ext[i:j], st[i:j]))
+        i = j
+
+    def t(xs):
+        return str(xs[0]) if len(xs) == 1 else "(" + ",".join(map(str, xs)) + ")"
+
+    if len(modes) == 1 and len(modes[0][0]) == 1:
+        text = f"{ext[0]}:{st[0]}"
+    else:
+        text = "(" + ",".join(t(m[0]) for m in modes) + "):(" + ",".join(t(m[1]) for m in modes) + ")"
+    if rng.random() < swz_p:
+        b = rng.randint(1, 2)
+        text = f"Sw<{b},{rng.randint(0, 2)},{rng.randint(b, 3)}> o " + text
+    return text
+
+
+def test_exports_every_header_symbol():
+    names = lr.header_symbols()
+    assert len(names) >= 19
+    h = lr.lib()
+    for n in names:
+        assert hasattr(h, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert exported == names
+
+
+def test_parse_format_pins():
+    for t in ["(4,2):(2,1)", "((4,2),(2,4)):((2,16),(1,8))", "Sw<3,3,3> o ((128,32),(64,64)):((64,524288),(1,8192))",
+              "8:1", "(4,2,2):(8,2,1)", "((4,8),2):((16,1),8)"]:
+        assert str(lr.parse(t)) == t
+    assert str(lr.parse("(4,2,2):(_8,_2,_1)")) == "(4,2,2):(8,2,1)"
+    assert str(lr.parse("Sw<3,0,3> ∘ (8,8):(8,1)")) == "Sw<3,0,3> o (8,8):(8,1)"
+    L = lr.parse("(((2,2),3),5):(((1,2),4),12)")
+    assert L.leaves == [(2, 1), (2, 2), (3, 4), (5, 12)] and L.mode_end == [3, 4]
+    for bad, code in [("(4,2):(1)", lr.binding.ERR_INVALID), ("(4,2):(1,-1)", lr.binding.ERR_INVALID),
+                      ("(0,2):(1,1)", lr.binding.ERR_INVALID), ("Sw<3,0,2> o 8:1", lr.binding.ERR_SWIZZLE),
+                      ("8:1 junk", lr.binding.ERR_INVALID), ("(1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17):"
+                                                              "(1,2,3,4,5,6,7,8,9,10,11,12,13,14,15,16,17)",
+                                                              lr.binding.ERR_INVALID)]:
+        with pytest.raises(lr.LayoutRemapError) as e:
+            lr.parse(bad)
+        assert e.value.code == code, bad
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.parse("(4294967296,4294967296,4294967296):(1,1,1)")
+    assert e.value.code == lr.binding.ERR_OVERFLOW
+
+
+def test_parse_matches_oracle_random():
+    rng = random.Random(17)
+    for _ in range(2000):
+        t = _rand_layout(rng, max_leaves=6, swz_p=0.3)
+        Lc, Lo = lr.parse(t), O.parse(t)
+        assert _same(Lc, Lo), t
+        assert Lc.size == O.size(Lo)
+        if Lo.swz is None:
+            assert Lc.cosize == O.cosize(Lo)
+        else:
+            assert Lc.cosize >= O.cosize(Lo)
+        assert str(lr.parse(str(Lc))) == str(Lc)
+
+
+def test_coalesce_matches_oracle():
+    rng = random.Random(18)
+    assert str(lr.coalesce("(8,8):(1,8)")) == "64:1"
+    for _ in range(2000):
+        t = _rand_layout(rng, max_leaves=6, swz_p=0.3)
+        assert _same(lr.coalesce(t), O.coalesce(O.parse(t))), t
+
+
+def test_composition_matches_oracle():
+    assert str(lr.composition("(8,8):(1,9)", "((4,8),2):((16,1),8)")) == "((4,8),2):((18,1),9)"
+    assert str(lr.composition("(8,8):(1,8)", "((4,8),2):((16,1),8)")) == "((4,8),2):((16,1),8)"
+    rng = random.Random(19)
+    agree = 0
+    for _ in range(4000):
+        ta = _rand_layout(rng, swz_p=0.2)
+        tb = _rand_layout(rng, max_stride=6, swz_p=0.05)
+        try:
+            want = O.compose(O.parse(ta), O.parse(tb))
+        except OL.NotRepresentable:
+            want = None
+        try:
+            got = lr.composition(ta, tb)
+        except lr.LayoutRemapError as e:
+            assert e.code == lr.binding.ERR_NOT_REPRESENTABLE
+            got = None
+        assert (got is None) == (want is None), (ta, tb)
+        if got is not None:
+            agree += 1
+            assert _same(got, want), (ta, tb, str(got), O.fmt(want))
+    assert agree > 1000
+
+
+def test_right_inverse_matches_oracle():
+    assert str(lr.right_inverse("((4,8),2):((16,1),8)")) == "(8,2,4):(4,32,1)"
+    rng = random.Random(20)
+    for _ in range(2000):
+        t = _rand_layout(rng)
+        assert _same(lr.right_inverse(t), O.right_inverse(O.parse(t))), t
+    with pytest.raises(lr.LayoutRemapError):
+        lr.right_inverse("Sw<1,0,1> o 4:1")
+
+
+def test_zipped_divide_matches_oracle():
+    Z = lr.zipped_divide("(128,128):(1,128)", (4, 8))
+    assert str(Z) == "((4,8),(32,16)):((1,128),(4,1024))"
+    rng = random.Random(21)
+    for _ in range(500):
+        r, c = rng.choice([2, 4, 6, 8, 12]), rng.choice([2, 3, 4, 8])
+        t = f"({r},{c}):({rng.randint(0, 5)},{rng.randint(1, 20)})"
+        tr = rng.choice([x for x in (1, 2, 3, 4) if r % x == 0])
+        tc = rng.choice([x for x in (1, 2, 4) if c % x == 0])
+        got = lr.zipped_divide(t, (tr, tc))
+        want = O.zipped_divide(O.parse(t), (tr, tc))
+        assert got.leaves == O.flatten(want)
+    with pytest.raises(lr.LayoutRemapError):
+        lr.zipped_divide("(6,4):(1,6)", (4,))
+
+
+def test_is_injective_matches_oracle():
+    assert not lr.is_injective("((4,2),(2,4)):((2,16),(1,8))")
+    assert lr.is_injective("(4,2,2):(8,2,1)")
+    assert lr.is_injective("(3,2):(2,3)")  # small: exact
+    rng = random.Random(22)
+    for _ in range(3000):
+        t = _rand_layout(rng, max_leaves=5, swz_p=0.3)
+        assert lr.is_injective(t) == O.is_injective(O.parse(t)), t
+    for name in W.FULL:
+        w = W.full(name)
+        assert lr.is_injective(w.dst_layout) == O.is_injective(O.parse(w.dst_layout))
+
+
+def test_thread_map_matches_oracle():
+    for p, s, k, t in [(8, 4, 16, 64), (8, 2, 16, 32), (4, 3, 17, 100), (32, 1, 64, 256)]:
+        L = lr.thread_map(p, s, k, t)
+        assert L.leaves == O.flatten(O.stripmined_layout(p, s, k, t))
+        B = lr.thread_map(p, 0, k, t)
+        assert B.leaves == O.flatten(O.pitch_linear_layout(p, k, t))
+
+
+def test_common_vector_sound_and_tight_on_workloads():
+    rng = random.Random(23)
+    for _ in range(1500):
+        td = _rand_layout(rng, max_stride=12, swz_p=0.2, allow_zero=False)
+        Ld = O.parse(td)
+        ts = _rand_layout(rng, max_stride=12, allow_zero=False)
+        if O.size(O.parse(ts)) != O.size(Ld):
+            ts = f"{O.size(Ld)}:1"
+        for eb in (1, 2, 4, 8):
+            v = lr.max_common_vector(ts, td, eb)
+            w = O.max_common_vector(O.parse(ts), Ld, eb)
+            assert v <= w and w % v == 0, (ts, td, eb, v, w)
+    for name, want in [("tile8x8", 1), ("transpose", 1), ("retile", 8), ("interleave", 1), ("nhwc2nchw", 1),
+                       ("padtiles", 1)]:
+        w = W.small(name)
+        v = lr.max_common_vector(w.src_layout, w.dst_layout, w.elem_bytes)
+        assert v == want == O.max_common_vector(O.parse(w.src_layout), O.parse(w.dst_layout), w.elem_bytes)
+    assert lr.max_common_vector("64:1", "64:1", 2) == 8
+    assert lr.max_common_vector("(4,4):(1,5)", "(4,4):(1,4)", 4) == 1
+
+
+EXPECTED_PATH = {"tile8x8": "alias", "transpose": "transpose", "retile": "vector", "interleave": "interleave",
+                 "nhwc2nchw": "transpose", "padtiles": "staged"}
+
+
+@pytest.mark.parametrize("name", list(W.FULL))
+def test_plan_of_workloads(name):
+    w = W.full(name)
+    flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
+    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
+    assert p["path"] == EXPECTED_PATH[name]
+    if name != "tile8x8":
+        want = O.joint_flat(O.parse(w.src_layout), O.parse(w.dst_layout), sort_by_dst=True)
+        assert p["joint"] == [tuple(m) for m in want]
+    if name == "retile":
+        assert p["vec_elems"] * w.elem_bytes == 16
+
+
+def test_plan_joint_matches_oracle_random():
+    rng = random.Random(24)
+    n = 0
+    for _ in range(2000):
+        ts = _rand_layout(rng, max_leaves=5, max_stride=40, allow_zero=False)
+        Ls = O.parse(ts)
+        exts = [e for e, _ in O.flatten(Ls)]
+        rng.shuffle(exts)
+        Ld = O.Layout(tuple(exts), tuple(rng.randint(1, 60) for _ in exts)) if len(exts) > 1 else O.Layout(exts[0], 1)
+        if not O.is_injective(Ld):
+            continue
+        jm = O.joint_flat(Ls, Ld, sort_by_dst=True)
+        if jm is None:  # no common refinement: generic cannot apply, dual does
+            with pytest.raises(lr.LayoutRemapError):
+                lr.copy_plan(ts, O.cosize(Ls), O.fmt(Ld), O.cosize(Ld), 4, lr.COPY_FORCE_PATH(lr.PATH_GENERIC))
+            assert lr.copy_plan(ts, O.cosize(Ls), O.fmt(Ld), O.cosize(Ld), 4)["path"] == "dual"
+            continue
+        p = lr.copy_plan(ts, O.cosize(Ls), O.fmt(Ld), O.cosize(Ld), 4, lr.COPY_FORCE_PATH(lr.PATH_GENERIC))
+        n += 1
+        assert p["joint"] == [tuple(m) for m in jm], (ts, O.fmt(Ld))
+    assert n > 300
+
+
+def test_plan_errors():
+    E = lr.binding
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.copy_plan("8:1", 8, "4:1", 4, 4)
+    assert e.value.code == E.ERR_SIZE_MISMATCH
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.copy_plan("8:1", 7, "8:1", 8, 4)
+    assert e.value.code == E.ERR_BOUNDS
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.copy_plan("(8,8):(1,8)", 64, "((4,2),(2,4)):((2,16),(1,8))", 64, 4)
+    assert e.value.code == E.ERR_ALIAS
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.copy_plan("8:1", 8, "8:1", 8, 3)
+    assert e.value.code == E.ERR_ELEM_BYTES
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.copy_plan("8:1", 8, "8:1", 8, 4, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
+    assert e.value.code == E.ERR_PATH
+    with pytest.raises(lr.LayoutRemapError) as e:  # ordered alias beyond its limits
+        lr.copy_plan("(67108864,2):(1,67108864)", 1 << 27, "(67108864,2):(1,0)", 1 << 26, 1,
+                     lr.COPY_ORDERED_ALIAS)
+    assert e.value.code == E.ERR_ALIAS
+    with pytest.raises(lr.LayoutRemapError) as e:  # destination cosize above 2^26
+        lr.copy_plan("(134217728,2):(1,134217728)", 1 << 28, "(134217728,2):(1,0)", 1 << 27, 1,
+                     lr.COPY_ORDERED_ALIAS)
+    assert e.value.code == E.ERR_ALIAS
+    p = lr.copy_plan("(1048576,128):(1,1048576)", 1 << 27, "(1048576,128):(1,0)", 1 << 20, 1, lr.COPY_ORDERED_ALIAS)
+    assert p["path"] == "alias" and p["grid"] == 128
+    p = lr.copy_plan("(8,8):(1,8)", 64, "((4,2),(2,4)):((2,16),(1,8))", 64, 4, lr.COPY_ORDERED_ALIAS)
+    assert p["path"] == "alias" and p["grid"] == 1
+
+
+def test_plan_alignment_drops_vector_width():
+    w = W.full("retile")
+    for align, want in [(16, 8), (8, 4), (4, 2), (2, 1)]:
+        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2, src_align=align)
+        assert p["vec_elems"] == want, align
+
+
+def test_plan_wide_index_for_big_offsets():
+    p = lr.copy_plan("(2,4):(1,1099511627776)", 3298534883330, "(2,4):(4,1)", 8, 1)
+    assert p["wide"] and p["path"] == "generic"
+    p = lr.copy_plan("64:1", 64, "64:1", 64, 4, lr.COPY_WIDE_INDEX)
+    assert p["wide"]
+
+
+# ---------------------------------------------------------------------------
+# Multiply-high division constants: built with g++ from the library's own host
+# sources, checked exhaustively for a few divisors over all 31-bit dividends and
+# at every quotient boundary for many more.  Also run under ASan/UBSan with a
+# random walk through the host algebra.
+# ---------------------------------------------------------------------------
+def _gpp(tmp_path, sanitize=False):
+    if not shutil.which("g++"):
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / ("host_check_san" if sanitize else "host_check"))
+    src = [os.path.join(ROOT, "tests", "host_check.cpp"),
+           os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", "host_layout.cpp"),
+           os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", "plan.cpp")]
+    flags = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"] if sanitize else ["-O2"]
+    cmd = ["g++", "-std=c++17", *flags, "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(ROOT, "layout_remapping_copy_amd", "csrc"), *src, "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return exe
+
+
+def test_fastdiv_exact(tmp_path):
+    exe = _gpp(tmp_path)
+    r = subprocess.run([exe, "fastdiv"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "fastdiv ok" in r.stdout
+
+
+def test_host_algebra_under_sanitizers(tmp_path):
+    exe = _gpp(tmp_path, sanitize=True)
+    r = subprocess.run([exe, "fuzz"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "fuzz ok" in r.stdout

@@ -1,0 +1,237 @@
+"""Benchmark of the layout-remapping copy on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input: a
+single lr_layout_copy of the fp16 8192 x 8192 transpose
+(8192,8192):(8192,1) -> (8192,8192):(1,8192) -- plan, launch, kernel.  Inputs are
+resident in HBM before the timed region.  Steps rotate over several source /
+destination buffer pairs (>= 1 GiB together) so that no step finds its data in
+the 256 MB Infinity Cache left there by the step before.
+
+Prints one JSON line.  `value` is effective GB/s = (bytes read + bytes written) /
+time, with algorithmic bytes 2 * N * elem_bytes per step.  The `roofline` object
+reports the dominant kernel's average duration from HIP events recorded on the
+launch stream over the timed region; `cpu_baseline` times the CPU oracle on a
+bounded slice of the same workload.  `workloads` adds the other large layouts
+(each timed the same way) for reference.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "plan.cpp", "lr_internal.h"):
+        with open(os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload_key: str):
+    """HBM bytes per launch measured by rocprofv3 counters (scaled by a plain copy
+    of known size), if taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(workload_key)
+    if not e or e.get("kernel_hash") != _kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
+    """Back-to-back copies rotating over buffer pairs; returns (ms per step, ms per
+    kernel from HIP events on the launch stream)."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        s, d = pairs[i % len(pairs)]
+        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        s, d = pairs[i % len(pairs)]
+        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, ev0.elapsed_time(ev1) / steps
+
+
+def _pairs(torch, dev, nbytes_src, nbytes_dst, first_src=None, min_total=1 << 30):
+    n = max(2, -(-min_total // (nbytes_src + nbytes_dst)))
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    out = []
+    for i in range(n):
+        if i == 0 and first_src is not None:
+            s = first_src
+        else:
+            s = torch.randint(0, 256, (nbytes_src,), dtype=torch.uint8, device=dev, generator=g)
+        d = torch.full((nbytes_dst,), 0xA5, dtype=torch.uint8, device=dev)
+        out.append((s, d))
+    return out
+
+
+def _cpu_baseline(w, seconds: float):
+    """The oracle's copy (as it stands) on the first rows of the same transpose,
+    repeated until about `seconds` of CPU time; GB/s on algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    n = 8192
+    rows = 512
+    src = W.make_src(w)
+    dst = W.make_dst(w)
+    Ls = oracle.parse(f"({rows},{n}):({n},1)")   # rows [0, 512) of the source, all columns
+    Ld = oracle.parse(f"({rows},{n}):(1,{n})")   # their transposed destinations
+    done, t0 = 0, time.perf_counter()
+    while True:
+        dst = oracle.copy(src, Ls, dst, Ld, w.elem_bytes)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    bytes_ = 2 * rows * n * w.elem_bytes * done
+    del np
+    return {
+        "value": round(bytes_ / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle.copy of rows 0..{rows - 1} of the 8192x8192 fp16 transpose "
+                  f"({rows}x{n} elements), {done} repetitions in {dt:.1f} s, single NumPy thread",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--path", default=None, help="force a copy path (for experiments)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the copy is measured on a single "
+                                   "MI355X; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import layout_remapping_copy_amd as lr
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    lr.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    flags = 0
+    if args.path:
+        flags = lr.COPY_FORCE_PATH({v: k for k, v in lr.binding.PATH_NAMES.items()}[args.path])
+
+    # ---- headline: fp16 8192 x 8192 transpose
+    w = W.full("transpose")
+    src0 = torch.from_numpy(W.make_src(w)).to(dev)
+    pairs = _pairs(torch, dev, w.src_elems * 2, w.dst_elems * 2, first_src=src0)
+    plan = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2, flags)
+    bytes_step = W.bytes_moved(w)
+    torch.cuda.synchronize()
+    wall_ms, kern_ms = _time_copies(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, args.warmup, flags)
+    value = bytes_step / (wall_ms * 1e-3) / 1e9
+    achieved = bytes_step / (kern_ms * 1e-3) / 1e9
+
+    # same-box device-to-device copy of equal bytes, for context
+    a, b = pairs[0][0], pairs[1][1]
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(20):
+        pairs[(i + 1) % len(pairs)][1].copy_(pairs[i % len(pairs)][0])
+    e1.record()
+    torch.cuda.synchronize()
+    d2d = bytes_step / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
+    del pairs, src0, a, b
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": "layout_copy effective GB/s (read+write) and % of HBM peak on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {
+            "workload": "transpose fp16 8192x8192: (8192,8192):(8192,1) -> (8192,8192):(1,8192)",
+            "path": plan["path"],
+            "vec_elems": plan["vec_elems"],
+            "bytes_per_step": bytes_step,
+            "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+            "d2d_copy_GBps": round(d2d, 1),
+            "frac_of_d2d_copy": round(value / d2d, 4),
+            "buffers": "rotating pairs, >= 1 GiB in total",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic("transpose8192_fp16"),
+        },
+    }
+
+    # ---- the other large remapping copies, timed the same way
+    if not args.no_others:
+        others = {}
+        for name in ("retile", "interleave", "nhwc2nchw", "padtiles"):
+            wo = W.full(name)
+            p = lr.copy_plan(wo.src_layout, wo.src_elems, wo.dst_layout, wo.dst_elems, wo.elem_bytes)
+            prs = _pairs(torch, dev, wo.src_elems * wo.elem_bytes, wo.dst_elems * wo.elem_bytes)
+            steps = max(10, args.steps)
+            _, km = _time_copies(lr, torch, prs, wo.src_layout, wo.dst_layout, wo.elem_bytes, steps, args.warmup)
+            gb = W.bytes_moved(wo) / (km * 1e-3) / 1e9
+            others[wo.name] = {"path": p["path"], "us": round(km * 1e3, 2), "GBps": round(gb, 1),
+                               "hbm_frac": round(gb / HBM_PEAK_GBPS, 4)}
+            del prs
+            torch.cuda.empty_cache()
+        out["workloads"] = others
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -919,6 +919,7 @@ int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_el
   const uintptr_t s1 = s0 + (uintptr_t)src_capacity_elems * elem_bytes;
   const uintptr_t d1 = d0 + (uintptr_t)dst_capacity_elems * elem_bytes;
   if (s0 < d1 && d0 < s1) return LR_ERR_OVERLAP;
+  if ((rc = verify_plan(p, src_capacity_elems, dst_capacity_elems))) return rc;
   return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
 }
 

@@ -52,6 +52,7 @@ struct Swz {
 struct Plan {
   int path;           // lr_path
   int eb;             // bytes per (fused) element
+  int orig_eb;        // the caller's elem_bytes
   int v;              // elements per unit (generic/vector) or per chunk (transpose/interleave)
   bool wide;
   int rank;           // joint modes (after fusion)
@@ -73,6 +74,9 @@ struct Plan {
 // Plans a copy; fills `p`.  Returns 0 or an lr_status.
 int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld,
               int64_t dst_cap, size_t dst_align, size_t elem_bytes, uint32_t flags, Plan* p);
+
+// Re-checks the invariants the chosen kernel relies on; LR_ERR_PATH if violated.
+int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap);
 
 void set_hip_error(const char* text);
 

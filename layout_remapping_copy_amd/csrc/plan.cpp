@@ -158,6 +158,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   if (!mul_ok(src_cap, (int64_t)elem_bytes, &t) || !mul_ok(dst_cap, (int64_t)elem_bytes, &t)) return LR_ERR_OVERFLOW;
   p->n = n;
   p->eb = (int)elem_bytes;
+  p->orig_eb = (int)elem_bytes;
   p->sw_s = {Ls->swz_b, Ls->swz_m, Ls->swz_s};
   p->sw_d = {Ld->swz_b, Ld->swz_m, Ld->swz_s};
   if (src_align == 0) src_align = 1;
@@ -184,6 +185,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   // --- joint flat form
   int rank = 0;
   const bool have_joint = joint_flat(Ls, Ld, p->m, &rank, true);
+  if (have_joint && rank == 0) {  // a single element: one trivial mode
+    p->m[0] = {1, 1, 1};
+    rank = 1;
+  }
   p->rank = have_joint ? rank : 0;
   if (!have_joint || forced == LR_PATH_DUAL || (have_joint && rank > kMaxKernelModes)) {
     if (forced >= 0 && forced != LR_PATH_DUAL) return LR_ERR_PATH;
@@ -360,6 +365,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   }
 
   // generic: one unit per lane over the (fused) joint modes
+  if (forced >= 0 && forced != LR_PATH_GENERIC) return LR_ERR_PATH;
   p->path = LR_PATH_GENERIC;
   p->a = p->b = -1;
   int64_t v = unit_width(*p, src_align, dst_align);
@@ -369,6 +375,85 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   p->n_units = ne / v;
   p->grid = (p->n_units + 1023) / 1024;
   return LR_OK;
+}
+
+// Re-checks, independently of the choices above, the invariants each kernel's
+// indexing relies on; a violation means a planner bug and nothing is launched.
+int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
+  auto bad = [] { return LR_ERR_PATH; };
+  if (p.path == LR_PATH_DUAL || p.path == LR_PATH_ALIAS) return LR_OK;  // evaluate the validated layouts
+  if (p.rank < 1 || p.rank > kMaxKernelModes) return bad();
+  int64_t ms = 0, md = 0, prod = 1;
+  for (int k = 0; k < p.rank; ++k) {
+    if (p.m[k].ext < 1 || p.m[k].ss < 0 || p.m[k].sd < 0) return bad();
+    ms += (p.m[k].ext - 1) * p.m[k].ss;
+    md += (p.m[k].ext - 1) * p.m[k].sd;
+    prod *= p.m[k].ext;
+  }
+  // bytes touched on each side (strides are in fused elements of p.eb bytes;
+  // capacities in elements of the caller's elem_bytes)
+  auto bound = [](int64_t m, const Swz& z) {
+    return z.b ? (m | ((int64_t(1) << (z.m + z.b)) - 1)) + 1 : m + 1;
+  };
+  if (bound(ms, p.sw_s) * p.eb > src_cap * p.orig_eb) return bad();
+  if (bound(md, p.sw_d) * p.eb > dst_cap * p.orig_eb) return bad();
+  const int64_t v = p.v;
+  if (v < 1 || v * p.eb > 16) return bad();
+  switch (p.path) {
+    case LR_PATH_GENERIC:
+    case LR_PATH_VECTOR:
+      if (v > 1) {
+        if (p.m[0].ss != 1 || p.m[0].sd != 1 || p.m[0].ext % v) return bad();
+        for (int k = 1; k < p.rank; ++k)
+          if (p.m[k].ss % v || p.m[k].sd % v) return bad();
+      }
+      if (p.n_units * v != prod) return bad();
+      return LR_OK;
+    case LR_PATH_TRANSPOSE:
+    case LR_PATH_TRANSPOSE_DIRECT: {
+      if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
+      if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1) return bad();
+      if (p.m[p.a].ext % v || p.m[p.b].ext % v) return bad();
+      if (p.tile_a != 16 * v || p.tile_b != 16 * v) return bad();
+      for (int k = 0; k < p.rank; ++k) {
+        if (k != p.a && p.m[k].ss % v) return bad();
+        if (k != p.b && p.m[k].sd % v) return bad();
+      }
+      return LR_OK;
+    }
+    case LR_PATH_INTERLEAVE: {
+      if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
+      const int64_t nb = p.m[p.b].ext;
+      if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.a].sd != nb || p.tile_b != nb) return bad();
+      if (v * p.eb != 16 || p.m[p.a].ext % v || nb * p.eb > 16) return bad();
+      for (int k = 0; k < p.rank; ++k) {
+        if (k != p.a && p.m[k].ss % v) return bad();
+        if (k != p.a && k != p.b && p.m[k].sd % v) return bad();
+      }
+      return LR_OK;
+    }
+    case LR_PATH_STAGED: {
+      const int in = p.staged_inner;
+      if (in < 1 || in >= p.rank || v * p.eb != 16) return bad();
+      int64_t P = 1, F = 1;
+      for (int k = 0; k < in; ++k) {
+        if (p.m[k].sd != P) return bad();
+        P *= p.m[k].ext;
+        F += (p.m[k].ext - 1) * p.m[k].ss;
+      }
+      if (P != p.staged_P || F != p.staged_F || p.m[in].sd != P) return bad();
+      if (p.staged_Fc * 16 < F * p.eb || p.staged_cpt * 16 != P * p.eb || 256 % p.staged_cpt) return bad();
+      if (p.staged_K < 1 || p.staged_K * p.staged_Fc * 16 > 65536) return bad();
+      int64_t maxbase = 0;
+      for (int k = in; k < p.rank; ++k) {
+        if ((p.m[k].ss * p.eb) % 16 || (p.m[k].sd * p.eb) % 16) return bad();
+        maxbase += (p.m[k].ext - 1) * p.m[k].ss;
+      }
+      if ((maxbase * p.eb + p.staged_Fc * 16) > src_cap * p.orig_eb) return bad();
+      return LR_OK;
+    }
+  }
+  return bad();
 }
 
 }  // namespace lr
@@ -383,6 +468,7 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   Plan p;
   int rc = plan_copy(Ls, src_capacity_elems, src_align, Ld, dst_capacity_elems, dst_align, elem_bytes, flags, &p);
   if (rc) return rc;
+  if ((rc = verify_plan(p, src_capacity_elems, dst_capacity_elems))) return rc;
   std::memset(out, 0, sizeof(*out));
   out->path = p.path;
   out->elem_bytes = p.eb;

@@ -1,0 +1,52 @@
+"""Closed forms of the six workload copies as NumPy reshapes, transposes and
+takes.  TEST INFRASTRUCTURE ONLY.
+
+Each function returns the expected destination bytes for a workload's source
+bytes; they are the same results as ``oracle.copy`` (tests/test_oracle.py pins
+each form against it at small sizes) but run in seconds at full size, so the GPU
+tests can compare whole destination buffers, not only samples.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def transpose(src: np.ndarray, n: int) -> np.ndarray:
+    """(n,n):(n,1) -> (n,n):(1,n): dst[j*n + i] = src[i*n + j]."""
+    return np.ascontiguousarray(src.view(np.uint16).reshape(n, n).T).reshape(-1).view(np.uint8)
+
+
+def retile(src: np.ndarray, n: int, tr: int = 128, tc: int = 64) -> np.ndarray:
+    """Row-major n x n -> tr x tc tiles in row-major tile order, row-major inside a
+    tile, then the 8-element (16-byte) chunk c of tile row r moves to c ^ (r % 8)
+    (Swizzle<3,3,3> on bf16 offsets, [print_layout page, section 4.3])."""
+    s = src.view(np.uint16).reshape(n // tr, tr, n // tc, tc).transpose(0, 2, 1, 3)
+    tiles = s.reshape(-1, tr, tc // 8, 8)
+    rows = np.arange(tr)[:, None]
+    chunks = np.arange(tc // 8)[None, :]
+    out = np.empty_like(tiles)
+    out[:, rows, chunks ^ (rows % 8)] = tiles[:, rows, chunks]
+    return out.reshape(-1).view(np.uint8)
+
+
+def interleave(src: np.ndarray, b: int, h: int, s: int, d: int) -> np.ndarray:
+    """(b,h,s,d) contiguous -> head pairs adjacent at stride 1 ([print_layout page,
+    section 4.2]): dst[b][hp][s][d][hl] = src[b][2*hp + hl][s][d]."""
+    x = src.view(np.uint16).reshape(b, h // 2, 2, s, d).transpose(0, 1, 3, 4, 2)
+    return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
+
+
+def nhwc2nchw(src: np.ndarray, n: int, h: int, w: int, c: int) -> np.ndarray:
+    x = src.view(np.uint16).reshape(n, h, w, c).transpose(0, 3, 1, 2)
+    return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
+
+
+def padtiles(src: np.ndarray, tiles: int) -> np.ndarray:
+    """Per tile of 72 words: element k of the destination tile is word
+    18*(k%4) + (k/4)%8 + 9*(k/32) of the source tile, i.e. the padded (8,8):(1,9)
+    tile read through ((4,8),2):((16,1),8) ([CuTe algebra page, section 2.2])."""
+    k = np.arange(64)
+    table = 18 * (k % 4) + (k // 4) % 8 + 9 * (k // 32)
+    s = src.view(np.uint32).reshape(tiles, 72)
+    return np.ascontiguousarray(np.take(s, table, axis=1)).reshape(-1).view(np.uint8)

@@ -139,9 +139,30 @@ static int run_fuzz() {
     int64_t v;
     lr_max_common_vector(&a, &b, 4, &v);
     lr_plan p;
+    // a compact destination over a's extents in a random order: a bijective copy
+    lr_layout c = a;
+    c.swz_b = 0;
+    {
+      int perm[LR_MAX_LEAVES];
+      for (int i = 0; i < a.nleaves; ++i) perm[i] = i;
+      for (int i = a.nleaves - 1; i > 0; --i) std::swap(perm[i], perm[rng() % (i + 1)]);
+      int64_t w = 1;
+      for (int i = 0; i < a.nleaves; ++i) {
+        c.stride[perm[i]] = w;
+        w *= a.shape[perm[i]];
+      }
+    }
     for (uint32_t fl : {0u, 1u, 2u}) {
-      lr_copy_plan(&a, 1 << 20, 16, &b, 1 << 20, 16, 2, fl, &p);
-      lr_copy_plan(&a, 1 << 20, 4, &a, 1 << 20, 8, 4, fl, &p);
+      for (int eb : {1, 2, 4, 8, 16}) {
+        // the planner's own choice must always pass its invariant check
+        if (lr_copy_plan(&a, 1 << 20, 16, &b, 1 << 20, 16, eb, fl, &p) == LR_ERR_PATH ||
+            lr_copy_plan(&a, 1 << 20, 4, &a, 1 << 20, 8, eb, fl, &p) == LR_ERR_PATH ||
+            lr_copy_plan(&a, 1 << 20, 16, &c, 1 << 20, 16, eb, fl, &p) == LR_ERR_PATH ||
+            lr_copy_plan(&c, 1 << 20, 16, &a, 1 << 20, 16, eb, fl, &p) == LR_ERR_PATH) {
+          std::printf("planner chose a path its check rejects: %s -> %s eb=%d\n", ta.c_str(), tb.c_str(), eb);
+          return 1;
+        }
+      }
     }
     for (int path = 0; path < 8; ++path) lr_copy_plan(&a, 1 << 20, 16, &a, 1 << 20, 16, 1, LR_COPY_FORCE_PATH(path), &p);
     ++n_ok;

@@ -1,0 +1,378 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, byte for byte.
+
+Every destination buffer starts filled with 0xA5 and is compared whole, so
+positions a layout does not reach are checked to stay untouched.  Full-size
+workloads run in the same launch configuration as bench.py and are compared
+whole against NumPy closed forms (each pinned to the oracle's copy) and at
+sampled indices against the oracle's own evaluation.
+"""
+
+import os
+import random
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import forms as F
+import workloads as W
+
+torch = pytest.importorskip("torch")
+import layout_remapping_copy_amd as lr  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert os.path.exists(lr.LIB_PATH), "liblayout_remap.so is not built"
+    lr.lib()
+    return torch.device("cuda:0")
+
+
+def gpu_copy(dev, src, Ls, dst, Ld, eb, flags=0, src_off=0, dst_off=0):
+    s = torch.zeros(src.nbytes + src_off, dtype=torch.uint8, device=dev)
+    d = torch.zeros(dst.nbytes + dst_off, dtype=torch.uint8, device=dev)
+    s[src_off:] = torch.from_numpy(src).to(dev)
+    d[dst_off:] = torch.from_numpy(dst).to(dev)
+    lr.layout_copy(s[src_off:], Ls, d[dst_off:], Ld, elem_bytes=eb, flags=flags)
+    torch.cuda.synchronize()
+    return d[dst_off:].cpu().numpy()
+
+
+def gpu_eval(dev, L, n=None, idx=None):
+    t = lr.layout_eval(L, idx=idx, n=n, device=dev)
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Evaluation
+# ---------------------------------------------------------------------------
+EVAL_LAYOUTS = ["((4,8),2):((16,1),8)", "Sw<3,0,3> o (8,8):(8,1)", "((4,2),(2,4)):((2,16),(1,8))", "(4,2):(2,1)",
+                "(4,2):(1,4)", "(4,2,2):(8,2,1)", "Sw<3,3,3> o ((128,32),(64,64)):((64,524288),(1,8192))",
+                "(8,4,2):(1,16,512)", "(8,2):(1,16)", "((4,8),2,1000):((18,1),9,72)"]
+
+
+@pytest.mark.parametrize("text", EVAL_LAYOUTS)
+def test_eval_layouts(dev, text):
+    say("eval", text)
+    L = O.parse(text)
+    got = gpu_eval(dev, text)
+    want = O.eval_indices(L, np.arange(O.size(L)))
+    assert np.array_equal(got, want)
+
+
+def test_eval_thread_maps(dev):
+    for p, s, k, t in [(8, 4, 16, 64), (8, 2, 16, 32), (4, 3, 17, 96)]:
+        say("eval thread map", p, s, k, t)
+        L = lr.thread_map(p, s, k, t)
+        got = gpu_eval(dev, L, n=t)
+        assert got.tolist() == [O.stripmined_offset(i, p, s, k) for i in range(t)]
+        B = lr.thread_map(p, 0, k, t)
+        got = gpu_eval(dev, B, n=t)
+        assert got.tolist() == [O.pitch_linear_offset(i, p, k) for i in range(t)]
+
+
+def test_eval_indices_and_out_of_range(dev):
+    say("eval idx")
+    text = "((4,8),2):((16,1),8)"
+    idx = torch.tensor([5, 0, 63, -1, 64, 17, 1 << 40], dtype=torch.int64, device=dev)
+    got = gpu_eval(dev, text, idx=idx)
+    L = O.parse(text)
+    assert got.tolist() == [O.eval_index(L, 5), 0, 63, -1, -1, O.eval_index(L, 17), -1]
+
+
+def test_eval_coords(dev):
+    say("eval coords")
+    text = "((4,2),(2,4)):((2,16),(1,8))"
+    L = O.parse(text)
+    rc = [(r, c) for r in range(8) for c in range(8)] + [(8, 0), (0, -1)]
+    t = torch.tensor(rc, dtype=torch.int64, device=dev)
+    got = lr.layout_eval_coords(text, t).cpu().tolist()
+    assert got[:64] == [O.eval_coord(L, x) for x in rc[:64]] and got[64:] == [-1, -1]
+    nat = [(i0, i1, j0, j1) for i0 in range(4) for i1 in range(2) for j0 in range(2) for j1 in range(4)]
+    t = torch.tensor(nat + [(4, 0, 0, 0)], dtype=torch.int64, device=dev)
+    got = lr.layout_eval_coords(text, t).cpu().tolist()
+    assert got[:-1] == [O.eval_coord(L, ((a, b), (c, d))) for a, b, c, d in nat] and got[-1] == -1
+    # golden: blocked natural coordinates and the swizzle
+    assert got[nat.index((0, 1, 0, 0))] == 16 and got[nat.index((1, 0, 0, 0))] == 2
+    sw = torch.tensor([(2, 0), (2, 1)], dtype=torch.int64, device=dev)
+    assert lr.layout_eval_coords("Sw<3,0,3> o (8,8):(8,1)", sw).cpu().tolist() == [18, 19]
+
+
+def _rand_text(rng, swz=True, max_leaves=5):
+    nl = rng.randint(1, max_leaves)
+    ext = [rng.randint(1, 7) for _ in range(nl)]
+    st = [rng.randint(0, 50) for _ in range(nl)]
+    t = "(" + ",".join(map(str, ext)) + "):(" + ",".join(map(str, st)) + ")"
+    if swz and rng.random() < 0.3:
+        b = rng.randint(1, 3)
+        t = f"Sw<{b},{rng.randint(0, 3)},{rng.randint(b, 4)}> o " + t
+    return t
+
+
+def test_eval_random(dev):
+    rng = random.Random(31)
+    for i in range(200):
+        t = _rand_text(rng)
+        if i % 50 == 0:
+            say("eval random", i, t)
+        L = O.parse(t)
+        assert np.array_equal(gpu_eval(dev, t), O.eval_indices(L, np.arange(O.size(L)))), t
+
+
+def test_eval_wide(dev):
+    say("eval wide")
+    text = "(65536,65536):(65536,1)"  # 2^32 indices: 64-bit division path
+    L = O.parse(text)
+    ks = np.random.default_rng(5).integers(0, 1 << 32, 100000, dtype=np.int64)
+    got = gpu_eval(dev, text, idx=torch.from_numpy(ks).to(dev))
+    assert np.array_equal(got, O.eval_indices(L, ks))
+
+
+# ---------------------------------------------------------------------------
+# Copies at sizes the oracle finishes quickly
+# ---------------------------------------------------------------------------
+def _oracle_copy(w):
+    src, dst = W.make_src(w), W.make_dst(w)
+    want = O.copy(src, O.parse(w.src_layout), dst, O.parse(w.dst_layout), w.elem_bytes,
+                  ordered_alias=w.ordered_alias)
+    return src, dst, want
+
+
+@pytest.mark.parametrize("name", list(W.FULL))
+def test_copy_small_workloads(dev, name):
+    w = W.small(name)
+    say("copy small", w.name, w.src_layout, "->", w.dst_layout)
+    src, dst, want = _oracle_copy(w)
+    flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
+    got = gpu_copy(dev, src, w.src_layout, dst, w.dst_layout, w.elem_bytes, flags)
+    assert np.array_equal(got, want)
+
+
+def test_copy_tile8x8_aliased(dev):
+    w = W.tile8x8()
+    src, dst, want = _oracle_copy(w)
+    say("copy tile8x8 default flags")
+    with pytest.raises(lr.LayoutRemapError) as e:
+        gpu_copy(dev, src, w.src_layout, dst, w.dst_layout, 4, 0)
+    assert e.value.code == lr.binding.ERR_ALIAS
+    got = gpu_copy(dev, src, w.src_layout, dst, w.dst_layout, 4, lr.COPY_ORDERED_ALIAS)
+    idx = [0, 8, 1, 9, 2, 10, 3, 11, 16, 24, 17, 25, 18, 26, 19, 27, 32, 40, 33, 41, 34, 42, 35, 43,
+           48, 56, 49, 57, 50, 58, 51, 59, 36, 44, 37, 45, 38, 46, 39, 47, 52, 60, 53, 61, 54, 62, 55, 63]
+    assert got.view(np.uint32)[:48].tolist() == src.view(np.uint32)[idx].tolist()
+    assert np.all(got[48 * 4:] == 0xA5)
+    assert np.array_equal(got, want)
+
+
+ALL_PATHS = [lr.PATH_GENERIC, lr.PATH_VECTOR, lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT, lr.PATH_INTERLEAVE,
+             lr.PATH_STAGED, lr.PATH_DUAL, lr.PATH_ALIAS]
+
+
+def _case_pairs():
+    """Layout pairs (src, dst, src_elems, dst_elems, eb) that admit the various paths."""
+    cases = []
+    for name in ["transpose", "retile", "interleave", "nhwc2nchw", "padtiles"]:
+        w = W.small(name)
+        cases.append((w.src_layout, w.dst_layout, w.src_elems, w.dst_elems, w.elem_bytes))
+    # transposes at every element size, ragged tile edges
+    for eb, (r, c) in [(1, (272, 48)), (2, (136, 24)), (4, (40, 36)), (8, (34, 6)), (16, (17, 5)), (2, (7, 9))]:
+        cases.append((f"({r},{c}):({c},1)", f"({r},{c}):(1,{r})", r * c, r * c, eb))
+    # interleave of a short dst-contiguous mode at every element size
+    for eb, nb in [(1, 2), (1, 4), (1, 8), (1, 16), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (8, 2)]:
+        a, bt = 16 // eb * 6, 3
+        cases.append((f"({nb},{a},{bt}):({a},1,{a * nb})", f"({nb},{a},{bt}):(1,{nb},{a * nb})", a * nb * bt,
+                      a * nb * bt, eb))
+    # padded tiles at two element sizes, swizzled and vector copies
+    for eb in (2, 4):
+        t = 37
+        cases.append((f"((4,8),2,{t}):((18,1),9,72)", f"((4,8),2,{t}):((1,4),32,64)", 72 * t, 64 * t, eb))
+    cases.append(("(64,64):(64,1)", "Sw<3,3,3> o (64,64):(64,1)", 4096, 4096, 2))
+    cases.append(("Sw<2,2,3> o (32,32):(32,1)", "(32,32):(1,32)", 1024, 1024, 4))
+    cases.append(("(96,5,3):(1,96,480)", "(96,5,3):(1,288,96)", 1440, 1440, 2))
+    # non-refinable pair (dual) and a broadcast source
+    cases.append(("(6,4):(1,6)", "(4,6):(1,4)", 24, 24, 4))
+    cases.append(("(8,16):(0,1)", "(8,16):(16,1)", 16, 128, 8))
+    return cases
+
+
+@pytest.mark.parametrize("ci", range(len(_case_pairs())))
+def test_copy_every_path(dev, ci):
+    ts, td, ns, nd, eb = _case_pairs()[ci]
+    rng = np.random.default_rng(ci)
+    src = rng.integers(0, 256, ns * eb, dtype=np.uint8)
+    dst = np.full(nd * eb, 0xA5, np.uint8)
+    want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+    ran = []
+    for path in ALL_PATHS:
+        flags = lr.COPY_FORCE_PATH(path)
+        try:
+            lr.copy_plan(ts, ns, td, nd, eb, flags)
+        except lr.LayoutRemapError as e:
+            assert e.code == lr.binding.ERR_PATH
+            continue
+        say("copy path", lr.binding.PATH_NAMES[path], ts, "->", td, "eb", eb)
+        got = gpu_copy(dev, src, ts, dst, td, eb, flags)
+        assert np.array_equal(got, want), lr.binding.PATH_NAMES[path]
+        ran.append(path)
+    # also the default plan and the 64-bit index variant
+    got = gpu_copy(dev, src, ts, dst, td, eb, 0)
+    assert np.array_equal(got, want)
+    try:
+        got = gpu_copy(dev, src, ts, dst, td, eb, lr.COPY_WIDE_INDEX)
+        assert np.array_equal(got, want)
+    except lr.LayoutRemapError as e:
+        assert e.code == lr.binding.ERR_PATH
+    assert len(ran) >= 2
+
+
+def _rand_pair(rng):
+    nd = rng.randint(1, 4)
+    exts = [rng.choice([1, 2, 3, 4, 5, 7, 8, 16, 24, 32, 40, 64, 72, 100, 128]) for _ in range(nd)]
+    while np.prod(exts) > (1 << 17):
+        exts[rng.randrange(nd)] = rng.choice([2, 3, 4, 8])
+
+    def compact(order, pad):
+        st, w = [0] * nd, 1
+        for i in order:
+            st[i] = w
+            w *= exts[i] + (pad if i == order[0] else 0)
+        return st, w
+
+    o1, o2 = list(range(nd)), list(range(nd))
+    rng.shuffle(o1)
+    rng.shuffle(o2)
+    ss, ns = compact(o1, rng.choice([0, 0, 1, 3]))
+    sd, nd_ = compact(o2, 0)
+    ts = "(" + ",".join(map(str, exts)) + "):(" + ",".join(map(str, ss)) + ")"
+    td = "(" + ",".join(map(str, exts)) + "):(" + ",".join(map(str, sd)) + ")"
+    if rng.random() < 0.2 and nd_ >= 64:
+        td = "Sw<2,3,3> o " + td
+        nd_ = lr.parse(td).cosize  # the library's swizzle-aware bound
+    return ts, td, max(ns, O.cosize(O.parse(ts))), nd_
+
+
+def test_copy_random_pairs(dev):
+    rng = random.Random(41)
+    for i in range(150):
+        ts, td, ns, nd = _rand_pair(rng)
+        eb = rng.choice([1, 2, 4, 8, 16])
+        src = np.random.default_rng(i).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        p = lr.copy_plan(ts, ns, td, nd, eb)
+        if i % 25 == 0:
+            say("copy random", i, ts, "->", td, "eb", eb, p["path"])
+        got = gpu_copy(dev, src, ts, dst, td, eb)
+        assert np.array_equal(got, want), (ts, td, eb, p["path"])
+
+
+def test_copy_misaligned_pointers(dev):
+    w = W.small("retile")
+    src, dst, want = _oracle_copy(w)
+    for so, do in [(2, 0), (0, 4), (8, 8), (6, 2)]:
+        say("copy misaligned", so, do)
+        got = gpu_copy(dev, src, w.src_layout, dst, w.dst_layout, 2, 0, src_off=so, dst_off=do)
+        assert np.array_equal(got, want)
+
+
+def test_copy_size_one_and_rank16(dev):
+    say("copy size one")
+    src = np.arange(16, dtype=np.uint8)
+    got = gpu_copy(dev, src, "1:0", np.full(4, 0xA5, np.uint8), "(1,1):(0,0)", 4)
+    assert got.tolist() == [0, 1, 2, 3]
+    say("copy rank 16")
+    ts = "(" + ",".join(["2"] * 16) + "):(" + ",".join(str(1 << i) for i in range(16)) + ")"
+    td = "(" + ",".join(["2"] * 16) + "):(" + ",".join(str(1 << (15 - i)) for i in range(16)) + ")"
+    src = np.random.default_rng(3).integers(0, 256, (1 << 16) * 2, dtype=np.uint8)
+    dst = np.full((1 << 16) * 2, 0xA5, np.uint8)
+    want = O.copy(src, O.parse(ts), dst, O.parse(td), 2)
+    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, 2), want)
+
+
+def test_copy_errors(dev):
+    say("copy errors")
+    t = torch.zeros(256, dtype=torch.uint8, device=dev)
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.layout_copy(t[:128], "32:1", t[64:], "32:1", elem_bytes=4)
+    assert e.value.code == lr.binding.ERR_OVERLAP
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.layout_copy(t[:128], "33:1", t[128:], "33:1", elem_bytes=4)
+    assert e.value.code == lr.binding.ERR_BOUNDS
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.layout_copy(t[:128], "(4,8):(1,4)", t[128:], "(4,8):(1,0)", elem_bytes=4)
+    assert e.value.code == lr.binding.ERR_ALIAS
+
+
+def test_copy_ordered_alias_larger(dev):
+    # several 8192-offset windows, many writers per offset
+    say("copy ordered alias")
+    ts, td = "(300,50):(1,300)", "(300,50):(7,100)"
+    Ls, Ld = O.parse(ts), O.parse(td)
+    src = np.random.default_rng(8).integers(0, 256, 15000 * 4, dtype=np.uint8)
+    dst = np.full(O.cosize(Ld) * 4, 0xA5, np.uint8)
+    want = O.copy(src, Ls, dst, Ld, 4, ordered_alias=True)
+    got = gpu_copy(dev, src, ts, dst, td, 4, lr.COPY_ORDERED_ALIAS)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# Full sizes, in the launch configuration bench.py times
+# ---------------------------------------------------------------------------
+FORMS = {
+    "transpose": lambda s: F.transpose(s, 8192),
+    "retile": lambda s: F.retile(s, 4096),
+    "interleave": lambda s: F.interleave(s, 16, 32, 4096, 128),
+    "nhwc2nchw": lambda s: F.nhwc2nchw(s, 128, 56, 56, 256),
+    "padtiles": lambda s: F.padtiles(s, 1 << 20),
+}
+
+FULL_PATH = {"transpose": "transpose", "retile": "vector", "interleave": "interleave", "nhwc2nchw": "transpose",
+             "padtiles": "staged"}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(FORMS))
+def test_full_size(dev, name):
+    w = W.full(name)
+    say("full", w.name, "generate")
+    src = W.make_src(w)
+    Ls, Ld = O.parse(w.src_layout), O.parse(w.dst_layout)
+    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
+    assert p["path"] == FULL_PATH[name]
+    s = torch.from_numpy(src).to(dev)
+    d = torch.full((w.dst_elems * w.elem_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+    say("full", w.name, "copy", p["path"])
+    lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=w.elem_bytes)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    del s, d
+    # sampled indices against the oracle's own evaluation
+    ks = np.random.default_rng(7).integers(0, w.n_elems, 1 << 20, dtype=np.int64)
+    assert O.copy_sampled_check(src, Ls, got, Ld, w.elem_bytes, ks) == 0
+    # the whole buffer against the NumPy closed form
+    say("full", w.name, "compare")
+    assert np.array_equal(got, FORMS[name](src))
+
+
+@pytest.mark.slow
+def test_full_transpose_both_variants(dev):
+    w = W.full("transpose")
+    src = W.make_src(w)
+    want = F.transpose(src, 8192)
+    s = torch.from_numpy(src).to(dev)
+    for path in (lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT):
+        say("full transpose", lr.binding.PATH_NAMES[path])
+        d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
+        lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=2, flags=lr.COPY_FORCE_PATH(path))
+        torch.cuda.synchronize()
+        assert np.array_equal(d.cpu().numpy(), want)

@@ -234,7 +234,7 @@ def test_plan_joint_matches_oracle_random():
             continue
         p = lr.copy_plan(ts, O.cosize(Ls), O.fmt(Ld), O.cosize(Ld), 4, lr.COPY_FORCE_PATH(lr.PATH_GENERIC))
         n += 1
-        assert p["joint"] == [tuple(m) for m in jm], (ts, O.fmt(Ld))
+        assert [m for m in p["joint"] if m[0] > 1] == [tuple(m) for m in jm], (ts, O.fmt(Ld))
     assert n > 300
 
 

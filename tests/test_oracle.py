@@ -592,3 +592,23 @@ def test_planted_dropped_alignment_in_vector_width_is_caught():
     assert np.all(so == so[:, :1] + np.arange(4))          # contiguous runs ...
     assert not np.all(so[:, 0] % 4 == 0)                   # ... not aligned
     assert O.max_common_vector(Ls, Ld, 4) == 1
+
+
+# ---------------------------------------------------------------------------
+# NumPy closed forms used for whole-buffer checks at full size: each equals the
+# oracle's copy at a reduced size with the same structure
+# ---------------------------------------------------------------------------
+def test_forms_equal_oracle_copy():
+    from oracle import forms as F
+
+    cases = {
+        "transpose": lambda s: F.transpose(s, 520),
+        "retile": lambda s: F.retile(s, 512),
+        "interleave": lambda s: F.interleave(s, 2, 4, 72, 128),
+        "nhwc2nchw": lambda s: F.nhwc2nchw(s, 3, 7, 9, 40),
+        "padtiles": lambda s: F.padtiles(s, 1000),
+    }
+    for name, form in cases.items():
+        w = W.small(name)
+        src, out = _run(w)
+        assert np.array_equal(form(src), out), name

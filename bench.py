@@ -122,6 +122,32 @@ def _cpu_baseline(w, seconds: float):
     }
 
 
+def counters_run(lr, torch, W, reps: int = 3):
+    """Launch sequence for rocprofv3 runs (kernel trace or --pmc): each large
+    workload `reps` times after one warm-up, then a plain contiguous copy of
+    256 MiB (the reference of known size that scales FETCH_SIZE / WRITE_SIZE)."""
+    dev = torch.device("cuda:0")
+    names = ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles")
+    for name in names:
+        w = W.full(name)
+        s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)
+        d = torch.empty(w.dst_elems * w.elem_bytes, dtype=torch.uint8, device=dev)
+        for _ in range(reps + 1):
+            lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=w.elem_bytes)
+        torch.cuda.synchronize()
+        print(f"counters: {name} grid={lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)['grid']}",
+              flush=True)
+        del s, d
+    n = 256 << 20
+    s = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    d = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(reps + 1):
+        lr.layout_copy(s, f"{n // 16}:1", d, f"{n // 16}:1", elem_bytes=16)
+    torch.cuda.synchronize()
+    print(f"counters: plain copy {n} bytes grid={lr.copy_plan(f'{n // 16}:1', n // 16, f'{n // 16}:1', n // 16, 16)['grid']}",
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +157,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--path", default=None, help="force a copy path (for experiments)")
+    ap.add_argument("--counters", action="store_true",
+                    help="only launch each large workload a few times (for rocprofv3 runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -148,6 +176,9 @@ def main():
         sys.exit(1)
     lr.lib()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.counters:
+        counters_run(lr, torch, W)
+        return
 
     flags = 0
     if args.path:

@@ -21,6 +21,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "lr_internal.h"
 
@@ -75,6 +76,33 @@ template <typename T, int V>
 struct alignas(V * sizeof(T) >= 16 ? 16 : V * sizeof(T)) Chunk {
   T e[V];
 };
+
+
+// Global loads/stores of a raw element or chunk.  cache bit 0: non-temporal
+// stores, bit 1: non-temporal loads (streaming data that will not be re-read).
+template <int S> struct NativeOf;
+template <> struct NativeOf<1> { using T = uint8_t; };
+template <> struct NativeOf<2> { using T = uint16_t; };
+template <> struct NativeOf<4> { using T = uint32_t; };
+template <> struct NativeOf<8> { using T = unsigned int __attribute__((ext_vector_type(2))); };
+template <> struct NativeOf<16> { using T = unsigned int __attribute__((ext_vector_type(4))); };
+
+template <typename C>
+__device__ __forceinline__ C gload(const void* p, uint32_t cache) {
+  using N = typename NativeOf<sizeof(C)>::T;
+  N x = (cache & 2u) ? __builtin_nontemporal_load((const N*)p) : *(const N*)p;
+  return __builtin_bit_cast(C, x);
+}
+
+template <typename C>
+__device__ __forceinline__ void gstore(void* p, const C& v, uint32_t cache) {
+  using N = typename NativeOf<sizeof(C)>::T;
+  N x = __builtin_bit_cast(N, v);
+  if (cache & 1u)
+    __builtin_nontemporal_store(x, (N*)p);
+  else
+    *(N*)p = x;
+}
 
 // ------------------------------------------------------------------ eval
 
@@ -174,6 +202,7 @@ struct GenericArgs {
   ModeArg64 w[kMaxKernelModes];
   SwzArg sws, swd;
   uint64_t sws_mask64, swd_mask64;
+  uint32_t cache;
   int64_t n_units;
   int64_t n_chunks;  // groups of 1024 units
 };
@@ -181,54 +210,77 @@ struct GenericArgs {
 // One unit (UB bytes) per lane and step; four independent units per lane so each
 // lane keeps four loads in flight before its stores.  Lanes of a wave take
 // consecutive units, i.e. consecutive positions of the fastest joint mode.
-template <int UB, bool WIDE>
+template <bool WIDE>
+__device__ __forceinline__ void generic_offsets(const GenericArgs& a, int64_t idx, uint64_t* so, uint64_t* dof) {
+  if (WIDE) {
+    uint64_t r = (uint64_t)idx, s = 0, d = 0;
+    for (int k = 0; k < a.rank; ++k) {
+      uint64_t e = (uint64_t)a.w[k].ext;
+      uint64_t q = r / e;
+      uint64_t g = r - q * e;
+      s += g * (uint64_t)a.w[k].ss;
+      d += g * (uint64_t)a.w[k].sd;
+      r = q;
+    }
+    *so = swz64(s, a.sws_mask64, a.sws.shift);
+    *dof = swz64(d, a.swd_mask64, a.swd.shift);
+  } else {
+    uint32_t r = (uint32_t)idx, s = 0, d = 0;
+    for (int k = 0; k < a.rank; ++k) {
+      uint32_t q = (k == a.rank - 1) ? 0u : fdiv(r, a.m[k].fd);
+      uint32_t g = r - q * a.m[k].ext;
+      s += g * a.m[k].ss;
+      d += g * a.m[k].sd;
+      r = q;
+    }
+    *so = swz32(s, a.sws);
+    *dof = swz32(d, a.swd);
+  }
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = 0..N-1, so per-lane
+// values live in named registers (a runtime-indexed local array of vectors would
+// be placed in LDS or scratch, serialising the loads behind it).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int UB, bool WIDE, int U>
 __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
+  static_assert(U == 1 || U == 4, "one or four units per lane");
   using T = typename Raw<UB>::T;
   const T* __restrict__ src = (const T*)a.src;
   T* __restrict__ dst = (T*)a.dst;
-  constexpr int U = 4;
   for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
-    T val[U];
-    uint64_t dof[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t idx = ch * (256 * U) + u * 256 + threadIdx.x;
-      ok[u] = idx < a.n_units;
-      dof[u] = 0;
-      if (ok[u]) {
-        uint64_t so = 0, d = 0;
-        if (WIDE) {
-          uint64_t r = (uint64_t)idx;
-          for (int k = 0; k < a.rank; ++k) {
-            uint64_t e = (uint64_t)a.w[k].ext;
-            uint64_t q = r / e;
-            uint64_t g = r - q * e;
-            so += g * (uint64_t)a.w[k].ss;
-            d += g * (uint64_t)a.w[k].sd;
-            r = q;
-          }
-          so = swz64(so, a.sws_mask64, a.sws.shift);
-          d = swz64(d, a.swd_mask64, a.swd.shift);
-        } else {
-          uint32_t r = (uint32_t)idx, s32 = 0, d32 = 0;
-          for (int k = 0; k < a.rank; ++k) {
-            uint32_t q = (k == a.rank - 1) ? 0u : fdiv(r, a.m[k].fd);
-            uint32_t g = r - q * a.m[k].ext;
-            s32 += g * a.m[k].ss;
-            d32 += g * a.m[k].sd;
-            r = q;
-          }
-          so = swz32(s32, a.sws);
-          d = swz32(d32, a.swd);
-        }
-        val[u] = src[so];
-        dof[u] = d;
+    const int64_t i0 = ch * (256 * U) + threadIdx.x;
+    if constexpr (U == 1) {
+      if (i0 < a.n_units) {
+        uint64_t s0, d0;
+        generic_offsets<WIDE>(a, i0, &s0, &d0);
+        gstore<T>(dst + d0, gload<T>(src + s0, a.cache), a.cache);
       }
+    } else {
+      uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+      const bool k0 = i0 < a.n_units, k1 = i0 + 256 < a.n_units, k2 = i0 + 512 < a.n_units,
+                 k3 = i0 + 768 < a.n_units;
+      if (k0) generic_offsets<WIDE>(a, i0, &s0, &d0);
+      if (k1) generic_offsets<WIDE>(a, i0 + 256, &s1, &d1);
+      if (k2) generic_offsets<WIDE>(a, i0 + 512, &s2, &d2);
+      if (k3) generic_offsets<WIDE>(a, i0 + 768, &s3, &d3);
+      T v0, v1, v2, v3;
+      if (k0) v0 = gload<T>(src + s0, a.cache);
+      if (k1) v1 = gload<T>(src + s1, a.cache);
+      if (k2) v2 = gload<T>(src + s2, a.cache);
+      if (k3) v3 = gload<T>(src + s3, a.cache);
+      if (k0) gstore<T>(dst + d0, v0, a.cache);
+      if (k1) gstore<T>(dst + d1, v1, a.cache);
+      if (k2) gstore<T>(dst + d2, v2, a.cache);
+      if (k3) gstore<T>(dst + d3, v3, a.cache);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (ok[u]) dst[dof[u]] = val[u];
   }
 }
 
@@ -270,6 +322,7 @@ struct DualArgs {
   const void* src;
   void* dst;
   SideArg s, d;
+  uint32_t cache;
   int64_t n;
   int64_t n_chunks;
 };
@@ -281,24 +334,18 @@ __global__ void __launch_bounds__(256) k_dual(DualArgs a) {
   using T = typename Raw<EB>::T;
   const T* __restrict__ src = (const T*)a.src;
   T* __restrict__ dst = (T*)a.dst;
-  constexpr int U = 4;
   for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
-    T val[U];
-    uint64_t dof[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t k = ch * (256 * U) + u * 256 + threadIdx.x;
-      ok[u] = k < a.n;
-      dof[u] = 0;
-      if (ok[u]) {
-        val[u] = src[side_eval<WIDE>(a.s, k)];
-        dof[u] = side_eval<WIDE>(a.d, k);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (ok[u]) dst[dof[u]] = val[u];
+    const int64_t i0 = ch * 1024 + threadIdx.x;
+    const bool k0 = i0 < a.n, k1 = i0 + 256 < a.n, k2 = i0 + 512 < a.n, k3 = i0 + 768 < a.n;
+    T v0, v1, v2, v3;
+    if (k0) v0 = gload<T>(src + side_eval<WIDE>(a.s, i0), a.cache);
+    if (k1) v1 = gload<T>(src + side_eval<WIDE>(a.s, i0 + 256), a.cache);
+    if (k2) v2 = gload<T>(src + side_eval<WIDE>(a.s, i0 + 512), a.cache);
+    if (k3) v3 = gload<T>(src + side_eval<WIDE>(a.s, i0 + 768), a.cache);
+    if (k0) gstore<T>(dst + side_eval<WIDE>(a.d, i0), v0, a.cache);
+    if (k1) gstore<T>(dst + side_eval<WIDE>(a.d, i0 + 256), v1, a.cache);
+    if (k2) gstore<T>(dst + side_eval<WIDE>(a.d, i0 + 512), v2, a.cache);
+    if (k3) gstore<T>(dst + side_eval<WIDE>(a.d, i0 + 768), v3, a.cache);
   }
 }
 
@@ -364,6 +411,8 @@ struct TransposeArgs {
   FD fd_ta, fd_tb;
   BatchArg batch;
   SwzArg sws, swd;
+  uint32_t cache;
+  uint32_t order;  // 0: tiles along a vary fastest across workgroups, 1: along b, 2: diagonal
 };
 
 // Tile of 16V x 16V elements per workgroup; each lane owns a V x V register block:
@@ -387,11 +436,29 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
-  uint32_t blk = blockIdx.x;
-  uint32_t r1 = fdiv(blk, t.fd_ta);
-  uint32_t ta = blk - r1 * t.tiles_a;
-  uint32_t r2 = fdiv(r1, t.fd_tb);
-  uint32_t tb = r1 - r2 * t.tiles_b;
+  uint32_t blk = blockIdx.x, ta, tb, r2;
+  if (t.order == 0) {
+    uint32_t r1 = fdiv(blk, t.fd_ta);
+    ta = blk - r1 * t.tiles_a;
+    r2 = fdiv(r1, t.fd_tb);
+    tb = r1 - r2 * t.tiles_b;
+  } else if (t.order == 1) {
+    uint32_t r1 = fdiv(blk, t.fd_tb);
+    tb = blk - r1 * t.tiles_b;
+    r2 = fdiv(r1, t.fd_ta);
+    ta = r1 - r2 * t.tiles_a;
+  } else {
+    // diagonal: consecutive workgroups take consecutive a-tiles and, with them,
+    // shifted b-tiles, so that neither the rows they read nor the rows they write
+    // share one column offset (power-of-two pitches otherwise land every row of a
+    // tile band on the same HBM channels)
+    uint32_t r1 = fdiv(blk, t.fd_ta);
+    ta = blk - r1 * t.tiles_a;
+    r2 = fdiv(r1, t.fd_tb);
+    uint32_t ta_mod = ta - fdiv(ta, t.fd_tb) * t.tiles_b;  // ta % tiles_b
+    uint32_t d = (r1 - r2 * t.tiles_b) + ta_mod;            // < 2 * tiles_b
+    tb = d >= t.tiles_b ? d - t.tiles_b : d;
+  }
   uint32_t bs, bd;
   batch_offsets(t.batch, r2, &bs, &bd);
 
@@ -414,7 +481,7 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint32_t so = swz32(a_blk + (b_blk + j) * t.ss_b + bs, t.sws);
-      in[j] = *(const C*)(src + (size_t)so * EB);
+      in[j] = gload<C>(src + (size_t)so * EB, t.cache);
     }
   }
   C out[V];
@@ -428,7 +495,7 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         uint32_t dof = swz32((a_blk + i) * t.sd_a + b_blk + bd, t.swd);
-        *(C*)(dst + (size_t)dof * EB) = out[i];
+        gstore<C>(dst + (size_t)dof * EB, out[i], t.cache);
       }
     }
     return;
@@ -448,7 +515,7 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
     if (a < t.ext_a && b < t.ext_b) {
       C v = tile[row][c ^ ((row / V) & 15)];
       uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
-      *(C*)(dst + (size_t)dof * EB) = v;
+      gstore<C>(dst + (size_t)dof * EB, v, t.cache);
     }
   }
 }
@@ -464,6 +531,7 @@ struct InterleaveArgs {
   FD fd_ta;
   BatchArg batch;
   SwzArg sws, swd;
+  uint32_t cache;
 };
 
 // The dst-contiguous mode b is short (NB * EB <= 16 bytes) and a follows it in
@@ -476,7 +544,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
   using C = Chunk<T, V>;
-  constexpr int U = 4;
+  constexpr int U = NB >= 8 ? 1 : 8 / NB;  // a-chunks per lane: U * NB loads in flight
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
@@ -496,7 +564,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
-        in[u][b] = *(const C*)(src + (size_t)so * EB);
+        in[u][b] = gload<C>(src + (size_t)so * EB, t.cache);
       }
     }
   }
@@ -513,7 +581,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
         o.e[x] = in[u][e % NB].e[e / NB];
       }
       uint32_t dof = swz32(a0 * NB + c * V + bd, t.swd);
-      *(C*)(dst + (size_t)dof * EB) = o;
+      gstore<C>(dst + (size_t)dof * EB, o, t.cache);
     }
   }
 }
@@ -538,6 +606,7 @@ struct StagedArgs {
   FD fd_tg;
   BatchArg batch;
   SwzArg swd;
+  uint32_t cache;
 };
 
 // Padded or gathered tiles ([CuTe algebra page, section 2.2]: composing a padded
@@ -568,7 +637,7 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
     uint32_t tile = t0 + kk;
     if (tile < t.T) {
       size_t byte = (size_t)(tile * t.Ts + bs) * EB + (size_t)c * 16;
-      lds[idx] = *(const uint4*)(src + byte);
+      lds[idx] = gload<uint4>(src + byte, t.cache);
     }
   }
   __syncthreads();
@@ -597,7 +666,7 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
 #pragma unroll
     for (int x = 0; x < V; ++x) o.e[x] = ldsT[base + g[x]];
     uint32_t dof = swz32(tile * t.Td + bd + c * V, t.swd);
-    *(C*)(dst + (size_t)dof * EB) = o;
+    gstore<C>(dst + (size_t)dof * EB, o, t.cache);
   }
 }
 
@@ -647,11 +716,13 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1) {
 }
 
 template <int UB>
-static void launch_generic(const GenericArgs& a, bool wide, unsigned grid, hipStream_t st) {
+static void launch_generic(const GenericArgs& a, bool wide, int unroll, unsigned grid, hipStream_t st) {
   if (wide)
-    hipLaunchKernelGGL((k_generic<UB, true>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, true, 4>), dim3(grid), dim3(256), 0, st, a);
+  else if (unroll == 1)
+    hipLaunchKernelGGL((k_generic<UB, false, 1>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_generic<UB, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, false, 4>), dim3(grid), dim3(256), 0, st, a);
 }
 
 template <int EB>
@@ -739,9 +810,10 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.sws_mask64 = zs.b ? (((uint64_t(1) << zs.b) - 1) << zs.m) : 0;
       a.swd_mask64 = zd.b ? (((uint64_t(1) << zd.b) - 1) << zd.m) : 0;
       a.n_units = p.n_units;
-      a.n_chunks = (p.n_units + 1023) / 1024;
+      a.n_chunks = (p.n_units + 256 * p.unroll - 1) / (256 * p.unroll);
+      a.cache = p.cache;
       const int ub = p.v * p.eb;
-      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, grid, st));
+      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, grid, st));
       return check_launch();
     }
     case LR_PATH_DUAL:
@@ -754,6 +826,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       fill_side(&a.d, Ld, p.wide);
       a.n = p.n;
       a.n_chunks = (p.n + 1023) / 1024;
+      a.cache = p.cache;
       if (p.path == LR_PATH_ALIAS) {
         LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_alias<EBV>), dim3(grid), dim3(1024), 0, st, a));
       } else {
@@ -778,6 +851,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       fill_batch(&a.batch, p, p.a, p.b);
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
+      a.cache = p.cache;
+      a.order = p.torder;
       const bool lds = p.path == LR_PATH_TRANSPOSE;
       bool ok = false;
       LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, grid, st));
@@ -796,6 +871,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       fill_batch(&a.batch, p, p.a, p.b);
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
+      a.cache = p.cache;
       bool ok = false;
       LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, grid, st));
       if (!ok) return LR_ERR_PATH;
@@ -832,6 +908,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         a.batch.sd[r] = (uint32_t)p.m[k].sd;
       }
       a.swd = swz_arg(p.sw_d);
+      a.cache = p.cache;
       const size_t shm = (size_t)p.staged_K * (size_t)p.staged_Fc * 16;
       LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV>), dim3(grid), dim3(256), shm, st, a));
       return check_launch();

@@ -69,6 +69,11 @@ struct Plan {
   int64_t staged_P, staged_F, staged_Fc, staged_K, staged_cpt;
   // alias path
   int64_t alias_windows;
+  // tuning: cache policy bits (1: non-temporal stores, 2: non-temporal loads) and
+  // the transpose's workgroup order (0: a-tiles fastest, 1: b-tiles fastest)
+  uint32_t cache;
+  uint32_t torder;
+  int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
 };
 
 // Plans a copy; fills `p`.  Returns 0 or an lr_status.

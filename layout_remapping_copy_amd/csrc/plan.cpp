@@ -127,6 +127,12 @@ static bool env_flag(const char* name) {
   return e && *e && std::strcmp(e, "0") != 0;
 }
 
+static uint32_t env_u32(const char* name, uint32_t dflt) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return dflt;
+  return (uint32_t)std::strtoul(e, nullptr, 0);
+}
+
 static int plan_alias(Plan* p, int64_t n, int64_t cos_s, int64_t cos_d) {
   const int64_t win = 8192;  // dst offsets owned by one workgroup (LDS owner table)
   int64_t windows = (cos_d + win - 1) / win;
@@ -172,6 +178,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   const int64_t lim32 = int64_t(1) << 31;
   p->wide = (flags & LR_COPY_WIDE_INDEX) || n >= lim32 || cos_s >= lim32 || cos_d >= lim32;
   p->block = 256;
+  p->cache = env_u32("LR_CACHE", 0) & 3u;
+  // one unit per lane measured fastest for streaming copies on MI355X (more waves
+  // in flight beat more loads per wave); LR_UNROLL=4 selects four
+  p->unroll = env_u32("LR_UNROLL", 1) == 4 ? 4 : 1;
 
   // --- non-injective destination: sequential semantics
   const bool inj = injective(Ld);
@@ -203,6 +213,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     if (forced >= 0 && forced != LR_PATH_GENERIC) return LR_ERR_PATH;
     p->path = LR_PATH_GENERIC;
     p->v = 1;
+    p->unroll = 4;
     p->n_units = n;
     p->grid = (n + 1023) / 1024;
     return LR_OK;
@@ -217,7 +228,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     p->path = forced == LR_PATH_GENERIC ? LR_PATH_GENERIC : (v0 > 1 ? LR_PATH_VECTOR : LR_PATH_GENERIC);
     p->v = (int)v0;
     p->n_units = n / v0;
-    p->grid = (p->n_units + 1023) / 1024;
+    p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
     return LR_OK;
   }
 
@@ -272,7 +283,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->a = a;
       p->b = b;
       p->v = (int)V;
-      p->tile_a = 4 * 256 * V;  // a-elements per workgroup: 4 chunks per lane
+      p->tile_a = (nb >= 8 ? 1 : 8 / nb) * 256 * V;  // a-elements per workgroup (matches the kernel's per-lane unroll)
       p->tile_b = nb;
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
@@ -303,6 +314,15 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->v = (int)V;
       p->tile_a = 16 * V;
       p->tile_b = 16 * V;
+      // Workgroup order.  When the source rows of consecutive b-tiles are close
+      // (pitch <= 2 KiB, e.g. NHWC channels) b-tiles go fastest: both the reads
+      // and the writes of neighbouring workgroups are then adjacent.  Otherwise
+      // (large pitches such as a square transpose's 16 KiB rows) a diagonal order
+      // keeps the workgroups in flight from sharing one column offset, which with
+      // power-of-two pitches concentrates them on a few HBM channels.
+      p->torder = (p->m[b].ss * p->eb <= 2048) ? 1u : 2u;
+      const uint32_t tord = env_u32("LR_TORDER", 99);
+      if (tord <= 2) p->torder = tord;
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
         if (k != a && k != b) batch *= p->m[k].ext;
@@ -373,7 +393,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   int64_t ne = 1;
   for (int k = 0; k < p->rank; ++k) ne *= p->m[k].ext;
   p->n_units = ne / v;
-  p->grid = (p->n_units + 1023) / 1024;
+  p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
   return LR_OK;
 }
 
@@ -426,6 +446,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       const int64_t nb = p.m[p.b].ext;
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.a].sd != nb || p.tile_b != nb) return bad();
       if (v * p.eb != 16 || p.m[p.a].ext % v || nb * p.eb > 16) return bad();
+      if (p.tile_a != (nb >= 8 ? 1 : 8 / nb) * 256 * v) return bad();  // the kernel's per-lane unroll
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.a && k != p.b && p.m[k].sd % v) return bad();

@@ -412,27 +412,32 @@ struct TransposeArgs {
   BatchArg batch;
   SwzArg sws, swd;
   uint32_t cache;
-  uint32_t order;  // 0: tiles along a vary fastest across workgroups, 1: along b, 2: diagonal
+  uint32_t order;  // 0: tiles along a vary fastest across workgroups, 1: along b, 2: diagonal,
+                   // 3: diagonal over 4 x 4 groups of tiles
+  uint32_t gta, gtb;  // order 3: groups along a and b
+  FD fd_gta, fd_gtb;
 };
 
-// Tile of 16V x 16V elements per workgroup; each lane owns a V x V register block:
-// V chunk loads of V elements along a (one per b row), an in-register transpose,
-// V chunk stores of V elements along b (one per a row).  V*EB == 16 normally, so
-// every global access is a 16-byte vector.
+// Tile of (TA*V) x (TB*V) elements per workgroup of TA*TB lanes; each lane owns a
+// V x V register block: V chunk loads of V elements along a (one per b row), an
+// in-register transpose, V chunk stores of V elements along b (one per a row).
+// V*EB == 16 normally, so every global access is a 16-byte vector.
 //
 // LDS == true: the transposed chunks go through LDS so that a wave's stores run
-// along 16 consecutive chunks of one dst row (256 contiguous bytes per row for 16-B
-// chunks).  The LDS tile is addressed [row][chunk ^ (row / V)], an XOR swizzle of
-// the 16-byte chunk index ([print_layout page, sections 4.3 and 5.2]: XOR spreads
-// a column across banks, where padding would also do), so both the chunk writes
-// (16 lanes of one chunk column) and the row reads (16 lanes of one row) touch 16
-// distinct chunk slots of a 256-byte bank window.
-// LDS == false: lanes are arranged 8 x 8 per wave so each load and store
-// instruction covers eight full 128-byte lines, with no LDS at all.
-template <int EB, int V, bool LDS>
-__global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
+// along TB consecutive chunks of one dst row (TB*16 contiguous bytes per row for
+// 16-B chunks).  The LDS tile is addressed [row][chunk ^ ((row / V) % TB)], an XOR
+// swizzle of the 16-byte chunk index ([print_layout page, sections 4.3 and 5.2]:
+// XOR spreads a column across banks, where padding would also do), so both the
+// chunk writes (lanes of one chunk column) and the row reads (lanes of one row)
+// touch distinct chunk slots of a bank window.
+// LDS == false (TA == TB == 16 only): lanes are arranged 8 x 8 per wave so each
+// load and store instruction covers eight full 128-byte lines, with no LDS.
+template <int EB, int V, bool LDS, int TA, int TB>
+__global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   using T = typename Raw<EB>::T;
   using C = Chunk<T, V>;
+  constexpr int NT = TA * TB;
+  static_assert(LDS || (TA == 16 && TB == 16), "the direct variant uses 16 x 16 blocks");
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
@@ -447,7 +452,7 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
     tb = blk - r1 * t.tiles_b;
     r2 = fdiv(r1, t.fd_ta);
     ta = r1 - r2 * t.tiles_a;
-  } else {
+  } else if (t.order == 2) {
     // diagonal: consecutive workgroups take consecutive a-tiles and, with them,
     // shifted b-tiles, so that neither the rows they read nor the rows they write
     // share one column offset (power-of-two pitches otherwise land every row of a
@@ -458,6 +463,21 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
     uint32_t ta_mod = ta - fdiv(ta, t.fd_tb) * t.tiles_b;  // ta % tiles_b
     uint32_t d = (r1 - r2 * t.tiles_b) + ta_mod;            // < 2 * tiles_b
     tb = d >= t.tiles_b ? d - t.tiles_b : d;
+  } else {
+    // grouped diagonal: 16 consecutive workgroups cover a 4 x 4 group of tiles,
+    // so the workgroups in flight read and write 4 adjacent tile rows' worth of
+    // contiguous bytes per row (DRAM page locality on both sides), and the groups
+    // themselves are laid out diagonally as above (channel spread).  Needs
+    // tiles_a and tiles_b to be multiples of 4; gta = tiles_a / 4, gtb = tiles_b / 4.
+    const uint32_t g = blk >> 4, w = blk & 15u;
+    uint32_t r1 = fdiv(g, t.fd_gta);
+    const uint32_t ga = g - r1 * t.gta;
+    r2 = fdiv(r1, t.fd_gtb);
+    const uint32_t ga_mod = ga - fdiv(ga, t.fd_gtb) * t.gtb;
+    const uint32_t d = (r1 - r2 * t.gtb) + ga_mod;
+    const uint32_t gb = d >= t.gtb ? d - t.gtb : d;
+    ta = 4 * ga + (w & 3u);
+    tb = 4 * gb + (w >> 2);
   }
   uint32_t bs, bd;
   batch_offsets(t.batch, r2, &bs, &bd);
@@ -465,14 +485,14 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
   const int tid = threadIdx.x;
   int alpha, beta;
   if (LDS) {
-    alpha = tid & 15;
-    beta = tid >> 4;
+    alpha = tid % TA;
+    beta = tid / TA;
   } else {
     const int lane = tid & 63, w = tid >> 6;
     alpha = (lane & 7) + 8 * (w & 1);
     beta = (lane >> 3) + 8 * (w >> 1);
   }
-  const uint32_t a0 = ta * (16 * V), b0 = tb * (16 * V);
+  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
   const uint32_t a_blk = a0 + V * alpha, b_blk = b0 + V * beta;
   const bool valid = a_blk < t.ext_a && b_blk < t.ext_b;
 
@@ -501,19 +521,19 @@ __global__ void __launch_bounds__(256) k_transpose(TransposeArgs t) {
     return;
   }
 
-  __shared__ C tile[16 * V][16];
+  __shared__ C tile[TA * V][TB];
   if (valid) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) tile[V * alpha + i][beta ^ alpha] = out[i];
+    for (int i = 0; i < V; ++i) tile[V * alpha + i][beta ^ (alpha % TB)] = out[i];
   }
   __syncthreads();
-  const int c = tid & 15;
+  const int c = tid % TB;
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const int row = (tid >> 4) + 16 * k;
+    const int row = tid / TB + (NT / TB) * k;
     const uint32_t a = a0 + row, b = b0 + V * c;
     if (a < t.ext_a && b < t.ext_b) {
-      C v = tile[row][c ^ ((row / V) & 15)];
+      C v = tile[row][c ^ ((row / V) % TB)];
       uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
       gstore<C>(dst + (size_t)dof * EB, v, t.cache);
     }
@@ -535,16 +555,19 @@ struct InterleaveArgs {
 };
 
 // The dst-contiguous mode b is short (NB * EB <= 16 bytes) and a follows it in
-// dst, so V consecutive a positions times NB form NB contiguous dst chunks.  Each
-// lane loads NB 16-byte chunks (one per b) and writes them interleaved.  This is
-// the pairing of [print_layout page, section 4.2] (two heads side by side so one
-// wide load brings both), done in registers.
-template <int EB, int NB>
+// dst, so V consecutive a positions times NB form NB contiguous dst chunks.  This
+// is the pairing of [print_layout page, section 4.2] (two heads side by side so
+// one wide load brings both), done in registers.
+//   NARROW == false: each lane loads NB 16-byte chunks (one per b) and writes
+//     them interleaved as NB chunks;
+//   NARROW == true: each lane writes one 16-byte dst chunk, built from NB loads of
+//     16/NB bytes (P = V/NB positions of a, one load per b), so that every store
+//     instruction of a wave covers 1 KiB of contiguous dst.
+template <int EB, int NB, bool NARROW>
 __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
   using C = Chunk<T, V>;
-  constexpr int U = NB >= 8 ? 1 : 8 / NB;  // a-chunks per lane: U * NB loads in flight
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
@@ -554,34 +577,66 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
   uint32_t bs, bd;
   batch_offsets(t.batch, r1, &bs, &bd);
 
-  C in[U][NB];
-  bool ok[U];
+  if constexpr (NARROW) {
+    constexpr int P = V / NB;  // a positions per dst chunk
+    using H = Chunk<T, P>;
+    constexpr int U = 4;
+    H in[U][NB];
+    bool ok[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    uint32_t a0 = (ta * (256 * U) + u * 256 + threadIdx.x) * V;
-    ok[u] = a0 < t.ext_a;
-    if (ok[u]) {
+    for (int u = 0; u < U; ++u) {
+      const uint32_t j = ta * (256 * U) + u * 256 + threadIdx.x;  // dst chunk index
+      const uint32_t a0 = j * P;
+      ok[u] = a0 < t.ext_a;
+      if (ok[u]) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
-        in[u][b] = gload<C>(src + (size_t)so * EB, t.cache);
+        for (int b = 0; b < NB; ++b) {
+          uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
+          in[u][b] = gload<H>(src + (size_t)so * EB, t.cache);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (!ok[u]) continue;
-    uint32_t a0 = (ta * (256 * U) + u * 256 + threadIdx.x) * V;
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      const uint32_t j = ta * (256 * U) + u * 256 + threadIdx.x;
       C o;
 #pragma unroll
-      for (int x = 0; x < V; ++x) {
-        const int e = c * V + x;  // element a0*NB + e: a = a0 + e / NB, b = e % NB
-        o.e[x] = in[u][e % NB].e[e / NB];
-      }
-      uint32_t dof = swz32(a0 * NB + c * V + bd, t.swd);
+      for (int x = 0; x < V; ++x) o.e[x] = in[u][x % NB].e[x / NB];
+      uint32_t dof = swz32(j * V + bd, t.swd);
       gstore<C>(dst + (size_t)dof * EB, o, t.cache);
+    }
+  } else {
+    constexpr int U = NB >= 8 ? 1 : 8 / NB;  // a-chunks per lane: U * NB loads in flight
+    C in[U][NB];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t a0 = (ta * (256 * U) + u * 256 + threadIdx.x) * V;
+      ok[u] = a0 < t.ext_a;
+      if (ok[u]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
+          in[u][b] = gload<C>(src + (size_t)so * EB, t.cache);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      uint32_t a0 = (ta * (256 * U) + u * 256 + threadIdx.x) * V;
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        C o;
+#pragma unroll
+        for (int x = 0; x < V; ++x) {
+          const int e = c * V + x;  // element a0*NB + e: a = a0 + e / NB, b = e % NB
+          o.e[x] = in[u][e % NB].e[e / NB];
+        }
+        uint32_t dof = swz32(a0 * NB + c * V + bd, t.swd);
+        gstore<C>(dst + (size_t)dof * EB, o, t.cache);
+      }
     }
   }
 }
@@ -733,35 +788,57 @@ static void launch_dual(const DualArgs& a, bool wide, unsigned grid, hipStream_t
     hipLaunchKernelGGL((k_dual<EB, false>), dim3(grid), dim3(256), 0, st, a);
 }
 
+template <int EB, int V, int TA, int TB>
+static void launch_transpose_shape(const TransposeArgs& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_transpose<EB, V, true, TA, TB>), dim3(grid), dim3(TA * TB), 0, st, a);
+}
+
 template <int EB, int V>
-static void launch_transpose_v(const TransposeArgs& a, bool lds, unsigned grid, hipStream_t st) {
-  if (lds)
-    hipLaunchKernelGGL((k_transpose<EB, V, true>), dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_transpose<EB, V, false>), dim3(grid), dim3(256), 0, st, a);
+static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, unsigned grid, hipStream_t st) {
+  if (!lds) {
+    if (shape != 0) return false;
+    hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16>), dim3(grid), dim3(256), 0, st, a);
+    return true;
+  }
+  if constexpr (V * EB == 16 && V <= 8) {  // wider tiles: full 16-byte chunks, LDS <= 128 KiB
+    switch (shape) {
+      case 1: launch_transpose_shape<EB, V, 32, 16>(a, grid, st); return true;
+      case 2: launch_transpose_shape<EB, V, 16, 32>(a, grid, st); return true;
+      case 3: launch_transpose_shape<EB, V, 32, 32>(a, grid, st); return true;
+      default: break;
+    }
+  }
+  if (shape != 0) return false;
+  launch_transpose_shape<EB, V, 16, 16>(a, grid, st);
+  return true;
 }
 
 template <int EB>
-static bool launch_transpose(const TransposeArgs& a, int v, bool lds, unsigned grid, hipStream_t st) {
+static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, unsigned grid, hipStream_t st) {
   switch (v) {
-    case 1: launch_transpose_v<EB, 1>(a, lds, grid, st); return true;
-    case 2: if constexpr (EB <= 8) { launch_transpose_v<EB, 2>(a, lds, grid, st); return true; } break;
-    case 4: if constexpr (EB <= 4) { launch_transpose_v<EB, 4>(a, lds, grid, st); return true; } break;
-    case 8: if constexpr (EB <= 2) { launch_transpose_v<EB, 8>(a, lds, grid, st); return true; } break;
-    case 16: if constexpr (EB == 1) { launch_transpose_v<EB, 16>(a, lds, grid, st); return true; } break;
+    case 1: return launch_transpose_v<EB, 1>(a, lds, shape, grid, st);
+    case 2: if constexpr (EB <= 8) return launch_transpose_v<EB, 2>(a, lds, shape, grid, st); break;
+    case 4: if constexpr (EB <= 4) return launch_transpose_v<EB, 4>(a, lds, shape, grid, st); break;
+    case 8: if constexpr (EB <= 2) return launch_transpose_v<EB, 8>(a, lds, shape, grid, st); break;
+    case 16: if constexpr (EB == 1) return launch_transpose_v<EB, 16>(a, lds, shape, grid, st); break;
+  }
+  return false;
+}
+
+template <int EB, bool NARROW>
+static bool launch_interleave_n(const InterleaveArgs& a, int nb, unsigned grid, hipStream_t st) {
+  switch (nb) {
+    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
   }
   return false;
 }
 
 template <int EB>
-static bool launch_interleave(const InterleaveArgs& a, int nb, unsigned grid, hipStream_t st) {
-  switch (nb) {
-    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-  }
-  return false;
+static bool launch_interleave(const InterleaveArgs& a, int nb, bool narrow, unsigned grid, hipStream_t st) {
+  return narrow ? launch_interleave_n<EB, true>(a, nb, grid, st) : launch_interleave_n<EB, false>(a, nb, grid, st);
 }
 
 #define LR_DISPATCH_EB(eb, CALL)          \
@@ -853,9 +930,15 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.swd = swz_arg(p.sw_d);
       a.cache = p.cache;
       a.order = p.torder;
+      if (p.torder == 3) {
+        a.gta = a.tiles_a / 4;
+        a.gtb = a.tiles_b / 4;
+        a.fd_gta = fd_of(a.gta);
+        a.fd_gtb = fd_of(a.gtb);
+      }
       const bool lds = p.path == LR_PATH_TRANSPOSE;
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
@@ -873,7 +956,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.swd = swz_arg(p.sw_d);
       a.cache = p.cache;
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, p.inarrow != 0, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }

@@ -74,6 +74,8 @@ struct Plan {
   uint32_t cache;
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
+  int tshape;         // transpose tile: 0 16x16, 1 32x16, 2 16x32, 3 32x32 chunks (a x b)
+  int inarrow;        // interleave: 1 = one 16-byte store per lane from NB narrow loads
 };
 
 // Plans a copy; fills `p`.  Returns 0 or an lr_status.

@@ -283,7 +283,11 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->a = a;
       p->b = b;
       p->v = (int)V;
-      p->tile_a = (nb >= 8 ? 1 : 8 / nb) * 256 * V;  // a-elements per workgroup (matches the kernel's per-lane unroll)
+      // one 16-byte store per lane from NB narrow loads measured faster (every store
+      // instruction covers 1 KiB of contiguous dst); LR_INARROW=0 selects the other
+      p->inarrow = (int)(env_u32("LR_INARROW", 1) & 1u);
+      // a-elements per workgroup, matching the kernel's per-lane unroll
+      p->tile_a = p->inarrow ? 4 * 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
       p->tile_b = nb;
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
@@ -312,8 +316,19 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->a = a;
       p->b = b;
       p->v = (int)V;
-      p->tile_a = 16 * V;
-      p->tile_b = 16 * V;
+      // tile shape in 16-byte chunks (a x b): wider tiles only for full chunks on
+      // the LDS variant.  With large source pitches (rows far apart on both sides)
+      // 32 x 16 chunks (512-byte source runs per row) measured fastest; with close
+      // source rows the 16 x 16 tile did.
+      const bool far_rows = p->m[b].ss * p->eb > 2048;
+      const bool wide_ok = V * p->eb == 16 && V <= 8 && p->path == LR_PATH_TRANSPOSE;
+      p->tshape = (far_rows && wide_ok) ? 1 : 0;
+      const uint32_t shp = env_u32("LR_TSHAPE", 99);
+      if (shp <= 3) p->tshape = wide_ok ? (int)shp : 0;
+      static const int kTA[4] = {16, 32, 16, 32}, kTB[4] = {16, 16, 32, 32};
+      p->tile_a = kTA[p->tshape] * V;
+      p->tile_b = kTB[p->tshape] * V;
+      p->block = kTA[p->tshape] * kTB[p->tshape];
       // Workgroup order.  When the source rows of consecutive b-tiles are close
       // (pitch <= 2 KiB, e.g. NHWC channels) b-tiles go fastest: both the reads
       // and the writes of neighbouring workgroups are then adjacent.  Otherwise
@@ -322,7 +337,12 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // power-of-two pitches concentrates them on a few HBM channels.
       p->torder = (p->m[b].ss * p->eb <= 2048) ? 1u : 2u;
       const uint32_t tord = env_u32("LR_TORDER", 99);
-      if (tord <= 2) p->torder = tord;
+      if (tord <= 3) p->torder = tord;
+      {
+        const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
+        const int64_t ntb = (p->m[b].ext + p->tile_b - 1) / p->tile_b;
+        if (p->torder == 3 && (nta % 4 || ntb % 4)) p->torder = 2;  // grouped order needs 4 | tiles
+      }
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
         if (k != a && k != b) batch *= p->m[k].ext;
@@ -434,7 +454,13 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1) return bad();
       if (p.m[p.a].ext % v || p.m[p.b].ext % v) return bad();
-      if (p.tile_a != 16 * v || p.tile_b != 16 * v) return bad();
+      static const int kTA[4] = {16, 32, 16, 32}, kTB[4] = {16, 16, 32, 32};
+      if (p.tshape < 0 || p.tshape > 3 || (p.tshape != 0 && (v * p.eb != 16 || v > 8 || p.path != LR_PATH_TRANSPOSE)))
+        return bad();
+      if (p.torder > 3) return bad();
+      if (p.torder == 3 && ((p.m[p.a].ext + p.tile_a - 1) / p.tile_a % 4 || (p.m[p.b].ext + p.tile_b - 1) / p.tile_b % 4))
+        return bad();
+      if (p.tile_a != kTA[p.tshape] * v || p.tile_b != kTB[p.tshape] * v) return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.b && p.m[k].sd % v) return bad();
@@ -446,7 +472,8 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       const int64_t nb = p.m[p.b].ext;
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.a].sd != nb || p.tile_b != nb) return bad();
       if (v * p.eb != 16 || p.m[p.a].ext % v || nb * p.eb > 16) return bad();
-      if (p.tile_a != (nb >= 8 ? 1 : 8 / nb) * 256 * v) return bad();  // the kernel's per-lane unroll
+      // the kernel's per-lane unroll
+      if (p.tile_a != (p.inarrow ? 4 * 256 * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v)) return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.a && k != p.b && p.m[k].sd % v) return bad();

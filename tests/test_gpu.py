@@ -376,3 +376,51 @@ def test_full_transpose_both_variants(dev):
         lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=2, flags=lr.COPY_FORCE_PATH(path))
         torch.cuda.synchronize()
         assert np.array_equal(d.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+# Tuning variants chosen at plan time (tile shapes, narrow-load interleave)
+# ---------------------------------------------------------------------------
+@pytest.fixture
+def env_knob(monkeypatch):
+    return monkeypatch
+
+
+@pytest.mark.parametrize("shape", [0, 1, 2, 3])
+def test_transpose_tile_shapes(dev, env_knob, shape):
+    env_knob.setenv("LR_TSHAPE", str(shape))
+    for ts, td, n, eb in [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
+                          ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 7560, 2),
+                          ("(100,72):(72,1)", "(100,72):(1,100)", 7200, 4),
+                          ("(64,96,5):(96,1,6144)", "(64,96,5):(1,64,6144)", 30720, 8),
+                          ("(1024,512):(512,1)", "(1024,512):(1,1024)", 1024 * 512, 2)]:
+        src = np.random.default_rng(shape).integers(0, 256, n * eb, dtype=np.uint8)
+        dst = np.full(n * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for path in (lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT):
+            flags = lr.COPY_FORCE_PATH(path)
+            try:
+                lr.copy_plan(ts, n, td, n, eb, flags)
+            except lr.LayoutRemapError:
+                continue
+            say("transpose shape", shape, lr.binding.PATH_NAMES[path], ts, "eb", eb)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
+        for orient in ("0", "1", "2", "3"):
+            env_knob.setenv("LR_TORDER", orient)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)
+        env_knob.delenv("LR_TORDER")
+
+
+@pytest.mark.parametrize("narrow", [0, 1])
+def test_interleave_variants(dev, env_knob, narrow):
+    env_knob.setenv("LR_INARROW", str(narrow))
+    for eb, nb in [(1, 2), (1, 4), (1, 8), (1, 16), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (8, 2)]:
+        a, bt = 16 // eb * 40, 3
+        ts, td = f"({nb},{a},{bt}):({a},1,{a * nb})", f"({nb},{a},{bt}):(1,{nb},{a * nb})"
+        n = a * nb * bt
+        assert lr.copy_plan(ts, n, td, n, eb)["path"] == "interleave"
+        src = np.random.default_rng(eb * 31 + nb).integers(0, 256, n * eb, dtype=np.uint8)
+        dst = np.full(n * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        say("interleave narrow", narrow, "eb", eb, "nb", nb)
+        assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)

@@ -204,11 +204,11 @@ struct GenericArgs {
   uint64_t sws_mask64, swd_mask64;
   uint32_t cache;
   int64_t n_units;
-  int64_t n_chunks;  // groups of 1024 units
+  int64_t n_chunks;  // groups of 256 * U units, U the per-lane unroll
 };
 
-// One unit (UB bytes) per lane and step; four independent units per lane so each
-// lane keeps four loads in flight before its stores.  Lanes of a wave take
+// One unit (UB bytes) per lane and step, one or four units per lane (U); with four,
+// each lane issues all four loads before its stores.  Lanes of a wave take
 // consecutive units, i.e. consecutive positions of the fastest joint mode.
 template <bool WIDE>
 __device__ __forceinline__ void generic_offsets(const GenericArgs& a, int64_t idx, uint64_t* so, uint64_t* dof) {
@@ -685,15 +685,30 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   batch_offsets(t.batch, r1, &bs, &bd);
   const uint32_t t0 = tg * t.K;
 
+  // Four independent 16-byte loads per lane per round, all issued before any LDS
+  // write, so each lane keeps four loads in flight (a load-then-store loop body
+  // would wait for every load before issuing the next).
   const uint32_t nload = t.K * t.Fc;
-  for (uint32_t idx = threadIdx.x; idx < nload; idx += 256) {
-    uint32_t kk = fdiv(idx, t.fd_Fc);
-    uint32_t c = idx - kk * t.Fc;
-    uint32_t tile = t0 + kk;
-    if (tile < t.T) {
-      size_t byte = (size_t)(tile * t.Ts + bs) * EB + (size_t)c * 16;
-      lds[idx] = gload<uint4>(src + byte, t.cache);
-    }
+  auto chunk_ok = [&](uint32_t idx, size_t* byte) {
+    if (idx >= nload) return false;
+    const uint32_t kk = fdiv(idx, t.fd_Fc);
+    const uint32_t tile = t0 + kk;
+    *byte = (size_t)(tile * t.Ts + bs) * EB + (size_t)(idx - kk * t.Fc) * 16;
+    return tile < t.T;
+  };
+  for (uint32_t i0 = threadIdx.x; i0 < nload; i0 += 1024) {
+    size_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+    const bool k0 = chunk_ok(i0, &b0), k1 = chunk_ok(i0 + 256, &b1), k2 = chunk_ok(i0 + 512, &b2),
+               k3 = chunk_ok(i0 + 768, &b3);
+    uint4 v0, v1, v2, v3;
+    if (k0) v0 = gload<uint4>(src + b0, t.cache);
+    if (k1) v1 = gload<uint4>(src + b1, t.cache);
+    if (k2) v2 = gload<uint4>(src + b2, t.cache);
+    if (k3) v3 = gload<uint4>(src + b3, t.cache);
+    if (k0) lds[i0] = v0;
+    if (k1) lds[i0 + 256] = v1;
+    if (k2) lds[i0 + 512] = v2;
+    if (k3) lds[i0 + 768] = v3;
   }
   __syncthreads();
 
@@ -800,11 +815,14 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, unsi
     hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16>), dim3(grid), dim3(256), 0, st, a);
     return true;
   }
-  if constexpr (V * EB == 16 && V <= 8) {  // wider tiles: full 16-byte chunks, LDS <= 128 KiB
+  if constexpr (V * EB == 16 && V <= 8) {  // other shapes: full 16-byte chunks, LDS <= 128 KiB
     switch (shape) {
-      case 1: launch_transpose_shape<EB, V, 32, 16>(a, grid, st); return true;
-      case 2: launch_transpose_shape<EB, V, 16, 32>(a, grid, st); return true;
-      case 3: launch_transpose_shape<EB, V, 32, 32>(a, grid, st); return true;
+      case 1: launch_transpose_shape<EB, V, kTileTA[1], kTileTB[1]>(a, grid, st); return true;
+      case 2: launch_transpose_shape<EB, V, kTileTA[2], kTileTB[2]>(a, grid, st); return true;
+      case 3: launch_transpose_shape<EB, V, kTileTA[3], kTileTB[3]>(a, grid, st); return true;
+      case 4: launch_transpose_shape<EB, V, kTileTA[4], kTileTB[4]>(a, grid, st); return true;
+      case 5: launch_transpose_shape<EB, V, kTileTA[5], kTileTB[5]>(a, grid, st); return true;
+      case 6: launch_transpose_shape<EB, V, kTileTA[6], kTileTB[6]>(a, grid, st); return true;
       default: break;
     }
   }

@@ -48,6 +48,12 @@ struct Swz {
   int32_t b, m, s;  // b == 0: none
 };
 
+// Transpose tile shapes in 16-byte chunks along a (source-contiguous) x b
+// (destination-contiguous); the workgroup has TA * TB lanes.
+constexpr int kTileShapes = 7;
+constexpr int kTileTA[kTileShapes] = {16, 32, 16, 32, 32, 64, 64};
+constexpr int kTileTB[kTileShapes] = {16, 16, 32, 32, 8, 8, 16};
+
 // Everything the launch code needs.
 struct Plan {
   int path;           // lr_path
@@ -74,7 +80,7 @@ struct Plan {
   uint32_t cache;
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
-  int tshape;         // transpose tile: 0 16x16, 1 32x16, 2 16x32, 3 32x32 chunks (a x b)
+  int tshape;         // transpose tile shape index into kTileTA / kTileTB
   int inarrow;        // interleave: 1 = one 16-byte store per lane from NB narrow loads
 };
 

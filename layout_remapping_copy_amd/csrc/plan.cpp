@@ -229,6 +229,15 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     p->v = (int)v0;
     p->n_units = n / v0;
     p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
+    // Traversal order after the common contiguous mode.  Any order of the joint
+    // modes is the same copy when the destination is injective; walking the source
+    // order (reads in long runs, writes in runs of the common mode) measured
+    // faster than the destination order when the common run is short (the 128-byte
+    // rows of the 4096^2 retile).  LR_VORDER=0 keeps the destination order.
+    if (env_u32("LR_VORDER", 1) == 1 && p->rank > 2)
+      std::stable_sort(p->m + 1, p->m + p->rank, [](const JMode& x, const JMode& y) {
+        return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
+      });
     return LR_OK;
   }
 
@@ -324,11 +333,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       const bool wide_ok = V * p->eb == 16 && V <= 8 && p->path == LR_PATH_TRANSPOSE;
       p->tshape = (far_rows && wide_ok) ? 1 : 0;
       const uint32_t shp = env_u32("LR_TSHAPE", 99);
-      if (shp <= 3) p->tshape = wide_ok ? (int)shp : 0;
-      static const int kTA[4] = {16, 32, 16, 32}, kTB[4] = {16, 16, 32, 32};
-      p->tile_a = kTA[p->tshape] * V;
-      p->tile_b = kTB[p->tshape] * V;
-      p->block = kTA[p->tshape] * kTB[p->tshape];
+      if (shp < (uint32_t)kTileShapes) p->tshape = wide_ok ? (int)shp : 0;
+      p->tile_a = kTileTA[p->tshape] * V;
+      p->tile_b = kTileTB[p->tshape] * V;
+      p->block = kTileTA[p->tshape] * kTileTB[p->tshape];
       // Workgroup order.  When the source rows of consecutive b-tiles are close
       // (pitch <= 2 KiB, e.g. NHWC channels) b-tiles go fastest: both the reads
       // and the writes of neighbouring workgroups are then adjacent.  Otherwise
@@ -454,13 +462,13 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1) return bad();
       if (p.m[p.a].ext % v || p.m[p.b].ext % v) return bad();
-      static const int kTA[4] = {16, 32, 16, 32}, kTB[4] = {16, 16, 32, 32};
-      if (p.tshape < 0 || p.tshape > 3 || (p.tshape != 0 && (v * p.eb != 16 || v > 8 || p.path != LR_PATH_TRANSPOSE)))
+      if (p.tshape < 0 || p.tshape >= kTileShapes ||
+          (p.tshape != 0 && (v * p.eb != 16 || v > 8 || p.path != LR_PATH_TRANSPOSE)))
         return bad();
       if (p.torder > 3) return bad();
       if (p.torder == 3 && ((p.m[p.a].ext + p.tile_a - 1) / p.tile_a % 4 || (p.m[p.b].ext + p.tile_b - 1) / p.tile_b % 4))
         return bad();
-      if (p.tile_a != kTA[p.tshape] * v || p.tile_b != kTB[p.tshape] * v) return bad();
+      if (p.tile_a != kTileTA[p.tshape] * v || p.tile_b != kTileTB[p.tshape] * v) return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.b && p.m[k].sd % v) return bad();

@@ -386,7 +386,7 @@ def env_knob(monkeypatch):
     return monkeypatch
 
 
-@pytest.mark.parametrize("shape", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
 def test_transpose_tile_shapes(dev, env_knob, shape):
     env_knob.setenv("LR_TSHAPE", str(shape))
     for ts, td, n, eb in [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
@@ -423,4 +423,22 @@ def test_interleave_variants(dev, env_knob, narrow):
         dst = np.full(n * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         say("interleave narrow", narrow, "eb", eb, "nb", nb)
+        assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)
+
+
+@pytest.mark.parametrize("vorder", [0, 1])
+def test_vector_traversal_orders(dev, env_knob, vorder):
+    env_knob.setenv("LR_VORDER", str(vorder))
+    cases = [(W.small("retile").src_layout, W.small("retile").dst_layout, 512 * 512, 512 * 512, 2),
+             ("(64,64):(64,1)", "Sw<3,3,3> o (64,64):(64,1)", 4096, 4096, 2),
+             ("(96,5,3):(1,96,480)", "(96,5,3):(1,288,96)", 1440, 1440, 2),
+             ("8192:1", "8192:1", 8192, 8192, 4),
+             ("(8,2048):(1,8)", "(8,2048):(1,8)", 16384, 16384, 1),
+             ("(16,3,256):(1,4096,16)", "(16,3,256):(1,16,48)", 12288, 12288, 2),
+             ("(4,64,7):(1,4,256)", "(4,64,7):(1,28,4)", 1792, 1792, 4)]
+    for ts, td, ns, nd, eb in cases:
+        src = np.random.default_rng(ns).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        say("vector order", vorder, ts, "->", td, "eb", eb, lr.copy_plan(ts, ns, td, nd, eb)["path"])
         assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)

@@ -127,7 +127,7 @@ def counters_run(lr, torch, W, reps: int = 3):
     workload `reps` times after one warm-up, then a plain contiguous copy of
     256 MiB (the reference of known size that scales FETCH_SIZE / WRITE_SIZE)."""
     dev = torch.device("cuda:0")
-    names = ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles")
+    names = ("transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles")
     for name in names:
         w = W.full(name)
         s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)
@@ -246,7 +246,7 @@ def main():
     # ---- the other large remapping copies, timed the same way
     if not args.no_others:
         others = {}
-        for name in ("retile", "interleave", "nhwc2nchw", "padtiles"):
+        for name in ("retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles"):
             wo = W.full(name)
             p = lr.copy_plan(wo.src_layout, wo.src_elems, wo.dst_layout, wo.dst_elems, wo.elem_bytes)
             prs = _pairs(torch, dev, wo.src_elems * wo.elem_bytes, wo.dst_elems * wo.elem_bytes)

@@ -198,6 +198,7 @@ typedef struct {
   int32_t joint_rank;  /* number of joint modes (0 for the dual/alias paths) */
   int32_t a_mode;      /* joint mode contiguous in src (transpose/interleave), else -1 */
   int32_t b_mode;      /* joint mode contiguous in dst (transpose/interleave), else -1 */
+  int32_t b2_mode;     /* transpose: mode continuing b_mode in dst, grouped with it, else -1 */
   int32_t block;       /* threads per workgroup */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */

@@ -407,6 +407,11 @@ struct TransposeArgs {
   void* dst;
   uint32_t ext_a, ext_b;  // a: src-contiguous mode, b: dst-contiguous mode
   uint32_t ss_b, sd_a;    // the other stride of each
+  // b may be a group of two joint modes that run on in dst (the first of extent
+  // 2^bshift at dst stride 1, the second at dst stride 2^bshift): the source offset
+  // of row b is then (b & bmask) * ss_b + (b >> bshift) * ss_b2.  For a single
+  // mode bmask is all ones, bshift 31 and ss_b2 0.
+  uint32_t bmask, bshift, ss_b2;
   uint32_t tiles_a, tiles_b;
   FD fd_ta, fd_tb;
   BatchArg batch;
@@ -500,7 +505,8 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   if (valid) {
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      uint32_t so = swz32(a_blk + (b_blk + j) * t.ss_b + bs, t.sws);
+      const uint32_t b = b_blk + j;
+      uint32_t so = swz32(a_blk + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
       in[j] = gload<C>(src + (size_t)so * EB, t.cache);
     }
   }
@@ -773,10 +779,10 @@ static void fill_side(SideArg* s, const lr_layout* L, bool wide) {
   s->mask64 = L->swz_b > 0 ? (((uint64_t(1) << L->swz_b) - 1) << L->swz_m) : 0;
 }
 
-static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1) {
+static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int skip2 = -1) {
   std::memset(b, 0, sizeof(*b));
   for (int k = 0; k < p.rank; ++k) {
-    if (k == skip0 || k == skip1) continue;
+    if (k == skip0 || k == skip1 || k == skip2) continue;
     int r = b->rank++;
     b->ext[r] = (uint32_t)p.m[k].ext;
     b->fd[r] = fd_of(p.m[k].ext);
@@ -935,15 +941,27 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       std::memset(&a, 0, sizeof(a));
       a.src = src;
       a.dst = dst;
+      const int64_t ext_b = p.m[p.b].ext * (p.b2 >= 0 ? p.m[p.b2].ext : 1);
       a.ext_a = (uint32_t)p.m[p.a].ext;
-      a.ext_b = (uint32_t)p.m[p.b].ext;
+      a.ext_b = (uint32_t)ext_b;
       a.ss_b = (uint32_t)p.m[p.b].ss;
       a.sd_a = (uint32_t)p.m[p.a].sd;
+      if (p.b2 >= 0) {
+        uint32_t sh = 0;
+        while ((int64_t(1) << sh) < p.m[p.b].ext) ++sh;
+        a.bmask = (1u << sh) - 1u;
+        a.bshift = sh;
+        a.ss_b2 = (uint32_t)p.m[p.b2].ss;
+      } else {
+        a.bmask = 0xFFFFFFFFu;
+        a.bshift = 31;
+        a.ss_b2 = 0;
+      }
       a.tiles_a = (uint32_t)((p.m[p.a].ext + p.tile_a - 1) / p.tile_a);
-      a.tiles_b = (uint32_t)((p.m[p.b].ext + p.tile_b - 1) / p.tile_b);
+      a.tiles_b = (uint32_t)((ext_b + p.tile_b - 1) / p.tile_b);
       a.fd_ta = fd_of(a.tiles_a);
       a.fd_tb = fd_of(a.tiles_b);
-      fill_batch(&a.batch, p, p.a, p.b);
+      fill_batch(&a.batch, p, p.a, p.b, p.b2);
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
       a.cache = p.cache;

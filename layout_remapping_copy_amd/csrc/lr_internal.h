@@ -64,6 +64,7 @@ struct Plan {
   int rank;           // joint modes (after fusion)
   JMode m[kMaxJoint];
   int a, b;           // src-contiguous / dst-contiguous modes, -1 if none
+  int b2;             // transpose: mode continuing b in dst (b grouped with it), -1 if none
   Swz sw_s, sw_d;     // swizzles in units of (fused) elements
   int block;
   int64_t tile_a, tile_b;

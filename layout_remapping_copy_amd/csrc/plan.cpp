@@ -155,7 +155,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     return LR_ERR_ELEM_BYTES;
   if (src_cap < 0 || dst_cap < 0) return LR_ERR_INVALID;
   std::memset(p, 0, sizeof(*p));
-  p->a = p->b = -1;
+  p->a = p->b = p->b2 = -1;
   const int64_t n = size_of(Ls);
   if (size_of(Ld) != n) return LR_ERR_SIZE_MISMATCH;
   const int64_t cos_s = cosize_bound(Ls), cos_d = cosize_bound(Ld);
@@ -307,29 +307,49 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     if (forced == LR_PATH_INTERLEAVE) return LR_ERR_PATH;
   }
 
-  // transpose: register blocks of V x V elements, tiles of 16V x 16V
+  // transpose: register blocks of V x V elements over the src-contiguous mode a and
+  // the dst-contiguous run b.  When the dst-contiguous mode is short (a power of
+  // two under 16 bytes) and another mode b2 continues it in dst (dst stride equal
+  // to b's extent), the pair acts as one b of extent ext_b * ext_b2 whose source
+  // row offsets split over the two modes (a three-way remap such as head pairs
+  // interleaved inside column-major tiles).
   const bool want_t = forced < 0 || forced == LR_PATH_TRANSPOSE || forced == LR_PATH_TRANSPOSE_DIRECT;
   if (a >= 0 && b >= 0 && a != b && want_t) {
+    int b2 = -1;
+    if (is_pow2(p->m[b].ext) && p->m[b].ext * p->eb < 16)
+      for (int k = 0; k < p->rank && b2 < 0; ++k)
+        if (k != a && k != b && p->m[k].sd == p->m[b].ext) b2 = k;
+    const int64_t ext_b = p->m[b].ext * (b2 >= 0 ? p->m[b2].ext : 1);
+    auto strides_ok = [&](int64_t V) {
+      for (int k = 0; k < p->rank; ++k) {
+        if (k != a && p->m[k].ss % V) return false;
+        if (k != b && k != b2 && p->m[k].sd % V) return false;
+      }
+      return true;
+    };
     int64_t V = V16;
     while (V > 1) {
-      bool ok = p->m[a].ext % V == 0 && p->m[b].ext % V == 0 && batch_ok(V, V, a, b) && swz_keeps(p->sw_s, V) &&
+      bool ok = p->m[a].ext % V == 0 && ext_b % V == 0 && strides_ok(V) && swz_keeps(p->sw_s, V) &&
                 swz_keeps(p->sw_d, V) && src_align % (size_t)(V * p->eb) == 0 &&
                 dst_align % (size_t)(V * p->eb) == 0;
       if (ok) break;
       V >>= 1;
     }
-    const bool long_b = p->m[b].ext * p->eb > 16 && p->m[a].ext * p->eb > 16;
+    const bool long_b = ext_b * p->eb > 16 && p->m[a].ext * p->eb > 16;
     if (long_b || forced >= 0) {
       p->path = forced == LR_PATH_TRANSPOSE_DIRECT ? LR_PATH_TRANSPOSE_DIRECT : LR_PATH_TRANSPOSE;
       if (forced < 0 && env_flag("LR_TRANSPOSE_DIRECT")) p->path = LR_PATH_TRANSPOSE_DIRECT;
       p->a = a;
       p->b = b;
+      p->b2 = b2;
       p->v = (int)V;
+      // source distance between nearby b rows
+      const int64_t pitch = (b2 >= 0 ? std::min(p->m[b].ss, p->m[b2].ss) : p->m[b].ss) * p->eb;
       // tile shape in 16-byte chunks (a x b): wider tiles only for full chunks on
       // the LDS variant.  With large source pitches (rows far apart on both sides)
       // 32 x 16 chunks (512-byte source runs per row) measured fastest; with close
       // source rows the 16 x 16 tile did.
-      const bool far_rows = p->m[b].ss * p->eb > 2048;
+      const bool far_rows = pitch > 2048;
       const bool wide_ok = V * p->eb == 16 && V <= 8 && p->path == LR_PATH_TRANSPOSE;
       p->tshape = (far_rows && wide_ok) ? 1 : 0;
       const uint32_t shp = env_u32("LR_TSHAPE", 99);
@@ -343,18 +363,16 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // (large pitches such as a square transpose's 16 KiB rows) a diagonal order
       // keeps the workgroups in flight from sharing one column offset, which with
       // power-of-two pitches concentrates them on a few HBM channels.
-      p->torder = (p->m[b].ss * p->eb <= 2048) ? 1u : 2u;
+      p->torder = far_rows ? 2u : 1u;
       const uint32_t tord = env_u32("LR_TORDER", 99);
       if (tord <= 3) p->torder = tord;
-      {
-        const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
-        const int64_t ntb = (p->m[b].ext + p->tile_b - 1) / p->tile_b;
-        if (p->torder == 3 && (nta % 4 || ntb % 4)) p->torder = 2;  // grouped order needs 4 | tiles
-      }
+      const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
+      const int64_t ntb = (ext_b + p->tile_b - 1) / p->tile_b;
+      if (p->torder == 3 && (nta % 4 || ntb % 4)) p->torder = 2;  // grouped order needs 4 | tiles
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
-        if (k != a && k != b) batch *= p->m[k].ext;
-      p->grid = ((p->m[a].ext + p->tile_a - 1) / p->tile_a) * ((p->m[b].ext + p->tile_b - 1) / p->tile_b) * batch;
+        if (k != a && k != b && k != b2) batch *= p->m[k].ext;
+      p->grid = nta * ntb * batch;
       return LR_OK;
     }
   }
@@ -460,18 +478,25 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
     case LR_PATH_TRANSPOSE:
     case LR_PATH_TRANSPOSE_DIRECT: {
       if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
+      if (p.b2 >= p.rank || p.b2 == p.a || p.b2 == p.b) return bad();
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1) return bad();
-      if (p.m[p.a].ext % v || p.m[p.b].ext % v) return bad();
+      int64_t ext_b = p.m[p.b].ext;
+      if (p.b2 >= 0) {
+        const int64_t e0 = p.m[p.b].ext;
+        if ((e0 & (e0 - 1)) || p.m[p.b2].sd != e0) return bad();
+        ext_b *= p.m[p.b2].ext;
+      }
+      if (p.m[p.a].ext % v || ext_b % v) return bad();
       if (p.tshape < 0 || p.tshape >= kTileShapes ||
           (p.tshape != 0 && (v * p.eb != 16 || v > 8 || p.path != LR_PATH_TRANSPOSE)))
         return bad();
       if (p.torder > 3) return bad();
-      if (p.torder == 3 && ((p.m[p.a].ext + p.tile_a - 1) / p.tile_a % 4 || (p.m[p.b].ext + p.tile_b - 1) / p.tile_b % 4))
-        return bad();
       if (p.tile_a != kTileTA[p.tshape] * v || p.tile_b != kTileTB[p.tshape] * v) return bad();
+      if (p.torder == 3 && ((p.m[p.a].ext + p.tile_a - 1) / p.tile_a % 4 || (ext_b + p.tile_b - 1) / p.tile_b % 4))
+        return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
-        if (k != p.b && p.m[k].sd % v) return bad();
+        if (k != p.b && k != p.b2 && p.m[k].sd % v) return bad();
       }
       return LR_OK;
     }
@@ -533,6 +558,7 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   out->joint_rank = p.rank;
   out->a_mode = p.a;
   out->b_mode = p.b;
+  out->b2_mode = p.b2;
   out->block = p.block;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;

@@ -37,6 +37,14 @@ def interleave(src: np.ndarray, b: int, h: int, s: int, d: int) -> np.ndarray:
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
 
 
+def interleave_cm(src: np.ndarray, b: int, h: int, s: int, d: int) -> np.ndarray:
+    """(b,h,s,d) contiguous -> dst[b][hp][d][s][hl] = src[b][2*hp + hl][s][d]: head
+    pairs adjacent, (s, d) column-major inside a pair ([print_layout page, section
+    4.2], its prose example read literally)."""
+    x = src.view(np.uint16).reshape(b, h // 2, 2, s, d).transpose(0, 1, 4, 3, 2)
+    return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
+
+
 def nhwc2nchw(src: np.ndarray, n: int, h: int, w: int, c: int) -> np.ndarray:
     x = src.view(np.uint16).reshape(n, h, w, c).transpose(0, 3, 1, 2)
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)

@@ -181,7 +181,7 @@ ALL_PATHS = [lr.PATH_GENERIC, lr.PATH_VECTOR, lr.PATH_TRANSPOSE, lr.PATH_TRANSPO
 def _case_pairs():
     """Layout pairs (src, dst, src_elems, dst_elems, eb) that admit the various paths."""
     cases = []
-    for name in ["transpose", "retile", "interleave", "nhwc2nchw", "padtiles"]:
+    for name in ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles"]:
         w = W.small(name)
         cases.append((w.src_layout, w.dst_layout, w.src_elems, w.dst_elems, w.elem_bytes))
     # transposes at every element size, ragged tile edges
@@ -332,12 +332,13 @@ FORMS = {
     "transpose": lambda s: F.transpose(s, 8192),
     "retile": lambda s: F.retile(s, 4096),
     "interleave": lambda s: F.interleave(s, 16, 32, 4096, 128),
+    "interleave_cm": lambda s: F.interleave_cm(s, 16, 32, 4096, 128),
     "nhwc2nchw": lambda s: F.nhwc2nchw(s, 128, 56, 56, 256),
     "padtiles": lambda s: F.padtiles(s, 1 << 20),
 }
 
-FULL_PATH = {"transpose": "transpose", "retile": "vector", "interleave": "interleave", "nhwc2nchw": "transpose",
-             "padtiles": "staged"}
+FULL_PATH = {"transpose": "transpose", "retile": "vector", "interleave": "interleave", "interleave_cm": "transpose",
+             "nhwc2nchw": "transpose", "padtiles": "staged"}
 
 
 @pytest.mark.slow

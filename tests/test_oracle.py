@@ -384,13 +384,14 @@ JOINT_FULL = {
     "transpose": [(8192, 8192, 1), (8192, 1, 8192)],
     "retile": [(64, 1, 1), (128, 4096, 64), (64, 64, 8192), (32, 524288, 524288)],
     "interleave": [(2, 524288, 1), (524288, 1, 2), (256, 1048576, 1048576)],
+    "interleave_cm": [(2, 524288, 1), (4096, 128, 2), (128, 1, 8192), (256, 1048576, 1048576)],
     "nhwc2nchw": [(3136, 256, 1), (256, 1, 3136), (128, 802816, 802816)],
     "padtiles": [(4, 18, 1), (8, 1, 4), (2, 9, 32), (1048576, 72, 64)],
     "tile8x8": [(8, 1, 1), (8, 8, 8)],  # dst (8,8) refinement, aliased: not used
 }
 
 
-@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "nhwc2nchw", "padtiles"])
+@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles"])
 def test_joint_flat_of_workloads(name):
     w = W.full(name)
     got = O.joint_flat(O.parse(w.src_layout), O.parse(w.dst_layout), sort_by_dst=True)
@@ -605,6 +606,7 @@ def test_forms_equal_oracle_copy():
         "transpose": lambda s: F.transpose(s, 520),
         "retile": lambda s: F.retile(s, 512),
         "interleave": lambda s: F.interleave(s, 2, 4, 72, 128),
+        "interleave_cm": lambda s: F.interleave_cm(s, 2, 4, 72, 136),
         "nhwc2nchw": lambda s: F.nhwc2nchw(s, 3, 7, 9, 40),
         "padtiles": lambda s: F.padtiles(s, 1000),
     }

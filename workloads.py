@@ -13,6 +13,8 @@ The five workloads (names follow the sizes they carry):
 * ``retile``      bf16 4096x4096 row-major -> 128x64 tiles in row-major tile order,
                   row-major inside a tile with Swizzle<3,3,3>.
 * ``interleave``  bf16 (16,32,4096,128) contiguous -> heads paired at stride 1.
+* ``interleave_cm`` the same tensor -> head pairs at stride 1 inside column-major
+                  (s, d) tiles (the other reading of the interleaved layout).
 * ``nhwc2nchw``   fp16 NHWC (128,56,56,256) -> NCHW.
 * ``padtiles``    2**20 padded 8x8 fp32 tiles, source (8,8):(1,9) per tile read in
                   thread-value order ((4,8),2):((16,1),8), destination compact.
@@ -148,6 +150,19 @@ def interleave(b: int = 16, h: int = 32, s: int = 4096, d: int = 128) -> Workloa
         n_elems=b * h * sd)
 
 
+def interleave_cm(b: int = 16, h: int = 32, s: int = 4096, d: int = 128) -> Workload:
+    # the column-major-inside reading of the interleaved pair: within a head pair,
+    # (s, d) is stored column-major with the two heads adjacent, i.e. offset
+    # 2*(s + S*d) + hl; logical (b, h, s, d) with h = hl + 2*hp
+    sd = s * d
+    return Workload(
+        name=f"interleave_cm{b}x{h}x{s}x{d}", elem_bytes=2,
+        src_layout=f"({b},{h},{s},{d}):({h * sd},{sd},{d},1)",
+        dst_layout=f"({b},(2,{h // 2}),{s},{d}):({h * sd},(1,{2 * sd}),2,{2 * s})",
+        src_elems=b * h * sd, dst_elems=b * h * sd, seed=7, values="normal_bf16",
+        n_elems=b * h * sd)
+
+
 def nhwc2nchw(n: int = 128, h: int = 56, w: int = 56, c: int = 256) -> Workload:
     hw = h * w
     return Workload(
@@ -174,6 +189,7 @@ FULL = {
     "transpose": transpose,
     "retile": retile,
     "interleave": interleave,
+    "interleave_cm": interleave_cm,
     "nhwc2nchw": nhwc2nchw,
     "padtiles": padtiles,
 }
@@ -186,6 +202,7 @@ def small(name: str) -> Workload:
         "transpose": lambda: transpose(520),
         "retile": lambda: retile(512),
         "interleave": lambda: interleave(2, 4, 72, 128),
+        "interleave_cm": lambda: interleave_cm(2, 4, 72, 136),
         "nhwc2nchw": lambda: nhwc2nchw(3, 7, 9, 40),
         "padtiles": lambda: padtiles(1000),
     }[name]()

@@ -147,6 +147,30 @@ int lr_right_inverse(const lr_layout* in, lr_layout* out);
  * n_m, else LR_ERR_NOT_REPRESENTABLE. */
 int lr_zipped_divide(const lr_layout* in, const int64_t* tiler, int32_t ntiler, lr_layout* out);
 
+/* Complement of A up to size M ([CuTe algebra page, section 3.2]: what a tile
+ * leaves over): with A's leaves of extent > 1 and stride > 0 sorted by stride,
+ * each stride must be a multiple of the previous leaf's extent * stride
+ * (LR_ERR_NOT_REPRESENTABLE otherwise); the result is (d_0 : 1),
+ * (d_{i+1}/(n_i d_i) : n_i d_i)..., (ceil(M/(n_k d_k)) : n_k d_k), coalesced, one
+ * leaf per top-level mode.  (A, complement(A, M)) is then a bijection onto a
+ * prefix [0, M') with M' >= M.  A swizzled A gives LR_ERR_NOT_REPRESENTABLE; M >= 1. */
+int lr_complement(const lr_layout* A, int64_t M, lr_layout* out);
+
+/* logical_divide(A, B) = A o (B, complement(B, size(A))): top-level mode 0 is the
+ * tile B selects from A, mode 1 enumerates the tiles (CuTe algebra page, section
+ * 3.2).  B must be unswizzled; composition rules as lr_composition. */
+int lr_logical_divide(const lr_layout* A, const lr_layout* B, lr_layout* out);
+
+/* logical_product(A, B) = (A, complement(A, size(A)*cosize(B)) o B): mode 0 is A,
+ * mode 1 places one copy of A at each position B describes.  Unswizzled A and B. */
+int lr_logical_product(const lr_layout* A, const lr_layout* B, lr_layout* out);
+
+/* blocked_product(A, B): the logical product regrouped mode by mode, top-level
+ * mode i = (A's mode i, the copies' mode i) -- [CuTe algebra page, section 4.1]: a
+ * 4x8 block over a 2x5 grid gives a "4x2, 8x5" layout.  A and B need the same
+ * number of top-level modes (LR_ERR_INVALID otherwise). */
+int lr_blocked_product(const lr_layout* A, const lr_layout* B, lr_layout* out);
+
 /* Injectivity of L as a function of the 1-D index: exact (a bitmap over the
  * offsets) when size <= 2^20; above that the sufficient test "sorted by stride,
  * each stride exceeds the largest offset of the smaller ones" (*result 0 then

@@ -21,7 +21,9 @@ from .binding import (  # noqa: F401
     Layout,
     LayoutRemapError,
     LibraryNotBuilt,
+    blocked_product,
     coalesce,
+    complement,
     composition,
     copy_plan,
     header_symbols,
@@ -30,6 +32,8 @@ from .binding import (  # noqa: F401
     layout_eval,
     layout_eval_coords,
     lib,
+    logical_divide,
+    logical_product,
     max_common_vector,
     parse,
     right_inverse,

@@ -110,6 +110,10 @@ _SIGS = {
     "lr_composition": (ctypes.c_int, [_L, _L, _L]),
     "lr_right_inverse": (ctypes.c_int, [_L, _L]),
     "lr_zipped_divide": (ctypes.c_int, [_L, _P(ctypes.c_int64), ctypes.c_int32, _L]),
+    "lr_complement": (ctypes.c_int, [_L, ctypes.c_int64, _L]),
+    "lr_logical_divide": (ctypes.c_int, [_L, _L, _L]),
+    "lr_logical_product": (ctypes.c_int, [_L, _L, _L]),
+    "lr_blocked_product": (ctypes.c_int, [_L, _L, _L]),
     "lr_is_injective": (ctypes.c_int, [_L, _P(ctypes.c_int32)]),
     "lr_max_common_vector": (ctypes.c_int, [_L, _L, ctypes.c_size_t, _P(ctypes.c_int64)]),
     "lr_thread_map": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _L]),
@@ -245,6 +249,31 @@ def zipped_divide(L, tiler: Sequence[int]) -> Layout:
     _check(lib().lr_zipped_divide(ctypes.byref(_as_layout(L).c), arr, len(tiler), ctypes.byref(out)),
            "zipped_divide")
     return Layout(out)
+
+
+def complement(A, M: int) -> Layout:
+    out = lr_layout()
+    _check(lib().lr_complement(ctypes.byref(_as_layout(A).c), M, ctypes.byref(out)), "complement")
+    return Layout(out)
+
+
+def _binary(name: str, A, B) -> Layout:
+    out = lr_layout()
+    _check(getattr(lib(), name)(ctypes.byref(_as_layout(A).c), ctypes.byref(_as_layout(B).c), ctypes.byref(out)),
+           name)
+    return Layout(out)
+
+
+def logical_divide(A, B) -> Layout:
+    return _binary("lr_logical_divide", A, B)
+
+
+def logical_product(A, B) -> Layout:
+    return _binary("lr_logical_product", A, B)
+
+
+def blocked_product(A, B) -> Layout:
+    return _binary("lr_blocked_product", A, B)
 
 
 def is_injective(L) -> bool:

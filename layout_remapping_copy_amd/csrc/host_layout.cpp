@@ -389,6 +389,53 @@ static std::string format_impl(const lr_layout* L) {
   return o;
 }
 
+// ---------------------------------------------------------------- complement,
+// logical divide and products ([CuTe algebra page, section 3.2]: tiles and the
+// rest; [section 4.1]: a tile repeated over a grid)
+
+// Leaves of the positions A leaves out up to size M (A unswizzled, strides nested).
+static int complement_leaves(const lr_layout* A, int64_t M, std::vector<Leaf>* out) {
+  std::vector<Leaf> lv;
+  for (int i = 0; i < A->nleaves; ++i)
+    if (A->shape[i] > 1 && A->stride[i] > 0) lv.push_back({A->shape[i], A->stride[i]});
+  std::sort(lv.begin(), lv.end(), [](const Leaf& x, const Leaf& y) { return x.d < y.d || (x.d == y.d && x.n < y.n); });
+  std::vector<Leaf> res;
+  int64_t cur = 1;
+  for (const Leaf& l : lv) {
+    if (l.d % cur) return LR_ERR_NOT_REPRESENTABLE;
+    res.push_back({l.d / cur, cur});
+    if (!mul_ok(l.n, l.d, &cur)) return LR_ERR_OVERFLOW;
+  }
+  res.push_back({(M + cur - 1) / cur, cur});
+  *out = coalesce_leaves(res);
+  if (out->empty()) out->push_back({1, 0});
+  return LR_OK;
+}
+
+// Two top-level modes: all leaves of x, then all leaves of y.
+static int concat2(const std::vector<Leaf>& x, const std::vector<Leaf>& y, lr_layout* out) {
+  if (x.size() + y.size() > LR_MAX_LEAVES) return LR_ERR_NOT_REPRESENTABLE;
+  std::vector<Leaf> all = x;
+  all.insert(all.end(), y.begin(), y.end());
+  std::vector<int> ends{(int)x.size(), (int)all.size()};
+  set_leaves(out, all, ends, 0, 0, 0);
+  return LR_OK;
+}
+
+static int logical_product_impl(const lr_layout* A, const lr_layout* B, lr_layout* rep) {
+  if (A->swz_b > 0 || B->swz_b > 0) return LR_ERR_NOT_REPRESENTABLE;
+  int64_t m;
+  if (!mul_ok(size_of(A), max_linear_offset(B) + 1, &m)) return LR_ERR_OVERFLOW;
+  std::vector<Leaf> c;
+  int rc = complement_leaves(A, m, &c);
+  if (rc) return rc;
+  lr_layout C;
+  std::vector<int> ends;
+  for (size_t i = 0; i < c.size(); ++i) ends.push_back((int)i + 1);
+  set_leaves(&C, c, ends, 0, 0, 0);
+  return compose_impl(&C, B, rep);  // B's top-level modes, repeated A's footprint
+}
+
 }  // namespace lr
 
 using namespace lr;
@@ -513,6 +560,64 @@ int lr_zipped_divide(const lr_layout* in, const int64_t* tiler, int32_t ntiler, 
   if ((int)all.size() > LR_MAX_LEAVES) return LR_ERR_NOT_REPRESENTABLE;
   std::vector<int> ends{(int)tiles.size(), (int)all.size()};
   set_leaves(out, all, ends, in->swz_b, in->swz_m, in->swz_s);
+  return LR_OK;
+}
+
+int lr_complement(const lr_layout* A, int64_t M, lr_layout* out) {
+  int rc = validate(A);
+  if (rc) return rc;
+  if (!out || M < 1) return LR_ERR_INVALID;
+  if (A->swz_b > 0) return LR_ERR_NOT_REPRESENTABLE;
+  std::vector<Leaf> c;
+  if ((rc = complement_leaves(A, M, &c))) return rc;
+  return emit_flat(out, c, 0, 0, 0);
+}
+
+int lr_logical_divide(const lr_layout* A, const lr_layout* B, lr_layout* out) {
+  int rc;
+  if ((rc = validate(A)) || (rc = validate(B))) return rc;
+  if (!out) return LR_ERR_INVALID;
+  if (B->swz_b > 0) return LR_ERR_NOT_REPRESENTABLE;
+  std::vector<Leaf> c;
+  if ((rc = complement_leaves(B, size_of(A), &c))) return rc;
+  lr_layout D;
+  if ((rc = concat2(leaves_of(B, 0, B->nleaves), c, &D))) return rc;
+  lr_layout tmp;
+  if ((rc = compose_impl(A, &D, &tmp))) return rc;
+  *out = tmp;
+  return LR_OK;
+}
+
+int lr_logical_product(const lr_layout* A, const lr_layout* B, lr_layout* out) {
+  int rc;
+  if ((rc = validate(A)) || (rc = validate(B))) return rc;
+  if (!out) return LR_ERR_INVALID;
+  lr_layout rep;
+  if ((rc = logical_product_impl(A, B, &rep))) return rc;
+  lr_layout tmp;
+  if ((rc = concat2(leaves_of(A, 0, A->nleaves), leaves_of(&rep, 0, rep.nleaves), &tmp))) return rc;
+  *out = tmp;
+  return LR_OK;
+}
+
+int lr_blocked_product(const lr_layout* A, const lr_layout* B, lr_layout* out) {
+  int rc;
+  if ((rc = validate(A)) || (rc = validate(B))) return rc;
+  if (!out || A->nmodes != B->nmodes) return LR_ERR_INVALID;
+  lr_layout rep;
+  if ((rc = logical_product_impl(A, B, &rep))) return rc;
+  if (A->nleaves + rep.nleaves > LR_MAX_LEAVES) return LR_ERR_NOT_REPRESENTABLE;
+  std::vector<Leaf> all;
+  std::vector<int> ends;
+  int la = 0, lb = 0;
+  for (int m = 0; m < A->nmodes; ++m) {  // mode m: A's mode m, then the repeats' mode m
+    for (; la < A->mode_end[m]; ++la) all.push_back({A->shape[la], A->stride[la]});
+    for (; lb < rep.mode_end[m]; ++lb) all.push_back({rep.shape[lb], rep.stride[lb]});
+    ends.push_back((int)all.size());
+  }
+  lr_layout tmp;
+  set_leaves(&tmp, all, ends, 0, 0, 0);
+  *out = tmp;
   return LR_OK;
 }
 

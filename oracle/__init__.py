@@ -41,6 +41,10 @@ from .layout import (  # noqa: F401
     right_inverse,
     right_inverse_fn,
     zipped_divide,
+    complement,
+    logical_divide,
+    logical_product,
+    blocked_product,
     is_injective,
     is_injective_bruteforce,
     injective_sufficient,

@@ -512,6 +512,63 @@ def zipped_divide(L: Layout, tiler: Sequence[int]) -> Layout:
 
 
 # ----------------------------------------------------------------------------
+# Complement, logical divide and products.  [CuTe algebra page, section 3.2]:
+# dividing a layout into tiles and what is left over; [section 4.1]: a tile
+# repeated over a grid with blocked_product (a 4x8 block over a 2x5 grid gives
+# the "4x2, 8x5" layout).
+# ----------------------------------------------------------------------------
+def complement(A: Layout, M: int) -> Layout:
+    """The layout of the positions A leaves out, up to size M: with A's leaves
+    (n_i : d_i) of extent > 1 and stride > 0 sorted by stride, each d_{i+1} must be
+    a multiple of n_i*d_i; the result is (d_0 : 1), (d_{i+1} / (n_i d_i) : n_i d_i)...,
+    (ceil(M / (n_k d_k)) : n_k d_k), extent-1 leaves dropped, coalesced.  Then the
+    concatenation (A, complement) is a bijection onto [0, multiple of n_k d_k >= M)."""
+    if A.swz is not None:
+        raise NotRepresentable("swizzled layout")
+    leaves = sorted(((d, n) for n, d in flatten(A) if n > 1 and d > 0))
+    out = []
+    cur = 1  # stride reached so far (product n_i d_i of the last leaf)
+    for d, n in leaves:
+        if d % cur:
+            raise NotRepresentable("strides are not nested")
+        out.append((d // cur, cur))
+        cur = n * d
+    out.append((-(-M // cur), cur))
+    return _from_leaves(_coalesce_leaves(out))
+
+
+def _concat(A: Layout, B: Layout) -> Layout:
+    return Layout((A.shape, B.shape), (A.stride, B.stride))
+
+
+def logical_divide(A: Layout, B: Layout) -> Layout:
+    """A o (B, complement(B, size(A))): mode 0 is the tile B picks out of A, mode 1
+    enumerates the tiles."""
+    return compose(A, _concat(B, complement(B, size(A))))
+
+
+def logical_product(A: Layout, B: Layout) -> Layout:
+    """(A, complement(A, size(A) * cosize(B)) o B): A repeated as B says."""
+    C = complement(A, size(A) * cosize(B))
+    return _concat(A, compose(C, B))
+
+
+def blocked_product(A: Layout, B: Layout) -> Layout:
+    """logical_product regrouped mode by mode: top-level mode i of the result is
+    (mode i of A, mode i of the repeated B).  A and B need the same number of
+    top-level modes."""
+    ma, mb = top_modes(A), top_modes(B)
+    if len(ma) != len(mb):
+        raise ValueError("blocked_product needs layouts with the same number of modes")
+    rep = logical_product(A, B)
+    reps = top_modes(Layout(rep.shape[1], rep.stride[1]))
+    if len(mb) == 1:
+        reps = [Layout(rep.shape[1], rep.stride[1])]
+    return Layout(tuple((x.shape, y.shape) for x, y in zip(ma, reps)),
+                  tuple((x.stride, y.stride) for x, y in zip(ma, reps)))
+
+
+# ----------------------------------------------------------------------------
 # Injectivity
 # ----------------------------------------------------------------------------
 BRUTE_INJECTIVE_LIMIT = 1 << 20

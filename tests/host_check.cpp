@@ -136,6 +136,10 @@ static int run_fuzz() {
     lr_zipped_divide(&a, tiler, a.nmodes < 2 ? a.nmodes : 2, &r);
     int32_t inj;
     lr_is_injective(&a, &inj);
+    lr_complement(&a, 1 + (int64_t)(rng() % 100), &r);
+    lr_logical_divide(&a, &b, &r);
+    lr_logical_product(&a, &b, &r);
+    lr_blocked_product(&a, &b, &r);
     int64_t v;
     lr_max_common_vector(&a, &b, 4, &v);
     lr_plan p;

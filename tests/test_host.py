@@ -156,6 +156,51 @@ def test_zipped_divide_matches_oracle():
         lr.zipped_divide("(6,4):(1,6)", (4,))
 
 
+def _nested_text(rng):
+    n = rng.randint(1, 3)
+    leaves, cur = [], 1
+    for _ in range(n):
+        d = cur * rng.choice([1, 1, 2, 3])
+        e = rng.randint(2, 4)
+        leaves.append((e, d))
+        cur = e * d
+    rng.shuffle(leaves)
+    if n == 1:
+        return f"{leaves[0][0]}:{leaves[0][1]}"
+    return "(" + ",".join(str(e) for e, _ in leaves) + "):(" + ",".join(str(d) for _, d in leaves) + ")"
+
+
+def test_complement_divide_products_match_oracle():
+    assert str(lr.complement("(4,8):(1,4)", 64)) == "2:32"
+    assert str(lr.logical_divide("24:1", "4:2")) == "(4,(2,3)):(2,(1,8))"
+    assert str(lr.blocked_product("(4,8):(1,4)", "(2,5):(1,2)")) == "((4,2),(8,5)):((1,32),(4,64))"
+    rng = random.Random(71)
+    counts = [0, 0, 0, 0]
+    for _ in range(1500):
+        ta, tb = _nested_text(rng), _nested_text(rng)
+        A, B = O.parse(ta), O.parse(tb)
+        M = O.cosize(A) * rng.randint(1, 3) + rng.randint(0, 4)
+        for i, (fo, fc) in enumerate([(lambda: O.complement(A, M), lambda: lr.complement(ta, M)),
+                                      (lambda: O.logical_divide(O.Layout(O.cosize(B) * 2, 1), B),
+                                       lambda: lr.logical_divide(f"{O.cosize(B) * 2}:1", tb)),
+                                      (lambda: O.logical_product(A, B), lambda: lr.logical_product(ta, tb)),
+                                      (lambda: O.blocked_product(A, B), lambda: lr.blocked_product(ta, tb))]):
+            try:
+                want = fo()
+            except (OL.NotRepresentable, ValueError):
+                want = None
+            try:
+                got = fc()
+            except lr.LayoutRemapError as e:
+                assert e.code in (lr.binding.ERR_NOT_REPRESENTABLE, lr.binding.ERR_INVALID)
+                got = None
+            assert (got is None) == (want is None), (i, ta, tb)
+            if got is not None:
+                counts[i] += 1
+                assert got.leaves == O.flatten(want), (i, ta, tb, str(got), O.fmt(want))
+    assert min(counts) > 100, counts
+
+
 def test_is_injective_matches_oracle():
     assert not lr.is_injective("((4,2),(2,4)):((2,16),(1,8))")
     assert lr.is_injective("(4,2,2):(8,2,1)")

@@ -614,3 +614,99 @@ def test_forms_equal_oracle_copy():
         w = W.small(name)
         src, out = _run(w)
         assert np.array_equal(form(src), out), name
+
+
+# ---------------------------------------------------------------------------
+# Complement, logical divide and products
+# ---------------------------------------------------------------------------
+def test_blocked_product_golden_shape():
+    kv = {}
+    with open(os.path.join(GOLDEN, "blocked_product.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k] = v.strip()
+    R = O.blocked_product(O.parse(kv["tile"]), O.parse(kv["grid"]))
+    assert O.fmt(R).split(":")[0] == kv["shape"]
+    # every block position holds one whole copy of the tile, tiles laid out compactly
+    offs = sorted(O.eval_indices(R, np.arange(O.size(R))).tolist())
+    assert offs == list(range(320))
+    for i in range(4):
+        for j in range(8):
+            assert O.eval_coord(R, ((i, 0), (j, 0))) == O.eval_coord(O.parse(kv["tile"]), (i, j))
+
+
+def _nested_layout(rng):
+    """Random injective layout whose leaves, sorted by stride, are disjoint and nested."""
+    n = rng.randint(1, 3)
+    leaves, cur = [], 1
+    for _ in range(n):
+        gap = rng.choice([1, 1, 2, 3])
+        d = cur * gap
+        e = rng.randint(2, 4)
+        leaves.append((e, d))
+        cur = e * d
+    rng.shuffle(leaves)
+    return O.Layout(tuple(e for e, _ in leaves), tuple(d for _, d in leaves)) if n > 1 else O.Layout(*leaves[0])
+
+
+def test_complement_fills_the_gaps():
+    rng = random.Random(61)
+    assert O.fmt(O.complement(O.parse("(4,8):(1,4)"), 64)) == "2:32"
+    assert O.fmt(O.complement(O.parse("4:2"), 24)) == "(2,3):(1,8)"
+    for _ in range(500):
+        A = _nested_layout(rng)
+        M = O.cosize(A) * rng.randint(1, 3) + rng.randint(0, 5)
+        C = O.complement(A, M)
+        cat = O.Layout((A.shape, C.shape), (A.stride, C.stride))
+        offs = sorted(O.eval_indices(cat, np.arange(O.size(cat))).tolist())
+        assert offs == list(range(len(offs))), (A, M)  # a bijection onto a prefix
+        assert len(offs) >= M
+    with pytest.raises(OL.NotRepresentable):
+        O.complement(O.parse("(2,2):(1,3)"), 12)  # 3 is not a multiple of 2*1
+
+
+def test_logical_divide_rearranges():
+    rng = random.Random(62)
+    assert O.fmt(O.logical_divide(O.parse("24:1"), O.parse("4:2"))) == "(4,(2,3)):(2,(1,8))"
+    hits = 0
+    for _ in range(500):
+        B = _nested_layout(rng)
+        A = O.Layout(O.cosize(B) * rng.randint(1, 3), rng.choice([1, 2]))
+        try:
+            R = O.logical_divide(A, B)
+        except OL.NotRepresentable:
+            continue
+        hits += 1
+        if O.size(R) == O.size(A):  # the tiles and the rest cover A exactly once
+            assert sorted(O.eval_indices(R, np.arange(O.size(R))).tolist()) == \
+                sorted(O.eval_indices(A, np.arange(O.size(A))).tolist())
+        tile = O.Layout(R.shape[0], R.stride[0])
+        assert np.array_equal(O.eval_indices(tile, np.arange(O.size(B))), O.compose_table(A, B))
+    assert hits > 300
+
+
+def test_logical_product_repeats():
+    rng = random.Random(63)
+    hits = 0
+    for _ in range(300):
+        A, B = _nested_layout(rng), _nested_layout(rng)
+        try:
+            R = O.logical_product(A, B)
+        except OL.NotRepresentable:
+            continue
+        hits += 1
+        assert O.Layout(R.shape[0], R.stride[0]) == A
+        assert O.is_injective_bruteforce(R)
+        # repetition r of A sits at an offset that A itself never reaches
+        k = np.arange(O.size(R))
+        offs = O.eval_indices(R, k)
+        first = offs[: O.size(A)]
+        for r in range(1, O.size(B)):
+            rep = offs[r * O.size(A):(r + 1) * O.size(A)]
+            assert not set(rep.tolist()) & set(first.tolist())
+        BP_ok = len(O.top_modes(A)) == len(O.top_modes(B))
+        if BP_ok:
+            P = O.blocked_product(A, B)
+            assert sorted(O.eval_indices(P, k).tolist()) == sorted(offs.tolist())
+    assert hits > 100

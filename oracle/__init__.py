@@ -57,5 +57,7 @@ from .layout import (  # noqa: F401
     copy,
     copy_sampled_check,
     print_layout,
+    bank_ways,
+    lines_touched,
     layout_grid,
 )

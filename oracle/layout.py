@@ -293,6 +293,34 @@ def print_layout(L: Layout) -> str:
 
 
 # ----------------------------------------------------------------------------
+# Access-pattern checks.  [print_layout page, sections 4.3, 5.2 and 6.4]: shared
+# memory is split into banks, accesses by one warp to different addresses in the
+# same bank are serialised (the same address is broadcast), padding a row by one
+# element or an XOR swizzle spreads a column over the banks; adjacent threads
+# should touch adjacent addresses so a warp's accesses fall in few cache lines.
+# Lane t accesses element L(t) (elem_bytes bytes).
+# ----------------------------------------------------------------------------
+def bank_ways(L: Layout, elem_bytes: int, lanes: int = 32, banks: int = 32, bank_bytes: int = 4) -> int:
+    """Largest number of distinct bank words one bank must serve for the access
+    of lanes 0..lanes-1 (1 means conflict-free)."""
+    per_bank = {}
+    for t in range(lanes):
+        a = eval_index(L, t) * elem_bytes
+        for w in range(a // bank_bytes, (a + elem_bytes - 1) // bank_bytes + 1):
+            per_bank.setdefault(w % banks, set()).add(w)
+    return max(len(v) for v in per_bank.values())
+
+
+def lines_touched(L: Layout, elem_bytes: int, lanes: int = 64, line_bytes: int = 128) -> int:
+    """Distinct cache lines the access of lanes 0..lanes-1 touches."""
+    lines = set()
+    for t in range(lanes):
+        a = eval_index(L, t) * elem_bytes
+        lines.update(range(a // line_bytes, (a + elem_bytes - 1) // line_bytes + 1))
+    return len(lines)
+
+
+# ----------------------------------------------------------------------------
 # Coalesce: the same function of the 1-D index on [0, size) with extent-1 leaves
 # dropped and neighbours merged whenever stride[i+1] == extent[i] * stride[i].
 # ----------------------------------------------------------------------------

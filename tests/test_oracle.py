@@ -710,3 +710,39 @@ def test_logical_product_repeats():
             P = O.blocked_product(A, B)
             assert sorted(O.eval_indices(P, k).tolist()) == sorted(offs.tolist())
     assert hits > 100
+
+
+# ---------------------------------------------------------------------------
+# Access-pattern checks (bank conflicts, cache lines)
+# ---------------------------------------------------------------------------
+def test_bank_conflicts_of_a_column_read():
+    # [print_layout page, section 4.3]: 32 threads reading one column of 8-wide
+    # row-major rows.  The page calls this 32-way; with 32 banks of 4 bytes the rows
+    # are 32 bytes apart, so offsets 8t fall on banks 0, 8, 16, 24: 8-way.
+    col = O.parse("32:8")                                  # thread t -> row t, column 0
+    assert O.bank_ways(col, 4) == 8
+    # [section 5.2]: padding the row to 9 elements spreads the column over all banks
+    assert O.bank_ways(O.parse("32:9"), 4) == 1
+    # [section 4.3]: the XOR swizzle row*8 + (col ^ row) on the same column access
+    sw = O.parse("Sw<3,0,3> o (32,8):(8,1)")
+    assert O.bank_ways(sw, 4) == 4
+    # a row read is conflict-free; the same address is a broadcast, not a conflict
+    assert O.bank_ways(O.parse("32:1"), 4) == 1
+    assert O.bank_ways(O.parse("32:0"), 4) == 1
+
+
+def test_lines_touched():
+    # [print_layout page, section 5.1]: adjacent threads on adjacent addresses
+    assert O.lines_touched(O.parse("64:1"), 4) == 2          # 256 contiguous bytes
+    assert O.lines_touched(O.parse("64:32"), 4) == 64        # one line per thread
+    assert O.lines_touched(O.parse("(8,8):(1,1024)"), 16) == 8  # 8 rows of 128 bytes
+    # brute-force cross-check with a different counting
+    rng = random.Random(81)
+    for _ in range(200):
+        L = _rand_layout(rng, max_stride=40, allow_zero=False)
+        if O.size(L) < 8:
+            continue
+        eb = rng.choice([1, 2, 4, 16])
+        n = min(O.size(L), 64)
+        byts = {O.eval_index(L, t) * eb + i for t in range(n) for i in range(eb)}
+        assert O.lines_touched(L, eb, lanes=n) == len({b // 128 for b in byts})

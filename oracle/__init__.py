@@ -59,5 +59,8 @@ from .layout import (  # noqa: F401
     print_layout,
     bank_ways,
     lines_touched,
+    lds_cycles,
+    access_report,
+    thread_offset_table,
     layout_grid,
 )

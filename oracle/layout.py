@@ -320,6 +320,51 @@ def lines_touched(L: Layout, elem_bytes: int, lanes: int = 64, line_bytes: int =
     return len(lines)
 
 
+def lds_cycles(L: Layout, elem_bytes: int, lanes: int, banks: int, lanes_per_phase: int):
+    """One wavefront access served in phases of lanes_per_phase consecutive lanes;
+    each phase costs the bank_ways of its own lanes.  Returns (cycles, phases,
+    worst ways, distinct words per bank in the first worst phase)."""
+    cycles, worst, hist, phases = 0, 0, None, 0
+    for p in range(0, lanes, lanes_per_phase):
+        per_bank = {}
+        for t in range(p, min(lanes, p + lanes_per_phase)):
+            a = eval_index(L, t) * elem_bytes
+            for w in range(a // 4, (a + elem_bytes - 1) // 4 + 1):
+                per_bank.setdefault(w % banks, set()).add(w)
+        ways = max(len(v) for v in per_bank.values())
+        cycles += ways
+        phases += 1
+        if ways > worst:
+            worst = ways
+            hist = [len(per_bank.get(b, ())) for b in range(banks)]
+    return cycles, phases, worst, hist
+
+
+def access_report(L: Layout, elem_bytes: int, lanes: int, banks: int, lanes_per_phase: int,
+                  line_bytes: int = 128) -> dict:
+    """[print_layout page, section 6.4]: the two checks on a candidate layout, for
+    lane t accessing element L(t): are consecutive lanes on consecutive offsets, and
+    how evenly do the lanes spread over the banks; plus the cache lines touched."""
+    offs = [eval_index(L, t) for t in range(lanes)]
+    cyc, ph, worst, hist = lds_cycles(L, elem_bytes, lanes, banks, lanes_per_phase)
+    gap = next((t for t in range(lanes - 1) if offs[t + 1] != offs[t] + 1), -1)
+    byts = {o * elem_bytes + i for o in offs for i in range(elem_bytes)}
+    return {"offsets": offs, "cycles": cyc, "phases": ph, "ways_max": worst,
+            "conflict_cycles": cyc - ph, "bank_words": hist,
+            "lines": lines_touched(L, elem_bytes, lanes, line_bytes),
+            "min_lines": -(-len(byts) // line_bytes),
+            "adjacent": gap < 0, "first_gap": gap}
+
+
+def thread_offset_table(L: Layout, n: int) -> str:
+    """[ThreadMap page, section 5.3]: the thread-to-offset table, one line per
+    thread, numbers right-aligned to the widest entry."""
+    offs = [eval_index(L, t) for t in range(n)]
+    wt = len(str(n - 1))
+    wo = max(len(str(o)) for o in offs)
+    return "\n".join(f"thread {t:>{wt}} -> offset {o:>{wo}}" for t, o in enumerate(offs))
+
+
 # ----------------------------------------------------------------------------
 # Coalesce: the same function of the 1-D index on [0, size) with extent-1 leaves
 # dropped and neighbours merged whenever stride[i+1] == extent[i] * stride[i].

@@ -193,6 +193,68 @@ int lr_max_common_vector(const lr_layout* src, const lr_layout* dst, size_t elem
  * tid%P + (tid/P)*kRow, i.e. (P, ceil(T/P)):(1, kRow). */
 int lr_thread_map(int64_t pitch, int64_t strips, int64_t krow, int64_t threads, lr_layout* out);
 
+/* --------------------------------------------------------------- inspection */
+
+/* Print a layout with two top-level modes as a grid ([print_layout page, sections
+ * 2.3 and 3.1]: rows walk mode 0, columns walk mode 1, each cell is the offset of
+ * (row, col)).  First line: the text form of L.  Cells are right-aligned to the
+ * widest offset ([print_layout page, section 6.3]) and separated by one space;
+ * every line ends in '\n'.  *needed (if needed != NULL) receives the bytes the text
+ * takes with its NUL, also when buf is NULL or cap too small (LR_ERR_CAPACITY,
+ * buf untouched).  LR_ERR_INVALID unless L has exactly two top-level modes and at
+ * most 2^20 cells. */
+int lr_layout_print(const lr_layout* L, char* buf, size_t cap, size_t* needed);
+
+/* Thread-to-offset table ([ThreadMap page, section 5.3]): for t = 0..n-1 the line
+ * "thread <t> -> offset <L(t)>\n", both numbers right-aligned to the widest.
+ * 1 <= n <= min(size(L), 2^20) (LR_ERR_INVALID otherwise); buf, cap and needed as
+ * lr_layout_print. */
+int lr_layout_print_table(const lr_layout* L, int64_t n, char* buf, size_t cap, size_t* needed);
+
+#define LR_WAVE_LANES 64
+
+/* Result of lr_access_check: lane t of one wavefront accesses the elem_bytes bytes
+ * at element offset L(t). */
+typedef struct {
+  int32_t lanes, elem_bytes;  /* as passed */
+  int32_t banks;              /* LDS banks of 4 bytes in the model used */
+  int32_t lanes_per_phase;    /* lanes served together in the model used */
+  int32_t line_bytes;         /* cache-line size used for `lines` */
+  int32_t phases;             /* ceil(lanes / lanes_per_phase) */
+  int32_t cycles;             /* sum over phases of the phase's worst bank ways */
+  int32_t conflict_cycles;    /* cycles - phases; 0 means conflict-free */
+  int32_t ways_max;           /* worst ways in any phase (1 = conflict-free) */
+  int32_t bank_words[LR_WAVE_LANES]; /* distinct words per bank in the first worst phase */
+  int32_t adjacent;           /* 1 if L(t+1) == L(t) + 1 for every t < lanes-1 */
+  int32_t first_gap;          /* smallest t with L(t+1) != L(t) + 1, else -1 */
+  int64_t lines;              /* distinct line_bytes-byte lines the lanes touch */
+  int64_t min_lines;          /* ceil(distinct bytes touched / line_bytes) */
+  int64_t offsets[LR_WAVE_LANES]; /* L(t) for t < lanes, in elements */
+} lr_access_report;
+
+/* LDS models for lr_access_check. */
+#define LR_LDS_CUSTOM 0       /* banks and lanes_per_phase as passed */
+#define LR_LDS_GFX950_READ 1  /* gfx950 ds_read: elem_bytes <= 4: 32 banks, 32 lanes a phase;
+                                 8: 64 banks, 32 lanes; 16: 64 banks, 16 lanes */
+#define LR_LDS_GFX950_WRITE 2 /* gfx950 ds_write: elem_bytes <= 4: 32 banks, 32 lanes a phase;
+                                 8: 32 banks, 16 lanes; 16: 32 banks, 8 lanes */
+
+/* The two checks the print_layout page (section 6.4) asks of a candidate layout,
+ * for lanes 0..lanes-1 of one wavefront accessing L(0..lanes-1): whether adjacent
+ * lanes hit adjacent offsets, and how evenly the lanes spread over the LDS banks
+ * ([print_layout page, sections 4.3 and 5.2]: distinct 4-byte words in one bank are
+ * served one after another, one word read by several lanes is served once).  Lanes
+ * are served in phases of lanes_per_phase consecutive lanes, a phase taking as many
+ * cycles as its busiest bank has distinct words.  lds_model LR_LDS_GFX950_READ or
+ * LR_LDS_GFX950_WRITE takes banks and lanes_per_phase from the measured gfx950
+ * behaviour (pass 0 for both); LR_LDS_CUSTOM uses them as given, each in [1, 64]
+ * (banks = lanes_per_phase = lanes = 32 is the page's warp model).  line_bytes 0
+ * means 128.  lanes in [1, min(64, size(L))] (LR_ERR_INVALID otherwise),
+ * elem_bytes as lr_layout_copy (LR_ERR_ELEM_BYTES); LR_ERR_OVERFLOW if a byte
+ * address does not fit in int64. */
+int lr_access_check(const lr_layout* L, size_t elem_bytes, int32_t lanes, int32_t lds_model, int32_t banks,
+                    int32_t lanes_per_phase, int32_t line_bytes, lr_access_report* out);
+
 /* --------------------------------------------------------------- copy plan */
 
 /* Copy paths (what lr_copy_plan chose). */

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     Layout,
     LayoutRemapError,
+    access_check,
     LibraryNotBuilt,
     blocked_product,
     coalesce,
@@ -36,6 +37,8 @@ from .binding import (  # noqa: F401
     logical_product,
     max_common_vector,
     parse,
+    print_layout,
+    print_table,
     right_inverse,
     thread_map,
     zipped_divide,

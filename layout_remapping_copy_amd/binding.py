@@ -88,6 +88,29 @@ class lr_plan(ctypes.Structure):
     ]
 
 
+WAVE_LANES = 64
+
+
+class lr_access_report(ctypes.Structure):
+    _fields_ = [
+        ("lanes", ctypes.c_int32),
+        ("elem_bytes", ctypes.c_int32),
+        ("banks", ctypes.c_int32),
+        ("lanes_per_phase", ctypes.c_int32),
+        ("line_bytes", ctypes.c_int32),
+        ("phases", ctypes.c_int32),
+        ("cycles", ctypes.c_int32),
+        ("conflict_cycles", ctypes.c_int32),
+        ("ways_max", ctypes.c_int32),
+        ("bank_words", ctypes.c_int32 * WAVE_LANES),
+        ("adjacent", ctypes.c_int32),
+        ("first_gap", ctypes.c_int32),
+        ("lines", ctypes.c_int64),
+        ("min_lines", ctypes.c_int64),
+        ("offsets", ctypes.c_int64 * WAVE_LANES),
+    ]
+
+
 class LibraryNotBuilt(RuntimeError):
     pass
 
@@ -117,6 +140,11 @@ _SIGS = {
     "lr_is_injective": (ctypes.c_int, [_L, _P(ctypes.c_int32)]),
     "lr_max_common_vector": (ctypes.c_int, [_L, _L, ctypes.c_size_t, _P(ctypes.c_int64)]),
     "lr_thread_map": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _L]),
+    "lr_layout_print": (ctypes.c_int, [_L, ctypes.c_char_p, ctypes.c_size_t, _P(ctypes.c_size_t)]),
+    "lr_layout_print_table": (ctypes.c_int, [_L, ctypes.c_int64, ctypes.c_char_p, ctypes.c_size_t,
+                                             _P(ctypes.c_size_t)]),
+    "lr_access_check": (ctypes.c_int, [_L, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _P(lr_access_report)]),
     "lr_copy_plan": (ctypes.c_int, [_L, ctypes.c_int64, ctypes.c_size_t, _L, ctypes.c_int64, ctypes.c_size_t,
                                     ctypes.c_size_t, ctypes.c_uint32, _P(lr_plan)]),
     "lr_layout_eval": (ctypes.c_int, [_L, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
@@ -293,6 +321,47 @@ def thread_map(pitch: int, strips: int, krow: int, threads: int) -> Layout:
     out = lr_layout()
     _check(lib().lr_thread_map(pitch, strips, krow, threads, ctypes.byref(out)), "thread_map")
     return Layout(out)
+
+
+def _print_text(fn, what, *args) -> str:
+    need = ctypes.c_size_t()
+    rc = fn(*args, None, 0, ctypes.byref(need))
+    if rc != ERR_CAPACITY:
+        _check(rc, what)
+    buf = ctypes.create_string_buffer(need.value)
+    _check(fn(*args, buf, need.value, ctypes.byref(need)), what)
+    return buf.value.decode()
+
+
+def print_layout(L) -> str:
+    """Grid of a two-mode layout: rows over mode 0, columns over mode 1."""
+    return _print_text(lib().lr_layout_print, "layout_print", ctypes.byref(_as_layout(L).c))
+
+
+def print_table(L, n: int) -> str:
+    """'thread t -> offset L(t)' for t < n."""
+    return _print_text(lib().lr_layout_print_table, "layout_print_table", ctypes.byref(_as_layout(L).c), n)
+
+
+LDS_CUSTOM = 0
+LDS_GFX950_READ = 1
+LDS_GFX950_WRITE = 2
+
+
+def access_check(L, elem_bytes: int, lanes: int = WAVE_LANES, op: str = "read", banks: int = 0,
+                 lanes_per_phase: int = 0, line_bytes: int = 0) -> dict:
+    """Bank cycles, adjacency and cache lines of one wavefront accessing L(0..lanes-1).
+    op "read"/"write" selects the gfx950 LDS model; op "custom" uses banks and
+    lanes_per_phase."""
+    model = {"read": LDS_GFX950_READ, "write": LDS_GFX950_WRITE, "custom": LDS_CUSTOM}[op]
+    r = lr_access_report()
+    _check(lib().lr_access_check(ctypes.byref(_as_layout(L).c), elem_bytes, lanes, model, banks, lanes_per_phase,
+                                 line_bytes, ctypes.byref(r)), "access_check")
+    out = {k: getattr(r, k) for k, _ in lr_access_report._fields_ if k not in ("bank_words", "offsets")}
+    out["bank_words"] = list(r.bank_words[:r.banks])
+    out["offsets"] = list(r.offsets[:r.lanes])
+    out["adjacent"] = bool(r.adjacent)
+    return out
 
 
 def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, flags: int = 0,

@@ -142,6 +142,17 @@ static int run_fuzz() {
     lr_blocked_product(&a, &b, &r);
     int64_t v;
     lr_max_common_vector(&a, &b, 4, &v);
+    {
+      static char text[1 << 16];
+      size_t need = 0;
+      lr_layout_print(&a, text, sizeof(text), &need);
+      lr_layout_print(&a, nullptr, 0, &need);
+      lr_layout_print_table(&a, 1 + (int64_t)(rng() % 70), text, sizeof(text), &need);
+      lr_access_report rep;
+      for (int eb : {1, 2, 4, 8, 16})
+        lr_access_check(&a, eb, 1 + (int)(rng() % 64), (int)(rng() % 4), (int)(rng() % 3) * 32,
+                        (int)(rng() % 3) * 16, (int)(rng() % 3) * 64, &rep);
+    }
     lr_plan p;
     // a compact destination over a's extents in a random order: a bijective copy
     lr_layout c = a;

@@ -222,6 +222,118 @@ def test_thread_map_matches_oracle():
         assert B.leaves == O.flatten(O.pitch_linear_layout(p, k, t))
 
 
+def _rank2_text(rng, swz_p=0.3):
+    def mode():
+        k = rng.randint(1, 2)
+        e = [rng.randint(1, 5) for _ in range(k)]
+        d = [rng.randint(0, 40) for _ in range(k)]
+        if k == 1:
+            return str(e[0]), str(d[0])
+        return "(" + ",".join(map(str, e)) + ")", "(" + ",".join(map(str, d)) + ")"
+    (e0, d0), (e1, d1) = mode(), mode()
+    text = f"({e0},{e1}):({d0},{d1})"
+    if rng.random() < swz_p:
+        b = rng.randint(1, 3)
+        text = f"Sw<{b},{rng.randint(0, 2)},{rng.randint(b, 4)}> o " + text
+    return text
+
+
+def test_print_layout_and_table_match_oracle():
+    # [print_layout page, section 3.1]: the 4x2 row-major example
+    assert lr.print_layout("(4,2):(2,1)") == "(4,2):(2,1)\n0 1\n2 3\n4 5\n6 7\n"
+    rng = random.Random(91)
+    for _ in range(300):
+        t = _rank2_text(rng)
+        assert lr.print_layout(t) == O.print_layout(O.parse(t)) + "\n", t
+        n = rng.randint(1, O.size(O.parse(t)))
+        assert lr.print_table(t, n) == O.thread_offset_table(O.parse(t), n) + "\n", t
+    # the ThreadMap page's strip-mined map, 64 threads
+    L = lr.thread_map(8, 4, 16, 64)
+    assert lr.print_table(L, 64) == O.thread_offset_table(O.stripmined_layout(8, 4, 16, 64), 64) + "\n"
+    for bad in ("8:1", "(2,2,2):(1,2,4)"):
+        with pytest.raises(lr.LayoutRemapError):
+            lr.print_layout(bad)
+    with pytest.raises(lr.LayoutRemapError):
+        lr.print_table("8:1", 9)
+    with pytest.raises(lr.LayoutRemapError):
+        lr.print_layout("(1024,1025):(1,1024)")   # more than 2^20 cells
+    # capacity protocol: too small a buffer reports the size and writes nothing
+    import ctypes
+    need = ctypes.c_size_t()
+    buf = ctypes.create_string_buffer(b"x" * 8)
+    rc = lr.lib().lr_layout_print(ctypes.byref(lr.parse("(4,2):(2,1)").c), buf, 8, ctypes.byref(need))
+    assert rc == lr.binding.ERR_CAPACITY and need.value == len("(4,2):(2,1)\n0 1\n2 3\n4 5\n6 7\n") + 1
+    assert buf.raw[:8] == b"x" * 8
+
+
+def test_access_check_matches_oracle():
+    rng = random.Random(92)
+    for _ in range(600):
+        t = _rand_layout(rng, max_leaves=4, max_ext=6, max_stride=70, swz_p=0.3)
+        Lo = O.parse(t)
+        n = O.size(Lo)
+        lanes = rng.randint(1, min(64, n))
+        eb = rng.choice([1, 2, 4, 8, 16])
+        op = rng.choice(["read", "write", "custom", "custom"])
+        if op != "custom":
+            banks = lpp = 0
+        else:
+            banks, lpp = rng.choice([32, 64, 17]), rng.choice([1, 8, 16, 32, 64])
+        line = rng.choice([0, 64, 128, 256])
+        r = lr.access_check(t, eb, lanes, op, banks, lpp, line)
+        if op == "read":
+            banks, lpp = {1: (32, 32), 2: (32, 32), 4: (32, 32), 8: (64, 32), 16: (64, 16)}[eb]
+        elif op == "write":
+            banks, lpp = {1: (32, 32), 2: (32, 32), 4: (32, 32), 8: (32, 16), 16: (32, 8)}[eb]
+        want = O.access_report(Lo, eb, lanes, banks, lpp, line or 128)
+        assert (r["banks"], r["lanes_per_phase"], r["line_bytes"]) == (banks, lpp, line or 128)
+        for k in ("offsets", "cycles", "phases", "ways_max", "conflict_cycles", "bank_words", "lines",
+                  "min_lines", "adjacent", "first_gap"):
+            assert r[k] == want[k], (t, eb, lanes, banks, lpp, k, r[k], want[k])
+    # the print_layout page's column read under its own warp model, and padded
+    assert lr.access_check("32:8", 4, 32, "custom", 32, 32)["ways_max"] == 8
+    assert lr.access_check("32:9", 4, 32, "custom", 32, 32)["conflict_cycles"] == 0
+    for args in [("8:1", 4, 9), ("64:1", 4, 65), ("64:1", 3, 64), ("64:1", 4, 64, "custom", 32, 0),
+                 ("64:1", 4, 64, "custom", 65, 8), ("64:1", 4, 64, "read", 32, 32), ("64:1", 4, 64, "read", 0, 0, -1),
+                 ("2:4611686018427387903", 16, 2)]:
+        with pytest.raises(lr.LayoutRemapError):
+            lr.access_check(*args)
+    import ctypes
+    r = lr.binding.lr_access_report()
+    assert lr.lib().lr_access_check(ctypes.byref(lr.parse("64:1").c), 4, 64, 3, 0, 0, 0, ctypes.byref(r)) == \
+        lr.binding.ERR_INVALID
+
+
+TILE_SHAPES = [(16, 16), (32, 16), (16, 32), (32, 32), (32, 8), (64, 8), (64, 16)]
+
+
+@pytest.mark.parametrize("ta,tb", TILE_SHAPES)
+def test_transpose_lds_tile_accesses_conflict_free(ta, tb):
+    """The transpose kernel's LDS tile is C tile[TA*V][TB] with C = V elements of EB
+    bytes; thread tid = alpha + TA*beta stores its i-th transposed row at
+    tile[V*alpha + i][beta ^ (alpha % TB)], and after the barrier thread tid loads
+    tile[row][c ^ ((row / V) % TB)] with c = tid % TB, row = tid / TB (+ a multiple of
+    NT/TB).  For wave 0 and i = 0 the store is the layout
+    Sw<log2 TB, 0, log2(V*TB)> o (min(TA,64), 64/TA):(V*TB, 1) over the lane, the load
+    Sw<log2 TB, 0, log2(TB*V)> o 64:1 (other waves and i only XOR or shift the
+    offsets by constants that keep the bank pattern).  With 16-byte chunks both are conflict-free under the gfx950
+    model; the hardware counter shows 0 conflict cycles for these kernels."""
+    for V in (1, 4, 8, 16):
+        la = min(ta, 64)
+        lb = 64 // la
+        B, S = tb.bit_length() - 1, (V * tb).bit_length() - 1
+        text = f"Sw<{B},0,{S}> o ({la},{lb}):({V * tb},1)" if lb > 1 else f"Sw<{B},0,{S}> o {la}:{V * tb}"
+        rep = lr.access_check(text, 16, 64, "write")
+        want = [(V * (t % ta)) * tb + ((t // ta) ^ ((t % ta) % tb)) for t in range(64)]
+        assert rep["offsets"] == want, text
+        assert rep["conflict_cycles"] == 0, (text, rep["conflict_cycles"])
+        # the load: row = t / TB, so the XOR term takes the bits of t above TB*V
+        load = [(t // tb) * tb + ((t % tb) ^ ((t // tb // V) % tb)) for t in range(64)]
+        rep = lr.access_check(f"Sw<{B},0,{(tb * V).bit_length() - 1}> o 64:1", 16, 64, "read")
+        assert rep["offsets"] == load
+        assert rep["conflict_cycles"] == 0
+
+
 def test_common_vector_sound_and_tight_on_workloads():
     rng = random.Random(23)
     for _ in range(1500):
@@ -343,6 +455,7 @@ def _gpp(tmp_path, sanitize=False):
     exe = str(tmp_path / ("host_check_san" if sanitize else "host_check"))
     src = [os.path.join(ROOT, "tests", "host_check.cpp"),
            os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", "host_layout.cpp"),
+           os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", "inspect.cpp"),
            os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", "plan.cpp")]
     flags = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"] if sanitize else ["-O2"]
     cmd = ["g++", "-std=c++17", *flags, "-I", os.path.join(ROOT, "include"),

@@ -286,6 +286,8 @@ typedef struct {
   int32_t b_mode;      /* joint mode contiguous in dst (transpose/interleave), else -1 */
   int32_t b2_mode;     /* transpose: mode continuing b_mode in dst, grouped with it, else -1 */
   int32_t block;       /* threads per workgroup */
+  int32_t streaming;   /* 1 if loads and stores are non-temporal: by default when the source
+                          plus destination bytes reach 256 MiB, the last-level cache size */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */

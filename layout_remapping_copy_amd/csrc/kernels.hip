@@ -78,8 +78,10 @@ struct alignas(V * sizeof(T) >= 16 ? 16 : V * sizeof(T)) Chunk {
 };
 
 
-// Global loads/stores of a raw element or chunk.  cache bit 0: non-temporal
-// stores, bit 1: non-temporal loads (streaming data that will not be re-read).
+// Global loads/stores of a raw element or chunk.  NT: non-temporal (streaming data
+// that will not be re-read soon).  The policy is a template parameter: chosen at
+// run time between two otherwise identical accesses, the compiler merges them
+// into one plain access and the hint is lost.
 template <int S> struct NativeOf;
 template <> struct NativeOf<1> { using T = uint8_t; };
 template <> struct NativeOf<2> { using T = uint16_t; };
@@ -87,18 +89,22 @@ template <> struct NativeOf<4> { using T = uint32_t; };
 template <> struct NativeOf<8> { using T = unsigned int __attribute__((ext_vector_type(2))); };
 template <> struct NativeOf<16> { using T = unsigned int __attribute__((ext_vector_type(4))); };
 
-template <typename C>
-__device__ __forceinline__ C gload(const void* p, uint32_t cache) {
+template <bool NT, typename C>
+__device__ __forceinline__ C gload(const void* p) {
   using N = typename NativeOf<sizeof(C)>::T;
-  N x = (cache & 2u) ? __builtin_nontemporal_load((const N*)p) : *(const N*)p;
+  N x;
+  if constexpr (NT)
+    x = __builtin_nontemporal_load((const N*)p);
+  else
+    x = *(const N*)p;
   return __builtin_bit_cast(C, x);
 }
 
-template <typename C>
-__device__ __forceinline__ void gstore(void* p, const C& v, uint32_t cache) {
+template <bool NT, typename C>
+__device__ __forceinline__ void gstore(void* p, const C& v) {
   using N = typename NativeOf<sizeof(C)>::T;
   N x = __builtin_bit_cast(N, v);
-  if (cache & 1u)
+  if constexpr (NT)
     __builtin_nontemporal_store(x, (N*)p);
   else
     *(N*)p = x;
@@ -202,7 +208,6 @@ struct GenericArgs {
   ModeArg64 w[kMaxKernelModes];
   SwzArg sws, swd;
   uint64_t sws_mask64, swd_mask64;
-  uint32_t cache;
   int64_t n_units;
   int64_t n_chunks;  // groups of 256 * U units, U the per-lane unroll
 };
@@ -249,7 +254,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int UB, bool WIDE, int U>
+template <int UB, bool WIDE, int U, bool NT>
 __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
   static_assert(U == 1 || U == 4, "one or four units per lane");
   using T = typename Raw<UB>::T;
@@ -261,7 +266,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
       if (i0 < a.n_units) {
         uint64_t s0, d0;
         generic_offsets<WIDE>(a, i0, &s0, &d0);
-        gstore<T>(dst + d0, gload<T>(src + s0, a.cache), a.cache);
+        gstore<NT, T>(dst + d0, gload<NT, T>(src + s0));
       }
     } else {
       uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, d0 = 0, d1 = 0, d2 = 0, d3 = 0;
@@ -272,14 +277,14 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
       if (k2) generic_offsets<WIDE>(a, i0 + 512, &s2, &d2);
       if (k3) generic_offsets<WIDE>(a, i0 + 768, &s3, &d3);
       T v0, v1, v2, v3;
-      if (k0) v0 = gload<T>(src + s0, a.cache);
-      if (k1) v1 = gload<T>(src + s1, a.cache);
-      if (k2) v2 = gload<T>(src + s2, a.cache);
-      if (k3) v3 = gload<T>(src + s3, a.cache);
-      if (k0) gstore<T>(dst + d0, v0, a.cache);
-      if (k1) gstore<T>(dst + d1, v1, a.cache);
-      if (k2) gstore<T>(dst + d2, v2, a.cache);
-      if (k3) gstore<T>(dst + d3, v3, a.cache);
+      if (k0) v0 = gload<NT, T>(src + s0);
+      if (k1) v1 = gload<NT, T>(src + s1);
+      if (k2) v2 = gload<NT, T>(src + s2);
+      if (k3) v3 = gload<NT, T>(src + s3);
+      if (k0) gstore<NT, T>(dst + d0, v0);
+      if (k1) gstore<NT, T>(dst + d1, v1);
+      if (k2) gstore<NT, T>(dst + d2, v2);
+      if (k3) gstore<NT, T>(dst + d3, v3);
     }
   }
 }
@@ -322,7 +327,6 @@ struct DualArgs {
   const void* src;
   void* dst;
   SideArg s, d;
-  uint32_t cache;
   int64_t n;
   int64_t n_chunks;
 };
@@ -338,14 +342,14 @@ __global__ void __launch_bounds__(256) k_dual(DualArgs a) {
     const int64_t i0 = ch * 1024 + threadIdx.x;
     const bool k0 = i0 < a.n, k1 = i0 + 256 < a.n, k2 = i0 + 512 < a.n, k3 = i0 + 768 < a.n;
     T v0, v1, v2, v3;
-    if (k0) v0 = gload<T>(src + side_eval<WIDE>(a.s, i0), a.cache);
-    if (k1) v1 = gload<T>(src + side_eval<WIDE>(a.s, i0 + 256), a.cache);
-    if (k2) v2 = gload<T>(src + side_eval<WIDE>(a.s, i0 + 512), a.cache);
-    if (k3) v3 = gload<T>(src + side_eval<WIDE>(a.s, i0 + 768), a.cache);
-    if (k0) gstore<T>(dst + side_eval<WIDE>(a.d, i0), v0, a.cache);
-    if (k1) gstore<T>(dst + side_eval<WIDE>(a.d, i0 + 256), v1, a.cache);
-    if (k2) gstore<T>(dst + side_eval<WIDE>(a.d, i0 + 512), v2, a.cache);
-    if (k3) gstore<T>(dst + side_eval<WIDE>(a.d, i0 + 768), v3, a.cache);
+    if (k0) v0 = gload<false, T>(src + side_eval<WIDE>(a.s, i0));
+    if (k1) v1 = gload<false, T>(src + side_eval<WIDE>(a.s, i0 + 256));
+    if (k2) v2 = gload<false, T>(src + side_eval<WIDE>(a.s, i0 + 512));
+    if (k3) v3 = gload<false, T>(src + side_eval<WIDE>(a.s, i0 + 768));
+    if (k0) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0), v0);
+    if (k1) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0 + 256), v1);
+    if (k2) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0 + 512), v2);
+    if (k3) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0 + 768), v3);
   }
 }
 
@@ -416,7 +420,6 @@ struct TransposeArgs {
   FD fd_ta, fd_tb;
   BatchArg batch;
   SwzArg sws, swd;
-  uint32_t cache;
   uint32_t order;  // 0: tiles along a vary fastest across workgroups, 1: along b, 2: diagonal,
                    // 3: diagonal over 4 x 4 groups of tiles
   uint32_t gta, gtb;  // order 3: groups along a and b
@@ -437,11 +440,11 @@ struct TransposeArgs {
 // touch distinct chunk slots of a bank window.
 // LDS == false (TA == TB == 16 only): lanes are arranged 8 x 8 per wave so each
 // load and store instruction covers eight full 128-byte lines, with no LDS.
-template <int EB, int V, bool LDS, int TA, int TB>
+template <int EB, int V, bool LDS, int TA, int TB, bool NT>
 __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   using T = typename Raw<EB>::T;
   using C = Chunk<T, V>;
-  constexpr int NT = TA * TB;
+  constexpr int NTH = TA * TB;  // threads
   static_assert(LDS || (TA == 16 && TB == 16), "the direct variant uses 16 x 16 blocks");
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
@@ -507,7 +510,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
     for (int j = 0; j < V; ++j) {
       const uint32_t b = b_blk + j;
       uint32_t so = swz32(a_blk + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
-      in[j] = gload<C>(src + (size_t)so * EB, t.cache);
+      in[j] = gload<NT, C>(src + (size_t)so * EB);
     }
   }
   C out[V];
@@ -521,7 +524,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         uint32_t dof = swz32((a_blk + i) * t.sd_a + b_blk + bd, t.swd);
-        gstore<C>(dst + (size_t)dof * EB, out[i], t.cache);
+        gstore<NT, C>(dst + (size_t)dof * EB, out[i]);
       }
     }
     return;
@@ -536,12 +539,12 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   const int c = tid % TB;
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const int row = tid / TB + (NT / TB) * k;
+    const int row = tid / TB + (NTH / TB) * k;
     const uint32_t a = a0 + row, b = b0 + V * c;
     if (a < t.ext_a && b < t.ext_b) {
       C v = tile[row][c ^ ((row / V) % TB)];
       uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
-      gstore<C>(dst + (size_t)dof * EB, v, t.cache);
+      gstore<NT, C>(dst + (size_t)dof * EB, v);
     }
   }
 }
@@ -557,7 +560,6 @@ struct InterleaveArgs {
   FD fd_ta;
   BatchArg batch;
   SwzArg sws, swd;
-  uint32_t cache;
 };
 
 // The dst-contiguous mode b is short (NB * EB <= 16 bytes) and a follows it in
@@ -569,7 +571,7 @@ struct InterleaveArgs {
 //   NARROW == true: each lane writes one 16-byte dst chunk, built from NB loads of
 //     16/NB bytes (P = V/NB positions of a, one load per b), so that every store
 //     instruction of a wave covers 1 KiB of contiguous dst.
-template <int EB, int NB, bool NARROW>
+template <int EB, int NB, bool NARROW, bool NT>
 __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
@@ -598,7 +600,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
-          in[u][b] = gload<H>(src + (size_t)so * EB, t.cache);
+          in[u][b] = gload<NT, H>(src + (size_t)so * EB);
         }
       }
     }
@@ -610,7 +612,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
 #pragma unroll
       for (int x = 0; x < V; ++x) o.e[x] = in[u][x % NB].e[x / NB];
       uint32_t dof = swz32(j * V + bd, t.swd);
-      gstore<C>(dst + (size_t)dof * EB, o, t.cache);
+      gstore<NT, C>(dst + (size_t)dof * EB, o);
     }
   } else {
     constexpr int U = NB >= 8 ? 1 : 8 / NB;  // a-chunks per lane: U * NB loads in flight
@@ -624,7 +626,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           uint32_t so = swz32(a0 + b * t.ss_b + bs, t.sws);
-          in[u][b] = gload<C>(src + (size_t)so * EB, t.cache);
+          in[u][b] = gload<NT, C>(src + (size_t)so * EB);
         }
       }
     }
@@ -641,7 +643,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
           o.e[x] = in[u][e % NB].e[e / NB];
         }
         uint32_t dof = swz32(a0 * NB + c * V + bd, t.swd);
-        gstore<C>(dst + (size_t)dof * EB, o, t.cache);
+        gstore<NT, C>(dst + (size_t)dof * EB, o);
       }
     }
   }
@@ -667,7 +669,6 @@ struct StagedArgs {
   FD fd_tg;
   BatchArg batch;
   SwzArg swd;
-  uint32_t cache;
 };
 
 // Padded or gathered tiles ([CuTe algebra page, section 2.2]: composing a padded
@@ -675,7 +676,7 @@ struct StagedArgs {
 // footprint of K tiles in LDS with 16-byte loads (pad words included: DRAM
 // fetches them with their lines anyway), then each lane builds 16-byte dst chunks
 // by gathering elements from LDS and stores them contiguously.
-template <int EB>
+template <int EB, bool NT>
 __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
@@ -707,10 +708,10 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
     const bool k0 = chunk_ok(i0, &b0), k1 = chunk_ok(i0 + 256, &b1), k2 = chunk_ok(i0 + 512, &b2),
                k3 = chunk_ok(i0 + 768, &b3);
     uint4 v0, v1, v2, v3;
-    if (k0) v0 = gload<uint4>(src + b0, t.cache);
-    if (k1) v1 = gload<uint4>(src + b1, t.cache);
-    if (k2) v2 = gload<uint4>(src + b2, t.cache);
-    if (k3) v3 = gload<uint4>(src + b3, t.cache);
+    if (k0) v0 = gload<NT, uint4>(src + b0);
+    if (k1) v1 = gload<NT, uint4>(src + b1);
+    if (k2) v2 = gload<NT, uint4>(src + b2);
+    if (k3) v3 = gload<NT, uint4>(src + b3);
     if (k0) lds[i0] = v0;
     if (k1) lds[i0 + 256] = v1;
     if (k2) lds[i0 + 512] = v2;
@@ -742,7 +743,7 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
 #pragma unroll
     for (int x = 0; x < V; ++x) o.e[x] = ldsT[base + g[x]];
     uint32_t dof = swz32(tile * t.Td + bd + c * V, t.swd);
-    gstore<C>(dst + (size_t)dof * EB, o, t.cache);
+    gstore<NT, C>(dst + (size_t)dof * EB, o);
   }
 }
 
@@ -791,14 +792,22 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int ski
   }
 }
 
-template <int UB>
-static void launch_generic(const GenericArgs& a, bool wide, int unroll, unsigned grid, hipStream_t st) {
+template <int UB, bool NT>
+static void launch_generic_nt(const GenericArgs& a, bool wide, int unroll, unsigned grid, hipStream_t st) {
   if (wide)
-    hipLaunchKernelGGL((k_generic<UB, true, 4>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, true, 4, NT>), dim3(grid), dim3(256), 0, st, a);
   else if (unroll == 1)
-    hipLaunchKernelGGL((k_generic<UB, false, 1>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, false, 1, NT>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_generic<UB, false, 4>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, false, 4, NT>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int UB>
+static void launch_generic(const GenericArgs& a, bool wide, int unroll, bool nt, unsigned grid, hipStream_t st) {
+  if (nt)
+    launch_generic_nt<UB, true>(a, wide, unroll, grid, st);
+  else
+    launch_generic_nt<UB, false>(a, wide, unroll, grid, st);
 }
 
 template <int EB>
@@ -809,60 +818,71 @@ static void launch_dual(const DualArgs& a, bool wide, unsigned grid, hipStream_t
     hipLaunchKernelGGL((k_dual<EB, false>), dim3(grid), dim3(256), 0, st, a);
 }
 
-template <int EB, int V, int TA, int TB>
+template <int EB, int V, int TA, int TB, bool NT>
 static void launch_transpose_shape(const TransposeArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_transpose<EB, V, true, TA, TB>), dim3(grid), dim3(TA * TB), 0, st, a);
+  hipLaunchKernelGGL((k_transpose<EB, V, true, TA, TB, NT>), dim3(grid), dim3(TA * TB), 0, st, a);
 }
 
-template <int EB, int V>
+template <int EB, int V, bool NT>
 static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, unsigned grid, hipStream_t st) {
   if (!lds) {
     if (shape != 0) return false;
-    hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a);
     return true;
   }
   if constexpr (V * EB == 16 && V <= 8) {  // other shapes: full 16-byte chunks, LDS <= 128 KiB
     switch (shape) {
-      case 1: launch_transpose_shape<EB, V, kTileTA[1], kTileTB[1]>(a, grid, st); return true;
-      case 2: launch_transpose_shape<EB, V, kTileTA[2], kTileTB[2]>(a, grid, st); return true;
-      case 3: launch_transpose_shape<EB, V, kTileTA[3], kTileTB[3]>(a, grid, st); return true;
-      case 4: launch_transpose_shape<EB, V, kTileTA[4], kTileTB[4]>(a, grid, st); return true;
-      case 5: launch_transpose_shape<EB, V, kTileTA[5], kTileTB[5]>(a, grid, st); return true;
-      case 6: launch_transpose_shape<EB, V, kTileTA[6], kTileTB[6]>(a, grid, st); return true;
+      case 1: launch_transpose_shape<EB, V, kTileTA[1], kTileTB[1], NT>(a, grid, st); return true;
+      case 2: launch_transpose_shape<EB, V, kTileTA[2], kTileTB[2], NT>(a, grid, st); return true;
+      case 3: launch_transpose_shape<EB, V, kTileTA[3], kTileTB[3], NT>(a, grid, st); return true;
+      case 4: launch_transpose_shape<EB, V, kTileTA[4], kTileTB[4], NT>(a, grid, st); return true;
+      case 5: launch_transpose_shape<EB, V, kTileTA[5], kTileTB[5], NT>(a, grid, st); return true;
+      case 6: launch_transpose_shape<EB, V, kTileTA[6], kTileTB[6], NT>(a, grid, st); return true;
       default: break;
     }
   }
   if (shape != 0) return false;
-  launch_transpose_shape<EB, V, 16, 16>(a, grid, st);
+  launch_transpose_shape<EB, V, 16, 16, NT>(a, grid, st);
   return true;
 }
 
-template <int EB>
-static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, unsigned grid, hipStream_t st) {
+template <int EB, bool NT>
+static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int shape, unsigned grid, hipStream_t st) {
   switch (v) {
-    case 1: return launch_transpose_v<EB, 1>(a, lds, shape, grid, st);
-    case 2: if constexpr (EB <= 8) return launch_transpose_v<EB, 2>(a, lds, shape, grid, st); break;
-    case 4: if constexpr (EB <= 4) return launch_transpose_v<EB, 4>(a, lds, shape, grid, st); break;
-    case 8: if constexpr (EB <= 2) return launch_transpose_v<EB, 8>(a, lds, shape, grid, st); break;
-    case 16: if constexpr (EB == 1) return launch_transpose_v<EB, 16>(a, lds, shape, grid, st); break;
+    case 1: return launch_transpose_v<EB, 1, NT>(a, lds, shape, grid, st);
+    case 2: if constexpr (EB <= 8) return launch_transpose_v<EB, 2, NT>(a, lds, shape, grid, st); break;
+    case 4: if constexpr (EB <= 4) return launch_transpose_v<EB, 4, NT>(a, lds, shape, grid, st); break;
+    case 8: if constexpr (EB <= 2) return launch_transpose_v<EB, 8, NT>(a, lds, shape, grid, st); break;
+    case 16: if constexpr (EB == 1) return launch_transpose_v<EB, 16, NT>(a, lds, shape, grid, st); break;
   }
   return false;
 }
 
-template <int EB, bool NARROW>
+template <int EB>
+static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, bool nt, unsigned grid,
+                             hipStream_t st) {
+  return nt ? launch_transpose_nt<EB, true>(a, v, lds, shape, grid, st)
+            : launch_transpose_nt<EB, false>(a, v, lds, shape, grid, st);
+}
+
+template <int EB, bool NARROW, bool NT>
 static bool launch_interleave_n(const InterleaveArgs& a, int nb, unsigned grid, hipStream_t st) {
   switch (nb) {
-    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16, NARROW>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
   }
   return false;
 }
 
 template <int EB>
-static bool launch_interleave(const InterleaveArgs& a, int nb, bool narrow, unsigned grid, hipStream_t st) {
-  return narrow ? launch_interleave_n<EB, true>(a, nb, grid, st) : launch_interleave_n<EB, false>(a, nb, grid, st);
+static bool launch_interleave(const InterleaveArgs& a, int nb, bool narrow, bool nt, unsigned grid, hipStream_t st) {
+  if (nt)
+    return narrow ? launch_interleave_n<EB, true, true>(a, nb, grid, st)
+                  : launch_interleave_n<EB, false, true>(a, nb, grid, st);
+  return narrow ? launch_interleave_n<EB, true, false>(a, nb, grid, st)
+                : launch_interleave_n<EB, false, false>(a, nb, grid, st);
 }
 
 #define LR_DISPATCH_EB(eb, CALL)          \
@@ -912,9 +932,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.swd_mask64 = zd.b ? (((uint64_t(1) << zd.b) - 1) << zd.m) : 0;
       a.n_units = p.n_units;
       a.n_chunks = (p.n_units + 256 * p.unroll - 1) / (256 * p.unroll);
-      a.cache = p.cache;
       const int ub = p.v * p.eb;
-      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, grid, st));
+      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.nt, grid, st));
       return check_launch();
     }
     case LR_PATH_DUAL:
@@ -927,7 +946,6 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       fill_side(&a.d, Ld, p.wide);
       a.n = p.n;
       a.n_chunks = (p.n + 1023) / 1024;
-      a.cache = p.cache;
       if (p.path == LR_PATH_ALIAS) {
         LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_alias<EBV>), dim3(grid), dim3(1024), 0, st, a));
       } else {
@@ -964,7 +982,6 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       fill_batch(&a.batch, p, p.a, p.b, p.b2);
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
-      a.cache = p.cache;
       a.order = p.torder;
       if (p.torder == 3) {
         a.gta = a.tiles_a / 4;
@@ -974,7 +991,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       }
       const bool lds = p.path == LR_PATH_TRANSPOSE;
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
@@ -990,9 +1007,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       fill_batch(&a.batch, p, p.a, p.b);
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
-      a.cache = p.cache;
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, p.inarrow != 0, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, p.inarrow != 0, p.nt, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
@@ -1027,9 +1043,12 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         a.batch.sd[r] = (uint32_t)p.m[k].sd;
       }
       a.swd = swz_arg(p.sw_d);
-      a.cache = p.cache;
       const size_t shm = (size_t)p.staged_K * (size_t)p.staged_Fc * 16;
-      LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV>), dim3(grid), dim3(256), shm, st, a));
+      if (p.nt) {
+        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, true>), dim3(grid), dim3(256), shm, st, a));
+      } else {
+        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, false>), dim3(grid), dim3(256), shm, st, a));
+      }
       return check_launch();
     }
   }

@@ -76,9 +76,10 @@ struct Plan {
   int64_t staged_P, staged_F, staged_Fc, staged_K, staged_cpt;
   // alias path
   int64_t alias_windows;
-  // tuning: cache policy bits (1: non-temporal stores, 2: non-temporal loads) and
-  // the transpose's workgroup order (0: a-tiles fastest, 1: b-tiles fastest)
-  uint32_t cache;
+  // tuning: non-temporal loads and stores (streaming data), and the transpose's
+  // workgroup order (0: a-tiles fastest, 1: b-tiles fastest, 2: diagonal, 3:
+  // diagonal over 4x4 tile groups)
+  bool nt;
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB

@@ -139,6 +139,7 @@ static int plan_alias(Plan* p, int64_t n, int64_t cos_s, int64_t cos_d) {
   if (cos_d > (int64_t(1) << 26) || n >= (int64_t(1) << 31) || cos_s >= (int64_t(1) << 31)) return LR_ERR_ALIAS;
   if ((double)n * (double)windows > (double)(int64_t(1) << 36)) return LR_ERR_ALIAS;
   p->path = LR_PATH_ALIAS;
+  p->nt = false;  // plain accesses: every workgroup re-reads the source
   p->alias_windows = windows;
   p->block = 1024;
   p->grid = windows;
@@ -178,7 +179,14 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   const int64_t lim32 = int64_t(1) << 31;
   p->wide = (flags & LR_COPY_WIDE_INDEX) || n >= lim32 || cos_s >= lim32 || cos_d >= lim32;
   p->block = 256;
-  p->cache = env_u32("LR_CACHE", 0) & 3u;
+  // Non-temporal loads and stores when the footprint (source plus destination
+  // bytes) is at least the 256 MiB last-level cache: nothing the copy touches can
+  // stay cached for a later reader, and streaming accesses measured 5-15 % faster
+  // on every large workload.  Smaller copies keep plain accesses, which leave the
+  // data cache-resident (measured faster when the copy's data is re-read).
+  // LR_NT=0/1 overrides.
+  const bool big_footprint = n >= (int64_t(128) << 20) / (int64_t)elem_bytes;
+  p->nt = env_u32("LR_NT", big_footprint ? 1u : 0u) != 0;
   // one unit per lane measured fastest for streaming copies on MI355X (more waves
   // in flight beat more loads per wave); LR_UNROLL=4 selects four
   p->unroll = env_u32("LR_UNROLL", 1) == 4 ? 4 : 1;
@@ -203,6 +211,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   if (!have_joint || forced == LR_PATH_DUAL || (have_joint && rank > kMaxKernelModes)) {
     if (forced >= 0 && forced != LR_PATH_DUAL) return LR_ERR_PATH;
     p->path = LR_PATH_DUAL;
+    p->nt = false;  // the per-element fallback keeps plain accesses
     p->rank = 0;
     p->v = 1;
     p->n_units = n;
@@ -268,13 +277,6 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     if (a < 0 && p->m[k].ss == 1) a = k;
   }
   const int V16 = 16 / p->eb;
-  auto batch_ok = [&](int64_t vs, int64_t vd, int ka, int kb) {
-    for (int k = 0; k < p->rank; ++k) {
-      if (k != ka && p->m[k].ss % vs) return false;
-      if (k != kb && p->m[k].sd % vd) return false;
-    }
-    return true;
-  };
 
   // interleave: the dst-contiguous mode b is short and a follows it in dst
   if (a >= 0 && b >= 0 && a != b && (forced < 0 || forced == LR_PATH_INTERLEAVE)) {
@@ -346,12 +348,22 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // source distance between nearby b rows
       const int64_t pitch = (b2 >= 0 ? std::min(p->m[b].ss, p->m[b2].ss) : p->m[b].ss) * p->eb;
       // tile shape in 16-byte chunks (a x b): wider tiles only for full chunks on
-      // the LDS variant.  With large source pitches (rows far apart on both sides)
-      // 32 x 16 chunks (512-byte source runs per row) measured fastest; with close
-      // source rows the 16 x 16 tile did.
+      // the LDS variant.  Measured with streaming (non-temporal) accesses:
+      //  - when one tile spans the whole a extent and consecutive b rows are
+      //    adjacent in the source (each tile reads one contiguous block, e.g.
+      //    NHWC -> NCHW), 32 x 8 chunks: small workgroups, many per CU;
+      //  - otherwise the longest runs on both sides, 32 x 32 chunks (16 x 32 when
+      //    16 chunks already cover the a extent).
       const bool far_rows = pitch > 2048;
       const bool wide_ok = V * p->eb == 16 && V <= 8 && p->path == LR_PATH_TRANSPOSE;
-      p->tshape = (far_rows && wide_ok) ? 1 : 0;
+      const int64_t ext_a = p->m[a].ext;
+      const bool block_rows = ext_a <= 32 * V && p->m[b].ss == ext_a;
+      if (!wide_ok)
+        p->tshape = 0;
+      else if (block_rows)
+        p->tshape = ext_a > 16 * V ? 4 : 0;
+      else
+        p->tshape = ext_a > 16 * V ? 3 : 2;
       const uint32_t shp = env_u32("LR_TSHAPE", 99);
       if (shp < (uint32_t)kTileShapes) p->tshape = wide_ok ? (int)shp : 0;
       p->tile_a = kTileTA[p->tshape] * V;
@@ -560,6 +572,7 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   out->b_mode = p.b;
   out->b2_mode = p.b2;
   out->block = p.block;
+  out->streaming = p.nt ? 1 : 0;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

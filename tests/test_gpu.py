@@ -366,13 +366,17 @@ def test_full_size(dev, name):
 
 
 @pytest.mark.slow
-def test_full_transpose_both_variants(dev):
+@pytest.mark.parametrize("nt", ["0", "1"])
+def test_full_transpose_both_variants(dev, monkeypatch, nt):
+    # plain and streaming (non-temporal) accesses; the default for this size is streaming
+    monkeypatch.setenv("LR_NT", nt)
     w = W.full("transpose")
+    assert lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)["streaming"] == (nt == "1")
     src = W.make_src(w)
     want = F.transpose(src, 8192)
     s = torch.from_numpy(src).to(dev)
     for path in (lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT):
-        say("full transpose", lr.binding.PATH_NAMES[path])
+        say("full transpose", lr.binding.PATH_NAMES[path], "nt", nt)
         d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
         lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=2, flags=lr.COPY_FORCE_PATH(path))
         torch.cuda.synchronize()
@@ -410,6 +414,32 @@ def test_transpose_tile_shapes(dev, env_knob, shape):
             env_knob.setenv("LR_TORDER", orient)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)
         env_knob.delenv("LR_TORDER")
+
+
+def test_streaming_accesses_every_path(dev, env_knob):
+    """Small copies default to plain accesses; LR_NT=1 forces the non-temporal
+    kernels, which must give the same bytes on every path and workload."""
+    env_knob.setenv("LR_NT", "1")
+    for name in W.FULL:
+        w = W.small(name)
+        flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
+        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
+        assert p["streaming"] == (p["path"] not in ("alias", "dual")), p["path"]
+        src, dst, want = _oracle_copy(w)
+        say("streaming small", w.name)
+        assert np.array_equal(gpu_copy(dev, src, w.src_layout, dst, w.dst_layout, w.elem_bytes, flags), want)
+    for ci, (ts, td, ns, nd, eb) in enumerate(_case_pairs()):
+        src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for path in ALL_PATHS:
+            flags = lr.COPY_FORCE_PATH(path)
+            try:
+                lr.copy_plan(ts, ns, td, nd, eb, flags)
+            except lr.LayoutRemapError:
+                continue
+            say("streaming path", lr.binding.PATH_NAMES[path], ts, "->", td, "eb", eb)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
 
 
 @pytest.mark.parametrize("narrow", [0, 1])

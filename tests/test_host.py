@@ -398,6 +398,33 @@ def test_plan_joint_matches_oracle_random():
     assert n > 300
 
 
+def test_plan_streaming_default_and_tile_shapes(monkeypatch):
+    monkeypatch.delenv("LR_NT", raising=False)
+    monkeypatch.delenv("LR_TSHAPE", raising=False)
+    # non-temporal accesses from a 256 MiB footprint (source plus destination bytes)
+    n = (128 << 20) // 4
+    assert lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 4)["streaming"]
+    assert not lr.copy_plan(f"{n - 1}:1", n, f"{n - 1}:1", n, 4)["streaming"]
+    monkeypatch.setenv("LR_NT", "0")
+    assert not lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 4)["streaming"]
+    monkeypatch.setenv("LR_NT", "1")
+    assert lr.copy_plan("64:1", 64, "64:1", 64, 4)["streaming"]
+    # the per-element and aliased fallbacks keep plain accesses
+    p = lr.copy_plan("(6,4):(1,6)", 24, "(4,6):(1,4)", 24, 4)
+    assert p["path"] == "dual" and not p["streaming"]
+    p = lr.copy_plan("8:1", 8, "8:0", 1, 4, lr.COPY_ORDERED_ALIAS)
+    assert p["path"] == "alias" and not p["streaming"]
+    monkeypatch.delenv("LR_NT")
+    # transpose tiles: rows far apart -> 32 x 32 chunks (16 x 32 when 16 chunks
+    # cover the contiguous extent); a contiguous source block per tile -> 32 x 8
+    want = {"transpose": (256, 256, 1024), "interleave_cm": (128, 256, 512), "nhwc2nchw": (256, 64, 256)}
+    for name, (ta, tb, block) in want.items():
+        w = W.full(name)
+        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
+        assert p["path"] == "transpose" and p["streaming"]
+        assert (p["tile_a"], p["tile_b"], p["block"]) == (ta, tb, block), name
+
+
 def test_plan_errors():
     E = lr.binding
     with pytest.raises(lr.LayoutRemapError) as e:

@@ -504,8 +504,13 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
         return bad();
       if (p.torder > 3) return bad();
       if (p.tile_a != kTileTA[p.tshape] * v || p.tile_b != kTileTB[p.tshape] * v) return bad();
-      if (p.torder == 3 && ((p.m[p.a].ext + p.tile_a - 1) / p.tile_a % 4 || (ext_b + p.tile_b - 1) / p.tile_b % 4))
-        return bad();
+      const int64_t nta = (p.m[p.a].ext + p.tile_a - 1) / p.tile_a, ntb = (ext_b + p.tile_b - 1) / p.tile_b;
+      if (p.torder == 3 && (nta % 4 || ntb % 4)) return bad();
+      // one workgroup per tile and batch index, all launched (no grid cap)
+      int64_t batch = 1;
+      for (int k = 0; k < p.rank; ++k)
+        if (k != p.a && k != p.b && k != p.b2) batch *= p.m[k].ext;
+      if (p.grid != nta * ntb * batch || p.grid > 0x7FFFFFFF) return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.b && k != p.b2 && p.m[k].sd % v) return bad();

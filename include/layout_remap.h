@@ -291,6 +291,9 @@ typedef struct {
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */
+  int64_t blocks;      /* launches: 1, or the number of blocks a copy too large for 32-bit offsets
+                          is cut into (each planned on its own; the fields above then describe
+                          the first block, joint modes excepted) */
   int64_t ext[2 * LR_MAX_LEAVES];   /* joint modes, sorted by dst stride, in fused elements */
   int64_t s_src[2 * LR_MAX_LEAVES];
   int64_t s_dst[2 * LR_MAX_LEAVES];
@@ -330,7 +333,11 @@ int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, 
  * The byte ranges [src, src+cap*eb) and [dst, dst+cap*eb) must not overlap
  * (LR_ERR_OVERLAP).  A non-injective Ld needs LR_COPY_ORDERED_ALIAS
  * (LR_ERR_ALIAS otherwise); the ordered copy then handles destination cosize up
- * to 2^26 elements with N * ceil(cosize/16384) <= 2^36. */
+ * to 2^26 elements with N * ceil(cosize/16384) <= 2^36.  A copy whose size or
+ * offsets reach 2^31 runs as blocks of its joint modes that each fit 32-bit
+ * offsets, launched one after another on the stream at offset base pointers (any
+ * partition is the same copy when Ld is injective); with LR_COPY_WIDE_INDEX, a
+ * swizzle, a forced path or an aliased Ld it is one launch with 64-bit indices. */
 int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
                    void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
                    size_t elem_bytes, uint32_t flags, void* stream);

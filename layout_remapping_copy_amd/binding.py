@@ -83,6 +83,7 @@ class lr_plan(ctypes.Structure):
         ("tile_b", ctypes.c_int64),
         ("grid", ctypes.c_int64),
         ("n_elems", ctypes.c_int64),
+        ("blocks", ctypes.c_int64),
         ("ext", ctypes.c_int64 * (2 * MAX_LEAVES)),
         ("s_src", ctypes.c_int64 * (2 * MAX_LEAVES)),
         ("s_dst", ctypes.c_int64 * (2 * MAX_LEAVES)),
@@ -375,7 +376,7 @@ def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, fla
         "path": PATH_NAMES[p.path], "elem_bytes": p.elem_bytes, "vec_elems": p.vec_elems, "wide": bool(p.wide),
         "a_mode": p.a_mode, "b_mode": p.b_mode, "b2_mode": p.b2_mode, "block": p.block,
         "streaming": bool(p.streaming), "tile_a": p.tile_a, "tile_b": p.tile_b,
-        "grid": p.grid, "n_elems": p.n_elems,
+        "grid": p.grid, "n_elems": p.n_elems, "blocks": p.blocks,
         "joint": [(p.ext[i], p.s_src[i], p.s_dst[i]) for i in range(r)],
     }
 

@@ -1135,7 +1135,31 @@ int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_el
   const uintptr_t d1 = d0 + (uintptr_t)dst_capacity_elems * elem_bytes;
   if (s0 < d1 && d0 < s1) return LR_ERR_OVERLAP;
   if ((rc = verify_plan(p, src_capacity_elems, dst_capacity_elems))) return rc;
-  return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
+  int64_t cext[kMaxJoint], nblocks = 0;
+  if (!block_extents(p, flags, cext, &nblocks)) return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
+  // too large for 32-bit offsets: blocks of the joint modes, each within 32 bits,
+  // launched one after another on the stream (disjoint parts of an injective copy)
+  int64_t start[kMaxJoint] = {0};
+  for (int64_t blk = 0; blk < nblocks; ++blk) {
+    lr_layout ls, ld;
+    int64_t os = 0, od = 0;
+    make_block(p, cext, start, &ls, &ld, &os, &od);
+    const char* s = (const char*)src + os * (int64_t)elem_bytes;
+    char* d = (char*)dst + od * (int64_t)elem_bytes;
+    const int64_t cs = cosize_bound(&ls), cd = cosize_bound(&ld);
+    Plan pb;
+    if ((rc = plan_copy(&ls, cs, ptr_align(s), &ld, cd, ptr_align(d), elem_bytes, flags, &pb))) return rc;
+    if (pb.wide) return LR_ERR_PATH;
+    pb.nt = p.nt && pb.path != LR_PATH_DUAL && pb.path != LR_PATH_ALIAS;  // the whole copy's policy
+    if ((rc = verify_plan(pb, cs, cd))) return rc;
+    if ((rc = run_copy(s, &ls, d, &ld, pb, (hipStream_t)stream))) return rc;
+    for (int k = 0; k < p.rank; ++k) {  // next block, mode 0 fastest
+      start[k] += cext[k];
+      if (start[k] < p.m[k].ext) break;
+      start[k] = 0;
+    }
+  }
+  return LR_OK;
 }
 
 }  // extern "C"

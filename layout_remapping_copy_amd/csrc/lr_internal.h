@@ -93,6 +93,16 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
 // Re-checks the invariants the chosen kernel relies on; LR_ERR_PATH if violated.
 int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap);
 
+// A copy that needs 64-bit offsets only because of its size runs as blocks of its
+// joint modes, each small enough for 32-bit offsets and planned on its own.
+// block_extents: per-mode block extents (cext) and the number of blocks, or false
+// when the copy is not cut (not wide, 64-bit indices requested, a forced path, a
+// swizzle, or too many blocks).  make_block: the layouts of the block starting at
+// the per-mode indices `start`, and its base offsets on each side (elements).
+bool block_extents(const Plan& p, uint32_t flags, int64_t* cext, int64_t* nblocks);
+void make_block(const Plan& p, const int64_t* cext, const int64_t* start, lr_layout* ls, lr_layout* ld,
+                int64_t* src_off, int64_t* dst_off);
+
 void set_hip_error(const char* text);
 
 }  // namespace lr

@@ -219,12 +219,17 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     return LR_OK;
   }
   if (p->wide) {
-    if (forced >= 0 && forced != LR_PATH_GENERIC) return LR_ERR_PATH;
-    p->path = LR_PATH_GENERIC;
-    p->v = 1;
+    // 64-bit index arithmetic: the unit-per-lane kernel, four units per lane, with
+    // 16-byte vectors along a common contiguous mode when there is one
+    if (forced >= 0 && forced != LR_PATH_GENERIC && forced != LR_PATH_VECTOR) return LR_ERR_PATH;
+    const bool c0 = p->m[0].ss == 1 && p->m[0].sd == 1;
+    const int64_t v = (c0 && forced != LR_PATH_GENERIC) ? unit_width(*p, src_align, dst_align) : 1;
+    if (forced == LR_PATH_VECTOR && v <= 1) return LR_ERR_PATH;
+    p->path = v > 1 ? LR_PATH_VECTOR : LR_PATH_GENERIC;
+    p->v = (int)v;
     p->unroll = 4;
-    p->n_units = n;
-    p->grid = (n + 1023) / 1024;
+    p->n_units = n / v;
+    p->grid = (p->n_units + 1023) / 1024;
     return LR_OK;
   }
 
@@ -554,6 +559,65 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
   return bad();
 }
 
+bool block_extents(const Plan& p, uint32_t flags, int64_t* cext, int64_t* nblocks) {
+  if (!p.wide || (flags & (LR_COPY_WIDE_INDEX | 0xFF00u)) || p.path == LR_PATH_DUAL || p.path == LR_PATH_ALIAS)
+    return false;
+  if (p.sw_s.b || p.sw_d.b || p.rank < 1) return false;  // a base offset would move the swizzle's bits
+  const int64_t lim = int64_t(1) << 31;
+  for (int k = 0; k < p.rank; ++k) cext[k] = p.m[k].ext;
+  for (;;) {
+    int64_t n = 1, rs = 0, rd = 0;
+    for (int k = 0; k < p.rank; ++k) {
+      n *= cext[k];
+      rs += (cext[k] - 1) * p.m[k].ss;
+      rd += (cext[k] - 1) * p.m[k].sd;
+    }
+    if (n < lim && rs < lim - 1 && rd < lim - 1) break;
+    // halve the mode reaching furthest on either side (by count when strides are 0)
+    int best = -1;
+    int64_t reach = -1;
+    for (int k = 0; k < p.rank; ++k) {
+      if (cext[k] < 2) continue;
+      const int64_t r = (cext[k] - 1) * std::max<int64_t>(1, std::max(p.m[k].ss, p.m[k].sd));
+      if (r > reach) {
+        reach = r;
+        best = k;
+      }
+    }
+    if (best < 0) return false;
+    const int64_t c = cext[best], h = (c + 1) / 2;
+    // keep block starts on multiples of 64 elements (vector units and tiles stay whole)
+    cext[best] = c > 128 ? (h + 63) / 64 * 64 : h;
+  }
+  int64_t nb = 1;
+  for (int k = 0; k < p.rank; ++k) {
+    nb *= (p.m[k].ext + cext[k] - 1) / cext[k];
+    if (nb > 65536) return false;
+  }
+  if (nb < 2) return false;
+  *nblocks = nb;
+  return true;
+}
+
+void make_block(const Plan& p, const int64_t* cext, const int64_t* start, lr_layout* ls, lr_layout* ld,
+                int64_t* src_off, int64_t* dst_off) {
+  std::memset(ls, 0, sizeof(*ls));
+  std::memset(ld, 0, sizeof(*ld));
+  ls->nleaves = ld->nleaves = ls->nmodes = ld->nmodes = p.rank;
+  int64_t os = 0, od = 0;
+  for (int k = 0; k < p.rank; ++k) {
+    const int64_t e = std::min(cext[k], p.m[k].ext - start[k]);
+    ls->shape[k] = ld->shape[k] = e;
+    ls->stride[k] = p.m[k].ss;
+    ld->stride[k] = p.m[k].sd;
+    ls->mode_end[k] = ld->mode_end[k] = k + 1;
+    os += start[k] * p.m[k].ss;
+    od += start[k] * p.m[k].sd;
+  }
+  *src_off = os;
+  *dst_off = od;
+}
+
 }  // namespace lr
 
 using namespace lr;
@@ -568,6 +632,25 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   if (rc) return rc;
   if ((rc = verify_plan(p, src_capacity_elems, dst_capacity_elems))) return rc;
   std::memset(out, 0, sizeof(*out));
+  out->blocks = 1;
+  int64_t cext[kMaxJoint], nblocks = 0;
+  if (block_extents(p, flags, cext, &nblocks)) {
+    // report the first block's plan (it starts at offset 0 on both sides)
+    int64_t start[kMaxJoint] = {0}, os = 0, od = 0;
+    lr_layout ls, ld;
+    make_block(p, cext, start, &ls, &ld, &os, &od);
+    Plan pb;
+    if ((rc = plan_copy(&ls, cosize_bound(&ls), src_align, &ld, cosize_bound(&ld), dst_align, elem_bytes, flags, &pb)))
+      return rc;
+    if (pb.wide) return LR_ERR_PATH;
+    if ((rc = verify_plan(pb, cosize_bound(&ls), cosize_bound(&ld)))) return rc;
+    pb.nt = p.nt && pb.path != LR_PATH_DUAL && pb.path != LR_PATH_ALIAS;
+    pb.n = p.n;
+    pb.rank = p.rank;
+    std::memcpy(pb.m, p.m, sizeof(p.m));
+    out->blocks = nblocks;
+    p = pb;
+  }
   out->path = p.path;
   out->elem_bytes = p.eb;
   out->vec_elems = p.v;

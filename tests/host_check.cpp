@@ -182,6 +182,64 @@ static int run_fuzz() {
     for (int path = 0; path < 8; ++path) lr_copy_plan(&a, 1 << 20, 16, &a, 1 << 20, 16, 1, LR_COPY_FORCE_PATH(path), &p);
     ++n_ok;
   }
+  // copies too large for 32-bit offsets: the blocks cover every index once and fit
+  for (int it = 0; it < 3000; ++it) {
+    int nl = 1 + (int)(rng() % 4);
+    lr_layout a, b;
+    std::memset(&a, 0, sizeof(a));
+    a.nleaves = a.nmodes = nl;
+    int64_t n = 1;
+    for (int i = 0; i < nl; ++i) {
+      a.shape[i] = 1 + (int64_t)(rng() % (1u << (8 + rng() % 16)));
+      if (n > (int64_t(1) << 40) / a.shape[i]) a.shape[i] = 1;
+      n *= a.shape[i];
+      a.mode_end[i] = i + 1;
+    }
+    // source: compact in a random order, sometimes padded; destination: compact
+    int perm[LR_MAX_LEAVES];
+    for (int i = 0; i < nl; ++i) perm[i] = i;
+    for (int i = nl - 1; i > 0; --i) std::swap(perm[i], perm[rng() % (i + 1)]);
+    b = a;
+    int64_t w = 1, wd = 1;
+    for (int i = 0; i < nl; ++i) {
+      a.stride[perm[i]] = w;
+      w *= a.shape[perm[i]] + (rng() % 4 == 0 ? (int64_t)(rng() % 5) : 0);
+      b.stride[i] = wd;
+      wd *= b.shape[i];
+    }
+    lr::Plan p;
+    if (lr::plan_copy(&a, w, 16, &b, wd, 16, 2, 0, &p) != LR_OK) continue;
+    int64_t cext[lr::kMaxJoint], nb = 0;
+    if (!lr::block_extents(p, 0, cext, &nb)) continue;
+    int64_t start[lr::kMaxJoint] = {0}, covered = 0;
+    for (int64_t k = 0; k < nb; ++k) {
+      lr_layout ls, ld;
+      int64_t os, od;
+      lr::make_block(p, cext, start, &ls, &ld, &os, &od);
+      int64_t bn = 1;
+      for (int i = 0; i < ls.nleaves; ++i) bn *= ls.shape[i];
+      lr::Plan pb;
+      if (bn >= (int64_t(1) << 31) || lr::cosize_bound(&ls) >= (int64_t(1) << 31) ||
+          lr::cosize_bound(&ld) >= (int64_t(1) << 31) || os + lr::cosize_bound(&ls) > w ||
+          od + lr::cosize_bound(&ld) > wd ||
+          lr::plan_copy(&ls, lr::cosize_bound(&ls), 16, &ld, lr::cosize_bound(&ld), 16, 2, 0, &pb) != LR_OK ||
+          pb.wide || lr::verify_plan(pb, lr::cosize_bound(&ls), lr::cosize_bound(&ld)) != LR_OK) {
+        std::printf("bad block %lld of %lld\n", (long long)k, (long long)nb);
+        return 1;
+      }
+      covered += bn;
+      for (int i = 0; i < p.rank; ++i) {
+        start[i] += cext[i];
+        if (start[i] < p.m[i].ext) break;
+        start[i] = 0;
+      }
+    }
+    if (covered != n) {
+      std::printf("blocks cover %lld of %lld\n", (long long)covered, (long long)n);
+      return 1;
+    }
+    ++n_ok;
+  }
   // malformed and adversarial descriptors
   const char* bad[] = {"", "(", "()", "(1,2):(3)", "Sw<1,2> o 4:1", "((((((((((((((((((((((((((((((((((4))))))))))"
                        "))))))))))))))))))))))):1", "99999999999999999999:1", "(4,2):(1,2) trailing", "Sw<70,0,80> o 4:1"};

@@ -383,6 +383,38 @@ def test_full_transpose_both_variants(dev, monkeypatch, nt):
         assert np.array_equal(d.cpu().numpy(), want)
 
 
+@pytest.mark.slow
+def test_copy_beyond_2_31_elements(dev):
+    """More than 2^31 elements: by default the copy is cut into blocks that each fit
+    32-bit offsets (launched at offset base pointers); with LR_COPY_WIDE_INDEX it is
+    one launch with 64-bit index arithmetic."""
+    N = 715827883                      # 3 * N = 2^31 + 1
+    M = 46400                          # M^2 > 2^31, blocks of 23232 and 23168 rows
+    cases = [(f"(3,{N}):({N},1)", f"(3,{N}):(1,3)", 3 * N, lambda s: s.reshape(3, N).T.reshape(-1), "generic", 0),
+             (f"{(1 << 31) + 16}:1", f"{(1 << 31) + 16}:1", (1 << 31) + 16, lambda s: s, "vector", 0),
+             (f"{(1 << 31) + 16}:1", f"{(1 << 31) + 16}:1", (1 << 31) + 16, lambda s: s, "vector",
+              lr.COPY_WIDE_INDEX),
+             (f"({M},{M}):({M},1)", f"({M},{M}):(1,{M})", M * M, lambda s: s.reshape(M, M).T.reshape(-1),
+              "transpose", 0)]
+    for ts, td, n, form, path, flags in cases:
+        p = lr.copy_plan(ts, n, td, n, 1, flags)
+        assert p["path"] == path and (p["wide"] if flags else p["blocks"] > 1), p
+        say("beyond 2^31", ts, "->", td, p["path"], "vec", p["vec_elems"], "blocks", p["blocks"], "wide", p["wide"])
+        src = np.random.default_rng(n % 1000).integers(0, 256, n, dtype=np.uint8)
+        s = torch.from_numpy(src).to(dev)
+        d = torch.full((n,), 0xA5, dtype=torch.uint8, device=dev)
+        lr.layout_copy(s, ts, d, td, elem_bytes=1, flags=flags)
+        torch.cuda.synchronize()
+        got = d.cpu().numpy()
+        del s, d
+        torch.cuda.empty_cache()
+        ks = np.concatenate([np.random.default_rng(3).integers(0, n, 1 << 18, dtype=np.int64),
+                             np.arange(n - 4096, n, dtype=np.int64)])
+        assert O.copy_sampled_check(src, O.parse(ts), got, O.parse(td), 1, ks) == 0
+        assert np.array_equal(got, form(src))
+        del src, got
+
+
 # ---------------------------------------------------------------------------
 # Tuning variants chosen at plan time (tile shapes, narrow-load interleave)
 # ---------------------------------------------------------------------------

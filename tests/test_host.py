@@ -464,10 +464,37 @@ def test_plan_alignment_drops_vector_width():
 
 
 def test_plan_wide_index_for_big_offsets():
+    # offsets beyond 32 bits: four blocks (one per far source row) at offset bases,
+    # or one 64-bit launch when asked for
     p = lr.copy_plan("(2,4):(1,1099511627776)", 3298534883330, "(2,4):(4,1)", 8, 1)
-    assert p["wide"] and p["path"] == "generic"
+    assert not p["wide"] and p["blocks"] == 4 and p["path"] == "generic"
+    p = lr.copy_plan("(2,4):(1,1099511627776)", 3298534883330, "(2,4):(4,1)", 8, 1, lr.COPY_WIDE_INDEX)
+    assert p["wide"] and p["blocks"] == 1 and p["path"] == "generic"
     p = lr.copy_plan("64:1", 64, "64:1", 64, 4, lr.COPY_WIDE_INDEX)
-    assert p["wide"]
+    assert p["wide"] and p["path"] == "vector" and p["vec_elems"] == 4
+    # more than 2^31 elements: 64-bit indices, still 16-byte vectors along a common
+    # contiguous mode; a forced generic plan moves single elements
+    n = (1 << 31) + 16
+    p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 1, lr.COPY_WIDE_INDEX)
+    assert p["wide"] and p["path"] == "vector" and p["vec_elems"] == 16 and p["grid"] == -(-n // 16 // 1024)
+    assert p["blocks"] == 1
+    p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 1, lr.COPY_FORCE_PATH(lr.PATH_GENERIC))
+    assert p["path"] == "generic" and p["vec_elems"] == 1 and p["wide"] and p["blocks"] == 1
+    # by default such a copy is cut into blocks that each fit 32-bit offsets
+    p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 1)
+    assert p["blocks"] == 2 and not p["wide"] and p["path"] == "vector" and p["n_elems"] == n
+    # a 65536^2 fp16 transpose: four 32768^2 blocks on the transpose path
+    m = 65536
+    p = lr.copy_plan(f"({m},{m}):({m},1)", m * m, f"({m},{m}):(1,{m})", m * m, 2)
+    assert p["blocks"] == 4 and not p["wide"] and p["path"] == "transpose" and p["streaming"]
+    assert p["grid"] == (32768 // 256) ** 2
+    # a swizzle keeps the single 64-bit launch
+    p = lr.copy_plan(f"Sw<3,3,3> o ({m},{m}):({m},1)", m * m, f"({m},{m}):(1,{m})", m * m, 2)
+    assert p["blocks"] == 1 and p["wide"]
+    p = lr.copy_plan("(16,3):(1,32)", 96, "(16,3):(1,16)", 48, 2, lr.COPY_WIDE_INDEX)
+    assert p["path"] == "vector" and p["vec_elems"] == 8
+    with pytest.raises(lr.LayoutRemapError):
+        lr.copy_plan("(8,8):(8,1)", 64, "(8,8):(1,8)", 64, 2, lr.COPY_WIDE_INDEX | lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
 
 
 # ---------------------------------------------------------------------------

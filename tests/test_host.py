@@ -334,6 +334,22 @@ def test_transpose_lds_tile_accesses_conflict_free(ta, tb):
         assert rep["conflict_cycles"] == 0
 
 
+def test_staged_gather_conflicts_match_the_counter():
+    """The padded-tiles kernel gathers 4-byte words from LDS: lane l of a wave reads
+    word 72*(l/16) + (c%8) + 9*(c/8) + 18x with c = l % 16 (16 lanes per tile, the
+    tile's 72-word footprint with its pad word every 9th), i.e. the lane layout
+    (8,2,4):(1,9,72) plus a constant.  The model gives 2 extra cycles per wave read;
+    2^20 gather reads per launch then make 2,097,152 conflict cycles, the value
+    SQ_LDS_BANK_CONFLICT shows for that kernel.  No per-tile stride removes them:
+    each tile's 16 words leave a hole in its bank set, so two tiles in one phase
+    always share a bank."""
+    r = lr.access_check("(8,2,4):(1,9,72)", 4, 64, "read")
+    assert (r["cycles"], r["phases"], r["conflict_cycles"]) == (4, 2, 2)
+    assert (1 << 20) * r["conflict_cycles"] == 2097152
+    for S in range(72, 72 + 64):
+        assert lr.access_check(f"(8,2,4):(1,9,{S})", 4, 64, "read")["conflict_cycles"] == 2
+
+
 def test_common_vector_sound_and_tight_on_workloads():
     rng = random.Random(23)
     for _ in range(1500):

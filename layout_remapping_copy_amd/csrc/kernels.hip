@@ -110,6 +110,16 @@ __device__ __forceinline__ void gstore(void* p, const C& v) {
     *(N*)p = x;
 }
 
+// gfx950 direct global -> LDS load of 16 bytes per lane: lane i of the wave writes
+// its bytes at lds_wave + 16*i (lds_wave is the wave's common LDS base).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+// NT: the non-temporal cache-policy bit (2 on gfx950).
+template <bool NT>
+__device__ __forceinline__ void load_to_lds16(const void* g, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds((const global_void_t*)g, (lds_void_t*)lds_wave, 16, 0, NT ? 2 : 0);
+}
+
 // ------------------------------------------------------------------ eval
 
 struct EvalArgs {
@@ -426,30 +436,9 @@ struct TransposeArgs {
   FD fd_gta, fd_gtb;
 };
 
-// Tile of (TA*V) x (TB*V) elements per workgroup of TA*TB lanes; each lane owns a
-// V x V register block: V chunk loads of V elements along a (one per b row), an
-// in-register transpose, V chunk stores of V elements along b (one per a row).
-// V*EB == 16 normally, so every global access is a 16-byte vector.
-//
-// LDS == true: the transposed chunks go through LDS so that a wave's stores run
-// along TB consecutive chunks of one dst row (TB*16 contiguous bytes per row for
-// 16-B chunks).  The LDS tile is addressed [row][chunk ^ ((row / V) % TB)], an XOR
-// swizzle of the 16-byte chunk index ([print_layout page, sections 4.3 and 5.2]:
-// XOR spreads a column across banks, where padding would also do), so both the
-// chunk writes (lanes of one chunk column) and the row reads (lanes of one row)
-// touch distinct chunk slots of a bank window.
-// LDS == false (TA == TB == 16 only): lanes are arranged 8 x 8 per wave so each
-// load and store instruction covers eight full 128-byte lines, with no LDS.
-template <int EB, int V, bool LDS, int TA, int TB, bool NT>
-__global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
-  using T = typename Raw<EB>::T;
-  using C = Chunk<T, V>;
-  constexpr int NTH = TA * TB;  // threads
-  static_assert(LDS || (TA == 16 && TB == 16), "the direct variant uses 16 x 16 blocks");
-  const char* __restrict__ src = (const char*)t.src;
-  char* __restrict__ dst = (char*)t.dst;
-
-  uint32_t blk = blockIdx.x, ta, tb, r2;
+// Workgroup number -> (a-tile, b-tile, batch index) in the order t.order selects.
+__device__ __forceinline__ void transpose_tile(const TransposeArgs& t, uint32_t blk, uint32_t& ta, uint32_t& tb,
+                                               uint32_t& r2) {
   if (t.order == 0) {
     uint32_t r1 = fdiv(blk, t.fd_ta);
     ta = blk - r1 * t.tiles_a;
@@ -487,6 +476,33 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
     ta = 4 * ga + (w & 3u);
     tb = 4 * gb + (w >> 2);
   }
+}
+
+// Tile of (TA*V) x (TB*V) elements per workgroup of TA*TB lanes; each lane owns a
+// V x V register block: V chunk loads of V elements along a (one per b row), an
+// in-register transpose, V chunk stores of V elements along b (one per a row).
+// V*EB == 16 normally, so every global access is a 16-byte vector.
+//
+// LDS == true: the transposed chunks go through LDS so that a wave's stores run
+// along TB consecutive chunks of one dst row (TB*16 contiguous bytes per row for
+// 16-B chunks).  The LDS tile is addressed [row][chunk ^ ((row / V) % TB)], an XOR
+// swizzle of the 16-byte chunk index ([print_layout page, sections 4.3 and 5.2]:
+// XOR spreads a column across banks, where padding would also do), so both the
+// chunk writes (lanes of one chunk column) and the row reads (lanes of one row)
+// touch distinct chunk slots of a bank window.
+// LDS == false (TA == TB == 16 only): lanes are arranged 8 x 8 per wave so each
+// load and store instruction covers eight full 128-byte lines, with no LDS.
+template <int EB, int V, bool LDS, int TA, int TB, bool NT>
+__global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
+  using T = typename Raw<EB>::T;
+  using C = Chunk<T, V>;
+  constexpr int NTH = TA * TB;  // threads
+  static_assert(LDS || (TA == 16 && TB == 16), "the direct variant uses 16 x 16 blocks");
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blockIdx.x, ta, tb, r2);
   uint32_t bs, bd;
   batch_offsets(t.batch, r2, &bs, &bd);
 
@@ -547,6 +563,74 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
       gstore<NT, C>(dst + (size_t)dof * EB, v);
     }
   }
+}
+
+// The same tile with its source chunks loaded straight into LDS (gfx950 direct
+// loads): the tile's TB*V source rows of TA chunks land in LDS without passing
+// through registers, then each lane reads its V x V block (V chunks of one chunk
+// column, V consecutive rows), transposes it in registers and stores V chunks.
+// Lane tid = beta + TB * alpha owns a-chunk alpha and b rows V*beta .. V*beta+V-1,
+// so TB consecutive lanes store TB consecutive chunks of one destination row.  LDS
+// slot of (row r, chunk column c) = r * TA + (c ^ ((r / V) % 16)): the 16 lanes of
+// one 16-byte read phase (consecutive beta) then fall on 16 distinct slots modulo
+// 16, i.e. all 64 banks.  A direct load fills 64 consecutive slots per wave, so
+// lane l of load k of wave w takes slot 64 * (w * V + k) + l and loads the source
+// chunk that belongs there.  Needs full 16-byte chunks (V * EB == 16), TB >= 16
+// and TA in {16, 32}.
+template <int EB, int V, int TA, int TB, bool NT>
+__global__ void __launch_bounds__(TA * TB) k_transpose_dl(TransposeArgs t) {
+  using T = typename Raw<EB>::T;
+  using C = Chunk<T, V>;
+  static_assert(V * EB == 16 && TB >= 16 && (TA == 16 || TA == 32), "full chunks, 16-wide phases");
+  constexpr int NTH = TA * TB;
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+  __shared__ C tile[TB * V * TA];
+
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blockIdx.x, ta, tb, r2);
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const int base = 64 * (wave * V + k);       // first slot of this wave's load
+    const int s = base + lane;
+    const int r = s / TA, cs = s % TA;
+    const int c = cs ^ ((r / V) % 16);          // chunk column stored in slot s
+    const uint32_t a = a0 + V * c, b = b0 + r;
+    if (a < t.ext_a && b < t.ext_b) {
+      const uint32_t so = swz32(a + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
+      load_to_lds16<NT>(src + (size_t)so * EB, tile + __builtin_amdgcn_readfirstlane(base));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+  __syncthreads();
+
+  const int beta = tid % TB, alpha = tid / TB;
+  C in[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int r = V * beta + j;
+    in[j] = tile[r * TA + (alpha ^ ((r / V) % 16))];
+  }
+  C out[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+#pragma unroll
+    for (int j = 0; j < V; ++j) out[i].e[j] = in[j].e[i];
+  const uint32_t b = b0 + V * beta;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t a = a0 + V * alpha + i;
+    if (a < t.ext_a && b < t.ext_b) {
+      const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+      gstore<NT, C>(dst + (size_t)dof * EB, out[i]);
+    }
+  }
+  (void)NTH;
 }
 
 // ------------------------------------------------------------------ interleave
@@ -676,7 +760,7 @@ struct StagedArgs {
 // footprint of K tiles in LDS with 16-byte loads (pad words included: DRAM
 // fetches them with their lines anyway), then each lane builds 16-byte dst chunks
 // by gathering elements from LDS and stores them contiguously.
-template <int EB, bool NT>
+template <int EB, bool NT, bool DL>
 __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
@@ -703,19 +787,32 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
     *byte = (size_t)(tile * t.Ts + bs) * EB + (size_t)(idx - kk * t.Fc) * 16;
     return tile < t.T;
   };
-  for (uint32_t i0 = threadIdx.x; i0 < nload; i0 += 1024) {
-    size_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
-    const bool k0 = chunk_ok(i0, &b0), k1 = chunk_ok(i0 + 256, &b1), k2 = chunk_ok(i0 + 512, &b2),
-               k3 = chunk_ok(i0 + 768, &b3);
-    uint4 v0, v1, v2, v3;
-    if (k0) v0 = gload<NT, uint4>(src + b0);
-    if (k1) v1 = gload<NT, uint4>(src + b1);
-    if (k2) v2 = gload<NT, uint4>(src + b2);
-    if (k3) v3 = gload<NT, uint4>(src + b3);
-    if (k0) lds[i0] = v0;
-    if (k1) lds[i0 + 256] = v1;
-    if (k2) lds[i0 + 512] = v2;
-    if (k3) lds[i0 + 768] = v3;
+  if constexpr (DL) {
+    // Direct loads: chunk idx goes to lds[idx]; the 64 lanes of a wave take 64
+    // consecutive chunks, so the wave's LDS base is the chunk of its lane 0.  No
+    // registers hold the data, so every load of the footprint is issued at once.
+    const uint32_t lane = threadIdx.x & 63u;
+    for (uint32_t idx = threadIdx.x; idx < nload + lane; idx += 256) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(idx - lane);
+      size_t b = 0;
+      if (chunk_ok(idx, &b)) load_to_lds16<NT>(src + b, lds + base);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes have landed
+  } else {
+    for (uint32_t i0 = threadIdx.x; i0 < nload; i0 += 1024) {
+      size_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+      const bool k0 = chunk_ok(i0, &b0), k1 = chunk_ok(i0 + 256, &b1), k2 = chunk_ok(i0 + 512, &b2),
+                 k3 = chunk_ok(i0 + 768, &b3);
+      uint4 v0, v1, v2, v3;
+      if (k0) v0 = gload<NT, uint4>(src + b0);
+      if (k1) v1 = gload<NT, uint4>(src + b1);
+      if (k2) v2 = gload<NT, uint4>(src + b2);
+      if (k3) v3 = gload<NT, uint4>(src + b3);
+      if (k0) lds[i0] = v0;
+      if (k1) lds[i0 + 256] = v1;
+      if (k2) lds[i0 + 512] = v2;
+      if (k3) lds[i0 + 768] = v3;
+    }
   }
   __syncthreads();
 
@@ -824,7 +921,25 @@ static void launch_transpose_shape(const TransposeArgs& a, unsigned grid, hipStr
 }
 
 template <int EB, int V, bool NT>
-static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, unsigned grid, hipStream_t st) {
+static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool dl, unsigned grid,
+                               hipStream_t st) {
+  if constexpr (V * EB == 16) {
+    if (dl && lds) {
+      switch (shape) {
+        case 0: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a); return true;
+        case 1: hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 16, NT>), dim3(grid), dim3(512), 0, st, a); return true;
+        case 2: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 32, NT>), dim3(grid), dim3(512), 0, st, a); return true;
+        case 3:
+          if constexpr (V <= 8) {
+            hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 32, NT>), dim3(grid), dim3(1024), 0, st, a);
+            return true;
+          }
+          break;
+        default: break;
+      }
+      return false;
+    }
+  }
   if (!lds) {
     if (shape != 0) return false;
     hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a);
@@ -847,22 +962,23 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, unsi
 }
 
 template <int EB, bool NT>
-static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int shape, unsigned grid, hipStream_t st) {
+static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int shape, bool dl, unsigned grid,
+                                hipStream_t st) {
   switch (v) {
-    case 1: return launch_transpose_v<EB, 1, NT>(a, lds, shape, grid, st);
-    case 2: if constexpr (EB <= 8) return launch_transpose_v<EB, 2, NT>(a, lds, shape, grid, st); break;
-    case 4: if constexpr (EB <= 4) return launch_transpose_v<EB, 4, NT>(a, lds, shape, grid, st); break;
-    case 8: if constexpr (EB <= 2) return launch_transpose_v<EB, 8, NT>(a, lds, shape, grid, st); break;
-    case 16: if constexpr (EB == 1) return launch_transpose_v<EB, 16, NT>(a, lds, shape, grid, st); break;
+    case 1: return launch_transpose_v<EB, 1, NT>(a, lds, shape, dl, grid, st);
+    case 2: if constexpr (EB <= 8) return launch_transpose_v<EB, 2, NT>(a, lds, shape, dl, grid, st); break;
+    case 4: if constexpr (EB <= 4) return launch_transpose_v<EB, 4, NT>(a, lds, shape, dl, grid, st); break;
+    case 8: if constexpr (EB <= 2) return launch_transpose_v<EB, 8, NT>(a, lds, shape, dl, grid, st); break;
+    case 16: if constexpr (EB == 1) return launch_transpose_v<EB, 16, NT>(a, lds, shape, dl, grid, st); break;
   }
   return false;
 }
 
 template <int EB>
-static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, bool nt, unsigned grid,
+static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, bool nt, bool dl, unsigned grid,
                              hipStream_t st) {
-  return nt ? launch_transpose_nt<EB, true>(a, v, lds, shape, grid, st)
-            : launch_transpose_nt<EB, false>(a, v, lds, shape, grid, st);
+  return nt ? launch_transpose_nt<EB, true>(a, v, lds, shape, dl, grid, st)
+            : launch_transpose_nt<EB, false>(a, v, lds, shape, dl, grid, st);
 }
 
 template <int EB, bool NARROW, bool NT>
@@ -991,7 +1107,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       }
       const bool lds = p.path == LR_PATH_TRANSPOSE;
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, p.direct, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
@@ -1044,10 +1160,16 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       }
       a.swd = swz_arg(p.sw_d);
       const size_t shm = (size_t)p.staged_K * (size_t)p.staged_Fc * 16;
-      if (p.nt) {
-        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, true>), dim3(grid), dim3(256), shm, st, a));
+      if (p.direct) {
+        if (p.nt) {
+          LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, true, true>), dim3(grid), dim3(256), shm, st, a));
+        } else {
+          LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, false, true>), dim3(grid), dim3(256), shm, st, a));
+        }
+      } else if (p.nt) {
+        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, true, false>), dim3(grid), dim3(256), shm, st, a));
       } else {
-        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, false>), dim3(grid), dim3(256), shm, st, a));
+        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, false, false>), dim3(grid), dim3(256), shm, st, a));
       }
       return check_launch();
     }

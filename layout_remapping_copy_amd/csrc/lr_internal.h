@@ -80,6 +80,7 @@ struct Plan {
   // workgroup order (0: a-tiles fastest, 1: b-tiles fastest, 2: diagonal, 3:
   // diagonal over 4x4 tile groups)
   bool nt;
+  bool direct;        // staged: direct global -> LDS loads (no register round trip)
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB

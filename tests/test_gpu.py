@@ -474,6 +474,76 @@ def test_streaming_accesses_every_path(dev, env_knob):
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
 
 
+@pytest.mark.parametrize("shape", [0, 1, 2, 3])
+def test_transpose_direct_loads(dev, env_knob, shape):
+    """The transpose with its source tile loaded straight into LDS."""
+    env_knob.setenv("LR_TDIRECT", "1")
+    env_knob.setenv("LR_TSHAPE", str(shape))
+    cases = [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
+             ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 7560, 2),
+             ("(100,72):(72,1)", "(100,72):(1,100)", 7200, 4),
+             ("(64,96,5):(96,1,6144)", "(64,96,5):(1,64,6144)", 30720, 8),
+             ("(1024,512):(512,1)", "(1024,512):(1,1024)", 1024 * 512, 2),
+             ("(48,80):(80,1)", "(48,80):(1,48)", 3840, 16),
+             (W.small("interleave_cm").src_layout, W.small("interleave_cm").dst_layout,
+              W.small("interleave_cm").src_elems, 2)]
+    ran = 0
+    for ci, (ts, td, n, eb) in enumerate(cases):
+        src = np.random.default_rng(ci).integers(0, 256, n * eb, dtype=np.uint8)
+        dst = np.full(n * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for nt in ("0", "1"):
+            env_knob.setenv("LR_NT", nt)
+            for orient in ("0", "1", "2", "3"):
+                env_knob.setenv("LR_TORDER", orient)
+                p = lr.copy_plan(ts, n, td, n, eb)
+                if p["path"] != "transpose":
+                    continue
+                say("transpose direct", shape, ts, "eb", eb, "nt", nt, "order", orient, "tile", p["tile_a"], p["tile_b"])
+                assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, nt, orient)
+                ran += 1
+    assert ran >= 16
+
+
+@pytest.mark.slow
+def test_full_transpose_direct_loads(dev, monkeypatch):
+    monkeypatch.setenv("LR_TDIRECT", "1")
+    w = W.full("transpose")
+    src = W.make_src(w)
+    s = torch.from_numpy(src).to(dev)
+    d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
+    say("full transpose direct loads")
+    lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), F.transpose(src, 8192))
+
+
+@pytest.mark.parametrize("direct", [0, 1])
+def test_staged_direct_loads(dev, env_knob, direct):
+    """The staged path with its footprint loaded straight into LDS (gfx950 direct
+    loads) or through registers; both streaming policies."""
+    env_knob.setenv("LR_DIRECT", str(direct))
+    cases = [(W.small("padtiles").src_layout, W.small("padtiles").dst_layout, W.small("padtiles").src_elems,
+              W.small("padtiles").dst_elems, 4)]
+    cases += [c for c in _case_pairs()]
+    ran = 0
+    for nt in ("0", "1"):
+        env_knob.setenv("LR_NT", nt)
+        for ci, (ts, td, ns, nd, eb) in enumerate(cases):
+            flags = lr.COPY_FORCE_PATH(lr.PATH_STAGED)
+            try:
+                lr.copy_plan(ts, ns, td, nd, eb, flags)
+            except lr.LayoutRemapError:
+                continue
+            src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
+            dst = np.full(nd * eb, 0xA5, np.uint8)
+            want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+            say("staged direct", direct, "nt", nt, ts, "->", td, "eb", eb)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
+            ran += 1
+    assert ran >= 4
+
+
 @pytest.mark.parametrize("narrow", [0, 1])
 def test_interleave_variants(dev, env_knob, narrow):
     env_knob.setenv("LR_INARROW", str(narrow))

@@ -334,6 +334,34 @@ def test_transpose_lds_tile_accesses_conflict_free(ta, tb):
         assert rep["conflict_cycles"] == 0
 
 
+@pytest.mark.parametrize("ta,tb", [(16, 16), (32, 16), (16, 32), (32, 32)])
+def test_direct_load_transpose_lds_reads_conflict_free(ta, tb):
+    """The direct-load transpose keeps source chunk (row r, column c) at LDS slot
+    r*TA + (c ^ ((r/V) % 16)); lane tid = beta + TB*alpha reads rows V*beta + j of
+    column alpha.  For wave 0 and j = 0 that is Sw<4,0,log2(V*TA)> o
+    (TB,64/TB):(V*TA,1) over the lane (other waves and j XOR or shift by
+    constants), conflict-free for 16-byte reads; the loads write 64 consecutive
+    slots per wave."""
+    for V in (1, 2, 4, 8, 16):
+        if ta * tb * V * 16 > 160 * 1024:
+            continue
+        S = (V * ta).bit_length() - 1
+        text = f"Sw<4,0,{S}> o ({tb},{64 // tb}):({V * ta},1)" if tb < 64 else f"Sw<4,0,{S}> o 64:{V * ta}"
+        rep = lr.access_check(text, 16, 64, "read")
+        want = [(V * (t % tb)) * ta + ((t // tb) ^ ((t % tb) % 16)) for t in range(64)]
+        assert rep["offsets"] == want, text
+        assert rep["conflict_cycles"] == 0, (text, rep["conflict_cycles"])
+        assert lr.access_check("64:1", 16, 64, "write")["conflict_cycles"] == 0
+        # every slot of the tile is written once: slot -> (row, column) is a bijection
+        slots = set()
+        for s_ in range(tb * V * ta):
+            r, cs = divmod(s_, ta)
+            c = cs ^ ((r // V) % 16)
+            assert 0 <= c < ta
+            slots.add((r, c))
+        assert len(slots) == tb * V * ta
+
+
 def test_staged_gather_conflicts_match_the_counter():
     """The padded-tiles kernel gathers 4-byte words from LDS: lane l of a wave reads
     word 72*(l/16) + (c%8) + 9*(c/8) + 18x with c = l % 16 (16 lanes per tile, the

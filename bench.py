@@ -74,6 +74,24 @@ def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
     return wall, ev0.elapsed_time(ev1) / steps
 
 
+def _per_launch(lr, torch, pairs, Ls, Ld, eb, launches, flags=0, rotate=True):
+    """Kernel time of each launch (HIP events around it on the launch stream), in us:
+    rotating over the buffer pairs (cold: nothing cached from the previous launch)
+    or on the first pair only (warm: the last-level cache may hold the data)."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    s, d = pairs[0]
+    lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        s, d = pairs[i % len(pairs)] if rotate else pairs[0]
+        e0.record(stream)
+        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+
+
 def _pairs(torch, dev, nbytes_src, nbytes_dst, first_src=None, min_total=1 << 30):
     n = max(2, -(-min_total // (nbytes_src + nbytes_dst)))
     g = torch.Generator(device=dev)
@@ -111,8 +129,7 @@ def _cpu_baseline(w, seconds: float):
             break
     dt = time.perf_counter() - t0
     bytes_ = 2 * rows * n * w.elem_bytes * done
-    del np
-    return {
+    out = {
         "value": round(bytes_ / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
@@ -120,6 +137,29 @@ def _cpu_baseline(w, seconds: float):
         "sample": f"oracle.copy of rows 0..{rows - 1} of the 8192x8192 fp16 transpose "
                   f"({rows}x{n} elements), {done} repetitions in {dt:.1f} s, single NumPy thread",
     }
+    # the same sample on every host thread at once (each thread its own destination)
+    import concurrent.futures as cf
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    if threads > 1:
+        dsts = [W.make_dst(w) for _ in range(threads)]
+
+        def work(i):
+            k, t1 = 0, time.perf_counter()
+            while True:
+                oracle.copy(src, Ls, dsts[i], Ld, w.elem_bytes)
+                k += 1
+                if time.perf_counter() - t1 >= seconds:
+                    return k
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            counts = list(ex.map(work, range(threads)))
+        dt = time.perf_counter() - t0
+        out["parallel"] = {"value": round(2 * rows * n * w.elem_bytes * sum(counts) / dt / 1e9, 4), "cores": threads,
+                           "sample": f"the same sample, {sum(counts)} repetitions over {threads} threads in {dt:.1f} s"}
+    del np
+    return out
 
 
 def counters_run(lr, torch, W, reps: int = 3):
@@ -194,6 +234,9 @@ def main():
     wall_ms, kern_ms = _time_copies(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, args.warmup, flags)
     value = bytes_step / (wall_ms * 1e-3) / 1e9
     achieved = bytes_step / (kern_ms * 1e-3) / 1e9
+    # per-launch kernel times after the timed region: cold (rotating) and warm (one pair)
+    cold = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, flags)
+    warm = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, flags, rotate=False)
 
     # same-box device-to-device copy of equal bytes, for context
     a, b = pairs[0][0], pairs[1][1]
@@ -232,6 +275,9 @@ def main():
             "d2d_copy_GBps": round(d2d, 1),
             "frac_of_d2d_copy": round(value / d2d, 4),
             "buffers": "rotating pairs, >= 1 GiB in total",
+            "kernel_us": {"median": round(cold[len(cold) // 2], 2), "best": round(cold[0], 2),
+                          "warm_median": round(warm[len(warm) // 2], 2), "warm_best": round(warm[0], 2),
+                          "warm": "one buffer pair repeated, the last-level cache may hold part of it"},
         },
         "roofline": {
             "bound": "hbm",
@@ -253,8 +299,11 @@ def main():
             steps = max(10, args.steps)
             _, km = _time_copies(lr, torch, prs, wo.src_layout, wo.dst_layout, wo.elem_bytes, steps, args.warmup)
             gb = W.bytes_moved(wo) / (km * 1e-3) / 1e9
+            warm = _per_launch(lr, torch, prs, wo.src_layout, wo.dst_layout, wo.elem_bytes, steps, rotate=False)
+            wm = warm[len(warm) // 2]
             others[wo.name] = {"path": p["path"], "us": round(km * 1e3, 2), "GBps": round(gb, 1),
-                               "hbm_frac": round(gb / HBM_PEAK_GBPS, 4)}
+                               "hbm_frac": round(gb / HBM_PEAK_GBPS, 4), "us_warm_median": round(wm, 2),
+                               "GBps_warm": round(W.bytes_moved(wo) / (wm * 1e-6) / 1e9, 1)}
             del prs
             torch.cuda.empty_cache()
         out["workloads"] = others

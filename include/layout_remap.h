@@ -337,7 +337,10 @@ int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, 
  * offsets reach 2^31 runs as blocks of its joint modes that each fit 32-bit
  * offsets, launched one after another on the stream at offset base pointers (any
  * partition is the same copy when Ld is injective); with LR_COPY_WIDE_INDEX, a
- * swizzle, a forced path or an aliased Ld it is one launch with 64-bit indices. */
+ * swizzle, a forced path or an aliased Ld it is one launch with 64-bit indices.
+ * Every block is planned and checked before its launch; an error in a later block
+ * (in practice only LR_ERR_HIP) returns after the earlier blocks were launched, so
+ * dst is then partly written. */
 int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
                    void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
                    size_t elem_bytes, uint32_t flags, void* stream);

@@ -362,6 +362,26 @@ def test_direct_load_transpose_lds_reads_conflict_free(ta, tb):
         assert len(slots) == tb * V * ta
 
 
+def test_fast_paths_touch_the_fewest_lines():
+    """Per wave instruction, in 16-byte chunks (print_layout page, section 6.4: adjacent
+    lanes on adjacent addresses).  Transpose (fp16 8192^2, 32 x 32 chunks, V = 8):
+    a load instruction has lane (alpha, beta) = (l % 32, l / 32) read source row
+    b0 + 8*beta + j at chunk alpha, i.e. (32,2):(1,8*1024) chunks with a 1024-chunk
+    pitch; a store instruction has lane l write chunk l % 32 of destination row
+    a0 + l / 32 + 32*k, i.e. (32,2):(1,1024).  Vector path: 64 consecutive units.
+    Staged path (padded tiles): 64 consecutive 16-byte stores of the compact tiles.
+    Each touches exactly as many 128-byte lines as its bytes need."""
+    for text in ("(32,2):(1,8192)", "(32,2):(1,1024)", "64:1", "(16,4):(1,4)"):
+        r = lr.access_check(text, 16, 64, "read")
+        assert r["lines"] == r["min_lines"] == 8, text
+    # the column-major interleave tile (16 x 32 chunks): loads (16,4):(1,16*...) rows of 256 B
+    r = lr.access_check("(16,4):(1,2048)", 16, 64, "read")
+    assert r["lines"] == r["min_lines"] == 8
+    # a strided pattern the planner avoids: one chunk per row
+    r = lr.access_check("64:1024", 16, 64, "read")
+    assert r["lines"] == 64 and r["min_lines"] == 8
+
+
 def test_staged_gather_conflicts_match_the_counter():
     """The padded-tiles kernel gathers 4-byte words from LDS: lane l of a wave reads
     word 72*(l/16) + (c%8) + 9*(c/8) + 18x with c = l % 16 (16 lanes per tile, the

@@ -369,12 +369,13 @@ def test_fast_paths_touch_the_fewest_lines():
     b0 + 8*beta + j at chunk alpha, i.e. (32,2):(1,8*1024) chunks with a 1024-chunk
     pitch; a store instruction has lane l write chunk l % 32 of destination row
     a0 + l / 32 + 32*k, i.e. (32,2):(1,1024).  Vector path: 64 consecutive units.
-    Staged path (padded tiles): 64 consecutive 16-byte stores of the compact tiles.
+    Staged path (padded tiles): lane l stores chunk 16*tile + c = l of the compact
+    tiles, again 64:1.
     Each touches exactly as many 128-byte lines as its bytes need."""
-    for text in ("(32,2):(1,8192)", "(32,2):(1,1024)", "64:1", "(16,4):(1,4)"):
+    for text in ("(32,2):(1,8192)", "(32,2):(1,1024)", "64:1"):
         r = lr.access_check(text, 16, 64, "read")
         assert r["lines"] == r["min_lines"] == 8, text
-    # the column-major interleave tile (16 x 32 chunks): loads (16,4):(1,16*...) rows of 256 B
+    # a 16-chunk-wide tile (the column-major interleave's 16 x 32): rows of 256 B
     r = lr.access_check("(16,4):(1,2048)", 16, 64, "read")
     assert r["lines"] == r["min_lines"] == 8
     # a strided pattern the planner avoids: one chunk per row

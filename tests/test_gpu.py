@@ -415,6 +415,46 @@ def test_copy_beyond_2_31_elements(dev):
         del src, got
 
 
+def test_copies_replay_in_a_hip_graph(dev):
+    """lr_layout_copy allocates nothing and records no memset, so captured copies
+    (five paths in one graph) replay correctly; each replay is checked after eager
+    work has changed the sources."""
+    cases = []
+    for name in ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles"):
+        w = W.small(name)
+        cases.append((w.src_layout, w.dst_layout, w.src_elems, w.dst_elems, w.elem_bytes))
+    s_list, d_list, plans = [], [], []
+    for ts, td, ns, nd, eb in cases:
+        s_list.append(torch.zeros(ns * eb, dtype=torch.uint8, device=dev))
+        d_list.append(torch.full((nd * eb,), 0xA5, dtype=torch.uint8, device=dev))
+        plans.append((ts, td, ns, nd, eb))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            for (ts, td, ns, nd, eb), s, d in zip(plans, s_list, d_list):
+                lr.layout_copy(s, ts, d, td, elem_bytes=eb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        srcs = []
+        for i, ((ts, td, ns, nd, eb), s) in enumerate(zip(plans, s_list)):
+            host = np.random.default_rng(100 * rep + i).integers(0, 256, ns * eb, dtype=np.uint8)
+            s.copy_(torch.from_numpy(host).to(dev))   # eager work between replays
+            srcs.append(host)
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for (ts, td, ns, nd, eb), host, d in zip(plans, srcs, d_list):
+            want = O.copy(host, O.parse(ts), np.full(nd * eb, 0xA5, np.uint8), O.parse(td), eb)
+            got = d.cpu().numpy()
+            # positions outside the image of td keep what the previous replay left (0xA5 here)
+            assert np.array_equal(got, want), (rep, ts)
+
+
 # ---------------------------------------------------------------------------
 # Tuning variants chosen at plan time (tile shapes, narrow-load interleave)
 # ---------------------------------------------------------------------------

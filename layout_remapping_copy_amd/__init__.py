@@ -32,13 +32,13 @@ from .binding import (  # noqa: F401
     layout_copy,
     layout_eval,
     layout_eval_coords,
+    layout_print,
+    layout_print_table,
     lib,
     logical_divide,
     logical_product,
     max_common_vector,
     parse,
-    print_layout,
-    print_table,
     right_inverse,
     thread_map,
     zipped_divide,

@@ -335,12 +335,12 @@ def _print_text(fn, what, *args) -> str:
     return buf.value.decode()
 
 
-def print_layout(L) -> str:
+def layout_print(L) -> str:
     """Grid of a two-mode layout: rows over mode 0, columns over mode 1."""
     return _print_text(lib().lr_layout_print, "layout_print", ctypes.byref(_as_layout(L).c))
 
 
-def print_table(L, n: int) -> str:
+def layout_print_table(L, n: int) -> str:
     """'thread t -> offset L(t)' for t < n."""
     return _print_text(lib().lr_layout_print_table, "layout_print_table", ctypes.byref(_as_layout(L).c), n)
 

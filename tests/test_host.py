@@ -240,23 +240,23 @@ def _rank2_text(rng, swz_p=0.3):
 
 def test_print_layout_and_table_match_oracle():
     # [print_layout page, section 3.1]: the 4x2 row-major example
-    assert lr.print_layout("(4,2):(2,1)") == "(4,2):(2,1)\n0 1\n2 3\n4 5\n6 7\n"
+    assert lr.layout_print("(4,2):(2,1)") == "(4,2):(2,1)\n0 1\n2 3\n4 5\n6 7\n"
     rng = random.Random(91)
     for _ in range(300):
         t = _rank2_text(rng)
-        assert lr.print_layout(t) == O.print_layout(O.parse(t)) + "\n", t
+        assert lr.layout_print(t) == O.print_layout(O.parse(t)) + "\n", t
         n = rng.randint(1, O.size(O.parse(t)))
-        assert lr.print_table(t, n) == O.thread_offset_table(O.parse(t), n) + "\n", t
+        assert lr.layout_print_table(t, n) == O.thread_offset_table(O.parse(t), n) + "\n", t
     # the ThreadMap page's strip-mined map, 64 threads
     L = lr.thread_map(8, 4, 16, 64)
-    assert lr.print_table(L, 64) == O.thread_offset_table(O.stripmined_layout(8, 4, 16, 64), 64) + "\n"
+    assert lr.layout_print_table(L, 64) == O.thread_offset_table(O.stripmined_layout(8, 4, 16, 64), 64) + "\n"
     for bad in ("8:1", "(2,2,2):(1,2,4)"):
         with pytest.raises(lr.LayoutRemapError):
-            lr.print_layout(bad)
+            lr.layout_print(bad)
     with pytest.raises(lr.LayoutRemapError):
-        lr.print_table("8:1", 9)
+        lr.layout_print_table("8:1", 9)
     with pytest.raises(lr.LayoutRemapError):
-        lr.print_layout("(1024,1025):(1,1024)")   # more than 2^20 cells
+        lr.layout_print("(1024,1025):(1,1024)")   # more than 2^20 cells
     # capacity protocol: too small a buffer reports the size and writes nothing
     import ctypes
     need = ctypes.c_size_t()

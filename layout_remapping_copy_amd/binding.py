@@ -215,9 +215,14 @@ class Layout:
                    f"parse {text_or_struct!r}")
 
     def __str__(self):
-        buf = ctypes.create_string_buffer(1024)
-        _check(lib().lr_layout_format(ctypes.byref(self.c), buf, len(buf)), "format")
-        return buf.value.decode()
+        cap = 1024
+        while True:
+            buf = ctypes.create_string_buffer(cap)
+            rc = lib().lr_layout_format(ctypes.byref(self.c), buf, len(buf))
+            if rc != ERR_CAPACITY:
+                _check(rc, "format")
+                return buf.value.decode()
+            cap *= 4
 
     __repr__ = __str__
 
@@ -252,6 +257,41 @@ def _as_layout(x) -> Layout:
 
 def parse(text: str) -> Layout:
     return Layout(text)
+
+
+def layout_parse(text: str) -> Layout:
+    """lr_layout_parse."""
+    return Layout(text)
+
+
+def layout_format(L) -> str:
+    """lr_layout_format."""
+    return str(_as_layout(L))
+
+
+def layout_validate(L) -> None:
+    """lr_layout_validate: raises LayoutRemapError for a bad descriptor."""
+    _check(lib().lr_layout_validate(ctypes.byref(_as_layout(L).c)), "validate")
+
+
+def size(L) -> int:
+    """lr_size."""
+    return _as_layout(L).size
+
+
+def cosize(L) -> int:
+    """lr_cosize."""
+    return _as_layout(L).cosize
+
+
+def last_hip_error() -> str:
+    """lr_last_hip_error: text of the last HIP error on this thread."""
+    return lib().lr_last_hip_error().decode()
+
+
+def version() -> str:
+    """lr_version."""
+    return lib().lr_version().decode()
 
 
 def coalesce(L) -> Layout:

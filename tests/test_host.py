@@ -63,6 +63,20 @@ def test_exports_every_header_symbol():
     assert exported == names
 
 
+def test_binding_has_every_entry_point():
+    """Each lr_X of the header has a Python function X in the binding."""
+    from layout_remapping_copy_amd import binding as B
+    for name in lr.header_symbols():
+        assert callable(getattr(B, name[3:], None)), name
+    assert lr.layout_format(lr.layout_parse("(4,2):(_2,_1)")) == "(4,2):(2,1)"
+    assert (lr.size("(4,2):(2,1)"), lr.cosize("(4,2):(2,1)")) == (8, 8)
+    lr.layout_validate("Sw<3,3,3> o (64,64):(64,1)")
+    assert lr.version() and lr.last_hip_error() == ""
+    big = "(" + ",".join(["3"] * 16) + "):(" + ",".join([str(10 ** 18 + i) for i in range(16)]) + ")"
+    with pytest.raises(lr.LayoutRemapError):
+        lr.layout_validate(big)   # the largest offset overflows int64
+
+
 def test_parse_format_pins():
     for t in ["(4,2):(2,1)", "((4,2),(2,4)):((2,16),(1,8))", "Sw<3,3,3> o ((128,32),(64,64)):((64,524288),(1,8192))",
               "8:1", "(4,2,2):(8,2,1)", "((4,8),2):((16,1),8)"]:

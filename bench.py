@@ -306,6 +306,27 @@ def main():
                                "GBps_warm": round(W.bytes_moved(wo) / (wm * 1e-6) / 1e9, 1)}
             del prs
             torch.cuda.empty_cache()
+        # latency-only cases: the aliased 8x8 tile copy and two 64-index evaluations
+        # (per-launch HIP events, median of 50; these are launch-bound)
+        w1 = W.tile8x8()
+        s1 = torch.from_numpy(W.make_src(w1)).to(dev)
+        d1 = torch.from_numpy(W.make_dst(w1)).to(dev)
+        lat = _per_launch(lr, torch, [(s1, d1)], w1.src_layout, w1.dst_layout, 4, 50, lr.COPY_ORDERED_ALIAS, False)
+        others["tile8x8_aliased"] = {"path": lr.copy_plan(w1.src_layout, w1.src_elems, w1.dst_layout, w1.dst_elems, 4,
+                                                          lr.COPY_ORDERED_ALIAS)["path"],
+                                     "us_median": round(lat[len(lat) // 2], 2), "us_best": round(lat[0], 2)}
+        stream = torch.cuda.current_stream()
+        for text in ("((4,8),2):((16,1),8)", "Sw<3,0,3> o (8,8):(8,1)"):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+            lr.layout_eval(text, n=64)
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                e0.record(stream)
+                lr.layout_eval(text, n=64)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+            others[f"eval64 {text}"] = {"us_median": round(t[len(t) // 2], 2), "us_best": round(t[0], 2)}
         out["workloads"] = others
 
     if not args.no_cpu_baseline:

@@ -32,10 +32,18 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def _kernel_hash() -> str:
+    """Hash of the code that decides what the kernels read and write (the kernels and
+    the planner), with comments and whitespace removed: only a code change makes
+    the stored HBM counters stale."""
+    import re
+
     h = hashlib.sha256()
     for f in ("kernels.hip", "plan.cpp", "lr_internal.h"):
-        with open(os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "layout_remapping_copy_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,11 +10,14 @@
 // All work here is integer index arithmetic and byte movement: elements are moved
 // as opaque bit patterns in units of 1, 2, 4, 8 or 16 bytes.  Divisions by layout
 // extents use multiply-high constants computed on the host (make_fastdiv), exact
-// for dividends below 2^31; problems that do not fit 31-bit indices and offsets
-// take the 64-bit ("wide") kernels with ordinary division.
+// for dividends below 2^31.  Copies beyond 31-bit indices and offsets are cut
+// into blocks that fit (lr_layout_copy); the 64-bit ("wide") kernels with ordinary
+// division remain for the cases that cannot be cut (a swizzle, an aliased
+// destination, a forced path or an explicit request).
 //
-// Wavefronts are 64 lanes; every kernel runs 256-lane workgroups (4 waves, one
-// per SIMD) except the ordered-alias kernel (1024 lanes, one window per group).
+// Wavefronts are 64 lanes.  Workgroups have 256 lanes (4 waves, one per SIMD),
+// except the tile transposes (TA*TB lanes, 256 to 1024) and the ordered-alias
+// kernel (1024 lanes, one window per workgroup).
 
 #include <hip/hip_runtime.h>
 

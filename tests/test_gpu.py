@@ -261,19 +261,35 @@ def _rand_pair(rng):
     return ts, td, max(ns, O.cosize(O.parse(ts))), nd_
 
 
-def test_copy_random_pairs(dev):
+def test_copy_random_pairs(dev, monkeypatch):
+    """600 seeded random pairs (permuted, padded, swizzled, 1-16 byte elements, up to
+    2^17 elements), each by the default plan, by every path that applies when
+    forced, and with 64-bit indices, under randomly drawn plan-time variants
+    (access policy, direct loads, tile shape and order)."""
     rng = random.Random(41)
-    for i in range(150):
+    runs = 0
+    for i in range(600):
         ts, td, ns, nd = _rand_pair(rng)
         eb = rng.choice([1, 2, 4, 8, 16])
         src = np.random.default_rng(i).integers(0, 256, ns * eb, dtype=np.uint8)
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-        p = lr.copy_plan(ts, ns, td, nd, eb)
-        if i % 25 == 0:
-            say("copy random", i, ts, "->", td, "eb", eb, p["path"])
-        got = gpu_copy(dev, src, ts, dst, td, eb)
-        assert np.array_equal(got, want), (ts, td, eb, p["path"])
+        env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
+               "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 3))}
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        if i % 50 == 0:
+            say("copy random", i, ts, "->", td, "eb", eb, env)
+        for flags in [0, lr.COPY_WIDE_INDEX] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
+            try:
+                p = lr.copy_plan(ts, ns, td, nd, eb, flags)
+            except lr.LayoutRemapError as e:
+                assert e.code == lr.binding.ERR_PATH and flags
+                continue
+            got = gpu_copy(dev, src, ts, dst, td, eb, flags)
+            assert np.array_equal(got, want), (i, ts, td, eb, hex(flags), env, p["path"])
+            runs += 1
+    assert runs > 3000
 
 
 def test_copy_misaligned_pointers(dev):

@@ -179,7 +179,9 @@ def fmt(L: Layout) -> str:
 
 
 # ----------------------------------------------------------------------------
-# Structure
+# Structure.  [CuTe algebra page, section 2.1] and [print_layout page, section
+# 2.1]: a layout is shape and stride, one extent and one step per mode; its size
+# is the number of coordinates, the product of the extents.
 # ----------------------------------------------------------------------------
 def flatten(L: Layout):
     """Leaves depth-first, left to right, as a list of (extent, stride)."""
@@ -642,7 +644,10 @@ def blocked_product(A: Layout, B: Layout) -> Layout:
 
 
 # ----------------------------------------------------------------------------
-# Injectivity
+# Injectivity.  [CuTe algebra page, section 2.3]: the inverse layout answers which
+# logical coordinate a given offset holds, which is only one coordinate when no two
+# coordinates share an offset.  The pages give no test; this is the definition
+# (brute force) plus a sufficient condition on the strides.
 # ----------------------------------------------------------------------------
 BRUTE_INJECTIVE_LIMIT = 1 << 20
 
@@ -714,6 +719,9 @@ def max_common_vector(Ls: Layout, Ld: Layout, elem_bytes: int) -> int:
 
 # ----------------------------------------------------------------------------
 # Joint flat form of a pair of layouts over one index space (unswizzled parts).
+# [CuTe algebra page, section 2.3]: the copy between two layouts is planned from
+# what the two have in common; the pages do not spell out how, and this is the
+# common refinement of both leaf lists.
 # Both leaf lists are split at the union of their prefix products, which must form
 # a divisibility chain; extent-1 modes are dropped and neighbours contiguous on both
 # sides merged.  With ``sort_by_dst`` the modes are sorted by (dst stride, src

@@ -568,6 +568,76 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   }
 }
 
+// Element-granular tile transpose, for copies whose rows do not allow aligned
+// chunks of several elements (odd pitches, ragged extents): a tile of E x E
+// elements with E = 256 / EB, so every row segment on either side is 256 bytes.
+// Load: consecutive lanes read consecutive elements of a source row (a wave
+// instruction covers whole 128-byte lines); the elements go to LDS as rows of the
+// source.  Store: consecutive lanes take consecutive elements of a destination row,
+// i.e. one column of the LDS tile, whose rows are padded by one 4-byte word (two
+// for 8-byte elements) so that the lanes of a phase fall on distinct banks.
+template <int EB, bool NT>
+__global__ void __launch_bounds__(512) k_transpose_el(TransposeArgs t) {
+  using T = typename Raw<EB>::T;
+  static_assert(EB <= 8, "16-byte elements use the chunk transpose");
+  constexpr int E = 256 / EB;                 // tile extent in elements, both axes
+  constexpr int PITCH = 256 + (EB > 4 ? 8 : 4);  // LDS bytes per tile row
+  constexpr int NTH = 512;
+  constexpr int PER = E * E / NTH;            // elements per lane and phase
+  constexpr int BATCH = PER < 8 ? PER : 8;    // loads in flight per lane
+  static_assert(PER % BATCH == 0, "whole batches");
+  __shared__ __align__(16) char tile[E * PITCH];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blockIdx.x, ta, tb, r2);
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const uint32_t a0 = ta * E, b0 = tb * E;
+  const int tid = threadIdx.x;
+
+  // source rows b, elements a along each row
+#pragma unroll
+  for (int i0 = 0; i0 < PER; i0 += BATCH) {
+    T v[BATCH] = {};
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int e = tid + NTH * (i0 + i);
+      const uint32_t a = a0 + e % E, b = b0 + e / E;
+      if (a < t.ext_a && b < t.ext_b) {
+        const uint32_t so = swz32(a + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
+        v[i] = gload<NT, T>(src + (size_t)so * EB);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int e = tid + NTH * (i0 + i);
+      *(T*)(tile + (e / E) * PITCH + (e % E) * EB) = v[i];
+    }
+  }
+  __syncthreads();
+  // destination rows a, elements b along each row
+#pragma unroll
+  for (int i0 = 0; i0 < PER; i0 += BATCH) {
+    T v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int e = tid + NTH * (i0 + i);
+      v[i] = *(const T*)(tile + (e % E) * PITCH + (e / E) * EB);
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int e = tid + NTH * (i0 + i);
+      const uint32_t a = a0 + e / E, b = b0 + e % E;
+      if (a < t.ext_a && b < t.ext_b) {
+        const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+        gstore<NT, T>(dst + (size_t)dof * EB, v[i]);
+      }
+    }
+  }
+}
+
 // The same tile with its source chunks loaded straight into LDS (gfx950 direct
 // loads): the tile's TB*V source rows of TA chunks land in LDS without passing
 // through registers, then each lane reads its V x V block (V chunks of one chunk
@@ -965,6 +1035,11 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool
 }
 
 template <int EB, bool NT>
+static void launch_tel(const TransposeArgs& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_transpose_el<EB, NT>), dim3(grid), dim3(512), 0, st, a);
+}
+
+template <int EB, bool NT>
 static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int shape, bool dl, unsigned grid,
                                 hipStream_t st) {
   switch (v) {
@@ -1109,6 +1184,16 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         a.fd_gtb = fd_of(a.gtb);
       }
       const bool lds = p.path == LR_PATH_TRANSPOSE;
+      if (p.tel) {
+        if (p.eb > 8) return LR_ERR_PATH;
+        switch (p.eb) {
+          case 1: p.nt ? launch_tel<1, true>(a, grid, st) : launch_tel<1, false>(a, grid, st); break;
+          case 2: p.nt ? launch_tel<2, true>(a, grid, st) : launch_tel<2, false>(a, grid, st); break;
+          case 4: p.nt ? launch_tel<4, true>(a, grid, st) : launch_tel<4, false>(a, grid, st); break;
+          default: p.nt ? launch_tel<8, true>(a, grid, st) : launch_tel<8, false>(a, grid, st); break;
+        }
+        return check_launch();
+      }
       bool ok = false;
       LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, p.direct, grid, st));
       if (!ok) return LR_ERR_PATH;

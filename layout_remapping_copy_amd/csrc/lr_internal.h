@@ -81,6 +81,7 @@ struct Plan {
   // diagonal over 4x4 tile groups)
   bool nt;
   bool direct;        // staged: direct global -> LDS loads (no register round trip)
+  bool tel;           // transpose: element-granular tiles (rows without aligned chunks)
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB

@@ -275,7 +275,8 @@ def test_copy_random_pairs(dev, monkeypatch):
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
-               "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 3))}
+               "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 3)),
+               "LR_TEL": rng.choice(["0", "1", "2"])}
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         if i % 50 == 0:
@@ -528,6 +529,39 @@ def test_streaming_accesses_every_path(dev, env_knob):
                 continue
             say("streaming path", lr.binding.PATH_NAMES[path], ts, "->", td, "eb", eb)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+def test_transpose_element_tiles(dev, env_knob, eb):
+    """Transposes whose rows allow no aligned 16-byte chunks run element-granular
+    tiles: odd and ragged extents, a grouped dst-contiguous run, swizzles, a batch
+    mode, both access policies and every workgroup order."""
+    cases = [("(301,517):(517,1)", "(301,517):(1,301)", 301 * 517),
+             ("(1000,1001):(1001,1)", "(1000,1001):(1,1000)", 1000 * 1001),
+             ("(257,3,129):(387,129,1)", "(257,3,129):(1,33153,257)", 257 * 3 * 129),
+             ("(5,2,77):(77,385,1)", "(5,2,77):(2,1,10)", 5 * 2 * 77),
+             ("(255,255):(255,1)", "Sw<1,0,3> o (255,255):(1,255)", 256 * 255),
+             ("(130,66,3):(66,1,8580)", "(130,66,3):(1,130,8580)", 130 * 66 * 3)]
+    env_knob.setenv("LR_TEL", "1")
+    ran = 0
+    for ci, (ts, td, n) in enumerate(cases):
+        ns = max(n, O.cosize(O.parse(ts)))
+        nd = max(n, lr.parse(td).cosize)
+        src = np.random.default_rng(ci + 10 * eb).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for nt in ("0", "1"):
+            env_knob.setenv("LR_NT", nt)
+            for orient in ("0", "1", "2", "3"):
+                env_knob.setenv("LR_TORDER", orient)
+                p = lr.copy_plan(ts, ns, td, nd, eb, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
+                if p["tile_a"] != 256 // eb or p["block"] != 512:
+                    continue  # aligned chunks exist: the chunk transpose runs instead
+                say("transpose elements", ts, "->", td, "eb", eb, "nt", nt, "order", orient)
+                got = gpu_copy(dev, src, ts, dst, td, eb, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
+                assert np.array_equal(got, want), (ts, td, eb, nt, orient)
+                ran += 1
+    assert ran >= 16
 
 
 @pytest.mark.parametrize("shape", [0, 1, 2, 3])

@@ -397,6 +397,19 @@ def test_fast_paths_touch_the_fewest_lines():
     assert r["lines"] == 64 and r["min_lines"] == 8
 
 
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+def test_element_transpose_lds_conflict_free(eb):
+    """The element-granular transpose writes source rows into LDS rows of 256 bytes
+    padded to PITCH (260 bytes, 264 for 8-byte elements) and reads one column per
+    destination row: lane l reads row l, i.e. 64:(PITCH/EB) elements.  Both are
+    conflict-free under the gfx950 model."""
+    pitch = 256 + (8 if eb > 4 else 4)
+    assert lr.access_check(f"64:{pitch // eb}", eb, 64, "read")["conflict_cycles"] == 0
+    assert lr.access_check("64:1", eb, 64, "write")["conflict_cycles"] == 0
+    # without the padding the column read would serialise
+    assert lr.access_check(f"64:{256 // eb}", eb, 64, "read")["conflict_cycles"] > 0
+
+
 def test_staged_gather_conflicts_match_the_counter():
     """The padded-tiles kernel gathers 4-byte words from LDS: lane l of a wave reads
     word 72*(l/16) + (c%8) + 9*(c/8) + 18x with c = l % 16 (16 lanes per tile, the
@@ -502,6 +515,26 @@ def test_plan_streaming_default_and_tile_shapes(monkeypatch):
         p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
         assert p["path"] == "transpose" and p["streaming"]
         assert (p["tile_a"], p["tile_b"], p["block"]) == (ta, tb, block), name
+
+
+def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
+    """Transposes whose rows allow no aligned 16-byte chunks take element tiles of
+    256-byte rows, except 1-byte elements that still fit 2- to 8-byte chunks."""
+    monkeypatch.delenv("LR_TEL", raising=False)
+    # (n, bytes per element) -> element tiles?  (8190, 8) and (8192, 2) have full
+    # 16-byte chunks; 1-byte elements in 2- and 8-byte chunks keep the chunks
+    want = {(8191, 1): True, (8191, 2): True, (8191, 4): True, (8191, 8): True,
+            (8190, 1): False, (8190, 2): True, (8190, 4): True, (8190, 8): False,
+            (8200, 1): False, (8192, 2): False}
+    for (n, eb), element in want.items():
+        p = lr.copy_plan(f"({n},{n}):({n},1)", n * n, f"({n},{n}):(1,{n})", n * n, eb)
+        assert p["path"] == "transpose"
+        got = p["vec_elems"] == 1 and p["tile_a"] == p["tile_b"] == 256 // eb and p["block"] == 512
+        assert got == element, (n, eb, p)
+    monkeypatch.setenv("LR_TEL", "1")
+    assert lr.copy_plan("(8190,8190):(8190,1)", 8190 ** 2, "(8190,8190):(1,8190)", 8190 ** 2, 1)["tile_a"] == 256
+    monkeypatch.setenv("LR_TEL", "0")
+    assert lr.copy_plan("(8191,8191):(8191,1)", 8191 ** 2, "(8191,8191):(1,8191)", 8191 ** 2, 2)["tile_a"] == 16
 
 
 def test_plan_errors():

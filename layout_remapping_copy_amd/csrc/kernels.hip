@@ -1003,7 +1003,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool
         case 1: hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 16, NT>), dim3(grid), dim3(512), 0, st, a); return true;
         case 2: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 32, NT>), dim3(grid), dim3(512), 0, st, a); return true;
         case 3:
-          if constexpr (V <= 8) {
+          if constexpr (shape_fits(3, V)) {
             hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 32, NT>), dim3(grid), dim3(1024), 0, st, a);
             return true;
           }
@@ -1018,16 +1018,24 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool
     hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a);
     return true;
   }
-  if constexpr (V * EB == 16 && V <= 8) {  // other shapes: full 16-byte chunks, LDS <= 128 KiB
+  if constexpr (V * EB == 16) {  // other shapes: full 16-byte chunks, tiles that fit LDS
+#define LR_TSHAPE_CASE(S)                                                                \
+  case S:                                                                                \
+    if constexpr (shape_fits(S, V)) {                                                    \
+      launch_transpose_shape<EB, V, kTileTA[S], kTileTB[S], NT>(a, grid, st);            \
+      return true;                                                                       \
+    }                                                                                    \
+    break;
     switch (shape) {
-      case 1: launch_transpose_shape<EB, V, kTileTA[1], kTileTB[1], NT>(a, grid, st); return true;
-      case 2: launch_transpose_shape<EB, V, kTileTA[2], kTileTB[2], NT>(a, grid, st); return true;
-      case 3: launch_transpose_shape<EB, V, kTileTA[3], kTileTB[3], NT>(a, grid, st); return true;
-      case 4: launch_transpose_shape<EB, V, kTileTA[4], kTileTB[4], NT>(a, grid, st); return true;
-      case 5: launch_transpose_shape<EB, V, kTileTA[5], kTileTB[5], NT>(a, grid, st); return true;
-      case 6: launch_transpose_shape<EB, V, kTileTA[6], kTileTB[6], NT>(a, grid, st); return true;
+      LR_TSHAPE_CASE(1)
+      LR_TSHAPE_CASE(2)
+      LR_TSHAPE_CASE(3)
+      LR_TSHAPE_CASE(4)
+      LR_TSHAPE_CASE(5)
+      LR_TSHAPE_CASE(6)
       default: break;
     }
+#undef LR_TSHAPE_CASE
   }
   if (shape != 0) return false;
   launch_transpose_shape<EB, V, 16, 16, NT>(a, grid, st);

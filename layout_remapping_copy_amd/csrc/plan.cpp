@@ -358,19 +358,27 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       //    adjacent in the source (each tile reads one contiguous block, e.g.
       //    NHWC -> NCHW), 32 x 8 chunks: small workgroups, many per CU;
       //  - otherwise the longest runs on both sides, 32 x 32 chunks (16 x 32 when
-      //    16 chunks already cover the a extent).
+      //    16 chunks already cover the a extent); with only one or two elements per
+      //    chunk (8- and 16-byte elements) a lane has few loads in flight and
+      //    smaller tiles won: 32 x 16 chunks for two (5.48 vs 5.11 TB/s on an
+      //    8192^2 transpose), 16 x 16 for one (5.35 vs 5.26).
       const bool far_rows = pitch > 2048;
-      const bool wide_ok = V * p->eb == 16 && V <= 8 && p->path == LR_PATH_TRANSPOSE;
+      const bool wide_ok = V * p->eb == 16 && p->path == LR_PATH_TRANSPOSE;
       const int64_t ext_a = p->m[a].ext;
       const bool block_rows = ext_a <= 32 * V && p->m[b].ss == ext_a;
       if (!wide_ok)
         p->tshape = 0;
       else if (block_rows)
         p->tshape = ext_a > 16 * V ? 4 : 0;
-      else
+      else if (V >= 4)
         p->tshape = ext_a > 16 * V ? 3 : 2;
+      else
+        p->tshape = (V == 2 && ext_a > 16 * V) ? 1 : 0;
       const uint32_t shp = env_u32("LR_TSHAPE", 99);
       if (shp < (uint32_t)kTileShapes) p->tshape = wide_ok ? (int)shp : 0;
+      // 16-element chunks (1-byte elements): the 32 x 32 and 64 x 16 tiles would
+      // need 256 KiB of LDS; take the largest that fits
+      if (!shape_fits(p->tshape, (int)V)) p->tshape = p->tshape == 6 ? 5 : 1;
       p->tile_a = kTileTA[p->tshape] * V;
       p->tile_b = kTileTB[p->tshape] * V;
       p->block = kTileTA[p->tshape] * kTileTB[p->tshape];
@@ -402,7 +410,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // direct global -> LDS loads: full chunks, tiles 16 or 32 chunks wide along a
       // and at least 16 along b
       p->direct = env_u32("LR_TDIRECT", 0) != 0 && p->path == LR_PATH_TRANSPOSE && V * p->eb == 16 &&
-                  p->tshape <= 3 && (p->tshape != 3 || V <= 8);
+                  p->tshape <= 3 && shape_fits(p->tshape, (int)V);
       const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
       const int64_t ntb = (ext_b + p->tile_b - 1) / p->tile_b;
       if (p->torder == 3 && (nta % 4 || ntb % 4)) p->torder = 2;  // grouped order needs 4 | tiles
@@ -529,11 +537,11 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       }
       if (p.m[p.a].ext % v || ext_b % v) return bad();
       if (p.tshape < 0 || p.tshape >= kTileShapes ||
-          (p.tshape != 0 && (v * p.eb != 16 || v > 8 || p.path != LR_PATH_TRANSPOSE)))
+          (p.tshape != 0 && (v * p.eb != 16 || !shape_fits(p.tshape, (int)v) || p.path != LR_PATH_TRANSPOSE)))
         return bad();
       if (p.torder > 3) return bad();
       // direct-load kernel: full 16-byte chunks, tiles 16 or 32 chunks along a, >= 16 along b
-      if (p.direct && (p.path != LR_PATH_TRANSPOSE || v * p.eb != 16 || p.tshape > 3 || (p.tshape == 3 && v > 8)))
+      if (p.direct && (p.path != LR_PATH_TRANSPOSE || v * p.eb != 16 || p.tshape > 3 || !shape_fits(p.tshape, (int)v)))
         return bad();
       if (p.tel) {  // element-granular tiles of 256-byte rows
         if (p.path != LR_PATH_TRANSPOSE || p.eb > 8 || v != 1 || p.direct || p.tile_a != 256 / p.eb ||

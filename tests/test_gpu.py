@@ -487,7 +487,8 @@ def test_transpose_tile_shapes(dev, env_knob, shape):
                           ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 7560, 2),
                           ("(100,72):(72,1)", "(100,72):(1,100)", 7200, 4),
                           ("(64,96,5):(96,1,6144)", "(64,96,5):(1,64,6144)", 30720, 8),
-                          ("(1024,512):(512,1)", "(1024,512):(1,1024)", 1024 * 512, 2)]:
+                          ("(1024,512):(512,1)", "(1024,512):(1,1024)", 1024 * 512, 2),
+                          ("(512,272):(272,1)", "(512,272):(1,512)", 512 * 272, 1)]:
         src = np.random.default_rng(shape).integers(0, 256, n * eb, dtype=np.uint8)
         dst = np.full(n * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)

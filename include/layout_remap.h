@@ -288,6 +288,11 @@ typedef struct {
   int32_t block;       /* threads per workgroup */
   int32_t streaming;   /* 1 if loads and stores are non-temporal: by default when the source
                           plus destination bytes reach 256 MiB, the last-level cache size */
+  int32_t order;       /* transpose: workgroup -> tile order (0 a-tiles fastest, 1 b-tiles
+                          fastest, 2 diagonal with a fastest, 3 diagonal over 4 x 4 tile groups,
+                          4 diagonal with b fastest); -1 on other paths */
+  int32_t direct;      /* 1 if the source tile goes straight from global memory into LDS
+                          (staged and transpose paths) */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */

@@ -434,7 +434,7 @@ struct TransposeArgs {
   BatchArg batch;
   SwzArg sws, swd;
   uint32_t order;  // 0: tiles along a vary fastest across workgroups, 1: along b, 2: diagonal,
-                   // 3: diagonal over 4 x 4 groups of tiles
+                   // 3: diagonal over 4 x 4 groups of tiles, 4: diagonal with b fastest
   uint32_t gta, gtb;  // order 3: groups along a and b
   FD fd_gta, fd_gtb;
 };
@@ -463,6 +463,15 @@ __device__ __forceinline__ void transpose_tile(const TransposeArgs& t, uint32_t 
     uint32_t ta_mod = ta - fdiv(ta, t.fd_tb) * t.tiles_b;  // ta % tiles_b
     uint32_t d = (r1 - r2 * t.tiles_b) + ta_mod;            // < 2 * tiles_b
     tb = d >= t.tiles_b ? d - t.tiles_b : d;
+  } else if (t.order == 4) {
+    // the diagonal with the roles of a and b swapped: consecutive workgroups take
+    // consecutive b-tiles and, with them, shifted a-tiles
+    uint32_t r1 = fdiv(blk, t.fd_tb);
+    tb = blk - r1 * t.tiles_b;
+    r2 = fdiv(r1, t.fd_ta);
+    uint32_t tb_mod = tb - fdiv(tb, t.fd_ta) * t.tiles_a;  // tb % tiles_a
+    uint32_t d = (r1 - r2 * t.tiles_a) + tb_mod;            // < 2 * tiles_a
+    ta = d >= t.tiles_a ? d - t.tiles_a : d;
   } else {
     // grouped diagonal: 16 consecutive workgroups cover a 4 x 4 group of tiles,
     // so the workgroups in flight read and write 4 adjacent tile rows' worth of

@@ -80,8 +80,8 @@ struct Plan {
   // alias path
   int64_t alias_windows;
   // tuning: non-temporal loads and stores (streaming data), and the transpose's
-  // workgroup order (0: a-tiles fastest, 1: b-tiles fastest, 2: diagonal, 3:
-  // diagonal over 4x4 tile groups)
+  // workgroup order (0: a-tiles fastest, 1: b-tiles fastest, 2: diagonal with a
+  // fastest, 3: diagonal over 4x4 tile groups, 4: diagonal with b fastest)
   bool nt;
   bool direct;        // staged: direct global -> LDS loads (no register round trip)
   bool tel;           // transpose: element-granular tiles (rows without aligned chunks)

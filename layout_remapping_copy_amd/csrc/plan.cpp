@@ -362,7 +362,6 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       //    chunk (8- and 16-byte elements) a lane has few loads in flight and
       //    smaller tiles won: 32 x 16 chunks for two (5.48 vs 5.11 TB/s on an
       //    8192^2 transpose), 16 x 16 for one (5.35 vs 5.26).
-      const bool far_rows = pitch > 2048;
       const bool wide_ok = V * p->eb == 16 && p->path == LR_PATH_TRANSPOSE;
       const int64_t ext_a = p->m[a].ext;
       const bool block_rows = ext_a <= 32 * V && p->m[b].ss == ext_a;
@@ -398,15 +397,33 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         p->tile_a = p->tile_b = 256 / p->eb;
         p->block = 512;
       }
-      // Workgroup order.  When the source rows of consecutive b-tiles are close
-      // (pitch <= 2 KiB, e.g. NHWC channels) b-tiles go fastest: both the reads
-      // and the writes of neighbouring workgroups are then adjacent.  Otherwise
-      // (large pitches such as a square transpose's 16 KiB rows) a diagonal order
-      // keeps the workgroups in flight from sharing one column offset, which with
-      // power-of-two pitches concentrates them on a few HBM channels.
-      p->torder = far_rows ? 2u : 1u;
+      // Workgroup order (measured on fp16, fp32, 1-, 8- and 16-byte transposes from
+      // 2048 x 32768 to 16384^2).  b-tiles fastest by default: consecutive
+      // workgroups then write adjacent column blocks of the same destination rows
+      // and read adjacent row bands of one source column strip.  With pitches that
+      // are power-of-two heavy (a multiple of 16 KiB, or a power of two from 4 KiB)
+      // the rows of such a strip, or of a tile band, share their low address bits
+      // and the workgroups in flight camp on a few HBM channels (fp16 8192^2: 4.3
+      // TB/s); a diagonal order then spreads them (5.6).  Of the two diagonals, the
+      // one with b fastest (4) wins for tiles with equal row bytes on both sides
+      // (fp16 16384^2: 6.33 against 6.20; 2048 x 32768: 5.49 against 4.70); the one
+      // with a fastest (2) wins for tiles whose source rows are longer (1- and
+      // 8-byte elements: 4.65 against 4.40 on 1-byte 8192^2) unless there are more
+      // a-tiles than b-tiles, when its workgroups sharing a b-tile would read
+      // columns a power-of-two distance apart.  Other pitches keep b fastest:
+      // 11264^2 fp16 5.42 against 4.94 for the diagonal.
+      {
+        const int64_t pitch_d = p->m[a].sd * p->eb;
+        auto pow2_heavy = [](int64_t q) { return q % 16384 == 0 || (q >= 4096 && (q & (q - 1)) == 0); };
+        const int64_t nta0 = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
+        const int64_t ntb0 = (ext_b + p->tile_b - 1) / p->tile_b;
+        if (nta0 > 1 && (pow2_heavy(pitch) || pow2_heavy(pitch_d)))
+          p->torder = (p->tile_a > p->tile_b && nta0 <= ntb0) ? 2u : 4u;
+        else
+          p->torder = 1u;  // (with a single a-tile, order 4 is order 1)
+      }
       const uint32_t tord = env_u32("LR_TORDER", 99);
-      if (tord <= 3) p->torder = tord;
+      if (tord <= 4) p->torder = tord;
       // direct global -> LDS loads: full chunks, tiles 16 or 32 chunks wide along a
       // and at least 16 along b
       p->direct = env_u32("LR_TDIRECT", 0) != 0 && p->path == LR_PATH_TRANSPOSE && V * p->eb == 16 &&
@@ -539,7 +556,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (p.tshape < 0 || p.tshape >= kTileShapes ||
           (p.tshape != 0 && (v * p.eb != 16 || !shape_fits(p.tshape, (int)v) || p.path != LR_PATH_TRANSPOSE)))
         return bad();
-      if (p.torder > 3) return bad();
+      if (p.torder > 4) return bad();
       // direct-load kernel: full 16-byte chunks, tiles 16 or 32 chunks along a, >= 16 along b
       if (p.direct && (p.path != LR_PATH_TRANSPOSE || v * p.eb != 16 || p.tshape > 3 || !shape_fits(p.tshape, (int)v)))
         return bad();
@@ -702,6 +719,8 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   out->b2_mode = p.b2;
   out->block = p.block;
   out->streaming = p.nt ? 1 : 0;
+  out->order = (p.path == LR_PATH_TRANSPOSE || p.path == LR_PATH_TRANSPOSE_DIRECT) ? (int32_t)p.torder : -1;
+  out->direct = p.direct ? 1 : 0;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

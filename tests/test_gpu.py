@@ -275,7 +275,7 @@ def test_copy_random_pairs(dev, monkeypatch):
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
-               "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 3)),
+               "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 4)),
                "LR_TEL": rng.choice(["0", "1", "2"])}
         for k, v in env.items():
             monkeypatch.setenv(k, v)
@@ -500,7 +500,7 @@ def test_transpose_tile_shapes(dev, env_knob, shape):
                 continue
             say("transpose shape", shape, lr.binding.PATH_NAMES[path], ts, "eb", eb)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
-        for orient in ("0", "1", "2", "3"):
+        for orient in ("0", "1", "2", "3", "4"):
             env_knob.setenv("LR_TORDER", orient)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)
         env_knob.delenv("LR_TORDER")
@@ -553,7 +553,7 @@ def test_transpose_element_tiles(dev, env_knob, eb):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         for nt in ("0", "1"):
             env_knob.setenv("LR_NT", nt)
-            for orient in ("0", "1", "2", "3"):
+            for orient in ("0", "1", "2", "3", "4"):
                 env_knob.setenv("LR_TORDER", orient)
                 p = lr.copy_plan(ts, ns, td, nd, eb, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
                 if p["tile_a"] != 256 // eb or p["block"] != 512:
@@ -585,7 +585,7 @@ def test_transpose_direct_loads(dev, env_knob, shape):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         for nt in ("0", "1"):
             env_knob.setenv("LR_NT", nt)
-            for orient in ("0", "1", "2", "3"):
+            for orient in ("0", "1", "2", "3", "4"):
                 env_knob.setenv("LR_TORDER", orient)
                 p = lr.copy_plan(ts, n, td, n, eb)
                 if p["path"] != "transpose":

@@ -517,6 +517,37 @@ def test_plan_streaming_default_and_tile_shapes(monkeypatch):
         assert (p["tile_a"], p["tile_b"], p["block"]) == (ta, tb, block), name
 
 
+def test_plan_workgroup_order(monkeypatch):
+    """Transpose workgroup order: b-tiles fastest unless a pitch is power-of-two
+    heavy (a multiple of 16 KiB, or a power of two from 4 KiB); then the diagonal
+    with b fastest, or with a fastest for tiles with longer source rows and no more
+    a-tiles than b-tiles.  A single a-tile keeps b fastest."""
+    monkeypatch.delenv("LR_TORDER", raising=False)
+    monkeypatch.delenv("LR_TSHAPE", raising=False)
+
+    def order(rows, cols, eb):
+        p = lr.copy_plan(f"({cols},{rows}):(1,{cols})", rows * cols, f"({cols},{rows}):({rows},1)", rows * cols, eb)
+        assert p["path"] == "transpose"
+        return p["order"]
+
+    want = {(8192, 8192, 2): 4, (16384, 16384, 2): 4, (2048, 32768, 2): 4, (32768, 2048, 2): 4,
+            (8192, 8256, 2): 4,  # destination pitch 16 KiB
+            (11264, 11264, 2): 1, (12288, 12288, 2): 1, (8191, 8191, 2): 1, (6144, 6144, 4): 1,
+            (8192, 8192, 1): 2,  # 512 x 256 tiles, 16 a-tiles <= 32 b-tiles
+            (2048, 32768, 1): 4,  # 64 a-tiles > 8 b-tiles
+            (8192, 4096, 8): 2, (4096, 4096, 16): 4, (8192, 8192, 4): 4}
+    for (rows, cols, eb), o in want.items():
+        assert order(rows, cols, eb) == o, (rows, cols, eb)
+    for name, o in (("transpose", 4), ("interleave_cm", 1), ("nhwc2nchw", 1)):
+        w = W.full(name)
+        assert lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)["order"] == o, name
+    assert lr.copy_plan("64:1", 64, "64:1", 64, 4)["order"] == -1
+    monkeypatch.setenv("LR_TORDER", "3")
+    assert order(8192, 8192, 2) == 3
+    monkeypatch.setenv("LR_TORDER", "0")
+    assert order(8192, 8192, 2) == 0
+
+
 def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
     """Transposes whose rows allow no aligned 16-byte chunks take element tiles of
     256-byte rows, except 1-byte elements that still fit 2- to 8-byte chunks."""

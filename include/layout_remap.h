@@ -293,6 +293,10 @@ typedef struct {
                           4 diagonal with b fastest); -1 on other paths */
   int32_t direct;      /* 1 if the source tile goes straight from global memory into LDS
                           (staged and transpose paths) */
+  int32_t load_policy;  /* cache-policy bits of the source loads: 0 plain, 2 non-temporal */
+  int32_t store_policy; /* of the destination stores: 0 plain, 2 non-temporal, 18 non-temporal
+                           with the sc1 scope bit (the LDS transpose's streaming stores, as
+                           buffer stores, when a tile's destination span is under 4 GiB) */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */

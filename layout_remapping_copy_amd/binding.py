@@ -81,6 +81,8 @@ class lr_plan(ctypes.Structure):
         ("streaming", ctypes.c_int32),
         ("order", ctypes.c_int32),
         ("direct", ctypes.c_int32),
+        ("load_policy", ctypes.c_int32),
+        ("store_policy", ctypes.c_int32),
         ("tile_a", ctypes.c_int64),
         ("tile_b", ctypes.c_int64),
         ("grid", ctypes.c_int64),
@@ -418,6 +420,7 @@ def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, fla
         "path": PATH_NAMES[p.path], "elem_bytes": p.elem_bytes, "vec_elems": p.vec_elems, "wide": bool(p.wide),
         "a_mode": p.a_mode, "b_mode": p.b_mode, "b2_mode": p.b2_mode, "block": p.block,
         "streaming": bool(p.streaming), "order": p.order, "direct": bool(p.direct),
+        "load_policy": p.load_policy, "store_policy": p.store_policy,
         "tile_a": p.tile_a, "tile_b": p.tile_b,
         "grid": p.grid, "n_elems": p.n_elems, "blocks": p.blocks,
         "joint": [(p.ext[i], p.s_src[i], p.s_dst[i]) for i in range(r)],

@@ -113,6 +113,12 @@ __device__ __forceinline__ void gstore(void* p, const C& v) {
     *(N*)p = x;
 }
 
+// Buffer resources for raw (unformatted, stride 0) accesses: the descriptor's last
+// word for gfx950, and the cache-policy bits of a streaming store: nt (2) marks the
+// data non-temporal, sc1 (16) selects the wider coherence scope.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kPolicyNtSc1 = 2 | 16;
+
 // gfx950 direct global -> LDS load of 16 bytes per lane: lane i of the wave writes
 // its bytes at lds_wave + 16*i (lds_wave is the wave's common LDS base).
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -437,6 +443,11 @@ struct TransposeArgs {
                    // 3: diagonal over 4 x 4 groups of tiles, 4: diagonal with b fastest
   uint32_t gta, gtb;  // order 3: groups along a and b
   FD fd_gta, fd_gtb;
+  // streaming stores of the LDS tile transpose: 1 = buffer stores relative to the
+  // tile's lowest destination offset (rounded down by bufmask, which clears the
+  // bits a destination swizzle may change); the host checks that every offset of a
+  // tile lies less than 4 GiB above that base
+  uint32_t bufst, bufmask;
 };
 
 // Workgroup number -> (a-tile, b-tile, batch index) in the order t.order selects.
@@ -565,6 +576,29 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   }
   __syncthreads();
   const int c = tid % TB;
+  if constexpr (NT && sizeof(C) == 16) {
+    if (t.bufst) {
+      // Streaming 16-byte stores as buffer stores with the nt and sc1 policy bits,
+      // which measured faster than nt alone for this access pattern.  Offsets are
+      // taken from the tile's lowest destination offset (every stored offset of
+      // the tile is at or above it: a >= a0, b >= b0, and the swizzle changes only
+      // bits under ~bufmask).
+      const uint32_t tbase = (a0 * t.sd_a + b0 + bd) & t.bufmask;
+      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst + (size_t)tbase * EB, 0, -1, kBufferWord3);
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const int row = tid / TB + (NTH / TB) * k;
+        const uint32_t a = a0 + row, b = b0 + V * c;
+        if (a < t.ext_a && b < t.ext_b) {
+          C v = tile[row][c ^ ((row / V) % TB)];
+          const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, v), rd,
+                                                 (dof - tbase) * EB, 0, kPolicyNtSc1);
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     const int row = tid / TB + (NTH / TB) * k;
@@ -1194,6 +1228,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
       a.order = p.torder;
+      a.bufst = p.bufst ? 1u : 0u;
+      a.bufmask = p.sw_d.b ? ~((1u << (p.sw_d.m + p.sw_d.b)) - 1u) : ~0u;
       if (p.torder == 3) {
         a.gta = a.tiles_a / 4;
         a.gtb = a.tiles_b / 4;

@@ -428,6 +428,21 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // and at least 16 along b
       p->direct = env_u32("LR_TDIRECT", 0) != 0 && p->path == LR_PATH_TRANSPOSE && V * p->eb == 16 &&
                   p->tshape <= 3 && shape_fits(p->tshape, (int)V);
+      // Streaming stores of the LDS tile transpose go out as buffer stores with the
+      // nt and sc1 cache-policy bits: fp16 8192^2 5.62 -> 5.67 TB/s, the column-major
+      // head interleave 6.19 -> 6.35, NHWC -> NCHW 6.03 -> 6.11, fp32 8192^2 6.07 ->
+      // 6.26 (the interleave and staged kernels measured slower with them, 1-1.5 %).
+      // Buffer offsets are 32-bit: each workgroup stores relative to its tile's
+      // lowest destination offset, so the tile's destination span must stay under
+      // 4 GiB.  LR_TSC1=0 keeps global stores.
+      {
+        // rounding the base down and swizzling the highest offset up each add less
+        // than one swizzle block (2^(M+B) elements)
+        const int64_t swz_blk = p->sw_d.b ? (int64_t(1) << (p->sw_d.m + p->sw_d.b)) : 0;
+        const int64_t span = ((p->tile_a - 1) * p->m[a].sd + p->tile_b + 2 * swz_blk) * p->eb;
+        p->bufst = p->path == LR_PATH_TRANSPOSE && !p->tel && !p->direct && V * p->eb == 16 &&
+                   span < (int64_t(1) << 32) && env_u32("LR_TSC1", 1) != 0;
+      }
       const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
       const int64_t ntb = (ext_b + p->tile_b - 1) / p->tile_b;
       if (p->torder == 3 && (nta % 4 || ntb % 4)) p->torder = 2;  // grouped order needs 4 | tiles
@@ -557,6 +572,12 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
           (p.tshape != 0 && (v * p.eb != 16 || !shape_fits(p.tshape, (int)v) || p.path != LR_PATH_TRANSPOSE)))
         return bad();
       if (p.torder > 4) return bad();
+      if (p.bufst) {  // buffer stores: full chunks of the LDS kernel, tile span under 4 GiB
+        const int64_t swz_blk = p.sw_d.b ? (int64_t(1) << (p.sw_d.m + p.sw_d.b)) : 0;
+        const int64_t span = ((p.tile_a - 1) * p.m[p.a].sd + p.tile_b + 2 * swz_blk) * p.eb;
+        if (p.path != LR_PATH_TRANSPOSE || p.tel || p.direct || v * p.eb != 16 || span >= (int64_t(1) << 32))
+          return bad();
+      }
       // direct-load kernel: full 16-byte chunks, tiles 16 or 32 chunks along a, >= 16 along b
       if (p.direct && (p.path != LR_PATH_TRANSPOSE || v * p.eb != 16 || p.tshape > 3 || !shape_fits(p.tshape, (int)v)))
         return bad();
@@ -721,6 +742,8 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   out->streaming = p.nt ? 1 : 0;
   out->order = (p.path == LR_PATH_TRANSPOSE || p.path == LR_PATH_TRANSPOSE_DIRECT) ? (int32_t)p.torder : -1;
   out->direct = p.direct ? 1 : 0;
+  out->load_policy = p.nt ? 2 : 0;
+  out->store_policy = p.nt ? (p.bufst ? 18 : 2) : 0;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

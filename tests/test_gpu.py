@@ -276,7 +276,7 @@ def test_copy_random_pairs(dev, monkeypatch):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
                "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 4)),
-               "LR_TEL": rng.choice(["0", "1", "2"])}
+               "LR_TEL": rng.choice(["0", "1", "2"]), "LR_TSC1": rng.choice("01")}
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         if i % 50 == 0:
@@ -388,7 +388,8 @@ def test_full_transpose_both_variants(dev, monkeypatch, nt):
     # plain and streaming (non-temporal) accesses; the default for this size is streaming
     monkeypatch.setenv("LR_NT", nt)
     w = W.full("transpose")
-    assert lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)["streaming"] == (nt == "1")
+    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    assert p["streaming"] == (nt == "1") and p["store_policy"] == (18 if nt == "1" else 0)
     src = W.make_src(w)
     want = F.transpose(src, 8192)
     s = torch.from_numpy(src).to(dev)
@@ -530,6 +531,46 @@ def test_streaming_accesses_every_path(dev, env_knob):
                 continue
             say("streaming path", lr.binding.PATH_NAMES[path], ts, "->", td, "eb", eb)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
+
+
+@pytest.mark.parametrize("tsc1", ["0", "1"])
+def test_transpose_streaming_store_forms(dev, env_knob, tsc1):
+    """Streaming transposes store either with global non-temporal stores or with
+    buffer stores relative to each tile's lowest destination offset (nt and sc1
+    bits).  Every tile shape, with ragged edges, a batch mode, a grouped b run and
+    destination swizzles (the tile base is rounded down past the swizzled bits)."""
+    env_knob.setenv("LR_NT", "1")
+    env_knob.setenv("LR_TSC1", tsc1)
+    cm = W.small("interleave_cm")
+    cases = [("(520,264):(264,1)", "(520,264):(1,520)", 2),
+             ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 2),
+             ("(1024,512):(512,1)", "Sw<3,3,3> o (1024,512):(1,1024)", 2),
+             ("(600,328):(328,1)", "Sw<2,3,5> o (600,328):(1,600)", 2),
+             ("(100,72):(72,1)", "Sw<2,2,4> o (100,72):(1,100)", 4),
+             ("(64,96,5):(96,1,6144)", "(64,96,5):(1,64,6144)", 8),
+             ("(512,272):(272,1)", "(512,272):(1,512)", 1),
+             ("(48,80):(80,1)", "(48,80):(1,48)", 16),
+             (cm.src_layout, cm.dst_layout, 2)]
+    ran = 0
+    for shape in range(7):
+        env_knob.setenv("LR_TSHAPE", str(shape))
+        for ci, (ts, td, eb) in enumerate(cases):
+            n = O.size(O.parse(ts))
+            ns, nd = max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize)
+            p = lr.copy_plan(ts, ns, td, nd, eb)
+            if p["path"] != "transpose":
+                continue
+            src = np.random.default_rng(ci + 10 * shape).integers(0, 256, ns * eb, dtype=np.uint8)
+            dst = np.full(nd * eb, 0xA5, np.uint8)
+            want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+            if tsc1 == "1" and p["vec_elems"] * p["elem_bytes"] == 16:
+                assert p["store_policy"] == 18, (ts, td, p)
+            if tsc1 == "0":
+                assert p["store_policy"] == 2
+            say("transpose stores", "sc1" if p["store_policy"] == 18 else "global", "shape", shape, ts, "->", td, "eb", eb)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, shape)
+            ran += 1
+    assert ran >= 40
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])

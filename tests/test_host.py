@@ -548,6 +548,39 @@ def test_plan_workgroup_order(monkeypatch):
     assert order(8192, 8192, 2) == 0
 
 
+def test_plan_store_policy(monkeypatch):
+    """Streaming copies load and store non-temporally; the LDS transpose's streaming
+    stores also carry the sc1 scope bit (buffer stores), only while a tile's
+    destination span stays under 4 GiB (32-bit buffer offsets)."""
+    for k in ("LR_NT", "LR_TSC1", "LR_TDIRECT", "LR_TEL"):
+        monkeypatch.delenv(k, raising=False)
+
+    def plan(name):
+        w = W.full(name)
+        flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
+        return lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
+
+    want = {"transpose": (2, 18), "interleave_cm": (2, 18), "nhwc2nchw": (2, 18), "interleave": (2, 2),
+            "padtiles": (2, 2), "retile": (0, 0), "tile8x8": (0, 0)}
+    for name, pol in want.items():
+        p = plan(name)
+        assert (p["load_policy"], p["store_policy"]) == pol, (name, p["path"])
+    monkeypatch.setenv("LR_TSC1", "0")
+    assert plan("transpose")["store_policy"] == 2
+    monkeypatch.delenv("LR_TSC1")
+    monkeypatch.setenv("LR_TDIRECT", "1")
+    assert plan("transpose")["store_policy"] == 2  # the direct-load kernel keeps global stores
+    monkeypatch.delenv("LR_TDIRECT")
+    monkeypatch.setenv("LR_NT", "1")
+    # 16-byte elements, 16 x 16 tiles: the destination span of a tile is 15 rows of the
+    # a-mode's destination stride
+    for sd, pol in ((1 << 20, 18), ((1 << 32) // (15 * 16) - 16, 18), (1 << 25, 2)):
+        p = lr.copy_plan("(16,64):(1,16)", 1024, f"(16,64):({sd},1)", 15 * sd + 64, 16)
+        assert p["path"] == "transpose" and p["tile_a"] == 16 and p["store_policy"] == pol, (sd, p)
+    # element tiles (rows without aligned chunks) keep global stores
+    assert lr.copy_plan("(301,517):(517,1)", 301 * 517, "(301,517):(1,301)", 301 * 517, 2)["store_policy"] == 2
+
+
 def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
     """Transposes whose rows allow no aligned 16-byte chunks take element tiles of
     256-byte rows, except 1-byte elements that still fit 2- to 8-byte chunks."""

@@ -1,4 +1,4 @@
-"""Closed forms of the six workload copies as NumPy reshapes, transposes and
+"""Closed forms of the workload copies as NumPy reshapes, transposes and
 takes.  TEST INFRASTRUCTURE ONLY.
 
 Each function returns the expected destination bytes for a workload's source
@@ -58,3 +58,11 @@ def padtiles(src: np.ndarray, tiles: int) -> np.ndarray:
     table = 18 * (k % 4) + (k // 4) % 8 + 9 * (k // 32)
     s = src.view(np.uint32).reshape(tiles, 72)
     return np.ascontiguousarray(np.take(s, table, axis=1)).reshape(-1).view(np.uint8)
+
+
+def shard_pack(src: np.ndarray, rows: int, cols: int, parts: int) -> np.ndarray:
+    """Row block (rows, cols) row-major -> `parts` contiguous blocks, block j holding
+    columns [j*w, (j+1)*w) transposed (w = cols / parts): dst[j][c][r] =
+    src[r][j*w + c]."""
+    x = src.view(np.uint16).reshape(rows, parts, cols // parts).transpose(1, 2, 0)
+    return np.ascontiguousarray(x).reshape(-1).view(np.uint8)

@@ -352,10 +352,11 @@ FORMS = {
     "interleave_cm": lambda s: F.interleave_cm(s, 16, 32, 4096, 128),
     "nhwc2nchw": lambda s: F.nhwc2nchw(s, 128, 56, 56, 256),
     "padtiles": lambda s: F.padtiles(s, 1 << 20),
+    "shard_pack": lambda s: F.shard_pack(s, 1024, 8192, 8),
 }
 
 FULL_PATH = {"transpose": "transpose", "retile": "vector", "interleave": "interleave", "interleave_cm": "transpose",
-             "nhwc2nchw": "transpose", "padtiles": "staged"}
+             "nhwc2nchw": "transpose", "padtiles": "staged", "shard_pack": "transpose"}
 
 
 @pytest.mark.slow

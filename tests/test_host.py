@@ -439,7 +439,7 @@ def test_common_vector_sound_and_tight_on_workloads():
             w = O.max_common_vector(O.parse(ts), Ld, eb)
             assert v <= w and w % v == 0, (ts, td, eb, v, w)
     for name, want in [("tile8x8", 1), ("transpose", 1), ("retile", 8), ("interleave", 1), ("interleave_cm", 1),
-                       ("nhwc2nchw", 1), ("padtiles", 1)]:
+                       ("nhwc2nchw", 1), ("padtiles", 1), ("shard_pack", 1)]:
         w = W.small(name)
         v = lr.max_common_vector(w.src_layout, w.dst_layout, w.elem_bytes)
         assert v == want == O.max_common_vector(O.parse(w.src_layout), O.parse(w.dst_layout), w.elem_bytes)
@@ -448,7 +448,8 @@ def test_common_vector_sound_and_tight_on_workloads():
 
 
 EXPECTED_PATH = {"tile8x8": "alias", "transpose": "transpose", "retile": "vector", "interleave": "interleave",
-                 "interleave_cm": "transpose", "nhwc2nchw": "transpose", "padtiles": "staged"}
+                 "interleave_cm": "transpose", "nhwc2nchw": "transpose", "padtiles": "staged",
+                 "shard_pack": "transpose"}
 
 
 @pytest.mark.parametrize("name", list(W.FULL))

@@ -390,10 +390,13 @@ JOINT_FULL = {
     "nhwc2nchw": [(3136, 256, 1), (256, 1, 3136), (128, 802816, 802816)],
     "padtiles": [(4, 18, 1), (8, 1, 4), (2, 9, 32), (1048576, 72, 64)],
     "tile8x8": [(8, 1, 1), (8, 8, 8)],  # dst (8,8) refinement, aliased: not used
+    # block j's columns follow block j-1's in the destination: one rectangular transpose
+    "shard_pack": [(1024, 8192, 1), (8192, 1, 1024)],
 }
 
 
-@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles"])
+@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles",
+                                  "shard_pack"])
 def test_joint_flat_of_workloads(name):
     w = W.full(name)
     got = O.joint_flat(O.parse(w.src_layout), O.parse(w.dst_layout), sort_by_dst=True)
@@ -611,11 +614,33 @@ def test_forms_equal_oracle_copy():
         "interleave_cm": lambda s: F.interleave_cm(s, 2, 4, 72, 136),
         "nhwc2nchw": lambda s: F.nhwc2nchw(s, 3, 7, 9, 40),
         "padtiles": lambda s: F.padtiles(s, 1000),
+        "shard_pack": lambda s: F.shard_pack(s, 520, 2112, 8),
     }
     for name, form in cases.items():
         w = W.small(name)
         src, out = _run(w)
         assert np.array_equal(form(src), out), name
+
+
+def test_shard_pack_exchange_reassembles_the_transpose():
+    """The pack of a row-sharded transpose, followed by the exchange (GPU j receives
+    block j of every GPU's pack), leaves on each GPU its row block of the transposed
+    matrix: simulated for a 48 x 48 matrix over 4 GPUs with the oracle's copy."""
+    n, g = 48, 4
+    rows = n // g
+    m = np.random.default_rng(11).integers(0, 1 << 16, (n, n), dtype=np.uint16)
+    w = W.shard_pack(rows, n, g)
+    Ls, Ld = O.parse(w.src_layout), O.parse(w.dst_layout)
+    packs = []
+    for i in range(g):
+        block = np.ascontiguousarray(m[i * rows:(i + 1) * rows]).reshape(-1).view(np.uint8)
+        dst = np.full(block.size, 0xA5, np.uint8)
+        packs.append(O.copy(block, Ls, dst, Ld, 2).view(np.uint16).reshape(g, rows * rows))
+    for j in range(g):
+        # GPU j's share of the transposed matrix: rows [j*rows, (j+1)*rows), the
+        # columns coming from GPU i at [i*rows, (i+1)*rows)
+        got = np.concatenate([packs[i][j].reshape(rows, rows) for i in range(g)], axis=1)
+        assert np.array_equal(got, m.T[j * rows:(j + 1) * rows])
 
 
 # ---------------------------------------------------------------------------

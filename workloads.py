@@ -5,7 +5,7 @@ seeded random bytes.  It holds none of the layout arithmetic (no evaluation,
 composition or copying), so both the CPU oracle's tests and the HIP path's tests
 and benchmark can share it without sharing the method.
 
-The five workloads (names follow the sizes they carry):
+The workloads (names follow the sizes they carry):
 
 * ``tile8x8``     one 8x8 fp32 tile, column-major source, blocked (aliased)
                   destination ((4,2),(2,4)):((2,16),(1,8)).
@@ -18,6 +18,9 @@ The five workloads (names follow the sizes they carry):
 * ``nhwc2nchw``   fp16 NHWC (128,56,56,256) -> NCHW.
 * ``padtiles``    2**20 padded 8x8 fp32 tiles, source (8,8):(1,9) per tile read in
                   thread-value order ((4,8),2):((16,1),8), destination compact.
+* ``shard_pack``  the local pack of a transpose sharded by rows over 8 GPUs: one GPU's
+                  1024 x 8192 fp16 row block -> 8 contiguous 1024 x 1024 blocks, block j
+                  holding columns [1024 j, 1024 j + 1024) transposed (what GPU j receives).
 
 Every workload takes a ``scale`` so tests can run the same structure small.
 Destination buffers start filled with byte 0xA5 so untouched positions are checked.
@@ -184,6 +187,17 @@ def padtiles(tiles: int = 1 << 20) -> Workload:
         n_elems=64 * tiles)
 
 
+def shard_pack(rows: int = 1024, cols: int = 8192, parts: int = 8) -> Workload:
+    # logical (r, c, j) with column j*w + c of the row block, w = cols / parts; block j
+    # of the destination is contiguous, column-major over (r, c)
+    w = cols // parts
+    return Workload(
+        name=f"shard_pack{rows}x{cols}/{parts}", elem_bytes=2,
+        src_layout=f"({rows},{w},{parts}):({cols},1,{w})",
+        dst_layout=f"({rows},{w},{parts}):(1,{rows},{rows * w})",
+        src_elems=rows * cols, dst_elems=rows * cols, seed=8, values="bits16", n_elems=rows * cols)
+
+
 FULL = {
     "tile8x8": tile8x8,
     "transpose": transpose,
@@ -192,6 +206,7 @@ FULL = {
     "interleave_cm": interleave_cm,
     "nhwc2nchw": nhwc2nchw,
     "padtiles": padtiles,
+    "shard_pack": shard_pack,
 }
 
 
@@ -205,6 +220,7 @@ def small(name: str) -> Workload:
         "interleave_cm": lambda: interleave_cm(2, 4, 72, 136),
         "nhwc2nchw": lambda: nhwc2nchw(3, 7, 9, 40),
         "padtiles": lambda: padtiles(1000),
+        "shard_pack": lambda: shard_pack(520, 2112, 8),
     }[name]()
 
 

@@ -229,6 +229,7 @@ struct GenericArgs {
   uint64_t sws_mask64, swd_mask64;
   int64_t n_units;
   int64_t n_chunks;  // groups of 256 * U units, U the per-lane unroll
+  uint32_t bufst;    // 1: streaming 16-byte stores as buffer stores from dst (span < 4 GiB)
 };
 
 // One unit (UB bytes) per lane and step, one or four units per lane (U); with four,
@@ -279,6 +280,24 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
   using T = typename Raw<UB>::T;
   const T* __restrict__ src = (const T*)a.src;
   T* __restrict__ dst = (T*)a.dst;
+  if constexpr (NT && UB == 16 && U == 1 && !WIDE) {
+    if (a.bufst) {
+      // Streaming stores as buffer stores with the nt and sc1 policy bits (measured
+      // faster than nt alone on large copies); the host checks that every
+      // destination byte lies under 4 GiB from the base.
+      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.dst, 0, -1, kBufferWord3);
+      for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
+        const int64_t i0 = ch * 256 + threadIdx.x;
+        if (i0 < a.n_units) {
+          uint64_t s0, d0;
+          generic_offsets<false>(a, i0, &s0, &d0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, gload<NT, T>(src + s0)),
+                                                 rd, (uint32_t)(d0 * 16), 0, kPolicyNtSc1);
+        }
+      }
+      return;
+    }
+  }
   for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
     const int64_t i0 = ch * (256 * U) + threadIdx.x;
     if constexpr (U == 1) {
@@ -1177,6 +1196,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.swd_mask64 = zd.b ? (((uint64_t(1) << zd.b) - 1) << zd.m) : 0;
       a.n_units = p.n_units;
       a.n_chunks = (p.n_units + 256 * p.unroll - 1) / (256 * p.unroll);
+      a.bufst = p.bufst ? 1u : 0u;
       const int ub = p.v * p.eb;
       LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.nt, grid, st));
       return check_launch();

@@ -85,7 +85,8 @@ struct Plan {
   bool nt;
   bool direct;        // staged: direct global -> LDS loads (no register round trip)
   bool tel;           // transpose: element-granular tiles (rows without aligned chunks)
-  bool bufst;         // LDS transpose: streaming stores as buffer stores (tile span < 4 GiB)
+  bool bufst;         // streaming 16-byte stores as buffer stores with the nt and sc1 bits:
+                      // vector path (destination span < 4 GiB) and LDS transpose (tile span)
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB

@@ -133,6 +133,15 @@ static uint32_t env_u32(const char* name, uint32_t dflt) {
   return (uint32_t)std::strtoul(e, nullptr, 0);
 }
 
+// One past the highest destination byte the joint modes reach (a destination
+// swizzle changes only the bits under 2^(M+B)).
+static int64_t dst_span_bytes(const Plan& p) {
+  int64_t md = 0;
+  for (int k = 0; k < p.rank; ++k) md += (p.m[k].ext - 1) * p.m[k].sd;
+  if (p.sw_d.b) md |= (int64_t(1) << (p.sw_d.m + p.sw_d.b)) - 1;
+  return (md + 1) * p.eb;
+}
+
 static int plan_alias(Plan* p, int64_t n, int64_t cos_s, int64_t cos_d) {
   const int64_t win = 8192;  // dst offsets owned by one workgroup (LDS owner table)
   int64_t windows = (cos_d + win - 1) / win;
@@ -252,6 +261,12 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       std::stable_sort(p->m + 1, p->m + p->rank, [](const JMode& x, const JMode& y) {
         return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
       });
+    // Streaming 16-byte units are stored as buffer stores with the nt and sc1
+    // cache-policy bits (a 512 MiB copy: 6.41 -> 6.55 TB/s), addressed by one 32-bit
+    // byte offset from the destination base: the destination's span must stay
+    // under 4 GiB.  LR_SC1=0 keeps global stores.
+    p->bufst = p->v * p->eb == 16 && p->unroll == 1 && !p->wide && env_u32("LR_SC1", 1) != 0 &&
+               dst_span_bytes(*p) < (int64_t(1) << 32);
     return LR_OK;
   }
 
@@ -434,14 +449,14 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // 6.26 (the interleave and staged kernels measured slower with them, 1-1.5 %).
       // Buffer offsets are 32-bit: each workgroup stores relative to its tile's
       // lowest destination offset, so the tile's destination span must stay under
-      // 4 GiB.  LR_TSC1=0 keeps global stores.
+      // 4 GiB.  LR_SC1=0 keeps global stores.
       {
         // rounding the base down and swizzling the highest offset up each add less
         // than one swizzle block (2^(M+B) elements)
         const int64_t swz_blk = p->sw_d.b ? (int64_t(1) << (p->sw_d.m + p->sw_d.b)) : 0;
         const int64_t span = ((p->tile_a - 1) * p->m[a].sd + p->tile_b + 2 * swz_blk) * p->eb;
         p->bufst = p->path == LR_PATH_TRANSPOSE && !p->tel && !p->direct && V * p->eb == 16 &&
-                   span < (int64_t(1) << 32) && env_u32("LR_TSC1", 1) != 0;
+                   span < (int64_t(1) << 32) && env_u32("LR_SC1", 1) != 0;
       }
       const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
       const int64_t ntb = (ext_b + p->tile_b - 1) / p->tile_b;
@@ -521,6 +536,9 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   for (int k = 0; k < p->rank; ++k) ne *= p->m[k].ext;
   p->n_units = ne / v;
   p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
+  // 16-byte units (fused elements) take the vector path's buffer stores too
+  p->bufst = v * p->eb == 16 && p->unroll == 1 && !p->wide && env_u32("LR_SC1", 1) != 0 &&
+             dst_span_bytes(*p) < (int64_t(1) << 32);
   return LR_OK;
 }
 
@@ -528,6 +546,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
 // indexing relies on; a violation means a planner bug and nothing is launched.
 int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
   auto bad = [] { return LR_ERR_PATH; };
+  if (p.bufst && p.path != LR_PATH_GENERIC && p.path != LR_PATH_VECTOR && p.path != LR_PATH_TRANSPOSE) return bad();
   if (p.path == LR_PATH_DUAL || p.path == LR_PATH_ALIAS) return LR_OK;  // evaluate the validated layouts
   if (p.rank < 1 || p.rank > kMaxKernelModes) return bad();
   int64_t ms = 0, md = 0, prod = 1;
@@ -555,6 +574,9 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
           if (p.m[k].ss % v || p.m[k].sd % v) return bad();
       }
       if (p.n_units * v != prod) return bad();
+      // buffer stores: one 32-bit byte offset from the destination base
+      if (p.bufst && (v * p.eb != 16 || p.unroll != 1 || p.wide || (bound(md, p.sw_d) * p.eb >> 32) != 0))
+        return bad();
       return LR_OK;
     case LR_PATH_TRANSPOSE:
     case LR_PATH_TRANSPOSE_DIRECT: {

@@ -276,7 +276,7 @@ def test_copy_random_pairs(dev, monkeypatch):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
                "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 4)),
-               "LR_TEL": rng.choice(["0", "1", "2"]), "LR_TSC1": rng.choice("01")}
+               "LR_TEL": rng.choice(["0", "1", "2"]), "LR_SC1": rng.choice("01")}
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         if i % 50 == 0:
@@ -541,7 +541,7 @@ def test_transpose_streaming_store_forms(dev, env_knob, tsc1):
     bits).  Every tile shape, with ragged edges, a batch mode, a grouped b run and
     destination swizzles (the tile base is rounded down past the swizzled bits)."""
     env_knob.setenv("LR_NT", "1")
-    env_knob.setenv("LR_TSC1", tsc1)
+    env_knob.setenv("LR_SC1", tsc1)
     cm = W.small("interleave_cm")
     cases = [("(520,264):(264,1)", "(520,264):(1,520)", 2),
              ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 2),
@@ -572,6 +572,37 @@ def test_transpose_streaming_store_forms(dev, env_knob, tsc1):
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, shape)
             ran += 1
     assert ran >= 40
+
+
+@pytest.mark.parametrize("sc1", ["0", "1"])
+def test_vector_streaming_store_forms(dev, env_knob, sc1):
+    """The vector path's streaming stores, global nt or buffer stores with nt and sc1
+    from the destination base: contiguous, strided, swizzled and retiled layouts with
+    ragged unit counts, both traversal orders."""
+    env_knob.setenv("LR_NT", "1")
+    env_knob.setenv("LR_SC1", sc1)
+    rt = W.small("retile")
+    cases = [("100000:1", "100000:1", 100000, 2),
+             ("(64,130,3):(1,64,8320)", "(64,130,3):(1,200,26000)", 64 * 130 * 3, 2),
+             ("(8,4100):(1,8)", "Sw<2,2,3> o (8,4100):(1,8)", 8 * 4100, 4),
+             ("(2,777):(1,2)", "(2,777):(1,1600)", 2 * 777, 8),
+             ("(1,999):(1,1)", "(1,999):(1,3)", 999, 16),
+             (rt.src_layout, rt.dst_layout, rt.n_elems, 2)]
+    ran = 0
+    for vorder in ("0", "1"):
+        env_knob.setenv("LR_VORDER", vorder)
+        for ci, (ts, td, n, eb) in enumerate(cases):
+            ns, nd = max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize)
+            p = lr.copy_plan(ts, ns, td, nd, eb)
+            assert p["path"] in ("vector", "generic") and p["vec_elems"] * p["elem_bytes"] == 16, (ts, td, p)
+            assert p["store_policy"] == (18 if sc1 == "1" else 2), (ts, td, p)
+            src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
+            dst = np.full(nd * eb, 0xA5, np.uint8)
+            want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+            say("vector stores", "sc1" if sc1 == "1" else "global", ts, "->", td, "eb", eb, "vorder", vorder)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td)
+            ran += 1
+    assert ran == 2 * len(cases)
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])

@@ -550,10 +550,11 @@ def test_plan_workgroup_order(monkeypatch):
 
 
 def test_plan_store_policy(monkeypatch):
-    """Streaming copies load and store non-temporally; the LDS transpose's streaming
-    stores also carry the sc1 scope bit (buffer stores), only while a tile's
-    destination span stays under 4 GiB (32-bit buffer offsets)."""
-    for k in ("LR_NT", "LR_TSC1", "LR_TDIRECT", "LR_TEL"):
+    """Streaming copies load and store non-temporally; the LDS transpose's and the
+    vector path's streaming stores also carry the sc1 scope bit (buffer stores), only
+    while a tile's (transpose) or the whole destination's (vector) span stays under
+    4 GiB (32-bit buffer offsets)."""
+    for k in ("LR_NT", "LR_SC1", "LR_TDIRECT", "LR_TEL"):
         monkeypatch.delenv(k, raising=False)
 
     def plan(name):
@@ -566,9 +567,9 @@ def test_plan_store_policy(monkeypatch):
     for name, pol in want.items():
         p = plan(name)
         assert (p["load_policy"], p["store_policy"]) == pol, (name, p["path"])
-    monkeypatch.setenv("LR_TSC1", "0")
+    monkeypatch.setenv("LR_SC1", "0")
     assert plan("transpose")["store_policy"] == 2
-    monkeypatch.delenv("LR_TSC1")
+    monkeypatch.delenv("LR_SC1")
     monkeypatch.setenv("LR_TDIRECT", "1")
     assert plan("transpose")["store_policy"] == 2  # the direct-load kernel keeps global stores
     monkeypatch.delenv("LR_TDIRECT")
@@ -580,6 +581,15 @@ def test_plan_store_policy(monkeypatch):
         assert p["path"] == "transpose" and p["tile_a"] == 16 and p["store_policy"] == pol, (sd, p)
     # element tiles (rows without aligned chunks) keep global stores
     assert lr.copy_plan("(301,517):(517,1)", 301 * 517, "(301,517):(1,301)", 301 * 517, 2)["store_policy"] == 2
+    # the vector path and 16-byte generic units: stores from the destination base,
+    # span under 4 GiB
+    assert plan("retile")["store_policy"] == 18
+    for n, pol in (((1 << 28) - 1, 18), (1 << 28, 2)):
+        p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16)
+        assert p["vec_elems"] * p["elem_bytes"] == 16 and p["store_policy"] == pol, (n, p)
+    assert lr.copy_plan("4096:1", 4096, "4096:1", 4096, 4, lr.COPY_WIDE_INDEX)["store_policy"] == 2
+    monkeypatch.setenv("LR_SC1", "0")
+    assert plan("retile")["store_policy"] == 2
 
 
 def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):

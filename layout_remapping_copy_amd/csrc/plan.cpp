@@ -315,10 +315,16 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->b = b;
       p->v = (int)V;
       // one 16-byte store per lane from NB narrow loads measured faster (every store
-      // instruction covers 1 KiB of contiguous dst); LR_INARROW=0 selects the other
+      // instruction covers 1 KiB of contiguous dst; NB 16-byte stores per lane from NB
+      // wide loads write every NB-th chunk per instruction: 3.8 against 6.1 TB/s);
+      // LR_INARROW=0 selects the other
       p->inarrow = (int)(env_u32("LR_INARROW", 1) & 1u);
-      // a-elements per workgroup, matching the kernel's per-lane unroll
-      p->tile_a = p->inarrow ? 4 * 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
+      // a-elements per workgroup, matching the kernel's per-lane unroll (one dst
+      // chunk per lane on the narrow variant)
+      p->tile_a = p->inarrow ? 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
+      // the narrow variant's streaming stores as buffer stores with the nt and sc1
+      // bits from the destination base (head interleave 6.27 -> 6.55 TB/s)
+      p->bufst = p->inarrow && env_u32("LR_SC1", 1) != 0 && dst_span_bytes(*p) < (int64_t(1) << 32);
       p->tile_b = nb;
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
@@ -546,7 +552,9 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
 // indexing relies on; a violation means a planner bug and nothing is launched.
 int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
   auto bad = [] { return LR_ERR_PATH; };
-  if (p.bufst && p.path != LR_PATH_GENERIC && p.path != LR_PATH_VECTOR && p.path != LR_PATH_TRANSPOSE) return bad();
+  if (p.bufst && p.path != LR_PATH_GENERIC && p.path != LR_PATH_VECTOR && p.path != LR_PATH_TRANSPOSE &&
+      p.path != LR_PATH_INTERLEAVE)
+    return bad();
   if (p.path == LR_PATH_DUAL || p.path == LR_PATH_ALIAS) return LR_OK;  // evaluate the validated layouts
   if (p.rank < 1 || p.rank > kMaxKernelModes) return bad();
   int64_t ms = 0, md = 0, prod = 1;
@@ -629,7 +637,8 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.a].sd != nb || p.tile_b != nb) return bad();
       if (v * p.eb != 16 || p.m[p.a].ext % v || nb * p.eb > 16) return bad();
       // the kernel's per-lane unroll
-      if (p.tile_a != (p.inarrow ? 4 * 256 * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v)) return bad();
+      if (p.tile_a != (p.inarrow ? 256 * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v)) return bad();
+      if (p.bufst && (!p.inarrow || (bound(md, p.sw_d) * p.eb >> 32) != 0)) return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.a && k != p.b && p.m[k].sd % v) return bad();

@@ -710,17 +710,28 @@ def test_staged_direct_loads(dev, env_knob, direct):
 
 @pytest.mark.parametrize("narrow", [0, 1])
 def test_interleave_variants(dev, env_knob, narrow):
+    """Both load variants at every NB, with plain accesses and with streaming ones
+    (the narrow variant's streaming stores as global nt stores or as buffer stores
+    with nt and sc1), including a swizzled destination."""
     env_knob.setenv("LR_INARROW", str(narrow))
+    cases = []
     for eb, nb in [(1, 2), (1, 4), (1, 8), (1, 16), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (8, 2)]:
         a, bt = 16 // eb * 40, 3
-        ts, td = f"({nb},{a},{bt}):({a},1,{a * nb})", f"({nb},{a},{bt}):(1,{nb},{a * nb})"
-        n = a * nb * bt
-        assert lr.copy_plan(ts, n, td, n, eb)["path"] == "interleave"
-        src = np.random.default_rng(eb * 31 + nb).integers(0, 256, n * eb, dtype=np.uint8)
-        dst = np.full(n * eb, 0xA5, np.uint8)
+        cases.append((f"({nb},{a},{bt}):({a},1,{a * nb})", f"({nb},{a},{bt}):(1,{nb},{a * nb})", a * nb * bt, eb))
+    cases.append(("(2,6400,3):(6400,1,12800)", "Sw<2,4,3> o (2,6400,3):(1,2,12800)", 2 * 6400 * 3, 2))
+    for ci, (ts, td, n, eb) in enumerate(cases):
+        nd = max(n, lr.parse(td).cosize)
+        src = np.random.default_rng(ci).integers(0, 256, n * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-        say("interleave narrow", narrow, "eb", eb, "nb", nb)
-        assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)
+        for nt, sc1 in (("0", "1"), ("1", "0"), ("1", "1")):
+            env_knob.setenv("LR_NT", nt)
+            env_knob.setenv("LR_SC1", sc1)
+            p = lr.copy_plan(ts, n, td, nd, eb)
+            assert p["path"] == "interleave"
+            assert p["store_policy"] == (0 if nt == "0" else 18 if (sc1 == "1" and narrow) else 2), p
+            say("interleave narrow", narrow, ts, "->", td, "eb", eb, "nt", nt, "sc1", sc1)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, nt, sc1)
 
 
 @pytest.mark.parametrize("vorder", [0, 1])

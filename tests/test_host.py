@@ -550,10 +550,10 @@ def test_plan_workgroup_order(monkeypatch):
 
 
 def test_plan_store_policy(monkeypatch):
-    """Streaming copies load and store non-temporally; the LDS transpose's and the
-    vector path's streaming stores also carry the sc1 scope bit (buffer stores), only
-    while a tile's (transpose) or the whole destination's (vector) span stays under
-    4 GiB (32-bit buffer offsets)."""
+    """Streaming copies load and store non-temporally; the streaming stores of the
+    LDS transpose, the vector path and the narrow interleave also carry the sc1 scope
+    bit (buffer stores), only while a tile's (transpose) or the whole destination's
+    span stays under 4 GiB (32-bit buffer offsets)."""
     for k in ("LR_NT", "LR_SC1", "LR_TDIRECT", "LR_TEL"):
         monkeypatch.delenv(k, raising=False)
 
@@ -562,7 +562,7 @@ def test_plan_store_policy(monkeypatch):
         flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
         return lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
 
-    want = {"transpose": (2, 18), "interleave_cm": (2, 18), "nhwc2nchw": (2, 18), "interleave": (2, 2),
+    want = {"transpose": (2, 18), "interleave_cm": (2, 18), "nhwc2nchw": (2, 18), "interleave": (2, 18),
             "padtiles": (2, 2), "retile": (0, 0), "tile8x8": (0, 0)}
     for name, pol in want.items():
         p = plan(name)

@@ -507,8 +507,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         ok = (maxbase + Fc * 16 / p->eb) <= src_cap;
         if (ok) {
           const int64_t cpt = P * p->eb / 16;  // 16-byte dst chunks per tile
-          // about four dst chunks per lane, and at most 40 KiB of LDS per workgroup
-          const int64_t K = std::max<int64_t>(1, std::min<int64_t>(1024 / cpt, 2560 / Fc));
+          // about two dst chunks per lane (padded tiles: 5.85 TB/s, against 5.79 with
+          // four and 5.57 with eight; one measured 4.8-5.1), and at most 40 KiB of LDS
+          // per workgroup.  Stores with the sc1 bit measured no faster here.
+          const int64_t K = std::max<int64_t>(1, std::min<int64_t>(512 / cpt, 2560 / Fc));
           p->path = LR_PATH_STAGED;
           // direct global -> LDS loads measured 2.6 % faster on the padded tiles
           // (5.79 vs 5.64 TB/s): the footprint never passes through registers, so

@@ -18,6 +18,13 @@
 // Wavefronts are 64 lanes.  Workgroups have 256 lanes (4 waves, one per SIMD),
 // except the tile transposes (TA*TB lanes, 256 to 1024) and the ordered-alias
 // kernel (1024 lanes, one window per workgroup).
+//
+// Cache policy: streaming copies (by default when source plus destination reach
+// the 256 MiB last-level cache) load and store with the non-temporal bit.  The
+// streaming stores of the vector path, the head interleave and the LDS tile
+// transpose are buffer stores that also carry the sc1 scope bit, which HIP's
+// global stores cannot express; their 32-bit offsets run from a base the host has
+// checked (the destination, or a transpose tile's lowest offset).
 
 #include <hip/hip_runtime.h>
 
@@ -790,7 +797,8 @@ struct InterleaveArgs {
 //     them interleaved as NB chunks;
 //   NARROW == true: each lane writes one 16-byte dst chunk, built from NB loads of
 //     16/NB bytes (P = V/NB positions of a, one load per b), so that every store
-//     instruction of a wave covers 1 KiB of contiguous dst.
+//     instruction of a wave covers 1 KiB of contiguous dst.  One chunk per lane:
+//     more per lane measured slower.
 template <int EB, int NB, bool NARROW, bool NT>
 __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
   using T = typename Raw<EB>::T;

@@ -130,6 +130,33 @@ def test_eval_random(dev):
         assert np.array_equal(gpu_eval(dev, t), O.eval_indices(L, np.arange(O.size(L)))), t
 
 
+def test_eval_ranges_pairwise(dev):
+    """Index ranges of layouts whose offsets fit 31 bits run two indices per lane (the
+    second by a step of leaf 0 when its digit does not wrap) with 16-byte stores:
+    odd counts, counts past the size (-1 there), leaf-0 extents of 1 and 2,
+    swizzles, and an output only 8-byte aligned (one index per lane)."""
+    import ctypes
+    texts = ["Sw<3,3,3> o ((128,32),(64,64)):((64,524288),(1,8192))", "(1,7,3):(5,1,7)", "(2,9,5):(90,10,1)",
+             "((4,8),2,(3,5)):((16,1),8,(64,192))", "Sw<2,1,3> o (3,5,7):(35,7,1)", "5:0", "2147483:1000", "2147484:1001"]
+    for t in texts:
+        L = O.parse(t)
+        size = O.size(L)
+        for n in sorted({1, 2, 5, size, size + 3}):
+            ks = np.arange(n)
+            want = np.where(ks < size, O.eval_indices(L, np.minimum(ks, size - 1)), -1)
+            say("eval range", t, "n", n)
+            assert np.array_equal(gpu_eval(dev, t, n=n), want), (t, n)
+            # an output starting 8 bytes into an allocation
+            buf = torch.full((n + 1,), 7, dtype=torch.int64, device=dev)
+            Lc = lr.parse(t)
+            rc = lr.binding.lib().lr_layout_eval(ctypes.byref(Lc.c), None, n, ctypes.c_void_p(buf.data_ptr() + 8),
+                                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            assert rc == 0
+            torch.cuda.synchronize()
+            got = buf.cpu().numpy()
+            assert got[0] == 7 and np.array_equal(got[1:], want), (t, n)
+
+
 def test_eval_wide(dev):
     say("eval wide")
     text = "(65536,65536):(65536,1)"  # 2^32 indices: 64-bit division path

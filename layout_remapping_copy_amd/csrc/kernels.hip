@@ -234,7 +234,14 @@ __global__ void __launch_bounds__(256) k_eval_index(EvalArgs a) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (int64_t)gridDim.x * 256) {
     int64_t k = a.idx ? a.idx[i] : i;
     int64_t off = -1;
-    if (k >= 0 && k < a.size) off = (int64_t)swz64((uint64_t)eval_leaves(a, 0, a.nleaves, k), a.swz_mask, a.swz_shift);
+    if (k >= 0 && k < a.size) {
+      if (a.s32) {
+        uint32_t d;
+        off = swz32_eval(a, eval32(a, (uint32_t)k, &d));
+      } else {
+        off = (int64_t)swz64((uint64_t)eval_leaves(a, 0, a.nleaves, k), a.swz_mask, a.swz_shift);
+      }
+    }
     a.out[i] = off;
   }
 }

@@ -300,7 +300,7 @@ def main():
     # ---- the other large remapping copies, timed the same way
     if not args.no_others:
         others = {}
-        for name in ("retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack"):
+        for name in ("retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw"):
             wo = W.full(name)
             p = lr.copy_plan(wo.src_layout, wo.src_elems, wo.dst_layout, wo.dst_elems, wo.elem_bytes)
             prs = _pairs(torch, dev, wo.src_elems * wo.elem_bytes, wo.dst_elems * wo.elem_bytes)

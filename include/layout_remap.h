@@ -266,7 +266,9 @@ typedef enum {
   LR_PATH_STAGED = 4,     /* compact source footprint per tile staged in LDS, gathered */
   LR_PATH_DUAL = 5,       /* no joint refinement: each side evaluated from the index */
   LR_PATH_ALIAS = 6,      /* non-injective dst, sequential last-writer semantics */
-  LR_PATH_TRANSPOSE_DIRECT = 7 /* register-blocked transpose storing straight to global */
+  LR_PATH_TRANSPOSE_DIRECT = 7, /* register-blocked transpose storing straight to global */
+  LR_PATH_DEINTERLEAVE = 8     /* short src-contiguous mode (2..8 channels, <= 16 bytes) spread
+                                  into planes: the mirror of the interleave */
 } lr_path;
 
 /* Copy flags. */

@@ -42,8 +42,9 @@ PATH_STAGED = 4
 PATH_DUAL = 5
 PATH_ALIAS = 6
 PATH_TRANSPOSE_DIRECT = 7
+PATH_DEINTERLEAVE = 8
 PATH_NAMES = {0: "generic", 1: "vector", 2: "transpose", 3: "interleave", 4: "staged", 5: "dual",
-              6: "alias", 7: "transpose_direct"}
+              6: "alias", 7: "transpose_direct", 8: "deinterleave"}
 
 # flags
 COPY_ORDERED_ALIAS = 0x1

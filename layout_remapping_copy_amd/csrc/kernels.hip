@@ -941,6 +941,104 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
   }
 }
 
+// ------------------------------------------------------------------ channel shuffle
+
+struct ChanArgs {
+  const void* src;
+  void* dst;
+  uint32_t pixels;   // extent of the pixel mode (a multiple of the chunk's V elements)
+  uint32_t plane;    // stride of the channel mode on the planar side (elements)
+  uint32_t tiles;    // workgroups per batch index: pixels / (256 V), rounded up
+  FD fd_tiles;
+  BatchArg batch;
+  uint32_t bufst;    // 1: streaming stores as buffer stores from dst (span < 4 GiB)
+};
+
+// A 16-byte streaming store: a buffer store with the nt and sc1 bits from `base`
+// when `buf` (the host has checked the 4 GiB span), else a global store.
+template <bool NT, typename C>
+__device__ __forceinline__ void store16(char* base, uint32_t byte_off, const C& v, bool buf) {
+  static_assert(sizeof(C) == 16, "16-byte chunks");
+  if constexpr (NT) {
+    if (buf) {
+      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(base, 0, -1, kBufferWord3);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, v), rd, byte_off, 0,
+                                             kPolicyNtSc1);
+      return;
+    }
+  }
+  gstore<NT, C>(base + byte_off, v);
+}
+
+// Pixels with C channels side by side (the interleaved side: pixel stride C,
+// channel stride 1) <-> C planes (the planar side: channel stride `plane`, pixel
+// stride 1): image layouts such as NHWC <-> NCHW with few channels, where neither
+// side has a contiguous run of 16 bytes per channel on the interleaved side.  The
+// pairing is that of [print_layout page, section 4.2], for any C from 2 to 8.
+// Lane l of a workgroup owns V = 16/EB consecutive pixels of all C channels: C
+// chunks on either side, exchanged by a C x V transpose in registers.  On the
+// interleaved side those C chunks are contiguous per lane, so that side goes
+// through LDS: a wave instruction then moves 64 consecutive chunks on both sides.
+//   INTERLEAVE == false (de-interleave): loads of the contiguous interleaved block
+//     into LDS, C LDS reads per lane, stores of one chunk per plane;
+//   INTERLEAVE == true: loads of one chunk per plane, C LDS writes per lane,
+//     stores of the contiguous interleaved block.
+template <int EB, int C, bool INTERLEAVE, bool NT>
+__global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
+  using T = typename Raw<EB>::T;
+  constexpr int V = 16 / EB;
+  using Ch = Chunk<T, V>;
+  __shared__ Ch lds[256 * C];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  const uint32_t blk = blockIdx.x;
+  const uint32_t r = fdiv(blk, t.fd_tiles);
+  const uint32_t tile = blk - r * t.tiles;
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r, &bs, &bd);
+  const uint32_t p0 = tile * (256 * V);  // the workgroup's first pixel
+  const uint32_t left = (t.pixels - p0) / V;
+  const uint32_t nblk = left < 256u ? left : 256u;  // pixel blocks of V in this workgroup
+  const uint32_t l = threadIdx.x;
+  const bool mine = l < nblk;
+
+  if constexpr (!INTERLEAVE) {
+    const char* sb = src + (size_t)(p0 * C + bs) * EB;  // interleaved block: nblk * C chunks
+    Ch tmp[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      if (l + 256u * j < nblk * C) tmp[j] = gload<NT, Ch>(sb + (size_t)(l + 256u * j) * 16);
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      if (l + 256u * j < nblk * C) lds[l + 256u * j] = tmp[j];
+    __syncthreads();
+    if (!mine) return;
+    Ch in[C], out[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) in[j] = lds[l * C + j];
+#pragma unroll
+    for (int e = 0; e < C * V; ++e) out[e % C].e[e / C] = in[e / V].e[e % V];  // element e: pixel e / C, channel e % C
+#pragma unroll
+    for (int c = 0; c < C; ++c) store16<NT>(dst, (c * t.plane + p0 + V * l + bd) * EB, out[c], t.bufst);
+  } else {
+    if (mine) {
+      Ch in[C], out[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) in[c] = gload<NT, Ch>(src + (size_t)(c * t.plane + p0 + V * l + bs) * EB);
+#pragma unroll
+      for (int e = 0; e < C * V; ++e) out[e / V].e[e % V] = in[e % C].e[e / C];
+#pragma unroll
+      for (int j = 0; j < C; ++j) lds[l * C + j] = out[j];
+    }
+    __syncthreads();
+    const uint32_t db = (p0 * C + bd) * EB;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      if (l + 256u * j < nblk * C) store16<NT>(dst, db + (l + 256u * j) * 16, lds[l + 256u * j], t.bufst);
+  }
+}
+
 // ------------------------------------------------------------------ staged footprint gather
 
 struct StagedArgs {
@@ -1213,6 +1311,36 @@ static bool launch_interleave_n(const InterleaveArgs& a, int nb, unsigned grid, 
   return false;
 }
 
+template <int EB, int CC, bool INTERLEAVE, bool NT>
+static bool launch_chan_one(const ChanArgs& a, unsigned grid, hipStream_t st) {
+  if constexpr (chan_supported(EB, CC)) {
+    hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
+    return true;
+  }
+  return false;
+}
+
+template <int EB, bool INTERLEAVE, bool NT>
+static bool launch_chan_c(const ChanArgs& a, int c, unsigned grid, hipStream_t st) {
+  switch (c) {
+    case 2: return launch_chan_one<EB, 2, INTERLEAVE, NT>(a, grid, st);
+    case 3: return launch_chan_one<EB, 3, INTERLEAVE, NT>(a, grid, st);
+    case 4: return launch_chan_one<EB, 4, INTERLEAVE, NT>(a, grid, st);
+    case 5: return launch_chan_one<EB, 5, INTERLEAVE, NT>(a, grid, st);
+    case 6: return launch_chan_one<EB, 6, INTERLEAVE, NT>(a, grid, st);
+    case 7: return launch_chan_one<EB, 7, INTERLEAVE, NT>(a, grid, st);
+    case 8: return launch_chan_one<EB, 8, INTERLEAVE, NT>(a, grid, st);
+    default: return false;
+  }
+}
+
+template <int EB>
+static bool launch_chan(const ChanArgs& a, int c, bool interleave, bool nt, unsigned grid, hipStream_t st) {
+  if (interleave)
+    return nt ? launch_chan_c<EB, true, true>(a, c, grid, st) : launch_chan_c<EB, true, false>(a, c, grid, st);
+  return nt ? launch_chan_c<EB, false, true>(a, c, grid, st) : launch_chan_c<EB, false, false>(a, c, grid, st);
+}
+
 template <int EB>
 static bool launch_interleave(const InterleaveArgs& a, int nb, bool narrow, bool nt, unsigned grid, hipStream_t st) {
   if (nt)
@@ -1345,7 +1473,28 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
-    case LR_PATH_INTERLEAVE: {
+    case LR_PATH_DEINTERLEAVE:
+    case LR_PATH_INTERLEAVE:
+      if (p.path == LR_PATH_DEINTERLEAVE || p.inarrow == 2) {
+        // channel shuffle: the pixel mode is the one contiguous on the planar side
+        const bool il = p.path == LR_PATH_INTERLEAVE;
+        const int pm = il ? p.a : p.b, cm = il ? p.b : p.a;
+        ChanArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.src = src;
+        a.dst = dst;
+        a.pixels = (uint32_t)p.m[pm].ext;
+        a.plane = (uint32_t)(il ? p.m[cm].ss : p.m[cm].sd);
+        a.tiles = (uint32_t)((p.m[pm].ext + p.tile_a - 1) / p.tile_a);
+        a.fd_tiles = fd_of(a.tiles);
+        fill_batch(&a.batch, p, p.a, p.b);
+        a.bufst = p.bufst ? 1u : 0u;
+        bool ok = false;
+        LR_DISPATCH_EB(p.eb, ok = launch_chan<EBV>(a, (int)p.m[cm].ext, il, p.nt, grid, st));
+        if (!ok) return LR_ERR_PATH;
+        return check_launch();
+      }
+      {
       InterleaveArgs a;
       std::memset(&a, 0, sizeof(a));
       a.src = src;

@@ -184,7 +184,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
 
   const uint32_t forced_raw = (flags >> 8) & 0xFFu;
   const int forced = forced_raw ? (int)forced_raw - 1 : -1;
-  if (forced > LR_PATH_TRANSPOSE_DIRECT) return LR_ERR_INVALID;
+  if (forced > LR_PATH_DEINTERLEAVE) return LR_ERR_INVALID;
   const int64_t lim32 = int64_t(1) << 31;
   p->wide = (flags & LR_COPY_WIDE_INDEX) || n >= lim32 || cos_s >= lim32 || cos_d >= lim32;
   p->block = 256;
@@ -301,7 +301,12 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   // interleave: the dst-contiguous mode b is short and a follows it in dst
   if (a >= 0 && b >= 0 && a != b && (forced < 0 || forced == LR_PATH_INTERLEAVE)) {
     const int64_t nb = p->m[b].ext, V = V16;
-    bool ok = is_pow2(nb) && nb >= 2 && nb * p->eb <= 16 && p->m[a].sd == nb && p->m[a].ext % V == 0 &&
+    // NB a power of two: the register kernels; other NB from 3 to 8 (three colour
+    // channels, say): the channel shuffle through LDS, which applies no swizzle
+    const uint32_t inarrow_env = env_u32("LR_INARROW", 1);
+    const bool chan = chan_supported(p->eb, nb) && p->sw_s.b == 0 && p->sw_d.b == 0 &&
+                      (!is_pow2(nb) || inarrow_env == 2);
+    bool ok = (is_pow2(nb) || chan) && nb >= 2 && nb * p->eb <= 16 && p->m[a].sd == nb && p->m[a].ext % V == 0 &&
               swz_keeps(p->sw_s, V) && swz_keeps(p->sw_d, V) && src_align >= 16 && dst_align >= 16;
     if (ok) {
       for (int k = 0; k < p->rank && ok; ++k) {
@@ -318,13 +323,13 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // instruction covers 1 KiB of contiguous dst; NB 16-byte stores per lane from NB
       // wide loads write every NB-th chunk per instruction: 3.8 against 6.1 TB/s);
       // LR_INARROW=0 selects the other
-      p->inarrow = (int)(env_u32("LR_INARROW", 1) & 1u);
+      p->inarrow = chan ? 2 : (int)(inarrow_env & 1u);
       // a-elements per workgroup, matching the kernel's per-lane unroll (one dst
-      // chunk per lane on the narrow variant)
-      p->tile_a = p->inarrow ? 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
+      // chunk per lane on the narrow variant, V pixels per lane on the shuffle)
+      p->tile_a = p->inarrow == 2 ? 256 * V : p->inarrow ? 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
       // the narrow variant's streaming stores as buffer stores with the nt and sc1
       // bits from the destination base (head interleave 6.27 -> 6.55 TB/s)
-      p->bufst = p->inarrow && env_u32("LR_SC1", 1) != 0 && dst_span_bytes(*p) < (int64_t(1) << 32);
+      p->bufst = p->inarrow != 0 && env_u32("LR_SC1", 1) != 0 && dst_span_bytes(*p) < (int64_t(1) << 32);
       p->tile_b = nb;
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
@@ -333,6 +338,33 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       return LR_OK;
     }
     if (forced == LR_PATH_INTERLEAVE) return LR_ERR_PATH;
+  }
+
+  // de-interleave: the mirror of the above.  The src-contiguous mode a is short (C
+  // channels of at most 16 bytes together) and the dst-contiguous mode b follows it
+  // in src (the pixels of NHWC -> NCHW with few channels): each lane turns V pixels
+  // of C interleaved channels into C chunks of one plane each.
+  if (a >= 0 && b >= 0 && a != b && (forced < 0 || forced == LR_PATH_DEINTERLEAVE)) {
+    const int64_t C = p->m[a].ext, V = V16;
+    bool ok = chan_supported(p->eb, C) && p->m[b].ss == C && p->m[b].ext % V == 0 && p->m[a].sd % V == 0 &&
+              p->sw_s.b == 0 && p->sw_d.b == 0 && src_align >= 16 && dst_align >= 16;
+    for (int k = 0; k < p->rank && ok; ++k)
+      if (k != a && k != b && (p->m[k].ss % V || p->m[k].sd % V)) ok = false;
+    if (ok) {
+      p->path = LR_PATH_DEINTERLEAVE;
+      p->a = a;
+      p->b = b;
+      p->v = (int)V;
+      p->tile_a = 256 * V;  // pixels per workgroup (V per lane)
+      p->tile_b = C;
+      p->bufst = env_u32("LR_SC1", 1) != 0 && dst_span_bytes(*p) < (int64_t(1) << 32);
+      int64_t batch = 1;
+      for (int k = 0; k < p->rank; ++k)
+        if (k != a && k != b) batch *= p->m[k].ext;
+      p->grid = ((p->m[b].ext + p->tile_a - 1) / p->tile_a) * batch;
+      return LR_OK;
+    }
+    if (forced == LR_PATH_DEINTERLEAVE) return LR_ERR_PATH;
   }
 
   // transpose: register blocks of V x V elements over the src-contiguous mode a and
@@ -555,7 +587,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
 int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
   auto bad = [] { return LR_ERR_PATH; };
   if (p.bufst && p.path != LR_PATH_GENERIC && p.path != LR_PATH_VECTOR && p.path != LR_PATH_TRANSPOSE &&
-      p.path != LR_PATH_INTERLEAVE)
+      p.path != LR_PATH_INTERLEAVE && p.path != LR_PATH_DEINTERLEAVE)
     return bad();
   if (p.path == LR_PATH_DUAL || p.path == LR_PATH_ALIAS) return LR_OK;  // evaluate the validated layouts
   if (p.rank < 1 || p.rank > kMaxKernelModes) return bad();
@@ -639,12 +671,27 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.a].sd != nb || p.tile_b != nb) return bad();
       if (v * p.eb != 16 || p.m[p.a].ext % v || nb * p.eb > 16) return bad();
       // the kernel's per-lane unroll
-      if (p.tile_a != (p.inarrow ? 256 * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v)) return bad();
+      if (p.inarrow == 2) {  // channel shuffle: any NB it was built for, no swizzle
+        if (!chan_supported(p.eb, nb) || p.sw_s.b || p.sw_d.b || p.tile_a != 256 * v) return bad();
+      } else if (!is_pow2(nb) || p.tile_a != (p.inarrow ? 256 * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v)) {
+        return bad();
+      }
       if (p.bufst && (!p.inarrow || (bound(md, p.sw_d) * p.eb >> 32) != 0)) return bad();
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.a && k != p.b && p.m[k].sd % v) return bad();
       }
+      return LR_OK;
+    }
+    case LR_PATH_DEINTERLEAVE: {
+      if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
+      const int64_t C = p.m[p.a].ext;
+      if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.b].ss != C || !chan_supported(p.eb, C)) return bad();
+      if (v * p.eb != 16 || p.m[p.b].ext % v || p.m[p.a].sd % v || p.sw_s.b || p.sw_d.b) return bad();
+      if (p.bufst && (dst_span_bytes(p) >> 32) != 0) return bad();
+      if (p.tile_a != 256 * v || p.tile_b != C) return bad();
+      for (int k = 0; k < p.rank; ++k)
+        if (k != p.a && k != p.b && (p.m[k].ss % v || p.m[k].sd % v)) return bad();
       return LR_OK;
     }
     case LR_PATH_STAGED: {

@@ -202,7 +202,7 @@ def test_copy_tile8x8_aliased(dev):
 
 
 ALL_PATHS = [lr.PATH_GENERIC, lr.PATH_VECTOR, lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT, lr.PATH_INTERLEAVE,
-             lr.PATH_STAGED, lr.PATH_DUAL, lr.PATH_ALIAS]
+             lr.PATH_DEINTERLEAVE, lr.PATH_STAGED, lr.PATH_DUAL, lr.PATH_ALIAS]
 
 
 def _case_pairs():
@@ -380,10 +380,12 @@ FORMS = {
     "nhwc2nchw": lambda s: F.nhwc2nchw(s, 128, 56, 56, 256),
     "padtiles": lambda s: F.padtiles(s, 1 << 20),
     "shard_pack": lambda s: F.shard_pack(s, 1024, 8192, 8),
+    "rgb_nhwc2nchw": lambda s: F.nhwc2nchw(s, 512, 224, 224, 3),
 }
 
 FULL_PATH = {"transpose": "transpose", "retile": "vector", "interleave": "interleave", "interleave_cm": "transpose",
-             "nhwc2nchw": "transpose", "padtiles": "staged", "shard_pack": "transpose"}
+             "nhwc2nchw": "transpose", "padtiles": "staged", "shard_pack": "transpose",
+             "rgb_nhwc2nchw": "deinterleave"}
 
 
 @pytest.mark.slow
@@ -759,6 +761,50 @@ def test_interleave_variants(dev, env_knob, narrow):
             assert p["store_policy"] == (0 if nt == "0" else 18 if (sc1 == "1" and narrow) else 2), p
             say("interleave narrow", narrow, ts, "->", td, "eb", eb, "nt", nt, "sc1", sc1)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, nt, sc1)
+
+
+def _image(n, h, w, c):
+    hw = h * w
+    return f"({n},{h},{w},{c}):({hw * c},{w * c},{c},1)", f"({n},{h},{w},{c}):({hw * c},{w},1,{hw})"
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+def test_channel_shuffle(dev, env_knob, eb):
+    """Few-channel image layouts, NHWC <-> NCHW for every channel count the shuffle
+    kernels take (2..8 channels of at most 16 bytes), both access policies: a batch
+    mode, workgroups cut short at the end of each image, and the register interleave
+    replaced by the shuffle for power-of-two channel counts (LR_INARROW=2)."""
+    ran = 0
+    for c in range(2, 9):
+        if c * eb > 16:
+            continue
+        v = 16 // eb
+        # 3 images of 80 x (4 v) pixels, 320 blocks of v: two workgroups per image,
+        # the second holding 64 of its 256 blocks
+        n, h, w = 3, 80, 4 * v
+        nhwc, nchw = _image(n, h, w, c)
+        size = n * h * w * c
+        src = np.random.default_rng(c * 10 + eb).integers(0, 256, size * eb, dtype=np.uint8)
+        dst = np.full(size * eb, 0xA5, np.uint8)
+        for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
+            want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+            for nt in ("0", "1"):
+                for variant in ("default", "2"):
+                    env_knob.setenv("LR_NT", nt)
+                    if variant == "2":
+                        env_knob.setenv("LR_INARROW", "2")
+                    else:
+                        env_knob.delenv("LR_INARROW", raising=False)
+                    p = lr.copy_plan(ts, size, td, size, eb)
+                    assert p["path"] == path, (ts, td, eb, p["path"])
+                    shuffled = path == "deinterleave" or c & (c - 1) or variant == "2"
+                    if path == "interleave":
+                        assert (p["tile_a"] == 256 * v) == bool(shuffled), p
+                    say("channel shuffle", path, "eb", eb, "C", c, "nt", nt, "variant", variant)
+                    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, eb, nt, variant)
+                    ran += 1
+    env_knob.delenv("LR_INARROW", raising=False)
+    assert ran >= 8
 
 
 @pytest.mark.parametrize("vorder", [0, 1])

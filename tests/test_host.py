@@ -439,7 +439,7 @@ def test_common_vector_sound_and_tight_on_workloads():
             w = O.max_common_vector(O.parse(ts), Ld, eb)
             assert v <= w and w % v == 0, (ts, td, eb, v, w)
     for name, want in [("tile8x8", 1), ("transpose", 1), ("retile", 8), ("interleave", 1), ("interleave_cm", 1),
-                       ("nhwc2nchw", 1), ("padtiles", 1), ("shard_pack", 1)]:
+                       ("nhwc2nchw", 1), ("padtiles", 1), ("shard_pack", 1), ("rgb_nhwc2nchw", 1)]:
         w = W.small(name)
         v = lr.max_common_vector(w.src_layout, w.dst_layout, w.elem_bytes)
         assert v == want == O.max_common_vector(O.parse(w.src_layout), O.parse(w.dst_layout), w.elem_bytes)
@@ -449,7 +449,7 @@ def test_common_vector_sound_and_tight_on_workloads():
 
 EXPECTED_PATH = {"tile8x8": "alias", "transpose": "transpose", "retile": "vector", "interleave": "interleave",
                  "interleave_cm": "transpose", "nhwc2nchw": "transpose", "padtiles": "staged",
-                 "shard_pack": "transpose"}
+                 "shard_pack": "transpose", "rgb_nhwc2nchw": "deinterleave"}
 
 
 @pytest.mark.parametrize("name", list(W.FULL))
@@ -590,6 +590,35 @@ def test_plan_store_policy(monkeypatch):
     assert lr.copy_plan("4096:1", 4096, "4096:1", 4096, 4, lr.COPY_WIDE_INDEX)["store_policy"] == 2
     monkeypatch.setenv("LR_SC1", "0")
     assert plan("retile")["store_policy"] == 2
+
+
+def test_plan_few_channel_images(monkeypatch):
+    """NHWC <-> NCHW with 2..8 channels of at most 16 bytes: the channel shuffle (the
+    de-interleave one way; the interleave, through LDS unless the channel count is a
+    power of two, the other).  Pixel counts that are not a multiple of one 16-byte
+    chunk, and swizzles, keep the general kernels."""
+    monkeypatch.delenv("LR_INARROW", raising=False)
+
+    def image(n, h, w, c):
+        hw = h * w
+        return f"({n},{h},{w},{c}):({hw * c},{w * c},{c},1)", f"({n},{h},{w},{c}):({hw * c},{w},1,{hw})"
+
+    for eb in (1, 2, 4, 8):
+        for c in range(2, 9):
+            nhwc, nchw = image(8, 32, 32, c)
+            size = 8 * 32 * 32 * c
+            p, q = lr.copy_plan(nhwc, size, nchw, size, eb), lr.copy_plan(nchw, size, nhwc, size, eb)
+            if c * eb <= 16:
+                assert p["path"] == "deinterleave" and p["tile_a"] == 256 * 16 // eb and p["tile_b"] == c, (eb, c, p)
+                assert q["path"] == "interleave", (eb, c, q)
+                assert (q["tile_a"] == 256 * 16 // eb) == bool(c & (c - 1)), (eb, c, q)
+            else:
+                assert p["path"] != "deinterleave"
+    nhwc, nchw = image(3, 7, 9, 3)  # 63 pixels: no whole 16-byte chunks per plane
+    assert lr.copy_plan(nhwc, 567, nchw, 567, 2)["path"] == "generic"
+    assert lr.copy_plan("Sw<1,3,4> o (64,3):(3,1)", 192, "(64,3):(1,64)", 192, 2)["path"] != "deinterleave"
+    with pytest.raises(lr.LayoutRemapError):
+        lr.copy_plan("(8,8):(1,8)", 64, "(8,8):(1,8)", 64, 2, lr.COPY_FORCE_PATH(lr.PATH_DEINTERLEAVE))
 
 
 def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):

@@ -392,11 +392,12 @@ JOINT_FULL = {
     "tile8x8": [(8, 1, 1), (8, 8, 8)],  # dst (8,8) refinement, aliased: not used
     # block j's columns follow block j-1's in the destination: one rectangular transpose
     "shard_pack": [(1024, 8192, 1), (8192, 1, 1024)],
+    "rgb_nhwc2nchw": [(50176, 3, 1), (3, 1, 50176), (512, 150528, 150528)],
 }
 
 
 @pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles",
-                                  "shard_pack"])
+                                  "shard_pack", "rgb_nhwc2nchw"])
 def test_joint_flat_of_workloads(name):
     w = W.full(name)
     got = O.joint_flat(O.parse(w.src_layout), O.parse(w.dst_layout), sort_by_dst=True)
@@ -615,6 +616,7 @@ def test_forms_equal_oracle_copy():
         "nhwc2nchw": lambda s: F.nhwc2nchw(s, 3, 7, 9, 40),
         "padtiles": lambda s: F.padtiles(s, 1000),
         "shard_pack": lambda s: F.shard_pack(s, 520, 2112, 8),
+        "rgb_nhwc2nchw": lambda s: F.nhwc2nchw(s, 3, 17, 40, 3),
     }
     for name, form in cases.items():
         w = W.small(name)

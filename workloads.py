@@ -18,6 +18,8 @@ The workloads (names follow the sizes they carry):
 * ``nhwc2nchw``   fp16 NHWC (128,56,56,256) -> NCHW.
 * ``padtiles``    2**20 padded 8x8 fp32 tiles, source (8,8):(1,9) per tile read in
                   thread-value order ((4,8),2):((16,1),8), destination compact.
+* ``rgb_nhwc2nchw`` fp16 NHWC (512,224,224,3) -> NCHW: three colour channels, so no
+                  channel run reaches 16 bytes (the de-interleave).
 * ``shard_pack``  the local pack of a transpose sharded by rows over 8 GPUs: one GPU's
                   1024 x 8192 fp16 row block -> 8 contiguous 1024 x 1024 blocks, block j
                   holding columns [1024 j, 1024 j + 1024) transposed (what GPU j receives).
@@ -187,6 +189,13 @@ def padtiles(tiles: int = 1 << 20) -> Workload:
         n_elems=64 * tiles)
 
 
+def rgb_nhwc2nchw(n: int = 512, h: int = 224, w: int = 224, c: int = 3) -> Workload:
+    wl = nhwc2nchw(n, h, w, c)
+    wl.name = f"rgb_nhwc2nchw{n}x{h}x{w}x{c}"
+    wl.seed = 9
+    return wl
+
+
 def shard_pack(rows: int = 1024, cols: int = 8192, parts: int = 8) -> Workload:
     # logical (r, c, j) with column j*w + c of the row block, w = cols / parts; block j
     # of the destination is contiguous, column-major over (r, c)
@@ -207,6 +216,7 @@ FULL = {
     "nhwc2nchw": nhwc2nchw,
     "padtiles": padtiles,
     "shard_pack": shard_pack,
+    "rgb_nhwc2nchw": rgb_nhwc2nchw,
 }
 
 
@@ -221,6 +231,7 @@ def small(name: str) -> Workload:
         "nhwc2nchw": lambda: nhwc2nchw(3, 7, 9, 40),
         "padtiles": lambda: padtiles(1000),
         "shard_pack": lambda: shard_pack(520, 2112, 8),
+        "rgb_nhwc2nchw": lambda: rgb_nhwc2nchw(3, 17, 40, 3),
     }[name]()
 
 

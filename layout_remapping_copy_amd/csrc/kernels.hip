@@ -262,7 +262,19 @@ __global__ void __launch_bounds__(256) k_eval_coords(EvalArgs a) {
       for (int m = 0; m < a.nmodes; ++m) {
         int64_t x = c[m];
         ok = ok && x >= 0 && x < a.mode_size[m];
-        if (ok) off += eval_leaves(a, lo, a.mode_end[m], x);
+        if (ok) {
+          if (a.s32) {  // 32-bit digits when every offset fits 31 bits
+            uint32_t r = (uint32_t)x, o = 0;
+            for (int i = lo; i < a.mode_end[m]; ++i) {
+              const uint32_t q = (i == a.mode_end[m] - 1) ? 0u : fdiv(r, a.fd[i]);
+              o += (r - q * (uint32_t)a.shape[i]) * (uint32_t)a.stride[i];
+              r = q;
+            }
+            off += o;
+          } else {
+            off += eval_leaves(a, lo, a.mode_end[m], x);
+          }
+        }
         lo = a.mode_end[m];
       }
     }

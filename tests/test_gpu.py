@@ -109,6 +109,33 @@ def test_eval_coords(dev):
     assert lr.layout_eval_coords("Sw<3,0,3> o (8,8):(8,1)", sw).cpu().tolist() == [18, 19]
 
 
+def test_eval_coords_random(dev):
+    """Per-mode coordinates of random nested layouts (32-bit and 64-bit offset
+    ranges), in range and out of range, against the oracle."""
+    rng = random.Random(37)
+    for i in range(60):
+        nm = rng.randint(1, 4)
+        modes = []
+        for _ in range(nm):
+            nl = rng.randint(1, 3)
+            ext = [rng.randint(1, 6) for _ in range(nl)]
+            big = i % 3 == 0
+            st = [rng.randint(0, 40) * (1 << 29 if big else 1) for _ in range(nl)]
+            if nl == 1:
+                modes.append((f"{ext[0]}", f"{st[0]}"))
+            else:
+                modes.append(("(" + ",".join(map(str, ext)) + ")", "(" + ",".join(map(str, st)) + ")"))
+        t = "(" + ",".join(m[0] for m in modes) + "):(" + ",".join(m[1] for m in modes) + ")"
+        L = O.parse(t)
+        sizes = [O.size(O.parse(f"{m[0]}:{m[1]}")) for m in modes]
+        rows = [tuple(rng.randint(0, sz - 1) for sz in sizes) for _ in range(40)]
+        rows += [tuple(sz if j == 0 else 0 for j, sz in enumerate(sizes)), tuple(-1 for _ in sizes)]
+        ct = torch.tensor(rows, dtype=torch.int64, device=dev)
+        got = lr.layout_eval_coords(t, ct).cpu().tolist()
+        want = [O.eval_coord(L, r) for r in rows[:-2]] + [-1, -1]
+        assert got == want, (t, rows[:3])
+
+
 def _rand_text(rng, swz=True, max_leaves=5):
     nl = rng.randint(1, max_leaves)
     ext = [rng.randint(1, 7) for _ in range(nl)]

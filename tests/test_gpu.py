@@ -330,7 +330,8 @@ def test_copy_random_pairs(dev, monkeypatch):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
                "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 4)),
-               "LR_TEL": rng.choice(["0", "1", "2"]), "LR_SC1": rng.choice("01")}
+               "LR_TEL": rng.choice(["0", "1", "2"]), "LR_SC1": rng.choice("01"),
+               "LR_INARROW": rng.choice(["0", "1", "2"])}
         for k, v in env.items():
             monkeypatch.setenv(k, v)
         if i % 50 == 0:

@@ -1016,6 +1016,11 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
   const bool mine = l < nblk;
 
   if constexpr (!INTERLEAVE) {
+    // LDS slot of chunk q.  Lane l reads chunks l*C + j: for C odd a 16-lane phase
+    // touches 16 distinct chunk slots mod 16 (all 64 banks once); for C = 2, 4, 8 the
+    // XOR of bits 4-7 into bits 0-3 (Sw<4,0,4> on chunk indices, [print_layout page,
+    // section 4.3]) spreads them the same way, where plain slots would collide C-fold.
+    auto slot = [](uint32_t q) { return (C & (C - 1)) == 0 ? q ^ ((q >> 4) & 15u) : q; };
     const char* sb = src + (size_t)(p0 * C + bs) * EB;  // interleaved block: nblk * C chunks
     Ch tmp[C];
 #pragma unroll
@@ -1023,12 +1028,12 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
       if (l + 256u * j < nblk * C) tmp[j] = gload<NT, Ch>(sb + (size_t)(l + 256u * j) * 16);
 #pragma unroll
     for (int j = 0; j < C; ++j)
-      if (l + 256u * j < nblk * C) lds[l + 256u * j] = tmp[j];
+      if (l + 256u * j < nblk * C) lds[slot(l + 256u * j)] = tmp[j];
     __syncthreads();
     if (!mine) return;
     Ch in[C], out[C];
 #pragma unroll
-    for (int j = 0; j < C; ++j) in[j] = lds[l * C + j];
+    for (int j = 0; j < C; ++j) in[j] = lds[slot(l * C + j)];
 #pragma unroll
     for (int e = 0; e < C * V; ++e) out[e % C].e[e / C] = in[e / V].e[e % V];  // element e: pixel e / C, channel e % C
 #pragma unroll

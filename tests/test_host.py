@@ -376,6 +376,20 @@ def test_direct_load_transpose_lds_reads_conflict_free(ta, tb):
         assert len(slots) == tb * V * ta
 
 
+def test_channel_shuffle_lds_reads():
+    """The de-interleave's lanes read LDS chunks l*C + j (16 bytes each): with C odd
+    the plain slots are conflict-free under the gfx950 model, with C = 2, 4, 8 the
+    kernel's Sw<4,0,4> on chunk slots makes them so, and its consecutive-chunk
+    writes stay conflict-free.  C = 6 keeps a two-way conflict."""
+    for c in (3, 5, 7):
+        assert lr.access_check(f"64:{c}", 16, 64, "read")["conflict_cycles"] == 0, c
+    for c in (2, 4, 8):
+        assert lr.access_check(f"64:{c}", 16, 64, "read")["conflict_cycles"] > 0, c
+        assert lr.access_check(f"Sw<4,0,4> o 64:{c}", 16, 64, "read")["conflict_cycles"] == 0, c
+    assert lr.access_check("Sw<4,0,4> o 64:1", 16, 64, "write")["conflict_cycles"] == 0
+    assert lr.access_check("64:6", 16, 64, "read")["conflict_cycles"] == 4
+
+
 def test_fast_paths_touch_the_fewest_lines():
     """Per wave instruction, in 16-byte chunks (print_layout page, section 6.4: adjacent
     lanes on adjacent addresses).  Transpose (fp16 8192^2, 32 x 32 chunks, V = 8):

@@ -491,14 +491,21 @@ def test_copy_beyond_2_31_elements(dev):
         del src, got
 
 
-def test_copies_replay_in_a_hip_graph(dev):
+@pytest.mark.parametrize("nt", ["0", "1"])
+def test_copies_replay_in_a_hip_graph(dev, monkeypatch, nt):
     """lr_layout_copy allocates nothing and records no memset, so captured copies
-    (five paths in one graph) replay correctly; each replay is checked after eager
-    work has changed the sources."""
+    (seven paths in one graph, with plain or streaming accesses, the latter with the
+    sc1 buffer stores) replay correctly; each replay is checked after eager work has
+    changed the sources."""
+    monkeypatch.setenv("LR_NT", nt)
     cases = []
-    for name in ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles"):
+    for name in ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles", "rgb_nhwc2nchw"):
         w = W.small(name)
         cases.append((w.src_layout, w.dst_layout, w.src_elems, w.dst_elems, w.elem_bytes))
+    rgb = W.small("rgb_nhwc2nchw")  # and back: the channel-shuffle interleave
+    cases.append((rgb.dst_layout, rgb.src_layout, rgb.dst_elems, rgb.src_elems, rgb.elem_bytes))
+    paths = {lr.copy_plan(ts, ns, td, nd, eb)["path"] for ts, td, ns, nd, eb in cases}
+    assert {"transpose", "vector", "interleave", "staged", "deinterleave"} <= paths, paths
     s_list, d_list, plans = [], [], []
     for ts, td, ns, nd, eb in cases:
         s_list.append(torch.zeros(ns * eb, dtype=torch.uint8, device=dev))

@@ -1056,6 +1056,75 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
   }
 }
 
+// Element-granular form of the channel shuffle, for pixel counts, plane strides or
+// batch offsets that leave the planes without aligned 16-byte chunks (a 299 x 299
+// image, say): the same exchange through LDS, with single-element accesses on both
+// sides (consecutive lanes take consecutive elements, so a wave instruction still
+// covers consecutive bytes).  A workgroup holds KP pixels per lane (256 KP pixels,
+// at most 32 KiB of LDS).
+template <int EB, int C, bool INTERLEAVE, bool NT>
+__global__ void __launch_bounds__(256) k_chan_el(ChanArgs t) {
+  using T = typename Raw<EB>::T;
+  constexpr int PT = chan_el_pixels(EB, C);  // pixels per workgroup
+  constexpr int KP = PT / 256;               // pixels per lane
+  constexpr int N = KP * C;                  // elements per lane on each side
+  constexpr int BATCH = N < 8 ? N : 8;      // loads in flight per lane
+  __shared__ T lds[PT * C];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  const uint32_t blk = blockIdx.x;
+  const uint32_t r = fdiv(blk, t.fd_tiles);
+  const uint32_t tile = blk - r * t.tiles;
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r, &bs, &bd);
+  const uint32_t p0 = tile * PT;
+  const uint32_t left = t.pixels - p0;
+  const uint32_t np = left < (uint32_t)PT ? left : (uint32_t)PT;  // pixels in this workgroup
+  const uint32_t l = threadIdx.x;
+  // element i of this lane: interleaved index e = l + 256 i (pixel e / C, channel
+  // e % C); planar index: channel i / KP, pixel l + 256 (i % KP)
+  const char* s_il = src + (size_t)(p0 * C + bs) * EB;
+  char* d_il = dst + (size_t)(p0 * C + bd) * EB;
+#pragma unroll
+  for (int i0 = 0; i0 < N; i0 += BATCH) {
+    T v[BATCH] = {};
+#pragma unroll
+    for (int i = 0; i < BATCH && i0 + i < N; ++i) {
+      const int k = i0 + i;
+      if constexpr (!INTERLEAVE) {
+        const uint32_t e = l + 256u * k;
+        if (e < np * C) v[i] = gload<NT, T>(s_il + (size_t)e * EB);
+      } else {
+        const uint32_t c = k / KP, p = l + 256u * (k % KP);
+        if (p < np) v[i] = gload<NT, T>(src + (size_t)(c * t.plane + p0 + p + bs) * EB);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH && i0 + i < N; ++i) {
+      const int k = i0 + i;
+      if constexpr (!INTERLEAVE) {
+        const uint32_t e = l + 256u * k;
+        if (e < np * C) lds[e] = v[i];
+      } else {
+        const uint32_t c = k / KP, p = l + 256u * (k % KP);
+        if (p < np) lds[p * C + c] = v[i];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    if constexpr (!INTERLEAVE) {
+      const uint32_t c = k / KP, p = l + 256u * (k % KP);
+      if (p < np) gstore<NT, T>(dst + (size_t)(c * t.plane + p0 + p + bd) * EB, lds[p * C + c]);
+    } else {
+      const uint32_t e = l + 256u * k;
+      if (e < np * C) gstore<NT, T>(d_il + (size_t)e * EB, lds[e]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ staged footprint gather
 
 struct StagedArgs {
@@ -1329,33 +1398,36 @@ static bool launch_interleave_n(const InterleaveArgs& a, int nb, unsigned grid, 
 }
 
 template <int EB, int CC, bool INTERLEAVE, bool NT>
-static bool launch_chan_one(const ChanArgs& a, unsigned grid, hipStream_t st) {
+static bool launch_chan_one(const ChanArgs& a, bool elem, unsigned grid, hipStream_t st) {
   if constexpr (chan_supported(EB, CC)) {
-    hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
+    if (elem)
+      hipLaunchKernelGGL((k_chan_el<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
     return true;
   }
   return false;
 }
 
 template <int EB, bool INTERLEAVE, bool NT>
-static bool launch_chan_c(const ChanArgs& a, int c, unsigned grid, hipStream_t st) {
+static bool launch_chan_c(const ChanArgs& a, int c, bool elem, unsigned grid, hipStream_t st) {
   switch (c) {
-    case 2: return launch_chan_one<EB, 2, INTERLEAVE, NT>(a, grid, st);
-    case 3: return launch_chan_one<EB, 3, INTERLEAVE, NT>(a, grid, st);
-    case 4: return launch_chan_one<EB, 4, INTERLEAVE, NT>(a, grid, st);
-    case 5: return launch_chan_one<EB, 5, INTERLEAVE, NT>(a, grid, st);
-    case 6: return launch_chan_one<EB, 6, INTERLEAVE, NT>(a, grid, st);
-    case 7: return launch_chan_one<EB, 7, INTERLEAVE, NT>(a, grid, st);
-    case 8: return launch_chan_one<EB, 8, INTERLEAVE, NT>(a, grid, st);
+    case 2: return launch_chan_one<EB, 2, INTERLEAVE, NT>(a, elem, grid, st);
+    case 3: return launch_chan_one<EB, 3, INTERLEAVE, NT>(a, elem, grid, st);
+    case 4: return launch_chan_one<EB, 4, INTERLEAVE, NT>(a, elem, grid, st);
+    case 5: return launch_chan_one<EB, 5, INTERLEAVE, NT>(a, elem, grid, st);
+    case 6: return launch_chan_one<EB, 6, INTERLEAVE, NT>(a, elem, grid, st);
+    case 7: return launch_chan_one<EB, 7, INTERLEAVE, NT>(a, elem, grid, st);
+    case 8: return launch_chan_one<EB, 8, INTERLEAVE, NT>(a, elem, grid, st);
     default: return false;
   }
 }
 
 template <int EB>
-static bool launch_chan(const ChanArgs& a, int c, bool interleave, bool nt, unsigned grid, hipStream_t st) {
+static bool launch_chan(const ChanArgs& a, int c, bool interleave, bool elem, bool nt, unsigned grid, hipStream_t st) {
   if (interleave)
-    return nt ? launch_chan_c<EB, true, true>(a, c, grid, st) : launch_chan_c<EB, true, false>(a, c, grid, st);
-  return nt ? launch_chan_c<EB, false, true>(a, c, grid, st) : launch_chan_c<EB, false, false>(a, c, grid, st);
+    return nt ? launch_chan_c<EB, true, true>(a, c, elem, grid, st) : launch_chan_c<EB, true, false>(a, c, elem, grid, st);
+  return nt ? launch_chan_c<EB, false, true>(a, c, elem, grid, st) : launch_chan_c<EB, false, false>(a, c, elem, grid, st);
 }
 
 template <int EB>
@@ -1492,7 +1564,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
     }
     case LR_PATH_DEINTERLEAVE:
     case LR_PATH_INTERLEAVE:
-      if (p.path == LR_PATH_DEINTERLEAVE || p.inarrow == 2) {
+      if (p.path == LR_PATH_DEINTERLEAVE || p.inarrow >= 2) {
         // channel shuffle: the pixel mode is the one contiguous on the planar side
         const bool il = p.path == LR_PATH_INTERLEAVE;
         const int pm = il ? p.a : p.b, cm = il ? p.b : p.a;
@@ -1507,7 +1579,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         fill_batch(&a.batch, p, p.a, p.b);
         a.bufst = p.bufst ? 1u : 0u;
         bool ok = false;
-        LR_DISPATCH_EB(p.eb, ok = launch_chan<EBV>(a, (int)p.m[cm].ext, il, p.nt, grid, st));
+        // one element per lane unit (v == 1): the element-granular form
+        LR_DISPATCH_EB(p.eb, ok = launch_chan<EBV>(a, (int)p.m[cm].ext, il, p.v == 1, p.nt, grid, st));
         if (!ok) return LR_ERR_PATH;
         return check_launch();
       }

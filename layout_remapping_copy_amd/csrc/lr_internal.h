@@ -91,12 +91,19 @@ struct Plan {
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB
   int inarrow;        // interleave: 1 = one 16-byte store per lane from NB narrow loads,
-                      // 0 = NB wide loads and stores per lane, 2 = channel shuffle through LDS
+                      // 0 = NB wide loads and stores per lane, 2 = channel shuffle through LDS,
+                      // 3 = its element-granular form
 };
 
 // Channel-shuffle kernels (pixels with C interleaved channels <-> C planes) exist
 // for 2..8 channels of one 16-byte chunk or less per pixel.
 constexpr bool chan_supported(int eb, int64_t c) { return c >= 2 && c <= 8 && c * eb <= 16; }
+
+// Pixels per workgroup of the element-granular channel shuffle: 256 lanes of 1 to
+// 16 pixels each, the workgroup's pixels of all channels in at most 32 KiB of LDS.
+constexpr int chan_el_pixels(int eb, int c) {
+  return 256 * (128 / (c * eb) < 1 ? 1 : (128 / (c * eb) > 16 ? 16 : 128 / (c * eb)));
+}
 
 // Plans a copy; fills `p`.  Returns 0 or an lr_status.
 int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld,

@@ -610,7 +610,7 @@ def test_plan_few_channel_images(monkeypatch):
     """NHWC <-> NCHW with 2..8 channels of at most 16 bytes: the channel shuffle (the
     de-interleave one way; the interleave, through LDS unless the channel count is a
     power of two, the other).  Pixel counts that are not a multiple of one 16-byte
-    chunk, and swizzles, keep the general kernels."""
+    chunk take its element-granular form; swizzles keep the general kernels."""
     monkeypatch.delenv("LR_INARROW", raising=False)
 
     def image(n, h, w, c):
@@ -628,8 +628,18 @@ def test_plan_few_channel_images(monkeypatch):
                 assert (q["tile_a"] == 256 * 16 // eb) == bool(c & (c - 1)), (eb, c, q)
             else:
                 assert p["path"] != "deinterleave"
-    nhwc, nchw = image(3, 7, 9, 3)  # 63 pixels: no whole 16-byte chunks per plane
+    # 323 pixels: no whole 16-byte chunks per plane, so the element-granular form
+    nhwc, nchw = image(3, 17, 19, 3)
+    for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
+        p = lr.copy_plan(ts, 2907, td, 2907, 2)
+        assert p["path"] == path and p["vec_elems"] == 1 and p["tile_a"] == 256 * 16, p  # 16 pixels per lane
+    # under one pixel per lane (63 pixels) it is not worth a workgroup of 4096
+    nhwc, nchw = image(3, 7, 9, 3)
     assert lr.copy_plan(nhwc, 567, nchw, 567, 2)["path"] == "generic"
+    # nor does it take layouts a better kernel handles (the padded tiles look like
+    # eight pixels of four channels)
+    w = W.full("padtiles")
+    assert lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 4)["path"] == "staged"
     assert lr.copy_plan("Sw<1,3,4> o (64,3):(3,1)", 192, "(64,3):(1,64)", 192, 2)["path"] != "deinterleave"
     with pytest.raises(lr.LayoutRemapError):
         lr.copy_plan("(8,8):(1,8)", 64, "(8,8):(1,8)", 64, 2, lr.COPY_FORCE_PATH(lr.PATH_DEINTERLEAVE))

@@ -450,6 +450,17 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         p->tshape = ext_a > 16 * V ? 3 : 2;
       else
         p->tshape = (V == 2 && ext_a > 16 * V) ? 1 : 0;
+      // Fewer tiles than compute units (a 16 MiB transpose in 256 x 256 tiles is 128
+      // workgroups): 32 x 8 chunks, four times as many workgroups.  Measured on
+      // fp16 1024 x 8192 and 8192 x 1024, the 8-way shard pack of 1024 x 8192 and u8
+      // 4096^2: +2 to +8 % (16 MiB copies run near a plain copy's 3.2-3.6 TB/s).
+      if (wide_ok && !block_rows) {
+        int64_t tiles = ((ext_a + kTileTA[p->tshape] * V - 1) / (kTileTA[p->tshape] * V)) *
+                        ((ext_b + kTileTB[p->tshape] * V - 1) / (kTileTB[p->tshape] * V));
+        for (int k = 0; k < p->rank; ++k)
+          if (k != a && k != b && k != b2) tiles *= p->m[k].ext;
+        if (tiles < 256) p->tshape = 4;
+      }
       const uint32_t shp = env_u32("LR_TSHAPE", 99);
       if (shp < (uint32_t)kTileShapes) p->tshape = wide_ok ? (int)shp : 0;
       // 16-element chunks (1-byte elements): the 32 x 32 and 64 x 16 tiles would

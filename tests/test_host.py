@@ -530,6 +530,17 @@ def test_plan_streaming_default_and_tile_shapes(monkeypatch):
         p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
         assert p["path"] == "transpose" and p["streaming"]
         assert (p["tile_a"], p["tile_b"], p["block"]) == (ta, tb, block), name
+    # fewer 32 x 32-chunk tiles than compute units: 32 x 8 chunks (the shard pack:
+    # 128 -> 512 workgroups); 4096^2 fp16 fills the 256 units and keeps 32 x 32
+    w = W.full("shard_pack")
+    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
+    assert (p["tile_a"], p["tile_b"], p["block"], p["grid"]) == (256, 64, 256, 512), p
+    p = lr.copy_plan("(1024,8192):(8192,1)", 1 << 23, "(1024,8192):(1,1024)", 1 << 23, 2)
+    assert (p["tile_a"], p["tile_b"], p["grid"]) == (256, 64, 512), p
+    p = lr.copy_plan("(4096,4096):(4096,1)", 1 << 24, "(4096,4096):(1,4096)", 1 << 24, 2)
+    assert (p["tile_a"], p["tile_b"], p["grid"]) == (256, 256, 256), p
+    p = lr.copy_plan("(4096,4096):(4096,1)", 1 << 24, "(4096,4096):(1,4096)", 1 << 24, 1)
+    assert (p["tile_a"], p["tile_b"], p["grid"]) == (512, 128, 256), p
 
 
 def test_plan_workgroup_order(monkeypatch):

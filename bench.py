@@ -246,6 +246,12 @@ def main():
     cold = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, flags)
     warm = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, flags, rotate=False)
 
+    # the library's own contiguous copy (16 bytes per lane) of equal bytes on the same
+    # rotating buffers: what a copy without any remapping reaches at this size here
+    n16 = bytes_step // 2 // 16
+    _, copy_ms = _time_copies(lr, torch, pairs, f"{n16}:1", f"{n16}:1", 16, args.steps, args.warmup)
+    copy_kernel = bytes_step / (copy_ms * 1e-3) / 1e9
+
     # same-box device-to-device copy of equal bytes, for context
     a, b = pairs[0][0], pairs[1][1]
     for _ in range(3):
@@ -282,6 +288,8 @@ def main():
             "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
             "d2d_copy_GBps": round(d2d, 1),
             "frac_of_d2d_copy": round(value / d2d, 4),
+            "copy_kernel_GBps": round(copy_kernel, 1),
+            "kernel_frac_of_copy_kernel": round(achieved / copy_kernel, 4),
             "buffers": "rotating pairs, >= 1 GiB in total",
             "kernel_us": {"median": round(cold[len(cold) // 2], 2), "best": round(cold[0], 2),
                           "warm_median": round(warm[len(warm) // 2], 2), "warm_best": round(warm[0], 2),

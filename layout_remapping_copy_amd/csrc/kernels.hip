@@ -1056,20 +1056,52 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
   }
 }
 
-// Element-granular form of the channel shuffle, for pixel counts, plane strides or
+// Element-granular form of the same exchange, for pixel counts, plane strides or
 // batch offsets that leave the planes without aligned 16-byte chunks (a 299 x 299
-// image, say): the same exchange through LDS, with single-element accesses on both
-// sides (consecutive lanes take consecutive elements, so a wave instruction still
-// covers consecutive bytes).  A workgroup holds KP pixels per lane (256 KP pixels,
-// at most 32 KiB of LDS).
+// image, say), still with 16-byte accesses wherever a range allows them (element-
+// aligned pointers).  A workgroup's pixels are one contiguous byte range on the interleaved side
+// and one range per channel on the planar side, in general none of them 16-byte
+// aligned.  LDS holds the workgroup's pixels as an interleaved image placed at the
+// interleaved range's address modulo 16, so that range moves as its aligned interior
+// in 16-byte chunks plus single elements at its two ends.  Each planar range moves the
+// same way in global memory; its chunks are scattered into (INTERLEAVE) or gathered
+// from (de-interleave) the image element by element, at a stride of C elements.  For
+// even C that stride would put the lanes of a wave on few LDS banks: the image then
+// has one 16-byte pad slot after every 32 (512 bytes), which spreads them.
+template <int C>
+__device__ __forceinline__ uint32_t win_pos(uint32_t x) {
+  if constexpr ((C & 1) == 0) return x + ((x >> 9) << 4);
+  return x;
+}
+
+// Head, interior and tail of the EB-aligned byte range [g, g + len): `head` single
+// elements up to the first 16-byte boundary, `nint` whole chunks from `a0` bytes
+// into the range, `tail` single elements after them.  A range without a whole chunk
+// is all head.
+template <int EB>
+struct WinSplit {
+  uint32_t head, nint, tail, a0, a1;
+  __device__ __forceinline__ WinSplit(const void* g, uint32_t len) {
+    const uint32_t mis = (uint32_t)((uintptr_t)g & 15u);
+    const uint32_t first = (16u - mis) & 15u;                // bytes to the first boundary
+    const bool inner = len >= first + 16u;
+    a0 = inner ? first : len;
+    nint = inner ? (len - first) >> 4 : 0u;
+    a1 = a0 + 16u * nint;
+    head = a0 / EB;
+    tail = (len - a1) / EB;
+  }
+};
+
 template <int EB, int C, bool INTERLEAVE, bool NT>
-__global__ void __launch_bounds__(256) k_chan_el(ChanArgs t) {
+__global__ void __launch_bounds__(256) k_chan_win(ChanArgs t) {
   using T = typename Raw<EB>::T;
-  constexpr int PT = chan_el_pixels(EB, C);  // pixels per workgroup
-  constexpr int KP = PT / 256;               // pixels per lane
-  constexpr int N = KP * C;                  // elements per lane on each side
-  constexpr int BATCH = N < 8 ? N : 8;      // loads in flight per lane
-  __shared__ T lds[PT * C];
+  constexpr uint32_t V = 16 / EB;
+  using Ch = Chunk<T, V>;
+  constexpr uint32_t PT = 256 * V;                       // pixels per workgroup
+  constexpr uint32_t IMG = PT * C * EB + 16;             // image bytes (+ alignment)
+  constexpr uint32_t LB = (C & 1) ? IMG : IMG + ((IMG >> 9) + 1) * 16;
+  __shared__ __align__(16) unsigned char lds[LB];
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
@@ -1080,47 +1112,86 @@ __global__ void __launch_bounds__(256) k_chan_el(ChanArgs t) {
   batch_offsets(t.batch, r, &bs, &bd);
   const uint32_t p0 = tile * PT;
   const uint32_t left = t.pixels - p0;
-  const uint32_t np = left < (uint32_t)PT ? left : (uint32_t)PT;  // pixels in this workgroup
+  const uint32_t np = left < PT ? left : PT;  // pixels in this workgroup
   const uint32_t l = threadIdx.x;
-  // element i of this lane: interleaved index e = l + 256 i (pixel e / C, channel
-  // e % C); planar index: channel i / KP, pixel l + 256 (i % KP)
-  const char* s_il = src + (size_t)(p0 * C + bs) * EB;
-  char* d_il = dst + (size_t)(p0 * C + bd) * EB;
+
+  // the interleaved range and its place in the image: image byte m + (p C + c) EB
+  // holds pixel p, channel c
+  const char* gi = INTERLEAVE ? dst + (size_t)(p0 * C + bd) * EB : src + (size_t)(p0 * C + bs) * EB;
+  const uint32_t m = (uint32_t)((uintptr_t)gi & 15u);
+  const uint32_t ilen = np * C * EB;
+  const WinSplit<EB> wi(gi, ilen);
+
+  if constexpr (!INTERLEAVE) {
+    // interleaved range -> image
+    Ch v[C];
 #pragma unroll
-  for (int i0 = 0; i0 < N; i0 += BATCH) {
-    T v[BATCH] = {};
+    for (uint32_t j = 0; j < (uint32_t)C; ++j)
+      if (l + 256u * j < wi.nint) v[j] = gload<NT, Ch>(gi + wi.a0 + 16u * (l + 256u * j));
+    T e{};
+    const bool edge = l < wi.head + wi.tail;
+    const uint32_t eo = l < wi.head ? l * EB : wi.a1 + (l - wi.head) * EB;  // byte in the range
+    if (edge) e = gload<NT, T>(gi + eo);
 #pragma unroll
-    for (int i = 0; i < BATCH && i0 + i < N; ++i) {
-      const int k = i0 + i;
-      if constexpr (!INTERLEAVE) {
-        const uint32_t e = l + 256u * k;
-        if (e < np * C) v[i] = gload<NT, T>(s_il + (size_t)e * EB);
-      } else {
-        const uint32_t c = k / KP, p = l + 256u * (k % KP);
-        if (p < np) v[i] = gload<NT, T>(src + (size_t)(c * t.plane + p0 + p + bs) * EB);
+    for (uint32_t j = 0; j < (uint32_t)C; ++j)
+      if (l + 256u * j < wi.nint) *(Ch*)(lds + win_pos<C>(m + wi.a0 + 16u * (l + 256u * j))) = v[j];
+    if (edge) *(T*)(lds + win_pos<C>(m + eo)) = e;
+    __syncthreads();
+    // image -> planar ranges: chunk l of each channel, gathered at a stride of C
+#pragma unroll
+    for (uint32_t c = 0; c < (uint32_t)C; ++c) {
+      char* gp = dst + (size_t)(c * t.plane + p0 + bd) * EB;
+      const WinSplit<EB> wp(gp, np * EB);
+      if (l < wp.nint) {
+        const uint32_t x = m + ((wp.head + V * l) * C + c) * EB;  // image byte of its first element
+        Ch o;
+#pragma unroll
+        for (uint32_t k = 0; k < V; ++k) o.e[k] = *(const T*)(lds + win_pos<C>(x + k * C * EB));
+        gstore<NT, Ch>(gp + wp.a0 + 16u * l, o);
+      }
+      if (l < wp.head + wp.tail) {
+        const uint32_t px = l < wp.head ? l : wp.head + V * wp.nint + (l - wp.head);
+        gstore<NT, T>(gp + (size_t)px * EB, *(const T*)(lds + win_pos<C>(m + (px * C + c) * EB)));
+      }
+    }
+  } else {
+    // planar ranges -> image: chunk l of each channel scattered at a stride of C
+    Ch v[C];
+    T e[C];
+#pragma unroll
+    for (uint32_t c = 0; c < (uint32_t)C; ++c) {
+      const char* gp = src + (size_t)(c * t.plane + p0 + bs) * EB;
+      const WinSplit<EB> wp(gp, np * EB);
+      if (l < wp.nint) v[c] = gload<NT, Ch>(gp + wp.a0 + 16u * l);
+      if (l < wp.head + wp.tail) {
+        const uint32_t px = l < wp.head ? l : wp.head + V * wp.nint + (l - wp.head);
+        e[c] = gload<NT, T>(gp + (size_t)px * EB);
       }
     }
 #pragma unroll
-    for (int i = 0; i < BATCH && i0 + i < N; ++i) {
-      const int k = i0 + i;
-      if constexpr (!INTERLEAVE) {
-        const uint32_t e = l + 256u * k;
-        if (e < np * C) lds[e] = v[i];
-      } else {
-        const uint32_t c = k / KP, p = l + 256u * (k % KP);
-        if (p < np) lds[p * C + c] = v[i];
+    for (uint32_t c = 0; c < (uint32_t)C; ++c) {
+      const char* gp = src + (size_t)(c * t.plane + p0 + bs) * EB;
+      const WinSplit<EB> wp(gp, np * EB);
+      if (l < wp.nint) {
+        const uint32_t x = m + ((wp.head + V * l) * C + c) * EB;
+#pragma unroll
+        for (uint32_t k = 0; k < V; ++k) *(T*)(lds + win_pos<C>(x + k * C * EB)) = v[c].e[k];
+      }
+      if (l < wp.head + wp.tail) {
+        const uint32_t px = l < wp.head ? l : wp.head + V * wp.nint + (l - wp.head);
+        *(T*)(lds + win_pos<C>(m + (px * C + c) * EB)) = e[c];
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
+    // image -> interleaved range
 #pragma unroll
-  for (int k = 0; k < N; ++k) {
-    if constexpr (!INTERLEAVE) {
-      const uint32_t c = k / KP, p = l + 256u * (k % KP);
-      if (p < np) gstore<NT, T>(dst + (size_t)(c * t.plane + p0 + p + bd) * EB, lds[p * C + c]);
-    } else {
-      const uint32_t e = l + 256u * k;
-      if (e < np * C) gstore<NT, T>(d_il + (size_t)e * EB, lds[e]);
+    for (uint32_t j = 0; j < (uint32_t)C; ++j) {
+      const uint32_t q = l + 256u * j;
+      if (q < wi.nint) gstore<NT, Ch>((char*)gi + wi.a0 + 16u * q, *(const Ch*)(lds + win_pos<C>(m + wi.a0 + 16u * q)));
+    }
+    if (l < wi.head + wi.tail) {
+      const uint32_t eo = l < wi.head ? l * EB : wi.a1 + (l - wi.head) * EB;
+      gstore<NT, T>((char*)gi + eo, *(const T*)(lds + win_pos<C>(m + eo)));
     }
   }
 }
@@ -1401,7 +1472,7 @@ template <int EB, int CC, bool INTERLEAVE, bool NT>
 static bool launch_chan_one(const ChanArgs& a, bool elem, unsigned grid, hipStream_t st) {
   if constexpr (chan_supported(EB, CC)) {
     if (elem)
-      hipLaunchKernelGGL((k_chan_el<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_chan_win<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
     return true;

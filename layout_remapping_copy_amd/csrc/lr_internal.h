@@ -99,11 +99,8 @@ struct Plan {
 // for 2..8 channels of one 16-byte chunk or less per pixel.
 constexpr bool chan_supported(int eb, int64_t c) { return c >= 2 && c <= 8 && c * eb <= 16; }
 
-// Pixels per workgroup of the element-granular channel shuffle: 256 lanes of 1 to
-// 16 pixels each, the workgroup's pixels of all channels in at most 32 KiB of LDS.
-constexpr int chan_el_pixels(int eb, int c) {
-  return 256 * (128 / (c * eb) < 1 ? 1 : (128 / (c * eb) > 16 ? 16 : 128 / (c * eb)));
-}
+// Pixels per workgroup of the element-granular channel shuffle: 16/eb per lane.
+constexpr int chan_el_pixels(int eb) { return 256 * (16 / eb); }
 
 // Plans a copy; fills `p`.  Returns 0 or an lr_status.
 int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld,

@@ -146,18 +146,19 @@ static int64_t dst_span_bytes(const Plan& p) {
 // 16-byte chunks: odd image sizes, unaligned strides): `interleave` planes -> pixels
 // (a: the pixel mode, b: the channel mode), else pixels -> planes (a: channels, b:
 // pixels).  False when the layouts are not of that form.
-static bool plan_chan_elements(Plan* p, int a, int b, bool interleave) {
+static bool plan_chan_elements(Plan* p, int a, int b, bool interleave, size_t src_align, size_t dst_align) {
   if (a < 0 || b < 0 || a == b || p->sw_s.b || p->sw_d.b) return false;
   const int pm = interleave ? a : b, cm = interleave ? b : a;
   const int64_t C = p->m[cm].ext;
   const bool form = interleave ? p->m[a].sd == C : p->m[b].ss == C;
-  if (!chan_supported(p->eb, C) || !form) return false;
+  // element-aligned buffers: the kernel splits each range at 16-byte boundaries
+  if (!chan_supported(p->eb, C) || !form || src_align % (size_t)p->eb || dst_align % (size_t)p->eb) return false;
   p->path = interleave ? LR_PATH_INTERLEAVE : LR_PATH_DEINTERLEAVE;
   p->a = a;
   p->b = b;
   p->v = 1;
   p->inarrow = interleave ? 3 : 0;
-  p->tile_a = chan_el_pixels(p->eb, (int)C);
+  p->tile_a = chan_el_pixels(p->eb);
   p->tile_b = C;
   int64_t batch = 1;
   for (int k = 0; k < p->rank; ++k)
@@ -361,7 +362,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->grid = ((p->m[a].ext + p->tile_a - 1) / p->tile_a) * batch;
       return LR_OK;
     }
-    if (forced == LR_PATH_INTERLEAVE) return plan_chan_elements(p, a, b, true) ? LR_OK : LR_ERR_PATH;
+    if (forced == LR_PATH_INTERLEAVE) return plan_chan_elements(p, a, b, true, src_align, dst_align) ? LR_OK : LR_ERR_PATH;
   }
 
   // de-interleave: the mirror of the above.  The src-contiguous mode a is short (C
@@ -388,7 +389,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->grid = ((p->m[b].ext + p->tile_a - 1) / p->tile_a) * batch;
       return LR_OK;
     }
-    if (forced == LR_PATH_DEINTERLEAVE) return plan_chan_elements(p, a, b, false) ? LR_OK : LR_ERR_PATH;
+    if (forced == LR_PATH_DEINTERLEAVE) return plan_chan_elements(p, a, b, false, src_align, dst_align) ? LR_OK : LR_ERR_PATH;
   }
 
   // transpose: register blocks of V x V elements over the src-contiguous mode a and
@@ -603,15 +604,13 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
 
   // few channels whose planes have no whole 16-byte chunks (odd image sizes): the
   // element-granular channel shuffle, given at least one pixel per lane.  Measured
-  // on 299^2 and 331^2 images against the generic kernel: fp32 RGB 4.5-4.8 TB/s
-  // against 2.2-2.6, 1-byte RGB 1.5 against 0.8, fp16 RGB 2.0 against 1.4-1.5; fp16
-  // with four channels lost (1.45-1.49 against 1.45-1.63: its 2-byte LDS reads at an
-  // 8-byte stride meet two to a bank), so 2-byte elements take it for odd counts only.
+  // on 299^2 and 331^2 images with 2 to 8 channels, both directions, against the
+  // generic kernel: fp16 RGB 4.3-4.8 TB/s against 1.4-1.5, 1-byte RGB 4.3-4.6
+  // against 0.8, fp32 RGB 5.4-5.7 against 2.3-2.6, fp16 with four channels 3.8-4.2
+  // against 1.4-1.6, 8-byte pairs 4.9-5.1 against 4.0-4.3.
   if (forced < 0 && a >= 0 && b >= 0 && a != b) {
-    const bool il_ok = p->eb != 2 || (p->m[b].ext & 1);
-    const bool de_ok = p->eb != 2 || (p->m[a].ext & 1);
-    if (il_ok && p->m[a].ext >= 256 && plan_chan_elements(p, a, b, true)) return LR_OK;
-    if (de_ok && p->m[b].ext >= 256 && plan_chan_elements(p, a, b, false)) return LR_OK;
+    if (p->m[a].ext >= 256 && plan_chan_elements(p, a, b, true, src_align, dst_align)) return LR_OK;
+    if (p->m[b].ext >= 256 && plan_chan_elements(p, a, b, false, src_align, dst_align)) return LR_OK;
   }
 
   // generic: one unit per lane over the (fused) joint modes
@@ -719,7 +718,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.a].sd != nb || p.tile_b != nb) return bad();
       if (p.inarrow == 3) {  // element-granular channel shuffle: no chunk conditions
         if (!chan_supported(p.eb, nb) || p.sw_s.b || p.sw_d.b || v != 1 || p.bufst ||
-            p.tile_a != chan_el_pixels(p.eb, (int)nb))
+            p.tile_a != chan_el_pixels(p.eb))
           return bad();
         return LR_OK;
       }
@@ -742,7 +741,8 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       const int64_t C = p.m[p.a].ext;
       if (p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.b].ss != C || !chan_supported(p.eb, C)) return bad();
       if (v == 1)  // element-granular form
-        return (p.sw_s.b || p.sw_d.b || p.bufst || p.tile_a != chan_el_pixels(p.eb, (int)C) || p.tile_b != C)
+        return (p.sw_s.b || p.sw_d.b || p.bufst ||
+                p.tile_a != chan_el_pixels(p.eb) || p.tile_b != C)
                    ? bad()
                    : LR_OK;
       if (v * p.eb != 16 || p.m[p.b].ext % v || p.m[p.a].sd % v || p.sw_s.b || p.sw_d.b) return bad();

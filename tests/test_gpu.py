@@ -858,20 +858,12 @@ def test_channel_shuffle_any_pixel_count(dev, env_knob, eb):
             dst = np.full(size * eb, 0xA5, np.uint8)
             for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
                 want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-                # by default for all but 2-byte elements in even channel counts (the
-                # generic kernel measured faster there); forced, for every count
-                p = lr.copy_plan(ts, size, td, size, eb)
-                if eb == 2 and c % 2 == 0:
-                    assert p["path"] == "generic", (ts, td, eb, p)
-                else:
-                    assert p["path"] == path and p["vec_elems"] == 1, (ts, td, eb, p)
-                flags = lr.COPY_FORCE_PATH(lr.PATH_DEINTERLEAVE if path == "deinterleave" else lr.PATH_INTERLEAVE)
                 for nt in ("0", "1"):
                     env_knob.setenv("LR_NT", nt)
-                    p = lr.copy_plan(ts, size, td, size, eb, flags)
+                    p = lr.copy_plan(ts, size, td, size, eb)
                     assert p["path"] == path and p["vec_elems"] == 1, (ts, td, eb, p)
                     say("channel shuffle elements", path, "eb", eb, "C", c, (n, h, w), "nt", nt)
-                    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want), (ts, td, eb, nt)
+                    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, eb, nt)
                     ran += 1
     assert ran >= 8
 

@@ -640,10 +640,17 @@ def test_plan_few_channel_images(monkeypatch):
             else:
                 assert p["path"] != "deinterleave"
     # 323 pixels: no whole 16-byte chunks per plane, so the element-granular form
-    nhwc, nchw = image(3, 17, 19, 3)
-    for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
-        p = lr.copy_plan(ts, 2907, td, 2907, 2)
-        assert p["path"] == path and p["vec_elems"] == 1 and p["tile_a"] == 256 * 16, p  # 16 pixels per lane
+    # (16/eb pixels per lane), for any channel count; a buffer that is not element-
+    # aligned keeps the generic kernel
+    for c in (3, 4):
+        nhwc, nchw = image(3, 17, 19, c)
+        for eb in (1, 2, 4):
+            for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
+                p = lr.copy_plan(ts, 3 * 323 * c, td, 3 * 323 * c, eb)
+                want = (path, 1, 256 * 16 // eb, -(-323 // (256 * 16 // eb)) * 3) if c * eb <= 16 else ("generic",)
+                assert (p["path"], p["vec_elems"], p["tile_a"], p["grid"])[:len(want)] == want, (c, eb, p)
+        p = lr.copy_plan(nhwc, 3 * 323 * c, nchw, 3 * 323 * c, 2, src_align=1)
+        assert p["path"] == "generic", p
     # under one pixel per lane (63 pixels) it is not worth a workgroup of 4096
     nhwc, nchw = image(3, 7, 9, 3)
     assert lr.copy_plan(nhwc, 567, nchw, 567, 2)["path"] == "generic"

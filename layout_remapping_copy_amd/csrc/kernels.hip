@@ -519,6 +519,25 @@ __device__ __forceinline__ void batch_offsets(const BatchArg& b, uint32_t r, uin
 
 // ------------------------------------------------------------------ tile transpose
 
+// Head, interior and tail of the EB-aligned byte range [g, g + len): `head` single
+// elements up to the first 16-byte boundary, `nint` whole chunks from `a0` bytes
+// into the range, `tail` single elements after them.  A range without a whole chunk
+// is all head.
+template <int EB>
+struct WinSplit {
+  uint32_t head, nint, tail, a0, a1;
+  __device__ __forceinline__ WinSplit(const void* g, uint32_t len) {
+    const uint32_t mis = (uint32_t)((uintptr_t)g & 15u);
+    const uint32_t first = (16u - mis) & 15u;                // bytes to the first boundary
+    const bool inner = len >= first + 16u;
+    a0 = inner ? first : len;
+    nint = inner ? (len - first) >> 4 : 0u;
+    a1 = a0 + 16u * nint;
+    head = a0 / EB;
+    tail = (len - a1) / EB;
+  }
+};
+
 struct TransposeArgs {
   const void* src;
   void* dst;
@@ -770,6 +789,104 @@ __global__ void __launch_bounds__(512) k_transpose_el(TransposeArgs t) {
       if (a < t.ext_a && b < t.ext_b) {
         const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
         gstore<NT, T>(dst + (size_t)dof * EB, v[i]);
+      }
+    }
+  }
+}
+
+// The same element tiles with 16-byte accesses inside each row, for layouts without
+// swizzles on element-aligned buffers.  Every tile row on either side is one
+// contiguous range of at most 256 bytes (unaligned in general: an odd pitch moves
+// each row's start by EB bytes modulo 16); it moves as its aligned interior in
+// 16-byte chunks plus single elements at its two ends.  A lane takes chunk j of a
+// row, 16 lanes a row.  The LDS tile keeps the source rows in element order, so a
+// chunk goes in, or is gathered out, one element at a time at fixed offsets from
+// the lane's address.  Its row pitch of 256 + EB bytes spreads the lanes that
+// gather destination chunks (rows V apart) over the banks: two lanes a bank.
+template <int EB, bool NT>
+__global__ void __launch_bounds__(512) k_transpose_win(TransposeArgs t) {
+  using T = typename Raw<EB>::T;
+  static_assert(EB <= 8, "16-byte elements use the chunk transpose");
+  constexpr uint32_t V = 16 / EB;
+  using Ch = Chunk<T, V>;
+  constexpr uint32_t E = 256 / EB;        // tile extent in elements, both axes
+  constexpr uint32_t P = 256 + EB;        // LDS bytes per tile row
+  constexpr uint32_t ROWS = E / 32;       // rows per lane on either side
+  constexpr uint32_t NE = V > 8 ? 2 : 1;  // edge elements per lane and row (under 2 V a row)
+  __shared__ __align__(16) char tile[E * P];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blockIdx.x, ta, tb, r2);
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const uint32_t a0 = ta * E, b0 = tb * E;
+  const uint32_t na = t.ext_a - a0 < E ? t.ext_a - a0 : E;  // tile extents (ragged at the ends)
+  const uint32_t nb = t.ext_b - b0 < E ? t.ext_b - b0 : E;
+  const uint32_t j = threadIdx.x & 15u, rl = threadIdx.x >> 4;
+
+  // source rows b (elements a0 .. a0 + na - 1 of each) -> LDS rows in element order
+  Ch v[ROWS];
+  T e[ROWS][NE];
+  uint32_t hd[ROWS], ni[ROWS], ht[ROWS], a1[ROWS];
+#pragma unroll
+  for (uint32_t i = 0; i < ROWS; ++i) {
+    const uint32_t b = rl + 32u * i, bb = b0 + b;
+    ni[i] = 0;
+    ht[i] = 0;
+    if (b < nb) {
+      const char* g = src + (size_t)(a0 + (bb & t.bmask) * t.ss_b + (bb >> t.bshift) * t.ss_b2 + bs) * EB;
+      const WinSplit<EB> w(g, na * EB);
+      hd[i] = w.head;
+      ni[i] = w.nint;
+      ht[i] = w.head + w.tail;
+      a1[i] = w.a1;
+      if (j < w.nint) v[i] = gload<NT, Ch>(g + w.a0 + 16u * j);
+#pragma unroll
+      for (uint32_t u = 0; u < NE; ++u) {
+        const uint32_t k = j + 16u * u;
+        if (k < ht[i]) e[i][u] = gload<NT, T>(g + (k < w.head ? k * EB : w.a1 + (k - w.head) * EB));
+      }
+    }
+  }
+#pragma unroll
+  for (uint32_t i = 0; i < ROWS; ++i) {
+    char* row = tile + (rl + 32u * i) * P;
+    if (j < ni[i]) {
+      const uint32_t x = hd[i] * EB + 16u * j;  // byte of the chunk's first element in the row
+#pragma unroll
+      for (uint32_t k = 0; k < V; ++k) *(T*)(row + x + k * EB) = v[i].e[k];
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < NE; ++u) {
+      const uint32_t k = j + 16u * u;
+      if (k < ht[i]) *(T*)(row + (k < hd[i] ? k * EB : a1[i] + (k - hd[i]) * EB)) = e[i][u];
+    }
+  }
+  __syncthreads();
+  // destination rows a (elements b0 .. b0 + nb - 1 of each), gathered down LDS columns
+#pragma unroll
+  for (uint32_t i = 0; i < ROWS; ++i) {
+    const uint32_t a = rl + 32u * i;
+    if (a < na) {
+      char* g = dst + (size_t)((a0 + a) * t.sd_a + b0 + bd) * EB;
+      const WinSplit<EB> w(g, nb * EB);
+      const char* col = tile + a * EB;
+      if (j < w.nint) {
+        const char* c0 = col + (w.head + V * j) * P;
+        Ch o;
+#pragma unroll
+        for (uint32_t k = 0; k < V; ++k) o.e[k] = *(const T*)(c0 + k * P);
+        gstore<NT, Ch>(g + w.a0 + 16u * j, o);
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < NE; ++u) {
+        const uint32_t k = j + 16u * u;
+        if (k < w.head + w.tail) {
+          const uint32_t b = k < w.head ? k : w.head + V * w.nint + (k - w.head);
+          gstore<NT, T>(g + (size_t)b * EB, *(const T*)(col + b * P));
+        }
       }
     }
   }
@@ -1073,25 +1190,6 @@ __device__ __forceinline__ uint32_t win_pos(uint32_t x) {
   if constexpr ((C & 1) == 0) return x + ((x >> 9) << 4);
   return x;
 }
-
-// Head, interior and tail of the EB-aligned byte range [g, g + len): `head` single
-// elements up to the first 16-byte boundary, `nint` whole chunks from `a0` bytes
-// into the range, `tail` single elements after them.  A range without a whole chunk
-// is all head.
-template <int EB>
-struct WinSplit {
-  uint32_t head, nint, tail, a0, a1;
-  __device__ __forceinline__ WinSplit(const void* g, uint32_t len) {
-    const uint32_t mis = (uint32_t)((uintptr_t)g & 15u);
-    const uint32_t first = (16u - mis) & 15u;                // bytes to the first boundary
-    const bool inner = len >= first + 16u;
-    a0 = inner ? first : len;
-    nint = inner ? (len - first) >> 4 : 0u;
-    a1 = a0 + 16u * nint;
-    head = a0 / EB;
-    tail = (len - a1) / EB;
-  }
-};
 
 template <int EB, int C, bool INTERLEAVE, bool NT>
 __global__ void __launch_bounds__(256) k_chan_win(ChanArgs t) {
@@ -1433,8 +1531,14 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool
 }
 
 template <int EB, bool NT>
-static void launch_tel(const TransposeArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_transpose_el<EB, NT>), dim3(grid), dim3(512), 0, st, a);
+static bool launch_tel(const TransposeArgs& a, bool win, unsigned grid, hipStream_t st) {
+  if (win) {  // planned for 1-byte elements only
+    if constexpr (EB != 1) return false;
+    hipLaunchKernelGGL((k_transpose_win<EB, NT>), dim3(grid), dim3(512), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_transpose_el<EB, NT>), dim3(grid), dim3(512), 0, st, a);
+  }
+  return true;
 }
 
 template <int EB, bool NT>
@@ -1620,12 +1724,14 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       const bool lds = p.path == LR_PATH_TRANSPOSE;
       if (p.tel) {
         if (p.eb > 8) return LR_ERR_PATH;
+        bool ok = false;
         switch (p.eb) {
-          case 1: p.nt ? launch_tel<1, true>(a, grid, st) : launch_tel<1, false>(a, grid, st); break;
-          case 2: p.nt ? launch_tel<2, true>(a, grid, st) : launch_tel<2, false>(a, grid, st); break;
-          case 4: p.nt ? launch_tel<4, true>(a, grid, st) : launch_tel<4, false>(a, grid, st); break;
-          default: p.nt ? launch_tel<8, true>(a, grid, st) : launch_tel<8, false>(a, grid, st); break;
+          case 1: ok = p.nt ? launch_tel<1, true>(a, p.twin, grid, st) : launch_tel<1, false>(a, p.twin, grid, st); break;
+          case 2: ok = p.nt ? launch_tel<2, true>(a, p.twin, grid, st) : launch_tel<2, false>(a, p.twin, grid, st); break;
+          case 4: ok = p.nt ? launch_tel<4, true>(a, p.twin, grid, st) : launch_tel<4, false>(a, p.twin, grid, st); break;
+          default: ok = p.nt ? launch_tel<8, true>(a, p.twin, grid, st) : launch_tel<8, false>(a, p.twin, grid, st); break;
         }
+        if (!ok) return LR_ERR_PATH;
         return check_launch();
       }
       bool ok = false;

@@ -85,6 +85,8 @@ struct Plan {
   bool nt;
   bool direct;        // staged: direct global -> LDS loads (no register round trip)
   bool tel;           // transpose: element-granular tiles (rows without aligned chunks)
+  bool twin;          // element tiles with 16-byte accesses inside each row (no swizzles,
+                      // element-aligned buffers)
   bool bufst;         // streaming 16-byte stores as buffer stores with the nt and sc1 bits:
                       // vector path (destination span < 4 GiB) and LDS transpose (tile span)
   uint32_t torder;

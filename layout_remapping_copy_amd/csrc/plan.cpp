@@ -474,10 +474,12 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // element-granular tiles with 256-byte rows on both sides instead of narrow
       // chunks in small tiles.  Measured on fp16 8191^2: 1.13 -> 2.80 TB/s; it wins
       // for single elements of any size and for 2- to 8-byte elements in chunks of
-      // up to 8 bytes, while 1-byte elements in chunks of 2 to 8 keep the chunks.
+      // up to 8 bytes; 1-byte elements in chunks of 2 take them too (through the
+      // windowed kernel below), in chunks of 4 or 8 keep the chunks (u8 8188^2 2.55
+      // TB/s against 2.22-2.36, 8184^2 2.96 against 2.25-2.39).
       // LR_TEL=0 keeps the narrow chunks, LR_TEL=1 forces element tiles.
       const uint32_t tel_env = env_u32("LR_TEL", 2);
-      const bool tel_wins = V == 1 || p->eb >= 2;
+      const bool tel_wins = V <= 2 || p->eb >= 2;
       p->tel = p->path == LR_PATH_TRANSPOSE && V * p->eb < 16 && p->eb <= 8 &&
                (tel_env == 1 || (tel_env == 2 && tel_wins));
       if (p->tel) {
@@ -485,6 +487,12 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         p->tshape = 0;
         p->tile_a = p->tile_b = 256 / p->eb;
         p->block = 512;
+        // 1-byte elements: the windowed kernel, 16-byte accesses inside each tile row
+        // (u8 8191^2 1.49 -> 2.22 TB/s, 8190^2 in 2-byte chunks 2.04 -> 2.23).  For
+        // wider elements it measured slower than the per-element kernel on fp32 8191^2
+        // (2.90 against 3.20), on 8-byte elements and on rectangular fp16 (2.71 against
+        // 3.26), and faster only on square fp16 (3.44 against 3.31).
+        p->twin = p->eb == 1 && !p->sw_s.b && !p->sw_d.b;
       }
       // Workgroup order (measured on fp16, fp32, 1-, 8- and 16-byte transposes from
       // 2048 x 32768 to 16384^2).  b-tiles fastest by default: consecutive
@@ -500,7 +508,9 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // 8-byte elements: 4.65 against 4.40 on 1-byte 8192^2) unless there are more
       // a-tiles than b-tiles, when its workgroups sharing a b-tile would read
       // columns a power-of-two distance apart.  Other pitches keep b fastest:
-      // 11264^2 fp16 5.42 against 4.94 for the diagonal.
+      // 11264^2 fp16 5.42 against 4.94 for the diagonal; element tiles with more
+      // a-tiles than b-tiles take a fastest (u8 4097 x 16383 2.14 against 1.57,
+      // fp16 2.76 against 2.64; the mirror shapes lost with it, 1.91 against 2.27).
       {
         const int64_t pitch_d = p->m[a].sd * p->eb;
         auto pow2_heavy = [](int64_t q) { return q % 16384 == 0 || (q >= 4096 && (q & (q - 1)) == 0); };
@@ -508,6 +518,8 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         const int64_t ntb0 = (ext_b + p->tile_b - 1) / p->tile_b;
         if (nta0 > 1 && (pow2_heavy(pitch) || pow2_heavy(pitch_d)))
           p->torder = (p->tile_a > p->tile_b && nta0 <= ntb0) ? 2u : 4u;
+        else if (p->tel && nta0 > ntb0)
+          p->torder = 0u;  // element tiles with more a-tiles than b-tiles: a fastest
         else
           p->torder = 1u;  // (with a single a-tile, order 4 is order 1)
       }
@@ -696,7 +708,8 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
         if (p.path != LR_PATH_TRANSPOSE || p.eb > 8 || v != 1 || p.direct || p.tile_a != 256 / p.eb ||
             p.tile_b != 256 / p.eb || p.block != 512)
           return bad();
-      } else if (p.tile_a != kTileTA[p.tshape] * v || p.tile_b != kTileTB[p.tshape] * v) {
+        if (p.twin && (p.sw_s.b || p.sw_d.b || p.eb != 1)) return bad();  // rows: contiguous ranges
+      } else if (p.twin || p.tile_a != kTileTA[p.tshape] * v || p.tile_b != kTileTB[p.tshape] * v) {
         return bad();
       }
       const int64_t nta = (p.m[p.a].ext + p.tile_a - 1) / p.tile_a, ntb = (ext_b + p.tile_b - 1) / p.tile_b;

@@ -665,20 +665,27 @@ def test_plan_few_channel_images(monkeypatch):
 
 def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
     """Transposes whose rows allow no aligned 16-byte chunks take element tiles of
-    256-byte rows, except 1-byte elements that still fit 2- to 8-byte chunks."""
+    256-byte rows, except 1-byte elements that still fit 4- or 8-byte chunks; with
+    more a-tiles than b-tiles the tiles go a fastest."""
     monkeypatch.delenv("LR_TEL", raising=False)
+    monkeypatch.delenv("LR_TORDER", raising=False)
     # (n, bytes per element) -> element tiles?  (8190, 8) and (8192, 2) have full
-    # 16-byte chunks; 1-byte elements in 2- and 8-byte chunks keep the chunks
+    # 16-byte chunks; 1-byte elements in 4- and 8-byte chunks keep the chunks
     want = {(8191, 1): True, (8191, 2): True, (8191, 4): True, (8191, 8): True,
-            (8190, 1): False, (8190, 2): True, (8190, 4): True, (8190, 8): False,
-            (8200, 1): False, (8192, 2): False}
+            (8190, 1): True, (8188, 1): False, (8184, 1): False, (8190, 2): True, (8190, 4): True,
+            (8190, 8): False, (8200, 1): False, (8192, 2): False}
     for (n, eb), element in want.items():
         p = lr.copy_plan(f"({n},{n}):({n},1)", n * n, f"({n},{n}):(1,{n})", n * n, eb)
         assert p["path"] == "transpose"
         got = p["vec_elems"] == 1 and p["tile_a"] == p["tile_b"] == 256 // eb and p["block"] == 512
         assert got == element, (n, eb, p)
+        if element:
+            assert p["order"] == 1, (n, eb, p)  # as many a-tiles as b-tiles
+    for r, c, order in ((4097, 16383, 0), (16383, 4097, 1)):
+        p = lr.copy_plan(f"({r},{c}):({c},1)", r * c, f"({r},{c}):(1,{r})", r * c, 1)
+        assert p["tile_a"] == 256 and p["order"] == order, (r, c, p)
     monkeypatch.setenv("LR_TEL", "1")
-    assert lr.copy_plan("(8190,8190):(8190,1)", 8190 ** 2, "(8190,8190):(1,8190)", 8190 ** 2, 1)["tile_a"] == 256
+    assert lr.copy_plan("(8188,8188):(8188,1)", 8188 ** 2, "(8188,8188):(1,8188)", 8188 ** 2, 1)["tile_a"] == 256
     monkeypatch.setenv("LR_TEL", "0")
     assert lr.copy_plan("(8191,8191):(8191,1)", 8191 ** 2, "(8191,8191):(1,8191)", 8191 ** 2, 2)["tile_a"] == 16
 

@@ -669,6 +669,46 @@ def test_vector_streaming_store_forms(dev, env_knob, sc1):
     assert ran == 2 * len(cases)
 
 
+def _pow2_align(off):
+    return 16 if off % 16 == 0 else off & -off
+
+
+def test_windowed_kernels_misaligned_pointers(dev):
+    """The kernels that split each contiguous range into an aligned 16-byte interior
+    and single elements at its ends (the channel shuffle for unaligned planes, and
+    1-byte element tiles), on buffers starting at element-aligned offsets that are
+    not 16-byte aligned; the 2-byte element tiles beside them."""
+    def image(n, h, w, c):
+        hw = h * w
+        return f"({n},{h},{w},{c}):({hw * c},{w * c},{c},1)", f"({n},{h},{w},{c}):({hw * c},{w},1,{hw})"
+    ran = 0
+    for eb, c in ((2, 3), (1, 3), (4, 2), (1, 8), (8, 2)):
+        nhwc, nchw = image(2, 19, 23, c)
+        size = 2 * 19 * 23 * c
+        src = np.random.default_rng(eb * 10 + c).integers(0, 256, size * eb, dtype=np.uint8)
+        dst = np.full(size * eb, 0xA5, np.uint8)
+        for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
+            want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+            for so, do in ((eb, 0), (0, 3 * eb), (5 * eb, 7 * eb)):
+                p = lr.copy_plan(ts, size, td, size, eb, src_align=_pow2_align(so), dst_align=_pow2_align(do))
+                assert p["path"] == path and p["vec_elems"] == 1, (ts, td, eb, so, do, p)
+                say("windowed channel shuffle", path, "eb", eb, "C", c, "offsets", so, do)
+                assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, src_off=so, dst_off=do), want), (ts, eb, so, do)
+                ran += 1
+    for eb in (1, 2):
+        ts, td, n = "(301,517):(517,1)", "(301,517):(1,301)", 301 * 517
+        src = np.random.default_rng(40 + eb).integers(0, 256, n * eb, dtype=np.uint8)
+        dst = np.full(n * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for so, do in ((eb, 0), (0, 5 * eb), (3 * eb, 11 * eb)):
+            p = lr.copy_plan(ts, n, td, n, eb, src_align=_pow2_align(so), dst_align=_pow2_align(do))
+            assert p["path"] == "transpose" and p["tile_a"] == 256 // eb and p["block"] == 512, (eb, so, do, p)
+            say("element tiles", "eb", eb, "offsets", so, do)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, src_off=so, dst_off=do), want), (eb, so, do)
+            ran += 1
+    assert ran == 36
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
 def test_transpose_element_tiles(dev, env_knob, eb):
     """Transposes whose rows allow no aligned 16-byte chunks run element-granular

@@ -175,7 +175,7 @@ def counters_run(lr, torch, W, reps: int = 3):
     workload `reps` times after one warm-up, then a plain contiguous copy of
     256 MiB (the reference of known size that scales FETCH_SIZE / WRITE_SIZE)."""
     dev = torch.device("cuda:0")
-    names = ("transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles")
+    names = ("transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw")
     for name in names:
         w = W.full(name)
         s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)

@@ -1532,8 +1532,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool
 
 template <int EB, bool NT>
 static bool launch_tel(const TransposeArgs& a, bool win, unsigned grid, hipStream_t st) {
-  if (win) {  // planned for 1-byte elements only
-    if constexpr (EB != 1) return false;
+  if (win) {
     hipLaunchKernelGGL((k_transpose_win<EB, NT>), dim3(grid), dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL((k_transpose_el<EB, NT>), dim3(grid), dim3(512), 0, st, a);

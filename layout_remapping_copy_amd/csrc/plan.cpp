@@ -487,12 +487,16 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         p->tshape = 0;
         p->tile_a = p->tile_b = 256 / p->eb;
         p->block = 512;
-        // 1-byte elements: the windowed kernel, 16-byte accesses inside each tile row
-        // (u8 8191^2 1.49 -> 2.22 TB/s, 8190^2 in 2-byte chunks 2.04 -> 2.23).  For
-        // wider elements it measured slower than the per-element kernel on fp32 8191^2
-        // (2.90 against 3.20), on 8-byte elements and on rectangular fp16 (2.71 against
-        // 3.26), and faster only on square fp16 (3.44 against 3.31).
-        p->twin = p->eb == 1 && !p->sw_s.b && !p->sw_d.b;
+        // The windowed kernel (16-byte accesses inside each tile row) on element-aligned
+        // buffers without swizzles, with ordinary (cached) accesses at every size: the
+        // partial lines at the unaligned ends of the row segments then merge in L2.
+        // Measured on odd-pitch squares and rectangles of 1- to 8-byte elements, from
+        // 32 MiB to 512 MiB, against the per-element kernel with streaming accesses past
+        // 128 MiB: fp16 8191^2 3.34 -> 4.10 TB/s, 12287^2 3.45 -> 4.16, 4097 x 16383
+        // 2.78 -> 3.89; fp32 8191^2 3.22 -> 4.92; 8-byte 4095^2 3.57 -> 5.06; u8 16383^2
+        // 2.08 -> 2.40.  Streaming accesses alone cost the per-element kernel 8-18 %.
+        p->twin = !p->sw_s.b && !p->sw_d.b && src_align % (size_t)p->eb == 0 && dst_align % (size_t)p->eb == 0;
+        if (!std::getenv("LR_NT")) p->nt = false;
       }
       // Workgroup order (measured on fp16, fp32, 1-, 8- and 16-byte transposes from
       // 2048 x 32768 to 16384^2).  b-tiles fastest by default: consecutive
@@ -508,9 +512,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // 8-byte elements: 4.65 against 4.40 on 1-byte 8192^2) unless there are more
       // a-tiles than b-tiles, when its workgroups sharing a b-tile would read
       // columns a power-of-two distance apart.  Other pitches keep b fastest:
-      // 11264^2 fp16 5.42 against 4.94 for the diagonal; element tiles with more
-      // a-tiles than b-tiles take a fastest (u8 4097 x 16383 2.14 against 1.57,
-      // fp16 2.76 against 2.64; the mirror shapes lost with it, 1.91 against 2.27).
+      // 11264^2 fp16 5.42 against 4.94 for the diagonal.  Element tiles with at least
+      // as many a-tiles as b-tiles take a fastest: fp32 8191^2 4.92 against 3.63, fp16
+      // 12287^2 4.16 against 3.39, u8 4097 x 16383 2.15 against 1.58; the tall mirror
+      // shapes lost with it (u8 16383 x 4097 1.93 against 2.28).
       {
         const int64_t pitch_d = p->m[a].sd * p->eb;
         auto pow2_heavy = [](int64_t q) { return q % 16384 == 0 || (q >= 4096 && (q & (q - 1)) == 0); };
@@ -518,8 +523,8 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         const int64_t ntb0 = (ext_b + p->tile_b - 1) / p->tile_b;
         if (nta0 > 1 && (pow2_heavy(pitch) || pow2_heavy(pitch_d)))
           p->torder = (p->tile_a > p->tile_b && nta0 <= ntb0) ? 2u : 4u;
-        else if (p->tel && nta0 > ntb0)
-          p->torder = 0u;  // element tiles with more a-tiles than b-tiles: a fastest
+        else if (p->tel && nta0 >= ntb0)
+          p->torder = 0u;  // element tiles, at least as many a-tiles as b-tiles: a fastest
         else
           p->torder = 1u;  // (with a single a-tile, order 4 is order 1)
       }
@@ -708,7 +713,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
         if (p.path != LR_PATH_TRANSPOSE || p.eb > 8 || v != 1 || p.direct || p.tile_a != 256 / p.eb ||
             p.tile_b != 256 / p.eb || p.block != 512)
           return bad();
-        if (p.twin && (p.sw_s.b || p.sw_d.b || p.eb != 1)) return bad();  // rows: contiguous ranges
+        if (p.twin && (p.sw_s.b || p.sw_d.b)) return bad();  // rows: contiguous ranges
       } else if (p.twin || p.tile_a != kTileTA[p.tshape] * v || p.tile_b != kTileTB[p.tshape] * v) {
         return bad();
       }

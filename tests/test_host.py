@@ -547,7 +547,8 @@ def test_plan_workgroup_order(monkeypatch):
     """Transpose workgroup order: b-tiles fastest unless a pitch is power-of-two
     heavy (a multiple of 16 KiB, or a power of two from 4 KiB); then the diagonal
     with b fastest, or with a fastest for tiles with longer source rows and no more
-    a-tiles than b-tiles.  A single a-tile keeps b fastest."""
+    a-tiles than b-tiles.  A single a-tile keeps b fastest.  Element tiles (rows
+    without aligned chunks) go a fastest with at least as many a-tiles as b-tiles."""
     monkeypatch.delenv("LR_TORDER", raising=False)
     monkeypatch.delenv("LR_TSHAPE", raising=False)
 
@@ -558,7 +559,8 @@ def test_plan_workgroup_order(monkeypatch):
 
     want = {(8192, 8192, 2): 4, (16384, 16384, 2): 4, (2048, 32768, 2): 4, (32768, 2048, 2): 4,
             (8192, 8256, 2): 4,  # destination pitch 16 KiB
-            (11264, 11264, 2): 1, (12288, 12288, 2): 1, (8191, 8191, 2): 1, (6144, 6144, 4): 1,
+            (11264, 11264, 2): 1, (12288, 12288, 2): 1, (8191, 8191, 2): 0, (6144, 6144, 4): 1,
+            (16383, 4097, 2): 1, (4097, 16383, 2): 0,  # element tiles: 33 x 128 and 128 x 33 tiles
             (8192, 8192, 1): 2,  # 512 x 256 tiles, 16 a-tiles <= 32 b-tiles
             (2048, 32768, 1): 4,  # 64 a-tiles > 8 b-tiles
             (8192, 4096, 8): 2, (4096, 4096, 16): 4, (8192, 8192, 4): 4}
@@ -666,7 +668,7 @@ def test_plan_few_channel_images(monkeypatch):
 def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
     """Transposes whose rows allow no aligned 16-byte chunks take element tiles of
     256-byte rows, except 1-byte elements that still fit 4- or 8-byte chunks; with
-    more a-tiles than b-tiles the tiles go a fastest."""
+    at least as many a-tiles as b-tiles the tiles go a fastest."""
     monkeypatch.delenv("LR_TEL", raising=False)
     monkeypatch.delenv("LR_TORDER", raising=False)
     # (n, bytes per element) -> element tiles?  (8190, 8) and (8192, 2) have full
@@ -679,8 +681,8 @@ def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
         assert p["path"] == "transpose"
         got = p["vec_elems"] == 1 and p["tile_a"] == p["tile_b"] == 256 // eb and p["block"] == 512
         assert got == element, (n, eb, p)
-        if element:
-            assert p["order"] == 1, (n, eb, p)  # as many a-tiles as b-tiles
+        if element:  # as many a-tiles as b-tiles: a fastest; ordinary accesses at any size
+            assert p["order"] == 0 and not p["streaming"], (n, eb, p)
     for r, c, order in ((4097, 16383, 0), (16383, 4097, 1)):
         p = lr.copy_plan(f"({r},{c}):({c},1)", r * c, f"({r},{c}):(1,{r})", r * c, 1)
         assert p["tile_a"] == 256 and p["order"] == order, (r, c, p)

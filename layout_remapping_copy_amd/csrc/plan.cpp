@@ -512,17 +512,34 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // 8-byte elements: 4.65 against 4.40 on 1-byte 8192^2) unless there are more
       // a-tiles than b-tiles, when its workgroups sharing a b-tile would read
       // columns a power-of-two distance apart.  Other pitches keep b fastest:
-      // 11264^2 fp16 5.42 against 4.94 for the diagonal.  Element tiles with at least
+      // 11264^2 fp16 5.42 against 4.94 for the diagonal.  Chunk tiles whose pitch is
+      // within 64 bytes of a multiple of 16 KiB take the diagonal too (fp16 8224^2 4.33
+      // against 3.44, 8184^2 3.84 against 3.47, fp32 4100^2 3.91 against 3.66; 8200^2
+      // 3.71 against 3.74).  Element tiles whose pitch lies up to 64 bytes past a
+      // multiple of 8 KiB take the diagonal with b fastest (fp16 8193^2 3.80 against
+      // 3.22, 8196^2 4.13 against 3.12, 12289^2 3.71 against 3.18; fp32 4097 x 8193 4.43
+      // against 3.40), unless a pitch lies just short of one: 8191^2 takes a fastest (4.05
+      // against 2.83), 16383 x 4097 b fastest (3.37 against 2.59).  Element tiles with at least
       // as many a-tiles as b-tiles take a fastest: fp32 8191^2 4.92 against 3.63, fp16
       // 12287^2 4.16 against 3.39, u8 4097 x 16383 2.15 against 1.58; the tall mirror
       // shapes lost with it (u8 16383 x 4097 1.93 against 2.28).
       {
         const int64_t pitch_d = p->m[a].sd * p->eb;
         auto pow2_heavy = [](int64_t q) { return q % 16384 == 0 || (q >= 4096 && (q & (q - 1)) == 0); };
+        // chunk tiles: within 64 bytes of a multiple of 16 KiB behaves as a multiple
+        auto near_16k = [](int64_t q) { return q >= 16384 - 64 && (q % 16384 <= 64 || q % 16384 >= 16384 - 64); };
+        // element tiles: up to 64 bytes past a multiple of 8 KiB, unless the other pitch
+        // is up to 64 bytes short of one
+        auto past_8k = [](int64_t q) { return q >= 8192 && q % 8192 != 0 && q % 8192 <= 64; };
+        auto short_8k = [](int64_t q) { return q >= 8192 - 64 && q % 8192 >= 8192 - 64; };
         const int64_t nta0 = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
         const int64_t ntb0 = (ext_b + p->tile_b - 1) / p->tile_b;
-        if (nta0 > 1 && (pow2_heavy(pitch) || pow2_heavy(pitch_d)))
+        const bool camp = pow2_heavy(pitch) || pow2_heavy(pitch_d) ||
+                          (!p->tel && (near_16k(pitch) || near_16k(pitch_d)));
+        if (nta0 > 1 && camp)
           p->torder = (p->tile_a > p->tile_b && nta0 <= ntb0) ? 2u : 4u;
+        else if (nta0 > 1 && p->tel && (past_8k(pitch) || past_8k(pitch_d)) && !short_8k(pitch) && !short_8k(pitch_d))
+          p->torder = 4u;
         else if (p->tel && nta0 >= ntb0)
           p->torder = 0u;  // element tiles, at least as many a-tiles as b-tiles: a fastest
         else

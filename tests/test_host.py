@@ -547,8 +547,10 @@ def test_plan_workgroup_order(monkeypatch):
     """Transpose workgroup order: b-tiles fastest unless a pitch is power-of-two
     heavy (a multiple of 16 KiB, or a power of two from 4 KiB); then the diagonal
     with b fastest, or with a fastest for tiles with longer source rows and no more
-    a-tiles than b-tiles.  A single a-tile keeps b fastest.  Element tiles (rows
-    without aligned chunks) go a fastest with at least as many a-tiles as b-tiles."""
+    a-tiles than b-tiles.  A single a-tile keeps b fastest.  Chunk tiles within 64
+    bytes of a multiple of 16 KiB count as power-of-two heavy.  Element tiles (rows
+    without aligned chunks) take the diagonal with b fastest up to 64 bytes past a
+    multiple of 8 KiB, else a fastest with at least as many a-tiles as b-tiles."""
     monkeypatch.delenv("LR_TORDER", raising=False)
     monkeypatch.delenv("LR_TSHAPE", raising=False)
 
@@ -561,6 +563,9 @@ def test_plan_workgroup_order(monkeypatch):
             (8192, 8256, 2): 4,  # destination pitch 16 KiB
             (11264, 11264, 2): 1, (12288, 12288, 2): 1, (8191, 8191, 2): 0, (6144, 6144, 4): 1,
             (16383, 4097, 2): 1, (4097, 16383, 2): 0,  # element tiles: 33 x 128 and 128 x 33 tiles
+            (8184, 8184, 2): 4, (8224, 8224, 2): 4, (4100, 4100, 4): 4, (8256, 8256, 2): 1,  # near 16 KiB
+            (8193, 8193, 2): 4, (8196, 8196, 2): 4, (12289, 12289, 2): 4, (8188, 8188, 2): 0,  # past 8 KiB
+            (8193, 4097, 4): 4, (4097, 2049, 2): 4,  # both pitches past 8 KiB, or one past and one small
             (8192, 8192, 1): 2,  # 512 x 256 tiles, 16 a-tiles <= 32 b-tiles
             (2048, 32768, 1): 4,  # 64 a-tiles > 8 b-tiles
             (8192, 4096, 8): 2, (4096, 4096, 16): 4, (8192, 8192, 4): 4}

@@ -496,7 +496,8 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         // 2.78 -> 3.89; fp32 8191^2 3.22 -> 4.92; 8-byte 4095^2 3.57 -> 5.06; u8 16383^2
         // 2.08 -> 2.40.  Streaming accesses alone cost the per-element kernel 8-18 %.
         p->twin = !p->sw_s.b && !p->sw_d.b && src_align % (size_t)p->eb == 0 && dst_align % (size_t)p->eb == 0;
-        if (!std::getenv("LR_NT")) p->nt = false;
+        const char* nt_env = std::getenv("LR_NT");
+        if (!nt_env || !*nt_env) p->nt = false;  // LR_NT=0/1 still overrides
       }
       // Workgroup order (measured on fp16, fp32, 1-, 8- and 16-byte transposes from
       // 2048 x 32768 to 16384^2).  b-tiles fastest by default: consecutive

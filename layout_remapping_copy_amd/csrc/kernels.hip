@@ -826,42 +826,49 @@ __global__ void __launch_bounds__(512) k_transpose_win(TransposeArgs t) {
   const uint32_t nb = t.ext_b - b0 < E ? t.ext_b - b0 : E;
   const uint32_t j = threadIdx.x & 15u, rl = threadIdx.x >> 4;
 
-  // source rows b (elements a0 .. a0 + na - 1 of each) -> LDS rows in element order
-  Ch v[ROWS];
-  T e[ROWS][NE];
-  uint32_t hd[ROWS], ni[ROWS], ht[ROWS], a1[ROWS];
+  // source rows b (elements a0 .. a0 + na - 1 of each) -> LDS rows in element order;
+  // 1-byte elements in two batches of rows, so that the bytes unpacked for the LDS
+  // writes stay under 128 VGPRs (two workgroups a CU)
+  constexpr uint32_t BATCHES = EB == 1 ? 2 : 1;
+  constexpr uint32_t RB = ROWS / BATCHES;
 #pragma unroll
-  for (uint32_t i = 0; i < ROWS; ++i) {
-    const uint32_t b = rl + 32u * i, bb = b0 + b;
-    ni[i] = 0;
-    ht[i] = 0;
-    if (b < nb) {
-      const char* g = src + (size_t)(a0 + (bb & t.bmask) * t.ss_b + (bb >> t.bshift) * t.ss_b2 + bs) * EB;
-      const WinSplit<EB> w(g, na * EB);
-      hd[i] = w.head;
-      ni[i] = w.nint;
-      ht[i] = w.head + w.tail;
-      a1[i] = w.a1;
-      if (j < w.nint) v[i] = gload<NT, Ch>(g + w.a0 + 16u * j);
+  for (uint32_t h = 0; h < BATCHES; ++h) {
+    Ch v[RB];
+    T e[RB][NE];
+    uint32_t hd[RB], ni[RB], ht[RB], a1[RB];
+#pragma unroll
+    for (uint32_t i = 0; i < RB; ++i) {
+      const uint32_t b = rl + 32u * (h * RB + i), bb = b0 + b;
+      ni[i] = 0;
+      ht[i] = 0;
+      if (b < nb) {
+        const char* g = src + (size_t)(a0 + (bb & t.bmask) * t.ss_b + (bb >> t.bshift) * t.ss_b2 + bs) * EB;
+        const WinSplit<EB> w(g, na * EB);
+        hd[i] = w.head;
+        ni[i] = w.nint;
+        ht[i] = w.head + w.tail;
+        a1[i] = w.a1;
+        if (j < w.nint) v[i] = gload<NT, Ch>(g + w.a0 + 16u * j);
+#pragma unroll
+        for (uint32_t u = 0; u < NE; ++u) {
+          const uint32_t k = j + 16u * u;
+          if (k < ht[i]) e[i][u] = gload<NT, T>(g + (k < w.head ? k * EB : w.a1 + (k - w.head) * EB));
+        }
+      }
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < RB; ++i) {
+      char* row = tile + (rl + 32u * (h * RB + i)) * P;
+      if (j < ni[i]) {
+        const uint32_t x = hd[i] * EB + 16u * j;  // byte of the chunk's first element in the row
+#pragma unroll
+        for (uint32_t k = 0; k < V; ++k) *(T*)(row + x + k * EB) = v[i].e[k];
+      }
 #pragma unroll
       for (uint32_t u = 0; u < NE; ++u) {
         const uint32_t k = j + 16u * u;
-        if (k < ht[i]) e[i][u] = gload<NT, T>(g + (k < w.head ? k * EB : w.a1 + (k - w.head) * EB));
+        if (k < ht[i]) *(T*)(row + (k < hd[i] ? k * EB : a1[i] + (k - hd[i]) * EB)) = e[i][u];
       }
-    }
-  }
-#pragma unroll
-  for (uint32_t i = 0; i < ROWS; ++i) {
-    char* row = tile + (rl + 32u * i) * P;
-    if (j < ni[i]) {
-      const uint32_t x = hd[i] * EB + 16u * j;  // byte of the chunk's first element in the row
-#pragma unroll
-      for (uint32_t k = 0; k < V; ++k) *(T*)(row + x + k * EB) = v[i].e[k];
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < NE; ++u) {
-      const uint32_t k = j + 16u * u;
-      if (k < ht[i]) *(T*)(row + (k < hd[i] ? k * EB : a1[i] + (k - hd[i]) * EB)) = e[i][u];
     }
   }
   __syncthreads();

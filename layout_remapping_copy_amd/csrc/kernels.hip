@@ -16,15 +16,17 @@
 // destination, a forced path or an explicit request).
 //
 // Wavefronts are 64 lanes.  Workgroups have 256 lanes (4 waves, one per SIMD),
-// except the tile transposes (TA*TB lanes, 256 to 1024) and the ordered-alias
-// kernel (1024 lanes, one window per workgroup).
+// except the tile transposes (TA*TB lanes, 256 to 1024; 512 for element tiles) and
+// the ordered-alias kernel (1024 lanes, one window per workgroup).
 //
 // Cache policy: streaming copies (by default when source plus destination reach
-// the 256 MiB last-level cache) load and store with the non-temporal bit.  The
-// streaming stores of the vector path, the head interleave and the LDS tile
-// transpose are buffer stores that also carry the sc1 scope bit, which HIP's
-// global stores cannot express; their 32-bit offsets run from a base the host has
-// checked (the destination, or a transpose tile's lowest offset).
+// the 256 MiB last-level cache) load and store with the non-temporal bit; element
+// tiles keep ordinary accesses at every size, so the partial lines at their
+// unaligned row ends merge in L2.  The streaming stores of the vector path, the
+// head interleave, the channel shuffle and the LDS tile transpose are buffer
+// stores that also carry the sc1 scope bit, which HIP's global stores cannot
+// express; their 32-bit offsets run from a base the host has checked (the
+// destination, or a transpose tile's lowest offset).
 
 #include <hip/hip_runtime.h>
 

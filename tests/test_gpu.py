@@ -709,6 +709,33 @@ def test_windowed_kernels_misaligned_pointers(dev):
     assert ran == 36
 
 
+def test_odd_pitch_transposes_full_size(dev):
+    """Element-tile transposes at full size in the launch configurations the planner
+    picks for them (windowed tiles, ordinary accesses, each workgroup order rule):
+    whole destination buffers against NumPy's transpose."""
+    cases = [(8191, 8191, 2, 0),    # just short of a multiple of 8 KiB: a fastest
+             (8196, 8196, 2, 4),    # just past one: the diagonal with b fastest
+             (16383, 4097, 2, 1),   # one pitch just short: b fastest
+             (4097, 8193, 4, 4),    # both pitches just past
+             (8191, 8191, 1, 0),    # 1-byte elements, two load batches
+             (5793, 5793, 8, 0)]
+    for r, c, eb, order in cases:
+        n = r * c
+        ls, ld = f"({r},{c}):({c},1)", f"({r},{c}):(1,{r})"
+        p = lr.copy_plan(ls, n, ld, n, eb)
+        assert p["path"] == "transpose" and p["vec_elems"] == 1 and p["tile_a"] == 256 // eb, (r, c, eb, p)
+        assert p["order"] == order and not p["streaming"], (r, c, eb, p)
+        src = np.random.default_rng(r + c + eb).integers(0, 256, n * eb, dtype=np.uint8)
+        want = np.ascontiguousarray(src.reshape(r, c, eb).transpose(1, 0, 2)).reshape(-1)
+        say("odd-pitch transpose", r, c, "eb", eb, "order", order)
+        s = torch.from_numpy(src).to(dev)
+        d = torch.full((n * eb,), 0xA5, dtype=torch.uint8, device=dev)
+        lr.layout_copy(s, ls, d, ld, elem_bytes=eb)
+        torch.cuda.synchronize()
+        assert np.array_equal(d.cpu().numpy(), want), (r, c, eb)
+        del s, d
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
 def test_transpose_element_tiles(dev, env_knob, eb):
     """Transposes whose rows allow no aligned 16-byte chunks run element-granular

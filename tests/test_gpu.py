@@ -709,6 +709,32 @@ def test_windowed_kernels_misaligned_pointers(dev):
     assert ran == 36
 
 
+def test_odd_size_images_full_size(dev):
+    """The element-granular channel shuffle at full size, both directions, in the
+    plans the planner picks (ordinary accesses below the streaming threshold,
+    streaming above it): whole destination buffers against NumPy's permutation."""
+    for n, h, w, c, eb, streaming in ((128, 299, 299, 3, 2, False), (64, 331, 331, 4, 2, False),
+                                      (256, 299, 299, 3, 1, False), (300, 299, 299, 3, 2, True)):
+        hw = h * w
+        nhwc = f"({n},{h},{w},{c}):({hw * c},{w * c},{c},1)"
+        nchw = f"({n},{h},{w},{c}):({hw * c},{w},1,{hw})"
+        size = n * hw * c
+        src = np.random.default_rng(n + c + eb).integers(0, 256, size * eb, dtype=np.uint8)
+        planar = np.ascontiguousarray(src.reshape(n, h, w, c, eb).transpose(0, 3, 1, 2, 4)).reshape(-1)
+        interleaved = np.ascontiguousarray(src.reshape(n, c, h, w, eb).transpose(0, 2, 3, 1, 4)).reshape(-1)
+        s = torch.from_numpy(src).to(dev)
+        for ts, td, path, want in ((nhwc, nchw, "deinterleave", planar), (nchw, nhwc, "interleave", interleaved)):
+            p = lr.copy_plan(ts, size, td, size, eb)
+            assert p["path"] == path and p["vec_elems"] == 1 and p["streaming"] == streaming, (n, h, w, c, eb, p)
+            say("odd-size image", path, (n, h, w, c), "eb", eb)
+            d = torch.full((size * eb,), 0xA5, dtype=torch.uint8, device=dev)
+            lr.layout_copy(s, ts, d, td, elem_bytes=eb)
+            torch.cuda.synchronize()
+            assert np.array_equal(d.cpu().numpy(), want), (path, n, h, w, c, eb)
+            del d
+        del s
+
+
 def test_odd_pitch_transposes_full_size(dev):
     """Element-tile transposes at full size in the launch configurations the planner
     picks for them (windowed tiles, ordinary accesses, each workgroup order rule):

@@ -1515,7 +1515,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool
     hipLaunchKernelGGL((k_transpose<EB, V, false, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a);
     return true;
   }
-  if constexpr (V * EB == 16) {  // other shapes: full 16-byte chunks, tiles that fit LDS
+  if constexpr (V * EB == 16 || (EB == 1 && V == 8)) {  // other shapes: 16-byte chunks (8-byte for 1-byte elements), tiles that fit LDS
 #define LR_TSHAPE_CASE(S)                                                                \
   case S:                                                                                \
     if constexpr (shape_fits(S, V)) {                                                    \

@@ -412,7 +412,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       }
       return true;
     };
-    int64_t V = V16;
+    // 1-byte elements: 8-byte chunks (8 x 8 byte register blocks, 32 VGPRs of data
+    // against 128 for 16 x 16), measured faster in wide tiles: u8 4096^2 3.49 -> 3.91
+    // TB/s, 6144^2 3.65 -> 4.07, 8192 x 16384 5.23 -> 5.44, 8192^2 4.71 -> 4.78
+    int64_t V = p->eb == 1 ? 8 : V16;
     while (V > 1) {
       bool ok = p->m[a].ext % V == 0 && ext_b % V == 0 && strides_ok(V) && swz_keeps(p->sw_s, V) &&
                 swz_keeps(p->sw_d, V) && src_align % (size_t)(V * p->eb) == 0 &&
@@ -440,13 +443,15 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       //    chunk (8- and 16-byte elements) a lane has few loads in flight and
       //    smaller tiles won: 32 x 16 chunks for two (5.48 vs 5.11 TB/s on an
       //    8192^2 transpose), 16 x 16 for one (5.35 vs 5.26).
-      const bool wide_ok = V * p->eb == 16 && p->path == LR_PATH_TRANSPOSE;
+      const bool wide_ok = (V * p->eb == 16 || (p->eb == 1 && V == 8)) && p->path == LR_PATH_TRANSPOSE;
       const int64_t ext_a = p->m[a].ext;
       const bool block_rows = ext_a <= 32 * V && p->m[b].ss == ext_a;
       if (!wide_ok)
         p->tshape = 0;
       else if (block_rows)
         p->tshape = ext_a > 16 * V ? 4 : 0;
+      else if (p->eb == 1)
+        p->tshape = ext_a > 16 * V ? 1 : 0;  // 8-byte chunks: 32 x 16 (u8 8192^2 4.78 against 4.56 with 32 x 32)
       else if (V >= 4)
         p->tshape = ext_a > 16 * V ? 3 : 2;
       else
@@ -454,7 +459,8 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // Fewer tiles than compute units (a 16 MiB transpose in 256 x 256 tiles is 128
       // workgroups): 32 x 8 chunks, four times as many workgroups.  Measured on
       // fp16 1024 x 8192 and 8192 x 1024, the 8-way shard pack of 1024 x 8192 and u8
-      // 4096^2: +2 to +8 % (16 MiB copies run near a plain copy's 3.2-3.6 TB/s).
+      // 4096^2 in 16-byte chunks: +2 to +8 % (16 MiB copies run near a plain copy's
+      // 3.2-3.6 TB/s).
       if (wide_ok && !block_rows) {
         int64_t tiles = ((ext_a + kTileTA[p->tshape] * V - 1) / (kTileTA[p->tshape] * V)) *
                         ((ext_b + kTileTB[p->tshape] * V - 1) / (kTileTB[p->tshape] * V));
@@ -539,6 +545,8 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
                           (!p->tel && (near_16k(pitch) || near_16k(pitch_d)));
         if (nta0 > 1 && camp)
           p->torder = (p->tile_a > p->tile_b && nta0 <= ntb0) ? 2u : 4u;
+        else if (nta0 > 1 && p->eb == 1 && !p->tel && p->v == 8 && p->tile_a > p->tile_b && nta0 <= ntb0)
+          p->torder = 2u;  // 1-byte elements in 8-byte chunks: the diagonal at any pitch (u8 6144^2 4.07 against 3.73)
         else if (nta0 > 1 && p->tel && (past_8k(pitch) || past_8k(pitch_d)) && !short_8k(pitch) && !short_8k(pitch_d))
           p->torder = 4u;
         else if (p->tel && nta0 >= ntb0)
@@ -715,7 +723,8 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       }
       if (p.m[p.a].ext % v || ext_b % v) return bad();
       if (p.tshape < 0 || p.tshape >= kTileShapes ||
-          (p.tshape != 0 && (v * p.eb != 16 || !shape_fits(p.tshape, (int)v) || p.path != LR_PATH_TRANSPOSE)))
+          (p.tshape != 0 && ((v * p.eb != 16 && !(p.eb == 1 && v == 8)) || !shape_fits(p.tshape, (int)v) ||
+                             p.path != LR_PATH_TRANSPOSE)))
         return bad();
       if (p.torder > 4) return bad();
       if (p.bufst) {  // buffer stores: full chunks of the LDS kernel, tile span under 4 GiB

@@ -539,6 +539,9 @@ def test_plan_streaming_default_and_tile_shapes(monkeypatch):
     assert (p["tile_a"], p["tile_b"], p["grid"]) == (256, 64, 512), p
     p = lr.copy_plan("(4096,4096):(4096,1)", 1 << 24, "(4096,4096):(1,4096)", 1 << 24, 2)
     assert (p["tile_a"], p["tile_b"], p["grid"]) == (256, 256, 256), p
+    # 1-byte elements move in 8-byte chunks, 32 x 16 of them a tile (256 x 128 bytes)
+    p = lr.copy_plan("(8192,8192):(8192,1)", 1 << 26, "(8192,8192):(1,8192)", 1 << 26, 1)
+    assert (p["vec_elems"], p["tile_a"], p["tile_b"], p["block"]) == (8, 256, 128, 512), p
     # u8 4096^2 in 8-byte chunks: 32 x 16-chunk tiles of 256 x 128 bytes already make 512
     p = lr.copy_plan("(4096,4096):(4096,1)", 1 << 24, "(4096,4096):(1,4096)", 1 << 24, 1)
     assert (p["vec_elems"], p["tile_a"], p["tile_b"], p["grid"]) == (8, 256, 128, 512), p
@@ -567,6 +570,7 @@ def test_plan_workgroup_order(monkeypatch):
             (8184, 8184, 2): 4, (8224, 8224, 2): 4, (4100, 4100, 4): 4, (8256, 8256, 2): 1,  # near 16 KiB
             (8193, 8193, 2): 4, (8196, 8196, 2): 4, (12289, 12289, 2): 4, (8188, 8188, 2): 0,  # past 8 KiB
             (8193, 4097, 4): 4, (4097, 2049, 2): 4,  # both pitches past 8 KiB, or one past and one small
+            (6144, 6144, 1): 2, (11264, 11264, 1): 2, (8184, 8184, 1): 2,  # 1-byte, 8-byte chunks: order 2
             (8192, 8192, 1): 2,  # 256 x 128 tiles (8-byte chunks), 32 a-tiles <= 64 b-tiles
             (2048, 32768, 1): 4,  # 64 a-tiles > 8 b-tiles
             (8192, 4096, 8): 2, (4096, 4096, 16): 4, (8192, 8192, 4): 4}

@@ -289,7 +289,9 @@ typedef struct {
   int32_t b2_mode;     /* transpose: mode continuing b_mode in dst, grouped with it, else -1 */
   int32_t block;       /* threads per workgroup */
   int32_t streaming;   /* 1 if loads and stores are non-temporal: by default when the source
-                          plus destination bytes reach 256 MiB, the last-level cache size */
+                          plus destination bytes reach 256 MiB, the last-level cache size,
+                          except for element tiles (transposes of rows without aligned
+                          16-byte chunks), which keep ordinary accesses at any size */
   int32_t order;       /* transpose: workgroup -> tile order (0 a-tiles fastest, 1 b-tiles
                           fastest, 2 diagonal with a fastest, 3 diagonal over 4 x 4 tile groups,
                           4 diagonal with b fastest); -1 on other paths */
@@ -297,8 +299,10 @@ typedef struct {
                           (staged and transpose paths) */
   int32_t load_policy;  /* cache-policy bits of the source loads: 0 plain, 2 non-temporal */
   int32_t store_policy; /* of the destination stores: 0 plain, 2 non-temporal, 18 non-temporal
-                           with the sc1 scope bit (the LDS transpose's streaming stores, as
-                           buffer stores, when a tile's destination span is under 4 GiB) */
+                           with the sc1 scope bit (streaming 16-byte stores issued as buffer
+                           stores: the LDS transpose when a tile's destination span is under
+                           4 GiB; the vector path, the narrow interleave and the channel
+                           shuffle when the destination's is) */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */

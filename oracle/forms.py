@@ -45,8 +45,18 @@ def interleave_cm(src: np.ndarray, b: int, h: int, s: int, d: int) -> np.ndarray
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
 
 
-def nhwc2nchw(src: np.ndarray, n: int, h: int, w: int, c: int) -> np.ndarray:
-    x = src.view(np.uint16).reshape(n, h, w, c).transpose(0, 3, 1, 2)
+_UINT = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}
+
+
+def nhwc2nchw(src: np.ndarray, n: int, h: int, w: int, c: int, eb: int = 2) -> np.ndarray:
+    """(n,h,w,c) contiguous -> (n,c,h,w) contiguous, elements of eb bytes."""
+    x = src.view(_UINT[eb]).reshape(n, h, w, c).transpose(0, 3, 1, 2)
+    return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
+
+
+def nchw2nhwc(src: np.ndarray, n: int, h: int, w: int, c: int, eb: int = 2) -> np.ndarray:
+    """(n,c,h,w) contiguous -> (n,h,w,c) contiguous, elements of eb bytes."""
+    x = src.view(_UINT[eb]).reshape(n, c, h, w).transpose(0, 2, 3, 1)
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
 
 

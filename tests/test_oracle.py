@@ -533,6 +533,51 @@ def test_copy_holes_keep_sentinel_and_permutation():
     assert sorted(ov[sorted(image)].tolist()) == sorted(src.view(np.uint16).tolist())
 
 
+def test_copy_sampled_check_counts_planted_mismatches():
+    # The sampled checker against a destination built by NumPy's transpose, not by
+    # the oracle: index k of (48,48):(48,1) -> (48,48):(1,48) is (i, j) = (k % 48,
+    # k // 48) colex, read at 48 i + j and written at i + 48 j.
+    n = 48
+    rng = np.random.default_rng(11)
+    src = rng.integers(0, 1 << 16, n * n, dtype=np.uint16)
+    good = np.full(n * n + 16, 0xA5A5, np.uint16)  # 16 words past the image: holes
+    good[: n * n] = src.reshape(n, n).T.reshape(-1)
+    Ls, Ld = O.parse("(48,48):(48,1)"), O.parse("(48,48):(1,48)")
+    ks = rng.choice(n * n, 300, replace=False)
+
+    def check(dst):
+        return O.copy_sampled_check(src.view(np.uint8), Ls, dst.view(np.uint8), Ld, 2, ks)
+
+    assert check(good) == 0
+    holes = good.copy()
+    holes[n * n:] = 0x1234  # bytes outside the image are not the checker's business
+    assert check(holes) == 0
+    bad = good.copy()
+    planted = ks[[0, 5, 17, 99, 150, 222, 299]]
+    for k in planted:
+        bad[(k % n) + n * (k // n)] ^= 0x0100  # one flipped bit at a sampled destination
+    assert check(bad) == len(planted)
+    # a wrong element at an index outside the sample is not counted
+    outside = np.setdiff1d(np.arange(n * n), ks)[:5]
+    for k in outside:
+        bad[(k % n) + n * (k // n)] ^= 0x0001
+    assert check(bad) == len(planted)
+    # every sampled index wrong: the count is the sample size
+    assert check(np.zeros_like(good)) == int(np.count_nonzero(src[(ks % n) * n + ks // n] != 0))
+    # a swizzled destination: the checker must apply the swizzle (Sw<3,0,3> on an 8x8
+    # row-major tile puts (r, c) at 8 r + (c ^ r), [print_layout page, section 4.3])
+    s8 = rng.integers(0, 1 << 32, 64, dtype=np.uint32)
+    d8 = np.empty(64, np.uint32)
+    for r in range(8):
+        for c in range(8):
+            d8[8 * r + (c ^ r)] = s8[8 * r + c]
+    Lrow, Lsw = O.parse("(8,8):(8,1)"), O.parse("Sw<3,0,3> o (8,8):(8,1)")
+    all64 = np.arange(64)
+    assert O.copy_sampled_check(s8.view(np.uint8), Lrow, d8.view(np.uint8), Lsw, 4, all64) == 0
+    # the unswizzled destination differs wherever c ^ r != c, i.e. in every row but 0
+    assert O.copy_sampled_check(s8.view(np.uint8), Lrow, s8.view(np.uint8), Lsw, 4, all64) == 56
+
+
 def test_copy_bits_survive():
     # NaN payloads, infinities, subnormals: bytes move unchanged
     src = np.array([0x7E01, 0xFC00, 0x0001, 0x8000, 0x7FFF, 0xFFFF], np.uint16).view(np.uint8)
@@ -622,6 +667,17 @@ def test_forms_equal_oracle_copy():
         w = W.small(name)
         src, out = _run(w)
         assert np.array_equal(form(src), out), name
+    # the channel shuffles at other element sizes, both directions
+    rng = np.random.default_rng(12)
+    for eb in (1, 4, 8):
+        n, h, wd, c = 2, 5, 6, 3
+        hw = h * wd
+        nhwc = O.parse(f"({n},{h},{wd},{c}):({hw * c},{wd * c},{c},1)")
+        nchw = O.parse(f"({n},{h},{wd},{c}):({hw * c},{wd},1,{hw})")
+        src = rng.integers(0, 256, n * hw * c * eb, dtype=np.uint8)
+        blank = np.zeros_like(src)
+        assert np.array_equal(F.nhwc2nchw(src, n, h, wd, c, eb), O.copy(src, nhwc, blank, nchw, eb)), eb
+        assert np.array_equal(F.nchw2nhwc(src, n, h, wd, c, eb), O.copy(src, nchw, blank, nhwc, eb)), eb
 
 
 def test_shard_pack_exchange_reassembles_the_transpose():

@@ -1,26 +1,39 @@
 """Benchmark of the layout-remapping copy on one MI355X.
 
 One step is one pass of the whole hot path over one batch of synthetic input: a
-single lr_layout_copy of the fp16 8192 x 8192 transpose
-(8192,8192):(8192,1) -> (8192,8192):(1,8192) -- plan, launch, kernel.  Inputs are
-resident in HBM before the timed region.  Steps rotate over several source /
-destination buffer pairs (>= 1 GiB together) so that no step finds its data in
-the 256 MB Infinity Cache left there by the step before.
+single lr_layout_copy (plan, launch, kernel) of the largest configuration, the
+bf16 head interleave (16,32,4096,128) contiguous -> head pairs adjacent at stride
+1, 512 MiB read and 512 MiB written.  Inputs are resident in HBM before the timed
+region.  Steps rotate over source / destination buffer pairs (>= 1 GiB together)
+so that no step finds its data in the 256 MB Infinity Cache left there by the step
+before.
 
 Prints one JSON line.  `value` is effective GB/s = (bytes read + bytes written) /
-time, with algorithmic bytes 2 * N * elem_bytes per step.  The `roofline` object
-reports the dominant kernel's average duration from HIP events recorded on the
-launch stream over the timed region; `cpu_baseline` times the CPU oracle on a
-bounded slice of the same workload.  `workloads` adds the other large layouts
-(each timed the same way) for reference.
+wall time of K back-to-back steps, with algorithmic bytes 2 * N * elem_bytes per
+step.  `roofline` reports the copy kernel's average duration from HIP events
+recorded on the launch stream over the timed region; `cpu_baseline` times the CPU
+oracle on a bounded slice of the same workload.  `workloads` gives every other
+large layout the same treatment (its own roofline and its own same-size copy
+ceiling: the library's contiguous copy of the same bytes on the same buffers).
+
+Other modes (for rocprofv3 runs and their summaries under profiles/):
+  --counters            launch each large workload a few times, then a plain
+                        256 MiB copy whose counters scale FETCH_SIZE / WRITE_SIZE
+  --summarize-counters DIR_FETCH DIR_WRITE [DIR_LDS]
+                        read rocprofv3 --pmc CSV output and write profiles/traffic.json
+  --summarize-trace DIR read rocprofv3 --kernel-trace --stats CSV output and print
+                        a markdown table of per-kernel average durations
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -29,6 +42,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
+
+HEADLINE = "interleave"
+OTHERS = ("transpose", "retile", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw")
+# traffic.json keys: workload name + element type
+DTYPE_NAME = {"transpose": "fp16", "retile": "bf16", "interleave": "bf16", "interleave_cm": "bf16",
+              "nhwc2nchw": "fp16", "padtiles": "fp32", "shard_pack": "fp16", "rgb_nhwc2nchw": "fp16"}
 
 
 def _kernel_hash() -> str:
@@ -47,7 +66,11 @@ def _kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload_key: str):
+def _traffic_key(name: str, w) -> str:
+    return f"{w.name}_{DTYPE_NAME[name]}"
+
+
+def _traffic(key: str):
     """HBM bytes per launch measured by rocprofv3 counters (scaled by a plain copy
     of known size), if taken on the current kernel sources; else None."""
     path = os.path.join(PROFILES, "traffic.json")
@@ -55,15 +78,29 @@ def _traffic(workload_key: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    e = t.get(workload_key)
+    e = t.get(key)
     if not e or e.get("kernel_hash") != _kernel_hash():
         return None
     return e.get("bytes_per_launch")
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ----------------------------------------------------------------------------
+# timing helpers
+# ----------------------------------------------------------------------------
 def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
-    """Back-to-back copies rotating over buffer pairs; returns (ms per step, ms per
-    kernel from HIP events on the launch stream)."""
+    """Back-to-back copies rotating over buffer pairs; returns (ms per step of wall
+    time, ms per step from HIP events recorded on the launch stream)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         s, d = pairs[i % len(pairs)]
@@ -83,9 +120,9 @@ def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
 
 
 def _per_launch(lr, torch, pairs, Ls, Ld, eb, launches, flags=0, rotate=True):
-    """Kernel time of each launch (HIP events around it on the launch stream), in us:
-    rotating over the buffer pairs (cold: nothing cached from the previous launch)
-    or on the first pair only (warm: the last-level cache may hold the data)."""
+    """Kernel time of each launch (HIP events around it on the launch stream), in us,
+    sorted: rotating over the buffer pairs (cold: nothing cached from the previous
+    launch) or on the first pair only (warm: the last-level cache may hold data)."""
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
     s, d = pairs[0]
@@ -115,76 +152,119 @@ def _pairs(torch, dev, nbytes_src, nbytes_dst, first_src=None, min_total=1 << 30
     return out
 
 
-def _cpu_baseline(w, seconds: float):
-    """The oracle's copy (as it stands) on the first rows of the same transpose,
-    repeated until about `seconds` of CPU time; GB/s on algorithmic bytes."""
+def measure(lr, torch, dev, name, W, steps, warmup, flags=0, first_src=None):
+    """Times one workload: the copy over rotating buffers (wall and HIP-event time
+    per step), cold and warm per-launch times, and the library's contiguous copy of
+    the same bytes on the same buffers (the ceiling a copy without any remapping
+    reaches at this size)."""
+    w = W.full(name)
+    eb = w.elem_bytes
+    plan = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, eb, flags)
+    pairs = _pairs(torch, dev, w.src_elems * eb, w.dst_elems * eb, first_src=first_src)
+    nbytes = W.bytes_moved(w)
+    wall_ms, kern_ms = _time_copies(lr, torch, pairs, w.src_layout, w.dst_layout, eb, steps, warmup, flags)
+    cold = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, eb, steps, flags)
+    warm = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, eb, steps, flags, rotate=False)
+    n16 = nbytes // 2 // 16  # the same bytes each way, as 16-byte units
+    _, copy_ms = _time_copies(lr, torch, pairs, f"{n16}:1", f"{n16}:1", 16, steps, warmup)
+    del pairs
+    torch.cuda.empty_cache()
+    gbps = nbytes / (kern_ms * 1e-3) / 1e9
+    copy_gbps = nbytes / (copy_ms * 1e-3) / 1e9
+    wm = warm[len(warm) // 2]
+    return {
+        "w": w, "plan": plan, "bytes": nbytes, "wall_ms": wall_ms, "kern_ms": kern_ms,
+        "entry": {
+            "path": plan["path"],
+            "us": round(kern_ms * 1e3, 2),
+            "GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "copy_GBps": round(copy_gbps, 1),
+            "frac_of_copy": round(gbps / copy_gbps, 4),
+            "us_cold_median": round(cold[len(cold) // 2], 2),
+            "us_cold_best": round(cold[0], 2),
+            "us_warm_median": round(wm, 2),
+            "GBps_warm": round(nbytes / (wm * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": _traffic(_traffic_key(name, w))},
+        },
+    }
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# ----------------------------------------------------------------------------
+def _cpu_baseline(seconds: float):
+    """The oracle's copy on a slice of the head interleave: batch 0, heads 0..3 (two
+    head pairs), every (s, d) -- 2^21 elements, contiguous on both sides, so the
+    slice is its own source and destination buffer.  Repeated until about `seconds`
+    of work on one thread, then on every host thread at once (each thread its own
+    destination, the same sample)."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
     import workloads as W
 
-    n = 8192
-    rows = 512
-    src = W.make_src(w)
-    dst = W.make_dst(w)
-    Ls = oracle.parse(f"({rows},{n}):({n},1)")   # rows [0, 512) of the source, all columns
-    Ld = oracle.parse(f"({rows},{n}):(1,{n})")   # their transposed destinations
-    done, t0 = 0, time.perf_counter()
-    while True:
-        dst = oracle.copy(src, Ls, dst, Ld, w.elem_bytes)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    bytes_ = 2 * rows * n * w.elem_bytes * done
-    out = {
-        "value": round(bytes_ / dt / 1e9, 4),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"oracle.copy of rows 0..{rows - 1} of the 8192x8192 fp16 transpose "
-                  f"({rows}x{n} elements), {done} repetitions in {dt:.1f} s, single NumPy thread",
-    }
-    # the same sample on every host thread at once (each thread its own destination)
-    import concurrent.futures as cf
+    hs, s, d = 4, 4096, 128
+    n = hs * s * d
+    w = W.full(HEADLINE)
+    src = W.gen_normal_bf16(n, w.seed)  # the first 2^21 elements of the full source
+    Ls = oracle.parse(f"({hs},{s},{d}):({s * d},{d},1)")
+    Ld = oracle.parse(f"((2,{hs // 2}),{s},{d}):((1,{2 * s * d}),{2 * d},2)")
+    sample = (f"oracle.copy of batch 0, heads 0..3 of the (16,32,4096,128) bf16 head interleave "
+              f"({n} elements, {2 * n * 2} bytes moved per repetition)")
 
+    def run_for(dst, t_end):
+        k = 0
+        while True:
+            oracle.copy(src, Ls, dst, Ld, 2)
+            k += 1
+            if time.perf_counter() >= t_end:
+                return k
+
+    dst0 = np.full(n * 2, 0xA5, np.uint8)
+    t0 = time.perf_counter()
+    reps1 = run_for(dst0, t0 + seconds)
+    dt1 = time.perf_counter() - t0
+    single = 2 * n * 2 * reps1 / dt1 / 1e9
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    out = {"value": round(single, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{sample}; {reps1} repetitions in {dt1:.1f} s on one thread",
+           "cpu_model": _cpu_model(), "host_threads_available": len(os.sched_getaffinity(0))}
     if threads > 1:
-        dsts = [W.make_dst(w) for _ in range(threads)]
-
-        def work(i):
-            k, t1 = 0, time.perf_counter()
-            while True:
-                oracle.copy(src, Ls, dsts[i], Ld, w.elem_bytes)
-                k += 1
-                if time.perf_counter() - t1 >= seconds:
-                    return k
-
+        dsts = [np.full(n * 2, 0xA5, np.uint8) for _ in range(threads)]
         t0 = time.perf_counter()
         with cf.ThreadPoolExecutor(threads) as ex:
-            counts = list(ex.map(work, range(threads)))
+            counts = list(ex.map(lambda i: run_for(dsts[i], t0 + seconds), range(threads)))
         dt = time.perf_counter() - t0
-        out["parallel"] = {"value": round(2 * rows * n * w.elem_bytes * sum(counts) / dt / 1e9, 4), "cores": threads,
-                           "sample": f"the same sample, {sum(counts)} repetitions over {threads} threads in {dt:.1f} s"}
-    del np
+        par = 2 * n * 2 * sum(counts) / dt / 1e9
+        out.update({"value": round(par, 4), "cores": threads,
+                    "sample": f"{sample}; {sum(counts)} repetitions over {threads} threads in {dt:.1f} s "
+                              "(NumPy releases the GIL in its indexing)",
+                    "single_thread": {"value": round(single, 4), "cores": 1,
+                                      "sample": f"{reps1} repetitions in {dt1:.1f} s"}})
     return out
 
 
+# ----------------------------------------------------------------------------
+# rocprofv3 helpers
+# ----------------------------------------------------------------------------
 def counters_run(lr, torch, W, reps: int = 3):
     """Launch sequence for rocprofv3 runs (kernel trace or --pmc): each large
     workload `reps` times after one warm-up, then a plain contiguous copy of
     256 MiB (the reference of known size that scales FETCH_SIZE / WRITE_SIZE)."""
     dev = torch.device("cuda:0")
-    names = ("transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw")
-    for name in names:
+    for name in (HEADLINE,) + OTHERS:
         w = W.full(name)
         s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)
         d = torch.empty(w.dst_elems * w.elem_bytes, dtype=torch.uint8, device=dev)
         for _ in range(reps + 1):
             lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=w.elem_bytes)
         torch.cuda.synchronize()
-        print(f"counters: {name} grid={lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)['grid']}",
-              flush=True)
+        grid = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)["grid"]
+        print(f"counters: {_traffic_key(name, w)} grid={grid}", flush=True)
         del s, d
     n = 256 << 20
     s = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
@@ -192,23 +272,107 @@ def counters_run(lr, torch, W, reps: int = 3):
     for _ in range(reps + 1):
         lr.layout_copy(s, f"{n // 16}:1", d, f"{n // 16}:1", elem_bytes=16)
     torch.cuda.synchronize()
-    print(f"counters: plain copy {n} bytes grid={lr.copy_plan(f'{n // 16}:1', n // 16, f'{n // 16}:1', n // 16, 16)['grid']}",
+    print(f"counters: plain_copy_256MiB grid={lr.copy_plan(f'{n // 16}:1', n // 16, f'{n // 16}:1', n // 16, 16)['grid']}",
           flush=True)
 
 
+def _csv_rows(directory: str, suffix: str):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _pmc_per_dispatch(directory: str, counter: str):
+    """{dispatch id: (kernel name, grid size, counter value)} from a --pmc run."""
+    out = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        did = int(r["Dispatch_Id"])
+        val = float(r["Counter_Value"])
+        name = r.get("Kernel_Name", "")
+        grid = int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0)
+        k, g, v = out.get(did, (name, grid, 0.0))
+        out[did] = (k, g, v + val)  # per-XCD / per-instance rows add up
+    return out
+
+
+def summarize_counters(d_fetch: str, d_write: str, d_lds: str = None) -> None:
+    """Turns the counter runs of `bench.py --counters` into profiles/traffic.json:
+    per workload, HBM bytes per launch = counter KiB x 1024 x (what the same counter
+    reads for the plain 256 MiB copy, scaled to its known 256 MiB)."""
+    fetch = _pmc_per_dispatch(d_fetch, "FETCH_SIZE")
+    write = _pmc_per_dispatch(d_write, "WRITE_SIZE")
+    lds = _pmc_per_dispatch(d_lds, "SQ_LDS_BANK_CONFLICT") if d_lds else {}
+    lds_act = _pmc_per_dispatch(d_lds, "SQ_LDS_IDX_ACTIVE") if d_lds else {}
+    order = [_traffic_key(n, __import__("workloads").full(n)) for n in (HEADLINE,) + OTHERS] + ["plain_copy_256MiB"]
+
+    def groups(d):
+        # dispatches in launch order, grouped 4 per workload (warm-up + 3)
+        ids = sorted(d)
+        per = len(ids) // len(order)
+        return {order[i]: [d[x] for x in ids[i * per:(i + 1) * per]] for i in range(len(order))}
+
+    gf, gw = groups(fetch), groups(write)
+    gl, ga = (groups(lds), groups(lds_act)) if lds else ({}, {})
+    ref = 256 << 20
+    f_scale = ref / (sum(v for _, _, v in gf["plain_copy_256MiB"]) / len(gf["plain_copy_256MiB"]) * 1024)
+    w_scale = ref / (sum(v for _, _, v in gw["plain_copy_256MiB"]) / len(gw["plain_copy_256MiB"]) * 1024)
+    out = {"_scale": {"fetch": round(f_scale, 4), "write": round(w_scale, 4),
+                      "reference": "plain contiguous copy of 256 MiB each way"}}
+    for key in order:
+        f = [v for _, _, v in gf[key]]
+        wv = [v for _, _, v in gw[key]]
+        rd = sum(f) / len(f) * 1024 * f_scale
+        wr = sum(wv) / len(wv) * 1024 * w_scale
+        e = {"bytes_per_launch": int(round(rd + wr)), "read": int(round(rd)), "write": int(round(wr)),
+             "kernel_hash": _kernel_hash(), "kernel": gf[key][0][0], "fetch_kib": round(sum(f) / len(f)),
+             "write_kib": round(sum(wv) / len(wv))}
+        if gl:
+            e["lds_bank_conflict_cycles"] = round(sum(v for _, _, v in gl[key]) / len(gl[key]))
+            e["lds_active_cycles"] = round(sum(v for _, _, v in ga[key]) / len(ga[key]))
+        out[key] = e
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def summarize_trace(directory: str) -> None:
+    """Markdown table of per-kernel call counts and durations from a
+    rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    print("| kernel | calls | avg us | min us | max us |")
+    print("|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+
+# ----------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--path", default=None, help="force a copy path (for experiments)")
     ap.add_argument("--counters", action="store_true",
                     help="only launch each large workload a few times (for rocprofv3 runs)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR")
+    ap.add_argument("--summarize-trace", metavar="DIR")
     args = ap.parse_args()
 
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the copy is measured on a single "
                                    "MI355X; --gpus must be 1"}), flush=True)
@@ -232,40 +396,14 @@ def main():
     if args.path:
         flags = lr.COPY_FORCE_PATH({v: k for k, v in lr.binding.PATH_NAMES.items()}[args.path])
 
-    # ---- headline: fp16 8192 x 8192 transpose
-    w = W.full("transpose")
-    src0 = torch.from_numpy(W.make_src(w)).to(dev)
-    pairs = _pairs(torch, dev, w.src_elems * 2, w.dst_elems * 2, first_src=src0)
-    plan = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2, flags)
-    bytes_step = W.bytes_moved(w)
-    torch.cuda.synchronize()
-    wall_ms, kern_ms = _time_copies(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, args.warmup, flags)
-    value = bytes_step / (wall_ms * 1e-3) / 1e9
-    achieved = bytes_step / (kern_ms * 1e-3) / 1e9
-    # per-launch kernel times after the timed region: cold (rotating) and warm (one pair)
-    cold = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, flags)
-    warm = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, 2, args.steps, flags, rotate=False)
-
-    # the library's own contiguous copy (16 bytes per lane) of equal bytes on the same
-    # rotating buffers: what a copy without any remapping reaches at this size here
-    n16 = bytes_step // 2 // 16
-    _, copy_ms = _time_copies(lr, torch, pairs, f"{n16}:1", f"{n16}:1", 16, args.steps, args.warmup)
-    copy_kernel = bytes_step / (copy_ms * 1e-3) / 1e9
-
-    # same-box device-to-device copy of equal bytes, for context
-    a, b = pairs[0][0], pairs[1][1]
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(20):
-        pairs[(i + 1) % len(pairs)][1].copy_(pairs[i % len(pairs)][0])
-    e1.record()
-    torch.cuda.synchronize()
-    d2d = bytes_step / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
-    del pairs, src0, a, b
+    # ---- headline: the (16,32,4096,128) bf16 head interleave
+    src0 = torch.from_numpy(W.make_src(W.full(HEADLINE))).to(dev)
+    h = measure(lr, torch, dev, HEADLINE, W, args.steps, args.warmup, flags, first_src=src0)
+    del src0
     torch.cuda.empty_cache()
+    w = h["w"]
+    value = h["bytes"] / (h["wall_ms"] * 1e-3) / 1e9
+    e = h["entry"]
 
     out = {
         "metric": "layout_copy effective GB/s (read+write) and % of HBM peak on 1 MI355X",
@@ -274,54 +412,35 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 5),
+        "ms_per_step": round(h["wall_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u16",
         "data": "synthetic",
         "config": {
-            "workload": "transpose fp16 8192x8192: (8192,8192):(8192,1) -> (8192,8192):(1,8192)",
-            "path": plan["path"],
-            "vec_elems": plan["vec_elems"],
-            "bytes_per_step": bytes_step,
+            "workload": "head interleave bf16 (16,32,4096,128): (16,32,4096,128):(16777216,524288,128,1) -> "
+                        "(16,(2,16),4096,128):(16777216,(1,1048576),256,2)",
+            "path": h["plan"]["path"],
+            "vec_elems": h["plan"]["vec_elems"],
+            "bytes_per_step": h["bytes"],
             "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
-            "d2d_copy_GBps": round(d2d, 1),
-            "frac_of_d2d_copy": round(value / d2d, 4),
-            "copy_kernel_GBps": round(copy_kernel, 1),
-            "kernel_frac_of_copy_kernel": round(achieved / copy_kernel, 4),
+            "copy_kernel_GBps": e["copy_GBps"],
+            "kernel_frac_of_copy_kernel": e["frac_of_copy"],
             "buffers": "rotating pairs, >= 1 GiB in total",
-            "kernel_us": {"median": round(cold[len(cold) // 2], 2), "best": round(cold[0], 2),
-                          "warm_median": round(warm[len(warm) // 2], 2), "warm_best": round(warm[0], 2),
+            "kernel_us": {"timed_region_mean": e["us"], "cold_median": e["us_cold_median"],
+                          "cold_best": e["us_cold_best"], "warm_median": e["us_warm_median"],
                           "warm": "one buffer pair repeated, the last-level cache may hold part of it"},
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": _traffic("transpose8192_fp16"),
-        },
+        "roofline": e["roofline"],
     }
 
-    # ---- the other large remapping copies, timed the same way
+    # ---- every other large remapping copy, each with its own roofline and ceiling
     if not args.no_others:
         others = {}
-        for name in ("retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw"):
-            wo = W.full(name)
-            p = lr.copy_plan(wo.src_layout, wo.src_elems, wo.dst_layout, wo.dst_elems, wo.elem_bytes)
-            prs = _pairs(torch, dev, wo.src_elems * wo.elem_bytes, wo.dst_elems * wo.elem_bytes)
-            steps = max(10, args.steps)
-            _, km = _time_copies(lr, torch, prs, wo.src_layout, wo.dst_layout, wo.elem_bytes, steps, args.warmup)
-            gb = W.bytes_moved(wo) / (km * 1e-3) / 1e9
-            warm = _per_launch(lr, torch, prs, wo.src_layout, wo.dst_layout, wo.elem_bytes, steps, rotate=False)
-            wm = warm[len(warm) // 2]
-            others[wo.name] = {"path": p["path"], "us": round(km * 1e3, 2), "GBps": round(gb, 1),
-                               "hbm_frac": round(gb / HBM_PEAK_GBPS, 4), "us_warm_median": round(wm, 2),
-                               "GBps_warm": round(W.bytes_moved(wo) / (wm * 1e-6) / 1e9, 1)}
-            del prs
-            torch.cuda.empty_cache()
+        for name in OTHERS:
+            r = measure(lr, torch, dev, name, W, max(20, args.steps), args.warmup)
+            others[r["w"].name] = r["entry"]
         # latency-only cases: the aliased 8x8 tile copy and two 64-index evaluations
         # (per-launch HIP events, median of 50; these are launch-bound)
         w1 = W.tile8x8()
@@ -352,21 +471,20 @@ def main():
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
         ev_out = [lr.layout_eval(ev_layout, n=n_ev) for _ in range(2)]
         torch.cuda.synchronize()
-        times = []
         for i, (e0, e1) in enumerate(evs):
             e0.record(stream)
             ev_out[i % 2] = lr.layout_eval(ev_layout, n=n_ev)
             e1.record(stream)
         torch.cuda.synchronize()
         t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
-        others["eval 2^27 of a 16384x8192 retile layout"] = {"us_median": round(t[len(t) // 2], 1),
-                                             "Gindex_per_s": round(n_ev / (t[len(t) // 2] * 1e-6) / 1e9, 1),
-                                             "GBps_written": round(8 * n_ev / (t[len(t) // 2] * 1e-6) / 1e9, 1)}
+        others["eval 2^27 of a 16384x8192 retile layout"] = {
+            "us_median": round(t[len(t) // 2], 1), "Gindex_per_s": round(n_ev / (t[len(t) // 2] * 1e-6) / 1e9, 1),
+            "GBps_written": round(8 * n_ev / (t[len(t) // 2] * 1e-6) / 1e9, 1)}
         del ev_out
         out["workloads"] = others
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = _cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

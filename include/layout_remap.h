@@ -147,6 +147,23 @@ int lr_right_inverse(const lr_layout* in, lr_layout* out);
  * n_m, else LR_ERR_NOT_REPRESENTABLE. */
 int lr_zipped_divide(const lr_layout* in, const int64_t* tiler, int32_t ntiler, lr_layout* out);
 
+/* Slice ([CuTe algebra page, section 3.2]: one tile of a zipped_divide is the
+ * layout with the rest mode fixed at the tile's coordinate and the tile mode left
+ * free): fix some coordinates of L, keep the others.  coord has ncoord entries:
+ * ncoord == nmodes gives one integer per top-level mode (-1 keeps the whole mode,
+ * otherwise a 1-D index within the mode, split colexicographically over its
+ * leaves); ncoord == nleaves gives one per leaf (-1 keeps the leaf, otherwise its
+ * coordinate).  *out receives the kept leaves, in order, grouped by the top-level
+ * mode they came from -- when only one such group is left, each of its leaves is a
+ * top-level mode of its own (the tile of a zipped_divide keeps its 2-D shape); 1:0
+ * when nothing is kept -- and *offset the offset the fixed
+ * coordinates contribute, so that L(c) = *offset + out(c') for every c whose fixed
+ * entries equal coord (c' its kept part).  A swizzled L keeps its swizzle when
+ * *offset is a multiple of 2^(M+S+B) (the swizzle then acts on the kept part
+ * alone); otherwise LR_ERR_NOT_REPRESENTABLE.  A coordinate out of range gives
+ * LR_ERR_INVALID. */
+int lr_slice(const lr_layout* L, const int64_t* coord, int32_t ncoord, lr_layout* out, int64_t* offset);
+
 /* Complement of A up to size M ([CuTe algebra page, section 3.2]: what a tile
  * leaves over): with A's leaves of extent > 1 and stride > 0 sorted by stride,
  * each stride must be a multiple of the previous leaf's extent * stride
@@ -288,10 +305,11 @@ typedef struct {
   int32_t b_mode;      /* joint mode contiguous in dst (transpose/interleave), else -1 */
   int32_t b2_mode;     /* transpose: mode continuing b_mode in dst, grouped with it, else -1 */
   int32_t block;       /* threads per workgroup */
-  int32_t streaming;   /* 1 if loads and stores are non-temporal: by default when the source
-                          plus destination bytes reach 256 MiB, the last-level cache size,
-                          except for element tiles (transposes of rows without aligned
-                          16-byte chunks), which keep ordinary accesses at any size */
+  int32_t streaming;   /* 1 if stores (and loads, see load_policy) are non-temporal: by
+                          default when the source plus destination bytes reach 64 MiB, a
+                          quarter of the 256 MiB last-level cache, except for element tiles
+                          (transposes of rows without aligned 16-byte chunks), which keep
+                          ordinary accesses at any size */
   int32_t order;       /* transpose: workgroup -> tile order (0 a-tiles fastest, 1 b-tiles
                           fastest, 2 diagonal with a fastest, 3 diagonal over 4 x 4 tile groups,
                           4 diagonal with b fastest); -1 on other paths */
@@ -303,6 +321,11 @@ typedef struct {
                            stores: the LDS transpose when a tile's destination span is under
                            4 GiB; the vector path, the narrow interleave and the channel
                            shuffle when the destination's is) */
+  int32_t vector_order; /* vector/generic: traversal after the common contiguous mode (0
+                           destination order, 1 source order, 2 source order in blocks of
+                           destination runs); -1 on other paths */
+  int32_t gather_chunks; /* staged: destination chunks of one tile per 32-lane slice of the
+                            gather (a slice covers 32 / gather_chunks tiles); -1 elsewhere */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */
@@ -320,6 +343,43 @@ typedef struct {
 int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align,
                  const lr_layout* Ld, int64_t dst_capacity_elems, size_t dst_align,
                  size_t elem_bytes, uint32_t flags, lr_plan* out);
+
+/* Overrides of the planner's launch choices, for measurement and tests.  A field
+ * of -1 leaves the choice to the planner (lr_copy_tuning_init sets every field to
+ * -1); any other value is used where the chosen path has that knob and ignored
+ * elsewhere.  No override changes what is copied, only how: every combination the
+ * planner accepts gives the same destination bytes.  A value the path cannot honour
+ * (a tile shape whose exchange does not fit the LDS, say) falls back to the
+ * planner's choice; a value outside the listed range gives LR_ERR_INVALID. */
+typedef struct {
+  int32_t load_policy;     /* 0 plain loads, 2 non-temporal */
+  int32_t store_policy;    /* 0 plain stores, 2 non-temporal, 18 non-temporal with the sc1 scope
+                              bit where the kernel issues buffer stores (else as 2).  A load
+                              policy different from the store policy is available on the
+                              generic and vector paths only (elsewhere: LR_ERR_PATH) */
+  int32_t units_per_lane;  /* generic/vector: 1 or 4 */
+  int32_t vector_order;    /* vector: modes after the common contiguous one walked in 0
+                              destination order, 1 source order, 2 source order in blocks
+                              of destination runs (see lr_plan.order) */
+  int32_t interleave_form; /* interleave: 0 one chunk per lane per head, 1 one destination
+                              chunk per lane from narrow loads, 2 the channel shuffle */
+  int32_t tile_shape;      /* transpose: 0..6, the tile shapes of lr_plan.tile_a/tile_b */
+  int32_t tile_order;      /* transpose: 0..4, as lr_plan.order */
+  int32_t element_tiles;   /* transpose: 0 chunk tiles, 1 element-granular tiles */
+  int32_t direct_loads;    /* staged and LDS transpose: 0 through registers, 1 global -> LDS */
+  int32_t gather_chunks;   /* staged: destination chunks of one tile per 32-lane slice of
+                              the gather (1, 2, 4, 8, 16 or 32; see lr_plan.gather_chunks) */
+  int32_t reserved[6];     /* must be -1 or 0 */
+} lr_copy_tuning;
+
+/* Every field of *t to -1 (the planner's choices). */
+void lr_copy_tuning_init(lr_copy_tuning* t);
+
+/* lr_copy_plan / lr_layout_copy with overrides; tuning == NULL is the same as
+ * lr_copy_plan / lr_layout_copy. */
+int lr_copy_plan_tuned(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align,
+                       const lr_layout* Ld, int64_t dst_capacity_elems, size_t dst_align,
+                       size_t elem_bytes, uint32_t flags, const lr_copy_tuning* tuning, lr_plan* out);
 
 /* --------------------------------------------------------------- device */
 
@@ -359,6 +419,10 @@ int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, 
 int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
                    void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
                    size_t elem_bytes, uint32_t flags, void* stream);
+
+int lr_layout_copy_tuned(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
+                         void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
+                         size_t elem_bytes, uint32_t flags, const lr_copy_tuning* tuning, void* stream);
 
 /* ------------------------------------------------------------------ misc */
 

@@ -84,6 +84,8 @@ class lr_plan(ctypes.Structure):
         ("direct", ctypes.c_int32),
         ("load_policy", ctypes.c_int32),
         ("store_policy", ctypes.c_int32),
+        ("vector_order", ctypes.c_int32),
+        ("gather_chunks", ctypes.c_int32),
         ("tile_a", ctypes.c_int64),
         ("tile_b", ctypes.c_int64),
         ("grid", ctypes.c_int64),
@@ -93,6 +95,39 @@ class lr_plan(ctypes.Structure):
         ("s_src", ctypes.c_int64 * (2 * MAX_LEAVES)),
         ("s_dst", ctypes.c_int64 * (2 * MAX_LEAVES)),
     ]
+
+
+class lr_copy_tuning(ctypes.Structure):
+    _fields_ = [
+        ("load_policy", ctypes.c_int32),
+        ("store_policy", ctypes.c_int32),
+        ("units_per_lane", ctypes.c_int32),
+        ("vector_order", ctypes.c_int32),
+        ("interleave_form", ctypes.c_int32),
+        ("tile_shape", ctypes.c_int32),
+        ("tile_order", ctypes.c_int32),
+        ("element_tiles", ctypes.c_int32),
+        ("direct_loads", ctypes.c_int32),
+        ("gather_chunks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 6),
+    ]
+
+
+TUNING_FIELDS = tuple(k for k, _ in lr_copy_tuning._fields_ if k != "reserved")
+
+
+def _tuning(tuning):
+    """A dict of lr_copy_tuning fields (unnamed ones stay -1: the planner's choice)
+    -> a pointer for the C call, or None."""
+    if not tuning:
+        return None
+    t = lr_copy_tuning()
+    lib().lr_copy_tuning_init(ctypes.byref(t))
+    for k, v in tuning.items():
+        if k not in TUNING_FIELDS:
+            raise KeyError(f"unknown tuning field {k!r}")
+        setattr(t, k, int(v))
+    return ctypes.byref(t)
 
 
 WAVE_LANES = 64
@@ -141,6 +176,7 @@ _SIGS = {
     "lr_right_inverse": (ctypes.c_int, [_L, _L]),
     "lr_zipped_divide": (ctypes.c_int, [_L, _P(ctypes.c_int64), ctypes.c_int32, _L]),
     "lr_complement": (ctypes.c_int, [_L, ctypes.c_int64, _L]),
+    "lr_slice": (ctypes.c_int, [_L, _P(ctypes.c_int64), ctypes.c_int32, _L, _P(ctypes.c_int64)]),
     "lr_logical_divide": (ctypes.c_int, [_L, _L, _L]),
     "lr_logical_product": (ctypes.c_int, [_L, _L, _L]),
     "lr_blocked_product": (ctypes.c_int, [_L, _L, _L]),
@@ -154,11 +190,16 @@ _SIGS = {
                                        ctypes.c_int32, ctypes.c_int32, _P(lr_access_report)]),
     "lr_copy_plan": (ctypes.c_int, [_L, ctypes.c_int64, ctypes.c_size_t, _L, ctypes.c_int64, ctypes.c_size_t,
                                     ctypes.c_size_t, ctypes.c_uint32, _P(lr_plan)]),
+    "lr_copy_tuning_init": (None, [_P(lr_copy_tuning)]),
+    "lr_copy_plan_tuned": (ctypes.c_int, [_L, ctypes.c_int64, ctypes.c_size_t, _L, ctypes.c_int64, ctypes.c_size_t,
+                                          ctypes.c_size_t, ctypes.c_uint32, _P(lr_copy_tuning), _P(lr_plan)]),
     "lr_layout_eval": (ctypes.c_int, [_L, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "lr_layout_eval_coords": (ctypes.c_int, [_L, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                              ctypes.c_void_p]),
     "lr_layout_copy": (ctypes.c_int, [ctypes.c_void_p, _L, ctypes.c_int64, ctypes.c_void_p, _L, ctypes.c_int64,
                                       ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
+    "lr_layout_copy_tuned": (ctypes.c_int, [ctypes.c_void_p, _L, ctypes.c_int64, ctypes.c_void_p, _L, ctypes.c_int64,
+                                            ctypes.c_size_t, ctypes.c_uint32, _P(lr_copy_tuning), ctypes.c_void_p]),
     "lr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "lr_last_hip_error": (ctypes.c_char_p, []),
     "lr_version": (ctypes.c_char_p, []),
@@ -332,6 +373,18 @@ def complement(A, M: int) -> Layout:
     return Layout(out)
 
 
+def slice(L, coord: Sequence[int]):
+    """lr_slice: (the layout of the kept coordinates, the offset of the fixed ones).
+    coord: one entry per top-level mode or per leaf, -1 (or None) keeping it."""
+    L = _as_layout(L)
+    vals = [-1 if c is None else int(c) for c in coord]
+    arr = (ctypes.c_int64 * max(1, len(vals)))(*vals)
+    out = lr_layout()
+    off = ctypes.c_int64()
+    _check(lib().lr_slice(ctypes.byref(L.c), arr, len(vals), ctypes.byref(out), ctypes.byref(off)), "slice")
+    return Layout(out), off.value
+
+
 def _binary(name: str, A, B) -> Layout:
     out = lr_layout()
     _check(getattr(lib(), name)(ctypes.byref(_as_layout(A).c), ctypes.byref(_as_layout(B).c), ctypes.byref(out)),
@@ -412,16 +465,20 @@ def access_check(L, elem_bytes: int, lanes: int = WAVE_LANES, op: str = "read", 
 
 
 def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, flags: int = 0,
-              src_align: int = 16, dst_align: int = 16) -> dict:
+              src_align: int = 16, dst_align: int = 16, tuning: Optional[dict] = None) -> dict:
+    """The plan lr_layout_copy would launch (host only).  ``tuning``: a dict of
+    lr_copy_tuning fields overriding the planner's launch choices."""
     p = lr_plan()
-    _check(lib().lr_copy_plan(ctypes.byref(_as_layout(Ls).c), src_capacity, src_align, ctypes.byref(_as_layout(Ld).c),
-                              dst_capacity, dst_align, elem_bytes, flags, ctypes.byref(p)), "copy_plan")
+    _check(lib().lr_copy_plan_tuned(ctypes.byref(_as_layout(Ls).c), src_capacity, src_align,
+                                    ctypes.byref(_as_layout(Ld).c), dst_capacity, dst_align, elem_bytes, flags,
+                                    _tuning(tuning), ctypes.byref(p)), "copy_plan")
     r = p.joint_rank
     return {
         "path": PATH_NAMES[p.path], "elem_bytes": p.elem_bytes, "vec_elems": p.vec_elems, "wide": bool(p.wide),
         "a_mode": p.a_mode, "b_mode": p.b_mode, "b2_mode": p.b2_mode, "block": p.block,
         "streaming": bool(p.streaming), "order": p.order, "direct": bool(p.direct),
         "load_policy": p.load_policy, "store_policy": p.store_policy,
+        "vector_order": p.vector_order, "gather_chunks": p.gather_chunks,
         "tile_a": p.tile_a, "tile_b": p.tile_b,
         "grid": p.grid, "n_elems": p.n_elems, "blocks": p.blocks,
         "joint": [(p.ext[i], p.s_src[i], p.s_dst[i]) for i in range(r)],
@@ -485,9 +542,12 @@ def layout_eval_coords(L, coords, stream=None):
     return out
 
 
-def layout_copy(src, Ls, dst, Ld, elem_bytes: Optional[int] = None, flags: int = 0, stream=None):
+def layout_copy(src, Ls, dst, Ld, elem_bytes: Optional[int] = None, flags: int = 0, stream=None,
+                tuning: Optional[dict] = None):
     """dst[Ld(k)] = src[Ls(k)] for every k, on the GPU; src and dst are contiguous
-    GPU tensors viewed as flat element buffers of ``elem_bytes`` bytes."""
+    GPU tensors viewed as flat element buffers of ``elem_bytes`` bytes.  ``tuning``:
+    a dict of lr_copy_tuning fields overriding the planner's launch choices (the
+    result is the same bytes)."""
     _device_tensor(src, "src")
     _device_tensor(dst, "dst")
     if src.device != dst.device:
@@ -498,6 +558,29 @@ def layout_copy(src, Ls, dst, Ld, elem_bytes: Optional[int] = None, flags: int =
     db = dst.numel() * dst.element_size()
     if sb % eb or db % eb:
         raise ValueError("buffer sizes are not multiples of elem_bytes")
-    _check(lib().lr_layout_copy(src.data_ptr(), ctypes.byref(Ls.c), sb // eb, dst.data_ptr(), ctypes.byref(Ld.c),
-                                db // eb, eb, flags, _stream_ptr(stream)), "layout_copy")
+    if tuning:
+        rc = lib().lr_layout_copy_tuned(src.data_ptr(), ctypes.byref(Ls.c), sb // eb, dst.data_ptr(),
+                                        ctypes.byref(Ld.c), db // eb, eb, flags, _tuning(tuning), _stream_ptr(stream))
+    else:
+        rc = lib().lr_layout_copy(src.data_ptr(), ctypes.byref(Ls.c), sb // eb, dst.data_ptr(), ctypes.byref(Ld.c),
+                                  db // eb, eb, flags, _stream_ptr(stream))
+    _check(rc, "layout_copy")
     return dst
+
+
+def copy_tuning_init() -> dict:
+    """lr_copy_tuning_init: every override at -1 (the planner's choices), as a dict."""
+    t = lr_copy_tuning()
+    lib().lr_copy_tuning_init(ctypes.byref(t))
+    return {k: getattr(t, k) for k in TUNING_FIELDS}
+
+
+def copy_plan_tuned(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, tuning: dict, flags: int = 0,
+                    src_align: int = 16, dst_align: int = 16) -> dict:
+    """lr_copy_plan_tuned: copy_plan with overrides."""
+    return copy_plan(Ls, src_capacity, Ld, dst_capacity, elem_bytes, flags, src_align, dst_align, tuning=tuning)
+
+
+def layout_copy_tuned(src, Ls, dst, Ld, tuning: dict, elem_bytes: Optional[int] = None, flags: int = 0, stream=None):
+    """lr_layout_copy_tuned: layout_copy with overrides."""
+    return layout_copy(src, Ls, dst, Ld, elem_bytes, flags, stream, tuning=tuning)

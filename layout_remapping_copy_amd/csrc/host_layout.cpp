@@ -563,6 +563,65 @@ int lr_zipped_divide(const lr_layout* in, const int64_t* tiler, int32_t ntiler, 
   return LR_OK;
 }
 
+int lr_slice(const lr_layout* L, const int64_t* coord, int32_t ncoord, lr_layout* out, int64_t* offset) {
+  int rc = validate(L);
+  if (rc) return rc;
+  if (!coord || !out || !offset) return LR_ERR_INVALID;
+  if (ncoord != L->nmodes && ncoord != L->nleaves) return LR_ERR_INVALID;
+  const bool per_mode = ncoord == L->nmodes;  // the same reading when every mode is one leaf
+  std::vector<Leaf> kept;
+  std::vector<int> ends;
+  int64_t off = 0;
+  int lo = 0;
+  for (int m = 0; m < L->nmodes; ++m) {
+    const int hi = L->mode_end[m];
+    bool any = false;
+    if (per_mode && coord[m] == -1) {
+      for (int i = lo; i < hi; ++i) kept.push_back({L->shape[i], L->stride[i]});
+      any = true;
+    } else if (per_mode) {
+      // one integer for the whole mode, split colexicographically over its leaves
+      int64_t c = coord[m], size = 1;
+      for (int i = lo; i < hi; ++i) size *= L->shape[i];
+      if (c < 0 || c >= size) return LR_ERR_INVALID;
+      for (int i = lo; i < hi; ++i) {
+        off += (c % L->shape[i]) * L->stride[i];
+        c /= L->shape[i];
+      }
+    } else {
+      for (int i = lo; i < hi; ++i) {
+        if (coord[i] == -1) {
+          kept.push_back({L->shape[i], L->stride[i]});
+          any = true;
+        } else if (coord[i] < 0 || coord[i] >= L->shape[i]) {
+          return LR_ERR_INVALID;
+        } else {
+          off += coord[i] * L->stride[i];
+        }
+      }
+    }
+    if (any) ends.push_back((int)kept.size());
+    lo = hi;
+  }
+  if (kept.empty()) {
+    kept.push_back({1, 0});
+    ends.push_back(1);
+  } else if (ends.size() == 1) {
+    // one mode survives: its leaves are the result's modes (tile (3,5) of the
+    // zipped_divide is a 4 x 8 layout of its own)
+    ends.clear();
+    for (size_t i = 0; i < kept.size(); ++i) ends.push_back((int)i + 1);
+  }
+  // The swizzle reads bits [M+S, M+S+B) and rewrites bits [M, M+B) of the whole
+  // offset; a base that is a multiple of 2^(M+S+B) leaves all of them to the kept
+  // part, so Sw(base + o) = base + Sw(o).  Any other base: not a layout plus offset.
+  if (L->swz_b > 0 && off % (int64_t(1) << (L->swz_m + L->swz_s + L->swz_b)) != 0)
+    return LR_ERR_NOT_REPRESENTABLE;
+  set_leaves(out, kept, ends, L->swz_b, L->swz_m, L->swz_s);
+  *offset = off;
+  return LR_OK;
+}
+
 int lr_complement(const lr_layout* A, int64_t M, lr_layout* out) {
   int rc = validate(A);
   if (rc) return rc;

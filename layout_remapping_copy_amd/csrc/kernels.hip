@@ -32,6 +32,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -351,13 +352,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int UB, bool WIDE, int U, bool NT>
+// LNT / SNT: non-temporal loads / stores (chosen apart: a source read once with a
+// destination that should stay cached for its next reader).
+template <int UB, bool WIDE, int U, bool LNT, bool SNT>
 __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
   static_assert(U == 1 || U == 4, "one or four units per lane");
   using T = typename Raw<UB>::T;
   const T* __restrict__ src = (const T*)a.src;
   T* __restrict__ dst = (T*)a.dst;
-  if constexpr (NT && UB == 16 && U == 1 && !WIDE) {
+  if constexpr (SNT && UB == 16 && U == 1 && !WIDE) {
     if (a.bufst) {
       // Streaming stores as buffer stores with the nt and sc1 policy bits (measured
       // faster than nt alone on large copies); the host checks that every
@@ -368,7 +371,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
         if (i0 < a.n_units) {
           uint64_t s0, d0;
           generic_offsets<false>(a, i0, &s0, &d0);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, gload<NT, T>(src + s0)),
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, gload<LNT, T>(src + s0)),
                                                  rd, (uint32_t)(d0 * 16), 0, kPolicyNtSc1);
         }
       }
@@ -381,7 +384,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
       if (i0 < a.n_units) {
         uint64_t s0, d0;
         generic_offsets<WIDE>(a, i0, &s0, &d0);
-        gstore<NT, T>(dst + d0, gload<NT, T>(src + s0));
+        gstore<SNT, T>(dst + d0, gload<LNT, T>(src + s0));
       }
     } else {
       uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, d0 = 0, d1 = 0, d2 = 0, d3 = 0;
@@ -392,14 +395,14 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
       if (k2) generic_offsets<WIDE>(a, i0 + 512, &s2, &d2);
       if (k3) generic_offsets<WIDE>(a, i0 + 768, &s3, &d3);
       T v0, v1, v2, v3;
-      if (k0) v0 = gload<NT, T>(src + s0);
-      if (k1) v1 = gload<NT, T>(src + s1);
-      if (k2) v2 = gload<NT, T>(src + s2);
-      if (k3) v3 = gload<NT, T>(src + s3);
-      if (k0) gstore<NT, T>(dst + d0, v0);
-      if (k1) gstore<NT, T>(dst + d1, v1);
-      if (k2) gstore<NT, T>(dst + d2, v2);
-      if (k3) gstore<NT, T>(dst + d3, v3);
+      if (k0) v0 = gload<LNT, T>(src + s0);
+      if (k1) v1 = gload<LNT, T>(src + s1);
+      if (k2) v2 = gload<LNT, T>(src + s2);
+      if (k3) v3 = gload<LNT, T>(src + s3);
+      if (k0) gstore<SNT, T>(dst + d0, v0);
+      if (k1) gstore<SNT, T>(dst + d1, v1);
+      if (k2) gstore<SNT, T>(dst + d2, v2);
+      if (k3) gstore<SNT, T>(dst + d3, v3);
     }
   }
 }
@@ -1094,14 +1097,17 @@ struct ChanArgs {
 
 // A 16-byte streaming store: a buffer store with the nt and sc1 bits from `base`
 // when `buf` (the host has checked the 4 GiB span), else a global store.
+// The byte offset is 64-bit: a destination may span more than 4 GiB (element
+// offsets stay under 2^31, bytes do not); only the buffer store, whose span the
+// host has checked, narrows it to its 32-bit offset.
 template <bool NT, typename C>
-__device__ __forceinline__ void store16(char* base, uint32_t byte_off, const C& v, bool buf) {
+__device__ __forceinline__ void store16(char* base, size_t byte_off, const C& v, bool buf) {
   static_assert(sizeof(C) == 16, "16-byte chunks");
   if constexpr (NT) {
     if (buf) {
       const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(base, 0, -1, kBufferWord3);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, v), rd, byte_off, 0,
-                                             kPolicyNtSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, v), rd,
+                                             (uint32_t)byte_off, 0, kPolicyNtSc1);
       return;
     }
   }
@@ -1163,7 +1169,7 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
 #pragma unroll
     for (int e = 0; e < C * V; ++e) out[e % C].e[e / C] = in[e / V].e[e % V];  // element e: pixel e / C, channel e % C
 #pragma unroll
-    for (int c = 0; c < C; ++c) store16<NT>(dst, (c * t.plane + p0 + V * l + bd) * EB, out[c], t.bufst);
+    for (int c = 0; c < C; ++c) store16<NT>(dst, (size_t)(c * t.plane + p0 + V * l + bd) * EB, out[c], t.bufst);
   } else {
     if (mine) {
       Ch in[C], out[C];
@@ -1175,10 +1181,10 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
       for (int j = 0; j < C; ++j) lds[l * C + j] = out[j];
     }
     __syncthreads();
-    const uint32_t db = (p0 * C + bd) * EB;
+    const size_t db = (size_t)(p0 * C + bd) * EB;
 #pragma unroll
     for (int j = 0; j < C; ++j)
-      if (l + 256u * j < nblk * C) store16<NT>(dst, db + (l + 256u * j) * 16, lds[l + 256u * j], t.bufst);
+      if (l + 256u * j < nblk * C) store16<NT>(dst, db + (size_t)(l + 256u * j) * 16, lds[l + 256u * j], t.bufst);
   }
 }
 
@@ -1319,6 +1325,7 @@ struct StagedArgs {
   uint32_t K;                          // tiles per workgroup
   uint32_t cpt;                        // 16-byte dst chunks per tile (power of two <= 256)
   uint32_t cpt_shift;                  // log2(cpt)
+  uint32_t cps_shift;                  // log2 of the chunks per 32-lane slice of the gather
   uint32_t tgroups;
   FD fd_tg;
   BatchArg batch;
@@ -1386,8 +1393,14 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   }
   __syncthreads();
 
-  // this lane's chunk position inside a tile is fixed (cpt divides 256)
-  const uint32_t c = threadIdx.x & (t.cpt - 1);
+  // Gather grouping: the 32-lane slice q = idx / 32 covers 32 / cps tiles x cps
+  // chunks of each (tile (q / slices) * (32 / cps) + l / cps, chunk (q % slices) * cps
+  // + l % cps, l = idx % 32, slices = cpt / cps); the planner picks cps from the LDS
+  // bank model.  slices divides 8, so this lane's chunk position is the same in
+  // every round of 256 jobs.
+  const uint32_t slice_shift = t.cpt_shift - t.cps_shift, g_shift = 5u - t.cps_shift;
+  const uint32_t c = (((threadIdx.x >> 5) & ((1u << slice_shift) - 1u)) << t.cps_shift) +
+                     (threadIdx.x & ((1u << t.cps_shift) - 1u));
   uint32_t g[V];
 #pragma unroll
   for (int x = 0; x < V; ++x) {
@@ -1402,7 +1415,7 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   const T* ldsT = (const T*)lds;
   const uint32_t nstore = t.K * t.cpt;
   for (uint32_t idx = threadIdx.x; idx < nstore; idx += 256) {
-    uint32_t kk = idx >> t.cpt_shift;
+    const uint32_t kk = (((idx >> 5) >> slice_shift) << g_shift) + ((idx & 31u) >> t.cps_shift);
     uint32_t tile = t0 + kk;
     if (tile >= t.T) continue;
     C o;
@@ -1459,22 +1472,27 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int ski
   }
 }
 
-template <int UB, bool NT>
+template <int UB, bool LNT, bool SNT>
 static void launch_generic_nt(const GenericArgs& a, bool wide, int unroll, unsigned grid, hipStream_t st) {
   if (wide)
-    hipLaunchKernelGGL((k_generic<UB, true, 4, NT>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, true, 4, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
   else if (unroll == 1)
-    hipLaunchKernelGGL((k_generic<UB, false, 1, NT>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, false, 1, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_generic<UB, false, 4, NT>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_generic<UB, false, 4, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
 }
 
 template <int UB>
-static void launch_generic(const GenericArgs& a, bool wide, int unroll, bool nt, unsigned grid, hipStream_t st) {
-  if (nt)
-    launch_generic_nt<UB, true>(a, wide, unroll, grid, st);
+static void launch_generic(const GenericArgs& a, bool wide, int unroll, bool nt_ld, bool nt_st, unsigned grid,
+                           hipStream_t st) {
+  if (nt_ld && nt_st)
+    launch_generic_nt<UB, true, true>(a, wide, unroll, grid, st);
+  else if (nt_ld)
+    launch_generic_nt<UB, true, false>(a, wide, unroll, grid, st);
+  else if (nt_st)
+    launch_generic_nt<UB, false, true>(a, wide, unroll, grid, st);
   else
-    launch_generic_nt<UB, false>(a, wide, unroll, grid, st);
+    launch_generic_nt<UB, false, false>(a, wide, unroll, grid, st);
 }
 
 template <int EB>
@@ -1671,7 +1689,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.n_chunks = (p.n_units + 256 * p.unroll - 1) / (256 * p.unroll);
       a.bufst = p.bufst ? 1u : 0u;
       const int ub = p.v * p.eb;
-      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.nt, grid, st));
+      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.nt_ld, p.nt, grid, st));
       return check_launch();
     }
     case LR_PATH_DUAL:
@@ -1807,6 +1825,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.K = (uint32_t)p.staged_K;
       a.cpt = (uint32_t)p.staged_cpt;
       while ((1u << a.cpt_shift) < a.cpt) ++a.cpt_shift;
+      while ((int64_t(1) << a.cps_shift) < p.staged_cps) ++a.cps_shift;
       a.tgroups = (uint32_t)((tm.ext + p.staged_K - 1) / p.staged_K);
       a.fd_tg = fd_of(a.tgroups);
       std::memset(&a.batch, 0, sizeof(a.batch));
@@ -1834,6 +1853,37 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
     }
   }
   return LR_ERR_PATH;
+}
+
+// LR_LOG=1 (read once): every lr_layout_copy prints its plan to stderr -- path,
+// element and unit sizes, tiles, grid, policies and the joint modes -- the
+// library's counterpart of printing a layout's thread-to-offset map
+// ([ThreadMap page, section 5.3]).  It changes nothing else.
+static bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("LR_LOG");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+static void log_plan(const Plan& p, int64_t blocks) {
+  static const char* names[] = {"generic", "vector", "transpose", "interleave", "staged",
+                                "dual", "alias", "transpose_direct", "deinterleave"};
+  char modes[1024];
+  int at = 0;
+  for (int k = 0; k < p.rank && at < (int)sizeof(modes) - 64; ++k)
+    at += std::snprintf(modes + at, sizeof(modes) - at, "%s(%lld:%lld:%lld)", k ? " " : "", (long long)p.m[k].ext,
+                        (long long)p.m[k].ss, (long long)p.m[k].sd);
+  if (at == 0) modes[0] = 0;
+  std::fprintf(stderr,
+               "lr plan: path=%s elem_bytes=%d vec=%d wide=%d a=%d b=%d b2=%d tile=%lldx%lld shape=%d order=%d "
+               "block=%d grid=%lld blocks=%lld nt_load=%d nt_store=%d sc1=%d direct=%d elem_tiles=%d "
+               "vorder=%d gather_chunks=%lld joint=[%s]\n",
+               p.path >= 0 && p.path <= 8 ? names[p.path] : "?", p.eb, p.v, p.wide ? 1 : 0, p.a, p.b, p.b2,
+               (long long)p.tile_a, (long long)p.tile_b, p.tshape, (int)p.torder, p.block, (long long)p.grid,
+               (long long)blocks, p.nt_ld ? 1 : 0, p.nt ? 1 : 0, (p.nt && p.bufst) ? 1 : 0, p.direct ? 1 : 0,
+               p.tel ? 1 : 0, p.vorder, (long long)p.staged_cps, modes);
 }
 
 static int fill_eval(EvalArgs* a, const lr_layout* L) {
@@ -1917,10 +1967,17 @@ int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, 
 
 int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst, const lr_layout* Ld,
                    int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags, void* stream) {
+  return lr_layout_copy_tuned(src, Ls, src_capacity_elems, dst, Ld, dst_capacity_elems, elem_bytes, flags, nullptr,
+                              stream);
+}
+
+int lr_layout_copy_tuned(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst,
+                         const lr_layout* Ld, int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags,
+                         const lr_copy_tuning* tuning, void* stream) {
   if (!src || !dst) return LR_ERR_INVALID;
   Plan p;
   int rc = plan_copy(Ls, src_capacity_elems, ptr_align(src), Ld, dst_capacity_elems, ptr_align(dst), elem_bytes,
-                     flags, &p);
+                     flags, tuning, &p);
   if (rc) return rc;
   // storage overlap: [src, src + cap*eb) vs [dst, dst + cap*eb)
   const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
@@ -1929,7 +1986,9 @@ int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_el
   if (s0 < d1 && d0 < s1) return LR_ERR_OVERLAP;
   if ((rc = verify_plan(p, src_capacity_elems, dst_capacity_elems))) return rc;
   int64_t cext[kMaxJoint], nblocks = 0;
-  if (!block_extents(p, flags, cext, &nblocks)) return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
+  const bool cut = block_extents(p, flags, cext, &nblocks);
+  if (log_enabled()) log_plan(p, cut ? nblocks : 1);
+  if (!cut) return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
   // too large for 32-bit offsets: blocks of the joint modes, each within 32 bits,
   // launched one after another on the stream (disjoint parts of an injective copy)
   int64_t start[kMaxJoint] = {0};
@@ -1941,10 +2000,11 @@ int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_el
     char* d = (char*)dst + od * (int64_t)elem_bytes;
     const int64_t cs = cosize_bound(&ls), cd = cosize_bound(&ld);
     Plan pb;
-    if ((rc = plan_copy(&ls, cs, ptr_align(s), &ld, cd, ptr_align(d), elem_bytes, flags, &pb))) return rc;
+    if ((rc = plan_copy(&ls, cs, ptr_align(s), &ld, cd, ptr_align(d), elem_bytes, flags, tuning, &pb))) return rc;
     if (pb.wide) return LR_ERR_PATH;
-    pb.nt = p.nt && pb.path != LR_PATH_DUAL && pb.path != LR_PATH_ALIAS;  // the whole copy's policy
+    inherit_policy(p, &pb);  // the whole copy's load and store policies
     if ((rc = verify_plan(pb, cs, cd))) return rc;
+    if (log_enabled() && blk == 0) log_plan(pb, -1);
     if ((rc = run_copy(s, &ls, d, &ld, pb, (hipStream_t)stream))) return rc;
     for (int k = 0; k < p.rank; ++k) {  // next block, mode 0 fastest
       start[k] += cext[k];

@@ -17,8 +17,8 @@
 // staging).
 
 #include <algorithm>
-#include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 
 #include "lr_internal.h"
 
@@ -122,15 +122,24 @@ static int64_t unit_width(const Plan& p, size_t align_s, size_t align_d) {
   return v;
 }
 
-static bool env_flag(const char* name) {
-  const char* e = std::getenv(name);
-  return e && *e && std::strcmp(e, "0") != 0;
-}
+// An override of lr_copy_tuning, or the planner's own choice when it is -1.
+static int32_t knob(int32_t v, int32_t dflt) { return v < 0 ? dflt : v; }
 
-static uint32_t env_u32(const char* name, uint32_t dflt) {
-  const char* e = std::getenv(name);
-  if (!e || !*e) return dflt;
-  return (uint32_t)std::strtoul(e, nullptr, 0);
+static bool tuning_valid(const lr_copy_tuning& t) {
+  auto in = [](int32_t v, std::initializer_list<int32_t> ok) {
+    if (v == -1) return true;
+    for (int32_t o : ok)
+      if (v == o) return true;
+    return false;
+  };
+  if (!in(t.load_policy, {0, 2}) || !in(t.store_policy, {0, 2, 18}) || !in(t.units_per_lane, {1, 4}) ||
+      !in(t.vector_order, {0, 1, 2}) || !in(t.interleave_form, {0, 1, 2}) ||
+      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6}) || !in(t.tile_order, {0, 1, 2, 3, 4}) ||
+      !in(t.element_tiles, {0, 1}) || !in(t.direct_loads, {0, 1}) || !in(t.gather_chunks, {1, 2, 4, 8, 16, 32}))
+    return false;
+  for (int32_t r : t.reserved)
+    if (r != -1 && r != 0) return false;
+  return true;
 }
 
 // One past the highest destination byte the joint modes reach (a destination
@@ -167,21 +176,132 @@ static bool plan_chan_elements(Plan* p, int a, int b, bool interleave, size_t sr
   return true;
 }
 
+// The staged gather's lane grouping.  Job idx (one 16-byte destination chunk) of a
+// workgroup belongs to 32-lane slice q = idx / 32; a slice covers G = 32 / cps
+// tiles x cps chunks of each: tile (q / slices) * G + l / cps, chunk (q % slices) * cps
+// + l % cps with l = idx % 32 and slices = cpt / cps.  With cps = min(cpt, 32) this is
+// tile idx / cpt, chunk idx % cpt.  Each lane gathers its chunk's V elements from the
+// staged footprint one LDS read at a time; the LDS serves the lanes of a slice
+// together ([print_layout page, sections 4.3 and 5.2]: distinct words in one bank are
+// served one after another), so the grouping decides the bank conflicts.  The planner
+// evaluates the gfx950 bank model over every wave of one workgroup's first round for
+// each admissible cps and keeps the cheapest, the widest on a tie (longer contiguous
+// destination runs per store instruction).
+static int64_t staged_gather_cps(const Plan& p, int inner, int64_t cpt, int64_t K, int64_t Fc) {
+  const int V = 16 / p.eb;
+  int64_t g[16];  // element offset in the footprint of element x of chunk c: filled per c
+  auto offs = [&](int64_t c, int64_t* out) {
+    for (int x = 0; x < V; ++x) {
+      int64_t e = c * V + x, off = 0;
+      for (int k = 0; k < inner; ++k) {
+        off += (e % p.m[k].ext) * p.m[k].ss;
+        e /= p.m[k].ext;
+      }
+      out[x] = off;
+    }
+  };
+  int32_t banks, lpp;
+  gfx950_lds_model((size_t)p.eb, false, &banks, &lpp);
+  const int64_t dflt = std::min<int64_t>(cpt, 32);
+  int64_t best = dflt, best_cost = -1;
+  for (int64_t cps = dflt; cps >= 1; cps >>= 1) {
+    const int64_t slices = cpt / cps, G = 32 / cps;
+    // a lane's chunk stays fixed across rounds (slices | 8); a narrower grouping
+    // needs whole groups of G tiles (the default one is tile idx / cpt for any K)
+    if (slices > 8 || 8 % slices || (cps != dflt && K % G)) continue;
+    int64_t cost = 0;
+    const int64_t jobs = std::min<int64_t>(256, K * cpt);
+    for (int64_t w0 = 0; w0 < jobs; w0 += 64) {
+      int64_t addr[16][64];
+      int lanes = (int)std::min<int64_t>(64, jobs - w0);
+      for (int l = 0; l < lanes; ++l) {
+        const int64_t idx = w0 + l, q = idx >> 5, li = idx & 31;
+        const int64_t kk = (q / slices) * G + li / cps, c = (q % slices) * cps + li % cps;
+        offs(c, g);
+        for (int x = 0; x < V; ++x) addr[x][l] = (kk * Fc * 16) + g[x] * p.eb;
+      }
+      for (int x = 0; x < V; ++x) cost += lds_cycles(addr[x], lanes, p.eb, banks, lpp, nullptr, nullptr);
+    }
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = cps;
+    }
+  }
+  return best;
+}
+
 static int plan_alias(Plan* p, int64_t n, int64_t cos_s, int64_t cos_d) {
   const int64_t win = 8192;  // dst offsets owned by one workgroup (LDS owner table)
   int64_t windows = (cos_d + win - 1) / win;
   if (cos_d > (int64_t(1) << 26) || n >= (int64_t(1) << 31) || cos_s >= (int64_t(1) << 31)) return LR_ERR_ALIAS;
   if ((double)n * (double)windows > (double)(int64_t(1) << 36)) return LR_ERR_ALIAS;
   p->path = LR_PATH_ALIAS;
-  p->nt = false;  // plain accesses: every workgroup re-reads the source
+  p->nt = p->nt_ld = false;  // plain accesses: every workgroup re-reads the source
   p->alias_windows = windows;
   p->block = 1024;
   p->grid = windows;
   return LR_OK;
 }
 
-int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
-              size_t dst_align, size_t elem_bytes, uint32_t flags, Plan* p) {
+// Traversal order 2 of the vector path: the lanes of a wave walk the source's
+// order (after the common contiguous mode), the four waves of a workgroup the
+// destination's, and everything after that the source's again.  A workgroup then
+// reads a few long source runs and writes a few long destination runs, where either
+// order alone makes one side a scatter of short runs (the 128-byte tile rows of a
+// retile).  Modes are split where a wave or workgroup boundary falls inside one; a
+// mode that does not divide there is taken whole.  Any order of the joint modes is
+// the same copy when the destination is injective.
+static void block_vector_order(Plan* p) {
+  if (p->rank + 2 > kMaxKernelModes) {
+    std::stable_sort(p->m + 1, p->m + p->rank, [](const JMode& x, const JMode& y) {
+      return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
+    });
+    return;
+  }
+  JMode rest[kMaxJoint];
+  int nr = 0;
+  for (int k = 1; k < p->rank; ++k) rest[nr++] = p->m[k];
+  JMode out[kMaxJoint];
+  int no = 0;
+  out[no++] = p->m[0];
+  int64_t lanes = p->m[0].ext / p->v;  // units along the common mode
+  auto first = [&](bool by_src) {
+    int best = 0;
+    for (int k = 1; k < nr; ++k) {
+      const int64_t a = by_src ? rest[k].ss : rest[k].sd, b = by_src ? rest[best].ss : rest[best].sd;
+      if (a < b) best = k;
+    }
+    return best;
+  };
+  auto fill = [&](int64_t target, bool by_src) {
+    while (lanes < target && nr > 0) {
+      const int k = first(by_src);
+      const int64_t need = target / lanes;
+      JMode m = rest[k];
+      if (target % lanes == 0 && m.ext > need && m.ext % need == 0) {
+        out[no++] = {need, m.ss, m.sd};
+        rest[k] = {m.ext / need, m.ss * need, m.sd * need};
+        lanes *= need;
+      } else {
+        out[no++] = m;
+        lanes *= m.ext;
+        for (int j = k; j + 1 < nr; ++j) rest[j] = rest[j + 1];
+        --nr;
+      }
+    }
+  };
+  fill(64, true);    // a wave's lanes
+  fill(256, false);  // a workgroup's waves
+  std::stable_sort(rest, rest + nr, [](const JMode& x, const JMode& y) {
+    return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
+  });
+  for (int k = 0; k < nr; ++k) out[no++] = rest[k];
+  std::memcpy(p->m, out, sizeof(JMode) * no);
+  p->rank = no;
+}
+
+static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
+                     size_t dst_align, size_t elem_bytes, uint32_t flags, const lr_copy_tuning& tun, Plan* p) {
   int rc;
   if ((rc = validate(Ls))) return rc;
   if ((rc = validate(Ld))) return rc;
@@ -214,16 +334,24 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   p->wide = (flags & LR_COPY_WIDE_INDEX) || n >= lim32 || cos_s >= lim32 || cos_d >= lim32;
   p->block = 256;
   // Non-temporal loads and stores when the footprint (source plus destination
-  // bytes) is at least the 256 MiB last-level cache: nothing the copy touches can
-  // stay cached for a later reader, and streaming accesses measured 5-15 % faster
-  // on every large workload.  Smaller copies keep plain accesses, which leave the
-  // data cache-resident (measured faster when the copy's data is re-read).
-  // LR_NT=0/1 overrides.
-  const bool big_footprint = n >= (int64_t(128) << 20) / (int64_t)elem_bytes;
-  p->nt = env_u32("LR_NT", big_footprint ? 1u : 0u) != 0;
+  // bytes) is at least 64 MiB, a quarter of the 256 MiB last-level cache.  From
+  // there a copy from memory runs faster streaming: 5-15 % on every workload of
+  // 256 MiB and more, 7 % on the 64 MiB retile (13.6 against 14.6 us), whose plain
+  // stores would leave the result cached for a reader that follows at once (the
+  // caller can ask for that with the store policy).  Smaller copies keep plain
+  // accesses, which keep the data cache-resident.  An override of one of the two
+  // policies alone sets the other to match.  Stores carry the sc1 scope bit
+  // (buffer stores) where a kernel has them, unless the store policy asks for nt
+  // alone.
+  const bool big_footprint = n >= (int64_t(32) << 20) / (int64_t)elem_bytes;
+  const int32_t lp = tun.load_policy, sp = tun.store_policy;
+  p->nt_ld = lp >= 0 ? lp == 2 : (sp >= 0 ? sp != 0 : big_footprint);
+  p->nt = sp >= 0 ? sp != 0 : (lp >= 0 ? lp == 2 : big_footprint);
+  p->policy_set = lp >= 0 || sp >= 0;
+  const bool sc1_ok = sp != 2;
   // one unit per lane measured fastest for streaming copies on MI355X (more waves
-  // in flight beat more loads per wave); LR_UNROLL=4 selects four
-  p->unroll = env_u32("LR_UNROLL", 1) == 4 ? 4 : 1;
+  // in flight beat more loads per wave)
+  p->unroll = knob(tun.units_per_lane, 1);
 
   // --- non-injective destination: sequential semantics
   const bool inj = injective(Ld);
@@ -245,7 +373,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   if (!have_joint || forced == LR_PATH_DUAL || (have_joint && rank > kMaxKernelModes)) {
     if (forced >= 0 && forced != LR_PATH_DUAL) return LR_ERR_PATH;
     p->path = LR_PATH_DUAL;
-    p->nt = false;  // the per-element fallback keeps plain accesses
+    p->nt = p->nt_ld = false;  // the per-element fallback keeps plain accesses
     p->rank = 0;
     p->v = 1;
     p->n_units = n;
@@ -281,16 +409,21 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     // modes is the same copy when the destination is injective; walking the source
     // order (reads in long runs, writes in runs of the common mode) measured
     // faster than the destination order when the common run is short (the 128-byte
-    // rows of the 4096^2 retile).  LR_VORDER=0 keeps the destination order.
-    if (env_u32("LR_VORDER", 1) == 1 && p->rank > 2)
-      std::stable_sort(p->m + 1, p->m + p->rank, [](const JMode& x, const JMode& y) {
-        return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
-      });
+    // rows of the 4096^2 retile).
+    p->vorder = knob(tun.vector_order, 1);
+    if (p->vorder >= 1 && p->rank > 2) {
+      if (p->vorder == 2 && p->unroll == 1 && !p->wide)
+        block_vector_order(p);
+      else
+        std::stable_sort(p->m + 1, p->m + p->rank, [](const JMode& x, const JMode& y) {
+          return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
+        });
+    }
     // Streaming 16-byte units are stored as buffer stores with the nt and sc1
     // cache-policy bits (a 512 MiB copy: 6.41 -> 6.55 TB/s), addressed by one 32-bit
     // byte offset from the destination base: the destination's span must stay
     // under 4 GiB.  LR_SC1=0 keeps global stores.
-    p->bufst = p->v * p->eb == 16 && p->unroll == 1 && !p->wide && env_u32("LR_SC1", 1) != 0 &&
+    p->bufst = p->v * p->eb == 16 && p->unroll == 1 && !p->wide && sc1_ok &&
                dst_span_bytes(*p) < (int64_t(1) << 32);
     return LR_OK;
   }
@@ -328,7 +461,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     const int64_t nb = p->m[b].ext, V = V16;
     // NB a power of two: the register kernels; other NB from 3 to 8 (three colour
     // channels, say): the channel shuffle through LDS, which applies no swizzle
-    const uint32_t inarrow_env = env_u32("LR_INARROW", 1);
+    const int32_t inarrow_env = knob(tun.interleave_form, 1);
     const bool chan = chan_supported(p->eb, nb) && p->sw_s.b == 0 && p->sw_d.b == 0 &&
                       (!is_pow2(nb) || inarrow_env == 2);
     bool ok = (is_pow2(nb) || chan) && nb >= 2 && nb * p->eb <= 16 && p->m[a].sd == nb && p->m[a].ext % V == 0 &&
@@ -346,15 +479,14 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->v = (int)V;
       // one 16-byte store per lane from NB narrow loads measured faster (every store
       // instruction covers 1 KiB of contiguous dst; NB 16-byte stores per lane from NB
-      // wide loads write every NB-th chunk per instruction: 3.8 against 6.1 TB/s);
-      // LR_INARROW=0 selects the other
-      p->inarrow = chan ? 2 : (int)(inarrow_env & 1u);
+      // wide loads write every NB-th chunk per instruction: 3.8 against 6.1 TB/s)
+      p->inarrow = chan ? 2 : (int)(inarrow_env & 1);
       // a-elements per workgroup, matching the kernel's per-lane unroll (one dst
       // chunk per lane on the narrow variant, V pixels per lane on the shuffle)
       p->tile_a = p->inarrow == 2 ? 256 * V : p->inarrow ? 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
       // the narrow variant's streaming stores as buffer stores with the nt and sc1
       // bits from the destination base (head interleave 6.27 -> 6.55 TB/s)
-      p->bufst = p->inarrow != 0 && env_u32("LR_SC1", 1) != 0 && dst_span_bytes(*p) < (int64_t(1) << 32);
+      p->bufst = p->inarrow != 0 && sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
       p->tile_b = nb;
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
@@ -382,7 +514,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       p->v = (int)V;
       p->tile_a = 256 * V;  // pixels per workgroup (V per lane)
       p->tile_b = C;
-      p->bufst = env_u32("LR_SC1", 1) != 0 && dst_span_bytes(*p) < (int64_t(1) << 32);
+      p->bufst = sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
         if (k != a && k != b) batch *= p->m[k].ext;
@@ -426,7 +558,6 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     const bool long_b = ext_b * p->eb > 16 && p->m[a].ext * p->eb > 16;
     if (long_b || forced >= 0) {
       p->path = forced == LR_PATH_TRANSPOSE_DIRECT ? LR_PATH_TRANSPOSE_DIRECT : LR_PATH_TRANSPOSE;
-      if (forced < 0 && env_flag("LR_TRANSPOSE_DIRECT")) p->path = LR_PATH_TRANSPOSE_DIRECT;
       p->a = a;
       p->b = b;
       p->b2 = b2;
@@ -468,8 +599,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
           if (k != a && k != b && k != b2) tiles *= p->m[k].ext;
         if (tiles < 256) p->tshape = 4;
       }
-      const uint32_t shp = env_u32("LR_TSHAPE", 99);
-      if (shp < (uint32_t)kTileShapes) p->tshape = wide_ok ? (int)shp : 0;
+      if (tun.tile_shape >= 0) p->tshape = wide_ok ? tun.tile_shape : 0;
       // 16-element chunks (1-byte elements): the 32 x 32 and 64 x 16 tiles would
       // need 256 KiB of LDS; take the largest that fits
       if (!shape_fits(p->tshape, (int)V)) p->tshape = p->tshape == 6 ? 5 : 1;
@@ -483,11 +613,9 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // up to 8 bytes; 1-byte elements in chunks of 2 take them too (through the
       // windowed kernel below), in chunks of 4 or 8 keep the chunks (u8 8188^2 2.55
       // TB/s against 2.22-2.36, 8184^2 2.96 against 2.25-2.39).
-      // LR_TEL=0 keeps the narrow chunks, LR_TEL=1 forces element tiles.
-      const uint32_t tel_env = env_u32("LR_TEL", 2);
       const bool tel_wins = V <= 2 || p->eb >= 2;
       p->tel = p->path == LR_PATH_TRANSPOSE && V * p->eb < 16 && p->eb <= 8 &&
-               (tel_env == 1 || (tel_env == 2 && tel_wins));
+               (tun.element_tiles == 1 || (tun.element_tiles < 0 && tel_wins));
       if (p->tel) {
         p->v = 1;
         p->tshape = 0;
@@ -502,8 +630,7 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         // 2.78 -> 3.89; fp32 8191^2 3.22 -> 4.92; 8-byte 4095^2 3.57 -> 5.06; u8 16383^2
         // 2.08 -> 2.40.  Streaming accesses alone cost the per-element kernel 8-18 %.
         p->twin = !p->sw_s.b && !p->sw_d.b && src_align % (size_t)p->eb == 0 && dst_align % (size_t)p->eb == 0;
-        const char* nt_env = std::getenv("LR_NT");
-        if (!nt_env || !*nt_env) p->nt = false;  // LR_NT=0/1 still overrides
+        if (!p->policy_set) p->nt = p->nt_ld = false;  // an explicit policy still applies
       }
       // Workgroup order (measured on fp16, fp32, 1-, 8- and 16-byte transposes from
       // 2048 x 32768 to 16384^2).  b-tiles fastest by default: consecutive
@@ -554,11 +681,10 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
         else
           p->torder = 1u;  // (with a single a-tile, order 4 is order 1)
       }
-      const uint32_t tord = env_u32("LR_TORDER", 99);
-      if (tord <= 4) p->torder = tord;
+      if (tun.tile_order >= 0) p->torder = (uint32_t)tun.tile_order;
       // direct global -> LDS loads: full chunks, tiles 16 or 32 chunks wide along a
       // and at least 16 along b
-      p->direct = env_u32("LR_TDIRECT", 0) != 0 && p->path == LR_PATH_TRANSPOSE && V * p->eb == 16 &&
+      p->direct = tun.direct_loads == 1 && p->path == LR_PATH_TRANSPOSE && V * p->eb == 16 &&
                   p->tshape <= 3 && shape_fits(p->tshape, (int)V);
       // Streaming stores of the LDS tile transpose go out as buffer stores with the
       // nt and sc1 cache-policy bits: fp16 8192^2 5.62 -> 5.67 TB/s, the column-major
@@ -566,14 +692,14 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
       // 6.26 (the interleave and staged kernels measured slower with them, 1-1.5 %).
       // Buffer offsets are 32-bit: each workgroup stores relative to its tile's
       // lowest destination offset, so the tile's destination span must stay under
-      // 4 GiB.  LR_SC1=0 keeps global stores.
+      // 4 GiB.
       {
         // rounding the base down and swizzling the highest offset up each add less
         // than one swizzle block (2^(M+B) elements)
         const int64_t swz_blk = p->sw_d.b ? (int64_t(1) << (p->sw_d.m + p->sw_d.b)) : 0;
         const int64_t span = ((p->tile_a - 1) * p->m[a].sd + p->tile_b + 2 * swz_blk) * p->eb;
         p->bufst = p->path == LR_PATH_TRANSPOSE && !p->tel && !p->direct && V * p->eb == 16 &&
-                   span < (int64_t(1) << 32) && env_u32("LR_SC1", 1) != 0;
+                   span < (int64_t(1) << 32) && sc1_ok;
       }
       const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
       const int64_t ntb = (ext_b + p->tile_b - 1) / p->tile_b;
@@ -625,14 +751,19 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
           p->path = LR_PATH_STAGED;
           // direct global -> LDS loads measured 2.6 % faster on the padded tiles
           // (5.79 vs 5.64 TB/s): the footprint never passes through registers, so
-          // every load of it is in flight at once.  LR_DIRECT=0 selects the other.
-          p->direct = env_u32("LR_DIRECT", 1) != 0;
+          // every load of it is in flight at once.
+          p->direct = knob(tun.direct_loads, 1) != 0;
           p->staged_inner = inner;
           p->staged_P = P;
           p->staged_F = F;
           p->staged_Fc = Fc;
           p->staged_cpt = cpt;
           p->staged_K = K;
+          p->staged_cps = staged_gather_cps(*p, inner, cpt, K, Fc);
+          if (tun.gather_chunks > 0 && tun.gather_chunks <= cpt && cpt % tun.gather_chunks == 0 &&
+              8 % (cpt / tun.gather_chunks) == 0 &&
+              (tun.gather_chunks == std::min<int64_t>(cpt, 32) || K % (32 / tun.gather_chunks) == 0))
+            p->staged_cps = tun.gather_chunks;
           p->v = V16;
           p->tile_a = K;
           int64_t batch = 1;
@@ -667,8 +798,24 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
   p->n_units = ne / v;
   p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
   // 16-byte units (fused elements) take the vector path's buffer stores too
-  p->bufst = v * p->eb == 16 && p->unroll == 1 && !p->wide && env_u32("LR_SC1", 1) != 0 &&
-             dst_span_bytes(*p) < (int64_t(1) << 32);
+  p->bufst = v * p->eb == 16 && p->unroll == 1 && !p->wide && sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
+  return LR_OK;
+}
+
+int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
+              size_t dst_align, size_t elem_bytes, uint32_t flags, const lr_copy_tuning* tuning, Plan* p) {
+  lr_copy_tuning tun;
+  lr_copy_tuning_init(&tun);
+  if (tuning) {
+    if (!tuning_valid(*tuning)) return LR_ERR_INVALID;
+    tun = *tuning;
+  }
+  const int rc = plan_path(Ls, src_cap, src_align, Ld, dst_cap, dst_align, elem_bytes, flags, tun, p);
+  if (rc) return rc;
+  // different load and store policies: the generic kernel only
+  if (p->nt_ld != p->nt && p->path != LR_PATH_GENERIC && p->path != LR_PATH_VECTOR) return LR_ERR_PATH;
+  if (p->path != LR_PATH_GENERIC && p->path != LR_PATH_VECTOR) p->vorder = -1;
+  if (p->path != LR_PATH_STAGED) p->staged_cps = -1;
   return LR_OK;
 }
 
@@ -679,6 +826,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
   if (p.bufst && p.path != LR_PATH_GENERIC && p.path != LR_PATH_VECTOR && p.path != LR_PATH_TRANSPOSE &&
       p.path != LR_PATH_INTERLEAVE && p.path != LR_PATH_DEINTERLEAVE)
     return bad();
+  if (p.nt_ld != p.nt && p.path != LR_PATH_GENERIC && p.path != LR_PATH_VECTOR) return bad();
   if (p.path == LR_PATH_DUAL || p.path == LR_PATH_ALIAS) return LR_OK;  // evaluate the validated layouts
   if (p.rank < 1 || p.rank > kMaxKernelModes) return bad();
   int64_t ms = 0, md = 0, prod = 1;
@@ -809,6 +957,12 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (P != p.staged_P || F != p.staged_F || p.m[in].sd != P) return bad();
       if (p.staged_Fc * 16 < F * p.eb || p.staged_cpt * 16 != P * p.eb || 256 % p.staged_cpt) return bad();
       if (p.staged_K < 1 || p.staged_K * p.staged_Fc * 16 > 65536) return bad();
+      {  // gather grouping: cps | cpt, cps | 32, cpt / cps | 8, and whole slices of tiles
+        const int64_t cps = p.staged_cps;
+        if (cps < 1 || cps > 32 || (cps & (cps - 1)) || p.staged_cpt % cps || 8 % (p.staged_cpt / cps) ||
+            (cps != std::min<int64_t>(p.staged_cpt, 32) && p.staged_K % (32 / cps)))
+          return bad();
+      }
       int64_t maxbase = 0;
       for (int k = in; k < p.rank; ++k) {
         if ((p.m[k].ss * p.eb) % 16 || (p.m[k].sd * p.eb) % 16) return bad();
@@ -861,6 +1015,13 @@ bool block_extents(const Plan& p, uint32_t flags, int64_t* cext, int64_t* nblock
   return true;
 }
 
+void inherit_policy(const Plan& whole, Plan* blk) {
+  const bool plain = blk->path == LR_PATH_DUAL || blk->path == LR_PATH_ALIAS;
+  blk->nt = whole.nt && !plain;
+  blk->nt_ld = whole.nt_ld && !plain;
+  if (blk->nt_ld != blk->nt && blk->path != LR_PATH_GENERIC && blk->path != LR_PATH_VECTOR) blk->nt_ld = blk->nt;
+}
+
 void make_block(const Plan& p, const int64_t* cext, const int64_t* start, lr_layout* ls, lr_layout* ld,
                 int64_t* src_off, int64_t* dst_off) {
   std::memset(ls, 0, sizeof(*ls));
@@ -886,11 +1047,26 @@ using namespace lr;
 
 extern "C" {
 
+void lr_copy_tuning_init(lr_copy_tuning* t) {
+  if (!t) return;
+  t->load_policy = t->store_policy = t->units_per_lane = t->vector_order = t->interleave_form = -1;
+  t->tile_shape = t->tile_order = t->element_tiles = t->direct_loads = t->gather_chunks = -1;
+  for (int32_t& r : t->reserved) r = -1;
+}
+
 int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align, const lr_layout* Ld,
                  int64_t dst_capacity_elems, size_t dst_align, size_t elem_bytes, uint32_t flags, lr_plan* out) {
+  return lr_copy_plan_tuned(Ls, src_capacity_elems, src_align, Ld, dst_capacity_elems, dst_align, elem_bytes, flags,
+                            nullptr, out);
+}
+
+int lr_copy_plan_tuned(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align, const lr_layout* Ld,
+                       int64_t dst_capacity_elems, size_t dst_align, size_t elem_bytes, uint32_t flags,
+                       const lr_copy_tuning* tuning, lr_plan* out) {
   if (!out) return LR_ERR_INVALID;
   Plan p;
-  int rc = plan_copy(Ls, src_capacity_elems, src_align, Ld, dst_capacity_elems, dst_align, elem_bytes, flags, &p);
+  int rc = plan_copy(Ls, src_capacity_elems, src_align, Ld, dst_capacity_elems, dst_align, elem_bytes, flags, tuning,
+                     &p);
   if (rc) return rc;
   if ((rc = verify_plan(p, src_capacity_elems, dst_capacity_elems))) return rc;
   std::memset(out, 0, sizeof(*out));
@@ -902,11 +1078,12 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
     lr_layout ls, ld;
     make_block(p, cext, start, &ls, &ld, &os, &od);
     Plan pb;
-    if ((rc = plan_copy(&ls, cosize_bound(&ls), src_align, &ld, cosize_bound(&ld), dst_align, elem_bytes, flags, &pb)))
+    if ((rc = plan_copy(&ls, cosize_bound(&ls), src_align, &ld, cosize_bound(&ld), dst_align, elem_bytes, flags,
+                        tuning, &pb)))
       return rc;
     if (pb.wide) return LR_ERR_PATH;
+    inherit_policy(p, &pb);
     if ((rc = verify_plan(pb, cosize_bound(&ls), cosize_bound(&ld)))) return rc;
-    pb.nt = p.nt && pb.path != LR_PATH_DUAL && pb.path != LR_PATH_ALIAS;
     pb.n = p.n;
     pb.rank = p.rank;
     std::memcpy(pb.m, p.m, sizeof(p.m));
@@ -925,8 +1102,10 @@ int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_ali
   out->streaming = p.nt ? 1 : 0;
   out->order = (p.path == LR_PATH_TRANSPOSE || p.path == LR_PATH_TRANSPOSE_DIRECT) ? (int32_t)p.torder : -1;
   out->direct = p.direct ? 1 : 0;
-  out->load_policy = p.nt ? 2 : 0;
+  out->load_policy = p.nt_ld ? 2 : 0;
   out->store_policy = p.nt ? (p.bufst ? 18 : 2) : 0;
+  out->vector_order = p.vorder;
+  out->gather_chunks = (int32_t)p.staged_cps;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

@@ -41,6 +41,7 @@ from .layout import (  # noqa: F401
     right_inverse,
     right_inverse_fn,
     zipped_divide,
+    slice_layout,
     complement,
     logical_divide,
     logical_product,

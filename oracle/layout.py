@@ -586,6 +586,59 @@ def zipped_divide(L: Layout, tiler: Sequence[int]) -> Layout:
     return Layout((tuple(tiles_s), tuple(rest_s)), (tuple(tiles_d), tuple(rest_d)), L.swz)
 
 
+def slice_layout(L: Layout, coord):
+    """[CuTe algebra page, section 3.2]: tile (3,5) of a zipped_divide is the layout
+    with its rest mode fixed at (3,5) and its tile mode left free ("_").  ``coord``
+    is congruent with (a prefix of the nesting of) L's shape: ``None`` keeps that
+    sub-mode, an integer fixes it (split colexicographically inside the sub-mode, as
+    in eval_coord).  Returns (layout of the kept sub-modes, offset of the fixed
+    ones) with L(c) = offset + result(kept part of c).  The kept sub-modes are
+    grouped by the top-level mode they belong to; when only one group is left, its
+    leaves are the result's top-level modes.  A swizzle stays on the result
+    when the offset is a multiple of 2^(M+S+B) -- the swizzle only reads and writes
+    bits below that, so it then acts on the kept part alone; otherwise the slice is
+    not a layout plus an offset."""
+    def rec(c, shape, stride):
+        if c is None:
+            return [(shape, stride)], 0
+        if isinstance(c, int):
+            return [], _crd2off(c, shape, stride)
+        if isinstance(shape, int) or len(c) != len(shape):
+            raise ValueError("coordinate not congruent with shape")
+        kept, off = [], 0
+        for ci, si, di in zip(c, shape, stride):
+            k, o = rec(ci, si, di)
+            kept += k
+            off += o
+        return kept, off
+
+    top = top_modes(L)
+    if isinstance(L.shape, int) and not (isinstance(coord, tuple) and len(coord) == 1):
+        coord = (coord,)  # a rank-1 layout: its one coordinate, bare or in a 1-tuple
+    if len(coord) != len(top):
+        raise ValueError("one coordinate per top-level mode")
+    shapes, strides, off = [], [], 0
+    for c, m in zip(coord, top):
+        kept, o = rec(c, m.shape, m.stride)
+        off += o
+        if kept:
+            shapes.append(kept[0][0] if len(kept) == 1 else tuple(k[0] for k in kept))
+            strides.append(kept[0][1] if len(kept) == 1 else tuple(k[1] for k in kept))
+    if not shapes:
+        shapes, strides = [1], [0]
+    elif len(shapes) == 1 and not isinstance(shapes[0], int):
+        # one mode survives: its leaves are the result's modes (tile (3,5) is a 4 x 8
+        # layout of its own)
+        shapes, strides = list(_leaves(shapes[0])), list(_leaves(strides[0]))
+    if L.swz is not None:
+        b, m, s = L.swz
+        if off % (1 << (m + s + b)):
+            raise NotRepresentable("the fixed offset moves bits the swizzle reads")
+    shp = shapes[0] if len(shapes) == 1 else tuple(shapes)
+    std = strides[0] if len(strides) == 1 else tuple(strides)
+    return Layout(shp, std, L.swz), off
+
+
 # ----------------------------------------------------------------------------
 # Complement, logical divide and products.  [CuTe algebra page, section 3.2]:
 # dividing a layout into tiles and what is left over; [section 4.1]: a tile

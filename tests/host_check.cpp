@@ -208,7 +208,7 @@ static int run_fuzz() {
       wd *= b.shape[i];
     }
     lr::Plan p;
-    if (lr::plan_copy(&a, w, 16, &b, wd, 16, 2, 0, &p) != LR_OK) continue;
+    if (lr::plan_copy(&a, w, 16, &b, wd, 16, 2, 0, nullptr, &p) != LR_OK) continue;
     int64_t cext[lr::kMaxJoint], nb = 0;
     if (!lr::block_extents(p, 0, cext, &nb)) continue;
     int64_t start[lr::kMaxJoint] = {0}, covered = 0;
@@ -222,7 +222,7 @@ static int run_fuzz() {
       if (bn >= (int64_t(1) << 31) || lr::cosize_bound(&ls) >= (int64_t(1) << 31) ||
           lr::cosize_bound(&ld) >= (int64_t(1) << 31) || os + lr::cosize_bound(&ls) > w ||
           od + lr::cosize_bound(&ld) > wd ||
-          lr::plan_copy(&ls, lr::cosize_bound(&ls), 16, &ld, lr::cosize_bound(&ld), 16, 2, 0, &pb) != LR_OK ||
+          lr::plan_copy(&ls, lr::cosize_bound(&ls), 16, &ld, lr::cosize_bound(&ld), 16, 2, 0, nullptr, &pb) != LR_OK ||
           pb.wide || lr::verify_plan(pb, lr::cosize_bound(&ls), lr::cosize_bound(&ld)) != LR_OK) {
         std::printf("bad block %lld of %lld\n", (long long)k, (long long)nb);
         return 1;

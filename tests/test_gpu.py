@@ -38,12 +38,59 @@ def dev():
     return torch.device("cuda:0")
 
 
+class Knobs:
+    """Overrides of the planner's launch choices (lr_copy_tuning fields) that every
+    copy and plan call of this module passes while a test holds them."""
+
+    def __init__(self):
+        self.t = {}
+
+    def set(self, **kw):
+        self.t.update(kw)
+
+    def unset(self, *names):
+        for n in names:
+            self.t.pop(n, None)
+
+    def policy(self, nt, sc1=None):
+        """nt "0": ordinary loads and stores; "1": non-temporal, the stores with the
+        sc1 bit where the kernel has buffer stores unless sc1 is "0"."""
+        self.unset("load_policy", "store_policy")
+        if nt == "0":
+            self.set(load_policy=0)
+        else:
+            self.set(load_policy=2)
+            if sc1 == "0":
+                self.set(store_policy=2)
+
+    def tuning(self):
+        return dict(self.t) or None
+
+
+KNOBS = Knobs()
+
+
+@pytest.fixture
+def knobs():
+    KNOBS.t.clear()
+    yield KNOBS
+    KNOBS.t.clear()
+
+
+def plan(Ls, ns, Ld, nd, eb, flags=0, **kw):
+    return lr.copy_plan(Ls, ns, Ld, nd, eb, flags, tuning=KNOBS.tuning(), **kw)
+
+
+def copy_(s, Ls, d, Ld, elem_bytes, flags=0):
+    return lr.layout_copy(s, Ls, d, Ld, elem_bytes=elem_bytes, flags=flags, tuning=KNOBS.tuning())
+
+
 def gpu_copy(dev, src, Ls, dst, Ld, eb, flags=0, src_off=0, dst_off=0):
     s = torch.zeros(src.nbytes + src_off, dtype=torch.uint8, device=dev)
     d = torch.zeros(dst.nbytes + dst_off, dtype=torch.uint8, device=dev)
     s[src_off:] = torch.from_numpy(src).to(dev)
     d[dst_off:] = torch.from_numpy(dst).to(dev)
-    lr.layout_copy(s[src_off:], Ls, d[dst_off:], Ld, elem_bytes=eb, flags=flags)
+    copy_(s[src_off:], Ls, d[dst_off:], Ld, eb, flags)
     torch.cuda.synchronize()
     return d[dst_off:].cpu().numpy()
 
@@ -196,6 +243,70 @@ def test_eval_wide(dev):
 # ---------------------------------------------------------------------------
 # Copies at sizes the oracle finishes quickly
 # ---------------------------------------------------------------------------
+def test_algebra_built_layouts_on_device(dev):
+    """Layouts built by the library's algebra -- slice of a zipped_divide,
+    (A, complement(A)), logical_divide, blocked_product -- evaluated and used as
+    copy layouts on the GPU, byte-exact against the oracle's own construction of
+    the same layouts ([CuTe algebra page, sections 3.2 and 4.1])."""
+    rng = np.random.default_rng(17)
+    cases = []
+    # tile (3,5) of the 128 x 128 column-major matrix split by 4 x 8
+    Z = lr.zipped_divide("(128,128):(1,128)", (4, 8))
+    T, off = lr.slice(Z, (-1, 3 + 32 * 5))
+    To, offo = O.slice_layout(O.zipped_divide(O.parse("(128,128):(1,128)"), (4, 8)), (None, (3, 5)))
+    assert off == offo == 5132
+    cases.append(("slice tile (3,5)", T, To, off))
+    # every tile of a 1024 x 512 matrix in 64 x 32 tiles: the same slice per tile
+    Zb = lr.zipped_divide("(1024,512):(512,1)", (64, 32))
+    Tb, offb = lr.slice(Zb, (-1, 7 + 16 * 9))
+    Tbo, offbo = O.slice_layout(O.zipped_divide(O.parse("(1024,512):(512,1)"), (64, 32)), (None, 7 + 16 * 9))
+    assert offb == offbo
+    cases.append(("slice tile (7,9) of 1024x512", Tb, Tbo, offb))
+    # a tile and what it leaves over: (A, complement(A, M)) is a bijection onto [0, M)
+    A = "(4,8):(1,16)"
+    C = lr.complement(A, 2048)
+    Co = O.complement(O.parse(A), 2048)
+    assert C.leaves == O.flatten(Co)
+    AC = lr.parse(f"(({A.split(':')[0][1:-1]}),({','.join(str(n) for n, _ in C.leaves)})):"
+                  f"(({A.split(':')[1][1:-1]}),({','.join(str(d) for _, d in C.leaves)}))")
+    ACo = O.parse(str(AC))
+    assert sorted(O.eval_indices(ACo, np.arange(O.size(ACo))).tolist()) == list(range(2048))
+    cases.append(("(A, complement(A, 2048))", AC, ACo, 0))
+    # logical_divide of a 4096-element run by 8:4 (tiles of 8 elements 4 apart)
+    D = lr.logical_divide("4096:1", "8:4")
+    Do = O.logical_divide(O.parse("4096:1"), O.parse("8:4"))
+    assert D.leaves == O.flatten(Do)
+    cases.append(("logical_divide(4096:1, 8:4)", D, Do, 0))
+    # [CuTe algebra page, section 4.1]: a 4 x 8 block over a 2 x 5 grid, and a
+    # 16 x 64 block over a 32 x 16 grid (a 512 x 1024 blocked matrix)
+    for a, b in (("(4,8):(1,4)", "(2,5):(1,2)"), ("(16,64):(1,16)", "(32,16):(1,32)")):
+        Bp = lr.blocked_product(a, b)
+        Bpo = O.blocked_product(O.parse(a), O.parse(b))
+        assert Bp.leaves == O.flatten(Bpo)
+        cases.append((f"blocked_product({a}, {b})", Bp, Bpo, 0))
+    for name, Lc, Lo, base in cases:
+        n = O.size(Lo)
+        # evaluation of every index on the GPU
+        got = gpu_eval(dev, Lc, n=n)
+        assert np.array_equal(got, O.eval_indices(Lo, np.arange(n))), name
+        for eb in (2, 4):
+            cos = O.cosize(Lo) + base
+            # gather through the built layout (source at the slice's base offset)
+            src = rng.integers(0, 256, cos * eb, dtype=np.uint8)
+            dst = np.full(n * eb, 0xA5, np.uint8)
+            want = O.copy(src[base * eb:], Lo, dst, O.parse(f"{n}:1"), eb)
+            got = gpu_copy(dev, src[base * eb:].copy(), Lc, dst, f"{n}:1", eb)
+            say("algebra layouts", name, "gather eb", eb)
+            assert np.array_equal(got, want), (name, eb)
+            # scatter through it (a bijection onto its image; holes keep 0xA5)
+            src2 = rng.integers(0, 256, n * eb, dtype=np.uint8)
+            dst2 = np.full((cos - base) * eb, 0xA5, np.uint8)
+            want = O.copy(src2, O.parse(f"{n}:1"), dst2, Lo, eb)
+            got = gpu_copy(dev, src2, f"{n}:1", dst2, Lc, eb)
+            say("algebra layouts", name, "scatter eb", eb)
+            assert np.array_equal(got, want), (name, eb)
+
+
 def _oracle_copy(w):
     src, dst = W.make_src(w), W.make_dst(w)
     want = O.copy(src, O.parse(w.src_layout), dst, O.parse(w.dst_layout), w.elem_bytes,
@@ -270,7 +381,7 @@ def test_copy_every_path(dev, ci):
     for path in ALL_PATHS:
         flags = lr.COPY_FORCE_PATH(path)
         try:
-            lr.copy_plan(ts, ns, td, nd, eb, flags)
+            plan(ts, ns, td, nd, eb, flags)
         except lr.LayoutRemapError as e:
             assert e.code == lr.binding.ERR_PATH
             continue
@@ -315,7 +426,7 @@ def _rand_pair(rng):
     return ts, td, max(ns, O.cosize(O.parse(ts))), nd_
 
 
-def test_copy_random_pairs(dev, monkeypatch):
+def test_copy_random_pairs(dev, knobs):
     """600 seeded random pairs (permuted, padded, swizzled, 1-16 byte elements, up to
     2^17 elements), each by the default plan, by every path that applies when
     forced, and with 64-bit indices, under randomly drawn plan-time variants
@@ -328,19 +439,23 @@ def test_copy_random_pairs(dev, monkeypatch):
         src = np.random.default_rng(i).integers(0, 256, ns * eb, dtype=np.uint8)
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-        env = {"LR_NT": rng.choice("01"), "LR_DIRECT": rng.choice("01"), "LR_TDIRECT": rng.choice("01"),
-               "LR_TSHAPE": str(rng.randint(0, 6)), "LR_TORDER": str(rng.randint(0, 4)),
-               "LR_TEL": rng.choice(["0", "1", "2"]), "LR_SC1": rng.choice("01"),
-               "LR_INARROW": rng.choice(["0", "1", "2"])}
-        for k, v in env.items():
-            monkeypatch.setenv(k, v)
+        pol = rng.choice([(0, -1), (2, -1), (2, 2), (2, 0)])  # the last: vector/generic paths only
+        env = {"load_policy": pol[0], "store_policy": pol[1], "direct_loads": rng.choice([-1, 0, 1]),
+               "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 4),
+               "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
+               "vector_order": rng.choice([-1, 0, 1, 2]), "units_per_lane": rng.choice([-1, 1, 4]),
+               "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32])}
+        knobs.t.clear()
+        knobs.set(**env)
         if i % 50 == 0:
             say("copy random", i, ts, "->", td, "eb", eb, env)
         for flags in [0, lr.COPY_WIDE_INDEX] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
             try:
-                p = lr.copy_plan(ts, ns, td, nd, eb, flags)
+                p = plan(ts, ns, td, nd, eb, flags)
             except lr.LayoutRemapError as e:
-                assert e.code == lr.binding.ERR_PATH and flags
+                # a forced path that does not apply, or loads and stores apart on a
+                # path other than vector/generic
+                assert e.code == lr.binding.ERR_PATH and (flags or pol == (2, 0))
                 continue
             got = gpu_copy(dev, src, ts, dst, td, eb, flags)
             assert np.array_equal(got, want), (i, ts, td, eb, hex(flags), env, p["path"])
@@ -423,12 +538,12 @@ def test_full_size(dev, name):
     say("full", w.name, "generate")
     src = W.make_src(w)
     Ls, Ld = O.parse(w.src_layout), O.parse(w.dst_layout)
-    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
+    p = plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
     assert p["path"] == FULL_PATH[name]
     s = torch.from_numpy(src).to(dev)
     d = torch.full((w.dst_elems * w.elem_bytes,), 0xA5, dtype=torch.uint8, device=dev)
     say("full", w.name, "copy", p["path"])
-    lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=w.elem_bytes)
+    copy_(s, w.src_layout, d, w.dst_layout, w.elem_bytes)
     torch.cuda.synchronize()
     got = d.cpu().numpy()
     del s, d
@@ -442,11 +557,11 @@ def test_full_size(dev, name):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("nt", ["0", "1"])
-def test_full_transpose_both_variants(dev, monkeypatch, nt):
+def test_full_transpose_both_variants(dev, knobs, nt):
     # plain and streaming (non-temporal) accesses; the default for this size is streaming
-    monkeypatch.setenv("LR_NT", nt)
+    knobs.policy(nt)
     w = W.full("transpose")
-    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    p = plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
     assert p["streaming"] == (nt == "1") and p["store_policy"] == (18 if nt == "1" else 0)
     src = W.make_src(w)
     want = F.transpose(src, 8192)
@@ -454,7 +569,7 @@ def test_full_transpose_both_variants(dev, monkeypatch, nt):
     for path in (lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT):
         say("full transpose", lr.binding.PATH_NAMES[path], "nt", nt)
         d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
-        lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=2, flags=lr.COPY_FORCE_PATH(path))
+        copy_(s, w.src_layout, d, w.dst_layout, 2, lr.COPY_FORCE_PATH(path))
         torch.cuda.synchronize()
         assert np.array_equal(d.cpu().numpy(), want)
 
@@ -473,13 +588,13 @@ def test_copy_beyond_2_31_elements(dev):
              (f"({M},{M}):({M},1)", f"({M},{M}):(1,{M})", M * M, lambda s: s.reshape(M, M).T.reshape(-1),
               "transpose", 0)]
     for ts, td, n, form, path, flags in cases:
-        p = lr.copy_plan(ts, n, td, n, 1, flags)
+        p = plan(ts, n, td, n, 1, flags)
         assert p["path"] == path and (p["wide"] if flags else p["blocks"] > 1), p
         say("beyond 2^31", ts, "->", td, p["path"], "vec", p["vec_elems"], "blocks", p["blocks"], "wide", p["wide"])
         src = np.random.default_rng(n % 1000).integers(0, 256, n, dtype=np.uint8)
         s = torch.from_numpy(src).to(dev)
         d = torch.full((n,), 0xA5, dtype=torch.uint8, device=dev)
-        lr.layout_copy(s, ts, d, td, elem_bytes=1, flags=flags)
+        copy_(s, ts, d, td, 1, flags)
         torch.cuda.synchronize()
         got = d.cpu().numpy()
         del s, d
@@ -491,20 +606,52 @@ def test_copy_beyond_2_31_elements(dev):
         del src, got
 
 
+@pytest.mark.slow
+def test_channel_shuffle_destination_beyond_4_gib(dev):
+    """fp32 RGB images (7200,224,224,3), 4.3 GB each way: element offsets stay under
+    2^31 (one launch, 32-bit element arithmetic) while destination byte offsets pass
+    4 GiB.  The de-interleave (NHWC -> NCHW) and the channel-shuffle interleave
+    (NCHW -> NHWC) must not wrap their stores at 4 GiB: whole buffers against the
+    NumPy closed forms.  The source is every element's own index, so a misplaced
+    element cannot match."""
+    n, h, w, c = 7200, 224, 224, 3
+    hw = h * w
+    N = n * hw * c
+    assert N < (1 << 31) and N * 4 > (1 << 32)
+    nhwc = f"({n},{h},{w},{c}):({hw * c},{w * c},{c},1)"
+    nchw = f"({n},{h},{w},{c}):({hw * c},{w},1,{hw})"
+    src = np.arange(N, dtype=np.uint32).view(np.uint8)
+    for ts, td, path, form in ((nhwc, nchw, "deinterleave", F.nhwc2nchw), (nchw, nhwc, "interleave", F.nchw2nhwc)):
+        p = plan(ts, N, td, N, 4)
+        assert p["path"] == path and not p["wide"] and p["blocks"] == 1, p
+        say("beyond 4 GiB", path, "store policy", p["store_policy"])
+        s = torch.from_numpy(src).to(dev)
+        d = torch.full((N * 4,), 0xA5, dtype=torch.uint8, device=dev)
+        copy_(s, ts, d, td, 4)
+        torch.cuda.synchronize()
+        del s
+        got = d.cpu().numpy()
+        del d
+        torch.cuda.empty_cache()
+        say("beyond 4 GiB", path, "compare")
+        assert np.array_equal(got, form(src, n, h, w, c, 4)), path
+        del got
+
+
 @pytest.mark.parametrize("nt", ["0", "1"])
-def test_copies_replay_in_a_hip_graph(dev, monkeypatch, nt):
+def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
     """lr_layout_copy allocates nothing and records no memset, so captured copies
     (seven paths in one graph, with plain or streaming accesses, the latter with the
     sc1 buffer stores) replay correctly; each replay is checked after eager work has
     changed the sources."""
-    monkeypatch.setenv("LR_NT", nt)
+    knobs.policy(nt)
     cases = []
     for name in ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles", "rgb_nhwc2nchw"):
         w = W.small(name)
         cases.append((w.src_layout, w.dst_layout, w.src_elems, w.dst_elems, w.elem_bytes))
     rgb = W.small("rgb_nhwc2nchw")  # and back: the channel-shuffle interleave
     cases.append((rgb.dst_layout, rgb.src_layout, rgb.dst_elems, rgb.src_elems, rgb.elem_bytes))
-    paths = {lr.copy_plan(ts, ns, td, nd, eb)["path"] for ts, td, ns, nd, eb in cases}
+    paths = {plan(ts, ns, td, nd, eb)["path"] for ts, td, ns, nd, eb in cases}
     assert {"transpose", "vector", "interleave", "staged", "deinterleave"} <= paths, paths
     s_list, d_list, plans = [], [], []
     for ts, td, ns, nd, eb in cases:
@@ -518,7 +665,7 @@ def test_copies_replay_in_a_hip_graph(dev, monkeypatch, nt):
     with torch.cuda.stream(side):
         with torch.cuda.graph(g):
             for (ts, td, ns, nd, eb), s, d in zip(plans, s_list, d_list):
-                lr.layout_copy(s, ts, d, td, elem_bytes=eb)
+                copy_(s, ts, d, td, eb)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     for rep in range(3):
@@ -541,14 +688,9 @@ def test_copies_replay_in_a_hip_graph(dev, monkeypatch, nt):
 # ---------------------------------------------------------------------------
 # Tuning variants chosen at plan time (tile shapes, narrow-load interleave)
 # ---------------------------------------------------------------------------
-@pytest.fixture
-def env_knob(monkeypatch):
-    return monkeypatch
-
-
 @pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
-def test_transpose_tile_shapes(dev, env_knob, shape):
-    env_knob.setenv("LR_TSHAPE", str(shape))
+def test_transpose_tile_shapes(dev, knobs, shape):
+    knobs.set(tile_shape=shape)
     for ts, td, n, eb in [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
                           ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 7560, 2),
                           ("(100,72):(72,1)", "(100,72):(1,100)", 7200, 4),
@@ -561,25 +703,25 @@ def test_transpose_tile_shapes(dev, env_knob, shape):
         for path in (lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT):
             flags = lr.COPY_FORCE_PATH(path)
             try:
-                lr.copy_plan(ts, n, td, n, eb, flags)
+                plan(ts, n, td, n, eb, flags)
             except lr.LayoutRemapError:
                 continue
             say("transpose shape", shape, lr.binding.PATH_NAMES[path], ts, "eb", eb)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
         for orient in ("0", "1", "2", "3", "4"):
-            env_knob.setenv("LR_TORDER", orient)
+            knobs.set(tile_order=int(orient))
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)
-        env_knob.delenv("LR_TORDER")
+        knobs.unset("tile_order")
 
 
-def test_streaming_accesses_every_path(dev, env_knob):
-    """Small copies default to plain accesses; LR_NT=1 forces the non-temporal
-    kernels, which must give the same bytes on every path and workload."""
-    env_knob.setenv("LR_NT", "1")
+def test_streaming_accesses_every_path(dev, knobs):
+    """Small copies default to plain accesses; a non-temporal load policy forces the
+    non-temporal kernels, which must give the same bytes on every path and workload."""
+    knobs.policy("1")
     for name in W.FULL:
         w = W.small(name)
         flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
-        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
+        p = plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
         assert p["streaming"] == (p["path"] not in ("alias", "dual")), p["path"]
         src, dst, want = _oracle_copy(w)
         say("streaming small", w.name)
@@ -591,7 +733,7 @@ def test_streaming_accesses_every_path(dev, env_knob):
         for path in ALL_PATHS:
             flags = lr.COPY_FORCE_PATH(path)
             try:
-                lr.copy_plan(ts, ns, td, nd, eb, flags)
+                plan(ts, ns, td, nd, eb, flags)
             except lr.LayoutRemapError:
                 continue
             say("streaming path", lr.binding.PATH_NAMES[path], ts, "->", td, "eb", eb)
@@ -599,13 +741,12 @@ def test_streaming_accesses_every_path(dev, env_knob):
 
 
 @pytest.mark.parametrize("tsc1", ["0", "1"])
-def test_transpose_streaming_store_forms(dev, env_knob, tsc1):
+def test_transpose_streaming_store_forms(dev, knobs, tsc1):
     """Streaming transposes store either with global non-temporal stores or with
     buffer stores relative to each tile's lowest destination offset (nt and sc1
     bits).  Every tile shape, with ragged edges, a batch mode, a grouped b run and
     destination swizzles (the tile base is rounded down past the swizzled bits)."""
-    env_knob.setenv("LR_NT", "1")
-    env_knob.setenv("LR_SC1", tsc1)
+    knobs.policy("1", tsc1)
     cm = W.small("interleave_cm")
     cases = [("(520,264):(264,1)", "(520,264):(1,520)", 2),
              ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 2),
@@ -618,11 +759,11 @@ def test_transpose_streaming_store_forms(dev, env_knob, tsc1):
              (cm.src_layout, cm.dst_layout, 2)]
     ran = 0
     for shape in range(7):
-        env_knob.setenv("LR_TSHAPE", str(shape))
+        knobs.set(tile_shape=shape)
         for ci, (ts, td, eb) in enumerate(cases):
             n = O.size(O.parse(ts))
             ns, nd = max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize)
-            p = lr.copy_plan(ts, ns, td, nd, eb)
+            p = plan(ts, ns, td, nd, eb)
             if p["path"] != "transpose":
                 continue
             src = np.random.default_rng(ci + 10 * shape).integers(0, 256, ns * eb, dtype=np.uint8)
@@ -639,12 +780,11 @@ def test_transpose_streaming_store_forms(dev, env_knob, tsc1):
 
 
 @pytest.mark.parametrize("sc1", ["0", "1"])
-def test_vector_streaming_store_forms(dev, env_knob, sc1):
+def test_vector_streaming_store_forms(dev, knobs, sc1):
     """The vector path's streaming stores, global nt or buffer stores with nt and sc1
     from the destination base: contiguous, strided, swizzled and retiled layouts with
     ragged unit counts, both traversal orders."""
-    env_knob.setenv("LR_NT", "1")
-    env_knob.setenv("LR_SC1", sc1)
+    knobs.policy("1", sc1)
     rt = W.small("retile")
     cases = [("100000:1", "100000:1", 100000, 2),
              ("(64,130,3):(1,64,8320)", "(64,130,3):(1,200,26000)", 64 * 130 * 3, 2),
@@ -653,11 +793,11 @@ def test_vector_streaming_store_forms(dev, env_knob, sc1):
              ("(1,999):(1,1)", "(1,999):(1,3)", 999, 16),
              (rt.src_layout, rt.dst_layout, rt.n_elems, 2)]
     ran = 0
-    for vorder in ("0", "1"):
-        env_knob.setenv("LR_VORDER", vorder)
+    for vorder in ("0", "1", "2"):
+        knobs.set(vector_order=int(vorder))
         for ci, (ts, td, n, eb) in enumerate(cases):
             ns, nd = max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize)
-            p = lr.copy_plan(ts, ns, td, nd, eb)
+            p = plan(ts, ns, td, nd, eb)
             assert p["path"] in ("vector", "generic") and p["vec_elems"] * p["elem_bytes"] == 16, (ts, td, p)
             assert p["store_policy"] == (18 if sc1 == "1" else 2), (ts, td, p)
             src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
@@ -666,7 +806,7 @@ def test_vector_streaming_store_forms(dev, env_knob, sc1):
             say("vector stores", "sc1" if sc1 == "1" else "global", ts, "->", td, "eb", eb, "vorder", vorder)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td)
             ran += 1
-    assert ran == 2 * len(cases)
+    assert ran == 3 * len(cases)
 
 
 def _pow2_align(off):
@@ -690,7 +830,7 @@ def test_windowed_kernels_misaligned_pointers(dev):
         for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
             want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
             for so, do in ((eb, 0), (0, 3 * eb), (5 * eb, 7 * eb)):
-                p = lr.copy_plan(ts, size, td, size, eb, src_align=_pow2_align(so), dst_align=_pow2_align(do))
+                p = plan(ts, size, td, size, eb, src_align=_pow2_align(so), dst_align=_pow2_align(do))
                 assert p["path"] == path and p["vec_elems"] == 1, (ts, td, eb, so, do, p)
                 say("windowed channel shuffle", path, "eb", eb, "C", c, "offsets", so, do)
                 assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, src_off=so, dst_off=do), want), (ts, eb, so, do)
@@ -701,7 +841,7 @@ def test_windowed_kernels_misaligned_pointers(dev):
         dst = np.full(n * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         for so, do in ((eb, 0), (0, 5 * eb), (3 * eb, 11 * eb)):
-            p = lr.copy_plan(ts, n, td, n, eb, src_align=_pow2_align(so), dst_align=_pow2_align(do))
+            p = plan(ts, n, td, n, eb, src_align=_pow2_align(so), dst_align=_pow2_align(do))
             assert p["path"] == "transpose" and p["tile_a"] == 256 // eb and p["block"] == 512, (eb, so, do, p)
             say("element tiles", "eb", eb, "offsets", so, do)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, src_off=so, dst_off=do), want), (eb, so, do)
@@ -724,11 +864,11 @@ def test_odd_size_images_full_size(dev):
         interleaved = np.ascontiguousarray(src.reshape(n, c, h, w, eb).transpose(0, 2, 3, 1, 4)).reshape(-1)
         s = torch.from_numpy(src).to(dev)
         for ts, td, path, want in ((nhwc, nchw, "deinterleave", planar), (nchw, nhwc, "interleave", interleaved)):
-            p = lr.copy_plan(ts, size, td, size, eb)
+            p = plan(ts, size, td, size, eb)
             assert p["path"] == path and p["vec_elems"] == 1 and p["streaming"] == streaming, (n, h, w, c, eb, p)
             say("odd-size image", path, (n, h, w, c), "eb", eb)
             d = torch.full((size * eb,), 0xA5, dtype=torch.uint8, device=dev)
-            lr.layout_copy(s, ts, d, td, elem_bytes=eb)
+            copy_(s, ts, d, td, eb)
             torch.cuda.synchronize()
             assert np.array_equal(d.cpu().numpy(), want), (path, n, h, w, c, eb)
             del d
@@ -748,7 +888,7 @@ def test_odd_pitch_transposes_full_size(dev):
     for r, c, eb, order in cases:
         n = r * c
         ls, ld = f"({r},{c}):({c},1)", f"({r},{c}):(1,{r})"
-        p = lr.copy_plan(ls, n, ld, n, eb)
+        p = plan(ls, n, ld, n, eb)
         assert p["path"] == "transpose" and p["vec_elems"] == 1 and p["tile_a"] == 256 // eb, (r, c, eb, p)
         assert p["order"] == order and not p["streaming"], (r, c, eb, p)
         src = np.random.default_rng(r + c + eb).integers(0, 256, n * eb, dtype=np.uint8)
@@ -756,14 +896,14 @@ def test_odd_pitch_transposes_full_size(dev):
         say("odd-pitch transpose", r, c, "eb", eb, "order", order)
         s = torch.from_numpy(src).to(dev)
         d = torch.full((n * eb,), 0xA5, dtype=torch.uint8, device=dev)
-        lr.layout_copy(s, ls, d, ld, elem_bytes=eb)
+        copy_(s, ls, d, ld, eb)
         torch.cuda.synchronize()
         assert np.array_equal(d.cpu().numpy(), want), (r, c, eb)
         del s, d
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
-def test_transpose_element_tiles(dev, env_knob, eb):
+def test_transpose_element_tiles(dev, knobs, eb):
     """Transposes whose rows allow no aligned 16-byte chunks run element-granular
     tiles: odd and ragged extents, a grouped dst-contiguous run, swizzles, a batch
     mode, both access policies and every workgroup order."""
@@ -773,7 +913,7 @@ def test_transpose_element_tiles(dev, env_knob, eb):
              ("(5,2,77):(77,385,1)", "(5,2,77):(2,1,10)", 5 * 2 * 77),
              ("(255,255):(255,1)", "Sw<1,0,3> o (255,255):(1,255)", 256 * 255),
              ("(130,66,3):(66,1,8580)", "(130,66,3):(1,130,8580)", 130 * 66 * 3)]
-    env_knob.setenv("LR_TEL", "1")
+    knobs.set(element_tiles=1)
     ran = 0
     for ci, (ts, td, n) in enumerate(cases):
         ns = max(n, O.cosize(O.parse(ts)))
@@ -782,10 +922,10 @@ def test_transpose_element_tiles(dev, env_knob, eb):
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         for nt in ("0", "1"):
-            env_knob.setenv("LR_NT", nt)
+            knobs.policy(nt)
             for orient in ("0", "1", "2", "3", "4"):
-                env_knob.setenv("LR_TORDER", orient)
-                p = lr.copy_plan(ts, ns, td, nd, eb, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
+                knobs.set(tile_order=int(orient))
+                p = plan(ts, ns, td, nd, eb, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))
                 if p["tile_a"] != 256 // eb or p["block"] != 512:
                     continue  # aligned chunks exist: the chunk transpose runs instead
                 say("transpose elements", ts, "->", td, "eb", eb, "nt", nt, "order", orient)
@@ -796,10 +936,10 @@ def test_transpose_element_tiles(dev, env_knob, eb):
 
 
 @pytest.mark.parametrize("shape", [0, 1, 2, 3])
-def test_transpose_direct_loads(dev, env_knob, shape):
+def test_transpose_direct_loads(dev, knobs, shape):
     """The transpose with its source tile loaded straight into LDS."""
-    env_knob.setenv("LR_TDIRECT", "1")
-    env_knob.setenv("LR_TSHAPE", str(shape))
+    knobs.set(direct_loads=1)
+    knobs.set(tile_shape=shape)
     cases = [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
              ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 7560, 2),
              ("(100,72):(72,1)", "(100,72):(1,100)", 7200, 4),
@@ -814,10 +954,10 @@ def test_transpose_direct_loads(dev, env_knob, shape):
         dst = np.full(n * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         for nt in ("0", "1"):
-            env_knob.setenv("LR_NT", nt)
+            knobs.policy(nt)
             for orient in ("0", "1", "2", "3", "4"):
-                env_knob.setenv("LR_TORDER", orient)
-                p = lr.copy_plan(ts, n, td, n, eb)
+                knobs.set(tile_order=int(orient))
+                p = plan(ts, n, td, n, eb)
                 if p["path"] != "transpose":
                     continue
                 say("transpose direct", shape, ts, "eb", eb, "nt", nt, "order", orient, "tile", p["tile_a"], p["tile_b"])
@@ -827,50 +967,58 @@ def test_transpose_direct_loads(dev, env_knob, shape):
 
 
 @pytest.mark.slow
-def test_full_transpose_direct_loads(dev, monkeypatch):
-    monkeypatch.setenv("LR_TDIRECT", "1")
+def test_full_transpose_direct_loads(dev, knobs):
+    knobs.set(direct_loads=1)
     w = W.full("transpose")
     src = W.make_src(w)
     s = torch.from_numpy(src).to(dev)
     d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
     say("full transpose direct loads")
-    lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=2)
+    copy_(s, w.src_layout, d, w.dst_layout, 2)
     torch.cuda.synchronize()
     assert np.array_equal(d.cpu().numpy(), F.transpose(src, 8192))
 
 
 @pytest.mark.parametrize("direct", [0, 1])
-def test_staged_direct_loads(dev, env_knob, direct):
+def test_staged_direct_loads(dev, knobs, direct):
     """The staged path with its footprint loaded straight into LDS (gfx950 direct
     loads) or through registers; both streaming policies."""
-    env_knob.setenv("LR_DIRECT", str(direct))
+    knobs.set(direct_loads=direct)
     cases = [(W.small("padtiles").src_layout, W.small("padtiles").dst_layout, W.small("padtiles").src_elems,
               W.small("padtiles").dst_elems, 4)]
     cases += [c for c in _case_pairs()]
     ran = 0
     for nt in ("0", "1"):
-        env_knob.setenv("LR_NT", nt)
+        knobs.policy(nt)
         for ci, (ts, td, ns, nd, eb) in enumerate(cases):
             flags = lr.COPY_FORCE_PATH(lr.PATH_STAGED)
             try:
-                lr.copy_plan(ts, ns, td, nd, eb, flags)
+                plan(ts, ns, td, nd, eb, flags)
             except lr.LayoutRemapError:
                 continue
             src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
             dst = np.full(nd * eb, 0xA5, np.uint8)
             want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-            say("staged direct", direct, "nt", nt, ts, "->", td, "eb", eb)
-            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want)
-            ran += 1
-    assert ran >= 4
+            seen = set()
+            for gc in (-1, 1, 2, 4, 8, 16, 32):  # every gather grouping the plan admits
+                knobs.set(gather_chunks=gc)
+                g = plan(ts, ns, td, nd, eb, flags)["gather_chunks"]
+                if g in seen:
+                    continue
+                seen.add(g)
+                say("staged direct", direct, "nt", nt, ts, "->", td, "eb", eb, "gather chunks", g)
+                assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want), (ts, td, g)
+                ran += 1
+            knobs.unset("gather_chunks")
+    assert ran >= 8
 
 
 @pytest.mark.parametrize("narrow", [0, 1])
-def test_interleave_variants(dev, env_knob, narrow):
+def test_interleave_variants(dev, knobs, narrow):
     """Both load variants at every NB, with plain accesses and with streaming ones
     (the narrow variant's streaming stores as global nt stores or as buffer stores
     with nt and sc1), including a swizzled destination."""
-    env_knob.setenv("LR_INARROW", str(narrow))
+    knobs.set(interleave_form=narrow)
     cases = []
     for eb, nb in [(1, 2), (1, 4), (1, 8), (1, 16), (2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (8, 2)]:
         a, bt = 16 // eb * 40, 3
@@ -882,13 +1030,35 @@ def test_interleave_variants(dev, env_knob, narrow):
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         for nt, sc1 in (("0", "1"), ("1", "0"), ("1", "1")):
-            env_knob.setenv("LR_NT", nt)
-            env_knob.setenv("LR_SC1", sc1)
-            p = lr.copy_plan(ts, n, td, nd, eb)
+            knobs.policy(nt, sc1)
+            p = plan(ts, n, td, nd, eb)
             assert p["path"] == "interleave"
             assert p["store_policy"] == (0 if nt == "0" else 18 if (sc1 == "1" and narrow) else 2), p
             say("interleave narrow", narrow, ts, "->", td, "eb", eb, "nt", nt, "sc1", sc1)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, nt, sc1)
+
+
+@pytest.mark.parametrize("pol", [(2, 0), (0, 2), (0, 18)])
+def test_vector_split_load_store_policies(dev, knobs, pol):
+    """The generic and vector paths with loads and stores under different cache
+    policies (non-temporal loads with plain stores, and the reverse), every
+    traversal order, 16-byte units and narrower ones."""
+    rt = W.small("retile")
+    cases = [(rt.src_layout, rt.dst_layout, rt.n_elems, rt.n_elems, 2),
+             ("(64,130,3):(1,64,8320)", "(64,130,3):(1,200,26000)", 64 * 130 * 3, 200 * 130 * 3, 2),
+             ("(100,7):(3,1000)", "(100,7):(1,100)", 3 * 99 + 6001, 700, 4),
+             ("100000:1", "100000:1", 100000, 100000, 1)]
+    for ci, (ts, td, ns, nd, eb) in enumerate(cases):
+        src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for vo in (0, 1, 2):
+            knobs.t.clear()
+            knobs.set(load_policy=pol[0], store_policy=pol[1], vector_order=vo)
+            p = plan(ts, ns, td, nd, eb)
+            assert p["path"] in ("vector", "generic") and p["load_policy"] == pol[0], (ts, p)
+            say("vector policies", pol, "order", vo, ts, "->", td, "eb", eb, p["path"])
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, pol, vo)
 
 
 def _image(n, h, w, c):
@@ -897,11 +1067,11 @@ def _image(n, h, w, c):
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
-def test_channel_shuffle(dev, env_knob, eb):
+def test_channel_shuffle(dev, knobs, eb):
     """Few-channel image layouts, NHWC <-> NCHW for every channel count the shuffle
     kernels take (2..8 channels of at most 16 bytes), both access policies: a batch
     mode, workgroups cut short at the end of each image, and the register interleave
-    replaced by the shuffle for power-of-two channel counts (LR_INARROW=2)."""
+    replaced by the shuffle for power-of-two channel counts (interleave_form 2)."""
     ran = 0
     for c in range(2, 9):
         if c * eb > 16:
@@ -918,12 +1088,12 @@ def test_channel_shuffle(dev, env_knob, eb):
             want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
             for nt in ("0", "1"):
                 for variant in ("default", "2"):
-                    env_knob.setenv("LR_NT", nt)
+                    knobs.policy(nt)
                     if variant == "2":
-                        env_knob.setenv("LR_INARROW", "2")
+                        knobs.set(interleave_form=2)
                     else:
-                        env_knob.delenv("LR_INARROW", raising=False)
-                    p = lr.copy_plan(ts, size, td, size, eb)
+                        knobs.unset("interleave_form")
+                    p = plan(ts, size, td, size, eb)
                     assert p["path"] == path, (ts, td, eb, p["path"])
                     shuffled = path == "deinterleave" or c & (c - 1) or variant == "2"
                     if path == "interleave":
@@ -931,12 +1101,12 @@ def test_channel_shuffle(dev, env_knob, eb):
                     say("channel shuffle", path, "eb", eb, "C", c, "nt", nt, "variant", variant)
                     assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, eb, nt, variant)
                     ran += 1
-    env_knob.delenv("LR_INARROW", raising=False)
+    knobs.unset("interleave_form")
     assert ran >= 8
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
-def test_channel_shuffle_any_pixel_count(dev, env_knob, eb):
+def test_channel_shuffle_any_pixel_count(dev, knobs, eb):
     """The element-granular channel shuffle: images whose pixel count leaves the
     planes without whole 16-byte chunks (odd sizes), every channel count, both
     directions and access policies, with a batch and workgroups cut short."""
@@ -952,8 +1122,8 @@ def test_channel_shuffle_any_pixel_count(dev, env_knob, eb):
             for ts, td, path in ((nhwc, nchw, "deinterleave"), (nchw, nhwc, "interleave")):
                 want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
                 for nt in ("0", "1"):
-                    env_knob.setenv("LR_NT", nt)
-                    p = lr.copy_plan(ts, size, td, size, eb)
+                    knobs.policy(nt)
+                    p = plan(ts, size, td, size, eb)
                     assert p["path"] == path and p["vec_elems"] == 1, (ts, td, eb, p)
                     say("channel shuffle elements", path, "eb", eb, "C", c, (n, h, w), "nt", nt)
                     assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, eb, nt)
@@ -961,9 +1131,9 @@ def test_channel_shuffle_any_pixel_count(dev, env_knob, eb):
     assert ran >= 8
 
 
-@pytest.mark.parametrize("vorder", [0, 1])
-def test_vector_traversal_orders(dev, env_knob, vorder):
-    env_knob.setenv("LR_VORDER", str(vorder))
+@pytest.mark.parametrize("vorder", [0, 1, 2])
+def test_vector_traversal_orders(dev, knobs, vorder):
+    knobs.set(vector_order=vorder)
     cases = [(W.small("retile").src_layout, W.small("retile").dst_layout, 512 * 512, 512 * 512, 2),
              ("(64,64):(64,1)", "Sw<3,3,3> o (64,64):(64,1)", 4096, 4096, 2),
              ("(96,5,3):(1,96,480)", "(96,5,3):(1,288,96)", 1440, 1440, 2),
@@ -975,5 +1145,5 @@ def test_vector_traversal_orders(dev, env_knob, vorder):
         src = np.random.default_rng(ns).integers(0, 256, ns * eb, dtype=np.uint8)
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-        say("vector order", vorder, ts, "->", td, "eb", eb, lr.copy_plan(ts, ns, td, nd, eb)["path"])
+        say("vector order", vorder, ts, "->", td, "eb", eb, plan(ts, ns, td, nd, eb)["path"])
         assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want)

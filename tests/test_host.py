@@ -1,6 +1,7 @@
 """Host side of the C ABI (no GPU): the library loads and exports what the header
 declares, and its layout algebra and copy planner agree with the CPU oracle."""
 
+import math
 import os
 import random
 import shutil
@@ -168,6 +169,70 @@ def test_zipped_divide_matches_oracle():
         assert got.leaves == O.flatten(want)
     with pytest.raises(lr.LayoutRemapError):
         lr.zipped_divide("(6,4):(1,6)", (4,))
+
+
+def _mode_ends(Lo):
+    ends, n = [], 0
+    for m in O.top_modes(Lo):
+        n += len(O.flatten(m))
+        ends.append(n)
+    return ends
+
+
+def test_slice_matches_oracle():
+    # [CuTe algebra page, section 3.2]: tile (3,5) of the zipped_divide
+    Z = lr.zipped_divide("(128,128):(1,128)", (4, 8))
+    T, off = lr.slice(Z, (-1, 3 + 32 * 5))
+    assert (str(T), off) == ("(4,8):(1,128)", 5132)
+    T2, off2 = lr.slice(Z, (-1, -1, 3, 5))  # one entry per leaf
+    assert (str(T2), off2) == ("(4,8):(1,128)", 5132)
+    rng = random.Random(33)
+    runs = 0
+    for _ in range(1500):
+        t = _rand_layout(rng, max_leaves=5, swz_p=0.2)
+        Lo, Lc = O.parse(t), lr.parse(t)
+        top = O.top_modes(Lo)
+        per_mode = rng.random() < 0.5
+        if per_mode:
+            coord = [None if rng.random() < 0.5 else rng.randrange(O.size(m)) for m in top]
+            oc = tuple(coord) if not isinstance(Lo.shape, int) else coord[0]
+        else:
+            # one entry per leaf; the oracle gets the same coordinate, nested like the shape
+            coord = [None if rng.random() < 0.5 else rng.randrange(n) for n, _ in O.flatten(Lo)]
+            it = iter(coord)
+
+            def nest(shape):
+                return next(it) if isinstance(shape, int) else tuple(nest(x) for x in shape)
+
+            oc = nest(Lo.shape)
+            if isinstance(Lo.shape, int):
+                oc = (oc,)
+        try:
+            want = O.slice_layout(Lo, oc)
+        except OL.NotRepresentable:
+            want = None
+        try:
+            got = lr.slice(Lc, coord)
+        except lr.LayoutRemapError as e:
+            assert e.code == lr.binding.ERR_NOT_REPRESENTABLE, (t, coord)
+            got = None
+        assert (got is None) == (want is None), (t, coord)
+        if got is None:
+            continue
+        (Sc, oc_), (So, oo) = got, want
+        assert oc_ == oo and _same(Sc, So), (t, coord, str(Sc), O.fmt(So))
+        # the same top-level modes
+        assert Sc.mode_end == _mode_ends(So), (t, coord, str(Sc), O.fmt(So))
+        runs += 1
+    assert runs > 1200
+    E = lr.binding
+    for bad in ((-1,), (0, 0, 0, 0, 0), (-1, 512)):
+        with pytest.raises(lr.LayoutRemapError) as e:
+            lr.slice(Z, bad)
+        assert e.value.code == E.ERR_INVALID, bad
+    with pytest.raises(lr.LayoutRemapError) as e:
+        lr.slice("Sw<3,3,3> o (64,64):(64,1)", (1, -1))
+    assert e.value.code == E.ERR_NOT_REPRESENTABLE
 
 
 def _nested_text(rng):
@@ -505,23 +570,23 @@ def test_plan_joint_matches_oracle_random():
     assert n > 300
 
 
-def test_plan_streaming_default_and_tile_shapes(monkeypatch):
-    monkeypatch.delenv("LR_NT", raising=False)
-    monkeypatch.delenv("LR_TSHAPE", raising=False)
-    # non-temporal accesses from a 256 MiB footprint (source plus destination bytes)
-    n = (128 << 20) // 4
+NT = {"load_policy": 2}     # streaming loads and stores (sc1 where the kernel has it)
+PLAIN = {"load_policy": 0}  # ordinary loads and stores
+
+
+def test_plan_streaming_default_and_tile_shapes():
+    # non-temporal accesses from a 64 MiB footprint (source plus destination bytes)
+    n = (32 << 20) // 4
     assert lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 4)["streaming"]
     assert not lr.copy_plan(f"{n - 1}:1", n, f"{n - 1}:1", n, 4)["streaming"]
-    monkeypatch.setenv("LR_NT", "0")
-    assert not lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 4)["streaming"]
-    monkeypatch.setenv("LR_NT", "1")
-    assert lr.copy_plan("64:1", 64, "64:1", 64, 4)["streaming"]
-    # the per-element and aliased fallbacks keep plain accesses
-    p = lr.copy_plan("(6,4):(1,6)", 24, "(4,6):(1,4)", 24, 4)
-    assert p["path"] == "dual" and not p["streaming"]
-    p = lr.copy_plan("8:1", 8, "8:0", 1, 4, lr.COPY_ORDERED_ALIAS)
-    assert p["path"] == "alias" and not p["streaming"]
-    monkeypatch.delenv("LR_NT")
+    assert not lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 4, tuning=PLAIN)["streaming"]
+    assert lr.copy_plan("64:1", 64, "64:1", 64, 4, tuning=NT)["streaming"]
+    # the per-element and aliased fallbacks keep plain accesses, whatever is asked
+    for t in (None, NT):
+        p = lr.copy_plan("(6,4):(1,6)", 24, "(4,6):(1,4)", 24, 4, tuning=t)
+        assert p["path"] == "dual" and not p["streaming"]
+        p = lr.copy_plan("8:1", 8, "8:0", 1, 4, lr.COPY_ORDERED_ALIAS, tuning=t)
+        assert p["path"] == "alias" and not p["streaming"]
     # transpose tiles: rows far apart -> 32 x 32 chunks (16 x 32 when 16 chunks
     # cover the contiguous extent); a contiguous source block per tile -> 32 x 8
     want = {"transpose": (256, 256, 1024), "interleave_cm": (128, 256, 512), "nhwc2nchw": (256, 64, 256)}
@@ -547,7 +612,7 @@ def test_plan_streaming_default_and_tile_shapes(monkeypatch):
     assert (p["vec_elems"], p["tile_a"], p["tile_b"], p["grid"]) == (8, 256, 128, 512), p
 
 
-def test_plan_workgroup_order(monkeypatch):
+def test_plan_workgroup_order():
     """Transpose workgroup order: b-tiles fastest unless a pitch is power-of-two
     heavy (a multiple of 16 KiB, or a power of two from 4 KiB); then the diagonal
     with b fastest, or with a fastest for tiles with longer source rows and no more
@@ -555,11 +620,10 @@ def test_plan_workgroup_order(monkeypatch):
     bytes of a multiple of 16 KiB count as power-of-two heavy.  Element tiles (rows
     without aligned chunks) take the diagonal with b fastest up to 64 bytes past a
     multiple of 8 KiB, else a fastest with at least as many a-tiles as b-tiles."""
-    monkeypatch.delenv("LR_TORDER", raising=False)
-    monkeypatch.delenv("LR_TSHAPE", raising=False)
 
-    def order(rows, cols, eb):
-        p = lr.copy_plan(f"({cols},{rows}):(1,{cols})", rows * cols, f"({cols},{rows}):({rows},1)", rows * cols, eb)
+    def order(rows, cols, eb, tuning=None):
+        p = lr.copy_plan(f"({cols},{rows}):(1,{cols})", rows * cols, f"({cols},{rows}):({rows},1)", rows * cols, eb,
+                         tuning=tuning)
         assert p["path"] == "transpose"
         return p["order"]
 
@@ -580,62 +644,136 @@ def test_plan_workgroup_order(monkeypatch):
         w = W.full(name)
         assert lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)["order"] == o, name
     assert lr.copy_plan("64:1", 64, "64:1", 64, 4)["order"] == -1
-    monkeypatch.setenv("LR_TORDER", "3")
-    assert order(8192, 8192, 2) == 3
-    monkeypatch.setenv("LR_TORDER", "0")
-    assert order(8192, 8192, 2) == 0
+    assert order(8192, 8192, 2, {"tile_order": 3}) == 3
+    assert order(8192, 8192, 2, {"tile_order": 0}) == 0
 
 
-def test_plan_store_policy(monkeypatch):
+def test_plan_store_policy():
     """Streaming copies load and store non-temporally; the streaming stores of the
     LDS transpose, the vector path and the narrow interleave also carry the sc1 scope
     bit (buffer stores), only while a tile's (transpose) or the whole destination's
     span stays under 4 GiB (32-bit buffer offsets)."""
-    for k in ("LR_NT", "LR_SC1", "LR_TDIRECT", "LR_TEL"):
-        monkeypatch.delenv(k, raising=False)
-
-    def plan(name):
+    def plan(name, tuning=None):
         w = W.full(name)
         flags = lr.COPY_ORDERED_ALIAS if w.ordered_alias else 0
-        return lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags)
+        return lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, flags, tuning=tuning)
 
     want = {"transpose": (2, 18), "interleave_cm": (2, 18), "nhwc2nchw": (2, 18), "interleave": (2, 18),
-            "padtiles": (2, 2), "retile": (0, 0), "tile8x8": (0, 0)}
+            "padtiles": (2, 2), "retile": (2, 18), "shard_pack": (0, 0), "tile8x8": (0, 0)}
     for name, pol in want.items():
         p = plan(name)
         assert (p["load_policy"], p["store_policy"]) == pol, (name, p["path"])
-    monkeypatch.setenv("LR_SC1", "0")
-    assert plan("transpose")["store_policy"] == 2
-    monkeypatch.delenv("LR_SC1")
-    monkeypatch.setenv("LR_TDIRECT", "1")
-    assert plan("transpose")["store_policy"] == 2  # the direct-load kernel keeps global stores
-    monkeypatch.delenv("LR_TDIRECT")
-    monkeypatch.setenv("LR_NT", "1")
+    assert plan("transpose", {"store_policy": 2})["store_policy"] == 2
+    # the direct-load kernel keeps global stores
+    assert plan("transpose", {"direct_loads": 1})["store_policy"] == 2
     # 16-byte elements, 16 x 16 tiles: the destination span of a tile is 15 rows of the
     # a-mode's destination stride
     for sd, pol in ((1 << 20, 18), ((1 << 32) // (15 * 16) - 16, 18), (1 << 25, 2)):
-        p = lr.copy_plan("(16,64):(1,16)", 1024, f"(16,64):({sd},1)", 15 * sd + 64, 16)
+        p = lr.copy_plan("(16,64):(1,16)", 1024, f"(16,64):({sd},1)", 15 * sd + 64, 16, tuning=NT)
         assert p["path"] == "transpose" and p["tile_a"] == 16 and p["store_policy"] == pol, (sd, p)
     # element tiles (rows without aligned chunks) keep global stores
-    assert lr.copy_plan("(301,517):(517,1)", 301 * 517, "(301,517):(1,301)", 301 * 517, 2)["store_policy"] == 2
+    p = lr.copy_plan("(301,517):(517,1)", 301 * 517, "(301,517):(1,301)", 301 * 517, 2, tuning=NT)
+    assert p["store_policy"] == 2
     # the vector path and 16-byte generic units: stores from the destination base,
     # span under 4 GiB
-    assert plan("retile")["store_policy"] == 18
+    assert plan("retile", NT)["store_policy"] == 18
     for n, pol in (((1 << 28) - 1, 18), (1 << 28, 2)):
-        p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16)
+        p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16, tuning=NT)
         assert p["vec_elems"] * p["elem_bytes"] == 16 and p["store_policy"] == pol, (n, p)
-    assert lr.copy_plan("4096:1", 4096, "4096:1", 4096, 4, lr.COPY_WIDE_INDEX)["store_policy"] == 2
-    monkeypatch.setenv("LR_SC1", "0")
-    assert plan("retile")["store_policy"] == 2
+    assert lr.copy_plan("4096:1", 4096, "4096:1", 4096, 4, lr.COPY_WIDE_INDEX, tuning=NT)["store_policy"] == 2
+    assert plan("retile", {"store_policy": 2})["store_policy"] == 2
+    # loads and stores apart: the vector path only
+    p = plan("retile", {"load_policy": 2, "store_policy": 0})
+    assert (p["load_policy"], p["store_policy"]) == (2, 0)
+    with pytest.raises(lr.LayoutRemapError) as e:
+        plan("transpose", {"load_policy": 2, "store_policy": 0})
+    assert e.value.code == lr.binding.ERR_PATH
 
 
-def test_plan_few_channel_images(monkeypatch):
+def test_tuning_overrides_are_checked():
+    w = W.full("transpose")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 5},
+                {"units_per_lane": 2}, {"vector_order": 3}, {"gather_chunks": 3}, {"direct_loads": 2}):
+        with pytest.raises(lr.LayoutRemapError) as e:
+            lr.copy_plan(*args, tuning=bad)
+        assert e.value.code == lr.binding.ERR_INVALID, bad
+    with pytest.raises(KeyError):
+        lr.copy_plan(*args, tuning={"no_such_knob": 1})
+    # knobs of other paths are ignored; -1 everywhere is the planner's own plan
+    assert lr.copy_plan(*args, tuning={"gather_chunks": 8, "vector_order": 0}) == lr.copy_plan(*args)
+    assert lr.copy_plan(*args, tuning={k: -1 for k in lr.binding.TUNING_FIELDS}) == lr.copy_plan(*args)
+
+
+def _table_cycles(words):
+    """Cycles of one 32-lane phase reading 4-byte words, per the gfx950 read model
+    (32 banks of 4 bytes; a bank serves its distinct words one per cycle)."""
+    per_bank = {}
+    for wd in set(words):
+        per_bank[wd % 32] = per_bank.get(wd % 32, 0) + 1
+    return max(per_bank.values())
+
+
+def test_staged_gather_grouping_is_conflict_free_on_padded_tiles():
+    """The padded tiles' gather: with 32 lanes over two tiles (16 chunks each) every
+    LDS read is 2-way conflicted in the gfx950 model -- the two tiles' footprints put
+    3 words in some banks, and no tile stride evens that out.  Over four tiles x 8
+    chunks (one half of each) every read is conflict-free; the planner picks that."""
+    w = W.full("padtiles")
+    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 4)
+    assert p["path"] == "staged" and p["gather_chunks"] == 8, p
+    # The lane grouping rebuilt here: footprint word of element x of dst chunk c of a
+    # tile is 18x + c%8 + 9(c//8), tiles 72 words apart, 32-lane slices of cps chunks
+    # from each of 32/cps tiles.  A wave's read of one x is costed phase by phase in
+    # the gfx950 read model (4-byte accesses: 32 banks, 32 lanes a phase -- the model
+    # tests/test_gpu_lds_model.py holds against the bank-conflict counter).
+    def cycles(cps, cpt=16):
+        slices, G = cpt // cps, 32 // cps
+        total = 0
+        for w0 in range(0, 256, 64):
+            for x in range(4):
+                words = []
+                for l in range(64):
+                    q, li = (w0 + l) // 32, (w0 + l) % 32
+                    kk, c = (q // slices) * G + li // cps, (q % slices) * cps + li % cps
+                    words.append(72 * kk + 18 * x + c % 8 + 9 * (c // 8))
+                total += sum(_table_cycles(words[h:h + 32]) for h in (0, 32))
+        return total
+    assert cycles(16) == 2 * cycles(8)       # the old grouping: every phase 2-way
+    assert cycles(8) == 4 * 4 * 2            # 4 waves x 4 reads x 2 phases, 1 cycle each
+    # the override reproduces the old grouping
+    q = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 4, tuning={"gather_chunks": 16})
+    assert q["gather_chunks"] == 16
+    # a small footprint that is conflict-free either way keeps the widest grouping
+    p = lr.copy_plan("((4,8),2,64):((8,1),32,64)", 64 * 64, "((4,8),2,64):((1,4),32,64)", 64 * 64, 4)
+    if p["path"] == "staged":
+        assert p["gather_chunks"] in (8, 16)
+
+
+def test_vector_blocked_order_on_the_retile():
+    """Traversal order 2 of the vector path: lanes of a wave along the source (8
+    tiles' 128-byte rows of one source row), the 4 waves of a workgroup along the
+    destination (4 consecutive tile rows), the rest in source order -- the same copy,
+    as joint modes split at the wave and workgroup boundaries."""
+    w = W.full("retile")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    p = lr.copy_plan(*args, tuning={"vector_order": 2})
+    assert p["path"] == "vector" and p["vector_order"] == 2
+    assert p["joint"] == [(64, 1, 1), (8, 64, 8192), (4, 4096, 64), (8, 512, 65536), (32, 16384, 256),
+                          (32, 524288, 524288)], p["joint"]
+    src_order = lr.copy_plan(*args, tuning={"vector_order": 1})["joint"]
+    assert src_order == [(64, 1, 1), (64, 64, 8192), (128, 4096, 64), (32, 524288, 524288)], src_order
+    # every order covers the same (extent, source, destination) points
+    for t in (0, 1, 2):
+        j = lr.copy_plan(*args, tuning={"vector_order": t})["joint"]
+        assert math.prod(e for e, _, _ in j) == 1 << 24
+
+
+def test_plan_few_channel_images():
     """NHWC <-> NCHW with 2..8 channels of at most 16 bytes: the channel shuffle (the
     de-interleave one way; the interleave, through LDS unless the channel count is a
     power of two, the other).  Pixel counts that are not a multiple of one 16-byte
     chunk take its element-granular form; swizzles keep the general kernels."""
-    monkeypatch.delenv("LR_INARROW", raising=False)
-
     def image(n, h, w, c):
         hw = h * w
         return f"({n},{h},{w},{c}):({hw * c},{w * c},{c},1)", f"({n},{h},{w},{c}):({hw * c},{w},1,{hw})"
@@ -675,12 +813,10 @@ def test_plan_few_channel_images(monkeypatch):
         lr.copy_plan("(8,8):(1,8)", 64, "(8,8):(1,8)", 64, 2, lr.COPY_FORCE_PATH(lr.PATH_DEINTERLEAVE))
 
 
-def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
+def test_plan_element_tiles_where_chunks_do_not_fit():
     """Transposes whose rows allow no aligned 16-byte chunks take element tiles of
     256-byte rows, except 1-byte elements that still fit 4- or 8-byte chunks; with
     at least as many a-tiles as b-tiles the tiles go a fastest."""
-    monkeypatch.delenv("LR_TEL", raising=False)
-    monkeypatch.delenv("LR_TORDER", raising=False)
     # (n, bytes per element) -> element tiles?  (8190, 8) and (8192, 2) have full
     # 16-byte chunks; 1-byte elements in 4- and 8-byte chunks keep the chunks
     want = {(8191, 1): True, (8191, 2): True, (8191, 4): True, (8191, 8): True,
@@ -696,10 +832,12 @@ def test_plan_element_tiles_where_chunks_do_not_fit(monkeypatch):
     for r, c, order in ((4097, 16383, 0), (16383, 4097, 1)):
         p = lr.copy_plan(f"({r},{c}):({c},1)", r * c, f"({r},{c}):(1,{r})", r * c, 1)
         assert p["tile_a"] == 256 and p["order"] == order, (r, c, p)
-    monkeypatch.setenv("LR_TEL", "1")
-    assert lr.copy_plan("(8188,8188):(8188,1)", 8188 ** 2, "(8188,8188):(1,8188)", 8188 ** 2, 1)["tile_a"] == 256
-    monkeypatch.setenv("LR_TEL", "0")
-    assert lr.copy_plan("(8191,8191):(8191,1)", 8191 ** 2, "(8191,8191):(1,8191)", 8191 ** 2, 2)["tile_a"] == 16
+    p = lr.copy_plan("(8188,8188):(8188,1)", 8188 ** 2, "(8188,8188):(1,8188)", 8188 ** 2, 1,
+                     tuning={"element_tiles": 1})
+    assert p["tile_a"] == 256
+    p = lr.copy_plan("(8191,8191):(8191,1)", 8191 ** 2, "(8191,8191):(1,8191)", 8191 ** 2, 2,
+                     tuning={"element_tiles": 0})
+    assert p["tile_a"] == 16
 
 
 def test_plan_errors():

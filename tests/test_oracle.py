@@ -284,6 +284,70 @@ def test_zipped_divide_tile_3_5():
     assert offs == want and offs[0] == 5132 and offs[-1] == 6031
 
 
+def test_slice_tile_3_5_of_the_zipped_divide():
+    # [CuTe algebra page, section 3.2]: the tile at rest coordinate (3,5), the tile
+    # mode left free: a 4x8 layout whose offsets are the block {r + 128 c : r in
+    # [12,16), c in [40,48)} of the column-major 128x128 data
+    Z = O.zipped_divide(O.parse("(128,128):(1,128)"), (4, 8))
+    T, off = O.slice_layout(Z, (None, (3, 5)))
+    assert off == 3 * 4 + 5 * 1024 == 5132
+    assert O.fmt(T) == "(4,8):(1,128)"
+    got = sorted(off + O.eval_index(T, k) for k in range(32))
+    assert got == sorted(r + 128 * c for r in range(12, 16) for c in range(40, 48))
+    # the rest coordinate as one integer (colex inside the mode): 3 + 32 * 5
+    assert O.slice_layout(Z, (None, 3 + 32 * 5)) == (T, off)
+    # fixing the tile instead: the tile's element (1, 2) in every tile
+    R, off2 = O.slice_layout(Z, ((1, 2), None))
+    assert off2 == 1 + 2 * 128 and O.fmt(R) == "(32,16):(4,1024)"
+    # everything fixed: a single offset; nothing fixed: the layout itself
+    assert O.slice_layout(Z, ((3, 7), (31, 15))) == (O.Layout(1, 0), 3 + 7 * 128 + 31 * 4 + 15 * 1024)
+    assert 3 + 7 * 128 + 31 * 4 + 15 * 1024 == 128 * 128 - 1  # the last element
+    A, z = O.slice_layout(Z, (None, None))
+    assert z == 0 and O.fmt(A) == O.fmt(Z)
+
+
+def test_slice_definition_random():
+    """L(c) == offset + slice(L, fixed)(free part of c), for every c whose fixed
+    entries match, on random nested layouts; keeping leaves inside a nested mode."""
+    rng = random.Random(5)
+    hits = 0
+    for _ in range(400):
+        L = _rand_layout(rng, max_leaves=5)
+        top = O.top_modes(L)
+        # per top-level mode: None keeps it, an integer fixes it
+        coord = tuple(None if rng.random() < 0.5 else rng.randrange(O.size(m)) for m in top)
+        S, off = O.slice_layout(L, coord)
+        free = [i for i, c in enumerate(coord) if c is None]
+        sizes = [O.size(top[i]) for i in free]
+        assert O.size(S) == math.prod(sizes)
+        for k in range(O.size(S)):
+            full, r = list(coord), k
+            for i, n in zip(free, sizes):  # the kept modes, colex
+                full[i], r = r % n, r // n
+            c = tuple(full) if len(top) > 1 else full[0]
+            assert O.eval_coord(L, c) == off + O.eval_index(S, k), (O.fmt(L), coord)
+        hits += 1
+    assert hits == 400
+    # a leaf inside a nested mode: ((4,2),3):((1,8),4) keeping the 4, fixing the 2 at 1
+    S, off = O.slice_layout(O.parse("((4,2),3):((1,8),4)"), ((None, 1), None))
+    assert off == 8 and O.fmt(S) == "(4,3):(1,4)"
+
+
+def test_slice_of_a_swizzled_layout():
+    # the retile's destination: tile (r_t, c_t) of 128 x 64 elements starts at a
+    # multiple of 8192, past every bit Sw<3,3,3> reads or writes (bits 3..8), so the
+    # slice keeps the swizzle and the tile's own offsets are Sw(64 r + c)
+    L = O.parse("Sw<3,3,3> o ((128,32),(64,64)):((64,524288),(1,8192))")
+    S, off = O.slice_layout(L, ((None, 2), (None, 5)))
+    assert off == 2 * 524288 + 5 * 8192 and S.swz == (3, 3, 3)
+    for r in range(128):
+        for c in range(64):
+            assert O.eval_coord(L, ((r, 2), (c, 5))) == off + O.eval_coord(S, (r, c))
+    # a base inside the swizzled bits is not a layout plus an offset
+    with pytest.raises(OL.NotRepresentable):
+        O.slice_layout(L, ((1, None), None))
+
+
 def test_zipped_divide_definition_random():
     rng = random.Random(11)
     for _ in range(500):

@@ -21,8 +21,11 @@ Other modes (for rocprofv3 runs and their summaries under profiles/):
                         256 MiB copy whose counters scale FETCH_SIZE / WRITE_SIZE
   --summarize-counters DIR_FETCH DIR_WRITE [DIR_LDS]
                         read rocprofv3 --pmc CSV output and write profiles/traffic.json
-  --summarize-trace DIR read rocprofv3 --kernel-trace --stats CSV output and print
-                        a markdown table of per-kernel average durations
+  --summarize-trace DIR read rocprofv3 --kernel-trace CSV output and print a
+                        markdown table of the library's kernels (per grid size)
+  --launch NAME[:JSON]  (repeatable) launch workload NAME four times with the
+                        lr_copy_tuning overrides in JSON, e.g.
+                        padtiles:{"gather_chunks":16}, for before/after profiles
 """
 
 from __future__ import annotations
@@ -276,6 +279,25 @@ def counters_run(lr, torch, W, reps: int = 3):
           flush=True)
 
 
+def launch_run(lr, torch, W, specs, reps: int = 4):
+    """Each NAME[:JSON] spec: its workload launched `reps` times with the tuning."""
+    dev = torch.device("cuda:0")
+    for spec in specs:
+        name, _, js = spec.partition(":")
+        tuning = json.loads(js) if js else None
+        w = W.full(name)
+        s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)
+        d = torch.empty(w.dst_elems * w.elem_bytes, dtype=torch.uint8, device=dev)
+        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, tuning=tuning)
+        for _ in range(reps):
+            lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=w.elem_bytes, tuning=tuning)
+        torch.cuda.synchronize()
+        print(f"launch: {w.name} tuning={tuning} path={p['path']} grid={p['grid']} "
+              f"gather_chunks={p['gather_chunks']}", flush=True)
+        del s, d
+        torch.cuda.empty_cache()
+
+
 def _csv_rows(directory: str, suffix: str):
     rows = []
     for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
@@ -288,7 +310,8 @@ def _pmc_per_dispatch(directory: str, counter: str):
     """{dispatch id: (kernel name, grid size, counter value)} from a --pmc run."""
     out = {}
     for r in _csv_rows(directory, "counter_collection.csv"):
-        if r.get("Counter_Name") != counter:
+        # the library's kernels only (not torch's fills and random draws between them)
+        if r.get("Counter_Name") != counter or "lr::k_" not in r.get("Kernel_Name", ""):
             continue
         did = int(r["Dispatch_Id"])
         val = float(r["Counter_Value"])
@@ -337,18 +360,49 @@ def summarize_counters(d_fetch: str, d_write: str, d_lds: str = None) -> None:
     with open(os.path.join(PROFILES, "traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
-    print(json.dumps(out, indent=1))
+    # the markdown table of profiles/hbm_traffic_counters.md
+    import workloads as W
+
+    alg = {_traffic_key(n, W.full(n)): W.bytes_moved(W.full(n)) for n in (HEADLINE,) + OTHERS}
+    alg["plain_copy_256MiB"] = 2 << 28
+    print("| workload | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | algorithmic MB |"
+          " traffic / algorithmic | LDS bank-conflict cycles | LDS active cycles |")
+    print("|---" * 10 + "|")
+    for key in order:
+        e = out[key]
+        print(f"| {key} | `{_short(e['kernel'])}` | {e['fetch_kib']} | {e['write_kib']} | {e['read'] / 1e6:.1f} | "
+              f"{e['write'] / 1e6:.1f} | {alg[key] / 1e6:.1f} | {e['bytes_per_launch'] / alg[key]:.4f} | "
+              f"{e.get('lds_bank_conflict_cycles', '')} | {e.get('lds_active_cycles', '')} |")
 
 
-def summarize_trace(directory: str) -> None:
-    """Markdown table of per-kernel call counts and durations from a
-    rocprofv3 --kernel-trace --stats run."""
-    rows = _csv_rows(directory, "kernel_stats.csv")
-    print("| kernel | calls | avg us | min us | max us |")
-    print("|---|---|---|---|---|")
-    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        print(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+def _short(name: str) -> str:
+    return name.replace("void ", "").replace("lr::", "").split("(")[0]
+
+
+def summarize_trace(directory: str, groups_of: int = 0) -> None:
+    """Markdown table of the library's kernels from a rocprofv3 --kernel-trace run:
+    per kernel and grid size, the number of dispatches and their durations.  With
+    groups_of = N, the library's dispatches in launch order, N at a time (the
+    --launch runs: one group per spec)."""
+    import statistics
+
+    disp = sorted((int(r["Dispatch_Id"]), r) for r in _csv_rows(directory, "kernel_trace.csv")
+                  if "lr::k_" in r["Kernel_Name"])
+    groups = {}
+    for i, (_, r) in enumerate(disp):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1))
+        if groups_of:
+            key = (i // groups_of,) + key
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    head = "| launch group " if groups_of else ""
+    print(head + "| kernel | grid (work-items) | dispatches | mean us | median us | min us | max us |")
+    print("|---" * (8 if groups_of else 7) + "|")
+    order = sorted(groups.items()) if groups_of else sorted(groups.items(), key=lambda x: -sum(x[1]))
+    for key, v in order:
+        g0 = f"| {key[0] + 1} " if groups_of else ""
+        k, g = key[-2:]
+        print(g0 + f"| `{k}` | {g} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
+              f"{min(v):.2f} | {max(v):.2f} |")
 
 
 # ----------------------------------------------------------------------------
@@ -365,13 +419,15 @@ def main():
                     help="only launch each large workload a few times (for rocprofv3 runs)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--groups-of", type=int, default=0, help="with --summarize-trace: dispatches per launch group")
+    ap.add_argument("--launch", action="append", metavar="NAME[:JSON]")
     args = ap.parse_args()
 
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.groups_of)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the copy is measured on a single "
@@ -390,6 +446,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.counters:
         counters_run(lr, torch, W)
+        return
+    if args.launch:
+        launch_run(lr, torch, W, args.launch)
         return
 
     flags = 0

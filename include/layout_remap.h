@@ -188,10 +188,16 @@ int lr_logical_product(const lr_layout* A, const lr_layout* B, lr_layout* out);
  * number of top-level modes (LR_ERR_INVALID otherwise). */
 int lr_blocked_product(const lr_layout* A, const lr_layout* B, lr_layout* out);
 
-/* Injectivity of L as a function of the 1-D index: exact (a bitmap over the
- * offsets) when size <= 2^20; above that the sufficient test "sorted by stride,
- * each stride exceeds the largest offset of the smaller ones" (*result 0 then
- * means not proven injective).  A swizzle never changes the answer. */
+/* Injectivity of L as a function of the 1-D index.  With the leaves of extent > 1
+ * sorted by stride, a leaf whose stride exceeds the largest offset of the smaller
+ * ones is separated (its copies of their image cannot meet), so L is injective
+ * exactly when the leaves up to the last one that is not separated are; those are
+ * enumerated over their offsets.  Exact whenever that prefix has at most 2^22
+ * elements (any layout of at most 2^22 elements, and any larger one whose big
+ * leaves are separated,
+ * e.g. (3,2,M):(2,3,8) for every M); beyond that *result 0 means not proven
+ * injective.  A stride-0 leaf of extent > 1 is not injective.  A swizzle never
+ * changes the answer. */
 int lr_is_injective(const lr_layout* L, int32_t* result);
 
 /* Widest vector (in elements, a power of two with elems*elem_bytes <= 16) that a
@@ -309,7 +315,8 @@ typedef struct {
                           default when the source plus destination bytes reach 64 MiB, a
                           quarter of the 256 MiB last-level cache, except for element tiles
                           (transposes of rows without aligned 16-byte chunks), which keep
-                          ordinary accesses at any size */
+                          ordinary accesses at any size, and the element-granular channel
+                          shuffle (planes without aligned chunks), which streams from 256 MiB */
   int32_t order;       /* transpose: workgroup -> tile order (0 a-tiles fastest, 1 b-tiles
                           fastest, 2 diagonal with a fastest, 3 diagonal over 4 x 4 tile groups,
                           4 diagonal with b fastest); -1 on other paths */
@@ -423,6 +430,21 @@ int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_el
 int lr_layout_copy_tuned(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
                          void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
                          size_t elem_bytes, uint32_t flags, const lr_copy_tuning* tuning, void* stream);
+
+/* Debugging aid (the write-race check of an injective copy): lr_layout_copy_tuned
+ * that also counts, for every destination element, the stores the kernels make to
+ * it.  counts: device int32[dst_capacity_elems], owned and zeroed by the caller;
+ * each store of n elements atomically adds 1 to each of their counters.  The copy
+ * itself is the same launch configuration and gives the same bytes.  A correct
+ * copy leaves 1 at every offset in the image of Ld and 0 elsewhere -- also for an
+ * aliased Ld under LR_COPY_ORDERED_ALIAS, where only the last writer of each
+ * offset stores ([CuTe algebra page, section 2.3]: the copy moves each element
+ * from its source offset to its destination offset).  Slow: meant for tests.
+ * LR_ERR_INVALID if counts is NULL; every other error as lr_layout_copy. */
+int lr_layout_copy_count_writes(const void* src, const lr_layout* Ls, int64_t src_capacity_elems,
+                                void* dst, const lr_layout* Ld, int64_t dst_capacity_elems,
+                                size_t elem_bytes, uint32_t flags, const lr_copy_tuning* tuning,
+                                int32_t* counts, void* stream);
 
 /* ------------------------------------------------------------------ misc */
 

@@ -200,6 +200,9 @@ _SIGS = {
                                       ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p]),
     "lr_layout_copy_tuned": (ctypes.c_int, [ctypes.c_void_p, _L, ctypes.c_int64, ctypes.c_void_p, _L, ctypes.c_int64,
                                             ctypes.c_size_t, ctypes.c_uint32, _P(lr_copy_tuning), ctypes.c_void_p]),
+    "lr_layout_copy_count_writes": (ctypes.c_int, [ctypes.c_void_p, _L, ctypes.c_int64, ctypes.c_void_p, _L,
+                                                   ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32,
+                                                   _P(lr_copy_tuning), ctypes.c_void_p, ctypes.c_void_p]),
     "lr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "lr_last_hip_error": (ctypes.c_char_p, []),
     "lr_version": (ctypes.c_char_p, []),
@@ -584,3 +587,28 @@ def copy_plan_tuned(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: in
 def layout_copy_tuned(src, Ls, dst, Ld, tuning: dict, elem_bytes: Optional[int] = None, flags: int = 0, stream=None):
     """lr_layout_copy_tuned: layout_copy with overrides."""
     return layout_copy(src, Ls, dst, Ld, elem_bytes, flags, stream, tuning=tuning)
+
+
+def layout_copy_count_writes(src, Ls, dst, Ld, counts, elem_bytes: Optional[int] = None, flags: int = 0,
+                             stream=None, tuning: Optional[dict] = None):
+    """lr_layout_copy_count_writes: layout_copy that also adds, in the int32 GPU
+    tensor ``counts`` (one entry per destination element, zeroed by the caller),
+    one per store the kernels make to each destination element."""
+    torch = _torch()
+    _device_tensor(src, "src")
+    _device_tensor(dst, "dst")
+    _device_tensor(counts, "counts")
+    if counts.dtype != torch.int32:
+        raise TypeError("counts must be int32")
+    Ls, Ld = _as_layout(Ls), _as_layout(Ld)
+    eb = elem_bytes if elem_bytes is not None else src.element_size()
+    sb = src.numel() * src.element_size()
+    db = dst.numel() * dst.element_size()
+    if sb % eb or db % eb:
+        raise ValueError("buffer sizes are not multiples of elem_bytes")
+    if counts.numel() < db // eb:
+        raise ValueError("counts needs one entry per destination element")
+    _check(lib().lr_layout_copy_count_writes(src.data_ptr(), ctypes.byref(Ls.c), sb // eb, dst.data_ptr(),
+                                             ctypes.byref(Ld.c), db // eb, eb, flags, _tuning(tuning),
+                                             counts.data_ptr(), _stream_ptr(stream)), "layout_copy_count_writes")
+    return counts

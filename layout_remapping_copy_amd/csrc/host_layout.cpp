@@ -113,35 +113,60 @@ static std::vector<Leaf> coalesce_leaves(const std::vector<Leaf>& in) {
 }
 
 bool injective(const lr_layout* L) {
-  // sufficient test: sorted by stride, each stride above everything below it
+  // Leaves of extent > 1 sorted by stride.  A leaf whose stride exceeds the largest
+  // offset R of the smaller-stride leaves is separated: its translates of their
+  // image lie in the disjoint ranges [c d, c d + R], so it keeps (or breaks)
+  // injectivity exactly as the smaller leaves alone do.  The whole layout is
+  // therefore injective iff the prefix up to the last leaf that is not separated
+  // is, and that prefix is checked exactly over its own offsets (a swizzle is a
+  // bijection and changes nothing).  A stride-0 leaf of extent > 1 repeats offsets.
   std::vector<Leaf> lv;
   for (int i = 0; i < L->nleaves; ++i)
     if (L->shape[i] > 1) lv.push_back({L->shape[i], L->stride[i]});
   std::sort(lv.begin(), lv.end(), [](const Leaf& x, const Leaf& y) { return x.d < y.d || (x.d == y.d && x.n < y.n); });
-  bool suff = true;
+  int last = -1;
   int64_t reach = 0;
-  for (const Leaf& l : lv) {
-    if (l.d == 0 || l.d < reach + 1) {
-      suff = false;
-      break;
-    }
-    reach += (l.n - 1) * l.d;
+  for (int k = 0; k < (int)lv.size(); ++k) {
+    if (lv[k].d == 0) return false;
+    if (lv[k].d <= reach) last = k;
+    reach += (lv[k].n - 1) * lv[k].d;
   }
-  if (suff) return true;
-  int64_t n = size_of(L);
-  if (n > (int64_t(1) << 20)) return false;  // not proven
-  // exact for small layouts: enumerate unswizzled offsets (the swizzle is a bijection)
-  std::vector<int64_t> offs((size_t)n);
+  if (last < 0) return true;
+  int64_t n = 1, cos = 1;
+  for (int k = 0; k <= last; ++k) {
+    n *= lv[k].n;
+    cos += (lv[k].n - 1) * lv[k].d;
+    if (n > kExactInjectiveElems) return false;  // not proven
+  }
+  // the prefix's offsets, by an odometer over its leaves: a bitmap of one bit per
+  // offset when the span is at most 2^26 (8 MiB), else sorted
+  std::vector<bool> seen;
+  std::vector<int64_t> offs;
+  const bool bitmap = cos <= (int64_t(1) << 26);
+  if (bitmap)
+    seen.assign((size_t)cos, false);
+  else
+    offs.reserve((size_t)n);
+  int64_t digit[LR_MAX_LEAVES] = {0}, o = 0;
   for (int64_t k = 0; k < n; ++k) {
-    int64_t r = k, o = 0;
-    for (int i = 0; i < L->nleaves; ++i) {
-      o += (r % L->shape[i]) * L->stride[i];
-      r /= L->shape[i];
+    if (bitmap) {
+      if (seen[(size_t)o]) return false;
+      seen[(size_t)o] = true;
+    } else {
+      offs.push_back(o);
     }
-    offs[(size_t)k] = o;
+    for (int j = 0; j <= last; ++j) {
+      o += lv[j].d;
+      if (++digit[j] < lv[j].n) break;
+      o -= lv[j].n * lv[j].d;
+      digit[j] = 0;
+    }
   }
-  std::sort(offs.begin(), offs.end());
-  return std::adjacent_find(offs.begin(), offs.end()) == offs.end();
+  if (!bitmap) {
+    std::sort(offs.begin(), offs.end());
+    return std::adjacent_find(offs.begin(), offs.end()) == offs.end();
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------- composition

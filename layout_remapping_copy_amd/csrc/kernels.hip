@@ -139,6 +139,21 @@ __device__ __forceinline__ void load_to_lds16(const void* g, void* lds_wave) {
   __builtin_amdgcn_global_load_lds((const global_void_t*)g, (lds_void_t*)lds_wave, 16, 0, NT ? 2 : 0);
 }
 
+// Write counting for lr_layout_copy_count_writes: every store of nbytes at p adds
+// one to the counter of each destination element (of 2^shift bytes) it covers.
+// Ordinary copies pass wc == NULL and skip it with one uniform branch.
+struct WriteCount {
+  int32_t* wc;
+  uint32_t shift;
+};
+
+__device__ __forceinline__ void count_store(const WriteCount& w, const void* dst_base, const void* p,
+                                            uint32_t nbytes) {
+  if (w.wc == nullptr) return;
+  const size_t b = (size_t)((const char*)p - (const char*)dst_base);
+  for (uint32_t i = 0; i < nbytes; i += (1u << w.shift)) atomicAdd(w.wc + ((b + i) >> w.shift), 1);
+}
+
 // ------------------------------------------------------------------ eval
 
 struct EvalArgs {
@@ -308,6 +323,7 @@ struct GenericArgs {
   int64_t n_units;
   int64_t n_chunks;  // groups of 256 * U units, U the per-lane unroll
   uint32_t bufst;    // 1: streaming 16-byte stores as buffer stores from dst (span < 4 GiB)
+  WriteCount wcnt;
 };
 
 // One unit (UB bytes) per lane and step, one or four units per lane (U); with four,
@@ -373,6 +389,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
           generic_offsets<false>(a, i0, &s0, &d0);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, gload<LNT, T>(src + s0)),
                                                  rd, (uint32_t)(d0 * 16), 0, kPolicyNtSc1);
+          count_store(a.wcnt, a.dst, (const char*)a.dst + d0 * 16, 16);
         }
       }
       return;
@@ -385,6 +402,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
         uint64_t s0, d0;
         generic_offsets<WIDE>(a, i0, &s0, &d0);
         gstore<SNT, T>(dst + d0, gload<LNT, T>(src + s0));
+        count_store(a.wcnt, a.dst, dst + d0, UB);
       }
     } else {
       uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, d0 = 0, d1 = 0, d2 = 0, d3 = 0;
@@ -403,6 +421,10 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
       if (k1) gstore<SNT, T>(dst + d1, v1);
       if (k2) gstore<SNT, T>(dst + d2, v2);
       if (k3) gstore<SNT, T>(dst + d3, v3);
+      if (k0) count_store(a.wcnt, a.dst, dst + d0, UB);
+      if (k1) count_store(a.wcnt, a.dst, dst + d1, UB);
+      if (k2) count_store(a.wcnt, a.dst, dst + d2, UB);
+      if (k3) count_store(a.wcnt, a.dst, dst + d3, UB);
     }
   }
 }
@@ -447,6 +469,7 @@ struct DualArgs {
   SideArg s, d;
   int64_t n;
   int64_t n_chunks;
+  WriteCount wcnt;
 };
 
 // Each lane evaluates both layouts from the index (used when the two layouts have
@@ -464,10 +487,18 @@ __global__ void __launch_bounds__(256) k_dual(DualArgs a) {
     if (k1) v1 = gload<false, T>(src + side_eval<WIDE>(a.s, i0 + 256));
     if (k2) v2 = gload<false, T>(src + side_eval<WIDE>(a.s, i0 + 512));
     if (k3) v3 = gload<false, T>(src + side_eval<WIDE>(a.s, i0 + 768));
-    if (k0) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0), v0);
-    if (k1) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0 + 256), v1);
-    if (k2) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0 + 512), v2);
-    if (k3) gstore<false, T>(dst + side_eval<WIDE>(a.d, i0 + 768), v3);
+    T* q0 = k0 ? dst + side_eval<WIDE>(a.d, i0) : dst;
+    T* q1 = k1 ? dst + side_eval<WIDE>(a.d, i0 + 256) : dst;
+    T* q2 = k2 ? dst + side_eval<WIDE>(a.d, i0 + 512) : dst;
+    T* q3 = k3 ? dst + side_eval<WIDE>(a.d, i0 + 768) : dst;
+    if (k0) gstore<false, T>(q0, v0);
+    if (k1) gstore<false, T>(q1, v1);
+    if (k2) gstore<false, T>(q2, v2);
+    if (k3) gstore<false, T>(q3, v3);
+    if (k0) count_store(a.wcnt, a.dst, q0, EB);
+    if (k1) count_store(a.wcnt, a.dst, q1, EB);
+    if (k2) count_store(a.wcnt, a.dst, q2, EB);
+    if (k3) count_store(a.wcnt, a.dst, q3, EB);
   }
 }
 
@@ -496,7 +527,10 @@ __global__ void __launch_bounds__(1024) k_alias(DualArgs a) {
   __syncthreads();
   for (int64_t k = threadIdx.x; k < a.n; k += 1024) {
     int64_t o = (int64_t)side_eval<false>(a.d, k) - w0;
-    if (o >= 0 && o < kAliasWindow && owner[o] == (int)k) dst[w0 + o] = src[side_eval<false>(a.s, k)];
+    if (o >= 0 && o < kAliasWindow && owner[o] == (int)k) {
+      dst[w0 + o] = src[side_eval<false>(a.s, k)];
+      count_store(a.wcnt, a.dst, dst + w0 + o, EB);
+    }
   }
 }
 
@@ -566,6 +600,7 @@ struct TransposeArgs {
   // bits a destination swizzle may change); the host checks that every offset of a
   // tile lies less than 4 GiB above that base
   uint32_t bufst, bufmask;
+  WriteCount wcnt;
 };
 
 // Workgroup number -> (a-tile, b-tile, batch index) in the order t.order selects.
@@ -682,6 +717,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
       for (int i = 0; i < V; ++i) {
         uint32_t dof = swz32((a_blk + i) * t.sd_a + b_blk + bd, t.swd);
         gstore<NT, C>(dst + (size_t)dof * EB, out[i]);
+        count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
       }
     }
     return;
@@ -712,6 +748,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
           const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, v), rd,
                                                  (dof - tbase) * EB, 0, kPolicyNtSc1);
+          count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, 16);
         }
       }
       return;
@@ -725,6 +762,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
       C v = tile[row][c ^ ((row / V) % TB)];
       uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
       gstore<NT, C>(dst + (size_t)dof * EB, v);
+      count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
     }
   }
 }
@@ -794,6 +832,7 @@ __global__ void __launch_bounds__(512) k_transpose_el(TransposeArgs t) {
       if (a < t.ext_a && b < t.ext_b) {
         const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
         gstore<NT, T>(dst + (size_t)dof * EB, v[i]);
+        count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, EB);
       }
     }
   }
@@ -891,6 +930,7 @@ __global__ void __launch_bounds__(512) k_transpose_win(TransposeArgs t) {
 #pragma unroll
         for (uint32_t k = 0; k < V; ++k) o.e[k] = *(const T*)(c0 + k * P);
         gstore<NT, Ch>(g + w.a0 + 16u * j, o);
+        count_store(t.wcnt, t.dst, g + w.a0 + 16u * j, 16);
       }
 #pragma unroll
       for (uint32_t u = 0; u < NE; ++u) {
@@ -898,6 +938,7 @@ __global__ void __launch_bounds__(512) k_transpose_win(TransposeArgs t) {
         if (k < w.head + w.tail) {
           const uint32_t b = k < w.head ? k : w.head + V * w.nint + (k - w.head);
           gstore<NT, T>(g + (size_t)b * EB, *(const T*)(col + b * P));
+          count_store(t.wcnt, t.dst, g + (size_t)b * EB, EB);
         }
       }
     }
@@ -967,6 +1008,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose_dl(TransposeArgs t) {
     if (a < t.ext_a && b < t.ext_b) {
       const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
       gstore<NT, C>(dst + (size_t)dof * EB, out[i]);
+      count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
     }
   }
   (void)NTH;
@@ -984,6 +1026,7 @@ struct InterleaveArgs {
   BatchArg batch;
   SwzArg sws, swd;
   uint32_t bufst;        // 1: streaming stores as buffer stores from dst (span < 4 GiB)
+  WriteCount wcnt;
 };
 
 // The dst-contiguous mode b is short (NB * EB <= 16 bytes) and a follows it in
@@ -1042,10 +1085,12 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
           const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, -1, kBufferWord3);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(typename NativeOf<16>::T, o), rd, dof * EB, 0,
                                                  kPolicyNtSc1);
+          count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, 16);
           continue;
         }
       }
       gstore<NT, C>(dst + (size_t)dof * EB, o);
+      count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
     }
   } else {
     constexpr int U = NB >= 8 ? 1 : 8 / NB;  // a-chunks per lane: U * NB loads in flight
@@ -1077,6 +1122,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
         }
         uint32_t dof = swz32(a0 * NB + c * V + bd, t.swd);
         gstore<NT, C>(dst + (size_t)dof * EB, o);
+        count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
       }
     }
   }
@@ -1093,6 +1139,7 @@ struct ChanArgs {
   FD fd_tiles;
   BatchArg batch;
   uint32_t bufst;    // 1: streaming stores as buffer stores from dst (span < 4 GiB)
+  WriteCount wcnt;
 };
 
 // A 16-byte streaming store: a buffer store with the nt and sc1 bits from `base`
@@ -1169,7 +1216,11 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
 #pragma unroll
     for (int e = 0; e < C * V; ++e) out[e % C].e[e / C] = in[e / V].e[e % V];  // element e: pixel e / C, channel e % C
 #pragma unroll
-    for (int c = 0; c < C; ++c) store16<NT>(dst, (size_t)(c * t.plane + p0 + V * l + bd) * EB, out[c], t.bufst);
+    for (int c = 0; c < C; ++c) {
+      const size_t off = (size_t)(c * t.plane + p0 + V * l + bd) * EB;
+      store16<NT>(dst, off, out[c], t.bufst);
+      count_store(t.wcnt, t.dst, dst + off, 16);
+    }
   } else {
     if (mine) {
       Ch in[C], out[C];
@@ -1184,7 +1235,10 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
     const size_t db = (size_t)(p0 * C + bd) * EB;
 #pragma unroll
     for (int j = 0; j < C; ++j)
-      if (l + 256u * j < nblk * C) store16<NT>(dst, db + (size_t)(l + 256u * j) * 16, lds[l + 256u * j], t.bufst);
+      if (l + 256u * j < nblk * C) {
+        store16<NT>(dst, db + (size_t)(l + 256u * j) * 16, lds[l + 256u * j], t.bufst);
+        count_store(t.wcnt, t.dst, dst + db + (size_t)(l + 256u * j) * 16, 16);
+      }
   }
 }
 
@@ -1261,10 +1315,12 @@ __global__ void __launch_bounds__(256) k_chan_win(ChanArgs t) {
 #pragma unroll
         for (uint32_t k = 0; k < V; ++k) o.e[k] = *(const T*)(lds + win_pos<C>(x + k * C * EB));
         gstore<NT, Ch>(gp + wp.a0 + 16u * l, o);
+        count_store(t.wcnt, t.dst, gp + wp.a0 + 16u * l, 16);
       }
       if (l < wp.head + wp.tail) {
         const uint32_t px = l < wp.head ? l : wp.head + V * wp.nint + (l - wp.head);
         gstore<NT, T>(gp + (size_t)px * EB, *(const T*)(lds + win_pos<C>(m + (px * C + c) * EB)));
+        count_store(t.wcnt, t.dst, gp + (size_t)px * EB, EB);
       }
     }
   } else {
@@ -1300,11 +1356,15 @@ __global__ void __launch_bounds__(256) k_chan_win(ChanArgs t) {
 #pragma unroll
     for (uint32_t j = 0; j < (uint32_t)C; ++j) {
       const uint32_t q = l + 256u * j;
-      if (q < wi.nint) gstore<NT, Ch>((char*)gi + wi.a0 + 16u * q, *(const Ch*)(lds + win_pos<C>(m + wi.a0 + 16u * q)));
+      if (q < wi.nint) {
+        gstore<NT, Ch>((char*)gi + wi.a0 + 16u * q, *(const Ch*)(lds + win_pos<C>(m + wi.a0 + 16u * q)));
+        count_store(t.wcnt, t.dst, gi + wi.a0 + 16u * q, 16);
+      }
     }
     if (l < wi.head + wi.tail) {
       const uint32_t eo = l < wi.head ? l * EB : wi.a1 + (l - wi.head) * EB;
       gstore<NT, T>((char*)gi + eo, *(const T*)(lds + win_pos<C>(m + eo)));
+      count_store(t.wcnt, t.dst, gi + eo, EB);
     }
   }
 }
@@ -1330,6 +1390,7 @@ struct StagedArgs {
   FD fd_tg;
   BatchArg batch;
   SwzArg swd;
+  WriteCount wcnt;
 };
 
 // Padded or gathered tiles ([CuTe algebra page, section 2.2]: composing a padded
@@ -1424,6 +1485,7 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
     for (int x = 0; x < V; ++x) o.e[x] = ldsT[base + g[x]];
     uint32_t dof = swz32(tile * t.Td + bd + c * V, t.swd);
     gstore<NT, C>(dst + (size_t)dof * EB, o);
+    count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
   }
 }
 
@@ -1658,13 +1720,14 @@ static size_t ptr_align(const void* p) {
 }
 
 static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_layout* Ld, const Plan& p,
-                    hipStream_t st) {
+                    hipStream_t st, WriteCount wc) {
   const unsigned grid = grid_cap(p.grid);
   switch (p.path) {
     case LR_PATH_GENERIC:
     case LR_PATH_VECTOR: {
       GenericArgs a;
       std::memset(&a, 0, sizeof(a));
+      a.wcnt = wc;
       a.src = src;
       a.dst = dst;
       a.rank = p.rank;
@@ -1696,6 +1759,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
     case LR_PATH_ALIAS: {
       DualArgs a;
       std::memset(&a, 0, sizeof(a));
+      a.wcnt = wc;
       a.src = src;
       a.dst = dst;
       fill_side(&a.s, Ls, p.wide);
@@ -1713,6 +1777,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
     case LR_PATH_TRANSPOSE_DIRECT: {
       TransposeArgs a;
       std::memset(&a, 0, sizeof(a));
+      a.wcnt = wc;
       a.src = src;
       a.dst = dst;
       const int64_t ext_b = p.m[p.b].ext * (p.b2 >= 0 ? p.m[p.b2].ext : 1);
@@ -1773,6 +1838,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         const int pm = il ? p.a : p.b, cm = il ? p.b : p.a;
         ChanArgs a;
         std::memset(&a, 0, sizeof(a));
+        a.wcnt = wc;
         a.src = src;
         a.dst = dst;
         a.pixels = (uint32_t)p.m[pm].ext;
@@ -1790,6 +1856,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       {
       InterleaveArgs a;
       std::memset(&a, 0, sizeof(a));
+      a.wcnt = wc;
       a.src = src;
       a.dst = dst;
       a.ext_a = (uint32_t)p.m[p.a].ext;
@@ -1808,6 +1875,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
     case LR_PATH_STAGED: {
       StagedArgs a;
       std::memset(&a, 0, sizeof(a));
+      a.wcnt = wc;
       a.src = src;
       a.dst = dst;
       a.inner = p.staged_inner;
@@ -1965,15 +2033,34 @@ int lr_layout_eval_coords(const lr_layout* L, const int64_t* coords, int64_t n, 
   return check_launch();
 }
 
+static int copy_impl(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst,
+                     const lr_layout* Ld, int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags,
+                     const lr_copy_tuning* tuning, int32_t* counts, void* stream);
+
 int lr_layout_copy(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst, const lr_layout* Ld,
                    int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags, void* stream) {
-  return lr_layout_copy_tuned(src, Ls, src_capacity_elems, dst, Ld, dst_capacity_elems, elem_bytes, flags, nullptr,
-                              stream);
+  return copy_impl(src, Ls, src_capacity_elems, dst, Ld, dst_capacity_elems, elem_bytes, flags, nullptr, nullptr,
+                   stream);
 }
 
 int lr_layout_copy_tuned(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst,
                          const lr_layout* Ld, int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags,
                          const lr_copy_tuning* tuning, void* stream) {
+  return copy_impl(src, Ls, src_capacity_elems, dst, Ld, dst_capacity_elems, elem_bytes, flags, tuning, nullptr,
+                   stream);
+}
+
+int lr_layout_copy_count_writes(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst,
+                                const lr_layout* Ld, int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags,
+                                const lr_copy_tuning* tuning, int32_t* counts, void* stream) {
+  if (!counts) return LR_ERR_INVALID;
+  return copy_impl(src, Ls, src_capacity_elems, dst, Ld, dst_capacity_elems, elem_bytes, flags, tuning, counts,
+                   stream);
+}
+
+static int copy_impl(const void* src, const lr_layout* Ls, int64_t src_capacity_elems, void* dst,
+                     const lr_layout* Ld, int64_t dst_capacity_elems, size_t elem_bytes, uint32_t flags,
+                     const lr_copy_tuning* tuning, int32_t* counts, void* stream) {
   if (!src || !dst) return LR_ERR_INVALID;
   Plan p;
   int rc = plan_copy(Ls, src_capacity_elems, ptr_align(src), Ld, dst_capacity_elems, ptr_align(dst), elem_bytes,
@@ -1988,7 +2075,9 @@ int lr_layout_copy_tuned(const void* src, const lr_layout* Ls, int64_t src_capac
   int64_t cext[kMaxJoint], nblocks = 0;
   const bool cut = block_extents(p, flags, cext, &nblocks);
   if (log_enabled()) log_plan(p, cut ? nblocks : 1);
-  if (!cut) return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream);
+  uint32_t wshift = 0;
+  while ((size_t(1) << wshift) < elem_bytes) ++wshift;
+  if (!cut) return run_copy(src, Ls, dst, Ld, p, (hipStream_t)stream, WriteCount{counts, wshift});
   // too large for 32-bit offsets: blocks of the joint modes, each within 32 bits,
   // launched one after another on the stream (disjoint parts of an injective copy)
   int64_t start[kMaxJoint] = {0};
@@ -2005,7 +2094,8 @@ int lr_layout_copy_tuned(const void* src, const lr_layout* Ls, int64_t src_capac
     inherit_policy(p, &pb);  // the whole copy's load and store policies
     if ((rc = verify_plan(pb, cs, cd))) return rc;
     if (log_enabled() && blk == 0) log_plan(pb, -1);
-    if ((rc = run_copy(s, &ls, d, &ld, pb, (hipStream_t)stream))) return rc;
+    if ((rc = run_copy(s, &ls, d, &ld, pb, (hipStream_t)stream, WriteCount{counts ? counts + od : nullptr, wshift})))
+      return rc;
     for (int k = 0; k < p.rank; ++k) {  // next block, mode 0 fastest
       start[k] += cext[k];
       if (start[k] < p.m[k].ext) break;

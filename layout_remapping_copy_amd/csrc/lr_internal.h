@@ -25,7 +25,12 @@ int validate(const lr_layout* L);
 int64_t size_of(const lr_layout* L);            // valid L only
 int64_t max_linear_offset(const lr_layout* L);  // valid L only, unswizzled
 int64_t cosize_bound(const lr_layout* L);       // valid L only
-bool injective(const lr_layout* L);             // valid L only
+bool injective(const lr_layout* L);             // valid L only; exact within the limits below
+
+// Limit of the exact injectivity check: the leaves that are not separated by
+// stride (see injective) are enumerated when their combined extent stays within
+// it; beyond it the answer is "not proven injective".
+constexpr int64_t kExactInjectiveElems = int64_t(1) << 22;
 
 // Multiply-high division by an invariant divisor d (1 <= d < 2^31), exact for
 // dividends x < 2^31 (Granlund & Montgomery, "Division by Invariant Integers using

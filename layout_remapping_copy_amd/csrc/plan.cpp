@@ -173,6 +173,10 @@ static bool plan_chan_elements(Plan* p, int a, int b, bool interleave, size_t sr
   for (int k = 0; k < p->rank; ++k)
     if (k != a && k != b) batch *= p->m[k].ext;
   p->grid = ((p->m[pm].ext + p->tile_a - 1) / p->tile_a) * batch;
+  // Its ranges start unaligned, so their partial lines at both ends merge in the
+  // cache under ordinary accesses: streaming only from the 256 MiB last-level cache
+  // size (source plus destination), unless the caller chose a policy.
+  if (!p->policy_set) p->nt = p->nt_ld = p->n >= (int64_t(128) << 20) / p->orig_eb;
   return true;
 }
 

@@ -33,6 +33,8 @@ import re
 from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple, Union
 
+import math
+
 import numpy as np
 
 Nested = Union[int, tuple]
@@ -723,11 +725,36 @@ def injective_sufficient(L: Layout) -> bool:
     return True
 
 
+# Limit of the exact check on the leaves that are not separated by stride: their
+# combined extent.  Beyond it: "not proven injective".
+EXACT_INJECTIVE_ELEMS = 1 << 22
+
+
 def is_injective(L: Layout) -> bool:
-    """Exact by brute force up to 2**20 elements; the sufficient test above that."""
+    """Exact by brute force up to 2**20 elements.  Above that: with the leaves of
+    extent > 1 sorted by stride, a leaf whose stride exceeds the largest offset
+    reachable by the smaller ones is separated -- its translates of their image
+    lie in disjoint ranges -- so L is injective iff the leaves up to the last one
+    that is not separated are; those are brute-forced (within the limit above,
+    else not proven).  A stride-0 leaf of extent > 1 is never injective."""
     if size(L) <= BRUTE_INJECTIVE_LIMIT:
         return is_injective_bruteforce(L)
-    return injective_sufficient(L)
+    leaves = sorted((d, n) for n, d in flatten(L) if n > 1)
+    if any(d == 0 for d, _ in leaves):
+        return False
+    last, reach = -1, 0
+    for k, (d, n) in enumerate(leaves):
+        if d <= reach:
+            last = k
+        reach += (n - 1) * d
+    if last < 0:
+        return True
+    prefix = leaves[: last + 1]
+    if math.prod(n for _, n in prefix) > EXACT_INJECTIVE_ELEMS:
+        return False
+    P = Layout(tuple(n for _, n in prefix), tuple(d for d, _ in prefix)) if len(prefix) > 1 else \
+        Layout(prefix[0][1], prefix[0][0])
+    return is_injective_bruteforce(P)
 
 
 # ----------------------------------------------------------------------------

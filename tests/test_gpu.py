@@ -463,6 +463,82 @@ def test_copy_random_pairs(dev, knobs):
     assert runs > 3000
 
 
+def _write_counts(dev, src, ts, dst, td, eb, flags=0):
+    s = torch.from_numpy(src).to(dev)
+    d = torch.from_numpy(dst).to(dev)
+    counts = torch.zeros(dst.nbytes // eb, dtype=torch.int32, device=dev)
+    lr.layout_copy_count_writes(s, ts, d, td, counts, elem_bytes=eb, flags=flags, tuning=KNOBS.tuning())
+    torch.cuda.synchronize()
+    return d.cpu().numpy(), counts.cpu().numpy()
+
+
+def _multiplicity(Ld, n, nd):
+    """How many logical indices the oracle sends to each destination offset."""
+    return np.bincount(O.eval_indices(Ld, np.arange(n)), minlength=nd)
+
+
+def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
+    """The kernels store every destination element exactly once: each offset the
+    oracle's copy writes (multiplicity >= 1) is stored once, every other offset
+    never -- on random pairs under the default plan, every forced path and random
+    tuning, and on the aliased 8x8 tile, where offsets 16..31 have multiplicity two
+    and only the last writer stores.  The copied bytes are checked too."""
+    w = W.tile8x8()
+    src, dst = W.make_src(w), W.make_dst(w)
+    Ld = O.parse(w.dst_layout)
+    mult = _multiplicity(Ld, 64, 64)
+    assert mult[16:32].tolist() == [2] * 16 and mult[48:].tolist() == [0] * 16
+    got, counts = _write_counts(dev, src, w.src_layout, dst, w.dst_layout, 4, lr.COPY_ORDERED_ALIAS)
+    assert np.array_equal(counts, (mult > 0).astype(np.int32))
+    assert np.array_equal(got, O.copy(src, O.parse(w.src_layout), dst, Ld, 4, ordered_alias=True))
+    rng = random.Random(77)
+    runs = 0
+    for i in range(150):
+        ts, td, ns, nd = _rand_pair(rng)
+        eb = rng.choice([1, 2, 4, 8, 16])
+        src = np.random.default_rng(1000 + i).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        Ls, Ld = O.parse(ts), O.parse(td)
+        want = O.copy(src, Ls, dst, Ld, eb)
+        mult = _multiplicity(Ld, O.size(Ls), nd)
+        knobs.t.clear()
+        knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 4), gather_chunks=rng.choice([-1, 8, 16]),
+                  vector_order=rng.choice([-1, 0, 1, 2]), element_tiles=rng.choice([-1, 0, 1]))
+        for flags in [0] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
+            try:
+                p = plan(ts, ns, td, nd, eb, flags)
+            except lr.LayoutRemapError as e:
+                assert e.code == lr.binding.ERR_PATH and flags
+                continue
+            got, counts = _write_counts(dev, src, ts, dst, td, eb, flags)
+            assert np.array_equal(counts, mult), (i, ts, td, eb, p["path"])
+            assert np.array_equal(got, want), (i, ts, td, eb, p["path"])
+            runs += 1
+        if i % 50 == 0:
+            say("write counts", i, ts, "->", td, "eb", eb)
+    assert runs > 600
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles"])
+def test_write_counts_full_size(dev, name):
+    """At full size, in the launch configuration the benchmark times: the
+    destination layouts are bijections onto [0, N) (the oracle's injectivity test
+    and cosize == size), so a correct copy stores every element exactly once."""
+    w = W.full(name)
+    Ld = O.parse(w.dst_layout)
+    assert O.is_injective(Ld) and O.cosize(Ld) == w.n_elems == w.dst_elems
+    s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)
+    d = torch.empty(w.dst_elems * w.elem_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.zeros(w.dst_elems, dtype=torch.int32, device=dev)
+    say("write counts full", w.name, plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)["path"])
+    lr.layout_copy_count_writes(s, w.src_layout, d, w.dst_layout, counts, elem_bytes=w.elem_bytes)
+    torch.cuda.synchronize()
+    assert int(counts.min()) == 1 and int(counts.max()) == 1
+    del s, d, counts
+    torch.cuda.empty_cache()
+
+
 def test_copy_misaligned_pointers(dev):
     w = W.small("retile")
     src, dst, want = _oracle_copy(w)

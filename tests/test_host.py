@@ -291,6 +291,22 @@ def test_is_injective_matches_oracle():
     for name in W.FULL:
         w = W.full(name)
         assert lr.is_injective(w.dst_layout) == O.is_injective(O.parse(w.dst_layout))
+    # above 2^20 elements: separated leaves and an exact prefix, as the oracle
+    M = (1 << 22) + 3
+    for t, want in ((f"(3,2,{M}):(2,3,8)", True), (f"(3,2,{M}):(2,2,8)", False), (f"(2,{M}):(0,1)", False),
+                    (f"Sw<2,1,3> o ({M},3,2):(8,2,3)", True), (f"({1 << 21},2):(1,{(1 << 21) - 1})", False),
+                    (f"({1 << 21},2):(1,{1 << 21})", True), (f"({1 << 13},{1 << 12}):(1,{(1 << 13) - 1})", False),
+                    ("(1024,3):(1048576,1048577)", True), ("(1024,3):(1048576,1048576)", False),
+                    (f"(1024,3,{M}):(1048576,1048577,{1 << 31})", True)):
+        assert lr.is_injective(t) == want == O.is_injective(O.parse(t)), t
+    rng = random.Random(23)
+    for _ in range(200):  # a small random head times a large separated tail
+        head = _rand_layout(rng, max_leaves=3, max_ext=5, max_stride=9)
+        Lh = O.parse(head)
+        span = O.cosize(Lh)
+        big = f"{(1 << 20) // O.size(Lh) + 7}:{span}"
+        t = f"({head.split(':')[0]},{big.split(':')[0]}):({head.split(':')[1]},{big.split(':')[1]})"
+        assert lr.is_injective(t) == O.is_injective(O.parse(t)) == O.is_injective_bruteforce(Lh), t
 
 
 def test_thread_map_matches_oracle():
@@ -801,6 +817,16 @@ def test_plan_few_channel_images():
                 assert (p["path"], p["vec_elems"], p["tile_a"], p["grid"])[:len(want)] == want, (c, eb, p)
         p = lr.copy_plan(nhwc, 3 * 323 * c, nchw, 3 * 323 * c, 2, src_align=1)
         assert p["path"] == "generic", p
+    # its streaming threshold is the 256 MiB last-level cache (its ranges start
+    # unaligned, so partial lines merge in the cache below that); aligned planes
+    # stream from 64 MiB like the other kernels
+    for n, want in ((128, False), (300, True)):
+        nhwc, nchw = image(n, 299, 299, 3)
+        p = lr.copy_plan(nhwc, n * 89401 * 3, nchw, n * 89401 * 3, 2)
+        assert (p["path"], p["vec_elems"], p["streaming"]) == ("deinterleave", 1, want), (n, p)
+    nhwc, nchw = image(128, 224, 224, 3)
+    p = lr.copy_plan(nhwc, 128 * 50176 * 3, nchw, 128 * 50176 * 3, 2)
+    assert (p["path"], p["vec_elems"], p["streaming"]) == ("deinterleave", 8, True), p
     # under one pixel per lane (63 pixels) it is not worth a workgroup of 4096
     nhwc, nchw = image(3, 7, 9, 3)
     assert lr.copy_plan(nhwc, 567, nchw, 567, 2)["path"] == "generic"

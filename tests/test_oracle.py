@@ -394,6 +394,35 @@ def test_injective_sufficient_is_sound():
     assert O.is_injective_bruteforce(L) and not O.injective_sufficient(L)
 
 
+def test_injective_by_separated_leaves_equals_brute_force(monkeypatch):
+    """The large-layout rule (separated leaves, brute force on the rest) used at
+    every size by lowering the brute-force limit to 0, against the definition
+    (every index to a distinct offset) on random layouts, including swizzled ones,
+    stride-0 leaves and layouts the plain sufficient test cannot prove."""
+    rng = random.Random(8)
+    monkeypatch.setattr(OL, "BRUTE_INJECTIVE_LIMIT", 0)
+    seen = {True: 0, False: 0}
+    hard = 0
+    for _ in range(6000):
+        L = _rand_layout(rng, max_leaves=5, max_ext=5, max_stride=12, swz_p=0.2)
+        want = O.is_injective_bruteforce(L)
+        assert O.is_injective(L) == want, O.fmt(L)
+        seen[want] += 1
+        hard += want and not O.injective_sufficient(L)
+    assert min(seen.values()) > 1000 and hard > 100, (seen, hard)
+    monkeypatch.undo()
+    # large: (3,2,M):(2,3,8) is injective for every M (the first two leaves give
+    # {0,2,3,4,5,7} inside [0,8)); (3,2,M):(2,2,8) repeats 2; a stride-0 leaf repeats
+    M = (1 << 22) + 3
+    assert O.is_injective(O.parse(f"(3,2,{M}):(2,3,8)"))
+    assert not O.is_injective(O.parse(f"(3,2,{M}):(2,2,8)"))
+    assert not O.is_injective(O.parse(f"(2,{M}):(0,1)"))
+    small = O.parse("(3,2,1000):(2,3,8)")
+    assert O.is_injective_bruteforce(small)
+    # beyond the limits of the exact part: not proven
+    assert not O.is_injective(O.parse(f"({1 << 13},{1 << 12}):(1,{(1 << 13) - 1})"))
+
+
 # ---------------------------------------------------------------------------
 # Widest common vector
 # ---------------------------------------------------------------------------

@@ -122,19 +122,20 @@ def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
     return wall, ev0.elapsed_time(ev1) / steps
 
 
-def _per_launch(lr, torch, pairs, Ls, Ld, eb, launches, flags=0, rotate=True):
+def _per_launch(lr, torch, pairs, Ls, Ld, eb, launches, flags=0, rotate=True, tuning=None):
     """Kernel time of each launch (HIP events around it on the launch stream), in us,
     sorted: rotating over the buffer pairs (cold: nothing cached from the previous
-    launch) or on the first pair only (warm: the last-level cache may hold data)."""
+    launch) or on the first pair only (warm: the last-level cache may hold data).
+    One untimed launch comes first."""
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
     s, d = pairs[0]
-    lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+    lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream, tuning=tuning)
     torch.cuda.synchronize()
     for i, (e0, e1) in enumerate(evs):
-        s, d = pairs[i % len(pairs)] if rotate else pairs[0]
+        s, d = pairs[(i + 1) % len(pairs)] if rotate else pairs[0]
         e0.record(stream)
-        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream, tuning=tuning)
         e1.record(stream)
     torch.cuda.synchronize()
     return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
@@ -279,22 +280,26 @@ def counters_run(lr, torch, W, reps: int = 3):
           flush=True)
 
 
-def launch_run(lr, torch, W, specs, reps: int = 4):
-    """Each NAME[:JSON] spec: its workload launched `reps` times with the tuning."""
+def launch_run(lr, torch, W, specs, reps: int = 12):
+    """Each NAME[:JSON] spec: its workload with that tuning, one untimed launch and
+    then `reps` launches rotating over buffer pairs of >= 1 GiB in total (cold, as in
+    the timed benchmark), each bracketed by HIP events.  Prints one line per spec;
+    under rocprofv3 each spec is one group of reps + 1 dispatches."""
     dev = torch.device("cuda:0")
     for spec in specs:
         name, _, js = spec.partition(":")
         tuning = json.loads(js) if js else None
         w = W.full(name)
-        s = torch.randint(0, 256, (w.src_elems * w.elem_bytes,), dtype=torch.uint8, device=dev)
-        d = torch.empty(w.dst_elems * w.elem_bytes, dtype=torch.uint8, device=dev)
-        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes, tuning=tuning)
-        for _ in range(reps):
-            lr.layout_copy(s, w.src_layout, d, w.dst_layout, elem_bytes=w.elem_bytes, tuning=tuning)
-        torch.cuda.synchronize()
+        eb = w.elem_bytes
+        p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, eb, tuning=tuning)
+        pairs = _pairs(torch, dev, w.src_elems * eb, w.dst_elems * eb)
+        us = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, eb, reps, tuning=tuning)
+        med = us[len(us) // 2]
         print(f"launch: {w.name} tuning={tuning} path={p['path']} grid={p['grid']} "
-              f"gather_chunks={p['gather_chunks']}", flush=True)
-        del s, d
+              f"tile={p['tile_a']}x{p['tile_b']} direct={p['direct']} pipeline_tiles={p['pipeline_tiles']} "
+              f"gather_chunks={p['gather_chunks']} us_median={med:.2f} us_best={us[0]:.2f} "
+              f"GBps_median={W.bytes_moved(w) / (med * 1e-6) / 1e9:.0f}", flush=True)
+        del pairs
         torch.cuda.empty_cache()
 
 

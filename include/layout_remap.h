@@ -333,6 +333,9 @@ typedef struct {
                            destination runs); -1 on other paths */
   int32_t gather_chunks; /* staged: destination chunks of one tile per 32-lane slice of the
                             gather (a slice covers 32 / gather_chunks tiles); -1 elsewhere */
+  int32_t pipeline_tiles; /* transpose: tiles per workgroup of the pipelined kernel, 0 when it
+                             is not used */
+  int32_t reserved_plan;  /* 0 */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */
@@ -376,7 +379,11 @@ typedef struct {
   int32_t direct_loads;    /* staged and LDS transpose: 0 through registers, 1 global -> LDS */
   int32_t gather_chunks;   /* staged: destination chunks of one tile per 32-lane slice of
                               the gather (1, 2, 4, 8, 16 or 32; see lr_plan.gather_chunks) */
-  int32_t reserved[6];     /* must be -1 or 0 */
+  int32_t pipeline_tiles;  /* LDS transpose with 16-byte chunks in tile shapes 0-2: 0 one tile
+                              per workgroup; 2..64 that many tiles per workgroup, software-
+                              pipelined through two LDS tiles with direct loads (the next tile's
+                              loads in flight while the current one is stored) */
+  int32_t reserved[5];     /* must be -1 or 0 */
 } lr_copy_tuning;
 
 /* Every field of *t to -1 (the planner's choices). */

@@ -86,6 +86,8 @@ class lr_plan(ctypes.Structure):
         ("store_policy", ctypes.c_int32),
         ("vector_order", ctypes.c_int32),
         ("gather_chunks", ctypes.c_int32),
+        ("pipeline_tiles", ctypes.c_int32),
+        ("reserved_plan", ctypes.c_int32),
         ("tile_a", ctypes.c_int64),
         ("tile_b", ctypes.c_int64),
         ("grid", ctypes.c_int64),
@@ -109,7 +111,8 @@ class lr_copy_tuning(ctypes.Structure):
         ("element_tiles", ctypes.c_int32),
         ("direct_loads", ctypes.c_int32),
         ("gather_chunks", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 6),
+        ("pipeline_tiles", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 5),
     ]
 
 
@@ -481,7 +484,7 @@ def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, fla
         "a_mode": p.a_mode, "b_mode": p.b_mode, "b2_mode": p.b2_mode, "block": p.block,
         "streaming": bool(p.streaming), "order": p.order, "direct": bool(p.direct),
         "load_policy": p.load_policy, "store_policy": p.store_policy,
-        "vector_order": p.vector_order, "gather_chunks": p.gather_chunks,
+        "vector_order": p.vector_order, "gather_chunks": p.gather_chunks, "pipeline_tiles": p.pipeline_tiles,
         "tile_a": p.tile_a, "tile_b": p.tile_b,
         "grid": p.grid, "n_elems": p.n_elems, "blocks": p.blocks,
         "joint": [(p.ext[i], p.s_src[i], p.s_dst[i]) for i in range(r)],

@@ -601,6 +601,9 @@ struct TransposeArgs {
   // tile lies less than 4 GiB above that base
   uint32_t bufst, bufmask;
   WriteCount wcnt;
+  // pipelined transpose: tiles per workgroup (0: one tile, not pipelined) and the
+  // total number of tiles (tiles_a * tiles_b * batch)
+  uint32_t pipe, ntiles;
 };
 
 // Workgroup number -> (a-tile, b-tile, batch index) in the order t.order selects.
@@ -945,6 +948,46 @@ __global__ void __launch_bounds__(512) k_transpose_win(TransposeArgs t) {
   }
 }
 
+// Transpose of a V x V block of EB-byte elements held as V 16-byte rows (V * EB ==
+// 16): element j of out[i] is element i of in[j].  Written on 32-bit words with
+// v_perm_b32 so that the rows stay whole 16-byte values: read from LDS element by
+// element, the compiler splits each row into unaligned 2- and 12-byte pieces.
+// __builtin_amdgcn_perm(a, b, sel): byte k of the result is byte sel_k of the
+// 8-byte value a:b (b holds bytes 0-3, a bytes 4-7); selector 12 gives zero.
+using U4 = NativeOf<16>::T;
+
+template <int EB>
+__device__ __forceinline__ void transpose_rows16(const U4* in, U4* out) {
+  if constexpr (EB == 16) {
+    out[0] = in[0];
+  } else if constexpr (EB == 8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) out[i] = U4{in[0][2 * i], in[0][2 * i + 1], in[1][2 * i], in[1][2 * i + 1]};
+  } else if constexpr (EB == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = U4{in[0][i], in[1][i], in[2][i], in[3][i]};
+  } else if constexpr (EB == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two words
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[i][q] = __builtin_amdgcn_perm(in[2 * q + 1][i / 2], in[2 * q][i / 2], sel);
+    }
+  } else {
+    static_assert(EB == 1, "elements of 1, 2, 4, 8 or 16 bytes");
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t pair = 0x0c0c0000u | (uint32_t)(i % 4) | ((uint32_t)(4 + i % 4) << 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = __builtin_amdgcn_perm(in[4 * q + 1][i / 4], in[4 * q][i / 4], pair);
+        const uint32_t hi = __builtin_amdgcn_perm(in[4 * q + 3][i / 4], in[4 * q + 2][i / 4], pair);
+        out[i][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+    }
+  }
+}
+
 // The same tile with its source chunks loaded straight into LDS (gfx950 direct
 // loads): the tile's TB*V source rows of TA chunks land in LDS without passing
 // through registers, then each lane reads its V x V block (V chunks of one chunk
@@ -990,28 +1033,141 @@ __global__ void __launch_bounds__(TA * TB) k_transpose_dl(TransposeArgs t) {
   __syncthreads();
 
   const int beta = tid % TB, alpha = tid / TB;
-  C in[V];
+  const U4* rows = (const U4*)tile;
+  U4 in[V], out[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int r = V * beta + j;
-    in[j] = tile[r * TA + (alpha ^ ((r / V) % 16))];
+    in[j] = rows[r * TA + (alpha ^ ((r / V) % 16))];
   }
-  C out[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i)
-#pragma unroll
-    for (int j = 0; j < V; ++j) out[i].e[j] = in[j].e[i];
+  transpose_rows16<EB>(in, out);
   const uint32_t b = b0 + V * beta;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const uint32_t a = a0 + V * alpha + i;
     if (a < t.ext_a && b < t.ext_b) {
       const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
-      gstore<NT, C>(dst + (size_t)dof * EB, out[i]);
+      gstore<NT, U4>(dst + (size_t)dof * EB, out[i]);
       count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
     }
   }
   (void)NTH;
+}
+
+// Vector-memory wait counts for s_waitcnt on gfx950 (vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8; a field at its maximum does not wait).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// Software-pipelined transpose ([CuTe algebra page, section 5.2]: the next tile's
+// copy is issued while the current one is consumed).  A workgroup takes t.pipe
+// consecutive tiles (in the order t.order selects) and alternates two LDS tiles:
+// the gfx950 direct global -> LDS loads of tile i+1 are issued before tile i is
+// read from LDS, transposed in registers and stored, so each CU has loads and
+// stores in flight together.  LDS arrangement and lane roles as k_transpose_dl.
+// Every lane issues exactly V loads per tile (a chunk outside the layout loads the
+// chunk at offset 0 into a slot no output reads), so "at most V vector-memory
+// operations outstanding" means the current tile has landed: loads complete in the
+// order they were issued.  The two buffers are distinct LDS objects and the loop
+// names them statically, so the compiler's own LDS-DMA tracking waits for the right
+// one only.  Barriers are plain s_barrier with explicit waits: a __syncthreads()
+// fence would drain the next tile's loads too.
+template <int EB, int V, int TA, int TB, bool NT>
+__device__ __forceinline__ void pipe_issue(const TransposeArgs& t, uint32_t blk, Chunk<typename Raw<EB>::T, V>* buf) {
+  const char* __restrict__ src = (const char*)t.src;
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blk, ta, tb, r2);
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const int base = 64 * (wave * V + k);
+    const int s = base + lane;
+    const int r = s / TA, cs = s % TA;
+    const int c = cs ^ ((r / V) % 16);
+    const uint32_t a = a0 + V * c, b = b0 + r;
+    uint32_t so = 0;  // outside the layout: the chunk at offset 0, never read back
+    if (a < t.ext_a && b < t.ext_b) so = swz32(a + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
+    load_to_lds16<NT>(src + (size_t)so * EB, buf + __builtin_amdgcn_readfirstlane(base));
+  }
+}
+
+template <int EB, int V, int TA, int TB, bool NT>
+__device__ __forceinline__ void pipe_consume(const TransposeArgs& t, uint32_t blk,
+                                             const Chunk<typename Raw<EB>::T, V>* buf) {
+  using C = Chunk<typename Raw<EB>::T, V>;
+  char* __restrict__ dst = (char*)t.dst;
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blk, ta, tb, r2);
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
+  const int beta = threadIdx.x % TB, alpha = threadIdx.x / TB;
+  const U4* rows = (const U4*)buf;
+  U4 in[V], out[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int r = V * beta + j;
+    in[j] = rows[r * TA + (alpha ^ ((r / V) % 16))];
+  }
+  transpose_rows16<EB>(in, out);
+  const uint32_t b = b0 + V * beta;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t a = a0 + V * alpha + i;
+    if (a < t.ext_a && b < t.ext_b) {
+      const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+      gstore<NT, U4>(dst + (size_t)dof * EB, out[i]);
+      count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
+    }
+  }
+}
+
+template <int EB, int V, int TA, int TB, bool NT>
+__global__ void __launch_bounds__(TA * TB) k_transpose_pipe(TransposeArgs t) {
+  using C = Chunk<typename Raw<EB>::T, V>;
+  static_assert(V * EB == 16 && TB >= 16 && (TA == 16 || TA == 32), "full chunks, 16-wide phases");
+  static_assert(2 * TB * V * TA * 16 <= 160 * 1024, "two tiles fit the LDS");
+  __shared__ C bufA[TB * V * TA];
+  __shared__ C bufB[TB * V * TA];
+  const uint32_t first = blockIdx.x * t.pipe;
+  const uint32_t last = first + t.pipe < t.ntiles ? first + t.pipe : t.ntiles;
+  uint32_t i = first;
+  pipe_issue<EB, V, TA, TB, NT>(t, i, bufA);
+  // Steady state, three or more tiles left: tile i is landing in A.  The waits are
+  // unconditional so that the compiler's own LDS-DMA tracking sees, on every path
+  // to a read, the wait that covers it.
+  while (i + 2 < last) {
+    pipe_issue<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(V));  // all but tile i + 1's loads: A has landed
+    __builtin_amdgcn_s_barrier();
+    pipe_consume<EB, V, TA, TB, NT>(t, i, bufA);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);     // this wave's reads of A are done
+    __builtin_amdgcn_s_barrier();
+    pipe_issue<EB, V, TA, TB, NT>(t, i + 2, bufA);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(V));
+    __builtin_amdgcn_s_barrier();
+    pipe_consume<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    i += 2;
+  }
+  // one or two tiles left, the first of them landing in A
+  if (i + 1 < last) {
+    pipe_issue<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(V));
+    __builtin_amdgcn_s_barrier();
+    pipe_consume<EB, V, TA, TB, NT>(t, i, bufA);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    pipe_consume<EB, V, TA, TB, NT>(t, i + 1, bufB);
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    pipe_consume<EB, V, TA, TB, NT>(t, i, bufA);
+  }
 }
 
 // ------------------------------------------------------------------ interleave
@@ -1574,6 +1730,29 @@ template <int EB, int V, bool NT>
 static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool dl, unsigned grid,
                                hipStream_t st) {
   if constexpr (V * EB == 16) {
+    if (a.pipe && lds) {
+      switch (shape) {
+        case 0:
+          if constexpr (pipe_fits(0, V)) {
+            hipLaunchKernelGGL((k_transpose_pipe<EB, V, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a);
+            return true;
+          }
+          return false;
+        case 1:
+          if constexpr (pipe_fits(1, V)) {
+            hipLaunchKernelGGL((k_transpose_pipe<EB, V, 32, 16, NT>), dim3(grid), dim3(512), 0, st, a);
+            return true;
+          }
+          return false;
+        case 2:
+          if constexpr (pipe_fits(2, V)) {
+            hipLaunchKernelGGL((k_transpose_pipe<EB, V, 16, 32, NT>), dim3(grid), dim3(512), 0, st, a);
+            return true;
+          }
+          return false;
+        default: return false;
+      }
+    }
     if (dl && lds) {
       switch (shape) {
         case 0: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a); return true;
@@ -1812,6 +1991,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         a.fd_gta = fd_of(a.gta);
         a.fd_gtb = fd_of(a.gtb);
       }
+      a.pipe = (uint32_t)p.pipe;
+      a.ntiles = (uint32_t)p.tiles_total;
       const bool lds = p.path == LR_PATH_TRANSPOSE;
       if (p.tel) {
         if (p.eb > 8) return LR_ERR_PATH;

@@ -62,6 +62,11 @@ constexpr int kTileTB[kTileShapes] = {16, 16, 32, 32, 8, 8, 16};
 // LDS bytes of a tile shape's exchange with V-element 16-byte chunks: TA*V rows of
 // TB chunks; a shape is usable when it fits the 160 KiB of a CU.
 constexpr bool shape_fits(int shape, int V) { return kTileTA[shape] * V * kTileTB[shape] * 16 <= 160 * 1024; }
+// The pipelined transpose holds two tiles of shapes 0-2 (16 or 32 chunks along a, at
+// least 16 along b) in LDS.
+constexpr bool pipe_fits(int shape, int V) {
+  return shape >= 0 && shape <= 2 && 2 * kTileTA[shape] * V * kTileTB[shape] * 16 <= 160 * 1024;
+}
 
 // Everything the launch code needs.
 struct Plan {
@@ -103,6 +108,8 @@ struct Plan {
   uint32_t torder;
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB
+  int pipe;           // pipelined transpose: tiles per workgroup (0: one tile, not pipelined)
+  int64_t tiles_total; // transpose: tiles over all batch indices
   int inarrow;        // interleave: 1 = one 16-byte store per lane from NB narrow loads,
                       // 0 = NB wide loads and stores per lane, 2 = channel shuffle through LDS,
                       // 3 = its element-granular form

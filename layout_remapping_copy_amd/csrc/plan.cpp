@@ -137,6 +137,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
       !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6}) || !in(t.tile_order, {0, 1, 2, 3, 4}) ||
       !in(t.element_tiles, {0, 1}) || !in(t.direct_loads, {0, 1}) || !in(t.gather_chunks, {1, 2, 4, 8, 16, 32}))
     return false;
+  if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;
   for (int32_t r : t.reserved)
     if (r != -1 && r != 0) return false;
   return true;
@@ -712,6 +713,16 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       for (int k = 0; k < p->rank; ++k)
         if (k != a && k != b && k != b2) batch *= p->m[k].ext;
       p->grid = nta * ntb * batch;
+      p->tiles_total = p->grid;
+      // software pipelining over two LDS tiles (tile shapes whose exchange fits twice):
+      // a workgroup takes pipeline_tiles consecutive tiles in the chosen order
+      if (tun.pipeline_tiles >= 2 && p->path == LR_PATH_TRANSPOSE && !p->tel && V * p->eb == 16 &&
+          pipe_fits(p->tshape, (int)V)) {
+        p->pipe = tun.pipeline_tiles;
+        p->direct = true;
+        p->bufst = false;
+        p->grid = (p->tiles_total + p->pipe - 1) / p->pipe;
+      }
       return LR_OK;
     }
   }
@@ -902,7 +913,15 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       int64_t batch = 1;
       for (int k = 0; k < p.rank; ++k)
         if (k != p.a && k != p.b && k != p.b2) batch *= p.m[k].ext;
-      if (p.grid != nta * ntb * batch || p.grid > 0x7FFFFFFF) return bad();
+      if (p.tiles_total != nta * ntb * batch || p.grid > 0x7FFFFFFF) return bad();
+      if (p.pipe) {  // pipelined: full chunks, tile shapes 0-2, direct loads into two LDS tiles
+        if (p.pipe < 2 || p.pipe > 64 || p.path != LR_PATH_TRANSPOSE || p.tel || v * p.eb != 16 ||
+            !pipe_fits(p.tshape, (int)v) ||
+            !p.direct || p.bufst || p.grid != (p.tiles_total + p.pipe - 1) / p.pipe)
+          return bad();
+      } else if (p.grid != p.tiles_total) {
+        return bad();
+      }
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.b && k != p.b2 && p.m[k].sd % v) return bad();
@@ -1054,7 +1073,7 @@ extern "C" {
 void lr_copy_tuning_init(lr_copy_tuning* t) {
   if (!t) return;
   t->load_policy = t->store_policy = t->units_per_lane = t->vector_order = t->interleave_form = -1;
-  t->tile_shape = t->tile_order = t->element_tiles = t->direct_loads = t->gather_chunks = -1;
+  t->tile_shape = t->tile_order = t->element_tiles = t->direct_loads = t->gather_chunks = t->pipeline_tiles = -1;
   for (int32_t& r : t->reserved) r = -1;
 }
 
@@ -1110,6 +1129,7 @@ int lr_copy_plan_tuned(const lr_layout* Ls, int64_t src_capacity_elems, size_t s
   out->store_policy = p.nt ? (p.bufst ? 18 : 2) : 0;
   out->vector_order = p.vorder;
   out->gather_chunks = (int32_t)p.staged_cps;
+  out->pipeline_tiles = p.pipe;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

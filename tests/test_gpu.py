@@ -444,7 +444,7 @@ def test_copy_random_pairs(dev, knobs):
                "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 4),
                "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
                "vector_order": rng.choice([-1, 0, 1, 2]), "units_per_lane": rng.choice([-1, 1, 4]),
-               "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32])}
+               "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5])}
         knobs.t.clear()
         knobs.set(**env)
         if i % 50 == 0:
@@ -503,7 +503,8 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
         mult = _multiplicity(Ld, O.size(Ls), nd)
         knobs.t.clear()
         knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 4), gather_chunks=rng.choice([-1, 8, 16]),
-                  vector_order=rng.choice([-1, 0, 1, 2]), element_tiles=rng.choice([-1, 0, 1]))
+                  vector_order=rng.choice([-1, 0, 1, 2]), element_tiles=rng.choice([-1, 0, 1]),
+                  pipeline_tiles=rng.choice([-1, 2, 3]))
         for flags in [0] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
             try:
                 p = plan(ts, ns, td, nd, eb, flags)
@@ -1050,6 +1051,87 @@ def test_full_transpose_direct_loads(dev, knobs):
     s = torch.from_numpy(src).to(dev)
     d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
     say("full transpose direct loads")
+    copy_(s, w.src_layout, d, w.dst_layout, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), F.transpose(src, 8192))
+
+
+def _pipe_cases():
+    cm = W.small("interleave_cm")
+    cases = [("(520,264):(264,1)", "(520,264):(1,520)", 2),
+             ("(2,2,128,40):(10240,5120,40,1)", "(2,2,128,40):(10240,5120,1,128)", 2),
+             ("(100,72):(72,1)", "(100,72):(1,100)", 4),
+             ("(64,96,5):(96,1,6144)", "(64,96,5):(1,64,6144)", 8),
+             ("(1024,512):(512,1)", "Sw<3,3,3> o (1024,512):(1,1024)", 2),
+             ("(600,328):(328,1)", "Sw<2,3,5> o (600,328):(1,600)", 2),
+             ("(48,80):(80,1)", "(48,80):(1,48)", 16),
+             ("(512,272):(272,1)", "(512,272):(1,512)", 1),
+             (cm.src_layout, cm.dst_layout, 2)]
+    out = []
+    for ts, td, eb in cases:
+        n = O.size(O.parse(ts))
+        out.append((ts, td, max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize), eb))
+    return out
+
+
+@pytest.mark.parametrize("shape", [0, 1, 2])
+def test_transpose_pipelined(dev, knobs, shape):
+    """The software-pipelined transpose: a workgroup takes pipeline_tiles tiles in
+    turn over two LDS tiles.  Tile counts that leave the last workgroup one tile,
+    two tiles or a full run; ragged edges, batch modes, a split b mode, 1- to
+    16-byte elements; both policies and every tile order."""
+    ran = 0
+    for ci, (ts, td, ns, nd, eb) in enumerate(_pipe_cases()):
+        src = np.random.default_rng(50 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for pipe in (2, 3, 4, 7):
+            knobs.t.clear()
+            knobs.set(tile_shape=shape, pipeline_tiles=pipe)
+            for nt in ("0", "1"):
+                knobs.policy(nt)
+                for orient in ("0", "1", "2", "3", "4"):
+                    knobs.set(tile_order=int(orient))
+                    p = plan(ts, ns, td, nd, eb)
+                    if p["path"] != "transpose" or p["pipeline_tiles"] != pipe:
+                        continue
+                    assert p["direct"]
+                    say("transpose pipelined", shape, pipe, ts, "eb", eb, "nt", nt, "order", orient, "grid", p["grid"])
+                    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, pipe, nt, orient)
+                    ran += 1
+    assert ran >= 60
+
+
+def test_transpose_pipelined_write_counts(dev, knobs):
+    """Every destination element of a pipelined transpose is stored exactly once."""
+    ran = 0
+    for ci, (ts, td, ns, nd, eb) in enumerate(_pipe_cases()):
+        src = np.random.default_rng(90 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        mult = _multiplicity(O.parse(td), O.size(O.parse(ts)), nd)
+        for shape, pipe in ((0, 3), (1, 2), (2, 5)):
+            knobs.t.clear()
+            knobs.set(tile_shape=shape, pipeline_tiles=pipe)
+            if plan(ts, ns, td, nd, eb)["pipeline_tiles"] != pipe:
+                continue
+            say("pipelined write counts", ts, "eb", eb, "shape", shape, "pipe", pipe)
+            got, counts = _write_counts(dev, src, ts, dst, td, eb)
+            assert np.array_equal(counts, (mult > 0).astype(np.int32)), (ts, shape, pipe)
+            assert np.array_equal(got, O.copy(src, O.parse(ts), dst, O.parse(td), eb))
+            ran += 1
+    assert ran >= 12
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("shape,pipe", [(1, 4), (0, 8)])
+def test_full_transpose_pipelined(dev, knobs, shape, pipe):
+    knobs.set(tile_shape=shape, pipeline_tiles=pipe)
+    w = W.full("transpose")
+    assert plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)["pipeline_tiles"] == pipe
+    src = W.make_src(w)
+    s = torch.from_numpy(src).to(dev)
+    d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
+    say("full transpose pipelined", shape, pipe)
     copy_(s, w.src_layout, d, w.dst_layout, 2)
     torch.cuda.synchronize()
     assert np.array_equal(d.cpu().numpy(), F.transpose(src, 8192))

@@ -710,7 +710,8 @@ def test_tuning_overrides_are_checked():
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
     for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 5},
-                {"units_per_lane": 2}, {"vector_order": 3}, {"gather_chunks": 3}, {"direct_loads": 2}):
+                {"units_per_lane": 2}, {"vector_order": 3}, {"gather_chunks": 3}, {"direct_loads": 2},
+                {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}):
         with pytest.raises(lr.LayoutRemapError) as e:
             lr.copy_plan(*args, tuning=bad)
         assert e.value.code == lr.binding.ERR_INVALID, bad
@@ -719,6 +720,29 @@ def test_tuning_overrides_are_checked():
     # knobs of other paths are ignored; -1 everywhere is the planner's own plan
     assert lr.copy_plan(*args, tuning={"gather_chunks": 8, "vector_order": 0}) == lr.copy_plan(*args)
     assert lr.copy_plan(*args, tuning={k: -1 for k in lr.binding.TUNING_FIELDS}) == lr.copy_plan(*args)
+
+
+def test_pipelined_transpose_plan():
+    """pipeline_tiles: tile shapes whose two LDS tiles fit (16x16, 32x16, 16x32 chunks of
+    16 bytes) take that many consecutive tiles per workgroup with direct loads; the
+    grid is the tile count divided up; elsewhere the override is ignored."""
+    w = W.full("transpose")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    for shape, tiles in ((0, 64 * 64), (1, 32 * 64), (2, 64 * 32)):
+        base = lr.copy_plan(*args, tuning={"tile_shape": shape})
+        assert base["grid"] == tiles and base["pipeline_tiles"] == 0
+        for pipe in (2, 3, 7, 64):
+            p = lr.copy_plan(*args, tuning={"tile_shape": shape, "pipeline_tiles": pipe})
+            assert p["pipeline_tiles"] == pipe and p["direct"], (shape, pipe)
+            assert p["grid"] == -(-tiles // pipe) and (p["tile_a"], p["tile_b"]) == (base["tile_a"], base["tile_b"])
+    # 32x32 chunks: 128 KiB of LDS per tile, two do not fit
+    assert lr.copy_plan(*args, tuning={"tile_shape": 3, "pipeline_tiles": 4})["pipeline_tiles"] == 0
+    # not a transpose, or no full 16-byte chunks: ignored
+    r = W.full("retile")
+    ra = (r.src_layout, r.src_elems, r.dst_layout, r.dst_elems, 2)
+    assert lr.copy_plan(*ra, tuning={"pipeline_tiles": 4}) == lr.copy_plan(*ra)
+    odd = ("(520,263):(263,1)", 520 * 263, "(520,263):(1,520)", 520 * 263, 2)
+    assert lr.copy_plan(*odd, tuning={"pipeline_tiles": 4})["pipeline_tiles"] == 0
 
 
 def _table_cycles(words):

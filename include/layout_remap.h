@@ -335,7 +335,8 @@ typedef struct {
                             gather (a slice covers 32 / gather_chunks tiles); -1 elsewhere */
   int32_t pipeline_tiles; /* transpose: tiles per workgroup of the pipelined kernel, 0 when it
                              is not used */
-  int32_t reserved_plan;  /* 0 */
+  int32_t transpose_reads; /* LDS transpose: 1 when the tile is read with the gfx950 transpose
+                              reads (ds_read_b64_tr_b16), 0 otherwise */
   int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */
@@ -383,7 +384,11 @@ typedef struct {
                               per workgroup; 2..64 that many tiles per workgroup, software-
                               pipelined through two LDS tiles with direct loads (the next tile's
                               loads in flight while the current one is stored) */
-  int32_t reserved[5];     /* must be -1 or 0 */
+  int32_t transpose_reads; /* LDS transpose with direct loads (or pipelined), 2-byte elements in
+                              16-byte chunks, tile shapes 0-3: 0 each lane reads V whole LDS rows
+                              and transposes them in registers; 1 the gfx950 transpose reads
+                              (ds_read_b64_tr_b16) hand each lane one column of four rows */
+  int32_t reserved[4];     /* must be -1 or 0 */
 } lr_copy_tuning;
 
 /* Every field of *t to -1 (the planner's choices). */

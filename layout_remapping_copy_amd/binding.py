@@ -87,7 +87,7 @@ class lr_plan(ctypes.Structure):
         ("vector_order", ctypes.c_int32),
         ("gather_chunks", ctypes.c_int32),
         ("pipeline_tiles", ctypes.c_int32),
-        ("reserved_plan", ctypes.c_int32),
+        ("transpose_reads", ctypes.c_int32),
         ("tile_a", ctypes.c_int64),
         ("tile_b", ctypes.c_int64),
         ("grid", ctypes.c_int64),
@@ -112,7 +112,8 @@ class lr_copy_tuning(ctypes.Structure):
         ("direct_loads", ctypes.c_int32),
         ("gather_chunks", ctypes.c_int32),
         ("pipeline_tiles", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("transpose_reads", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
     ]
 
 
@@ -485,6 +486,7 @@ def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, fla
         "streaming": bool(p.streaming), "order": p.order, "direct": bool(p.direct),
         "load_policy": p.load_policy, "store_policy": p.store_policy,
         "vector_order": p.vector_order, "gather_chunks": p.gather_chunks, "pipeline_tiles": p.pipeline_tiles,
+        "transpose_reads": bool(p.transpose_reads),
         "tile_a": p.tile_a, "tile_b": p.tile_b,
         "grid": p.grid, "n_elems": p.n_elems, "blocks": p.blocks,
         "joint": [(p.ext[i], p.s_src[i], p.s_dst[i]) for i in range(r)],

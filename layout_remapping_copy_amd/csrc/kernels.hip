@@ -990,68 +990,149 @@ __device__ __forceinline__ void transpose_rows16(const U4* in, U4* out) {
 
 // The same tile with its source chunks loaded straight into LDS (gfx950 direct
 // loads): the tile's TB*V source rows of TA chunks land in LDS without passing
-// through registers, then each lane reads its V x V block (V chunks of one chunk
-// column, V consecutive rows), transposes it in registers and stores V chunks.
-// Lane tid = beta + TB * alpha owns a-chunk alpha and b rows V*beta .. V*beta+V-1,
-// so TB consecutive lanes store TB consecutive chunks of one destination row.  LDS
-// slot of (row r, chunk column c) = r * TA + (c ^ ((r / V) % 16)): the 16 lanes of
-// one 16-byte read phase (consecutive beta) then fall on 16 distinct slots modulo
-// 16, i.e. all 64 banks.  A direct load fills 64 consecutive slots per wave, so
+// through registers.  A direct load fills 64 consecutive 16-byte slots per wave, so
 // lane l of load k of wave w takes slot 64 * (w * V + k) + l and loads the source
-// chunk that belongs there.  Needs full 16-byte chunks (V * EB == 16), TB >= 16
-// and TA in {16, 32}.
-template <int EB, int V, int TA, int TB, bool NT>
-__global__ void __launch_bounds__(TA * TB) k_transpose_dl(TransposeArgs t) {
-  using T = typename Raw<EB>::T;
-  using C = Chunk<T, V>;
-  static_assert(V * EB == 16 && TB >= 16 && (TA == 16 || TA == 32), "full chunks, 16-wide phases");
-  constexpr int NTH = TA * TB;
-  const char* __restrict__ src = (const char*)t.src;
-  char* __restrict__ dst = (char*)t.dst;
-  __shared__ C tile[TB * V * TA];
+// chunk that belongs there: slot r * TA + (c ^ lds_swz(r)) holds chunk column c of
+// tile row r (b index b0 + r).  Two ways to read the tile back:
+//  - whole rows (TR false): lane tid = beta + TB * alpha reads its V x V block (V
+//    chunks of chunk column alpha, rows V*beta .. V*beta+V-1) as V 16-byte rows,
+//    transposes it in registers and stores V chunks; TB consecutive lanes store TB
+//    consecutive chunks of one destination row.  lds_swz(r) = (r / V) % 16, so the 16
+//    lanes of a 16-byte read phase (consecutive beta) fall on 16 distinct slots
+//    modulo 16, i.e. all 64 banks.
+//  - gfx950 transpose reads (TR true, 2-byte elements): ds_read_b64_tr_b16 hands lane
+//    i of each 16-lane group element i % 4 of the 8 bytes that lane 4k + i / 4 of the
+//    group addresses, as its element k (k = 0..3).  Lane j of a group addresses row
+//    j / 4 of b-chunk j % 4 (and, in a second read, row j / 4 + 4), in the 8-byte half
+//    of the chunk column its group owns, so lane i receives one column (element i % 4
+//    of that half) of the 8 rows of b-chunk i / 4: a whole 16-byte destination chunk
+//    from two reads, with no register transpose.  The four groups of a wave cover both
+//    halves of one chunk column and 8 b-chunks (8 destination rows x 128 bytes per
+//    store instruction).  lds_swz(r) = (r % 4) + 4 * ((r / 8) % 4), so the 16 rows a
+//    group addresses fall on 16 distinct slots modulo 16 and, with the two groups of a
+//    32-lane phase on different halves, the phase's 32 8-byte reads on all 64 banks.
+// Needs full 16-byte chunks (V * EB == 16), TB >= 16 and TA in {16, 32}.
+template <int V, bool TR>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (TR)
+    return (r & 3) | (((r >> 3) & 3) << 2);
+  else
+    return (r / V) % 16;
+}
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// gfx950 transpose read of 2-byte elements (ds_read_b64_tr_b16), as two 32-bit words.
+__device__ __forceinline__ NativeOf<8>::T lds_read_tr16(const char* p) {
+  return __builtin_bit_cast(NativeOf<8>::T, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<char*>(p)));
+}
+
+// Direct loads of tile blk into buf.  ALL: every lane issues its V loads, a chunk
+// outside the layout loading the chunk at offset 0 into a slot no output reads (the
+// pipelined kernel counts outstanding loads); otherwise such lanes load nothing.
+// The chunk at offset 0 is in the source buffer: the a mode is contiguous in the
+// source with an extent that is a multiple of V.
+template <int EB, int V, int TA, int TB, bool NT, bool TR, bool ALL>
+__device__ __forceinline__ void dl_issue(const TransposeArgs& t, uint32_t blk, Chunk<typename Raw<EB>::T, V>* buf) {
+  const char* __restrict__ src = (const char*)t.src;
   uint32_t ta, tb, r2;
-  transpose_tile(t, blockIdx.x, ta, tb, r2);
+  transpose_tile(t, blk, ta, tb, r2);
   uint32_t bs, bd;
   batch_offsets(t.batch, r2, &bs, &bd);
   const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const int base = 64 * (wave * V + k);       // first slot of this wave's load
+    const int base = 64 * (wave * V + k);  // first slot of this wave's load
     const int s = base + lane;
     const int r = s / TA, cs = s % TA;
-    const int c = cs ^ ((r / V) % 16);          // chunk column stored in slot s
+    const int c = cs ^ lds_swz<V, TR>(r);   // chunk column stored in slot s
     const uint32_t a = a0 + V * c, b = b0 + r;
-    if (a < t.ext_a && b < t.ext_b) {
-      const uint32_t so = swz32(a + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
-      load_to_lds16<NT>(src + (size_t)so * EB, tile + __builtin_amdgcn_readfirstlane(base));
+    const bool in = a < t.ext_a && b < t.ext_b;
+    if (!ALL && !in) continue;
+    uint32_t so = 0;
+    if (in) so = swz32(a + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
+    load_to_lds16<NT>(src + (size_t)so * EB, buf + __builtin_amdgcn_readfirstlane(base));
+  }
+}
+
+// Reads tile blk back from buf (see above for the two forms) and stores it.
+template <int EB, int V, int TA, int TB, bool NT, bool TR>
+__device__ __forceinline__ void dl_consume(const TransposeArgs& t, uint32_t blk,
+                                           const Chunk<typename Raw<EB>::T, V>* buf) {
+  char* __restrict__ dst = (char*)t.dst;
+  uint32_t ta, tb, r2;
+  transpose_tile(t, blk, ta, tb, r2);
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
+  if constexpr (!TR) {
+    const int beta = threadIdx.x % TB, alpha = threadIdx.x / TB;
+    const U4* rows = (const U4*)buf;
+    U4 in[V], out[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int r = V * beta + j;
+      in[j] = rows[r * TA + (alpha ^ lds_swz<V, false>(r))];
+    }
+    transpose_rows16<EB>(in, out);
+    const uint32_t b = b0 + V * beta;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t a = a0 + V * alpha + i;
+      if (a < t.ext_a && b < t.ext_b) {
+        const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+        gstore<NT, U4>(dst + (size_t)dof * EB, out[i]);
+        count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, 16);
+      }
+    }
+  } else {
+    static_assert(EB == 2 && V == 8, "transpose reads: 2-byte elements in 16-byte chunks");
+    constexpr int UB = TB / 8;              // units of 8 b-chunks along b
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int half = g & 1, bh = g >> 1;     // the group's 8-byte half of the chunk column; its 4 of the 8 b-chunks
+    const int sk = i >> 2, sq = i & 3;       // addressed: row sk (and sk + 4) of b-chunk sq
+    const int e = i & 3, q = i >> 2;         // received: element e of the half, b-chunk q
+    const char* base = (const char*)buf;
+    // a wave's 8 units: chunk column c, 8 b-chunks from 8 * ub (the tile's TA * UB
+    // units over its TA * TB / 64 waves).  All 16 reads go out before the first store
+    // (the compiler keeps these reads in order with the stores).
+    NativeOf<8>::T lo[8], hi[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int u = w * 8 + it;
+      const int c = u / UB, ub = u % UB;
+      const int r0 = 64 * ub + 8 * (4 * bh + sq) + sk, r1 = r0 + 4;
+      lo[it] = lds_read_tr16(base + (r0 * TA + (c ^ lds_swz<V, true>(r0))) * 16 + 8 * half);
+      hi[it] = lds_read_tr16(base + (r1 * TA + (c ^ lds_swz<V, true>(r1))) * 16 + 8 * half);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int u = w * 8 + it;
+      const int c = u / UB, ub = u % UB;
+      const uint32_t a = a0 + V * c + 4 * half + e;
+      const uint32_t b = b0 + V * (8 * ub + 4 * bh + q);
+      if (a < t.ext_a && b < t.ext_b) {
+        const U4 o = {lo[it][0], lo[it][1], hi[it][0], hi[it][1]};
+        const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+        gstore<NT, U4>(dst + (size_t)dof * EB, o);
+        count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, 16);
+      }
     }
   }
+}
+
+template <int EB, int V, int TA, int TB, bool NT, bool TR>
+__global__ void __launch_bounds__(TA * TB) k_transpose_dl(TransposeArgs t) {
+  using C = Chunk<typename Raw<EB>::T, V>;
+  static_assert(V * EB == 16 && TB >= 16 && (TA == 16 || TA == 32), "full chunks, 16-wide phases");
+  __shared__ C tile[TB * V * TA];
+  dl_issue<EB, V, TA, TB, NT, TR, false>(t, blockIdx.x, tile);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   __syncthreads();
-
-  const int beta = tid % TB, alpha = tid / TB;
-  const U4* rows = (const U4*)tile;
-  U4 in[V], out[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int r = V * beta + j;
-    in[j] = rows[r * TA + (alpha ^ ((r / V) % 16))];
-  }
-  transpose_rows16<EB>(in, out);
-  const uint32_t b = b0 + V * beta;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint32_t a = a0 + V * alpha + i;
-    if (a < t.ext_a && b < t.ext_b) {
-      const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
-      gstore<NT, U4>(dst + (size_t)dof * EB, out[i]);
-      count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
-    }
-  }
-  (void)NTH;
+  dl_consume<EB, V, TA, TB, NT, TR>(t, blockIdx.x, tile);
 }
 
 // Vector-memory wait counts for s_waitcnt on gfx950 (vmcnt in bits 3:0 and 15:14,
@@ -1063,69 +1144,15 @@ constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 // copy is issued while the current one is consumed).  A workgroup takes t.pipe
 // consecutive tiles (in the order t.order selects) and alternates two LDS tiles:
 // the gfx950 direct global -> LDS loads of tile i+1 are issued before tile i is
-// read from LDS, transposed in registers and stored, so each CU has loads and
-// stores in flight together.  LDS arrangement and lane roles as k_transpose_dl.
-// Every lane issues exactly V loads per tile (a chunk outside the layout loads the
-// chunk at offset 0 into a slot no output reads), so "at most V vector-memory
-// operations outstanding" means the current tile has landed: loads complete in the
-// order they were issued.  The two buffers are distinct LDS objects and the loop
-// names them statically, so the compiler's own LDS-DMA tracking waits for the right
-// one only.  Barriers are plain s_barrier with explicit waits: a __syncthreads()
-// fence would drain the next tile's loads too.
-template <int EB, int V, int TA, int TB, bool NT>
-__device__ __forceinline__ void pipe_issue(const TransposeArgs& t, uint32_t blk, Chunk<typename Raw<EB>::T, V>* buf) {
-  const char* __restrict__ src = (const char*)t.src;
-  uint32_t ta, tb, r2;
-  transpose_tile(t, blk, ta, tb, r2);
-  uint32_t bs, bd;
-  batch_offsets(t.batch, r2, &bs, &bd);
-  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int k = 0; k < V; ++k) {
-    const int base = 64 * (wave * V + k);
-    const int s = base + lane;
-    const int r = s / TA, cs = s % TA;
-    const int c = cs ^ ((r / V) % 16);
-    const uint32_t a = a0 + V * c, b = b0 + r;
-    uint32_t so = 0;  // outside the layout: the chunk at offset 0, never read back
-    if (a < t.ext_a && b < t.ext_b) so = swz32(a + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
-    load_to_lds16<NT>(src + (size_t)so * EB, buf + __builtin_amdgcn_readfirstlane(base));
-  }
-}
-
-template <int EB, int V, int TA, int TB, bool NT>
-__device__ __forceinline__ void pipe_consume(const TransposeArgs& t, uint32_t blk,
-                                             const Chunk<typename Raw<EB>::T, V>* buf) {
-  using C = Chunk<typename Raw<EB>::T, V>;
-  char* __restrict__ dst = (char*)t.dst;
-  uint32_t ta, tb, r2;
-  transpose_tile(t, blk, ta, tb, r2);
-  uint32_t bs, bd;
-  batch_offsets(t.batch, r2, &bs, &bd);
-  const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
-  const int beta = threadIdx.x % TB, alpha = threadIdx.x / TB;
-  const U4* rows = (const U4*)buf;
-  U4 in[V], out[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int r = V * beta + j;
-    in[j] = rows[r * TA + (alpha ^ ((r / V) % 16))];
-  }
-  transpose_rows16<EB>(in, out);
-  const uint32_t b = b0 + V * beta;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint32_t a = a0 + V * alpha + i;
-    if (a < t.ext_a && b < t.ext_b) {
-      const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
-      gstore<NT, U4>(dst + (size_t)dof * EB, out[i]);
-      count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
-    }
-  }
-}
-
-template <int EB, int V, int TA, int TB, bool NT>
+// read from LDS and stored, so each CU has loads and stores in flight together.
+// LDS arrangement and lane roles as k_transpose_dl.  Every lane issues exactly V
+// loads per tile, so "at most V vector-memory operations outstanding" means the
+// current tile has landed: loads complete in the order they were issued.  The two
+// buffers are distinct LDS objects and the loop names them statically, so the
+// compiler's own LDS-DMA tracking waits for the right one only.  Barriers are plain
+// s_barrier with explicit waits: a __syncthreads() fence would drain the next tile's
+// loads too.
+template <int EB, int V, int TA, int TB, bool NT, bool TR>
 __global__ void __launch_bounds__(TA * TB) k_transpose_pipe(TransposeArgs t) {
   using C = Chunk<typename Raw<EB>::T, V>;
   static_assert(V * EB == 16 && TB >= 16 && (TA == 16 || TA == 32), "full chunks, 16-wide phases");
@@ -1135,38 +1162,38 @@ __global__ void __launch_bounds__(TA * TB) k_transpose_pipe(TransposeArgs t) {
   const uint32_t first = blockIdx.x * t.pipe;
   const uint32_t last = first + t.pipe < t.ntiles ? first + t.pipe : t.ntiles;
   uint32_t i = first;
-  pipe_issue<EB, V, TA, TB, NT>(t, i, bufA);
+  dl_issue<EB, V, TA, TB, NT, TR, true>(t, i, bufA);
   // Steady state, three or more tiles left: tile i is landing in A.  The waits are
   // unconditional so that the compiler's own LDS-DMA tracking sees, on every path
   // to a read, the wait that covers it.
   while (i + 2 < last) {
-    pipe_issue<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    dl_issue<EB, V, TA, TB, NT, TR, true>(t, i + 1, bufB);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(V));  // all but tile i + 1's loads: A has landed
     __builtin_amdgcn_s_barrier();
-    pipe_consume<EB, V, TA, TB, NT>(t, i, bufA);
+    dl_consume<EB, V, TA, TB, NT, TR>(t, i, bufA);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);     // this wave's reads of A are done
     __builtin_amdgcn_s_barrier();
-    pipe_issue<EB, V, TA, TB, NT>(t, i + 2, bufA);
+    dl_issue<EB, V, TA, TB, NT, TR, true>(t, i + 2, bufA);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(V));
     __builtin_amdgcn_s_barrier();
-    pipe_consume<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    dl_consume<EB, V, TA, TB, NT, TR>(t, i + 1, bufB);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     i += 2;
   }
   // one or two tiles left, the first of them landing in A
   if (i + 1 < last) {
-    pipe_issue<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    dl_issue<EB, V, TA, TB, NT, TR, true>(t, i + 1, bufB);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(V));
     __builtin_amdgcn_s_barrier();
-    pipe_consume<EB, V, TA, TB, NT>(t, i, bufA);
+    dl_consume<EB, V, TA, TB, NT, TR>(t, i, bufA);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    pipe_consume<EB, V, TA, TB, NT>(t, i + 1, bufB);
+    dl_consume<EB, V, TA, TB, NT, TR>(t, i + 1, bufB);
   } else {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    pipe_consume<EB, V, TA, TB, NT>(t, i, bufA);
+    dl_consume<EB, V, TA, TB, NT, TR>(t, i, bufA);
   }
 }
 
@@ -1726,48 +1753,57 @@ static void launch_transpose_shape(const TransposeArgs& a, unsigned grid, hipStr
   hipLaunchKernelGGL((k_transpose<EB, V, true, TA, TB, NT>), dim3(grid), dim3(TA * TB), 0, st, a);
 }
 
-template <int EB, int V, bool NT>
-static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, bool dl, unsigned grid,
-                               hipStream_t st) {
-  if constexpr (V * EB == 16) {
-    if (a.pipe && lds) {
-      switch (shape) {
-        case 0:
-          if constexpr (pipe_fits(0, V)) {
-            hipLaunchKernelGGL((k_transpose_pipe<EB, V, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a);
-            return true;
-          }
-          return false;
-        case 1:
-          if constexpr (pipe_fits(1, V)) {
-            hipLaunchKernelGGL((k_transpose_pipe<EB, V, 32, 16, NT>), dim3(grid), dim3(512), 0, st, a);
-            return true;
-          }
-          return false;
-        case 2:
-          if constexpr (pipe_fits(2, V)) {
-            hipLaunchKernelGGL((k_transpose_pipe<EB, V, 16, 32, NT>), dim3(grid), dim3(512), 0, st, a);
-            return true;
-          }
-          return false;
-        default: return false;
-      }
+// The direct-load kernels: pipelined (a.pipe) or one tile per workgroup.
+template <int EB, int V, bool NT, bool TR>
+static bool launch_dl(const TransposeArgs& a, int shape, unsigned grid, hipStream_t st) {
+  if (a.pipe) {
+    switch (shape) {
+      case 0:
+        if constexpr (pipe_fits(0, V)) {
+          hipLaunchKernelGGL((k_transpose_pipe<EB, V, 16, 16, NT, TR>), dim3(grid), dim3(256), 0, st, a);
+          return true;
+        }
+        return false;
+      case 1:
+        if constexpr (pipe_fits(1, V)) {
+          hipLaunchKernelGGL((k_transpose_pipe<EB, V, 32, 16, NT, TR>), dim3(grid), dim3(512), 0, st, a);
+          return true;
+        }
+        return false;
+      case 2:
+        if constexpr (pipe_fits(2, V)) {
+          hipLaunchKernelGGL((k_transpose_pipe<EB, V, 16, 32, NT, TR>), dim3(grid), dim3(512), 0, st, a);
+          return true;
+        }
+        return false;
+      default: return false;
     }
-    if (dl && lds) {
-      switch (shape) {
-        case 0: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 16, NT>), dim3(grid), dim3(256), 0, st, a); return true;
-        case 1: hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 16, NT>), dim3(grid), dim3(512), 0, st, a); return true;
-        case 2: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 32, NT>), dim3(grid), dim3(512), 0, st, a); return true;
-        case 3:
-          if constexpr (shape_fits(3, V)) {
-            hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 32, NT>), dim3(grid), dim3(1024), 0, st, a);
-            return true;
-          }
-          break;
-        default: break;
+  }
+  switch (shape) {
+    case 0: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 16, NT, TR>), dim3(grid), dim3(256), 0, st, a); return true;
+    case 1: hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 16, NT, TR>), dim3(grid), dim3(512), 0, st, a); return true;
+    case 2: hipLaunchKernelGGL((k_transpose_dl<EB, V, 16, 32, NT, TR>), dim3(grid), dim3(512), 0, st, a); return true;
+    case 3:
+      if constexpr (shape_fits(3, V)) {
+        hipLaunchKernelGGL((k_transpose_dl<EB, V, 32, 32, NT, TR>), dim3(grid), dim3(1024), 0, st, a);
+        return true;
       }
       return false;
+    default: return false;
+  }
+}
+
+// dl: 0 through registers, 1 direct loads, 2 direct loads read back with the gfx950
+// transpose reads
+template <int EB, int V, bool NT>
+static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, int dl, unsigned grid,
+                               hipStream_t st) {
+  if constexpr (V * EB == 16) {
+    if (dl == 2 && lds) {
+      if constexpr (EB == 2) return launch_dl<EB, V, NT, true>(a, shape, grid, st);
+      return false;
     }
+    if (dl == 1 && lds) return launch_dl<EB, V, NT, false>(a, shape, grid, st);
   }
   if (!lds) {
     if (shape != 0) return false;
@@ -1809,7 +1845,7 @@ static bool launch_tel(const TransposeArgs& a, bool win, unsigned grid, hipStrea
 }
 
 template <int EB, bool NT>
-static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int shape, bool dl, unsigned grid,
+static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int shape, int dl, unsigned grid,
                                 hipStream_t st) {
   switch (v) {
     case 1: return launch_transpose_v<EB, 1, NT>(a, lds, shape, dl, grid, st);
@@ -1822,7 +1858,7 @@ static bool launch_transpose_nt(const TransposeArgs& a, int v, bool lds, int sha
 }
 
 template <int EB>
-static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, bool nt, bool dl, unsigned grid,
+static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape, bool nt, int dl, unsigned grid,
                              hipStream_t st) {
   return nt ? launch_transpose_nt<EB, true>(a, v, lds, shape, dl, grid, st)
             : launch_transpose_nt<EB, false>(a, v, lds, shape, dl, grid, st);
@@ -2007,7 +2043,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         return check_launch();
       }
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, p.direct, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, p.direct ? (p.tr ? 2 : 1) : 0, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
@@ -2128,11 +2164,11 @@ static void log_plan(const Plan& p, int64_t blocks) {
   std::fprintf(stderr,
                "lr plan: path=%s elem_bytes=%d vec=%d wide=%d a=%d b=%d b2=%d tile=%lldx%lld shape=%d order=%d "
                "block=%d grid=%lld blocks=%lld nt_load=%d nt_store=%d sc1=%d direct=%d elem_tiles=%d "
-               "vorder=%d gather_chunks=%lld joint=[%s]\n",
+               "vorder=%d gather_chunks=%lld pipeline_tiles=%d transpose_reads=%d joint=[%s]\n",
                p.path >= 0 && p.path <= 8 ? names[p.path] : "?", p.eb, p.v, p.wide ? 1 : 0, p.a, p.b, p.b2,
                (long long)p.tile_a, (long long)p.tile_b, p.tshape, (int)p.torder, p.block, (long long)p.grid,
                (long long)blocks, p.nt_ld ? 1 : 0, p.nt ? 1 : 0, (p.nt && p.bufst) ? 1 : 0, p.direct ? 1 : 0,
-               p.tel ? 1 : 0, p.vorder, (long long)p.staged_cps, modes);
+               p.tel ? 1 : 0, p.vorder, (long long)p.staged_cps, p.pipe, p.tr ? 1 : 0, modes);
 }
 
 static int fill_eval(EvalArgs* a, const lr_layout* L) {

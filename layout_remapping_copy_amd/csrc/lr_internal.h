@@ -109,6 +109,7 @@ struct Plan {
   int unroll;         // generic/vector: units per lane (1 or 4; 4 when wide)
   int tshape;         // transpose tile shape index into kTileTA / kTileTB
   int pipe;           // pipelined transpose: tiles per workgroup (0: one tile, not pipelined)
+  bool tr;            // LDS transpose: the tile is read with gfx950 transpose reads
   int64_t tiles_total; // transpose: tiles over all batch indices
   int inarrow;        // interleave: 1 = one 16-byte store per lane from NB narrow loads,
                       // 0 = NB wide loads and stores per lane, 2 = channel shuffle through LDS,

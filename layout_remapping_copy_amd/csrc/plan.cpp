@@ -138,6 +138,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
       !in(t.element_tiles, {0, 1}) || !in(t.direct_loads, {0, 1}) || !in(t.gather_chunks, {1, 2, 4, 8, 16, 32}))
     return false;
   if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;
+  if (!in(t.transpose_reads, {0, 1})) return false;
   for (int32_t r : t.reserved)
     if (r != -1 && r != 0) return false;
   return true;
@@ -723,6 +724,13 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->bufst = false;
         p->grid = (p->tiles_total + p->pipe - 1) / p->pipe;
       }
+      // gfx950 transpose reads of the LDS tile: 2-byte elements in 16-byte chunks,
+      // tiles 16 or 32 chunks on each side, loaded directly (or pipelined)
+      if (tun.transpose_reads == 1 && p->path == LR_PATH_TRANSPOSE && !p->tel && p->eb == 2 && V == 8 &&
+          p->tshape <= 3 && (p->direct || p->pipe)) {
+        p->tr = true;
+        p->bufst = false;
+      }
       return LR_OK;
     }
   }
@@ -922,6 +930,10 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       } else if (p.grid != p.tiles_total) {
         return bad();
       }
+      if (p.tr) {  // transpose reads: 8 x 8 blocks of 2-byte elements, direct loads, shapes 0-3
+        if (p.path != LR_PATH_TRANSPOSE || p.tel || p.eb != 2 || v != 8 || p.tshape > 3 || !p.direct || p.bufst)
+          return bad();
+      }
       for (int k = 0; k < p.rank; ++k) {
         if (k != p.a && p.m[k].ss % v) return bad();
         if (k != p.b && k != p.b2 && p.m[k].sd % v) return bad();
@@ -1074,6 +1086,7 @@ void lr_copy_tuning_init(lr_copy_tuning* t) {
   if (!t) return;
   t->load_policy = t->store_policy = t->units_per_lane = t->vector_order = t->interleave_form = -1;
   t->tile_shape = t->tile_order = t->element_tiles = t->direct_loads = t->gather_chunks = t->pipeline_tiles = -1;
+  t->transpose_reads = -1;
   for (int32_t& r : t->reserved) r = -1;
 }
 
@@ -1130,6 +1143,7 @@ int lr_copy_plan_tuned(const lr_layout* Ls, int64_t src_capacity_elems, size_t s
   out->vector_order = p.vorder;
   out->gather_chunks = (int32_t)p.staged_cps;
   out->pipeline_tiles = p.pipe;
+  out->transpose_reads = p.tr ? 1 : 0;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

@@ -444,7 +444,8 @@ def test_copy_random_pairs(dev, knobs):
                "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 4),
                "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
                "vector_order": rng.choice([-1, 0, 1, 2]), "units_per_lane": rng.choice([-1, 1, 4]),
-               "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5])}
+               "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
+               "transpose_reads": rng.choice([-1, 0, 1])}
         knobs.t.clear()
         knobs.set(**env)
         if i % 50 == 0:
@@ -504,7 +505,8 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
         knobs.t.clear()
         knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 4), gather_chunks=rng.choice([-1, 8, 16]),
                   vector_order=rng.choice([-1, 0, 1, 2]), element_tiles=rng.choice([-1, 0, 1]),
-                  pipeline_tiles=rng.choice([-1, 2, 3]))
+                  pipeline_tiles=rng.choice([-1, 2, 3]), transpose_reads=rng.choice([-1, 1]),
+                  direct_loads=rng.choice([-1, 1]))
         for flags in [0] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
             try:
                 p = plan(ts, ns, td, nd, eb, flags)
@@ -1102,6 +1104,36 @@ def test_transpose_pipelined(dev, knobs, shape):
     assert ran >= 60
 
 
+@pytest.mark.parametrize("shape", [0, 1, 2, 3])
+def test_transpose_reads(dev, knobs, shape):
+    """The LDS tile read back with the gfx950 transpose reads (ds_read_b64_tr_b16), one
+    tile per workgroup and pipelined: 2-byte elements, ragged edges, batch modes, a
+    grouped b run, destination swizzles; both policies and every tile order."""
+    ran = 0
+    for ci, (ts, td, ns, nd, eb) in enumerate(_pipe_cases()):
+        if eb != 2:
+            continue
+        src = np.random.default_rng(70 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for pipe in (0, 3):
+            knobs.t.clear()
+            knobs.set(tile_shape=shape, transpose_reads=1, direct_loads=1)
+            if pipe:
+                knobs.set(pipeline_tiles=pipe)
+            for nt in ("0", "1"):
+                knobs.policy(nt)
+                for orient in ("0", "1", "2", "3", "4"):
+                    knobs.set(tile_order=int(orient))
+                    p = plan(ts, ns, td, nd, eb)
+                    if p["path"] != "transpose" or not p["transpose_reads"]:
+                        continue
+                    say("transpose reads", shape, pipe, ts, "nt", nt, "order", orient, "grid", p["grid"])
+                    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, pipe, nt, orient)
+                    ran += 1
+    assert ran >= 40 if shape < 3 else ran >= 20
+
+
 def test_transpose_pipelined_write_counts(dev, knobs):
     """Every destination element of a pipelined transpose is stored exactly once."""
     ran = 0
@@ -1109,29 +1141,35 @@ def test_transpose_pipelined_write_counts(dev, knobs):
         src = np.random.default_rng(90 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
         dst = np.full(nd * eb, 0xA5, np.uint8)
         mult = _multiplicity(O.parse(td), O.size(O.parse(ts)), nd)
-        for shape, pipe in ((0, 3), (1, 2), (2, 5)):
+        for shape, pipe, tr in ((0, 3, 0), (1, 2, 0), (2, 5, 0), (1, 2, 1), (3, 0, 1)):
             knobs.t.clear()
-            knobs.set(tile_shape=shape, pipeline_tiles=pipe)
-            if plan(ts, ns, td, nd, eb)["pipeline_tiles"] != pipe:
+            knobs.set(tile_shape=shape, transpose_reads=tr, direct_loads=1)
+            if pipe:
+                knobs.set(pipeline_tiles=pipe)
+            p = plan(ts, ns, td, nd, eb)
+            if p["path"] != "transpose" or p["pipeline_tiles"] != pipe or p["transpose_reads"] != bool(tr):
                 continue
-            say("pipelined write counts", ts, "eb", eb, "shape", shape, "pipe", pipe)
+            say("pipelined write counts", ts, "eb", eb, "shape", shape, "pipe", pipe, "transpose reads", tr)
             got, counts = _write_counts(dev, src, ts, dst, td, eb)
-            assert np.array_equal(counts, (mult > 0).astype(np.int32)), (ts, shape, pipe)
+            assert np.array_equal(counts, (mult > 0).astype(np.int32)), (ts, shape, pipe, tr)
             assert np.array_equal(got, O.copy(src, O.parse(ts), dst, O.parse(td), eb))
             ran += 1
-    assert ran >= 12
+    assert ran >= 20
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("shape,pipe", [(1, 4), (0, 8)])
-def test_full_transpose_pipelined(dev, knobs, shape, pipe):
-    knobs.set(tile_shape=shape, pipeline_tiles=pipe)
+@pytest.mark.parametrize("shape,pipe,tr", [(1, 4, 0), (0, 8, 0), (3, 0, 1), (1, 4, 1)])
+def test_full_transpose_pipelined(dev, knobs, shape, pipe, tr):
+    knobs.set(tile_shape=shape, transpose_reads=tr, direct_loads=1)
+    if pipe:
+        knobs.set(pipeline_tiles=pipe)
     w = W.full("transpose")
-    assert plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)["pipeline_tiles"] == pipe
+    p = plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    assert p["pipeline_tiles"] == pipe and p["transpose_reads"] == bool(tr)
     src = W.make_src(w)
     s = torch.from_numpy(src).to(dev)
     d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
-    say("full transpose pipelined", shape, pipe)
+    say("full transpose pipelined", shape, pipe, "transpose reads", tr)
     copy_(s, w.src_layout, d, w.dst_layout, 2)
     torch.cuda.synchronize()
     assert np.array_equal(d.cpu().numpy(), F.transpose(src, 8192))

@@ -1,0 +1,53 @@
+"""The lane layout of gfx950's transpose read of 2-byte elements (ds_read_b64_tr_b16),
+which the direct-load transpose's transpose_reads form is built on.
+
+tests/tr_read_probe.hip (compiled by this test) reads 8 bytes per lane from an LDS
+array holding each element's own index, at five address patterns.  Within each group
+of 16 lanes, lane i must receive, as its element k (k = 0..3), element i % 4 of the
+four 2-byte elements at the address of lane 4k + i // 4 of its group.
+"""
+
+import json
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def expected(addr):
+    out = []
+    for lane in range(64):
+        g, i = divmod(lane, 16)
+        out += [addr[16 * g + 4 * k + i // 4] // 2 + i % 4 for k in range(4)]
+    return out
+
+
+def test_expected_layout_examples():
+    # identity addresses: lane i of group 0 gets column i of the 16 x 4 block
+    e = expected([8 * l for l in range(64)])
+    assert e[0:4] == [0, 16, 32, 48] and e[4 * 5:4 * 6] == [5, 21, 37, 53]
+    assert e[4 * 16:4 * 17] == [64, 80, 96, 112]
+    # every lane reading one address: each lane gets one element four times
+    e = expected([56] * 64)
+    assert all(e[4 * l:4 * l + 4] == [28 + l % 4] * 4 for l in range(64))
+
+
+@pytest.mark.gpu
+def test_transpose_read_lane_layout(tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    exe = str(tmp_path / "tr_read_probe")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-Wall", os.path.join(HERE, "tr_read_probe.hip"), "-o", exe]
+    print("building the probe", flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    print("running the probe", flush=True)
+    p = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stderr[-2000:]
+    rows = [json.loads(x) for x in p.stdout.splitlines() if x.startswith("{")]
+    assert [r["pattern"] for r in rows] == ["identity", "reversed", "times5", "broadcast", "shuffled"]
+    for r in rows:
+        assert r["got"] == expected(r["addr"]), r["pattern"]

@@ -711,7 +711,7 @@ def test_tuning_overrides_are_checked():
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
     for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 5},
                 {"units_per_lane": 2}, {"vector_order": 3}, {"gather_chunks": 3}, {"direct_loads": 2},
-                {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}):
+                {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2}):
         with pytest.raises(lr.LayoutRemapError) as e:
             lr.copy_plan(*args, tuning=bad)
         assert e.value.code == lr.binding.ERR_INVALID, bad
@@ -743,6 +743,25 @@ def test_pipelined_transpose_plan():
     assert lr.copy_plan(*ra, tuning={"pipeline_tiles": 4}) == lr.copy_plan(*ra)
     odd = ("(520,263):(263,1)", 520 * 263, "(520,263):(1,520)", 520 * 263, 2)
     assert lr.copy_plan(*odd, tuning={"pipeline_tiles": 4})["pipeline_tiles"] == 0
+
+
+def test_transpose_reads_plan():
+    """transpose_reads: the direct-load (or pipelined) LDS transpose of 2-byte elements in
+    16-byte chunks, tile shapes 0-3; ignored without direct loads or for other element
+    sizes."""
+    w = W.full("transpose")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    assert not lr.copy_plan(*args)["transpose_reads"]
+    assert not lr.copy_plan(*args, tuning={"transpose_reads": 1})["transpose_reads"]  # no direct loads
+    for shape in range(4):
+        p = lr.copy_plan(*args, tuning={"transpose_reads": 1, "direct_loads": 1, "tile_shape": shape})
+        assert p["transpose_reads"] and p["direct"] and p["tile_a"] == p["tile_a"], shape
+    p = lr.copy_plan(*args, tuning={"transpose_reads": 1, "pipeline_tiles": 4, "tile_shape": 1})
+    assert p["transpose_reads"] and p["pipeline_tiles"] == 4
+    # 32 x 8 chunks (shape 4): the reads need 16 or 32 chunks on both sides
+    assert not lr.copy_plan(*args, tuning={"transpose_reads": 1, "direct_loads": 1, "tile_shape": 4})["transpose_reads"]
+    f32 = ("(4096,4096):(4096,1)", 4096 * 4096, "(4096,4096):(1,4096)", 4096 * 4096, 4)
+    assert not lr.copy_plan(*f32, tuning={"transpose_reads": 1, "direct_loads": 1})["transpose_reads"]
 
 
 def _table_cycles(words):

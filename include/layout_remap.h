@@ -330,7 +330,9 @@ typedef struct {
                            shuffle when the destination's is) */
   int32_t vector_order; /* vector/generic: traversal after the common contiguous mode (0
                            destination order, 1 source order, 2 source order in blocks of
-                           destination runs); -1 on other paths */
+                           destination runs, 3 tiles of atoms through LDS: a_mode continues
+                           the common mode in the source, b_mode in the destination, tiles of
+                           tile_a x tile_b atoms); -1 on other paths */
   int32_t gather_chunks; /* staged: destination chunks of one tile per 32-lane slice of the
                             gather (a slice covers 32 / gather_chunks tiles); -1 elsewhere */
   int32_t pipeline_tiles; /* transpose: tiles per workgroup of the pipelined kernel, 0 when it
@@ -371,7 +373,10 @@ typedef struct {
   int32_t units_per_lane;  /* generic/vector: 1 or 4 */
   int32_t vector_order;    /* vector: modes after the common contiguous one walked in 0
                               destination order, 1 source order, 2 source order in blocks
-                              of destination runs (see lr_plan.order) */
+                              of destination runs, 3 tiles of atoms through LDS where the
+                              common mode is an atom of 64-512 bytes that different modes
+                              continue in the source and the destination (else 1; see
+                              lr_plan.vector_order) */
   int32_t interleave_form; /* interleave: 0 one chunk per lane per head, 1 one destination
                               chunk per lane from narrow loads, 2 the channel shuffle */
   int32_t tile_shape;      /* transpose: 0..6, the tile shapes of lr_plan.tile_a/tile_b */

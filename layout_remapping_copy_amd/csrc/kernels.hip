@@ -101,6 +101,7 @@ template <> struct NativeOf<2> { using T = uint16_t; };
 template <> struct NativeOf<4> { using T = uint32_t; };
 template <> struct NativeOf<8> { using T = unsigned int __attribute__((ext_vector_type(2))); };
 template <> struct NativeOf<16> { using T = unsigned int __attribute__((ext_vector_type(4))); };
+using U4 = NativeOf<16>::T;  // one 16-byte chunk
 
 template <bool NT, typename C>
 __device__ __forceinline__ C gload(const void* p) {
@@ -556,6 +557,80 @@ __device__ __forceinline__ void batch_offsets(const BatchArg& b, uint32_t r, uin
   *sd = d;
 }
 
+// ------------------------------------------------------------------ tiles of atoms
+
+// The vector path's fourth traversal order: the common contiguous mode is an atom
+// of K 16-byte chunks, mode a continues it in the source and mode b in the
+// destination ([CuTe algebra page, section 3.2]: the copy is a zipped divide of the
+// (a, b) plane into T x T tiles of atoms, each tile moved as one unit).  A
+// 256-lane workgroup loads its tile as T source runs of T atoms (a wave instruction
+// reads consecutive chunks of one run), regroups it in LDS and stores it as T
+// destination runs of T atoms.  LDS slot of chunk q of atom (a = i, b = j) in the
+// tile: (j * T + (i ^ (j % T))) * K + q.  The stores' 16 lanes of a 16-byte read
+// phase cover 256 bytes of atoms j, j + 1, ... of one i, and the XOR puts those
+// atoms in distinct 256/K-chunk slots modulo 256 bytes; the loads' 8 lanes of a
+// write phase stay inside aligned groups of atoms, i.e. 128 contiguous bytes.  All
+// offsets are in 16-byte chunks, swizzles included.
+struct AtomArgs {
+  const void* src;
+  void* dst;
+  uint32_t ext_a, ext_b;   // atoms along a and b
+  uint32_t ss_b, sd_a;     // chunk strides of b in the source and of a in the destination
+  uint32_t tiles_a, tiles_b;
+  FD fd_ta, fd_tb;
+  BatchArg batch;          // the other modes (chunk strides)
+  SwzArg sws, swd;
+  uint32_t bufst;          // streaming stores as buffer stores (destination span < 4 GiB)
+  WriteCount wcnt;
+};
+
+template <int K, bool LNT, bool SNT>
+__global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
+  constexpr int T = (int)atom_tile(K);
+  constexpr int RUN = T * K;         // chunks in one run of T atoms
+  constexpr int CH = T * RUN, PER = CH / 256;
+  static_assert(PER >= 1 && CH % 256 == 0, "whole rounds of 256 lanes");
+  __shared__ U4 tile[CH];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+  const uint32_t r1 = fdiv(blockIdx.x, t.fd_ta), ta = blockIdx.x - r1 * t.tiles_a;
+  const uint32_t r2 = fdiv(r1, t.fd_tb), tb = r1 - r2 * t.tiles_b;
+  uint32_t bs, bd;
+  batch_offsets(t.batch, r2, &bs, &bd);
+  const int tid = threadIdx.x;
+  U4 v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int L = k * 256 + tid;                 // source order: run j, atom i, chunk q
+    const int j = L / RUN, i = (L % RUN) / K, q = L % K;
+    const uint32_t a = ta * T + i, b = tb * T + j;
+    if (a < t.ext_a && b < t.ext_b) v[k] = gload<LNT, U4>(src + (size_t)swz32(a * K + q + b * t.ss_b + bs, t.sws) * 16);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int L = k * 256 + tid;
+    const int j = L / RUN, i = (L % RUN) / K, q = L % K;
+    if (ta * T + i < t.ext_a && tb * T + j < t.ext_b) tile[(j * T + (i ^ (j % T))) * K + q] = v[k];
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, -1, kBufferWord3);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int S = k * 256 + tid;                 // destination order: run i, atom j, chunk q
+    const int i = S / RUN, j = (S % RUN) / K, q = S % K;
+    const uint32_t a = ta * T + i, b = tb * T + j;
+    if (a < t.ext_a && b < t.ext_b) {
+      const U4 x = tile[(j * T + (i ^ (j % T))) * K + q];
+      const uint32_t dof = swz32(b * K + q + a * t.sd_a + bd, t.swd);
+      if (SNT && t.bufst)
+        __builtin_amdgcn_raw_buffer_store_b128(x, rd, dof * 16u, 0, kPolicyNtSc1);
+      else
+        gstore<SNT, U4>(dst + (size_t)dof * 16, x);
+      count_store(t.wcnt, t.dst, dst + (size_t)dof * 16, 16);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ tile transpose
 
 // Head, interior and tail of the EB-aligned byte range [g, g + len): `head` single
@@ -954,8 +1029,6 @@ __global__ void __launch_bounds__(512) k_transpose_win(TransposeArgs t) {
 // element, the compiler splits each row into unaligned 2- and 12-byte pieces.
 // __builtin_amdgcn_perm(a, b, sel): byte k of the result is byte sel_k of the
 // 8-byte value a:b (b holds bytes 0-3, a bytes 4-7); selector 12 gives zero.
-using U4 = NativeOf<16>::T;
-
 template <int EB>
 __device__ __forceinline__ void transpose_rows16(const U4* in, U4* out) {
   if constexpr (EB == 16) {
@@ -1717,6 +1790,53 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int ski
   }
 }
 
+template <bool LNT, bool SNT>
+static bool launch_atoms_nt(const AtomArgs& a, int K, unsigned grid, hipStream_t st) {
+  switch (K) {
+    case 4: hipLaunchKernelGGL((k_atoms<4, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
+    case 8: hipLaunchKernelGGL((k_atoms<8, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
+    case 16: hipLaunchKernelGGL((k_atoms<16, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
+    case 32: hipLaunchKernelGGL((k_atoms<32, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
+    default: return false;
+  }
+}
+
+// Tiles of atoms (vector order 3), from the vector path's arguments in 16-byte units:
+// mode 0 is the atom, p.a and p.b the modes that continue it in the source and in
+// the destination.
+static bool launch_atoms(const Plan& p, const GenericArgs& g, unsigned grid, hipStream_t st) {
+  AtomArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src = g.src;
+  a.dst = g.dst;
+  a.wcnt = g.wcnt;
+  const int K = (int)g.m[0].ext;
+  const int64_t T = atom_tile(K);
+  a.ext_a = g.m[p.a].ext;
+  a.ext_b = g.m[p.b].ext;
+  a.ss_b = g.m[p.b].ss;
+  a.sd_a = g.m[p.a].sd;
+  a.tiles_a = (uint32_t)((a.ext_a + T - 1) / T);
+  a.tiles_b = (uint32_t)((a.ext_b + T - 1) / T);
+  a.fd_ta = fd_of(a.tiles_a);
+  a.fd_tb = fd_of(a.tiles_b);
+  for (int k = 1; k < p.rank; ++k) {
+    if (k == p.a || k == p.b) continue;
+    const int r = a.batch.rank++;
+    a.batch.ext[r] = g.m[k].ext;
+    a.batch.fd[r] = g.m[k].fd;
+    a.batch.ss[r] = g.m[k].ss;
+    a.batch.sd[r] = g.m[k].sd;
+  }
+  a.sws = g.sws;
+  a.swd = g.swd;
+  a.bufst = g.bufst;
+  if (p.nt_ld && p.nt) return launch_atoms_nt<true, true>(a, K, grid, st);
+  if (p.nt_ld) return launch_atoms_nt<true, false>(a, K, grid, st);
+  if (p.nt) return launch_atoms_nt<false, true>(a, K, grid, st);
+  return launch_atoms_nt<false, false>(a, K, grid, st);
+}
+
 template <int UB, bool LNT, bool SNT>
 static void launch_generic_nt(const GenericArgs& a, bool wide, int unroll, unsigned grid, hipStream_t st) {
   if (wide)
@@ -1967,6 +2087,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.n_chunks = (p.n_units + 256 * p.unroll - 1) / (256 * p.unroll);
       a.bufst = p.bufst ? 1u : 0u;
       const int ub = p.v * p.eb;
+      if (p.vorder == 3) return launch_atoms(p, a, grid, st) ? check_launch() : LR_ERR_PATH;
       LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.nt_ld, p.nt, grid, st));
       return check_launch();
     }

@@ -68,6 +68,10 @@ constexpr bool pipe_fits(int shape, int V) {
   return shape >= 0 && shape <= 2 && 2 * kTileTA[shape] * V * kTileTB[shape] * 16 <= 160 * 1024;
 }
 
+// Vector path, tiles of atoms (vector order 3): atoms of K 16-byte chunks per tile
+// side (1 KiB runs, at least 4 atoms).
+constexpr int64_t atom_tile(int64_t K) { return K >= 16 ? 4 : 64 / K; }
+
 // Everything the launch code needs.
 struct Plan {
   int path;           // lr_path
@@ -98,7 +102,8 @@ struct Plan {
   bool nt;           // non-temporal stores (and loads, except on the generic kernel)
   bool nt_ld;        // non-temporal loads
   bool policy_set;   // the caller chose the load or store policy
-  int vorder;        // vector/generic: traversal order after the common mode, -1 elsewhere
+  int vorder;        // vector/generic: traversal order after the common mode (3: tiles of
+                     // atoms through LDS, modes a and b, tile_a = tile_b atoms), -1 elsewhere
   bool direct;        // staged: direct global -> LDS loads (no register round trip)
   bool tel;           // transpose: element-granular tiles (rows without aligned chunks)
   bool twin;          // element tiles with 16-byte accesses inside each row (no swizzles,

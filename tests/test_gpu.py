@@ -443,7 +443,7 @@ def test_copy_random_pairs(dev, knobs):
         env = {"load_policy": pol[0], "store_policy": pol[1], "direct_loads": rng.choice([-1, 0, 1]),
                "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 4),
                "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
-               "vector_order": rng.choice([-1, 0, 1, 2]), "units_per_lane": rng.choice([-1, 1, 4]),
+               "vector_order": rng.choice([-1, 0, 1, 2, 3]), "units_per_lane": rng.choice([-1, 1, 4]),
                "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
                "transpose_reads": rng.choice([-1, 0, 1])}
         knobs.t.clear()
@@ -504,7 +504,7 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
         mult = _multiplicity(Ld, O.size(Ls), nd)
         knobs.t.clear()
         knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 4), gather_chunks=rng.choice([-1, 8, 16]),
-                  vector_order=rng.choice([-1, 0, 1, 2]), element_tiles=rng.choice([-1, 0, 1]),
+                  vector_order=rng.choice([-1, 0, 1, 2, 3]), element_tiles=rng.choice([-1, 0, 1]),
                   pipeline_tiles=rng.choice([-1, 2, 3]), transpose_reads=rng.choice([-1, 1]),
                   direct_loads=rng.choice([-1, 1]))
         for flags in [0] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
@@ -872,7 +872,7 @@ def test_vector_streaming_store_forms(dev, knobs, sc1):
              ("(1,999):(1,1)", "(1,999):(1,3)", 999, 16),
              (rt.src_layout, rt.dst_layout, rt.n_elems, 2)]
     ran = 0
-    for vorder in ("0", "1", "2"):
+    for vorder in ("0", "1", "2", "3"):
         knobs.set(vector_order=int(vorder))
         for ci, (ts, td, n, eb) in enumerate(cases):
             ns, nd = max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize)
@@ -885,7 +885,7 @@ def test_vector_streaming_store_forms(dev, knobs, sc1):
             say("vector stores", "sc1" if sc1 == "1" else "global", ts, "->", td, "eb", eb, "vorder", vorder)
             assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td)
             ran += 1
-    assert ran == 3 * len(cases)
+    assert ran == 4 * len(cases)
 
 
 def _pow2_align(off):
@@ -1248,7 +1248,7 @@ def test_vector_split_load_store_policies(dev, knobs, pol):
         src = np.random.default_rng(ci).integers(0, 256, ns * eb, dtype=np.uint8)
         dst = np.full(nd * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-        for vo in (0, 1, 2):
+        for vo in (0, 1, 2, 3):
             knobs.t.clear()
             knobs.set(load_policy=pol[0], store_policy=pol[1], vector_order=vo)
             p = plan(ts, ns, td, nd, eb)
@@ -1327,7 +1327,65 @@ def test_channel_shuffle_any_pixel_count(dev, knobs, eb):
     assert ran >= 8
 
 
-@pytest.mark.parametrize("vorder", [0, 1, 2])
+def _atom_cases():
+    """(src, dst, src elems, dst elems, eb): the atom (mode 0) of w elements continued by a
+    in the source and by b in the destination -- every atom size from 4 to 32 chunks
+    (64-512 bytes), extents that leave ragged tiles, batch modes with padding, swizzles
+    on either side, and the 512^2 retile."""
+    rt = W.small("retile")
+    cases = [
+        ("(64,13,21,3):(1,64,832,20000)", "(64,13,21,3):(1,1344,64,17600)", 2),   # K 8, ragged, batch
+        ("(64,40,70):(1,64,2560)", "(64,40,70):(1,4480,64)", 1),                    # K 4, T 16
+        ("(16,33,17):(1,16,528)", "(16,33,17):(1,272,16)", 4),                      # K 4, T 16
+        ("(32,9,6,2):(1,32,300,2000)", "(32,9,6,2):(1,192,32,1728)", 8),            # K 16, T 4
+        ("(32,5,7):(1,32,160)", "(32,5,7):(1,224,32)", 16),                         # K 32, T 4
+        ("(64,16,24):(1,64,1024)", "Sw<2,3,4> o (64,16,24):(1,1536,64)", 2),        # dst swizzle
+        ("Sw<1,4,3> o (64,16,24):(1,64,1024)", "(64,16,24):(1,1536,64)", 2),        # src swizzle
+        ("(8,17,40,8):(1,8,136,5600)", "(8,17,40,8):(1,320,8,5500)", 8),            # K 4, batch
+        (rt.src_layout, rt.dst_layout, 2),
+    ]
+    out = []
+    for ts, td, eb in cases:
+        n = O.size(O.parse(ts))
+        out.append((ts, td, max(n, O.cosize(O.parse(ts))), max(n, lr.parse(td).cosize), eb))
+    return out
+
+
+def test_atom_tiles(dev, knobs):
+    """The vector path's tiles of atoms through LDS (vector order 3, the planner's
+    choice for these layouts), under both streaming policies and both store forms,
+    byte-exact against the oracle."""
+    ran = 0
+    for ci, (ts, td, ns, nd, eb) in enumerate(_atom_cases()):
+        src = np.random.default_rng(200 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for pol in (None, ("0",), ("1", "1"), ("1", "0")):
+            knobs.t.clear()
+            if pol:
+                knobs.policy(*pol)
+            p = plan(ts, ns, td, nd, eb)
+            assert p["path"] in ("vector", "generic") and p["vector_order"] == 3, (ts, td, p)
+            say("atom tiles", ts, "->", td, "eb", eb, "policy", pol, "tile", p["tile_a"], "grid", p["grid"])
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, td, pol)
+            ran += 1
+    assert ran == 4 * len(_atom_cases())
+
+
+def test_atom_tiles_write_counts(dev, knobs):
+    """Every destination element of a tiles-of-atoms copy is stored exactly once."""
+    for ci, (ts, td, ns, nd, eb) in enumerate(_atom_cases()):
+        src = np.random.default_rng(300 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        mult = _multiplicity(O.parse(td), O.size(O.parse(ts)), nd)
+        assert plan(ts, ns, td, nd, eb)["vector_order"] == 3
+        say("atom tiles write counts", ts, "eb", eb)
+        got, counts = _write_counts(dev, src, ts, dst, td, eb)
+        assert np.array_equal(counts, (mult > 0).astype(np.int32)), ts
+        assert np.array_equal(got, O.copy(src, O.parse(ts), dst, O.parse(td), eb))
+
+
+@pytest.mark.parametrize("vorder", [0, 1, 2, 3])
 def test_vector_traversal_orders(dev, knobs, vorder):
     knobs.set(vector_order=vorder)
     cases = [(W.small("retile").src_layout, W.small("retile").dst_layout, 512 * 512, 512 * 512, 2),

@@ -710,7 +710,7 @@ def test_tuning_overrides_are_checked():
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
     for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 5},
-                {"units_per_lane": 2}, {"vector_order": 3}, {"gather_chunks": 3}, {"direct_loads": 2},
+                {"units_per_lane": 2}, {"vector_order": 4}, {"gather_chunks": 3}, {"direct_loads": 2},
                 {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2}):
         with pytest.raises(lr.LayoutRemapError) as e:
             lr.copy_plan(*args, tuning=bad)
@@ -743,6 +743,34 @@ def test_pipelined_transpose_plan():
     assert lr.copy_plan(*ra, tuning={"pipeline_tiles": 4}) == lr.copy_plan(*ra)
     odd = ("(520,263):(263,1)", 520 * 263, "(520,263):(1,520)", 520 * 263, 2)
     assert lr.copy_plan(*odd, tuning={"pipeline_tiles": 4})["pipeline_tiles"] == 0
+
+
+def test_atom_tiles_plan():
+    """Vector order 3 (tiles of atoms through LDS): the planner's choice when the common
+    contiguous mode is an atom of 64-512 bytes continued by different modes in the
+    source and the destination, each at least one tile (1 KiB runs, >= 4 atoms) long;
+    the source order otherwise, also when order 3 is asked for."""
+    w = W.full("retile")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    p = lr.copy_plan(*args)
+    assert (p["path"], p["vector_order"], p["tile_a"], p["tile_b"]) == ("vector", 3, 8, 8)
+    joint = p["joint"]
+    assert joint[0] == (64, 1, 1)
+    assert joint[p["a_mode"]][1] == 64 and joint[p["b_mode"]][2] == 64   # a continues the atom in src, b in dst
+    assert p["grid"] == (64 // 8) * (128 // 8) * 32
+    q = lr.copy_plan(*args, tuning={"vector_order": 1})
+    assert q["vector_order"] == 1 and q["grid"] == 4096 * 4096 // 8 // 256
+    # atom sizes: 64 bytes -> 16 atoms a side, 256 and 512 -> 4
+    for eb, w_, T in ((1, 64, 16), (2, 64, 8), (8, 32, 4), (16, 32, 4)):
+        ts, td = f"({w_},40,50):(1,{w_},{40 * w_})", f"({w_},40,50):(1,{50 * w_},{w_})"
+        r = lr.copy_plan(ts, 2000 * w_, td, 2000 * w_, eb)
+        assert r["vector_order"] == 3 and r["tile_a"] == T, (eb, w_, r)
+    # one side shorter than a tile, or a 16-byte atom: not tiles of atoms
+    short = lr.copy_plan("(64,7,50):(1,64,448)", 64 * 350, "(64,7,50):(1,3200,64)", 64 * 350, 2,
+                         tuning={"vector_order": 3})
+    assert short["vector_order"] == 1
+    small = lr.copy_plan("(8,40,50):(1,8,320)", 16000, "(8,40,50):(1,400,8)", 16000, 2)
+    assert small["vector_order"] != 3
 
 
 def test_transpose_reads_plan():

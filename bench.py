@@ -23,9 +23,12 @@ Other modes (for rocprofv3 runs and their summaries under profiles/):
                         read rocprofv3 --pmc CSV output and write profiles/traffic.json
   --summarize-trace DIR read rocprofv3 --kernel-trace CSV output and print a
                         markdown table of the library's kernels (per grid size)
-  --launch NAME[:JSON]  (repeatable) launch workload NAME four times with the
-                        lr_copy_tuning overrides in JSON, e.g.
-                        padtiles:{"gather_chunks":16}, for before/after profiles
+  --launch NAME[:JSON]  (repeatable) workload NAME with the lr_copy_tuning
+                        overrides in JSON, e.g. padtiles:{"gather_chunks":16}: one
+                        untimed launch, then 12 cold launches (rotating buffers)
+                        timed with HIP events; for before/after profiles
+  --back-to-back K      with --launch: also K launches back to back, timed like
+                        the benchmark's timed region
 """
 
 from __future__ import annotations
@@ -101,13 +104,13 @@ def _cpu_model() -> str:
 # ----------------------------------------------------------------------------
 # timing helpers
 # ----------------------------------------------------------------------------
-def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
+def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0, tuning=None):
     """Back-to-back copies rotating over buffer pairs; returns (ms per step of wall
     time, ms per step from HIP events recorded on the launch stream)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         s, d = pairs[i % len(pairs)]
-        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream, tuning=tuning)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -115,7 +118,7 @@ def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0):
     ev0.record(stream)
     for i in range(steps):
         s, d = pairs[i % len(pairs)]
-        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream)
+        lr.layout_copy(s, Ls, d, Ld, elem_bytes=eb, flags=flags, stream=stream, tuning=tuning)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
@@ -280,11 +283,14 @@ def counters_run(lr, torch, W, reps: int = 3):
           flush=True)
 
 
-def launch_run(lr, torch, W, specs, reps: int = 12):
+def launch_run(lr, torch, W, specs, reps: int = 12, back_to_back: int = 0):
     """Each NAME[:JSON] spec: its workload with that tuning, one untimed launch and
     then `reps` launches rotating over buffer pairs of >= 1 GiB in total (cold, as in
-    the timed benchmark), each bracketed by HIP events.  Prints one line per spec;
-    under rocprofv3 each spec is one group of reps + 1 dispatches."""
+    the timed benchmark), each bracketed by HIP events.  With back_to_back = K, then
+    also K launches back to back over the same buffers after 3 untimed ones, timed
+    like the benchmark's timed region (HIP events around all K).  Prints one line per
+    spec; under rocprofv3 each spec is one group of reps + 1 dispatches (reps + 4 + K
+    with back_to_back)."""
     dev = torch.device("cuda:0")
     for spec in specs:
         name, _, js = spec.partition(":")
@@ -295,10 +301,15 @@ def launch_run(lr, torch, W, specs, reps: int = 12):
         pairs = _pairs(torch, dev, w.src_elems * eb, w.dst_elems * eb)
         us = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, eb, reps, tuning=tuning)
         med = us[len(us) // 2]
+        b2b = ""
+        if back_to_back:
+            _, ms = _time_copies(lr, torch, pairs, w.src_layout, w.dst_layout, eb, back_to_back, 3, tuning=tuning)
+            b2b = (f" us_back_to_back={ms * 1e3:.2f} "
+                   f"GBps_back_to_back={W.bytes_moved(w) / (ms * 1e-3) / 1e9:.0f}")
         print(f"launch: {w.name} tuning={tuning} path={p['path']} grid={p['grid']} "
               f"tile={p['tile_a']}x{p['tile_b']} direct={p['direct']} pipeline_tiles={p['pipeline_tiles']} "
               f"gather_chunks={p['gather_chunks']} us_median={med:.2f} us_best={us[0]:.2f} "
-              f"GBps_median={W.bytes_moved(w) / (med * 1e-6) / 1e9:.0f}", flush=True)
+              f"GBps_median={W.bytes_moved(w) / (med * 1e-6) / 1e9:.0f}{b2b}", flush=True)
         del pairs
         torch.cuda.empty_cache()
 
@@ -426,6 +437,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--groups-of", type=int, default=0, help="with --summarize-trace: dispatches per launch group")
     ap.add_argument("--launch", action="append", metavar="NAME[:JSON]")
+    ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
+                    help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -453,7 +466,7 @@ def main():
         counters_run(lr, torch, W)
         return
     if args.launch:
-        launch_run(lr, torch, W, args.launch)
+        launch_run(lr, torch, W, args.launch, back_to_back=args.back_to_back)
         return
 
     flags = 0

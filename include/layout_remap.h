@@ -319,7 +319,8 @@ typedef struct {
                           shuffle (planes without aligned chunks), which streams from 256 MiB */
   int32_t order;       /* transpose: workgroup -> tile order (0 a-tiles fastest, 1 b-tiles
                           fastest, 2 diagonal with a fastest, 3 diagonal over 4 x 4 tile groups,
-                          4 diagonal with b fastest); -1 on other paths */
+                          4 diagonal with b fastest; 5..9 the same over workgroup numbers
+                          grouped by XCD, each XCD taking a contiguous run); -1 on other paths */
   int32_t direct;      /* 1 if the source tile goes straight from global memory into LDS
                           (staged and transpose paths) */
   int32_t load_policy;  /* cache-policy bits of the source loads: 0 plain, 2 non-temporal */
@@ -380,7 +381,7 @@ typedef struct {
   int32_t interleave_form; /* interleave: 0 one chunk per lane per head, 1 one destination
                               chunk per lane from narrow loads, 2 the channel shuffle */
   int32_t tile_shape;      /* transpose: 0..6, the tile shapes of lr_plan.tile_a/tile_b */
-  int32_t tile_order;      /* transpose: 0..4, as lr_plan.order */
+  int32_t tile_order;      /* transpose: 0..9, as lr_plan.order (5..9 not with pipeline_tiles) */
   int32_t element_tiles;   /* transpose: 0 chunk tiles, 1 element-granular tiles */
   int32_t direct_loads;    /* staged and LDS transpose: 0 through registers, 1 global -> LDS */
   int32_t gather_chunks;   /* staged: destination chunks of one tile per 32-lane slice of

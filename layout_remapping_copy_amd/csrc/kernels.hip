@@ -667,7 +667,9 @@ struct TransposeArgs {
   BatchArg batch;
   SwzArg sws, swd;
   uint32_t order;  // 0: tiles along a vary fastest across workgroups, 1: along b, 2: diagonal,
-                   // 3: diagonal over 4 x 4 groups of tiles, 4: diagonal with b fastest
+                   // 3: diagonal over 4 x 4 groups of tiles, 4: diagonal with b fastest;
+                   // 5..9: orders 0..4 over workgroup numbers grouped by XCD
+  uint32_t nwg;    // orders 5..9: workgroups launched
   uint32_t gta, gtb;  // order 3: groups along a and b
   FD fd_gta, fd_gtb;
   // streaming stores of the LDS tile transpose: 1 = buffer stores relative to the
@@ -682,19 +684,29 @@ struct TransposeArgs {
 };
 
 // Workgroup number -> (a-tile, b-tile, batch index) in the order t.order selects.
+// Orders 5..9 first renumber the workgroups by XCD: the dispatcher hands workgroup
+// w to XCD w % 8, so w -> (w % 8) * ceil-share + w / 8 gives each XCD a contiguous
+// run of numbers (the XCDs with index below nwg % 8 take one more), i.e. the
+// workgroups one XCD runs together take neighbouring tiles and share its L2.
 __device__ __forceinline__ void transpose_tile(const TransposeArgs& t, uint32_t blk, uint32_t& ta, uint32_t& tb,
                                                uint32_t& r2) {
-  if (t.order == 0) {
+  uint32_t order = t.order;
+  if (order >= 5) {
+    const uint32_t x = blk & 7u, q = t.nwg >> 3, r = t.nwg & 7u;
+    blk = x * q + (x < r ? x : r) + (blk >> 3);
+    order -= 5;
+  }
+  if (order == 0) {
     uint32_t r1 = fdiv(blk, t.fd_ta);
     ta = blk - r1 * t.tiles_a;
     r2 = fdiv(r1, t.fd_tb);
     tb = r1 - r2 * t.tiles_b;
-  } else if (t.order == 1) {
+  } else if (order == 1) {
     uint32_t r1 = fdiv(blk, t.fd_tb);
     tb = blk - r1 * t.tiles_b;
     r2 = fdiv(r1, t.fd_ta);
     ta = r1 - r2 * t.tiles_a;
-  } else if (t.order == 2) {
+  } else if (order == 2) {
     // diagonal: consecutive workgroups take consecutive a-tiles and, with them,
     // shifted b-tiles, so that neither the rows they read nor the rows they write
     // share one column offset (power-of-two pitches otherwise land every row of a
@@ -705,7 +717,7 @@ __device__ __forceinline__ void transpose_tile(const TransposeArgs& t, uint32_t 
     uint32_t ta_mod = ta - fdiv(ta, t.fd_tb) * t.tiles_b;  // ta % tiles_b
     uint32_t d = (r1 - r2 * t.tiles_b) + ta_mod;            // < 2 * tiles_b
     tb = d >= t.tiles_b ? d - t.tiles_b : d;
-  } else if (t.order == 4) {
+  } else if (order == 4) {
     // the diagonal with the roles of a and b swapped: consecutive workgroups take
     // consecutive b-tiles and, with them, shifted a-tiles
     uint32_t r1 = fdiv(blk, t.fd_tb);
@@ -2140,9 +2152,10 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.sws = swz_arg(p.sw_s);
       a.swd = swz_arg(p.sw_d);
       a.order = p.torder;
+      a.nwg = (uint32_t)p.grid;
       a.bufst = p.bufst ? 1u : 0u;
       a.bufmask = p.sw_d.b ? ~((1u << (p.sw_d.m + p.sw_d.b)) - 1u) : ~0u;
-      if (p.torder == 3) {
+      if (p.torder % 5 == 3) {
         a.gta = a.tiles_a / 4;
         a.gtb = a.tiles_b / 4;
         a.fd_gta = fd_of(a.gta);

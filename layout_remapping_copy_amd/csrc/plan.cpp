@@ -134,7 +134,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
   };
   if (!in(t.load_policy, {0, 2}) || !in(t.store_policy, {0, 2, 18}) || !in(t.units_per_lane, {1, 4}) ||
       !in(t.vector_order, {0, 1, 2, 3}) || !in(t.interleave_form, {0, 1, 2}) ||
-      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6}) || !in(t.tile_order, {0, 1, 2, 3, 4}) ||
+      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6}) || !in(t.tile_order, {0, 1, 2, 3, 4, 5, 6, 7, 8, 9}) ||
       !in(t.element_tiles, {0, 1}) || !in(t.direct_loads, {0, 1}) || !in(t.gather_chunks, {1, 2, 4, 8, 16, 32}))
     return false;
   if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;
@@ -747,7 +747,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       }
       const int64_t nta = (p->m[a].ext + p->tile_a - 1) / p->tile_a;
       const int64_t ntb = (ext_b + p->tile_b - 1) / p->tile_b;
-      if (p->torder == 3 && (nta % 4 || ntb % 4)) p->torder = 2;  // grouped order needs 4 | tiles
+      if (p->torder % 5 == 3 && (nta % 4 || ntb % 4)) p->torder -= 1;  // grouped order needs 4 | tiles
       int64_t batch = 1;
       for (int k = 0; k < p->rank; ++k)
         if (k != a && k != b && k != b2) batch *= p->m[k].ext;
@@ -761,6 +761,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->direct = true;
         p->bufst = false;
         p->grid = (p->tiles_total + p->pipe - 1) / p->pipe;
+        if (p->torder >= 5) p->torder -= 5;  // XCD grouping renumbers workgroups, not tiles
       }
       // gfx950 transpose reads of the LDS tile: 2-byte elements in 16-byte chunks,
       // tiles 16 or 32 chunks on each side, loaded directly (or pipelined)
@@ -945,7 +946,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
           (p.tshape != 0 && ((v * p.eb != 16 && !(p.eb == 1 && v == 8)) || !shape_fits(p.tshape, (int)v) ||
                              p.path != LR_PATH_TRANSPOSE)))
         return bad();
-      if (p.torder > 4) return bad();
+      if (p.torder > 9 || (p.torder >= 5 && p.pipe)) return bad();  // XCD grouping: one tile per workgroup
       if (p.bufst) {  // buffer stores: full chunks of the LDS kernel, tile span under 4 GiB
         const int64_t swz_blk = p.sw_d.b ? (int64_t(1) << (p.sw_d.m + p.sw_d.b)) : 0;
         const int64_t span = ((p.tile_a - 1) * p.m[p.a].sd + p.tile_b + 2 * swz_blk) * p.eb;
@@ -964,7 +965,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
         return bad();
       }
       const int64_t nta = (p.m[p.a].ext + p.tile_a - 1) / p.tile_a, ntb = (ext_b + p.tile_b - 1) / p.tile_b;
-      if (p.torder == 3 && (nta % 4 || ntb % 4)) return bad();
+      if (p.torder % 5 == 3 && (nta % 4 || ntb % 4)) return bad();
       // one workgroup per tile and batch index, all launched (no grid cap)
       int64_t batch = 1;
       for (int k = 0; k < p.rank; ++k)

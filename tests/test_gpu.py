@@ -441,7 +441,7 @@ def test_copy_random_pairs(dev, knobs):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         pol = rng.choice([(0, -1), (2, -1), (2, 2), (2, 0)])  # the last: vector/generic paths only
         env = {"load_policy": pol[0], "store_policy": pol[1], "direct_loads": rng.choice([-1, 0, 1]),
-               "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 4),
+               "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 9),
                "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
                "vector_order": rng.choice([-1, 0, 1, 2, 3]), "units_per_lane": rng.choice([-1, 1, 4]),
                "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
@@ -503,7 +503,7 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
         want = O.copy(src, Ls, dst, Ld, eb)
         mult = _multiplicity(Ld, O.size(Ls), nd)
         knobs.t.clear()
-        knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 4), gather_chunks=rng.choice([-1, 8, 16]),
+        knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 9), gather_chunks=rng.choice([-1, 8, 16]),
                   vector_order=rng.choice([-1, 0, 1, 2, 3]), element_tiles=rng.choice([-1, 0, 1]),
                   pipeline_tiles=rng.choice([-1, 2, 3]), transpose_reads=rng.choice([-1, 1]),
                   direct_loads=rng.choice([-1, 1]))
@@ -979,6 +979,40 @@ def test_odd_pitch_transposes_full_size(dev):
         torch.cuda.synchronize()
         assert np.array_equal(d.cpu().numpy(), want), (r, c, eb)
         del s, d
+
+
+def test_transpose_xcd_grouped_orders(dev, knobs):
+    """Tile orders 5..9: orders 0..4 over workgroup numbers renumbered by XCD (each XCD
+    a contiguous run; grids that are and are not multiples of 8).  Chunk tiles of
+    every read-back form, element tiles and the register-only transpose; every
+    destination element stored once."""
+    cases = _pipe_cases() + [("(301,517):(517,1)", "(301,517):(1,301)", 301 * 517, 301 * 517, 2)]
+    ran = 0
+    for ci, (ts, td, ns, nd, eb) in enumerate(cases):
+        src = np.random.default_rng(400 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        mult = _multiplicity(O.parse(td), O.size(O.parse(ts)), nd)
+        for order in (5, 6, 7, 8, 9):
+            for extra, flags in (({}, 0), ({"direct_loads": 1, "tile_shape": 1}, 0),
+                                 ({"direct_loads": 1, "transpose_reads": 1}, 0), ({"element_tiles": 1}, 0),
+                                 ({}, lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE_DIRECT))):
+                knobs.t.clear()
+                knobs.set(tile_order=order, **extra)
+                try:
+                    p = plan(ts, ns, td, nd, eb, flags)
+                except lr.LayoutRemapError:
+                    continue
+                if not p["path"].startswith("transpose"):
+                    continue
+                say("xcd order", order, extra, hex(flags), ts, "eb", eb, "grid", p["grid"], "order", p["order"])
+                assert p["order"] in (order, order - 1), p   # 8 falls back to 7 without 4 | tiles
+                assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want), (ts, order, extra)
+                if order == 6 and not flags:
+                    _, counts = _write_counts(dev, src, ts, dst, td, eb)
+                    assert np.array_equal(counts, (mult > 0).astype(np.int32)), (ts, extra)
+                ran += 1
+    assert ran >= 150
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])

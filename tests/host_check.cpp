@@ -109,6 +109,66 @@ static std::string rand_layout(std::mt19937_64& rng, bool swz) {
   return out;
 }
 
+// A random lr_copy_tuning: every field at one of its valid values or -1.
+static lr_copy_tuning rand_tuning(std::mt19937_64& rng) {
+  lr_copy_tuning t;
+  lr_copy_tuning_init(&t);
+  auto pick = [&](std::initializer_list<int32_t> v) { return *(v.begin() + rng() % v.size()); };
+  t.load_policy = pick({-1, 0, 2});
+  t.store_policy = pick({-1, 0, 2, 18});
+  t.units_per_lane = pick({-1, 1, 4});
+  t.vector_order = pick({-1, 0, 1, 2, 3});
+  t.interleave_form = pick({-1, 0, 1, 2});
+  t.tile_shape = pick({-1, 0, 1, 2, 3, 4, 5, 6});
+  t.tile_order = pick({-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9});
+  t.element_tiles = pick({-1, 0, 1});
+  t.direct_loads = pick({-1, 0, 1});
+  t.gather_chunks = pick({-1, 1, 2, 4, 8, 16, 32});
+  t.pipeline_tiles = pick({-1, 0, 2, 3, 5, 64});
+  t.transpose_reads = pick({-1, 0, 1});
+  return t;
+}
+
+// Plans a copy with the given overrides; a plan the planner accepts must pass its own
+// invariant check (the check every launch runs).
+static bool tuned_plan_ok(const lr_layout* a, int64_t cap_a, size_t align_a, const lr_layout* b, int64_t cap_b,
+                          size_t align_b, int eb, uint32_t fl, const lr_copy_tuning& t) {
+  lr::Plan p;
+  if (lr::plan_copy(a, cap_a, align_a, b, cap_b, align_b, eb, fl, &t, &p) != LR_OK) return true;
+  return lr::verify_plan(p, cap_a, cap_b) == LR_OK;
+}
+
+// A tiled pair: an atom of w elements continued by mode a in the source and by mode
+// b in the destination, a batch mode, padding on either side, sometimes a swizzle
+// that keeps 16-byte chunks (the structure of the vector path's tiles of atoms).
+static void rand_atom_pair(std::mt19937_64& rng, int eb, lr_layout* s, lr_layout* d) {
+  const int64_t w = (int64_t)((16 << (rng() % 6)) / eb), A = 1 + (int64_t)(rng() % 40), B = 1 + (int64_t)(rng() % 40),
+                C = 1 + (int64_t)(rng() % 3);
+  const int64_t pa = (rng() % 3 == 0) ? (int64_t)(16 / eb) * (int64_t)(rng() % 3) : 0;
+  const int64_t pb = (rng() % 3 == 0) ? (int64_t)(16 / eb) * (int64_t)(rng() % 3) : 0;
+  std::memset(s, 0, sizeof(*s));
+  s->nleaves = s->nmodes = 4;
+  const int64_t shape[4] = {w, A, B, C};
+  for (int i = 0; i < 4; ++i) {
+    s->shape[i] = shape[i];
+    s->mode_end[i] = i + 1;
+  }
+  *d = *s;
+  s->stride[0] = 1;
+  s->stride[1] = w;
+  s->stride[2] = w * A + pa;
+  s->stride[3] = (w * A + pa) * B;
+  d->stride[0] = 1;
+  d->stride[2] = w;
+  d->stride[1] = w * B + pb;
+  d->stride[3] = (w * B + pb) * A;
+  if (rng() % 4 == 0 && w * eb >= 64) {  // Sw<B,M,S> with M at least the 16-byte chunk
+    d->swz_b = 1 + (int)(rng() % 2);
+    d->swz_m = 4 - (eb >= 16 ? 4 : eb >= 8 ? 3 : eb >= 4 ? 2 : eb >= 2 ? 1 : 0) + (int)(rng() % 2);
+    d->swz_s = d->swz_b + 1 + (int)(rng() % 3);
+  }
+}
+
 static int run_fuzz() {
   std::mt19937_64 rng(777);
   char buf[1024];
@@ -180,7 +240,43 @@ static int run_fuzz() {
       }
     }
     for (int path = 0; path < 8; ++path) lr_copy_plan(&a, 1 << 20, 16, &a, 1 << 20, 16, 1, LR_COPY_FORCE_PATH(path), &p);
+    // random overrides
+    for (int k = 0; k < 4; ++k) {
+      const lr_copy_tuning t = rand_tuning(rng);
+      const int eb = 1 << (rng() % 5);
+      const uint32_t fl = (uint32_t)(rng() % 3);
+      if (!tuned_plan_ok(&a, 1 << 20, 16, &c, 1 << 20, 16, eb, fl, t) ||
+          !tuned_plan_ok(&c, 1 << 20, 16, &a, 1 << 20, 16, eb, fl, t) ||
+          !tuned_plan_ok(&a, 1 << 20, 16, &b, 1 << 20, 16, eb, fl, t)) {
+        std::printf("a tuned plan fails its check: %s -> %s eb=%d\n", ta.c_str(), tb.c_str(), eb);
+        return 1;
+      }
+    }
     ++n_ok;
+  }
+  // tiled pairs (tiles of atoms where they apply) under random overrides
+  int atoms = 0;
+  for (int it = 0; it < 20000; ++it) {
+    const int eb = 1 << (rng() % 5);
+    lr_layout s, d;
+    rand_atom_pair(rng, eb, &s, &d);
+    int64_t cs, cd;
+    lr_cosize(&s, &cs);
+    lr_cosize(&d, &cd);
+    const lr_copy_tuning t = rand_tuning(rng);
+    lr::Plan p;
+    const int rc = lr::plan_copy(&s, cs, 16, &d, cd, 16, eb, 0, (it % 2) ? &t : nullptr, &p);
+    if (rc == LR_OK) {
+      if (lr::verify_plan(p, cs, cd) != LR_OK) {
+        std::printf("tiled pair: plan fails its check (eb=%d w=%lld)\n", eb, (long long)s.shape[0]);
+        return 1;
+      }
+      atoms += p.vorder == 3;
+    }
+  }
+  if (atoms < 1000) {
+    std::printf("tiled pairs: only %d took tiles of atoms\n", atoms);
+    return 1;
   }
   // copies too large for 32-bit offsets: the blocks cover every index once and fit
   for (int it = 0; it < 3000; ++it) {
@@ -255,7 +351,7 @@ static int run_fuzz() {
   x.stride[0] = 1;
   x.stride[1] = int64_t(1) << 40;
   if (lr_layout_validate(&x) != LR_ERR_OVERFLOW) return 1;
-  std::printf("fuzz ok (%d)\n", n_ok);
+  std::printf("fuzz ok (%d; %d tiled pairs on tiles of atoms)\n", n_ok, atoms);
   return 0;
 }
 

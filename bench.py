@@ -50,10 +50,12 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 
 HEADLINE = "interleave"
-OTHERS = ("transpose", "retile", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw")
+OTHERS = ("transpose", "retile", "interleave_cm", "nhwc2nchw", "padtiles", "shard_pack", "rgb_nhwc2nchw",
+          "head_split")
 # traffic.json keys: workload name + element type
 DTYPE_NAME = {"transpose": "fp16", "retile": "bf16", "interleave": "bf16", "interleave_cm": "bf16",
-              "nhwc2nchw": "fp16", "padtiles": "fp32", "shard_pack": "fp16", "rgb_nhwc2nchw": "fp16"}
+              "nhwc2nchw": "fp16", "padtiles": "fp32", "shard_pack": "fp16", "rgb_nhwc2nchw": "fp16",
+              "head_split": "bf16"}
 
 
 def _kernel_hash() -> str:

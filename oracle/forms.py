@@ -60,6 +60,12 @@ def nchw2nhwc(src: np.ndarray, n: int, h: int, w: int, c: int, eb: int = 2) -> n
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
 
 
+def head_split(src: np.ndarray, b: int, s: int, h: int, d: int) -> np.ndarray:
+    """(b,s,h,d) contiguous -> (b,h,s,d) contiguous, 2-byte elements."""
+    x = src.view(np.uint16).reshape(b, s, h, d).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
+
+
 def padtiles(src: np.ndarray, tiles: int) -> np.ndarray:
     """Per tile of 72 words: element k of the destination tile is word
     18*(k%4) + (k/4)%8 + 9*(k/32) of the source tile, i.e. the padded (8,8):(1,9)

@@ -523,7 +523,8 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles"])
+@pytest.mark.parametrize("name", ["transpose", "retile", "interleave", "interleave_cm", "nhwc2nchw", "padtiles",
+                                  "head_split"])
 def test_write_counts_full_size(dev, name):
     """At full size, in the launch configuration the benchmark times: the
     destination layouts are bijections onto [0, N) (the oracle's injectivity test
@@ -603,11 +604,12 @@ FORMS = {
     "padtiles": lambda s: F.padtiles(s, 1 << 20),
     "shard_pack": lambda s: F.shard_pack(s, 1024, 8192, 8),
     "rgb_nhwc2nchw": lambda s: F.nhwc2nchw(s, 512, 224, 224, 3),
+    "head_split": lambda s: F.head_split(s, 16, 4096, 32, 128),
 }
 
 FULL_PATH = {"transpose": "transpose", "retile": "vector", "interleave": "interleave", "interleave_cm": "transpose",
              "nhwc2nchw": "transpose", "padtiles": "staged", "shard_pack": "transpose",
-             "rgb_nhwc2nchw": "deinterleave"}
+             "rgb_nhwc2nchw": "deinterleave", "head_split": "vector"}
 
 
 @pytest.mark.slow

@@ -755,6 +755,7 @@ def test_forms_equal_oracle_copy():
         "padtiles": lambda s: F.padtiles(s, 1000),
         "shard_pack": lambda s: F.shard_pack(s, 520, 2112, 8),
         "rgb_nhwc2nchw": lambda s: F.nhwc2nchw(s, 3, 17, 40, 3),
+        "head_split": lambda s: F.head_split(s, 2, 70, 6, 128),
     }
     for name, form in cases.items():
         w = W.small(name)

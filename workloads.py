@@ -207,6 +207,18 @@ def shard_pack(rows: int = 1024, cols: int = 8192, parts: int = 8) -> Workload:
         src_elems=rows * cols, dst_elems=rows * cols, seed=8, values="bits16", n_elems=rows * cols)
 
 
+def head_split(b: int = 16, s: int = 4096, h: int = 32, d: int = 128) -> Workload:
+    # logical (b, s, h, d): a (batch, sequence, head, head-dim) tensor regrouped head by
+    # head, (b, h, s, d); the head dimension stays contiguous on both sides (256-byte
+    # atoms for bf16 d = 128)
+    return Workload(
+        name=f"head_split{b}x{s}x{h}x{d}", elem_bytes=2,
+        src_layout=f"({b},{s},{h},{d}):({s * h * d},{h * d},{d},1)",
+        dst_layout=f"({b},{s},{h},{d}):({h * s * d},{d},{s * d},1)",
+        src_elems=b * s * h * d, dst_elems=b * s * h * d, seed=10, values="normal_bf16",
+        n_elems=b * s * h * d)
+
+
 FULL = {
     "tile8x8": tile8x8,
     "transpose": transpose,
@@ -217,6 +229,7 @@ FULL = {
     "padtiles": padtiles,
     "shard_pack": shard_pack,
     "rgb_nhwc2nchw": rgb_nhwc2nchw,
+    "head_split": head_split,
 }
 
 
@@ -232,6 +245,7 @@ def small(name: str) -> Workload:
         "padtiles": lambda: padtiles(1000),
         "shard_pack": lambda: shard_pack(520, 2112, 8),
         "rgb_nhwc2nchw": lambda: rgb_nhwc2nchw(3, 17, 40, 3),
+        "head_split": lambda: head_split(2, 70, 6, 128),
     }[name]()
 
 

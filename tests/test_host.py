@@ -544,7 +544,7 @@ def test_common_vector_sound_and_tight_on_workloads():
 
 EXPECTED_PATH = {"tile8x8": "alias", "transpose": "transpose", "retile": "vector", "interleave": "interleave",
                  "interleave_cm": "transpose", "nhwc2nchw": "transpose", "padtiles": "staged",
-                 "shard_pack": "transpose", "rgb_nhwc2nchw": "deinterleave"}
+                 "shard_pack": "transpose", "rgb_nhwc2nchw": "deinterleave", "head_split": "vector"}
 
 
 @pytest.mark.parametrize("name", list(W.FULL))
@@ -557,8 +557,8 @@ def test_plan_of_workloads(name):
         want = O.joint_flat(O.parse(w.src_layout), O.parse(w.dst_layout), sort_by_dst=True)
         # same modes; the vector path walks the modes after the first in source order
         assert p["joint"][0] == tuple(want[0]) and sorted(p["joint"]) == sorted(tuple(m) for m in want)
-    if name == "retile":
-        assert p["vec_elems"] * w.elem_bytes == 16
+    if name in ("retile", "head_split"):  # tiles of 128- and 256-byte atoms
+        assert p["vec_elems"] * w.elem_bytes == 16 and p["vector_order"] == 3
 
 
 def test_plan_joint_matches_oracle_random():

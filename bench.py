@@ -29,6 +29,8 @@ Other modes (for rocprofv3 runs and their summaries under profiles/):
                         timed with HIP events; for before/after profiles
   --back-to-back K      with --launch: also K launches back to back, timed like
                         the benchmark's timed region
+  --atom-sweep          head splits for head dims of 32-512 bytes: tiles of
+                        atoms against the source order, beside a plain copy
 """
 
 from __future__ import annotations
@@ -316,6 +318,45 @@ def launch_run(lr, torch, W, specs, reps: int = 12, back_to_back: int = 0):
         torch.cuda.empty_cache()
 
 
+def atom_sweep(lr, torch, steps: int = 20):
+    """(16,s,h,d) -> (16,h,s,d) bf16 head splits for head dims of 32-512 bytes: tiles
+    of atoms (vector order 3) against the source order (1), back to back over
+    rotating buffers, beside a contiguous copy of the same bytes.  One JSON line per
+    head dim.  An order the planner cannot take falls back (its plan is printed)."""
+    dev = torch.device("cuda:0")
+    for d, s, h in ((16, 4096, 32), (24, 4096, 32), (40, 4096, 32), (48, 4096, 32), (64, 4096, 32), (80, 4096, 32),
+                    (96, 4096, 32), (112, 4096, 32), (128, 4096, 32), (160, 4096, 16), (192, 4096, 16),
+                    (256, 4096, 16)):
+        b = 16
+        ts = f"({b},{s},{h},{d}):({s * h * d},{h * d},{d},1)"
+        td = f"({b},{s},{h},{d}):({h * s * d},{d},{s * d},1)"
+        n = b * s * h * d
+        pairs = _pairs(torch, dev, n * 2, n * 2)
+        res = {}
+        for vo in (3, 1):
+            p = lr.copy_plan(ts, n, td, n, 2, tuning={"vector_order": vo})
+            _, ms = _time_copies(lr, torch, pairs, ts, td, 2, steps, 3, tuning={"vector_order": vo})
+            res[vo] = {"path": p["path"], "vector_order": p["vector_order"], "tile": p["tile_a"],
+                       "us": round(ms * 1e3, 2), "GBps": round(4 * n / (ms * 1e-3) / 1e9)}
+        # the staged path, which takes short common runs when the atom tiles do not
+        staged = None
+        try:
+            fl = lr.COPY_FORCE_PATH(lr.PATH_STAGED)
+            lr.copy_plan(ts, n, td, n, 2, fl)
+            _, sms = _time_copies(lr, torch, pairs, ts, td, 2, steps, 3, flags=fl)
+            staged = {"us": round(sms * 1e3, 2), "GBps": round(4 * n / (sms * 1e-3) / 1e9)}
+        except lr.LayoutRemapError:
+            pass
+        n16 = n * 2 // 16
+        _, cms = _time_copies(lr, torch, pairs, f"{n16}:1", f"{n16}:1", 16, steps, 3)
+        default = lr.copy_plan(ts, n, td, n, 2)
+        print(json.dumps({"head_dim": d, "atom_bytes": 2 * d, "planner": [default["path"], default["vector_order"]],
+                          "order3": res[3], "order1": res[1], "staged": staged, "copy_us": round(cms * 1e3, 2)}),
+              flush=True)
+        del pairs
+        torch.cuda.empty_cache()
+
+
 def _csv_rows(directory: str, suffix: str):
     rows = []
     for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
@@ -439,6 +480,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--groups-of", type=int, default=0, help="with --summarize-trace: dispatches per launch group")
     ap.add_argument("--launch", action="append", metavar="NAME[:JSON]")
+    ap.add_argument("--atom-sweep", action="store_true",
+                    help="head splits for head dims of 32-512 bytes: tiles of atoms against the source order")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
                     help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
@@ -469,6 +512,9 @@ def main():
         return
     if args.launch:
         launch_run(lr, torch, W, args.launch, back_to_back=args.back_to_back)
+        return
+    if args.atom_sweep:
+        atom_sweep(lr, torch)
         return
 
     flags = 0

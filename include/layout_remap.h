@@ -375,7 +375,8 @@ typedef struct {
   int32_t vector_order;    /* vector: modes after the common contiguous one walked in 0
                               destination order, 1 source order, 2 source order in blocks
                               of destination runs, 3 tiles of atoms through LDS where the
-                              common mode is an atom of 64-512 bytes that different modes
+                              common mode is an atom of 32-256 bytes, or of up to 512 bytes
+                              that are not whole 128-byte lines, that different modes
                               continue in the source and the destination (else 1; see
                               lr_plan.vector_order) */
   int32_t interleave_form; /* interleave: 0 one chunk per lane per head, 1 one destination

@@ -565,12 +565,13 @@ __device__ __forceinline__ void batch_offsets(const BatchArg& b, uint32_t r, uin
 // (a, b) plane into T x T tiles of atoms, each tile moved as one unit).  A
 // 256-lane workgroup loads its tile as T source runs of T atoms (a wave instruction
 // reads consecutive chunks of one run), regroups it in LDS and stores it as T
-// destination runs of T atoms.  LDS slot of chunk q of atom (a = i, b = j) in the
-// tile: (j * T + (i ^ (j % T))) * K + q.  The stores' 16 lanes of a 16-byte read
-// phase cover 256 bytes of atoms j, j + 1, ... of one i, and the XOR puts those
-// atoms in distinct 256/K-chunk slots modulo 256 bytes; the loads' 8 lanes of a
-// write phase stay inside aligned groups of atoms, i.e. 128 contiguous bytes.  All
-// offsets are in 16-byte chunks, swizzles included.
+// destination runs of T atoms (T = atom_tile(K); a tile that is not a whole number
+// of 256-lane rounds leaves the last round partial).  LDS slot of chunk q of atom
+// (a = i, b = j) in the tile: (j * T + (i ^ (j % T))) * K + q.  For power-of-two K
+// the stores' 16 lanes of a 16-byte read phase cover 256 bytes of atoms j, j + 1, ...
+// of one i, and the XOR puts those atoms in distinct 256/K-chunk slots modulo 256
+// bytes; the loads' 8 lanes of a write phase stay inside aligned groups of atoms,
+// i.e. 128 contiguous bytes.  All offsets are in 16-byte chunks, swizzles included.
 struct AtomArgs {
   const void* src;
   void* dst;
@@ -588,8 +589,8 @@ template <int K, bool LNT, bool SNT>
 __global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
   constexpr int T = (int)atom_tile(K);
   constexpr int RUN = T * K;         // chunks in one run of T atoms
-  constexpr int CH = T * RUN, PER = CH / 256;
-  static_assert(PER >= 1 && CH % 256 == 0, "whole rounds of 256 lanes");
+  constexpr int CH = T * RUN, PER = (CH + 255) / 256;
+  constexpr bool WHOLE = CH % 256 == 0;  // else the last round of lanes is partial
   __shared__ U4 tile[CH];
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
@@ -604,13 +605,14 @@ __global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
     const int L = k * 256 + tid;                 // source order: run j, atom i, chunk q
     const int j = L / RUN, i = (L % RUN) / K, q = L % K;
     const uint32_t a = ta * T + i, b = tb * T + j;
-    if (a < t.ext_a && b < t.ext_b) v[k] = gload<LNT, U4>(src + (size_t)swz32(a * K + q + b * t.ss_b + bs, t.sws) * 16);
+    if ((WHOLE || L < CH) && a < t.ext_a && b < t.ext_b)
+      v[k] = gload<LNT, U4>(src + (size_t)swz32(a * K + q + b * t.ss_b + bs, t.sws) * 16);
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int L = k * 256 + tid;
     const int j = L / RUN, i = (L % RUN) / K, q = L % K;
-    if (ta * T + i < t.ext_a && tb * T + j < t.ext_b) tile[(j * T + (i ^ (j % T))) * K + q] = v[k];
+    if ((WHOLE || L < CH) && ta * T + i < t.ext_a && tb * T + j < t.ext_b) tile[(j * T + (i ^ (j % T))) * K + q] = v[k];
   }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, -1, kBufferWord3);
@@ -619,7 +621,7 @@ __global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
     const int S = k * 256 + tid;                 // destination order: run i, atom j, chunk q
     const int i = S / RUN, j = (S % RUN) / K, q = S % K;
     const uint32_t a = ta * T + i, b = tb * T + j;
-    if (a < t.ext_a && b < t.ext_b) {
+    if ((WHOLE || S < CH) && a < t.ext_a && b < t.ext_b) {
       const U4 x = tile[(j * T + (i ^ (j % T))) * K + q];
       const uint32_t dof = swz32(b * K + q + a * t.sd_a + bd, t.swd);
       if (SNT && t.bufst)
@@ -1802,14 +1804,17 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int ski
   }
 }
 
-template <bool LNT, bool SNT>
+// One kernel per atom size K = KK..32 chunks.
+template <int KK, bool LNT, bool SNT>
 static bool launch_atoms_nt(const AtomArgs& a, int K, unsigned grid, hipStream_t st) {
-  switch (K) {
-    case 4: hipLaunchKernelGGL((k_atoms<4, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
-    case 8: hipLaunchKernelGGL((k_atoms<8, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
-    case 16: hipLaunchKernelGGL((k_atoms<16, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
-    case 32: hipLaunchKernelGGL((k_atoms<32, LNT, SNT>), dim3(grid), dim3(256), 0, st, a); return true;
-    default: return false;
+  if constexpr (KK > 32) {
+    return false;
+  } else {
+    if (K == KK) {
+      hipLaunchKernelGGL((k_atoms<KK, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
+      return true;
+    }
+    return launch_atoms_nt<KK + 1, LNT, SNT>(a, K, grid, st);
   }
 }
 
@@ -1843,10 +1848,10 @@ static bool launch_atoms(const Plan& p, const GenericArgs& g, unsigned grid, hip
   a.sws = g.sws;
   a.swd = g.swd;
   a.bufst = g.bufst;
-  if (p.nt_ld && p.nt) return launch_atoms_nt<true, true>(a, K, grid, st);
-  if (p.nt_ld) return launch_atoms_nt<true, false>(a, K, grid, st);
-  if (p.nt) return launch_atoms_nt<false, true>(a, K, grid, st);
-  return launch_atoms_nt<false, false>(a, K, grid, st);
+  if (p.nt_ld && p.nt) return launch_atoms_nt<2, true, true>(a, K, grid, st);
+  if (p.nt_ld) return launch_atoms_nt<2, true, false>(a, K, grid, st);
+  if (p.nt) return launch_atoms_nt<2, false, true>(a, K, grid, st);
+  return launch_atoms_nt<2, false, false>(a, K, grid, st);
 }
 
 template <int UB, bool LNT, bool SNT>

@@ -68,9 +68,10 @@ constexpr bool pipe_fits(int shape, int V) {
   return shape >= 0 && shape <= 2 && 2 * kTileTA[shape] * V * kTileTB[shape] * 16 <= 160 * 1024;
 }
 
-// Vector path, tiles of atoms (vector order 3): atoms of K 16-byte chunks per tile
-// side (1 KiB runs, at least 4 atoms).
-constexpr int64_t atom_tile(int64_t K) { return K >= 16 ? 4 : 64 / K; }
+// Vector path, tiles of atoms (vector order 3): atoms of K = 2..32 16-byte chunks
+// per tile side -- 16 up to 64-byte atoms, 8 up to 240 bytes, 4 from 256 bytes (runs
+// of 512 bytes to 2 KiB).
+constexpr int64_t atom_tile(int64_t K) { return K <= 4 ? 16 : (K < 16 ? 8 : 4); }
 
 // Everything the launch code needs.
 struct Plan {

@@ -1365,19 +1365,26 @@ def test_channel_shuffle_any_pixel_count(dev, knobs, eb):
 
 def _atom_cases():
     """(src, dst, src elems, dst elems, eb): the atom (mode 0) of w elements continued by a
-    in the source and by b in the destination -- every atom size from 4 to 32 chunks
-    (64-512 bytes), extents that leave ragged tiles, batch modes with padding, swizzles
-    on either side, and the 512^2 retile."""
+    in the source and by b in the destination -- atoms of 2 to 20 chunks (32-320 bytes,
+    powers of two and not), extents that leave ragged tiles and partial rounds of
+    lanes, batch modes with padding, swizzles on either side, and the 512^2 retile."""
     rt = W.small("retile")
     cases = [
         ("(64,13,21,3):(1,64,832,20000)", "(64,13,21,3):(1,1344,64,17600)", 2),   # K 8, ragged, batch
         ("(64,40,70):(1,64,2560)", "(64,40,70):(1,4480,64)", 1),                    # K 4, T 16
         ("(16,33,17):(1,16,528)", "(16,33,17):(1,272,16)", 4),                      # K 4, T 16
         ("(32,9,6,2):(1,32,300,2000)", "(32,9,6,2):(1,192,32,1728)", 8),            # K 16, T 4
-        ("(32,5,7):(1,32,160)", "(32,5,7):(1,224,32)", 16),                         # K 32, T 4
+        ("(20,5,7):(1,20,100)", "(20,5,7):(1,140,20)", 16),                         # K 20, T 4, partial round
         ("(64,16,24):(1,64,1024)", "Sw<2,3,4> o (64,16,24):(1,1536,64)", 2),        # dst swizzle
         ("Sw<1,4,3> o (64,16,24):(1,64,1024)", "(64,16,24):(1,1536,64)", 2),        # src swizzle
         ("(8,17,40,8):(1,8,136,5600)", "(8,17,40,8):(1,320,8,5500)", 8),            # K 4, batch
+        ("(16,33,35):(1,16,528)", "(16,33,35):(1,560,16)", 2),                      # K 2 (32-byte atoms)
+        ("(24,37,19):(1,24,888)", "(24,37,19):(1,456,24)", 2),                      # K 3 (48 bytes)
+        ("(40,13,21,2):(1,40,520,11000)", "(40,13,21,2):(1,840,40,11000)", 2),      # K 5, T 8, batch
+        ("(24,19,23):(1,24,456)", "(24,19,23):(1,552,24)", 4),                      # K 6
+        ("(56,9,11,3):(1,56,504,5600)", "(56,9,11,3):(1,616,56,5600)", 2),          # K 7, ragged
+        ("(20,11,9):(1,20,220)", "(20,11,9):(1,180,20)", 8),                        # K 10
+        ("(96,10,9):(1,96,960)", "Sw<1,3,4> o (96,10,9):(1,864,96)", 2),            # K 12, dst swizzle
         (rt.src_layout, rt.dst_layout, 2),
     ]
     out = []

@@ -760,11 +760,17 @@ def test_atom_tiles_plan():
     assert p["grid"] == (64 // 8) * (128 // 8) * 32
     q = lr.copy_plan(*args, tuning={"vector_order": 1})
     assert q["vector_order"] == 1 and q["grid"] == 4096 * 4096 // 8 // 256
-    # atom sizes: 64 bytes -> 16 atoms a side, 256 and 512 -> 4
-    for eb, w_, T in ((1, 64, 16), (2, 64, 8), (8, 32, 4), (16, 32, 4)):
+    # atom sizes: up to 64 bytes -> 16 atoms a side, up to 240 -> 8, from 256 -> 4; from
+    # 256 bytes only atoms that are not whole 128-byte lines (order 1 otherwise); 32- and
+    # 48-byte atoms reach the vector path as tiles of atoms only
+    for eb, w_, T in ((2, 16, 16), (2, 24, 16), (1, 64, 16), (2, 40, 8), (2, 64, 8), (2, 112, 8), (8, 32, 4),
+                      (2, 160, 4), (2, 192, 0), (16, 32, 0)):
         ts, td = f"({w_},40,50):(1,{w_},{40 * w_})", f"({w_},40,50):(1,{50 * w_},{w_})"
         r = lr.copy_plan(ts, 2000 * w_, td, 2000 * w_, eb)
-        assert r["vector_order"] == 3 and r["tile_a"] == T, (eb, w_, r)
+        if T:
+            assert r["path"] in ("vector", "generic") and r["vector_order"] == 3 and r["tile_a"] == T, (eb, w_, r)
+        else:
+            assert r["vector_order"] == 1, (eb, w_, r)
     # one side shorter than a tile, or a 16-byte atom: not tiles of atoms
     short = lr.copy_plan("(64,7,50):(1,64,448)", 64 * 350, "(64,7,50):(1,3200,64)", 64 * 350, 2,
                          tuning={"vector_order": 3})

@@ -31,6 +31,7 @@ Other modes (for rocprofv3 runs and their summaries under profiles/):
                         the benchmark's timed region
   --atom-sweep          head splits for head dims of 32-512 bytes: tiles of
                         atoms against the source order, beside a plain copy
+  --layout-sweep        common layout transforms against a same-size copy
 """
 
 from __future__ import annotations
@@ -357,6 +358,51 @@ def atom_sweep(lr, torch, steps: int = 20):
         torch.cuda.empty_cache()
 
 
+# Common layout transforms beyond the workloads above: (name, source, destination,
+# element bytes).
+LAYOUT_SWEEP = (
+    ("fp8 transpose 16384^2", "(16384,16384):(16384,1)", "(16384,16384):(1,16384)", 1),
+    ("fp32 transpose 8192^2", "(8192,8192):(8192,1)", "(8192,8192):(1,8192)", 4),
+    ("fp64 transpose 4096x8192", "(4096,8192):(8192,1)", "(4096,8192):(1,4096)", 8),
+    ("odd-pitch fp16 transpose 8191^2", "(8191,8191):(8191,1)", "(8191,8191):(1,8191)", 2),
+    ("batched fp16 64x64 transposes x 16384", "(64,64,16384):(64,1,4096)", "(64,64,16384):(1,64,4096)", 2),
+    ("batched fp16 32x32 transposes x 65536", "(32,32,65536):(32,1,1024)", "(32,32,65536):(1,32,1024)", 2),
+    ("batched fp16 16x16 transposes x 262144", "(16,16,262144):(16,1,256)", "(16,16,262144):(1,16,256)", 2),
+    ("batched fp32 128x96 transposes x 4096", "(128,96,4096):(96,1,12288)", "(128,96,4096):(1,128,12288)", 4),
+    ("NCHW->NHWC fp16 (128,256,56,56)", "(128,3136,256):(802816,1,3136)", "(128,3136,256):(802816,256,1)", 2),
+    ("NCHW->NHWC fp16 (256,64,112,112)", "(256,12544,64):(802816,1,12544)", "(256,12544,64):(802816,64,1)", 2),
+    ("NCHW->NHWC fp16 (256,32,112,112)", "(256,12544,32):(401408,1,12544)", "(256,12544,32):(401408,32,1)", 2),
+    ("KV cache (b,s,h,d)->(b,h,d,s) bf16 (8,4096,32,128)", "(8,4096,32,128):(16777216,4096,128,1)",
+     "(8,4096,32,128):(16777216,1,524288,4096)", 2),
+    ("3-D reversal (a,b,c)->(c,b,a) fp32 512^3", "(512,512,512):(262144,512,1)", "(512,512,512):(1,512,262144)", 4),
+    ("3-D permute (a,b,c)->(b,a,c) fp16 (64,1024,2048)", "(2048,1024,64):(1,2048,2097152)",
+     "(2048,1024,64):(1,131072,2048)", 2),
+    ("padded rows 4096 of 4160 -> compact, fp16 x 8192", "(4096,8192):(1,4160)", "(4096,8192):(1,4096)", 2),
+    ("every second row -> compact, fp16 x 4096", "(4096,8192):(1,8192)", "(4096,8192):(1,4096)", 2),
+)
+
+
+def layout_sweep(lr, torch, steps: int = 20):
+    """Each LAYOUT_SWEEP transform by the planner's choice, back to back over rotating
+    buffers, beside a contiguous copy of the same bytes (of the same element size when
+    they are not whole 16-byte units).  One JSON line each."""
+    dev = torch.device("cuda:0")
+    for name, ts, td, eb in LAYOUT_SWEEP:
+        Ls = lr.parse(ts)
+        n, ns, nd = Ls.size, Ls.cosize, lr.parse(td).cosize
+        p = lr.copy_plan(ts, ns, td, nd, eb)
+        pairs = _pairs(torch, dev, ns * eb, nd * eb)
+        _, ms = _time_copies(lr, torch, pairs, ts, td, eb, steps, 3)
+        cu, ce = (n * eb // 16, 16) if (n * eb) % 16 == 0 else (n, eb)
+        _, cms = _time_copies(lr, torch, pairs, f"{cu}:1", f"{cu}:1", ce, steps, 3)
+        print(json.dumps({"case": name, "path": p["path"], "tile": [p["tile_a"], p["tile_b"]],
+                          "vector_order": p["vector_order"], "us": round(ms * 1e3, 2),
+                          "GBps": round(2 * n * eb / (ms * 1e-3) / 1e9), "copy_us": round(cms * 1e3, 2),
+                          "frac_of_copy": round(cms / ms, 3)}), flush=True)
+        del pairs
+        torch.cuda.empty_cache()
+
+
 def _csv_rows(directory: str, suffix: str):
     rows = []
     for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
@@ -482,6 +528,9 @@ def main():
     ap.add_argument("--launch", action="append", metavar="NAME[:JSON]")
     ap.add_argument("--atom-sweep", action="store_true",
                     help="head splits for head dims of 32-512 bytes: tiles of atoms against the source order")
+    ap.add_argument("--layout-sweep", action="store_true",
+                    help="common layout transforms (transposes of every element size, batched small "
+                         "matrices, NCHW <-> NHWC, 3-D permutes, row gathers) against a same-size copy")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
                     help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
@@ -515,6 +564,9 @@ def main():
         return
     if args.atom_sweep:
         atom_sweep(lr, torch)
+        return
+    if args.layout_sweep:
+        layout_sweep(lr, torch)
         return
 
     flags = 0

@@ -334,6 +334,76 @@ static bool atom_tiles(const Plan& p, int* a, int* b, int64_t* T) {
   return p.m[*a].ext >= *T && p.m[*b].ext >= *T;
 }
 
+// The staged path: a compact block of the inner destination modes whose source
+// footprint is small, staged in LDS and gathered into 16-byte stores.  b is the
+// destination-contiguous mode.  Fills *p and returns true when it applies.
+static bool plan_staged(Plan* p, int b, size_t src_align, size_t dst_align, int64_t src_cap,
+                        const lr_copy_tuning& tun) {
+  const int V16 = 16 / p->eb;
+  bool ok = b == 0 && p->sw_s.b == 0 && src_align >= 16 && dst_align >= 16;
+  int inner = 0;
+  int64_t P = 1, F = 1;
+  if (ok) {
+    // the longest compact dst prefix (at most 4 KiB) whose source footprint is small;
+    // a prefix can be compact where a shorter one is not (a whole small matrix)
+    int64_t want = 1, P2 = 1, F2 = 1;
+    for (int k = 0; k < p->rank - 1 && p->m[k].sd == want; ++k) {
+      P2 *= p->m[k].ext;
+      F2 += (p->m[k].ext - 1) * p->m[k].ss;
+      if (P2 * p->eb > 4096) break;
+      want = P2;
+      if (F2 <= 2 * P2 + 64) {
+        P = P2;
+        F = F2;
+        inner = k + 1;
+      }
+    }
+    ok = inner >= 1 && inner < p->rank && p->m[inner].sd == P && (P * p->eb) % 16 == 0 &&
+         is_pow2(P * p->eb / 16) && swz_keeps(p->sw_d, V16);
+    for (int k = inner; ok && k < p->rank; ++k) {
+      if ((p->m[k].ss * p->eb) % 16) ok = false;
+      if ((p->m[k].sd * p->eb) % 16) ok = false;
+    }
+    if (ok) {
+      const int64_t Fc = (F * p->eb + 15) / 16;
+      // the padded footprint of the last tile must stay inside the buffer
+      int64_t maxbase = 0;
+      for (int k = inner; k < p->rank; ++k) maxbase += (p->m[k].ext - 1) * p->m[k].ss;
+      ok = (maxbase + Fc * 16 / p->eb) <= src_cap;
+      if (ok) {
+        const int64_t cpt = P * p->eb / 16;  // 16-byte dst chunks per tile
+        // about two dst chunks per lane (padded tiles: 5.85 TB/s, against 5.79 with
+        // four and 5.57 with eight; one measured 4.8-5.1), and at most 40 KiB of LDS
+        // per workgroup.  Stores with the sc1 bit measured no faster here.
+        const int64_t K = std::max<int64_t>(1, std::min<int64_t>(512 / cpt, 2560 / Fc));
+        p->path = LR_PATH_STAGED;
+        // direct global -> LDS loads measured 2.6 % faster on the padded tiles
+        // (5.79 vs 5.64 TB/s): the footprint never passes through registers, so
+        // every load of it is in flight at once.
+        p->direct = knob(tun.direct_loads, 1) != 0;
+        p->staged_inner = inner;
+        p->staged_P = P;
+        p->staged_F = F;
+        p->staged_Fc = Fc;
+        p->staged_cpt = cpt;
+        p->staged_K = K;
+        p->staged_cps = staged_gather_cps(*p, inner, cpt, K, Fc);
+        if (tun.gather_chunks > 0 && tun.gather_chunks <= cpt && cpt % tun.gather_chunks == 0 &&
+            8 % (cpt / tun.gather_chunks) == 0 &&
+            (tun.gather_chunks == std::min<int64_t>(cpt, 32) || K % (32 / tun.gather_chunks) == 0))
+          p->staged_cps = tun.gather_chunks;
+        p->v = V16;
+        p->tile_a = K;
+        int64_t batch = 1;
+        for (int k = inner + 1; k < p->rank; ++k) batch *= p->m[k].ext;
+        p->grid = ((p->m[inner].ext + K - 1) / K) * batch;
+        return true;
+      }
+    }
+  }
+  return false;
+}
+
 static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
                      size_t dst_align, size_t elem_bytes, uint32_t flags, const lr_copy_tuning& tun, Plan* p) {
   int rc;
@@ -590,6 +660,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
   // interleaved inside column-major tiles).
   const bool want_t = forced < 0 || forced == LR_PATH_TRANSPOSE || forced == LR_PATH_TRANSPOSE_DIRECT;
   if (a >= 0 && b >= 0 && a != b && want_t) {
+    const Plan before_transpose = *p;
     int b2 = -1;
     if (is_pow2(p->m[b].ext) && p->m[b].ext * p->eb < 16)
       for (int k = 0; k < p->rank && b2 < 0; ++k)
@@ -645,6 +716,17 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->tshape = ext_a > 16 * V ? 3 : 2;
       else
         p->tshape = (V == 2 && ext_a > 16 * V) ? 1 : 0;
+      // A short destination-contiguous extent: no tile taller along b than it needs,
+      // else most of a tile's lanes idle.  Measured on NCHW -> NHWC fp16 (256 images of
+      // 112 x 112): 32 channels 145.0 -> 69.3 us with 32 x 8 chunks instead of 32 x 32,
+      // 64 channels 189.1 -> 137.2 us.
+      if (wide_ok && !block_rows) {
+        const int64_t nbc = (ext_b + V - 1) / V;  // b extent in chunks
+        if (nbc <= 8 && kTileTB[p->tshape] > 8)
+          p->tshape = 4;
+        else if (nbc <= 16 && kTileTB[p->tshape] > 16)
+          p->tshape = ext_a > 16 * V ? 1 : 0;
+      }
       // Fewer tiles than compute units (a 16 MiB transpose in 256 x 256 tiles is 128
       // workgroups): 32 x 8 chunks, four times as many workgroups.  Measured on
       // fp16 1024 x 8192 and 8192 x 1024, the 8-way shard pack of 1024 x 8192 and u8
@@ -784,6 +866,18 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->tr = true;
         p->bufst = false;
       }
+      // Small matrices in a batch (a whole matrix under a quarter of the smallest
+      // tile): the staged path where it applies, which moves each compact matrix as
+      // one block.  Measured on batched fp16 transposes: 32 x 32 115.6 -> 49.6 us,
+      // 16 x 16 406.6 -> 68.6 us (fp32 32 x 32, a quarter of its tile, ties: 46.1 us).
+      if (forced < 0 && tun.tile_shape < 0 && !p->tel) {
+        const int64_t fa = std::min<int64_t>(p->m[a].ext, p->tile_a), fb = std::min<int64_t>(ext_b, p->tile_b);
+        Plan st = before_transpose;
+        if (4 * fa * fb < p->tile_a * p->tile_b && plan_staged(&st, b, src_align, dst_align, src_cap, tun)) {
+          *p = st;
+          return LR_OK;
+        }
+      }
       return LR_OK;
     }
   }
@@ -791,64 +885,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
 
   // staged: a compact dst block of inner modes whose source footprint is small
   if (forced < 0 || forced == LR_PATH_STAGED) {
-    bool ok = b == 0 && p->sw_s.b == 0 && src_align >= 16 && dst_align >= 16;
-    int inner = 0;
-    int64_t P = 1, F = 1;
-    if (ok) {
-      // grow the compact dst prefix while the source footprint stays small
-      int64_t want = 1;
-      while (inner < p->rank - 1 && p->m[inner].sd == want) {
-        int64_t P2 = P * p->m[inner].ext;
-        int64_t F2 = F + (p->m[inner].ext - 1) * p->m[inner].ss;
-        if (P2 * p->eb > 4096 || F2 > 2 * P2 + 64) break;
-        P = P2;
-        F = F2;
-        want = P;
-        ++inner;
-      }
-      ok = inner >= 1 && inner < p->rank && p->m[inner].sd == P && (P * p->eb) % 16 == 0 &&
-           is_pow2(P * p->eb / 16) && swz_keeps(p->sw_d, V16);
-      for (int k = inner; ok && k < p->rank; ++k) {
-        if ((p->m[k].ss * p->eb) % 16) ok = false;
-        if ((p->m[k].sd * p->eb) % 16) ok = false;
-      }
-      if (ok) {
-        const int64_t Fc = (F * p->eb + 15) / 16;
-        // the padded footprint of the last tile must stay inside the buffer
-        int64_t maxbase = 0;
-        for (int k = inner; k < p->rank; ++k) maxbase += (p->m[k].ext - 1) * p->m[k].ss;
-        ok = (maxbase + Fc * 16 / p->eb) <= src_cap;
-        if (ok) {
-          const int64_t cpt = P * p->eb / 16;  // 16-byte dst chunks per tile
-          // about two dst chunks per lane (padded tiles: 5.85 TB/s, against 5.79 with
-          // four and 5.57 with eight; one measured 4.8-5.1), and at most 40 KiB of LDS
-          // per workgroup.  Stores with the sc1 bit measured no faster here.
-          const int64_t K = std::max<int64_t>(1, std::min<int64_t>(512 / cpt, 2560 / Fc));
-          p->path = LR_PATH_STAGED;
-          // direct global -> LDS loads measured 2.6 % faster on the padded tiles
-          // (5.79 vs 5.64 TB/s): the footprint never passes through registers, so
-          // every load of it is in flight at once.
-          p->direct = knob(tun.direct_loads, 1) != 0;
-          p->staged_inner = inner;
-          p->staged_P = P;
-          p->staged_F = F;
-          p->staged_Fc = Fc;
-          p->staged_cpt = cpt;
-          p->staged_K = K;
-          p->staged_cps = staged_gather_cps(*p, inner, cpt, K, Fc);
-          if (tun.gather_chunks > 0 && tun.gather_chunks <= cpt && cpt % tun.gather_chunks == 0 &&
-              8 % (cpt / tun.gather_chunks) == 0 &&
-              (tun.gather_chunks == std::min<int64_t>(cpt, 32) || K % (32 / tun.gather_chunks) == 0))
-            p->staged_cps = tun.gather_chunks;
-          p->v = V16;
-          p->tile_a = K;
-          int64_t batch = 1;
-          for (int k = inner + 1; k < p->rank; ++k) batch *= p->m[k].ext;
-          p->grid = ((p->m[inner].ext + K - 1) / K) * batch;
-          return LR_OK;
-        }
-      }
-    }
+    if (plan_staged(p, b, src_align, dst_align, src_cap, tun)) return LR_OK;
     if (forced == LR_PATH_STAGED) return LR_ERR_PATH;
   }
 

@@ -983,6 +983,41 @@ def test_odd_pitch_transposes_full_size(dev):
         del s, d
 
 
+def test_small_batched_and_narrow_transposes(dev, knobs):
+    """Transposes whose extents leave a tile mostly idle: batches of small matrices
+    (each under a quarter of the smallest tile) take the staged path, one compact
+    matrix a block; a short destination-contiguous extent (NCHW -> NHWC with few
+    channels) takes tiles no taller than it.  Ragged batches, both policies, and
+    every destination element stored once."""
+    cases = [("(32,32,300):(32,1,1024)", "(32,32,300):(1,32,1024)", 2, "staged"),
+             ("(16,16,1001):(16,1,256)", "(16,16,1001):(1,16,256)", 2, "staged"),
+             ("(16,32,257):(32,1,512)", "(16,32,257):(1,16,512)", 2, "staged"),
+             ("(32,32,100):(32,1,1024)", "(32,32,100):(1,32,1024)", 4, "transpose"),
+             ("(3,1000,32):(32000,1,1000)", "(3,1000,32):(32000,32,1)", 2, "transpose"),
+             ("(2,1000,64):(64000,1,1000)", "(2,1000,64):(64000,64,1)", 2, "transpose"),
+             ("(2,1000,128):(128000,1,1000)", "(2,1000,128):(128000,128,1)", 2, "transpose"),
+             ("(3,221,32):(7072,1,221)", "(3,221,32):(7072,32,1)", 2, "transpose")]
+    ran = 0
+    for ci, (ts, td, eb, path) in enumerate(cases):
+        n = O.size(O.parse(ts))
+        ns, nd = max(n, O.cosize(O.parse(ts))), max(n, O.cosize(O.parse(td)))
+        src = np.random.default_rng(500 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        mult = _multiplicity(O.parse(td), n, nd)
+        for nt in ("0", "1"):
+            knobs.t.clear()
+            knobs.policy(nt)
+            p = plan(ts, ns, td, nd, eb)
+            assert p["path"] == path, (ts, p)
+            say("small/narrow transpose", ts, "eb", eb, "nt", nt, p["path"], p["tile_a"], p["tile_b"])
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, nt)
+            got, counts = _write_counts(dev, src, ts, dst, td, eb)
+            assert np.array_equal(counts, (mult > 0).astype(np.int32)), ts
+            ran += 1
+    assert ran == 2 * len(cases)
+
+
 def test_transpose_xcd_grouped_orders(dev, knobs):
     """Tile orders 5..9: orders 0..4 over workgroup numbers renumbered by XCD (each XCD
     a contiguous run; grids that are and are not multiples of 8).  Chunk tiles of

@@ -384,8 +384,8 @@ LAYOUT_SWEEP = (
 
 def layout_sweep(lr, torch, steps: int = 20):
     """Each LAYOUT_SWEEP transform by the planner's choice, back to back over rotating
-    buffers, beside a contiguous copy of the same bytes (of the same element size when
-    they are not whole 16-byte units).  One JSON line each."""
+    buffers, beside a contiguous copy of the same bytes in 16-byte units (the last
+    partial unit left out).  One JSON line each."""
     dev = torch.device("cuda:0")
     for name, ts, td, eb in LAYOUT_SWEEP:
         Ls = lr.parse(ts)
@@ -393,8 +393,9 @@ def layout_sweep(lr, torch, steps: int = 20):
         p = lr.copy_plan(ts, ns, td, nd, eb)
         pairs = _pairs(torch, dev, ns * eb, nd * eb)
         _, ms = _time_copies(lr, torch, pairs, ts, td, eb, steps, 3)
-        cu, ce = (n * eb // 16, 16) if (n * eb) % 16 == 0 else (n, eb)
-        _, cms = _time_copies(lr, torch, pairs, f"{cu}:1", f"{cu}:1", ce, steps, 3)
+        cu = n * eb // 16
+        whole = [(s_[:cu * 16], d_[:cu * 16]) for s_, d_ in pairs]  # whole 16-byte units
+        _, cms = _time_copies(lr, torch, whole, f"{cu}:1", f"{cu}:1", 16, steps, 3)
         print(json.dumps({"case": name, "path": p["path"], "tile": [p["tile_a"], p["tile_b"]],
                           "vector_order": p["vector_order"], "us": round(ms * 1e3, 2),
                           "GBps": round(2 * n * eb / (ms * 1e-3) / 1e9), "copy_us": round(cms * 1e3, 2),

@@ -404,6 +404,41 @@ def layout_sweep(lr, torch, steps: int = 20):
         torch.cuda.empty_cache()
 
 
+# 1-byte transposes: matrix shapes (rows x columns, row-major source, column-major
+# destination) and the tunings compared on each
+BYTE_SHAPES = ((16384, 16384), (8192, 8192), (8192, 16384), (16384, 8192), (4096, 4096), (6144, 6144),
+               (12288, 12288), (2048, 32768), (32768, 2048))
+BYTE_TUNINGS = (None, {"chunk_bytes": 16, "tile_shape": 0}, {"chunk_bytes": 16, "tile_shape": 1},
+                {"chunk_bytes": 16, "tile_shape": 2}, {"chunk_bytes": 16, "tile_shape": 1, "direct_loads": 1},
+                {"transpose_reads": 1, "direct_loads": 1, "tile_shape": 0},
+                {"transpose_reads": 1, "direct_loads": 1, "tile_shape": 1},
+                {"transpose_reads": 1, "direct_loads": 1, "tile_shape": 2},
+                {"transpose_reads": 1, "pipeline_tiles": 2, "tile_shape": 0})
+
+
+def byte_transpose_sweep(lr, torch, shapes, steps: int = 20):
+    """1-byte (fp8 / u8) transposes: the planner's 8-byte chunks against 16-byte chunks
+    through registers, with direct loads, and read back with the gfx950 1-byte
+    transpose reads, back to back over rotating buffers, beside a contiguous copy of
+    the same bytes.  One JSON line per shape and tuning."""
+    dev = torch.device("cuda:0")
+    for R, C in shapes:
+        ts, td = f"({R},{C}):({C},1)", f"({R},{C}):(1,{R})"
+        n = R * C
+        pairs = _pairs(torch, dev, n, n)
+        _, cms = _time_copies(lr, torch, pairs, f"{n // 16}:1", f"{n // 16}:1", 16, steps, 3)
+        for t in BYTE_TUNINGS:
+            p = lr.copy_plan(ts, n, td, n, 1, tuning=t)
+            _, ms = _time_copies(lr, torch, pairs, ts, td, 1, steps, 3, tuning=t)
+            print(json.dumps({"shape": [R, C], "tuning": t, "chunk_bytes": p["vec_elems"], "direct": p["direct"],
+                              "transpose_reads": p["transpose_reads"], "pipeline_tiles": p["pipeline_tiles"],
+                              "order": p["order"], "tile": [p["tile_a"], p["tile_b"]], "us": round(ms * 1e3, 2),
+                              "GBps": round(2 * n / (ms * 1e-3) / 1e9), "copy_us": round(cms * 1e3, 2),
+                              "frac_of_copy": round(cms / ms, 3)}), flush=True)
+        del pairs
+        torch.cuda.empty_cache()
+
+
 def _csv_rows(directory: str, suffix: str):
     rows = []
     for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
@@ -532,6 +567,9 @@ def main():
     ap.add_argument("--layout-sweep", action="store_true",
                     help="common layout transforms (transposes of every element size, batched small "
                          "matrices, NCHW <-> NHWC, 3-D permutes, row gathers) against a same-size copy")
+    ap.add_argument("--byte-transpose-sweep", nargs="*", metavar="RxC",
+                    help="1-byte transposes (all listed shapes, or these): 8- against 16-byte chunks, "
+                         "direct loads and the 1-byte transpose reads")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
                     help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
@@ -568,6 +606,10 @@ def main():
         return
     if args.layout_sweep:
         layout_sweep(lr, torch)
+        return
+    if args.byte_transpose_sweep is not None:
+        shapes = [tuple(int(x) for x in s.split("x")) for s in args.byte_transpose_sweep] or BYTE_SHAPES
+        byte_transpose_sweep(lr, torch, shapes)
         return
 
     flags = 0

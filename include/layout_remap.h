@@ -391,11 +391,15 @@ typedef struct {
                               per workgroup; 2..64 that many tiles per workgroup, software-
                               pipelined through two LDS tiles with direct loads (the next tile's
                               loads in flight while the current one is stored) */
-  int32_t transpose_reads; /* LDS transpose with direct loads (or pipelined), 2-byte elements in
-                              16-byte chunks, tile shapes 0-3: 0 each lane reads V whole LDS rows
-                              and transposes them in registers; 1 the gfx950 transpose reads
-                              (ds_read_b64_tr_b16) hand each lane one column of four rows */
-  int32_t reserved[4];     /* must be -1 or 0 */
+  int32_t transpose_reads; /* LDS transpose with direct loads (or pipelined), 2- or 1-byte
+                              elements in 16-byte chunks, tile shapes 0-3: 0 each lane reads V
+                              whole LDS rows and transposes them in registers; 1 the gfx950
+                              transpose reads (ds_read_b64_tr_b16, ds_read_b64_tr_b8) hand each
+                              lane one column of four (eight) rows.  For 1-byte elements it
+                              implies 16-byte chunks unless chunk_bytes is 8 */
+  int32_t chunk_bytes;     /* transpose of 1-byte elements: 8 or 16 bytes per chunk (the most
+                              the layout's strides and alignment allow) */
+  int32_t reserved[3];     /* must be -1 or 0 */
 } lr_copy_tuning;
 
 /* Every field of *t to -1 (the planner's choices). */

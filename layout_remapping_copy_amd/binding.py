@@ -113,7 +113,8 @@ class lr_copy_tuning(ctypes.Structure):
         ("gather_chunks", ctypes.c_int32),
         ("pipeline_tiles", ctypes.c_int32),
         ("transpose_reads", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("chunk_bytes", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 

@@ -1098,11 +1098,17 @@ __device__ __forceinline__ void transpose_rows16(const U4* in, U4* out) {
 //    store instruction).  lds_swz(r) = (r % 4) + 4 * ((r / 8) % 4), so the 16 rows a
 //    group addresses fall on 16 distinct slots modulo 16 and, with the two groups of a
 //    32-lane phase on different halves, the phase's 32 8-byte reads on all 64 banks.
+//  - the same for 1-byte elements (TR true, V = 16) with ds_read_b64_tr_b8, which
+//    hands lane i of each group byte i % 8 of the 8 bytes that lane 2k + i / 8
+//    addresses, as its byte k (k = 0..7); see dl_consume.  lds_swz(r) = (r % 8) +
+//    8 * ((r / 16) % 2).
 // Needs full 16-byte chunks (V * EB == 16), TB >= 16 and TA in {16, 32}.
-template <int V, bool TR>
+template <int EB, int V, bool TR>
 __device__ __forceinline__ int lds_swz(int r) {
-  if constexpr (TR)
+  if constexpr (TR && EB == 2)
     return (r & 3) | (((r >> 3) & 3) << 2);
+  else if constexpr (TR)
+    return (r & 7) | (((r >> 4) & 1) << 3);
   else
     return (r / V) % 16;
 }
@@ -1113,6 +1119,16 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 // gfx950 transpose read of 2-byte elements (ds_read_b64_tr_b16), as two 32-bit words.
 __device__ __forceinline__ NativeOf<8>::T lds_read_tr16(const char* p) {
   return __builtin_bit_cast(NativeOf<8>::T, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<char*>(p)));
+}
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+
+// gfx950 transpose read of 1-byte elements (ds_read_b64_tr_b8): lane i of each
+// 16-lane group receives, as its byte k (k = 0..7), byte i % 8 of the 8 bytes that
+// lane 2k + i / 8 of the group addresses.
+__device__ __forceinline__ NativeOf<8>::T lds_read_tr8(const char* p) {
+  return __builtin_bit_cast(NativeOf<8>::T, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)const_cast<char*>(p)));
 }
 
 // Direct loads of tile blk into buf.  ALL: every lane issues its V loads, a chunk
@@ -1134,7 +1150,7 @@ __device__ __forceinline__ void dl_issue(const TransposeArgs& t, uint32_t blk, C
     const int base = 64 * (wave * V + k);  // first slot of this wave's load
     const int s = base + lane;
     const int r = s / TA, cs = s % TA;
-    const int c = cs ^ lds_swz<V, TR>(r);   // chunk column stored in slot s
+    const int c = cs ^ lds_swz<EB, V, TR>(r);   // chunk column stored in slot s
     const uint32_t a = a0 + V * c, b = b0 + r;
     const bool in = a < t.ext_a && b < t.ext_b;
     if (!ALL && !in) continue;
@@ -1161,7 +1177,7 @@ __device__ __forceinline__ void dl_consume(const TransposeArgs& t, uint32_t blk,
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int r = V * beta + j;
-      in[j] = rows[r * TA + (alpha ^ lds_swz<V, false>(r))];
+      in[j] = rows[r * TA + (alpha ^ lds_swz<EB, V, false>(r))];
     }
     transpose_rows16<EB>(in, out);
     const uint32_t b = b0 + V * beta;
@@ -1171,6 +1187,47 @@ __device__ __forceinline__ void dl_consume(const TransposeArgs& t, uint32_t blk,
       if (a < t.ext_a && b < t.ext_b) {
         const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
         gstore<NT, U4>(dst + (size_t)dof * EB, out[i]);
+        count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, 16);
+      }
+    }
+  } else if constexpr (EB == 1) {
+    // 1-byte elements in 16-byte chunks (V = 16).  A unit is one 8-byte half h of chunk
+    // column c by 8 b-chunks from 8 * bq: 8 destination rows of 128 bytes, one whole
+    // line each, over the wave's 64 lanes.  Lane j of group g addresses row j / 2 (and
+    // j / 2 + 8) of b-chunk 2g + j % 2 in half h, so lane i receives destination row
+    // 16c + 8h + i % 8, b-chunk 2g + i / 8: one whole 16-byte destination chunk from
+    // two reads.  A 32-lane phase reads 32 rows in one half, so its reads land two to
+    // a bank at best; the row swizzle (r % 8) + 8 * ((r / 16) % 2) makes it exactly two.
+    // (Units of both halves of a column over 16 rows, conflict-free, stored 64-byte
+    // row segments and ran 25 % slower.)
+    static_assert(V == 16, "transpose reads: 1-byte elements in 16-byte chunks");
+    constexpr int UB = TB / 8;              // units of 8 b-chunks along b
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int sk = i >> 1, sp = i & 1;      // addressed: row sk (and sk + 8) of b-chunk 2g + sp
+    const int e = i & 7, q = i >> 3;        // received: row 8h + e of the column, b-chunk 2g + q
+    const char* base = (const char*)buf;
+    // a wave's 16 units (the tile's TA * 2 * UB units over its TA * TB / 64 waves); all
+    // 32 reads go out before the first store
+    NativeOf<8>::T lo[16], hi[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int u = w * 16 + it;
+      const int bq = u % UB, h = (u / UB) & 1, c = u / (2 * UB);
+      const int r0 = 16 * (8 * bq + 2 * g + sp) + sk, r1 = r0 + 8;
+      lo[it] = lds_read_tr8(base + (r0 * TA + (c ^ lds_swz<EB, V, true>(r0))) * 16 + 8 * h);
+      hi[it] = lds_read_tr8(base + (r1 * TA + (c ^ lds_swz<EB, V, true>(r1))) * 16 + 8 * h);
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int u = w * 16 + it;
+      const int bq = u % UB, h = (u / UB) & 1, c = u / (2 * UB);
+      const uint32_t a = a0 + V * c + 8 * h + e;
+      const uint32_t b = b0 + V * (8 * bq + 2 * g + q);
+      if (a < t.ext_a && b < t.ext_b) {
+        const U4 o = {lo[it][0], lo[it][1], hi[it][0], hi[it][1]};
+        const uint32_t dof = swz32(a * t.sd_a + b + bd, t.swd);
+        gstore<NT, U4>(dst + (size_t)dof * EB, o);
         count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, 16);
       }
     }
@@ -1192,8 +1249,8 @@ __device__ __forceinline__ void dl_consume(const TransposeArgs& t, uint32_t blk,
       const int u = w * 8 + it;
       const int c = u / UB, ub = u % UB;
       const int r0 = 64 * ub + 8 * (4 * bh + sq) + sk, r1 = r0 + 4;
-      lo[it] = lds_read_tr16(base + (r0 * TA + (c ^ lds_swz<V, true>(r0))) * 16 + 8 * half);
-      hi[it] = lds_read_tr16(base + (r1 * TA + (c ^ lds_swz<V, true>(r1))) * 16 + 8 * half);
+      lo[it] = lds_read_tr16(base + (r0 * TA + (c ^ lds_swz<EB, V, true>(r0))) * 16 + 8 * half);
+      hi[it] = lds_read_tr16(base + (r1 * TA + (c ^ lds_swz<EB, V, true>(r1))) * 16 + 8 * half);
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
@@ -1937,7 +1994,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, int 
                                hipStream_t st) {
   if constexpr (V * EB == 16) {
     if (dl == 2 && lds) {
-      if constexpr (EB == 2) return launch_dl<EB, V, NT, true>(a, shape, grid, st);
+      if constexpr (EB <= 2) return launch_dl<EB, V, NT, true>(a, shape, grid, st);
       return false;
     }
     if (dl == 1 && lds) return launch_dl<EB, V, NT, false>(a, shape, grid, st);

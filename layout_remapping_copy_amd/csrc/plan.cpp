@@ -139,6 +139,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
     return false;
   if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;
   if (!in(t.transpose_reads, {0, 1})) return false;
+  if (!in(t.chunk_bytes, {8, 16})) return false;
   for (int32_t r : t.reserved)
     if (r != -1 && r != 0) return false;
   return true;
@@ -676,7 +677,10 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
     // 1-byte elements: 8-byte chunks (8 x 8 byte register blocks, 32 VGPRs of data
     // against 128 for 16 x 16), measured faster in wide tiles: u8 4096^2 3.49 -> 3.91
     // TB/s, 6144^2 3.65 -> 4.07, 8192 x 16384 5.23 -> 5.44, 8192^2 4.71 -> 4.78
-    int64_t V = p->eb == 1 ? 8 : V16;
+    // (16-byte chunks for 1-byte elements on request, and by default when their tile
+    // is read back with the transpose reads)
+    const bool chunk16 = tun.chunk_bytes == 16 || (tun.chunk_bytes < 0 && tun.transpose_reads == 1);
+    int64_t V = (p->eb == 1 && !chunk16) ? 8 : V16;
     while (V > 1) {
       bool ok = p->m[a].ext % V == 0 && ext_b % V == 0 && strides_ok(V) && swz_keeps(p->sw_s, V) &&
                 swz_keeps(p->sw_d, V) && src_align % (size_t)(V * p->eb) == 0 &&
@@ -859,9 +863,9 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->grid = (p->tiles_total + p->pipe - 1) / p->pipe;
         if (p->torder >= 5) p->torder -= 5;  // XCD grouping renumbers workgroups, not tiles
       }
-      // gfx950 transpose reads of the LDS tile: 2-byte elements in 16-byte chunks,
-      // tiles 16 or 32 chunks on each side, loaded directly (or pipelined)
-      if (tun.transpose_reads == 1 && p->path == LR_PATH_TRANSPOSE && !p->tel && p->eb == 2 && V == 8 &&
+      // gfx950 transpose reads of the LDS tile: 1- or 2-byte elements in 16-byte
+      // chunks, tiles 16 or 32 chunks on each side, loaded directly (or pipelined)
+      if (tun.transpose_reads == 1 && p->path == LR_PATH_TRANSPOSE && !p->tel && p->eb <= 2 && V * p->eb == 16 &&
           p->tshape <= 3 && (p->direct || p->pipe)) {
         p->tr = true;
         p->bufst = false;
@@ -1030,8 +1034,9 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       } else if (p.grid != p.tiles_total) {
         return bad();
       }
-      if (p.tr) {  // transpose reads: 8 x 8 blocks of 2-byte elements, direct loads, shapes 0-3
-        if (p.path != LR_PATH_TRANSPOSE || p.tel || p.eb != 2 || v != 8 || p.tshape > 3 || !p.direct || p.bufst)
+      if (p.tr) {  // transpose reads: 16-byte chunks of 1- or 2-byte elements, direct loads, shapes 0-3
+        if (p.path != LR_PATH_TRANSPOSE || p.tel || p.eb > 2 || v * p.eb != 16 || p.tshape > 3 || !p.direct ||
+            p.bufst)
           return bad();
       }
       for (int k = 0; k < p.rank; ++k) {
@@ -1187,6 +1192,7 @@ void lr_copy_tuning_init(lr_copy_tuning* t) {
   t->load_policy = t->store_policy = t->units_per_lane = t->vector_order = t->interleave_form = -1;
   t->tile_shape = t->tile_order = t->element_tiles = t->direct_loads = t->gather_chunks = t->pipeline_tiles = -1;
   t->transpose_reads = -1;
+  t->chunk_bytes = -1;
   for (int32_t& r : t->reserved) r = -1;
 }
 

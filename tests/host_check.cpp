@@ -126,6 +126,7 @@ static lr_copy_tuning rand_tuning(std::mt19937_64& rng) {
   t.gather_chunks = pick({-1, 1, 2, 4, 8, 16, 32});
   t.pipeline_tiles = pick({-1, 0, 2, 3, 5, 64});
   t.transpose_reads = pick({-1, 0, 1});
+  t.chunk_bytes = pick({-1, 8, 16});
   return t;
 }
 

@@ -445,7 +445,8 @@ def test_copy_random_pairs(dev, knobs):
                "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
                "vector_order": rng.choice([-1, 0, 1, 2, 3]), "units_per_lane": rng.choice([-1, 1, 4]),
                "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
-               "transpose_reads": rng.choice([-1, 0, 1])}
+               "transpose_reads": rng.choice([-1, 0, 1]),
+               "chunk_bytes": random.Random(i).choice([-1, -1, 8, 16])}
         knobs.t.clear()
         knobs.set(**env)
         if i % 50 == 0:
@@ -1139,6 +1140,8 @@ def _pipe_cases():
              ("(600,328):(328,1)", "Sw<2,3,5> o (600,328):(1,600)", 2),
              ("(48,80):(80,1)", "(48,80):(1,48)", 16),
              ("(512,272):(272,1)", "(512,272):(1,512)", 1),
+             ("(3,96,400):(38400,400,1)", "(3,96,400):(38400,1,96)", 1),
+             ("(640,320):(320,1)", "Sw<2,4,4> o (640,320):(1,640)", 1),
              (cm.src_layout, cm.dst_layout, 2)]
     out = []
     for ts, td, eb in cases:
@@ -1177,12 +1180,13 @@ def test_transpose_pipelined(dev, knobs, shape):
 
 @pytest.mark.parametrize("shape", [0, 1, 2, 3])
 def test_transpose_reads(dev, knobs, shape):
-    """The LDS tile read back with the gfx950 transpose reads (ds_read_b64_tr_b16), one
-    tile per workgroup and pipelined: 2-byte elements, ragged edges, batch modes, a
-    grouped b run, destination swizzles; both policies and every tile order."""
-    ran = 0
+    """The LDS tile read back with the gfx950 transpose reads (ds_read_b64_tr_b16 and
+    ds_read_b64_tr_b8), one tile per workgroup and pipelined: 2- and 1-byte elements,
+    ragged edges, batch modes, a grouped b run, destination swizzles; both policies and
+    every tile order."""
+    ran = {1: 0, 2: 0}
     for ci, (ts, td, ns, nd, eb) in enumerate(_pipe_cases()):
-        if eb != 2:
+        if eb > 2:
             continue
         src = np.random.default_rng(70 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
         dst = np.full(nd * eb, 0xA5, np.uint8)
@@ -1199,10 +1203,38 @@ def test_transpose_reads(dev, knobs, shape):
                     p = plan(ts, ns, td, nd, eb)
                     if p["path"] != "transpose" or not p["transpose_reads"]:
                         continue
-                    say("transpose reads", shape, pipe, ts, "nt", nt, "order", orient, "grid", p["grid"])
+                    say("transpose reads", shape, pipe, ts, "eb", eb, "nt", nt, "order", orient, "grid", p["grid"])
                     assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, pipe, nt, orient)
+                    ran[eb] += 1
+    assert ran[2] >= (40 if shape < 3 else 20)
+    assert ran[1] >= (20 if shape == 0 else 10)  # 16 x 16-byte chunks: 32 x 32 does not fit, no pipelined 32 x 16
+
+
+def test_byte_transpose_chunks(dev, knobs):
+    """1-byte transposes in 8- and 16-byte chunks (chunk_bytes), through registers and
+    with direct loads, in every tile shape that fits: ragged edges, a batch mode and a
+    destination swizzle."""
+    ran = 0
+    cases = [c for c in _pipe_cases() if c[4] == 1] + [
+        ("(1000,528):(528,1)", "(1000,528):(1,1000)", 1000 * 528, 1000 * 528, 1)]
+    for ci, (ts, td, ns, nd, eb) in enumerate(cases):
+        src = np.random.default_rng(130 + ci).integers(0, 256, ns, dtype=np.uint8)
+        dst = np.full(nd, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), 1)
+        for cb in (8, 16):
+            for shape in range(7):
+                for direct in (0, 1):
+                    knobs.t.clear()
+                    knobs.set(chunk_bytes=cb, tile_shape=shape, direct_loads=direct)
+                    p = plan(ts, ns, td, nd, 1)
+                    if p["path"] != "transpose":
+                        continue
+                    assert p["vec_elems"] == cb or cb == 16 and p["vec_elems"] < 16
+                    say("byte transpose chunks", ts, "chunk", cb, "shape", shape, "direct", direct, "tile",
+                        p["tile_a"], p["tile_b"])
+                    assert np.array_equal(gpu_copy(dev, src, ts, dst, td, 1), want), (ts, cb, shape, direct)
                     ran += 1
-    assert ran >= 40 if shape < 3 else ran >= 20
+    assert ran >= 50
 
 
 def test_transpose_pipelined_write_counts(dev, knobs):

@@ -711,7 +711,8 @@ def test_tuning_overrides_are_checked():
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
     for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 10},
                 {"units_per_lane": 2}, {"vector_order": 4}, {"gather_chunks": 3}, {"direct_loads": 2},
-                {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2}):
+                {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2},
+                {"chunk_bytes": 4}, {"chunk_bytes": 0}):
         with pytest.raises(lr.LayoutRemapError) as e:
             lr.copy_plan(*args, tuning=bad)
         assert e.value.code == lr.binding.ERR_INVALID, bad
@@ -780,8 +781,9 @@ def test_atom_tiles_plan():
 
 
 def test_transpose_reads_plan():
-    """transpose_reads: the direct-load (or pipelined) LDS transpose of 2-byte elements in
-    16-byte chunks, tile shapes 0-3; ignored without direct loads or for other element
+    """transpose_reads: the direct-load (or pipelined) LDS transpose of 2- or 1-byte
+    elements in 16-byte chunks, tile shapes 0-3 (0-2 for 1-byte elements, whose 32 x 32
+    chunk tile does not fit in LDS); ignored without direct loads or for other element
     sizes."""
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
@@ -789,13 +791,29 @@ def test_transpose_reads_plan():
     assert not lr.copy_plan(*args, tuning={"transpose_reads": 1})["transpose_reads"]  # no direct loads
     for shape in range(4):
         p = lr.copy_plan(*args, tuning={"transpose_reads": 1, "direct_loads": 1, "tile_shape": shape})
-        assert p["transpose_reads"] and p["direct"] and p["tile_a"] == p["tile_a"], shape
+        assert p["transpose_reads"] and p["direct"] and p["tile_a"] == (16, 32, 16, 32)[shape] * 8, shape
     p = lr.copy_plan(*args, tuning={"transpose_reads": 1, "pipeline_tiles": 4, "tile_shape": 1})
     assert p["transpose_reads"] and p["pipeline_tiles"] == 4
     # 32 x 8 chunks (shape 4): the reads need 16 or 32 chunks on both sides
     assert not lr.copy_plan(*args, tuning={"transpose_reads": 1, "direct_loads": 1, "tile_shape": 4})["transpose_reads"]
     f32 = ("(4096,4096):(4096,1)", 4096 * 4096, "(4096,4096):(1,4096)", 4096 * 4096, 4)
     assert not lr.copy_plan(*f32, tuning={"transpose_reads": 1, "direct_loads": 1})["transpose_reads"]
+    # 1-byte elements: 16-byte chunks (8-byte ones otherwise)
+    u8 = ("(4096,4096):(4096,1)", 4096 * 4096, "(4096,4096):(1,4096)", 4096 * 4096, 1)
+    assert lr.copy_plan(*u8)["vec_elems"] == 8 and not lr.copy_plan(*u8)["transpose_reads"]
+    for shape, ta, tb in ((0, 16, 16), (1, 32, 16), (2, 16, 32), (3, 32, 16)):
+        p = lr.copy_plan(*u8, tuning={"transpose_reads": 1, "direct_loads": 1, "tile_shape": shape})
+        assert p["transpose_reads"] and p["vec_elems"] == 16 and (p["tile_a"], p["tile_b"]) == (16 * ta, 16 * tb), shape
+    p = lr.copy_plan(*u8, tuning={"transpose_reads": 1, "pipeline_tiles": 3, "tile_shape": 0})
+    assert p["transpose_reads"] and p["pipeline_tiles"] == 3 and p["vec_elems"] == 16
+    # chunk_bytes: 16-byte chunks through registers; 8 turns the transpose reads off
+    p = lr.copy_plan(*u8, tuning={"chunk_bytes": 16})
+    assert p["vec_elems"] == 16 and not p["transpose_reads"] and not p["direct"]
+    p = lr.copy_plan(*u8, tuning={"chunk_bytes": 8, "transpose_reads": 1, "direct_loads": 1})
+    assert p["vec_elems"] == 8 and not p["transpose_reads"]
+    # a layout without 16-byte chunks keeps narrower ones
+    odd = ("(4096,4104):(4104,1)", 4096 * 4104, "(4096,4104):(1,4096)", 4096 * 4104, 1)
+    assert lr.copy_plan(*odd, tuning={"chunk_bytes": 16})["vec_elems"] == 8
 
 
 def _table_cycles(words):

@@ -439,6 +439,44 @@ def byte_transpose_sweep(lr, torch, shapes, steps: int = 20):
         torch.cuda.empty_cache()
 
 
+# Batched small-matrix transposes (matrix A x B, source rows of A, destination rows
+# of B, n matrices): element bytes, A, B, n -- 2^27 elements of 2 bytes, or 2^26 of 4
+# and 2^25 of 8 (128 MiB each way)
+BATCHED_SHAPES = ((2, 16, 16, 262144), (2, 32, 32, 65536), (2, 64, 64, 16384), (2, 24, 24, 116508),
+                  (2, 16, 32, 131072), (4, 8, 8, 524288), (4, 16, 16, 131072), (4, 32, 32, 32768),
+                  (4, 64, 32, 16384), (8, 16, 16, 65536), (8, 32, 32, 16384))
+
+
+def batched_sweep(lr, torch, steps: int = 20):
+    """Batched small-matrix transposes: the planner's path against the batched,
+    staged and transpose paths forced, back to back over rotating buffers, beside a
+    contiguous copy of the same bytes.  One JSON line per shape and variant."""
+    dev = torch.device("cuda:0")
+    for eb, A, B, n in BATCHED_SHAPES:
+        ts, td = f"({B},{A},{n}):({A},1,{A * B})", f"({B},{A},{n}):(1,{B},{A * B})"
+        Ls = lr.parse(ts)
+        ns, nd, N = Ls.cosize, lr.parse(td).cosize, Ls.size
+        pairs = _pairs(torch, dev, ns * eb, nd * eb)
+        cu = N * eb // 16
+        whole = [(s_[:cu * 16], d_[:cu * 16]) for s_, d_ in pairs]
+        _, cms = _time_copies(lr, torch, whole, f"{cu}:1", f"{cu}:1", 16, steps, 3)
+        for label, flags in (("planner", 0), ("batched", lr.COPY_FORCE_PATH(lr.PATH_BATCHED)),
+                             ("staged", lr.COPY_FORCE_PATH(lr.PATH_STAGED)),
+                             ("transpose", lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))):
+            try:
+                p = lr.copy_plan(ts, ns, td, nd, eb, flags)
+            except lr.LayoutRemapError:
+                print(json.dumps({"matrix": [A, B], "elem_bytes": eb, "count": n, "variant": label,
+                                  "path": None}), flush=True)
+                continue
+            _, ms = _time_copies(lr, torch, pairs, ts, td, eb, steps, 3, flags=flags)
+            print(json.dumps({"matrix": [A, B], "elem_bytes": eb, "count": n, "variant": label, "path": p["path"],
+                              "us": round(ms * 1e3, 2), "GBps": round(2 * N * eb / (ms * 1e-3) / 1e9),
+                              "copy_us": round(cms * 1e3, 2), "frac_of_copy": round(cms / ms, 3)}), flush=True)
+        del pairs, whole
+        torch.cuda.empty_cache()
+
+
 def _csv_rows(directory: str, suffix: str):
     rows = []
     for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
@@ -570,6 +608,9 @@ def main():
     ap.add_argument("--byte-transpose-sweep", nargs="*", metavar="RxC",
                     help="1-byte transposes (all listed shapes, or these): 8- against 16-byte chunks, "
                          "direct loads and the 1-byte transpose reads")
+    ap.add_argument("--batched-sweep", action="store_true",
+                    help="batched small-matrix transposes: the planner's path against the batched, staged and "
+                         "transpose paths")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
                     help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
@@ -606,6 +647,9 @@ def main():
         return
     if args.layout_sweep:
         layout_sweep(lr, torch)
+        return
+    if args.batched_sweep:
+        batched_sweep(lr, torch)
         return
     if args.byte_transpose_sweep is not None:
         shapes = [tuple(int(x) for x in s.split("x")) for s in args.byte_transpose_sweep] or BYTE_SHAPES

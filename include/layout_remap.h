@@ -290,8 +290,11 @@ typedef enum {
   LR_PATH_DUAL = 5,       /* no joint refinement: each side evaluated from the index */
   LR_PATH_ALIAS = 6,      /* non-injective dst, sequential last-writer semantics */
   LR_PATH_TRANSPOSE_DIRECT = 7, /* register-blocked transpose storing straight to global */
-  LR_PATH_DEINTERLEAVE = 8     /* short src-contiguous mode (2..8 channels, <= 16 bytes) spread
+  LR_PATH_DEINTERLEAVE = 8,    /* short src-contiguous mode (2..8 channels, <= 16 bytes) spread
                                   into planes: the mirror of the interleave */
+  LR_PATH_BATCHED = 9          /* a batch of small matrices, each compact on both sides (up to
+                                  8 KiB, sides multiples of a 16-byte chunk): whole matrices per
+                                  wavefront staged in LDS, transposed in registers */
 } lr_path;
 
 /* Copy flags. */
@@ -339,8 +342,14 @@ typedef struct {
   int32_t pipeline_tiles; /* transpose: tiles per workgroup of the pipelined kernel, 0 when it
                              is not used */
   int32_t transpose_reads; /* LDS transpose: 1 when the tile is read with the gfx950 transpose
-                              reads (ds_read_b64_tr_b16), 0 otherwise */
-  int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged) */
+                              reads (ds_read_b64_tr_b16, ds_read_b64_tr_b8), 0 otherwise */
+  int32_t batch_matrices;  /* batched: whole matrices per wavefront; -1 on other paths */
+  int32_t batch_swizzle[6]; /* batched: the LDS slot of 16-byte chunk c of a wavefront's region
+                               is c ^ (((c >> [0]) & [1]) << [2]) ^ (((c >> [3]) & [4]) << [5]) */
+  int32_t batch_order;     /* batched: blocks of a matrix over lanes, 0 a-blocks fastest, 1
+                              b-blocks fastest; -1 on other paths */
+  int64_t tile_a, tile_b; /* tile extents in the a/b modes (transpose), tiles per block (staged),
+                             the matrix (batched) */
   int64_t grid;        /* workgroups launched */
   int64_t n_elems;     /* logical elements of the original layouts */
   int64_t blocks;      /* launches: 1, or the number of blocks a copy too large for 32-bit offsets
@@ -399,7 +408,10 @@ typedef struct {
                               implies 16-byte chunks unless chunk_bytes is 8 */
   int32_t chunk_bytes;     /* transpose of 1-byte elements: 8 or 16 bytes per chunk (the most
                               the layout's strides and alignment allow) */
-  int32_t reserved[3];     /* must be -1 or 0 */
+  int32_t batch_swizzle;   /* batched: 0..15, the LDS swizzle of that index in the planner's
+                              candidate list (lr_plan.batch_swizzle shows it) */
+  int32_t batch_order;     /* batched: 0 a-blocks fastest over lanes, 1 b-blocks fastest */
+  int32_t reserved[1];     /* must be -1 or 0 */
 } lr_copy_tuning;
 
 /* Every field of *t to -1 (the planner's choices). */

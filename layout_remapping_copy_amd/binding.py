@@ -43,8 +43,9 @@ PATH_DUAL = 5
 PATH_ALIAS = 6
 PATH_TRANSPOSE_DIRECT = 7
 PATH_DEINTERLEAVE = 8
+PATH_BATCHED = 9
 PATH_NAMES = {0: "generic", 1: "vector", 2: "transpose", 3: "interleave", 4: "staged", 5: "dual",
-              6: "alias", 7: "transpose_direct", 8: "deinterleave"}
+              6: "alias", 7: "transpose_direct", 8: "deinterleave", 9: "batched"}
 
 # flags
 COPY_ORDERED_ALIAS = 0x1
@@ -88,6 +89,9 @@ class lr_plan(ctypes.Structure):
         ("gather_chunks", ctypes.c_int32),
         ("pipeline_tiles", ctypes.c_int32),
         ("transpose_reads", ctypes.c_int32),
+        ("batch_matrices", ctypes.c_int32),
+        ("batch_swizzle", ctypes.c_int32 * 6),
+        ("batch_order", ctypes.c_int32),
         ("tile_a", ctypes.c_int64),
         ("tile_b", ctypes.c_int64),
         ("grid", ctypes.c_int64),
@@ -114,7 +118,9 @@ class lr_copy_tuning(ctypes.Structure):
         ("pipeline_tiles", ctypes.c_int32),
         ("transpose_reads", ctypes.c_int32),
         ("chunk_bytes", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("batch_swizzle", ctypes.c_int32),
+        ("batch_order", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -488,6 +494,7 @@ def copy_plan(Ls, src_capacity: int, Ld, dst_capacity: int, elem_bytes: int, fla
         "load_policy": p.load_policy, "store_policy": p.store_policy,
         "vector_order": p.vector_order, "gather_chunks": p.gather_chunks, "pipeline_tiles": p.pipeline_tiles,
         "transpose_reads": bool(p.transpose_reads),
+        "batch_matrices": p.batch_matrices, "batch_swizzle": tuple(p.batch_swizzle), "batch_order": p.batch_order,
         "tile_a": p.tile_a, "tile_b": p.tile_b,
         "grid": p.grid, "n_elems": p.n_elems, "blocks": p.blocks,
         "joint": [(p.ext[i], p.s_src[i], p.s_dst[i]) for i in range(r)],

@@ -1816,6 +1816,125 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   }
 }
 
+// ------------------------------------------------------------------ batched small matrices
+
+struct BatchedArgs {
+  const void* src;
+  void* dst;
+  uint32_t P, Q;        // 16-byte chunks along a and V-row blocks along b: A = V * P, B = V * Q
+  uint32_t cpm;         // 16-byte chunks of one matrix (P * Q * V)
+  FD fd_cpm;
+  uint32_t pq;          // V x V blocks of one matrix (P * Q)
+  FD fd_pq;
+  uint32_t inner;       // the faster block index's extent: P (order 0, a-blocks fastest) or Q
+  FD fd_inner;
+  uint32_t order;
+  uint32_t mpw;         // whole matrices per wavefront (mpw * cpm <= 512)
+  uint32_t nblk;        // blocks per wavefront (mpw * pq)
+  uint32_t count;       // matrices
+  uint32_t sw[6];       // LDS slot of chunk c: c ^ (((c >> sw[0]) & sw[1]) << sw[2])
+                        //                        ^ (((c >> sw[3]) & sw[4]) << sw[5])
+  BatchArg batch;       // the matrix index over the other modes (element strides)
+  WriteCount wcnt;
+};
+
+// Batched small matrices ([CuTe algebra page, section 4.1]: a blocked product of one
+// small transpose over the batch modes).  Each matrix is compact on both sides: A
+// elements along a (source-contiguous) by B along b (destination-contiguous), rows of
+// A adjacent in the source and rows of B adjacent in the destination, A and B
+// multiples of V = 16 / EB.  A wavefront owns mpw whole matrices (up to 8 KiB) in an
+// LDS region of its own:
+//  1. direct global -> LDS loads, lane l of load k taking region slot 64k + l, which
+//     holds source chunk c = swz(slot) (the swizzle is an involution that permutes
+//     chunks inside aligned groups of 16, so each load instruction still reads 1 KiB
+//     of whole lines);
+//  2. each lane reads the V source rows of its V x V blocks (16-byte LDS reads) and
+//     transposes them in registers;
+//  3. it writes the V destination rows of each block back into the region, at the
+//     slots of their destination chunk indices;
+//  4. lane l of store k takes slot 64k + l, i.e. destination chunk swz(slot), and
+//     stores it: 1 KiB of whole lines per store instruction.
+// The planner picks the swizzle and the block order that its gfx950 bank model
+// finds cheapest for steps 2 and 3.  A workgroup is one wavefront (1-3 % faster than
+// four independent ones sharing barriers, over 2^27 elements of 2-, 4- and 8-byte
+// matrices from 8 x 8 to 64 x 64), with 8 KiB of LDS.
+template <int EB, bool NT>
+__global__ void __launch_bounds__(64) k_batched(BatchedArgs t) {
+  constexpr int V = 16 / EB;
+  constexpr int BPL = 8 / V;  // blocks per lane: 512 chunks of V-chunk blocks over 64 lanes
+  static_assert(V >= 2 && V <= 8, "2-, 4- and 8-byte elements");
+  __shared__ U4 reg[512];
+  const char* __restrict__ src = (const char*)t.src;
+  char* __restrict__ dst = (char*)t.dst;
+  const int lane = threadIdx.x;
+  const uint32_t m0 = blockIdx.x * t.mpw;
+  const uint32_t nch = t.mpw * t.cpm;
+  auto swz = [&](uint32_t c) {
+    return c ^ (((c >> t.sw[0]) & t.sw[1]) << t.sw[2]) ^ (((c >> t.sw[3]) & t.sw[4]) << t.sw[5]);
+  };
+  // matrix of region chunk c, and c's element offset inside its matrix
+  auto locate = [&](uint32_t c, uint32_t* m, uint32_t* off) {
+    const uint32_t mi = fdiv(c, t.fd_cpm);
+    *m = m0 + mi;
+    *off = (c - mi * t.cpm) * V;
+    return c < nch && *m < t.count;
+  };
+
+  // 1. loads
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t slot = 64u * k + lane;
+    uint32_t m, off;
+    if (!locate(swz(slot), &m, &off)) continue;
+    uint32_t bs, bd;
+    batch_offsets(t.batch, m, &bs, &bd);
+    load_to_lds16<NT>(src + (size_t)(bs + off) * EB, reg + 64 * k);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // 2. the blocks' source rows, transposed in registers
+  U4 in[BPL][V], out[BPL][V];
+  uint32_t mi_[BPL], ba_[BPL], bb_[BPL];
+#pragma unroll
+  for (int r = 0; r < BPL; ++r) {
+    const uint32_t u = 64u * r + lane;
+    const uint32_t mi = fdiv(u, t.fd_pq), rest = u - mi * t.pq;
+    const uint32_t hi = fdiv(rest, t.fd_inner), lo = rest - hi * t.inner;
+    mi_[r] = mi;
+    ba_[r] = t.order ? hi : lo;
+    bb_[r] = t.order ? lo : hi;
+    if (u < t.nblk) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) in[r][j] = reg[swz(mi * t.cpm + (V * bb_[r] + j) * t.P + ba_[r])];
+      transpose_rows16<EB>(in[r], out[r]);
+    }
+  }
+  __syncthreads();
+  // 3. destination rows back into the region
+#pragma unroll
+  for (int r = 0; r < BPL; ++r) {
+    if (64u * r + lane < t.nblk) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) reg[swz(mi_[r] * t.cpm + (V * ba_[r] + i) * t.Q + bb_[r])] = out[r][i];
+    }
+  }
+  __syncthreads();
+
+  // 4. stores
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t slot = 64u * k + lane;
+    uint32_t m, off;
+    if (!locate(swz(slot), &m, &off)) continue;
+    uint32_t bs, bd;
+    batch_offsets(t.batch, m, &bs, &bd);
+    char* p = dst + (size_t)(bd + off) * EB;
+    gstore<NT, U4>(p, reg[slot]);
+    count_store(t.wcnt, t.dst, p, 16);
+  }
+}
+
 // ------------------------------------------------------------------ launch helpers
 
 static int check_launch() {
@@ -1858,6 +1977,23 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int ski
     b->fd[r] = fd_of(p.m[k].ext);
     b->ss[r] = (uint32_t)p.m[k].ss;
     b->sd[r] = (uint32_t)p.m[k].sd;
+  }
+}
+
+template <int EB>
+static void launch_batched_eb(const BatchedArgs& a, bool nt, unsigned grid, hipStream_t st) {
+  if (nt)
+    hipLaunchKernelGGL((k_batched<EB, true>), dim3(grid), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_batched<EB, false>), dim3(grid), dim3(64), 0, st, a);
+}
+
+static bool launch_batched(const BatchedArgs& a, int eb, bool nt, unsigned grid, hipStream_t st) {
+  switch (eb) {
+    case 2: launch_batched_eb<2>(a, nt, grid, st); return true;
+    case 4: launch_batched_eb<4>(a, nt, grid, st); return true;
+    case 8: launch_batched_eb<8>(a, nt, grid, st); return true;
+    default: return false;
   }
 }
 
@@ -2285,6 +2421,30 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }
+    case LR_PATH_BATCHED: {
+      BatchedArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.wcnt = wc;
+      a.src = src;
+      a.dst = dst;
+      const uint32_t V = (uint32_t)p.v;
+      a.P = (uint32_t)(p.m[p.a].ext / V);
+      a.Q = (uint32_t)(p.m[p.b].ext / V);
+      a.cpm = a.P * a.Q * V;
+      a.fd_cpm = fd_of(a.cpm);
+      a.pq = a.P * a.Q;
+      a.fd_pq = fd_of(a.pq);
+      a.order = (uint32_t)p.bt_order;
+      a.inner = a.order ? a.Q : a.P;
+      a.fd_inner = fd_of(a.inner);
+      a.mpw = (uint32_t)p.bt_mpw;
+      a.nblk = a.mpw * a.pq;
+      a.count = (uint32_t)p.bt_count;
+      for (int i = 0; i < 6; ++i) a.sw[i] = (uint32_t)p.bt_sw[i];
+      fill_batch(&a.batch, p, p.a, p.b);
+      if (!launch_batched(a, p.eb, p.nt, grid, st)) return LR_ERR_PATH;
+      return check_launch();
+    }
     case LR_PATH_STAGED: {
       StagedArgs a;
       std::memset(&a, 0, sizeof(a));
@@ -2350,7 +2510,7 @@ static bool log_enabled() {
 
 static void log_plan(const Plan& p, int64_t blocks) {
   static const char* names[] = {"generic", "vector", "transpose", "interleave", "staged",
-                                "dual", "alias", "transpose_direct", "deinterleave"};
+                                "dual", "alias", "transpose_direct", "deinterleave", "batched"};
   char modes[1024];
   int at = 0;
   for (int k = 0; k < p.rank && at < (int)sizeof(modes) - 64; ++k)
@@ -2360,11 +2520,13 @@ static void log_plan(const Plan& p, int64_t blocks) {
   std::fprintf(stderr,
                "lr plan: path=%s elem_bytes=%d vec=%d wide=%d a=%d b=%d b2=%d tile=%lldx%lld shape=%d order=%d "
                "block=%d grid=%lld blocks=%lld nt_load=%d nt_store=%d sc1=%d direct=%d elem_tiles=%d "
-               "vorder=%d gather_chunks=%lld pipeline_tiles=%d transpose_reads=%d joint=[%s]\n",
-               p.path >= 0 && p.path <= 8 ? names[p.path] : "?", p.eb, p.v, p.wide ? 1 : 0, p.a, p.b, p.b2,
+               "vorder=%d gather_chunks=%lld pipeline_tiles=%d transpose_reads=%d batched=%lld/%d/%d,%d,%d,%d,%d,%d "
+               "joint=[%s]\n",
+               p.path >= 0 && p.path <= 9 ? names[p.path] : "?", p.eb, p.v, p.wide ? 1 : 0, p.a, p.b, p.b2,
                (long long)p.tile_a, (long long)p.tile_b, p.tshape, (int)p.torder, p.block, (long long)p.grid,
                (long long)blocks, p.nt_ld ? 1 : 0, p.nt ? 1 : 0, (p.nt && p.bufst) ? 1 : 0, p.direct ? 1 : 0,
-               p.tel ? 1 : 0, p.vorder, (long long)p.staged_cps, p.pipe, p.tr ? 1 : 0, modes);
+               p.tel ? 1 : 0, p.vorder, (long long)p.staged_cps, p.pipe, p.tr ? 1 : 0, (long long)p.bt_mpw,
+               p.bt_order, p.bt_sw[0], p.bt_sw[1], p.bt_sw[2], p.bt_sw[3], p.bt_sw[4], p.bt_sw[5], modes);
 }
 
 static int fill_eval(EvalArgs* a, const lr_layout* L) {

@@ -117,6 +117,12 @@ struct Plan {
   int pipe;           // pipelined transpose: tiles per workgroup (0: one tile, not pipelined)
   bool tr;            // LDS transpose: the tile is read with gfx950 transpose reads
   int64_t tiles_total; // transpose: tiles over all batch indices
+  // batched small matrices: whole matrices per wavefront, matrices, the LDS chunk
+  // swizzle (two XOR terms of shift, mask, target shift) and the block order (0:
+  // a-blocks fastest)
+  int64_t bt_mpw, bt_count;
+  int bt_sw[6];
+  int bt_order;
   int inarrow;        // interleave: 1 = one 16-byte store per lane from NB narrow loads,
                       // 0 = NB wide loads and stores per lane, 2 = channel shuffle through LDS,
                       // 3 = its element-granular form

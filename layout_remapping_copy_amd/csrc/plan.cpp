@@ -17,8 +17,11 @@
 // staging).
 
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <initializer_list>
+#include <unordered_map>
+#include <vector>
 
 #include "lr_internal.h"
 
@@ -140,6 +143,8 @@ static bool tuning_valid(const lr_copy_tuning& t) {
   if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;
   if (!in(t.transpose_reads, {0, 1})) return false;
   if (!in(t.chunk_bytes, {8, 16})) return false;
+  if (t.batch_swizzle != -1 && (t.batch_swizzle < 0 || t.batch_swizzle > 15)) return false;
+  if (!in(t.batch_order, {0, 1})) return false;
   for (int32_t r : t.reserved)
     if (r != -1 && r != 0) return false;
   return true;
@@ -405,6 +410,138 @@ static bool plan_staged(Plan* p, int b, size_t src_align, size_t dst_align, int6
   return false;
 }
 
+// Cycles of one wavefront's 16-byte LDS accesses to 16-byte slots, in the gfx950
+// model (lds_cycles): a slot covers 4 consecutive banks, so a phase costs the most
+// distinct slots that share one group of 4 banks (slot modulo banks / 4).
+static int64_t slot_cycles(const int64_t* slot, int lanes, int32_t banks, int32_t per) {
+  int64_t cycles = 0;
+  const int groups = banks / 4;
+  for (int p0 = 0; p0 < lanes; p0 += per) {
+    const int n = std::min(lanes, p0 + per) - p0;
+    int cnt[LR_WAVE_LANES] = {0};
+    int ways = 0;
+    for (int t = 0; t < n; ++t) {
+      bool seen = false;  // a slot several lanes read is served once
+      for (int q = 0; q < t && !seen; ++q) seen = slot[p0 + q] == slot[p0 + t];
+      if (!seen) ways = std::max(ways, ++cnt[slot[p0 + t] % groups]);
+    }
+    cycles += ways;
+  }
+  return cycles;
+}
+
+// LDS cycles of the batched kernel's two exchanges (the blocks' source-row reads and
+// destination-row writes, 16 bytes a lane) over one wavefront region, in the gfx950
+// model, for the chunk swizzle sw (two XOR terms of shift, mask, target shift) and
+// block order.
+static int64_t batched_lds_cycles(int64_t P, int64_t Q, int64_t V, int64_t mpw, const int sw[6], int order) {
+  int32_t rb, rl, wb, wl;
+  gfx950_lds_model(16, false, &rb, &rl);
+  gfx950_lds_model(16, true, &wb, &wl);
+  auto swz = [&](int64_t c) { return c ^ (((c >> sw[0]) & sw[1]) << sw[2]) ^ (((c >> sw[3]) & sw[4]) << sw[5]); };
+  const int64_t pq = P * Q, cpm = pq * V, nblk = mpw * pq;
+  int64_t cycles = 0;
+  int64_t ra[LR_WAVE_LANES], wa[LR_WAVE_LANES];
+  for (int64_t u0 = 0; u0 < nblk; u0 += LR_WAVE_LANES) {
+    const int lanes = (int)std::min<int64_t>(LR_WAVE_LANES, nblk - u0);
+    for (int64_t j = 0; j < V; ++j) {
+      for (int l = 0; l < lanes; ++l) {
+        const int64_t u = u0 + l, mi = u / pq, rest = u % pq;
+        const int64_t ba = order ? rest / Q : rest % P, bb = order ? rest % Q : rest / P;
+        ra[l] = swz(mi * cpm + (V * bb + j) * P + ba);
+        wa[l] = swz(mi * cpm + (V * ba + j) * Q + bb);
+      }
+      cycles += slot_cycles(ra, lanes, rb, rl) + slot_cycles(wa, lanes, wb, wl);
+    }
+  }
+  return cycles;
+}
+
+// Batched small matrices: modes a (source-contiguous) and b (destination-contiguous)
+// form a matrix that is compact on both sides (b's source stride is a's extent, a's
+// destination stride b's extent), both extents multiples of V = 16 / eb, at most
+// 8 KiB, over any other (batch) modes whose strides keep 16-byte chunks.  Fills *p and
+// returns true when it applies.
+// The LDS swizzle and block order are left to batched_swizzle.
+static bool plan_batched(Plan* p, int a, int b, size_t src_align, size_t dst_align) {
+  if (p->eb != 2 && p->eb != 4 && p->eb != 8) return false;
+  if (p->sw_s.b || p->sw_d.b || src_align < 16 || dst_align < 16 || p->rank - 2 > kMaxKernelModes) return false;
+  const int64_t V = 16 / p->eb, A = p->m[a].ext, B = p->m[b].ext;
+  if (A % V || B % V || p->m[b].ss != A || p->m[a].sd != B || A * B * p->eb > 8192) return false;
+  int64_t count = 1;
+  for (int k = 0; k < p->rank; ++k) {
+    if (k == a || k == b) continue;
+    if (p->m[k].ss % V || p->m[k].sd % V) return false;
+    count *= p->m[k].ext;
+  }
+  const int64_t P = A / V, Q = B / V, cpm = P * Q * V, mpw = 512 / cpm;
+  p->path = LR_PATH_BATCHED;
+  p->a = a;
+  p->b = b;
+  p->b2 = -1;
+  p->v = (int)V;
+  p->tile_a = A;
+  p->tile_b = B;
+  p->block = 64;  // one wavefront per workgroup
+  p->direct = true;
+  p->bufst = false;
+  p->tel = p->twin = p->tr = false;
+  p->pipe = 0;
+  p->bt_mpw = mpw;
+  p->bt_count = count;
+  p->grid = (count + mpw - 1) / mpw;
+  return true;
+}
+
+// The LDS swizzle and block order of a batched plan: the cheapest in the bank model.
+// The first eight candidates (each with the order it is tried in first) cover,
+// between them, every power-of-two matrix of 2-, 4- and 8-byte elements that some
+// two-term XOR swizzle inside 16-chunk groups leaves without conflicts in the model
+// (a greedy cover found by exhaustive search); the rest are single terms for other
+// sizes.  A conflict-free candidate ends the search (reads take 4 cycles per row of
+// blocks, writes 8).  Measured, the choice moves the kernel by 3 % at most, even
+// against no swizzle at 4-8 times the LDS cycles (the exchange is far from the
+// limit), and the model misses some conflicts the counters show; the search costs
+// up to ~100 us of host time, so its result is kept per matrix shape and override.
+static void batched_swizzle(Plan* p, const lr_copy_tuning& tun) {
+  static const int kCand[][7] = {
+      {3, 7, 0, 4, 7, 0, 0}, {4, 7, 1, 4, 15, 0, 1}, {3, 3, 1, 3, 7, 0, 0}, {5, 1, 2, 5, 15, 0, 1},
+      {4, 3, 2, 4, 7, 0, 0}, {3, 1, 2, 4, 3, 1, 0}, {3, 1, 2, 4, 3, 0, 1}, {3, 3, 1, 4, 7, 0, 0},
+      {4, 7, 1, 0, 0, 0, 0}, {4, 15, 0, 0, 0, 0, 0}, {4, 3, 2, 0, 0, 0, 0}, {4, 3, 1, 0, 0, 0, 0},
+      {3, 3, 1, 0, 0, 0, 0}, {3, 3, 0, 0, 0, 0, 0}, {5, 15, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0}};
+  const int64_t V = p->v, P = p->tile_a / V, Q = p->tile_b / V, mpw = p->bt_mpw;
+  const uint64_t key = (uint64_t)P | ((uint64_t)Q << 16) | ((uint64_t)V << 32) |
+                       ((uint64_t)(tun.batch_swizzle + 1) << 40) | ((uint64_t)(tun.batch_order + 1) << 48);
+  thread_local std::unordered_map<uint64_t, std::array<int, 7>> cache;
+  const auto hit = cache.find(key);
+  if (hit != cache.end()) {
+    for (int i = 0; i < 6; ++i) p->bt_sw[i] = hit->second[i];
+    p->bt_order = hit->second[6];
+    return;
+  }
+  const int64_t ideal = ((mpw * P * Q + LR_WAVE_LANES - 1) / LR_WAVE_LANES) * V * (4 + 8);
+  int64_t best = -1;
+  for (int ci = 0; ci < 16 && !(best >= 0 && best <= ideal); ++ci) {
+    if (tun.batch_swizzle >= 0 && ci != tun.batch_swizzle) continue;
+    for (int o = 0; o < 2; ++o) {
+      const int order = o ? 1 - kCand[ci][6] : kCand[ci][6];
+      if (tun.batch_order >= 0 && order != tun.batch_order) continue;
+      const int64_t cy = batched_lds_cycles(P, Q, V, mpw, kCand[ci], order);
+      if (best < 0 || cy < best) {
+        best = cy;
+        for (int i = 0; i < 6; ++i) p->bt_sw[i] = kCand[ci][i];
+        p->bt_order = order;
+      }
+      if (best <= ideal) break;
+    }
+  }
+  std::array<int, 7> r;
+  for (int i = 0; i < 6; ++i) r[i] = p->bt_sw[i];
+  r[6] = p->bt_order;
+  if (cache.size() > 4096) cache.clear();
+  cache.emplace(key, r);
+}
+
 static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
                      size_t dst_align, size_t elem_bytes, uint32_t flags, const lr_copy_tuning& tun, Plan* p) {
   int rc;
@@ -434,7 +571,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
 
   const uint32_t forced_raw = (flags >> 8) & 0xFFu;
   const int forced = forced_raw ? (int)forced_raw - 1 : -1;
-  if (forced > LR_PATH_DEINTERLEAVE) return LR_ERR_INVALID;
+  if (forced > LR_PATH_BATCHED) return LR_ERR_INVALID;
   const int64_t lim32 = int64_t(1) << 31;
   p->wide = (flags & LR_COPY_WIDE_INDEX) || n >= lim32 || cos_s >= lim32 || cos_d >= lim32;
   p->block = 256;
@@ -651,6 +788,26 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       return LR_OK;
     }
     if (forced == LR_PATH_DEINTERLEAVE) return plan_chan_elements(p, a, b, false, src_align, dst_align) ? LR_OK : LR_ERR_PATH;
+  }
+
+  // batched small matrices (each at most 8 KiB, compact on both sides): whole matrices
+  // per wavefront.  Taken at once for 2-byte elements (over 2^27 elements, back to
+  // back: 16 x 16 46.1 us against 46.8 staged, 32 x 32 46.5 against 47.2, 16 x 32 46.2
+  // against 46.7, 64 x 64 46.5 against 47.9 for the transpose); other small matrices
+  // take it below when the staged path does not apply.
+  Plan batched = *p;
+  const bool bt_ok = a >= 0 && b >= 0 && a != b && (forced < 0 || forced == LR_PATH_BATCHED) &&
+                     plan_batched(&batched, a, b, src_align, dst_align);
+  if (forced == LR_PATH_BATCHED) {
+    if (!bt_ok) return LR_ERR_PATH;
+    *p = batched;
+    batched_swizzle(p, tun);
+    return LR_OK;
+  }
+  if (bt_ok && forced < 0 && p->eb == 2) {
+    *p = batched;
+    batched_swizzle(p, tun);
+    return LR_OK;
   }
 
   // transpose: register blocks of V x V elements over the src-contiguous mode a and
@@ -870,15 +1027,26 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->tr = true;
         p->bufst = false;
       }
-      // Small matrices in a batch (a whole matrix under a quarter of the smallest
-      // tile): the staged path where it applies, which moves each compact matrix as
-      // one block.  Measured on batched fp16 transposes: 32 x 32 115.6 -> 49.6 us,
-      // 16 x 16 406.6 -> 68.6 us (fp32 32 x 32, a quarter of its tile, ties: 46.1 us).
+      // Small matrices in a batch (a whole matrix at most a quarter of the tile): the
+      // staged path where it applies, which moves each compact matrix as one block,
+      // else (under a quarter) the batched path.  Measured on batched fp16 transposes:
+      // 32 x 32 115.6 -> 49.6 us, 16 x 16 406.6 -> 68.6 us (fp32 32 x 32, a quarter of
+      // its tile, ties: 46.1 us; fp64 16 x 16, a quarter too, 58.8 -> 45.6 us); over 2^26
+      // 4-byte and 2^25 8-byte elements the staged path beats the batched one (fp32 8 x 8
+      // 45.4 against 46.6 us, 16 x 16 45.6 against 46.2, 32 x 32 45.0 against 46.8, fp64
+      // 16 x 16 45.7 against 46.1).
       if (forced < 0 && tun.tile_shape < 0 && !p->tel) {
         const int64_t fa = std::min<int64_t>(p->m[a].ext, p->tile_a), fb = std::min<int64_t>(ext_b, p->tile_b);
         Plan st = before_transpose;
-        if (4 * fa * fb < p->tile_a * p->tile_b && plan_staged(&st, b, src_align, dst_align, src_cap, tun)) {
+        if (4 * fa * fb <= p->tile_a * p->tile_b && plan_staged(&st, b, src_align, dst_align, src_cap, tun)) {
           *p = st;
+          return LR_OK;
+        }
+        // (a matrix of exactly a quarter keeps the transpose: fp16 64 x 64 48.6 us
+        // against 50.2 batched)
+        if (4 * fa * fb < p->tile_a * p->tile_b && bt_ok && b2 < 0) {
+          *p = batched;
+          batched_swizzle(p, tun);
           return LR_OK;
         }
       }
@@ -919,6 +1087,37 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
   return LR_OK;
 }
 
+static int plan_uncached(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld,
+                         int64_t dst_cap, size_t dst_align, size_t elem_bytes, uint32_t flags,
+                         const lr_copy_tuning& tun, Plan* p) {
+  const int rc = plan_path(Ls, src_cap, src_align, Ld, dst_cap, dst_align, elem_bytes, flags, tun, p);
+  if (rc) return rc;
+  // different load and store policies: the generic kernel only
+  if (p->nt_ld != p->nt && p->path != LR_PATH_GENERIC && p->path != LR_PATH_VECTOR) return LR_ERR_PATH;
+  if (p->path != LR_PATH_GENERIC && p->path != LR_PATH_VECTOR) p->vorder = -1;
+  if (p->path != LR_PATH_STAGED) p->staged_cps = -1;
+  return LR_OK;
+}
+
+// The planner's inputs as a flat key: the layouts' defined fields, capacities,
+// alignments as the planner reads them (the lowest set bit, at most 16), element
+// size, flags and tuning.
+static void plan_key(const lr_layout* L, std::vector<int64_t>* k) {
+  k->push_back(L->nleaves);
+  k->push_back(L->nmodes);
+  for (int i = 0; i < L->nleaves && i < LR_MAX_LEAVES; ++i) {
+    k->push_back(L->shape[i]);
+    k->push_back(L->stride[i]);
+  }
+  for (int i = 0; i < L->nmodes && i < LR_MAX_LEAVES; ++i) k->push_back(L->mode_end[i]);
+  k->push_back(L->swz_b);
+  k->push_back(L->swz_m);
+  k->push_back(L->swz_s);
+}
+
+// Plans are kept per thread for the last 32 distinct inputs: the same copy issued
+// again (a training step, a serving loop) skips the planner, whose bank-model
+// searches take tens of microseconds, as long as a small copy's kernel.
 int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
               size_t dst_align, size_t elem_bytes, uint32_t flags, const lr_copy_tuning* tuning, Plan* p) {
   lr_copy_tuning tun;
@@ -927,13 +1126,40 @@ int plan_copy(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_l
     if (!tuning_valid(*tuning)) return LR_ERR_INVALID;
     tun = *tuning;
   }
-  const int rc = plan_path(Ls, src_cap, src_align, Ld, dst_cap, dst_align, elem_bytes, flags, tun, p);
-  if (rc) return rc;
-  // different load and store policies: the generic kernel only
-  if (p->nt_ld != p->nt && p->path != LR_PATH_GENERIC && p->path != LR_PATH_VECTOR) return LR_ERR_PATH;
-  if (p->path != LR_PATH_GENERIC && p->path != LR_PATH_VECTOR) p->vorder = -1;
-  if (p->path != LR_PATH_STAGED) p->staged_cps = -1;
-  return LR_OK;
+  if (Ls->nleaves < 1 || Ls->nleaves > LR_MAX_LEAVES || Ld->nleaves < 1 || Ld->nleaves > LR_MAX_LEAVES)
+    return plan_uncached(Ls, src_cap, src_align, Ld, dst_cap, dst_align, elem_bytes, flags, tun, p);
+  auto norm = [](size_t a) -> int64_t { return a == 0 ? 1 : (int64_t)std::min<size_t>(a & (~a + 1), 16); };
+  std::vector<int64_t> key;
+  key.reserve(160);
+  plan_key(Ls, &key);
+  plan_key(Ld, &key);
+  key.push_back(src_cap);
+  key.push_back(dst_cap);
+  key.push_back(norm(src_align));
+  key.push_back(norm(dst_align));
+  key.push_back((int64_t)elem_bytes);
+  key.push_back(flags);
+  const int32_t* t = (const int32_t*)&tun;
+  for (size_t i = 0; i < sizeof(tun) / sizeof(int32_t); ++i) key.push_back(t[i]);
+  struct Entry {
+    std::vector<int64_t> key;
+    Plan plan;
+    int rc;
+  };
+  thread_local std::array<Entry, 32> cache;
+  thread_local int next = 0;
+  for (const Entry& e : cache)
+    if (e.key == key) {
+      if (e.rc == LR_OK) *p = e.plan;
+      return e.rc;
+    }
+  const int rc = plan_uncached(Ls, src_cap, src_align, Ld, dst_cap, dst_align, elem_bytes, flags, tun, p);
+  Entry& e = cache[next];
+  next = (next + 1) % 32;
+  e.key = std::move(key);
+  e.rc = rc;
+  if (rc == LR_OK) e.plan = *p;
+  return rc;
 }
 
 // Re-checks, independently of the choices above, the invariants each kernel's
@@ -1085,6 +1311,34 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
         if (k != p.a && k != p.b && (p.m[k].ss % v || p.m[k].sd % v)) return bad();
       return LR_OK;
     }
+    case LR_PATH_BATCHED: {
+      if (p.a < 0 || p.b < 0 || p.a == p.b || p.a >= p.rank || p.b >= p.rank) return bad();
+      if (p.eb != 2 && p.eb != 4 && p.eb != 8) return bad();
+      const int64_t A = p.m[p.a].ext, B = p.m[p.b].ext;
+      if (v * p.eb != 16 || p.m[p.a].ss != 1 || p.m[p.b].sd != 1 || p.m[p.b].ss != A || p.m[p.a].sd != B ||
+          A % v || B % v || A * B * p.eb > 8192 || p.sw_s.b || p.sw_d.b || p.bufst || !p.direct)
+        return bad();
+      int64_t count = 1;
+      for (int k = 0; k < p.rank; ++k) {
+        if (k == p.a || k == p.b) continue;
+        if (p.m[k].ss % v || p.m[k].sd % v) return bad();
+        count *= p.m[k].ext;
+      }
+      const int64_t cpm = A * B / v;
+      if (p.bt_count != count || p.bt_mpw != 512 / cpm || p.bt_mpw < 1) return bad();
+      if (p.grid != (count + p.bt_mpw - 1) / p.bt_mpw || p.grid > 0x7FFFFFFF || p.block != 64) return bad();
+      // the swizzle only permutes chunks inside aligned groups of 16 and is an
+      // involution: checked over two whole regions
+      if (p.bt_order < 0 || p.bt_order > 1) return bad();
+      for (int i = 0; i < 6; ++i)
+        if (p.bt_sw[i] < 0 || p.bt_sw[i] > 15) return bad();
+      auto swz = [&](int64_t c) {
+        return c ^ (((c >> p.bt_sw[0]) & p.bt_sw[1]) << p.bt_sw[2]) ^ (((c >> p.bt_sw[3]) & p.bt_sw[4]) << p.bt_sw[5]);
+      };
+      for (int64_t c = 0; c < 1024; ++c)
+        if (swz(swz(c)) != c || (swz(c) >> 4) != (c >> 4)) return bad();
+      return LR_OK;
+    }
     case LR_PATH_STAGED: {
       const int in = p.staged_inner;
       if (in < 1 || in >= p.rank || v * p.eb != 16) return bad();
@@ -1193,6 +1447,8 @@ void lr_copy_tuning_init(lr_copy_tuning* t) {
   t->tile_shape = t->tile_order = t->element_tiles = t->direct_loads = t->gather_chunks = t->pipeline_tiles = -1;
   t->transpose_reads = -1;
   t->chunk_bytes = -1;
+  t->batch_swizzle = -1;
+  t->batch_order = -1;
   for (int32_t& r : t->reserved) r = -1;
 }
 
@@ -1250,6 +1506,10 @@ int lr_copy_plan_tuned(const lr_layout* Ls, int64_t src_capacity_elems, size_t s
   out->gather_chunks = (int32_t)p.staged_cps;
   out->pipeline_tiles = p.pipe;
   out->transpose_reads = p.tr ? 1 : 0;
+  const bool bt = p.path == LR_PATH_BATCHED;
+  out->batch_matrices = bt ? (int32_t)p.bt_mpw : -1;
+  for (int i = 0; i < 6; ++i) out->batch_swizzle[i] = bt ? p.bt_sw[i] : 0;
+  out->batch_order = bt ? p.bt_order : -1;
   out->tile_a = p.tile_a;
   out->tile_b = p.tile_b;
   out->grid = p.grid;

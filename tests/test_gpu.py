@@ -340,7 +340,7 @@ def test_copy_tile8x8_aliased(dev):
 
 
 ALL_PATHS = [lr.PATH_GENERIC, lr.PATH_VECTOR, lr.PATH_TRANSPOSE, lr.PATH_TRANSPOSE_DIRECT, lr.PATH_INTERLEAVE,
-             lr.PATH_DEINTERLEAVE, lr.PATH_STAGED, lr.PATH_DUAL, lr.PATH_ALIAS]
+             lr.PATH_DEINTERLEAVE, lr.PATH_STAGED, lr.PATH_DUAL, lr.PATH_ALIAS, lr.PATH_BATCHED]
 
 
 def _case_pairs():
@@ -723,7 +723,7 @@ def test_channel_shuffle_destination_beyond_4_gib(dev):
 @pytest.mark.parametrize("nt", ["0", "1"])
 def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
     """lr_layout_copy allocates nothing and records no memset, so captured copies
-    (seven paths in one graph, with plain or streaming accesses, the latter with the
+    (eight paths in one graph, with plain or streaming accesses, the latter with the
     sc1 buffer stores) replay correctly; each replay is checked after eager work has
     changed the sources."""
     knobs.policy(nt)
@@ -733,8 +733,9 @@ def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
         cases.append((w.src_layout, w.dst_layout, w.src_elems, w.dst_elems, w.elem_bytes))
     rgb = W.small("rgb_nhwc2nchw")  # and back: the channel-shuffle interleave
     cases.append((rgb.dst_layout, rgb.src_layout, rgb.dst_elems, rgb.src_elems, rgb.elem_bytes))
+    cases.append(("(16,16,300):(16,1,256)", "(16,16,300):(1,16,256)", 76800, 76800, 2))  # batched matrices
     paths = {plan(ts, ns, td, nd, eb)["path"] for ts, td, ns, nd, eb in cases}
-    assert {"transpose", "vector", "interleave", "staged", "deinterleave"} <= paths, paths
+    assert {"transpose", "vector", "interleave", "staged", "deinterleave", "batched"} <= paths, paths
     s_list, d_list, plans = [], [], []
     for ts, td, ns, nd, eb in cases:
         s_list.append(torch.zeros(ns * eb, dtype=torch.uint8, device=dev))
@@ -986,14 +987,16 @@ def test_odd_pitch_transposes_full_size(dev):
 
 def test_small_batched_and_narrow_transposes(dev, knobs):
     """Transposes whose extents leave a tile mostly idle: batches of small matrices
-    (each under a quarter of the smallest tile) take the staged path, one compact
+    of 2-byte elements take the batched path, whole matrices per wavefront, and of
+    4-byte elements (a quarter of the tile or less) the staged path, one compact
     matrix a block; a short destination-contiguous extent (NCHW -> NHWC with few
     channels) takes tiles no taller than it.  Ragged batches, both policies, and
     every destination element stored once."""
-    cases = [("(32,32,300):(32,1,1024)", "(32,32,300):(1,32,1024)", 2, "staged"),
-             ("(16,16,1001):(16,1,256)", "(16,16,1001):(1,16,256)", 2, "staged"),
-             ("(16,32,257):(32,1,512)", "(16,32,257):(1,16,512)", 2, "staged"),
-             ("(32,32,100):(32,1,1024)", "(32,32,100):(1,32,1024)", 4, "transpose"),
+    cases = [("(32,32,300):(32,1,1024)", "(32,32,300):(1,32,1024)", 2, "batched"),
+             ("(16,16,1001):(16,1,256)", "(16,16,1001):(1,16,256)", 2, "batched"),
+             ("(16,32,257):(32,1,512)", "(16,32,257):(1,16,512)", 2, "batched"),
+             ("(32,32,100):(32,1,1024)", "(32,32,100):(1,32,1024)", 4, "staged"),
+             ("(16,16,333):(16,1,256)", "(16,16,333):(1,16,256)", 8, "staged"),
              ("(3,1000,32):(32000,1,1000)", "(3,1000,32):(32000,32,1)", 2, "transpose"),
              ("(2,1000,64):(64000,1,1000)", "(2,1000,64):(64000,64,1)", 2, "transpose"),
              ("(2,1000,128):(128000,1,1000)", "(2,1000,128):(128000,128,1)", 2, "transpose"),
@@ -1235,6 +1238,60 @@ def test_byte_transpose_chunks(dev, knobs):
                     assert np.array_equal(gpu_copy(dev, src, ts, dst, td, 1), want), (ts, cb, shape, direct)
                     ran += 1
     assert ran >= 50
+
+
+def _batched_cases():
+    """Batches of small matrices, each compact on both sides: (src, dst, eb)."""
+    return [("(16,16,100):(16,1,256)", "(16,16,100):(1,16,256)", 2),
+            ("(32,32,9):(32,1,1024)", "(32,32,9):(1,32,1024)", 2),
+            ("(64,64,5):(64,1,4096)", "(64,64,5):(1,64,4096)", 2),
+            ("(8,8,300):(8,1,64)", "(8,8,300):(1,8,64)", 4),
+            ("(16,16,37):(16,1,256)", "(16,16,37):(1,16,256)", 4),
+            ("(32,32,7):(32,1,1024)", "(32,32,7):(1,32,1024)", 4),
+            ("(24,24,21):(24,1,576)", "(24,24,21):(1,24,576)", 2),
+            ("(16,16,19):(16,1,256)", "(16,16,19):(1,16,256)", 8),
+            ("(32,32,3):(32,1,1024)", "(32,32,3):(1,32,1024)", 8),
+            ("(16,32,13):(32,1,512)", "(16,32,13):(1,16,512)", 2),
+            ("(8,16,3,7):(16,1,128,384)", "(8,16,3,7):(1,8,128,384)", 4),
+            ("(16,24,7):(24,1,400)", "(16,24,7):(1,16,400)", 2),
+            ("(32,16,11):(16,1,520)", "(32,16,11):(1,32,512)", 4),
+            ("(136,24):(24,1)", "(136,24):(1,136)", 2)]
+
+
+def test_batched_small_matrices(dev, knobs):
+    """The batched path: whole small matrices per wavefront, square and rectangular,
+    counts that leave the last wavefront or workgroup partly empty, padded batch
+    strides, two batch modes, one lone matrix; 2-, 4- and 8-byte elements; both
+    policies; the planner's own plan too.  Whole buffers against the oracle."""
+    force = lr.COPY_FORCE_PATH(lr.PATH_BATCHED)
+    for ci, (ts, td, eb) in enumerate(_batched_cases()):
+        ns, nd = lr.parse(ts).cosize, lr.parse(td).cosize
+        src = np.random.default_rng(150 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for nt in ("0", "1"):
+            knobs.t.clear()
+            knobs.policy(nt)
+            p = plan(ts, ns, td, nd, eb, force)
+            say("batched", ts, "eb", eb, "nt", nt, "matrices per wave", p["batch_matrices"], "swizzle",
+                p["batch_swizzle"], "order", p["batch_order"], "grid", p["grid"])
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, force), want), (ts, nt)
+        knobs.t.clear()
+        say("batched, planner's plan", plan(ts, ns, td, nd, eb)["path"])
+        assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), ts
+
+
+def test_batched_write_counts(dev):
+    """Every destination element of a batched copy is stored exactly once."""
+    for ci, (ts, td, eb) in enumerate(_batched_cases()):
+        ns, nd = lr.parse(ts).cosize, lr.parse(td).cosize
+        src = np.random.default_rng(170 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        mult = _multiplicity(O.parse(td), O.size(O.parse(ts)), nd)
+        say("batched write counts", ts, "eb", eb)
+        got, counts = _write_counts(dev, src, ts, dst, td, eb, lr.COPY_FORCE_PATH(lr.PATH_BATCHED))
+        assert np.array_equal(counts, (mult > 0).astype(np.int32)), ts
+        assert np.array_equal(got, O.copy(src, O.parse(ts), dst, O.parse(td), eb))
 
 
 def test_transpose_pipelined_write_counts(dev, knobs):

@@ -1066,3 +1066,83 @@ def test_host_algebra_under_sanitizers(tmp_path):
     r = subprocess.run([exe, "fuzz"], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "fuzz ok" in r.stdout
+
+
+def test_batched_plan():
+    """The batched path: whole compact small matrices per wavefront.  The planner takes
+    it for 2-byte elements (up to 8 KiB a matrix), and for other small matrices the
+    staged path does not take; it keeps the staged path for 4- and 8-byte elements
+    and the transpose for their 8 KiB matrices.  The LDS swizzle is conflict-free in the
+    bank model for power-of-two matrices and is an involution inside 16-chunk groups."""
+    def bt(A, B, n, eb):
+        return (f"({B},{A},{n}):({A},1,{A * B})", A * B * n, f"({B},{A},{n}):(1,{B},{A * B})", A * B * n, eb)
+    assert lr.copy_plan(*bt(16, 16, 4096, 2))["path"] == "batched"
+    assert lr.copy_plan(*bt(32, 32, 4096, 2))["path"] == "batched"
+    assert lr.copy_plan(*bt(24, 24, 4096, 2))["path"] == "batched"
+    assert lr.copy_plan(*bt(16, 16, 4096, 4))["path"] == "staged"
+    assert lr.copy_plan(*bt(16, 16, 4096, 8))["path"] == "staged"
+    assert lr.copy_plan(*bt(64, 64, 4096, 2))["path"] == "batched"
+    assert lr.copy_plan(*bt(64, 32, 4096, 4))["path"] == "transpose"
+    force = lr.COPY_FORCE_PATH(lr.PATH_BATCHED)
+    for A, B, eb in ((16, 16, 2), (32, 32, 2), (64, 64, 2), (16, 32, 2), (8, 16, 2), (8, 8, 4), (16, 16, 4),
+                     (32, 64, 4), (4, 4, 8), (16, 16, 8), (32, 32, 8)):
+        p = lr.copy_plan(*bt(A, B, 1000, eb), flags=force)
+        V = 16 // eb
+        cpm = A * B // V
+        assert p["path"] == "batched" and p["block"] == 64 and p["batch_matrices"] == 512 // cpm
+        assert p["grid"] == -(-1000 // p["batch_matrices"]) and (p["tile_a"], p["tile_b"]) == (A, B)
+        s0, m0, t0, s1, m1, t1 = p["batch_swizzle"]
+
+        def swz(c):
+            return c ^ (((c >> s0) & m0) << t0) ^ (((c >> s1) & m1) << t1)
+        assert all(swz(swz(c)) == c and swz(c) >> 4 == c >> 4 for c in range(1024))
+        # the gfx950 model: 16-byte reads in phases of 16 lanes over 64 banks, writes in
+        # phases of 8 over 32; every phase of both exchanges touches distinct bank groups
+        P, Q = A // V, B // V
+        nblk = p["batch_matrices"] * P * Q
+        for r in range(0, nblk, 64):
+            lanes = []
+            for u in range(r, min(nblk, r + 64)):
+                mi, rest = divmod(u, P * Q)
+                ba, bb = (rest // Q, rest % Q) if p["batch_order"] else (rest % P, rest // P)
+                lanes.append((mi, ba, bb))
+            for j in range(V):
+                rd = [swz(mi * cpm + (V * bb + j) * P + ba) for mi, ba, bb in lanes]
+                wr = [swz(mi * cpm + (V * ba + j) * Q + bb) for mi, ba, bb in lanes]
+                for q in range(0, len(rd), 16):
+                    assert len({x % 16 for x in rd[q:q + 16]}) == len(rd[q:q + 16]), (A, B, eb, "read")
+                for q in range(0, len(wr), 8):
+                    assert len({x % 8 for x in wr[q:q + 8]}) == len(wr[q:q + 8]), (A, B, eb, "write")
+    # not compact, too large, or narrow chunks: the path does not apply
+    for args in (("(16,16,64):(17,1,272)", 272 * 64, "(16,16,64):(1,16,256)", 256 * 64, 2),
+                 ("(128,64,8):(64,1,8192)", 8192 * 8, "(128,64,8):(1,128,8192)", 8192 * 8, 2),
+                 ("(12,12,64):(12,1,144)", 144 * 64, "(12,12,64):(1,12,144)", 144 * 64, 2)):
+        with pytest.raises(lr.LayoutRemapError):
+            lr.copy_plan(*args, flags=force)
+
+
+def test_plan_cache_returns_the_same_plans():
+    """Plans are cached per thread by their full input: asking again gives the same
+    plan (or the same error), and any change of input (capacity, alignment, tuning,
+    flags, a stride) gives that input's own plan."""
+    w = W.full("transpose")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    first = lr.copy_plan(*args)
+    for _ in range(3):
+        assert lr.copy_plan(*args) == first
+    t = lr.copy_plan(*args, tuning={"tile_shape": 1})
+    assert t["tile_b"] != first["tile_b"] and lr.copy_plan(*args) == first
+    assert lr.copy_plan(*args, tuning={"tile_shape": 1}) == t
+    odd = lr.copy_plan(*args, src_align=2)
+    assert odd != first and lr.copy_plan(*args, src_align=2) == odd
+    assert lr.copy_plan(*args, src_align=48) == first  # 48 = 16 * 3: aligned to 16
+    for _ in range(2):
+        with pytest.raises(lr.LayoutRemapError) as e:
+            lr.copy_plan(*args, flags=lr.COPY_FORCE_PATH(lr.PATH_INTERLEAVE))
+        assert e.value.code == lr.binding.ERR_PATH
+    other = lr.copy_plan("(8192,8192):(8193,1)", 8192 * 8193, w.dst_layout, w.dst_elems, 2)
+    assert other["joint"] != first["joint"]
+    # more distinct inputs than the cache holds, then the first again
+    for k in range(40):
+        lr.copy_plan(f"({64 + k},64):(64,1)", (64 + k) * 64, f"({64 + k},64):(1,{64 + k})", (64 + k) * 64, 4)
+    assert lr.copy_plan(*args) == first

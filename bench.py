@@ -447,11 +447,14 @@ BATCHED_SHAPES = ((2, 16, 16, 262144), (2, 32, 32, 65536), (2, 64, 64, 16384), (
                   (4, 64, 32, 16384), (8, 16, 16, 65536), (8, 32, 32, 16384))
 
 
-def batched_sweep(lr, torch, steps: int = 20):
+def batched_sweep(lr, torch, mode: str = "paths", steps: int = 20):
     """Batched small-matrix transposes: the planner's path against the batched,
-    staged and transpose paths forced, back to back over rotating buffers, beside a
-    contiguous copy of the same bytes.  One JSON line per shape and variant."""
+    staged and transpose paths forced (mode "paths"), or the batched path under each
+    of its 16 LDS swizzles and 2 block orders (mode "swizzles", 10 launches each),
+    back to back over rotating buffers, beside a contiguous copy of the same bytes.
+    One JSON line per shape and variant."""
     dev = torch.device("cuda:0")
+    force = lr.COPY_FORCE_PATH(lr.PATH_BATCHED)
     for eb, A, B, n in BATCHED_SHAPES:
         ts, td = f"({B},{A},{n}):({A},1,{A * B})", f"({B},{A},{n}):(1,{B},{A * B})"
         Ls = lr.parse(ts)
@@ -460,7 +463,19 @@ def batched_sweep(lr, torch, steps: int = 20):
         cu = N * eb // 16
         whole = [(s_[:cu * 16], d_[:cu * 16]) for s_, d_ in pairs]
         _, cms = _time_copies(lr, torch, whole, f"{cu}:1", f"{cu}:1", 16, steps, 3)
-        for label, flags in (("planner", 0), ("batched", lr.COPY_FORCE_PATH(lr.PATH_BATCHED)),
+        if mode == "swizzles":
+            for ci in range(16):
+                for order in (0, 1):
+                    t = {"batch_swizzle": ci, "batch_order": order}
+                    p = lr.copy_plan(ts, ns, td, nd, eb, force, tuning=t)
+                    _, ms = _time_copies(lr, torch, pairs, ts, td, eb, 10, 2, flags=force, tuning=t)
+                    print(json.dumps({"matrix": [A, B], "elem_bytes": eb, "swizzle": ci, "order": order,
+                                      "lds_swizzle": p["batch_swizzle"], "us": round(ms * 1e3, 2),
+                                      "frac_of_copy": round(cms / ms, 3)}), flush=True)
+            del pairs, whole
+            torch.cuda.empty_cache()
+            continue
+        for label, flags in (("planner", 0), ("batched", force),
                              ("staged", lr.COPY_FORCE_PATH(lr.PATH_STAGED)),
                              ("transpose", lr.COPY_FORCE_PATH(lr.PATH_TRANSPOSE))):
             try:
@@ -608,9 +623,9 @@ def main():
     ap.add_argument("--byte-transpose-sweep", nargs="*", metavar="RxC",
                     help="1-byte transposes (all listed shapes, or these): 8- against 16-byte chunks, "
                          "direct loads and the 1-byte transpose reads")
-    ap.add_argument("--batched-sweep", action="store_true",
+    ap.add_argument("--batched-sweep", nargs="?", const="paths", choices=["paths", "swizzles"],
                     help="batched small-matrix transposes: the planner's path against the batched, staged and "
-                         "transpose paths")
+                         "transpose paths, or the batched path under each LDS swizzle and block order")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
                     help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
@@ -649,7 +664,7 @@ def main():
         layout_sweep(lr, torch)
         return
     if args.batched_sweep:
-        batched_sweep(lr, torch)
+        batched_sweep(lr, torch, args.batched_sweep)
         return
     if args.byte_transpose_sweep is not None:
         shapes = [tuple(int(x) for x in s.split("x")) for s in args.byte_transpose_sweep] or BYTE_SHAPES

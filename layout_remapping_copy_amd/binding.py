@@ -120,6 +120,7 @@ class lr_copy_tuning(ctypes.Structure):
         ("chunk_bytes", ctypes.c_int32),
         ("batch_swizzle", ctypes.c_int32),
         ("batch_order", ctypes.c_int32),
+        ("workgroup_lanes", ctypes.c_int32),
         ("reserved", ctypes.c_int32 * 1),
     ]
 

@@ -370,10 +370,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // LNT / SNT: non-temporal loads / stores (chosen apart: a source read once with a
-// destination that should stay cached for its next reader).
-template <int UB, bool WIDE, int U, bool LNT, bool SNT>
-__global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
+// destination that should stay cached for its next reader).  L lanes per workgroup
+// (64, 128 or 256 with one unit per lane; 256 otherwise).
+template <int UB, bool WIDE, int U, bool LNT, bool SNT, int L = 256>
+__global__ void __launch_bounds__(L) k_generic(GenericArgs a) {
   static_assert(U == 1 || U == 4, "one or four units per lane");
+  static_assert(L == 256 || (U == 1 && !WIDE), "narrower workgroups with one unit per lane");
   using T = typename Raw<UB>::T;
   const T* __restrict__ src = (const T*)a.src;
   T* __restrict__ dst = (T*)a.dst;
@@ -384,7 +386,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
       // destination byte lies under 4 GiB from the base.
       const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.dst, 0, -1, kBufferWord3);
       for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
-        const int64_t i0 = ch * 256 + threadIdx.x;
+        const int64_t i0 = ch * L + threadIdx.x;
         if (i0 < a.n_units) {
           uint64_t s0, d0;
           generic_offsets<false>(a, i0, &s0, &d0);
@@ -397,7 +399,7 @@ __global__ void __launch_bounds__(256) k_generic(GenericArgs a) {
     }
   }
   for (int64_t ch = blockIdx.x; ch < a.n_chunks; ch += gridDim.x) {
-    const int64_t i0 = ch * (256 * U) + threadIdx.x;
+    const int64_t i0 = ch * (L * U) + threadIdx.x;
     if constexpr (U == 1) {
       if (i0 < a.n_units) {
         uint64_t s0, d0;
@@ -1366,8 +1368,9 @@ struct InterleaveArgs {
 //     16/NB bytes (P = V/NB positions of a, one load per b), so that every store
 //     instruction of a wave covers 1 KiB of contiguous dst.  One chunk per lane:
 //     more per lane measured slower.
-template <int EB, int NB, bool NARROW, bool NT>
-__global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
+template <int EB, int NB, bool NARROW, bool NT, int L = 256>
+__global__ void __launch_bounds__(L) k_interleave(InterleaveArgs t) {
+  static_assert(L == 256 || NARROW, "narrower workgroups on the narrow form");
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
   using C = Chunk<T, V>;
@@ -1388,7 +1391,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t j = ta * (256 * U) + u * 256 + threadIdx.x;  // dst chunk index
+      const uint32_t j = ta * (L * U) + u * L + threadIdx.x;  // dst chunk index
       const uint32_t a0 = j * P;
       ok[u] = a0 < t.ext_a;
       if (ok[u]) {
@@ -1402,7 +1405,7 @@ __global__ void __launch_bounds__(256) k_interleave(InterleaveArgs t) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
-      const uint32_t j = ta * (256 * U) + u * 256 + threadIdx.x;
+      const uint32_t j = ta * (L * U) + u * L + threadIdx.x;
       C o;
 #pragma unroll
       for (int x = 0; x < V; ++x) o.e[x] = in[u][x % NB].e[x / NB];
@@ -2048,9 +2051,14 @@ static bool launch_atoms(const Plan& p, const GenericArgs& g, unsigned grid, hip
 }
 
 template <int UB, bool LNT, bool SNT>
-static void launch_generic_nt(const GenericArgs& a, bool wide, int unroll, unsigned grid, hipStream_t st) {
+static void launch_generic_nt(const GenericArgs& a, bool wide, int unroll, int lanes, unsigned grid,
+                              hipStream_t st) {
   if (wide)
     hipLaunchKernelGGL((k_generic<UB, true, 4, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
+  else if (unroll == 1 && lanes == 64)
+    hipLaunchKernelGGL((k_generic<UB, false, 1, LNT, SNT, 64>), dim3(grid), dim3(64), 0, st, a);
+  else if (unroll == 1 && lanes == 128)
+    hipLaunchKernelGGL((k_generic<UB, false, 1, LNT, SNT, 128>), dim3(grid), dim3(128), 0, st, a);
   else if (unroll == 1)
     hipLaunchKernelGGL((k_generic<UB, false, 1, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
   else
@@ -2058,16 +2066,16 @@ static void launch_generic_nt(const GenericArgs& a, bool wide, int unroll, unsig
 }
 
 template <int UB>
-static void launch_generic(const GenericArgs& a, bool wide, int unroll, bool nt_ld, bool nt_st, unsigned grid,
-                           hipStream_t st) {
+static void launch_generic(const GenericArgs& a, bool wide, int unroll, int lanes, bool nt_ld, bool nt_st,
+                           unsigned grid, hipStream_t st) {
   if (nt_ld && nt_st)
-    launch_generic_nt<UB, true, true>(a, wide, unroll, grid, st);
+    launch_generic_nt<UB, true, true>(a, wide, unroll, lanes, grid, st);
   else if (nt_ld)
-    launch_generic_nt<UB, true, false>(a, wide, unroll, grid, st);
+    launch_generic_nt<UB, true, false>(a, wide, unroll, lanes, grid, st);
   else if (nt_st)
-    launch_generic_nt<UB, false, true>(a, wide, unroll, grid, st);
+    launch_generic_nt<UB, false, true>(a, wide, unroll, lanes, grid, st);
   else
-    launch_generic_nt<UB, false, false>(a, wide, unroll, grid, st);
+    launch_generic_nt<UB, false, false>(a, wide, unroll, lanes, grid, st);
 }
 
 template <int EB>
@@ -2194,15 +2202,26 @@ static bool launch_transpose(const TransposeArgs& a, int v, bool lds, int shape,
             : launch_transpose_nt<EB, false>(a, v, lds, shape, dl, grid, st);
 }
 
-template <int EB, bool NARROW, bool NT>
-static bool launch_interleave_n(const InterleaveArgs& a, int nb, unsigned grid, hipStream_t st) {
+template <int EB, bool NARROW, bool NT, int L>
+static bool launch_interleave_l(const InterleaveArgs& a, int nb, unsigned grid, hipStream_t st) {
   switch (nb) {
-    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
-    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16, NARROW, NT>), dim3(grid), dim3(256), 0, st, a); return true; } break;
+    case 2: if constexpr (EB <= 8) { hipLaunchKernelGGL((k_interleave<EB, 2, NARROW, NT, L>), dim3(grid), dim3(L), 0, st, a); return true; } break;
+    case 4: if constexpr (EB <= 4) { hipLaunchKernelGGL((k_interleave<EB, 4, NARROW, NT, L>), dim3(grid), dim3(L), 0, st, a); return true; } break;
+    case 8: if constexpr (EB <= 2) { hipLaunchKernelGGL((k_interleave<EB, 8, NARROW, NT, L>), dim3(grid), dim3(L), 0, st, a); return true; } break;
+    case 16: if constexpr (EB == 1) { hipLaunchKernelGGL((k_interleave<EB, 16, NARROW, NT, L>), dim3(grid), dim3(L), 0, st, a); return true; } break;
   }
   return false;
+}
+
+// lanes: workgroup lanes of the narrow form (64, 128 or 256; the wide form takes 256)
+template <int EB, bool NARROW, bool NT>
+static bool launch_interleave_n(const InterleaveArgs& a, int nb, int lanes, unsigned grid, hipStream_t st) {
+  if constexpr (NARROW) {
+    if (lanes == 64) return launch_interleave_l<EB, true, NT, 64>(a, nb, grid, st);
+    if (lanes == 128) return launch_interleave_l<EB, true, NT, 128>(a, nb, grid, st);
+  }
+  if (lanes != 256) return false;
+  return launch_interleave_l<EB, NARROW, NT, 256>(a, nb, grid, st);
 }
 
 template <int EB, int CC, bool INTERLEAVE, bool NT>
@@ -2239,12 +2258,13 @@ static bool launch_chan(const ChanArgs& a, int c, bool interleave, bool elem, bo
 }
 
 template <int EB>
-static bool launch_interleave(const InterleaveArgs& a, int nb, bool narrow, bool nt, unsigned grid, hipStream_t st) {
+static bool launch_interleave(const InterleaveArgs& a, int nb, bool narrow, bool nt, int lanes, unsigned grid,
+                              hipStream_t st) {
   if (nt)
-    return narrow ? launch_interleave_n<EB, true, true>(a, nb, grid, st)
-                  : launch_interleave_n<EB, false, true>(a, nb, grid, st);
-  return narrow ? launch_interleave_n<EB, true, false>(a, nb, grid, st)
-                : launch_interleave_n<EB, false, false>(a, nb, grid, st);
+    return narrow ? launch_interleave_n<EB, true, true>(a, nb, lanes, grid, st)
+                  : launch_interleave_n<EB, false, true>(a, nb, lanes, grid, st);
+  return narrow ? launch_interleave_n<EB, true, false>(a, nb, lanes, grid, st)
+                : launch_interleave_n<EB, false, false>(a, nb, lanes, grid, st);
 }
 
 #define LR_DISPATCH_EB(eb, CALL)          \
@@ -2294,11 +2314,11 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.sws_mask64 = zs.b ? (((uint64_t(1) << zs.b) - 1) << zs.m) : 0;
       a.swd_mask64 = zd.b ? (((uint64_t(1) << zd.b) - 1) << zd.m) : 0;
       a.n_units = p.n_units;
-      a.n_chunks = (p.n_units + 256 * p.unroll - 1) / (256 * p.unroll);
+      a.n_chunks = (p.n_units + p.block * p.unroll - 1) / (p.block * p.unroll);
       a.bufst = p.bufst ? 1u : 0u;
       const int ub = p.v * p.eb;
       if (p.vorder == 3) return launch_atoms(p, a, grid, st) ? check_launch() : LR_ERR_PATH;
-      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.nt_ld, p.nt, grid, st));
+      LR_DISPATCH_EB(ub, launch_generic<EBV>(a, p.wide, p.unroll, p.block, p.nt_ld, p.nt, grid, st));
       return check_launch();
     }
     case LR_PATH_DUAL:
@@ -2417,7 +2437,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       a.swd = swz_arg(p.sw_d);
       a.bufst = p.bufst ? 1u : 0u;
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, p.inarrow != 0, p.nt, grid, st));
+      LR_DISPATCH_EB(p.eb, ok = launch_interleave<EBV>(a, (int)p.tile_b, p.inarrow != 0, p.nt, p.block, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }

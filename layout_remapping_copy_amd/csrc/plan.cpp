@@ -145,6 +145,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
   if (!in(t.chunk_bytes, {8, 16})) return false;
   if (t.batch_swizzle != -1 && (t.batch_swizzle < 0 || t.batch_swizzle > 15)) return false;
   if (!in(t.batch_order, {0, 1})) return false;
+  if (!in(t.workgroup_lanes, {64, 128, 256})) return false;
   for (int32_t r : t.reserved)
     if (r != -1 && r != 0) return false;
   return true;
@@ -303,7 +304,7 @@ static void block_vector_order(Plan* p) {
     }
   };
   fill(64, true);    // a wave's lanes
-  fill(256, false);  // a workgroup's waves
+  fill(p->block, false);  // a workgroup's waves
   std::stable_sort(rest, rest + nr, [](const JMode& x, const JMode& y) {
     return x.ss < y.ss || (x.ss == y.ss && x.sd < y.sd);
   });
@@ -542,6 +543,13 @@ static void batched_swizzle(Plan* p, const lr_copy_tuning& tun) {
   cache.emplace(key, r);
 }
 
+// Lanes per workgroup of the vector / generic kernel with one unit per lane: one
+// wavefront for a single contiguous run from a 64 MiB footprint (measured on plain
+// copies: 64 MiB 12.9-13.1 -> 12.8 us, 256 MiB 43.1 -> 41.0, 1 GiB 164.7 -> 161.7; at
+// 16 MiB 256 lanes stay ahead, 7.9 against 8.3 us), 256 otherwise (a 3-D permute over
+// three modes lost 2-4 % with one wavefront, row gathers tied).
+static int stream_lanes(const Plan& p, bool big_footprint) { return big_footprint && p.rank == 1 ? 64 : 256; }
+
 static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, const lr_layout* Ld, int64_t dst_cap,
                      size_t dst_align, size_t elem_bytes, uint32_t flags, const lr_copy_tuning& tun, Plan* p) {
   int rc;
@@ -655,7 +663,8 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
     p->path = forced == LR_PATH_GENERIC ? LR_PATH_GENERIC : (v0 > 1 ? LR_PATH_VECTOR : LR_PATH_GENERIC);
     p->v = (int)v0;
     p->n_units = n / v0;
-    p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
+    p->block = (p->unroll == 1 && !p->wide) ? knob(tun.workgroup_lanes, stream_lanes(*p, big_footprint)) : 256;
+    p->grid = (p->n_units + p->block * p->unroll - 1) / (p->block * p->unroll);
     // Traversal order after the common contiguous mode.  Any order of the joint
     // modes is the same copy when the destination is injective; walking the source
     // order (reads in long runs, writes in runs of the common mode) measured
@@ -670,6 +679,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
     p->vorder = knob(tun.vector_order, atoms ? 3 : 1);
     if (p->vorder == 3 && !atoms) p->vorder = 1;
     if (p->vorder == 3) {
+      p->block = 256;
       p->a = aa;
       p->b = ab;
       p->tile_a = p->tile_b = at;
@@ -749,7 +759,11 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       p->inarrow = chan ? 2 : (int)(inarrow_env & 1);
       // a-elements per workgroup, matching the kernel's per-lane unroll (one dst
       // chunk per lane on the narrow variant, V pixels per lane on the shuffle)
-      p->tile_a = p->inarrow == 2 ? 256 * V : p->inarrow ? 256 * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
+      // one wavefront per workgroup from a 64 MiB footprint: the (16,32,4096,128) head
+      // interleave 162.4 -> 159.0-160.2 us back to back, a (16,64,4096,64) one with four
+      // heads 24.3 -> 17.1 us
+      p->block = p->inarrow == 1 ? knob(tun.workgroup_lanes, big_footprint ? 64 : 256) : 256;
+      p->tile_a = p->inarrow == 2 ? 256 * V : p->inarrow ? p->block * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
       // the narrow variant's streaming stores as buffer stores with the nt and sc1
       // bits from the destination base (head interleave 6.27 -> 6.55 TB/s)
       p->bufst = p->inarrow != 0 && sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
@@ -1081,7 +1095,8 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
   int64_t ne = 1;
   for (int k = 0; k < p->rank; ++k) ne *= p->m[k].ext;
   p->n_units = ne / v;
-  p->grid = (p->n_units + 256 * p->unroll - 1) / (256 * p->unroll);
+  p->block = (p->unroll == 1 && !p->wide) ? knob(tun.workgroup_lanes, stream_lanes(*p, big_footprint)) : 256;
+  p->grid = (p->n_units + p->block * p->unroll - 1) / (p->block * p->unroll);
   // 16-byte units (fused elements) take the vector path's buffer stores too
   p->bufst = v * p->eb == 16 && p->unroll == 1 && !p->wide && sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
   return LR_OK;
@@ -1197,6 +1212,9 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
           if (p.m[k].ss % v || p.m[k].sd % v) return bad();
       }
       if (p.n_units * v != prod) return bad();
+      // workgroup lanes: 64, 128 or 256 for one unit per lane with 32-bit indices
+      if (p.block != 256 && !((p.block == 64 || p.block == 128) && p.unroll == 1 && !p.wide && p.vorder != 3))
+        return bad();
       if (p.vorder == 3) {  // tiles of atoms: see atom_tiles
         int a = -1, b = -1;
         int64_t T = 0;
@@ -1285,7 +1303,8 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       // the kernel's per-lane unroll
       if (p.inarrow == 2) {  // channel shuffle: any NB it was built for, no swizzle
         if (!chan_supported(p.eb, nb) || p.sw_s.b || p.sw_d.b || p.tile_a != 256 * v) return bad();
-      } else if (!is_pow2(nb) || p.tile_a != (p.inarrow ? 256 * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v)) {
+      } else if (!is_pow2(nb) || p.tile_a != (p.inarrow ? p.block * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v) ||
+                 (p.block != 256 && !(p.inarrow == 1 && (p.block == 64 || p.block == 128)))) {
         return bad();
       }
       if (p.bufst && (!p.inarrow || (bound(md, p.sw_d) * p.eb >> 32) != 0)) return bad();
@@ -1449,6 +1468,7 @@ void lr_copy_tuning_init(lr_copy_tuning* t) {
   t->chunk_bytes = -1;
   t->batch_swizzle = -1;
   t->batch_order = -1;
+  t->workgroup_lanes = -1;
   for (int32_t& r : t->reserved) r = -1;
 }
 

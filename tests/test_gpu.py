@@ -446,7 +446,8 @@ def test_copy_random_pairs(dev, knobs):
                "vector_order": rng.choice([-1, 0, 1, 2, 3]), "units_per_lane": rng.choice([-1, 1, 4]),
                "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
                "transpose_reads": rng.choice([-1, 0, 1]),
-               "chunk_bytes": random.Random(i).choice([-1, -1, 8, 16])}
+               "chunk_bytes": random.Random(i).choice([-1, -1, 8, 16]),
+               "workgroup_lanes": random.Random(1000 + i).choice([-1, 64, 128, 256])}
         knobs.t.clear()
         knobs.set(**env)
         if i % 50 == 0:
@@ -1211,6 +1212,37 @@ def test_transpose_reads(dev, knobs, shape):
                     ran[eb] += 1
     assert ran[2] >= (40 if shape < 3 else 20)
     assert ran[1] >= (20 if shape == 0 else 10)  # 16 x 16-byte chunks: 32 x 32 does not fit, no pipelined 32 x 16
+
+
+def test_workgroup_lanes(dev, knobs):
+    """64-, 128- and 256-lane workgroups on the streaming kernels with one unit per lane:
+    vector copies with ragged unit counts and several modes, 2- to 16-byte units, both
+    policies, and the narrow interleave at every short extent."""
+    cases = [("(1000003):(1)", "(1000003):(1)", 2), ("(8,7,1001):(1,8,56)", "(8,7,1001):(1,8008,8)", 2),
+             ("(64,3,333):(1,64,192)", "(64,3,333):(1,21312,64)", 4), ("(5000,3):(1,5000)", "(5000,3):(3,1)", 16),
+             ("(128,50,7):(1,128,6400)", "(128,50,7):(1,896,128)", 2)]
+    for eb, nb in [(2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (8, 2), (1, 16)]:
+        a, bt = 16 // eb * 37 + (16 // eb) * 3, 5
+        cases.append((f"({nb},{a},{bt}):({a},1,{a * nb})", f"({nb},{a},{bt}):(1,{nb},{a * nb})", eb))
+    ran = 0
+    for ci, (ts, td, eb) in enumerate(cases):
+        ns, nd = lr.parse(ts).cosize, lr.parse(td).cosize
+        n = O.size(O.parse(ts))
+        ns, nd = max(ns, n), max(nd, n)
+        src = np.random.default_rng(210 + ci).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for lanes in (64, 128, 256):
+            for nt in ("0", "1"):
+                knobs.t.clear()
+                knobs.set(workgroup_lanes=lanes)
+                knobs.policy(nt)
+                p = plan(ts, ns, td, nd, eb)
+                say("workgroup lanes", lanes, ts, "eb", eb, "nt", nt, p["path"], "block", p["block"], "grid", p["grid"])
+                assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, lanes, nt)
+                if p["block"] == lanes and lanes != 256:
+                    ran += 1
+    assert ran >= 32  # 64 and 128 lanes, both policies: 2 vector / generic cases and 7 interleaves
 
 
 def test_byte_transpose_chunks(dev, knobs):

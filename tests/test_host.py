@@ -712,7 +712,8 @@ def test_tuning_overrides_are_checked():
     for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 10},
                 {"units_per_lane": 2}, {"vector_order": 4}, {"gather_chunks": 3}, {"direct_loads": 2},
                 {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2},
-                {"chunk_bytes": 4}, {"chunk_bytes": 0}):
+                {"chunk_bytes": 4}, {"chunk_bytes": 0}, {"workgroup_lanes": 32}, {"workgroup_lanes": 512},
+                {"batch_swizzle": 16}, {"batch_order": 2}):
         with pytest.raises(lr.LayoutRemapError) as e:
             lr.copy_plan(*args, tuning=bad)
         assert e.value.code == lr.binding.ERR_INVALID, bad
@@ -1146,3 +1147,33 @@ def test_plan_cache_returns_the_same_plans():
     for k in range(40):
         lr.copy_plan(f"({64 + k},64):(64,1)", (64 + k) * 64, f"({64 + k},64):(1,{64 + k})", (64 + k) * 64, 4)
     assert lr.copy_plan(*args) == first
+
+
+def test_workgroup_lanes_plan():
+    """workgroup_lanes: 64, 128 or 256 lanes per workgroup on the vector/generic kernel with
+    one unit per lane and on the narrow interleave; the grid (and the interleave's tile)
+    follow; tiles of atoms and 64-bit copies keep 256.  The planner takes one wavefront
+    for the interleave and single contiguous runs from a 64 MiB footprint."""
+    w = W.full("interleave")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    base = lr.copy_plan(*args)
+    for lanes in (64, 128, 256):
+        p = lr.copy_plan(*args, tuning={"workgroup_lanes": lanes})
+        assert p["path"] == "interleave" and p["block"] == lanes
+        assert p["tile_a"] * base["block"] == base["tile_a"] * lanes and p["grid"] * lanes == base["grid"] * base["block"]
+    n = 3 * (1 << 20) + 77
+    for lanes in (64, 128):
+        p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16, tuning={"workgroup_lanes": lanes})
+        assert p["path"] in ("vector", "generic") and p["block"] == lanes and p["grid"] == -(-n // lanes)
+    r = W.full("retile")
+    p = lr.copy_plan(r.src_layout, r.src_elems, r.dst_layout, r.dst_elems, 2, tuning={"workgroup_lanes": 64})
+    assert p["vector_order"] == 3 and p["block"] == 256
+    p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16, flags=lr.COPY_WIDE_INDEX, tuning={"workgroup_lanes": 64})
+    assert p["wide"] and p["block"] == 256
+    assert base["block"] == 64 and lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16)["block"] == 64  # 96 MiB moved
+    small = 1 << 19  # 16 MiB moved
+    assert lr.copy_plan(f"{small}:1", small, f"{small}:1", small, 16)["block"] == 256
+    s = W.small("interleave")
+    assert lr.copy_plan(s.src_layout, s.src_elems, s.dst_layout, s.dst_elems, 2)["block"] == 256
+    perm = ("(2048,1024,64):(1,2048,2097152)", 1 << 27, "(2048,1024,64):(1,131072,2048)", 1 << 27, 2)
+    assert lr.copy_plan(*perm)["block"] == 256  # three modes

@@ -412,8 +412,9 @@ typedef struct {
                               candidate list (lr_plan.batch_swizzle shows it) */
   int32_t batch_order;     /* batched: 0 a-blocks fastest over lanes, 1 b-blocks fastest */
   int32_t workgroup_lanes; /* vector/generic path with one 16-byte or narrower unit per lane (not
-                              tiles of atoms, not 64-bit indices) and the interleave with one
-                              destination chunk per lane: 64, 128 or 256 lanes per workgroup */
+                              64-bit indices) and its tiles of atoms, the interleave with one
+                              destination chunk per lane and the channel shuffle (both
+                              directions, chunk form): 64, 128 or 256 lanes per workgroup */
   int32_t reserved[1];     /* must be -1 or 0 */
 } lr_copy_tuning;
 

@@ -587,12 +587,12 @@ struct AtomArgs {
   WriteCount wcnt;
 };
 
-template <int K, bool LNT, bool SNT>
-__global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
+template <int K, bool LNT, bool SNT, int LANES = 256>
+__global__ void __launch_bounds__(LANES) k_atoms(AtomArgs t) {
   constexpr int T = (int)atom_tile(K);
   constexpr int RUN = T * K;         // chunks in one run of T atoms
-  constexpr int CH = T * RUN, PER = (CH + 255) / 256;
-  constexpr bool WHOLE = CH % 256 == 0;  // else the last round of lanes is partial
+  constexpr int CH = T * RUN, PER = (CH + LANES - 1) / LANES;
+  constexpr bool WHOLE = CH % LANES == 0;  // else the last round of lanes is partial
   __shared__ U4 tile[CH];
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
@@ -604,7 +604,7 @@ __global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
   U4 v[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int L = k * 256 + tid;                 // source order: run j, atom i, chunk q
+    const int L = k * LANES + tid;                 // source order: run j, atom i, chunk q
     const int j = L / RUN, i = (L % RUN) / K, q = L % K;
     const uint32_t a = ta * T + i, b = tb * T + j;
     if ((WHOLE || L < CH) && a < t.ext_a && b < t.ext_b)
@@ -612,7 +612,7 @@ __global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int L = k * 256 + tid;
+    const int L = k * LANES + tid;
     const int j = L / RUN, i = (L % RUN) / K, q = L % K;
     if ((WHOLE || L < CH) && ta * T + i < t.ext_a && tb * T + j < t.ext_b) tile[(j * T + (i ^ (j % T))) * K + q] = v[k];
   }
@@ -620,7 +620,7 @@ __global__ void __launch_bounds__(256) k_atoms(AtomArgs t) {
   const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, -1, kBufferWord3);
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int S = k * 256 + tid;                 // destination order: run i, atom j, chunk q
+    const int S = k * LANES + tid;                 // destination order: run i, atom j, chunk q
     const int i = S / RUN, j = (S % RUN) / K, q = S % K;
     const uint32_t a = ta * T + i, b = tb * T + j;
     if ((WHOLE || S < CH) && a < t.ext_a && b < t.ext_b) {
@@ -1496,7 +1496,7 @@ __device__ __forceinline__ void store16(char* base, size_t byte_off, const C& v,
 // stride 1): image layouts such as NHWC <-> NCHW with few channels, where neither
 // side has a contiguous run of 16 bytes per channel on the interleaved side.  The
 // pairing is that of [print_layout page, section 4.2], for any C from 2 to 8.
-// Lane l of a workgroup owns V = 16/EB consecutive pixels of all C channels: C
+// Lane l of a workgroup (L lanes) owns V = 16/EB consecutive pixels of all C channels: C
 // chunks on either side, exchanged by a C x V transpose in registers.  On the
 // interleaved side those C chunks are contiguous per lane, so that side goes
 // through LDS: a wave instruction then moves 64 consecutive chunks on both sides.
@@ -1504,12 +1504,12 @@ __device__ __forceinline__ void store16(char* base, size_t byte_off, const C& v,
 //     into LDS, C LDS reads per lane, stores of one chunk per plane;
 //   INTERLEAVE == true: loads of one chunk per plane, C LDS writes per lane,
 //     stores of the contiguous interleaved block.
-template <int EB, int C, bool INTERLEAVE, bool NT>
-__global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
+template <int EB, int C, bool INTERLEAVE, bool NT, int L = 256>
+__global__ void __launch_bounds__(L) k_chan(ChanArgs t) {
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
   using Ch = Chunk<T, V>;
-  __shared__ Ch lds[256 * C];
+  __shared__ Ch lds[L * C];
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
@@ -1518,9 +1518,9 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
   const uint32_t tile = blk - r * t.tiles;
   uint32_t bs, bd;
   batch_offsets(t.batch, r, &bs, &bd);
-  const uint32_t p0 = tile * (256 * V);  // the workgroup's first pixel
+  const uint32_t p0 = tile * (L * V);  // the workgroup's first pixel
   const uint32_t left = (t.pixels - p0) / V;
-  const uint32_t nblk = left < 256u ? left : 256u;  // pixel blocks of V in this workgroup
+  const uint32_t nblk = left < (uint32_t)L ? left : (uint32_t)L;  // pixel blocks of V in this workgroup
   const uint32_t l = threadIdx.x;
   const bool mine = l < nblk;
 
@@ -1534,10 +1534,10 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
     Ch tmp[C];
 #pragma unroll
     for (int j = 0; j < C; ++j)
-      if (l + 256u * j < nblk * C) tmp[j] = gload<NT, Ch>(sb + (size_t)(l + 256u * j) * 16);
+      if (l + (uint32_t)L * j < nblk * C) tmp[j] = gload<NT, Ch>(sb + (size_t)(l + (uint32_t)L * j) * 16);
 #pragma unroll
     for (int j = 0; j < C; ++j)
-      if (l + 256u * j < nblk * C) lds[slot(l + 256u * j)] = tmp[j];
+      if (l + (uint32_t)L * j < nblk * C) lds[slot(l + (uint32_t)L * j)] = tmp[j];
     __syncthreads();
     if (!mine) return;
     Ch in[C], out[C];
@@ -1565,9 +1565,9 @@ __global__ void __launch_bounds__(256) k_chan(ChanArgs t) {
     const size_t db = (size_t)(p0 * C + bd) * EB;
 #pragma unroll
     for (int j = 0; j < C; ++j)
-      if (l + 256u * j < nblk * C) {
-        store16<NT>(dst, db + (size_t)(l + 256u * j) * 16, lds[l + 256u * j], t.bufst);
-        count_store(t.wcnt, t.dst, dst + db + (size_t)(l + 256u * j) * 16, 16);
+      if (l + (uint32_t)L * j < nblk * C) {
+        store16<NT>(dst, db + (size_t)(l + (uint32_t)L * j) * 16, lds[l + (uint32_t)L * j], t.bufst);
+        count_store(t.wcnt, t.dst, dst + db + (size_t)(l + (uint32_t)L * j) * 16, 16);
       }
   }
 }
@@ -2000,17 +2000,22 @@ static bool launch_batched(const BatchedArgs& a, int eb, bool nt, unsigned grid,
   }
 }
 
-// One kernel per atom size K = KK..32 chunks.
+// One kernel per atom size K = KK..32 chunks, with 64, 128 or 256 lanes.
 template <int KK, bool LNT, bool SNT>
-static bool launch_atoms_nt(const AtomArgs& a, int K, unsigned grid, hipStream_t st) {
+static bool launch_atoms_nt(const AtomArgs& a, int K, int lanes, unsigned grid, hipStream_t st) {
   if constexpr (KK > 32) {
     return false;
   } else {
     if (K == KK) {
-      hipLaunchKernelGGL((k_atoms<KK, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
+      if (lanes == 64)
+        hipLaunchKernelGGL((k_atoms<KK, LNT, SNT, 64>), dim3(grid), dim3(64), 0, st, a);
+      else if (lanes == 128)
+        hipLaunchKernelGGL((k_atoms<KK, LNT, SNT, 128>), dim3(grid), dim3(128), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_atoms<KK, LNT, SNT>), dim3(grid), dim3(256), 0, st, a);
       return true;
     }
-    return launch_atoms_nt<KK + 1, LNT, SNT>(a, K, grid, st);
+    return launch_atoms_nt<KK + 1, LNT, SNT>(a, K, lanes, grid, st);
   }
 }
 
@@ -2044,10 +2049,10 @@ static bool launch_atoms(const Plan& p, const GenericArgs& g, unsigned grid, hip
   a.sws = g.sws;
   a.swd = g.swd;
   a.bufst = g.bufst;
-  if (p.nt_ld && p.nt) return launch_atoms_nt<2, true, true>(a, K, grid, st);
-  if (p.nt_ld) return launch_atoms_nt<2, true, false>(a, K, grid, st);
-  if (p.nt) return launch_atoms_nt<2, false, true>(a, K, grid, st);
-  return launch_atoms_nt<2, false, false>(a, K, grid, st);
+  if (p.nt_ld && p.nt) return launch_atoms_nt<2, true, true>(a, K, p.block, grid, st);
+  if (p.nt_ld) return launch_atoms_nt<2, true, false>(a, K, p.block, grid, st);
+  if (p.nt) return launch_atoms_nt<2, false, true>(a, K, p.block, grid, st);
+  return launch_atoms_nt<2, false, false>(a, K, p.block, grid, st);
 }
 
 template <int UB, bool LNT, bool SNT>
@@ -2225,10 +2230,14 @@ static bool launch_interleave_n(const InterleaveArgs& a, int nb, int lanes, unsi
 }
 
 template <int EB, int CC, bool INTERLEAVE, bool NT>
-static bool launch_chan_one(const ChanArgs& a, bool elem, unsigned grid, hipStream_t st) {
+static bool launch_chan_one(const ChanArgs& a, bool elem, int lanes, unsigned grid, hipStream_t st) {
   if constexpr (chan_supported(EB, CC)) {
     if (elem)
       hipLaunchKernelGGL((k_chan_win<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
+    else if (lanes == 64)
+      hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT, 64>), dim3(grid), dim3(64), 0, st, a);
+    else if (lanes == 128)
+      hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT, 128>), dim3(grid), dim3(128), 0, st, a);
     else
       hipLaunchKernelGGL((k_chan<EB, CC, INTERLEAVE, NT>), dim3(grid), dim3(256), 0, st, a);
     return true;
@@ -2237,24 +2246,27 @@ static bool launch_chan_one(const ChanArgs& a, bool elem, unsigned grid, hipStre
 }
 
 template <int EB, bool INTERLEAVE, bool NT>
-static bool launch_chan_c(const ChanArgs& a, int c, bool elem, unsigned grid, hipStream_t st) {
+static bool launch_chan_c(const ChanArgs& a, int c, bool elem, int lanes, unsigned grid, hipStream_t st) {
   switch (c) {
-    case 2: return launch_chan_one<EB, 2, INTERLEAVE, NT>(a, elem, grid, st);
-    case 3: return launch_chan_one<EB, 3, INTERLEAVE, NT>(a, elem, grid, st);
-    case 4: return launch_chan_one<EB, 4, INTERLEAVE, NT>(a, elem, grid, st);
-    case 5: return launch_chan_one<EB, 5, INTERLEAVE, NT>(a, elem, grid, st);
-    case 6: return launch_chan_one<EB, 6, INTERLEAVE, NT>(a, elem, grid, st);
-    case 7: return launch_chan_one<EB, 7, INTERLEAVE, NT>(a, elem, grid, st);
-    case 8: return launch_chan_one<EB, 8, INTERLEAVE, NT>(a, elem, grid, st);
+    case 2: return launch_chan_one<EB, 2, INTERLEAVE, NT>(a, elem, lanes, grid, st);
+    case 3: return launch_chan_one<EB, 3, INTERLEAVE, NT>(a, elem, lanes, grid, st);
+    case 4: return launch_chan_one<EB, 4, INTERLEAVE, NT>(a, elem, lanes, grid, st);
+    case 5: return launch_chan_one<EB, 5, INTERLEAVE, NT>(a, elem, lanes, grid, st);
+    case 6: return launch_chan_one<EB, 6, INTERLEAVE, NT>(a, elem, lanes, grid, st);
+    case 7: return launch_chan_one<EB, 7, INTERLEAVE, NT>(a, elem, lanes, grid, st);
+    case 8: return launch_chan_one<EB, 8, INTERLEAVE, NT>(a, elem, lanes, grid, st);
     default: return false;
   }
 }
 
 template <int EB>
-static bool launch_chan(const ChanArgs& a, int c, bool interleave, bool elem, bool nt, unsigned grid, hipStream_t st) {
+static bool launch_chan(const ChanArgs& a, int c, bool interleave, bool elem, bool nt, int lanes, unsigned grid,
+                        hipStream_t st) {
   if (interleave)
-    return nt ? launch_chan_c<EB, true, true>(a, c, elem, grid, st) : launch_chan_c<EB, true, false>(a, c, elem, grid, st);
-  return nt ? launch_chan_c<EB, false, true>(a, c, elem, grid, st) : launch_chan_c<EB, false, false>(a, c, elem, grid, st);
+    return nt ? launch_chan_c<EB, true, true>(a, c, elem, lanes, grid, st)
+              : launch_chan_c<EB, true, false>(a, c, elem, lanes, grid, st);
+  return nt ? launch_chan_c<EB, false, true>(a, c, elem, lanes, grid, st)
+            : launch_chan_c<EB, false, false>(a, c, elem, lanes, grid, st);
 }
 
 template <int EB>
@@ -2418,7 +2430,7 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         a.bufst = p.bufst ? 1u : 0u;
         bool ok = false;
         // one element per lane unit (v == 1): the element-granular form
-        LR_DISPATCH_EB(p.eb, ok = launch_chan<EBV>(a, (int)p.m[cm].ext, il, p.v == 1, p.nt, grid, st));
+        LR_DISPATCH_EB(p.eb, ok = launch_chan<EBV>(a, (int)p.m[cm].ext, il, p.v == 1, p.nt, p.block, grid, st));
         if (!ok) return LR_ERR_PATH;
         return check_launch();
       }

@@ -679,7 +679,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
     p->vorder = knob(tun.vector_order, atoms ? 3 : 1);
     if (p->vorder == 3 && !atoms) p->vorder = 1;
     if (p->vorder == 3) {
-      p->block = 256;
+      p->block = knob(tun.workgroup_lanes, 256);
       p->a = aa;
       p->b = ab;
       p->tile_a = p->tile_b = at;
@@ -762,8 +762,9 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       // one wavefront per workgroup from a 64 MiB footprint: the (16,32,4096,128) head
       // interleave 162.4 -> 159.0-160.2 us back to back, a (16,64,4096,64) one with four
       // heads 24.3 -> 17.1 us
-      p->block = p->inarrow == 1 ? knob(tun.workgroup_lanes, big_footprint ? 64 : 256) : 256;
-      p->tile_a = p->inarrow == 2 ? 256 * V : p->inarrow ? p->block * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
+      p->block = p->inarrow == 1 ? knob(tun.workgroup_lanes, big_footprint ? 64 : 256)
+                 : p->inarrow == 2 ? knob(tun.workgroup_lanes, 256) : 256;
+      p->tile_a = p->inarrow == 2 ? p->block * V : p->inarrow ? p->block * (V / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * V;
       // the narrow variant's streaming stores as buffer stores with the nt and sc1
       // bits from the destination base (head interleave 6.27 -> 6.55 TB/s)
       p->bufst = p->inarrow != 0 && sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
@@ -792,7 +793,8 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       p->a = a;
       p->b = b;
       p->v = (int)V;
-      p->tile_a = 256 * V;  // pixels per workgroup (V per lane)
+      p->block = knob(tun.workgroup_lanes, 256);
+      p->tile_a = p->block * V;  // pixels per workgroup (V per lane)
       p->tile_b = C;
       p->bufst = sc1_ok && dst_span_bytes(*p) < (int64_t(1) << 32);
       int64_t batch = 1;
@@ -1212,9 +1214,9 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
           if (p.m[k].ss % v || p.m[k].sd % v) return bad();
       }
       if (p.n_units * v != prod) return bad();
-      // workgroup lanes: 64, 128 or 256 for one unit per lane with 32-bit indices
-      if (p.block != 256 && !((p.block == 64 || p.block == 128) && p.unroll == 1 && !p.wide && p.vorder != 3))
-        return bad();
+      // workgroup lanes: 64, 128 or 256 for one unit per lane with 32-bit indices (and
+      // for the tiles of atoms)
+      if (p.block != 256 && !((p.block == 64 || p.block == 128) && p.unroll == 1 && !p.wide)) return bad();
       if (p.vorder == 3) {  // tiles of atoms: see atom_tiles
         int a = -1, b = -1;
         int64_t T = 0;
@@ -1302,7 +1304,9 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (v * p.eb != 16 || p.m[p.a].ext % v || nb * p.eb > 16) return bad();
       // the kernel's per-lane unroll
       if (p.inarrow == 2) {  // channel shuffle: any NB it was built for, no swizzle
-        if (!chan_supported(p.eb, nb) || p.sw_s.b || p.sw_d.b || p.tile_a != 256 * v) return bad();
+        if (!chan_supported(p.eb, nb) || p.sw_s.b || p.sw_d.b || p.tile_a != p.block * v ||
+            (p.block != 64 && p.block != 128 && p.block != 256))
+          return bad();
       } else if (!is_pow2(nb) || p.tile_a != (p.inarrow ? p.block * (v / nb) : (nb >= 8 ? 1 : 8 / nb) * 256 * v) ||
                  (p.block != 256 && !(p.inarrow == 1 && (p.block == 64 || p.block == 128)))) {
         return bad();
@@ -1325,7 +1329,7 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
                    : LR_OK;
       if (v * p.eb != 16 || p.m[p.b].ext % v || p.m[p.a].sd % v || p.sw_s.b || p.sw_d.b) return bad();
       if (p.bufst && (dst_span_bytes(p) >> 32) != 0) return bad();
-      if (p.tile_a != 256 * v || p.tile_b != C) return bad();
+      if (p.tile_a != p.block * v || p.tile_b != C || (p.block != 64 && p.block != 128 && p.block != 256)) return bad();
       for (int k = 0; k < p.rank; ++k)
         if (k != p.a && k != p.b && (p.m[k].ss % v || p.m[k].sd % v)) return bad();
       return LR_OK;

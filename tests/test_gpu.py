@@ -1224,6 +1224,10 @@ def test_workgroup_lanes(dev, knobs):
     for eb, nb in [(2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (8, 2), (1, 16)]:
         a, bt = 16 // eb * 37 + (16 // eb) * 3, 5
         cases.append((f"({nb},{a},{bt}):({a},1,{a * nb})", f"({nb},{a},{bt}):(1,{nb},{a * nb})", eb))
+    # the channel shuffle, both directions: 3 and 4 channels, ragged pixel counts
+    for eb, c, px in [(2, 3, 8 * 700), (4, 3, 4 * 333), (1, 4, 16 * 301), (2, 5, 8 * 129)]:
+        nhwc, nchw = f"({c},{px},3):(1,{c},{c * px})", f"({c},{px},3):({px},1,{c * px})"
+        cases += [(nhwc, nchw, eb), (nchw, nhwc, eb)]
     ran = 0
     for ci, (ts, td, eb) in enumerate(cases):
         ns, nd = lr.parse(ts).cosize, lr.parse(td).cosize
@@ -1242,7 +1246,7 @@ def test_workgroup_lanes(dev, knobs):
                 assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, lanes, nt)
                 if p["block"] == lanes and lanes != 256:
                     ran += 1
-    assert ran >= 32  # 64 and 128 lanes, both policies: 2 vector / generic cases and 7 interleaves
+    assert ran >= 64  # 64 and 128 lanes, both policies: 2 vector / generic cases, 7 interleaves, 8 shuffles
 
 
 def test_byte_transpose_chunks(dev, knobs):

@@ -1167,7 +1167,7 @@ def test_workgroup_lanes_plan():
         assert p["path"] in ("vector", "generic") and p["block"] == lanes and p["grid"] == -(-n // lanes)
     r = W.full("retile")
     p = lr.copy_plan(r.src_layout, r.src_elems, r.dst_layout, r.dst_elems, 2, tuning={"workgroup_lanes": 64})
-    assert p["vector_order"] == 3 and p["block"] == 256
+    assert p["vector_order"] == 3 and p["block"] == 64
     p = lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16, flags=lr.COPY_WIDE_INDEX, tuning={"workgroup_lanes": 64})
     assert p["wide"] and p["block"] == 256
     assert base["block"] == 64 and lr.copy_plan(f"{n}:1", n, f"{n}:1", n, 16)["block"] == 64  # 96 MiB moved

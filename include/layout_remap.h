@@ -390,7 +390,8 @@ typedef struct {
                               lr_plan.vector_order) */
   int32_t interleave_form; /* interleave: 0 one chunk per lane per head, 1 one destination
                               chunk per lane from narrow loads, 2 the channel shuffle */
-  int32_t tile_shape;      /* transpose: 0..6, the tile shapes of lr_plan.tile_a/tile_b */
+  int32_t tile_shape;      /* transpose: 0..7, the tile shapes of lr_plan.tile_a/tile_b (16-byte
+                              chunks a x b: 16x16, 32x16, 16x32, 32x32, 32x8, 64x8, 64x16, 8x8) */
   int32_t tile_order;      /* transpose: 0..9, as lr_plan.order (5..9 not with pipeline_tiles) */
   int32_t element_tiles;   /* transpose: 0 chunk tiles, 1 element-granular tiles */
   int32_t direct_loads;    /* staged and LDS transpose: 0 through registers, 1 global -> LDS */

@@ -2168,6 +2168,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, int 
       LR_TSHAPE_CASE(4)
       LR_TSHAPE_CASE(5)
       LR_TSHAPE_CASE(6)
+      LR_TSHAPE_CASE(7)
       default: break;
     }
 #undef LR_TSHAPE_CASE

@@ -137,7 +137,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
   };
   if (!in(t.load_policy, {0, 2}) || !in(t.store_policy, {0, 2, 18}) || !in(t.units_per_lane, {1, 4}) ||
       !in(t.vector_order, {0, 1, 2, 3}) || !in(t.interleave_form, {0, 1, 2}) ||
-      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6}) || !in(t.tile_order, {0, 1, 2, 3, 4, 5, 6, 7, 8, 9}) ||
+      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6, 7}) || !in(t.tile_order, {0, 1, 2, 3, 4, 5, 6, 7, 8, 9}) ||
       !in(t.element_tiles, {0, 1}) || !in(t.direct_loads, {0, 1}) || !in(t.gather_chunks, {1, 2, 4, 8, 16, 32}))
     return false;
   if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;

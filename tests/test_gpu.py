@@ -772,7 +772,7 @@ def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
 # ---------------------------------------------------------------------------
 # Tuning variants chosen at plan time (tile shapes, narrow-load interleave)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_transpose_tile_shapes(dev, knobs, shape):
     knobs.set(tile_shape=shape)
     for ts, td, n, eb in [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
@@ -842,7 +842,7 @@ def test_transpose_streaming_store_forms(dev, knobs, tsc1):
              ("(48,80):(80,1)", "(48,80):(1,48)", 16),
              (cm.src_layout, cm.dst_layout, 2)]
     ran = 0
-    for shape in range(7):
+    for shape in range(8):
         knobs.set(tile_shape=shape)
         for ci, (ts, td, eb) in enumerate(cases):
             n = O.size(O.parse(ts))
@@ -1261,7 +1261,7 @@ def test_byte_transpose_chunks(dev, knobs):
         dst = np.full(nd, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), 1)
         for cb in (8, 16):
-            for shape in range(7):
+            for shape in range(8):
                 for direct in (0, 1):
                     knobs.t.clear()
                     knobs.set(chunk_bytes=cb, tile_shape=shape, direct_loads=direct)

@@ -709,7 +709,7 @@ def test_plan_store_policy():
 def test_tuning_overrides_are_checked():
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
-    for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 7}, {"tile_order": 10},
+    for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 8}, {"tile_order": 10},
                 {"units_per_lane": 2}, {"vector_order": 4}, {"gather_chunks": 3}, {"direct_loads": 2},
                 {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2},
                 {"chunk_bytes": 4}, {"chunk_bytes": 0}, {"workgroup_lanes": 32}, {"workgroup_lanes": 512},

@@ -130,6 +130,25 @@ def _time_copies(lr, torch, pairs, Ls, Ld, eb, steps, warmup, flags=0, tuning=No
     return wall, ev0.elapsed_time(ev1) / steps
 
 
+def _time_torch_copies(torch, pairs, steps, warmup):
+    """torch's own device-to-device `dst.copy_(src)` of each pair's bytes, back to back
+    over the rotating pairs, timed like _time_copies (HIP events on the current
+    stream): the same-box copy the library's rates are also compared with."""
+    for i in range(warmup):
+        s, d = pairs[i % len(pairs)]
+        d.copy_(s)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        s, d = pairs[i % len(pairs)]
+        d.copy_(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
 def _per_launch(lr, torch, pairs, Ls, Ld, eb, launches, flags=0, rotate=True, tuning=None):
     """Kernel time of each launch (HIP events around it on the launch stream), in us,
     sorted: rotating over the buffer pairs (cold: nothing cached from the previous
@@ -179,7 +198,9 @@ def measure(lr, torch, dev, name, W, steps, warmup, flags=0, first_src=None):
     warm = _per_launch(lr, torch, pairs, w.src_layout, w.dst_layout, eb, steps, flags, rotate=False)
     n16 = nbytes // 2 // 16  # the same bytes each way, as 16-byte units
     _, copy_ms = _time_copies(lr, torch, pairs, f"{n16}:1", f"{n16}:1", 16, steps, warmup)
-    del pairs
+    whole = [(s_[:n16 * 16], d_[:n16 * 16]) for s_, d_ in pairs]
+    torch_ms = _time_torch_copies(torch, whole, steps, warmup)
+    del pairs, whole
     torch.cuda.empty_cache()
     gbps = nbytes / (kern_ms * 1e-3) / 1e9
     copy_gbps = nbytes / (copy_ms * 1e-3) / 1e9
@@ -193,6 +214,8 @@ def measure(lr, torch, dev, name, W, steps, warmup, flags=0, first_src=None):
             "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
             "copy_GBps": round(copy_gbps, 1),
             "frac_of_copy": round(gbps / copy_gbps, 4),
+            "torch_copy_GBps": round(nbytes / (torch_ms * 1e-3) / 1e9, 1),
+            "frac_of_torch_copy": round(gbps / (nbytes / (torch_ms * 1e-3) / 1e9), 4),
             "us_cold_median": round(cold[len(cold) // 2], 2),
             "us_cold_best": round(cold[0], 2),
             "us_warm_median": round(wm, 2),
@@ -706,6 +729,8 @@ def main():
             "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
             "copy_kernel_GBps": e["copy_GBps"],
             "kernel_frac_of_copy_kernel": e["frac_of_copy"],
+            "torch_copy_GBps": e["torch_copy_GBps"],
+            "kernel_frac_of_torch_copy": e["frac_of_torch_copy"],
             "buffers": "rotating pairs, >= 1 GiB in total",
             "kernel_us": {"timed_region_mean": e["us"], "cold_median": e["us_cold_median"],
                           "cold_best": e["us_cold_best"], "warm_median": e["us_warm_median"],

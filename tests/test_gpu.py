@@ -447,7 +447,9 @@ def test_copy_random_pairs(dev, knobs):
                "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
                "transpose_reads": rng.choice([-1, 0, 1]),
                "chunk_bytes": random.Random(i).choice([-1, -1, 8, 16]),
-               "workgroup_lanes": random.Random(1000 + i).choice([-1, 64, 128, 256])}
+               "workgroup_lanes": random.Random(1000 + i).choice([-1, 64, 128, 256]),
+               "batch_swizzle": random.Random(2000 + i).choice([-1, -1] + list(range(16))),
+               "batch_order": random.Random(3000 + i).choice([-1, 0, 1])}
         knobs.t.clear()
         knobs.set(**env)
         if i % 50 == 0:

@@ -342,12 +342,39 @@ def launch_run(lr, torch, W, specs, reps: int = 12, back_to_back: int = 0):
         torch.cuda.empty_cache()
 
 
-def atom_sweep(lr, torch, steps: int = 20):
+def atom_sweep(lr, torch, mode: str = "orders", steps: int = 20):
     """(16,s,h,d) -> (16,h,s,d) bf16 head splits for head dims of 32-512 bytes: tiles
-    of atoms (vector order 3) against the source order (1), back to back over
-    rotating buffers, beside a contiguous copy of the same bytes.  One JSON line per
-    head dim.  An order the planner cannot take falls back (its plan is printed)."""
+    of atoms (vector order 3) against the source order (1) (mode "orders"), or tiles of
+    atoms in 128- against 256-lane workgroups, with the 4096^2 retile too (mode
+    "lanes"), back to back over rotating buffers, beside a contiguous copy of the same
+    bytes.  One JSON line per head dim.  An order the planner cannot take falls back
+    (its plan is printed)."""
     dev = torch.device("cuda:0")
+    if mode == "lanes":
+        import workloads as W
+        r = W.full("retile")
+        cases = [("retile", r.src_layout, r.dst_layout, r.src_elems)]
+        for d, s, h in ((16, 4096, 32), (24, 4096, 32), (32, 4096, 32), (48, 4096, 32), (64, 4096, 32),
+                        (96, 4096, 32), (128, 4096, 32), (192, 4096, 16), (256, 4096, 16)):
+            cases.append((f"head dim {d}", f"(16,{s},{h},{d}):({s * h * d},{h * d},{d},1)",
+                          f"(16,{s},{h},{d}):({h * s * d},{d},{s * d},1)", 16 * s * h * d))
+        for name, ts, td, n in cases:
+            pairs = _pairs(torch, dev, n * 2, n * 2)
+            res = {}
+            for rep in range(2):
+                for lanes in (128, 256):
+                    t = {"vector_order": 3, "workgroup_lanes": lanes}
+                    p = lr.copy_plan(ts, n, td, n, 2, tuning=t)
+                    _, ms = _time_copies(lr, torch, pairs, ts, td, 2, steps, 3, tuning=t)
+                    res.setdefault(lanes, []).append(round(ms * 1e3, 2))
+            n16 = n * 2 // 16
+            _, cms = _time_copies(lr, torch, pairs, f"{n16}:1", f"{n16}:1", 16, steps, 3)
+            print(json.dumps({"case": name, "atom_bytes": None if name == "retile" else 2 * int(name.split()[-1]),
+                              "vector_order": p["vector_order"], "us_128": res[128], "us_256": res[256],
+                              "copy_us": round(cms * 1e3, 2)}), flush=True)
+            del pairs
+            torch.cuda.empty_cache()
+        return
     for d, s, h in ((16, 4096, 32), (24, 4096, 32), (40, 4096, 32), (48, 4096, 32), (64, 4096, 32), (80, 4096, 32),
                     (96, 4096, 32), (112, 4096, 32), (128, 4096, 32), (160, 4096, 16), (192, 4096, 16),
                     (256, 4096, 16)):
@@ -638,8 +665,9 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--groups-of", type=int, default=0, help="with --summarize-trace: dispatches per launch group")
     ap.add_argument("--launch", action="append", metavar="NAME[:JSON]")
-    ap.add_argument("--atom-sweep", action="store_true",
-                    help="head splits for head dims of 32-512 bytes: tiles of atoms against the source order")
+    ap.add_argument("--atom-sweep", nargs="?", const="orders", choices=["orders", "lanes"],
+                    help="head splits for head dims of 32-512 bytes: tiles of atoms against the source order, "
+                         "or in 128- against 256-lane workgroups")
     ap.add_argument("--layout-sweep", action="store_true",
                     help="common layout transforms (transposes of every element size, batched small "
                          "matrices, NCHW <-> NHWC, 3-D permutes, row gathers) against a same-size copy")
@@ -681,7 +709,7 @@ def main():
         launch_run(lr, torch, W, args.launch, back_to_back=args.back_to_back)
         return
     if args.atom_sweep:
-        atom_sweep(lr, torch)
+        atom_sweep(lr, torch, args.atom_sweep)
         return
     if args.layout_sweep:
         layout_sweep(lr, torch)

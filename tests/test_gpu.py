@@ -1319,6 +1319,38 @@ def test_batched_small_matrices(dev, knobs):
         assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), ts
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("count", [4194304, 8388609])
+def test_full_batched(dev, count):
+    """The batched path at its largest: 2^30 fp16 elements (16 x 16 matrices, 2 GiB each
+    way), and 2^31 + 256 elements (4 GiB each way), which the library cuts into two
+    launches of 32-bit offsets.  A million sampled outputs against the oracle's own
+    evaluation, and the whole destination as a permutation of the source's 2-byte
+    values (the histograms of both agree)."""
+    ts, td = f"(16,16,{count}):(16,1,256)", f"(16,16,{count}):(1,16,256)"
+    n = 256 * count
+    p = plan(ts, n, td, n, 2)
+    assert p["path"] == "batched" and p["blocks"] == (1 if n < (1 << 31) else 2)
+    say("full batched", count, "generate")
+    g = torch.Generator(device=dev)
+    g.manual_seed(count)
+    s = torch.randint(0, 256, (2 * n,), dtype=torch.uint8, device=dev, generator=g)
+    d = torch.zeros(2 * n, dtype=torch.uint8, device=dev)
+    say("full batched", count, "copy")
+    copy_(s, ts, d, td, 2)
+    torch.cuda.synchronize()
+    src = s.cpu().numpy()
+    got = d.cpu().numpy()
+    del s, d
+    torch.cuda.empty_cache()
+    say("full batched", count, "compare")
+    ks = np.random.default_rng(11).integers(0, n, 1 << 20, dtype=np.int64)
+    assert O.copy_sampled_check(src, O.parse(ts), got, O.parse(td), 2, ks) == 0
+    hs = np.bincount(src.view(np.uint16), minlength=1 << 16)
+    hg = np.bincount(got.view(np.uint16), minlength=1 << 16)
+    assert np.array_equal(hs, hg)
+
+
 def test_batched_write_counts(dev):
     """Every destination element of a batched copy is stored exactly once."""
     for ci, (ts, td, eb) in enumerate(_batched_cases()):

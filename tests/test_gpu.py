@@ -726,7 +726,7 @@ def test_channel_shuffle_destination_beyond_4_gib(dev):
 @pytest.mark.parametrize("nt", ["0", "1"])
 def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
     """lr_layout_copy allocates nothing and records no memset, so captured copies
-    (eight paths in one graph, with plain or streaming accesses, the latter with the
+    (eight copies on six paths in one graph, with plain or streaming accesses, the latter with the
     sc1 buffer stores) replay correctly; each replay is checked after eager work has
     changed the sources."""
     knobs.policy(nt)

@@ -414,8 +414,10 @@ typedef struct {
   int32_t batch_order;     /* batched: 0 a-blocks fastest over lanes, 1 b-blocks fastest */
   int32_t workgroup_lanes; /* vector/generic path with one 16-byte or narrower unit per lane (not
                               64-bit indices) and its tiles of atoms, the interleave with one
-                              destination chunk per lane and the channel shuffle (both
-                              directions, chunk form): 64, 128 or 256 lanes per workgroup */
+                              destination chunk per lane, the channel shuffle (both
+                              directions, chunk form) and the staged gather (raised to the
+                              16-byte destination chunks of one tile where that is more):
+                              64, 128 or 256 lanes per workgroup */
   int32_t reserved[1];     /* must be -1 or 0 */
 } lr_copy_tuning;
 

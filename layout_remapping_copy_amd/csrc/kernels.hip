@@ -1727,9 +1727,11 @@ struct StagedArgs {
 // layout skips the pad).  A workgroup stages the whole 16-byte-aligned source
 // footprint of K tiles in LDS with 16-byte loads (pad words included: DRAM
 // fetches them with their lines anyway), then each lane builds 16-byte dst chunks
-// by gathering elements from LDS and stores them contiguously.
-template <int EB, bool NT, bool DL>
-__global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
+// by gathering elements from LDS and stores them contiguously.  L lanes per
+// workgroup (64, 128 or 256).
+template <int EB, bool NT, bool DL, int L = 256>
+__global__ void __launch_bounds__(L) k_staged(StagedArgs t) {
+  static_assert(L == 64 || L == 128 || L == 256, "64, 128 or 256 lanes");
   using T = typename Raw<EB>::T;
   constexpr int V = 16 / EB;
   using C = Chunk<T, V>;
@@ -1760,26 +1762,26 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
     // consecutive chunks, so the wave's LDS base is the chunk of its lane 0.  No
     // registers hold the data, so every load of the footprint is issued at once.
     const uint32_t lane = threadIdx.x & 63u;
-    for (uint32_t idx = threadIdx.x; idx < nload + lane; idx += 256) {
+    for (uint32_t idx = threadIdx.x; idx < nload + lane; idx += L) {
       const uint32_t base = __builtin_amdgcn_readfirstlane(idx - lane);
       size_t b = 0;
       if (chunk_ok(idx, &b)) load_to_lds16<NT>(src + b, lds + base);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS writes have landed
   } else {
-    for (uint32_t i0 = threadIdx.x; i0 < nload; i0 += 1024) {
+    for (uint32_t i0 = threadIdx.x; i0 < nload; i0 += 4 * L) {
       size_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
-      const bool k0 = chunk_ok(i0, &b0), k1 = chunk_ok(i0 + 256, &b1), k2 = chunk_ok(i0 + 512, &b2),
-                 k3 = chunk_ok(i0 + 768, &b3);
+      const bool k0 = chunk_ok(i0, &b0), k1 = chunk_ok(i0 + L, &b1), k2 = chunk_ok(i0 + 2 * L, &b2),
+                 k3 = chunk_ok(i0 + 3 * L, &b3);
       uint4 v0, v1, v2, v3;
       if (k0) v0 = gload<NT, uint4>(src + b0);
       if (k1) v1 = gload<NT, uint4>(src + b1);
       if (k2) v2 = gload<NT, uint4>(src + b2);
       if (k3) v3 = gload<NT, uint4>(src + b3);
       if (k0) lds[i0] = v0;
-      if (k1) lds[i0 + 256] = v1;
-      if (k2) lds[i0 + 512] = v2;
-      if (k3) lds[i0 + 768] = v3;
+      if (k1) lds[i0 + L] = v1;
+      if (k2) lds[i0 + 2 * L] = v2;
+      if (k3) lds[i0 + 3 * L] = v3;
     }
   }
   __syncthreads();
@@ -1787,8 +1789,8 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   // Gather grouping: the 32-lane slice q = idx / 32 covers 32 / cps tiles x cps
   // chunks of each (tile (q / slices) * (32 / cps) + l / cps, chunk (q % slices) * cps
   // + l % cps, l = idx % 32, slices = cpt / cps); the planner picks cps from the LDS
-  // bank model.  slices divides 8, so this lane's chunk position is the same in
-  // every round of 256 jobs.
+  // bank model.  slices divides L / 32, so this lane's chunk position is the same
+  // in every round of L jobs.
   const uint32_t slice_shift = t.cpt_shift - t.cps_shift, g_shift = 5u - t.cps_shift;
   const uint32_t c = (((threadIdx.x >> 5) & ((1u << slice_shift) - 1u)) << t.cps_shift) +
                      (threadIdx.x & ((1u << t.cps_shift) - 1u));
@@ -1805,7 +1807,7 @@ __global__ void __launch_bounds__(256) k_staged(StagedArgs t) {
   }
   const T* ldsT = (const T*)lds;
   const uint32_t nstore = t.K * t.cpt;
-  for (uint32_t idx = threadIdx.x; idx < nstore; idx += 256) {
+  for (uint32_t idx = threadIdx.x; idx < nstore; idx += L) {
     const uint32_t kk = (((idx >> 5) >> slice_shift) << g_shift) + ((idx & 31u) >> t.cps_shift);
     uint32_t tile = t0 + kk;
     if (tile >= t.T) continue;
@@ -1981,6 +1983,17 @@ static void fill_batch(BatchArg* b, const Plan& p, int skip0, int skip1, int ski
     b->ss[r] = (uint32_t)p.m[k].ss;
     b->sd[r] = (uint32_t)p.m[k].sd;
   }
+}
+
+// The staged gather in 64-, 128- or 256-lane workgroups.
+template <int EB, bool NT, bool DL>
+static void launch_staged_l(const StagedArgs& a, int lanes, unsigned grid, size_t shm, hipStream_t st) {
+  if (lanes == 64)
+    hipLaunchKernelGGL((k_staged<EB, NT, DL, 64>), dim3(grid), dim3(64), shm, st, a);
+  else if (lanes == 128)
+    hipLaunchKernelGGL((k_staged<EB, NT, DL, 128>), dim3(grid), dim3(128), shm, st, a);
+  else
+    hipLaunchKernelGGL((k_staged<EB, NT, DL, 256>), dim3(grid), dim3(256), shm, st, a);
 }
 
 template <int EB>
@@ -2514,14 +2527,14 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
       const size_t shm = (size_t)p.staged_K * (size_t)p.staged_Fc * 16;
       if (p.direct) {
         if (p.nt) {
-          LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, true, true>), dim3(grid), dim3(256), shm, st, a));
+          LR_DISPATCH_EB(p.eb, (launch_staged_l<EBV, true, true>(a, (int)p.block, grid, shm, st)));
         } else {
-          LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, false, true>), dim3(grid), dim3(256), shm, st, a));
+          LR_DISPATCH_EB(p.eb, (launch_staged_l<EBV, false, true>(a, (int)p.block, grid, shm, st)));
         }
       } else if (p.nt) {
-        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, true, false>), dim3(grid), dim3(256), shm, st, a));
+        LR_DISPATCH_EB(p.eb, (launch_staged_l<EBV, true, false>(a, (int)p.block, grid, shm, st)));
       } else {
-        LR_DISPATCH_EB(p.eb, hipLaunchKernelGGL((k_staged<EBV, false, false>), dim3(grid), dim3(256), shm, st, a));
+        LR_DISPATCH_EB(p.eb, (launch_staged_l<EBV, false, false>(a, (int)p.block, grid, shm, st)));
       }
       return check_launch();
     }

@@ -200,7 +200,7 @@ static bool plan_chan_elements(Plan* p, int a, int b, bool interleave, size_t sr
 // evaluates the gfx950 bank model over every wave of one workgroup's first round for
 // each admissible cps and keeps the cheapest, the widest on a tie (longer contiguous
 // destination runs per store instruction).
-static int64_t staged_gather_cps(const Plan& p, int inner, int64_t cpt, int64_t K, int64_t Fc) {
+static int64_t staged_gather_cps(const Plan& p, int inner, int64_t cpt, int64_t K, int64_t Fc, int64_t L) {
   const int V = 16 / p.eb;
   int64_t g[16];  // element offset in the footprint of element x of chunk c: filled per c
   auto offs = [&](int64_t c, int64_t* out) {
@@ -219,11 +219,12 @@ static int64_t staged_gather_cps(const Plan& p, int inner, int64_t cpt, int64_t 
   int64_t best = dflt, best_cost = -1;
   for (int64_t cps = dflt; cps >= 1; cps >>= 1) {
     const int64_t slices = cpt / cps, G = 32 / cps;
-    // a lane's chunk stays fixed across rounds (slices | 8); a narrower grouping
-    // needs whole groups of G tiles (the default one is tile idx / cpt for any K)
-    if (slices > 8 || 8 % slices || (cps != dflt && K % G)) continue;
+    // a lane's chunk stays fixed across rounds of L jobs (slices | L / 32); a
+    // narrower grouping needs whole groups of G tiles (the default one is tile
+    // idx / cpt for any K)
+    if (slices > L / 32 || (L / 32) % slices || (cps != dflt && K % G)) continue;
     int64_t cost = 0;
-    const int64_t jobs = std::min<int64_t>(256, K * cpt);
+    const int64_t jobs = std::min<int64_t>(L, K * cpt);
     for (int64_t w0 = 0; w0 < jobs; w0 += 64) {
       int64_t addr[16][64];
       int lanes = (int)std::min<int64_t>(64, jobs - w0);
@@ -379,10 +380,15 @@ static bool plan_staged(Plan* p, int b, size_t src_align, size_t dst_align, int6
       ok = (maxbase + Fc * 16 / p->eb) <= src_cap;
       if (ok) {
         const int64_t cpt = P * p->eb / 16;  // 16-byte dst chunks per tile
+        // L lanes per workgroup, at least one per dst chunk of a tile (a lane's
+        // chunk position in the gather is then the same in every round)
+        int64_t L = knob(tun.workgroup_lanes, 256);
+        while (L < cpt) L *= 2;
         // about two dst chunks per lane (padded tiles: 5.85 TB/s, against 5.79 with
-        // four and 5.57 with eight; one measured 4.8-5.1), and at most 40 KiB of LDS
-        // per workgroup.  Stores with the sc1 bit measured no faster here.
-        const int64_t K = std::max<int64_t>(1, std::min<int64_t>(512 / cpt, 2560 / Fc));
+        // four and 5.57 with eight; one measured 4.8-5.1), and at most 10 KiB of LDS
+        // per 64 lanes.  Stores with the sc1 bit measured no faster here.
+        const int64_t K = std::max<int64_t>(1, std::min<int64_t>(2 * L / cpt, 10 * L / Fc));
+        p->block = L;
         p->path = LR_PATH_STAGED;
         // direct global -> LDS loads measured 2.6 % faster on the padded tiles
         // (5.79 vs 5.64 TB/s): the footprint never passes through registers, so
@@ -394,9 +400,9 @@ static bool plan_staged(Plan* p, int b, size_t src_align, size_t dst_align, int6
         p->staged_Fc = Fc;
         p->staged_cpt = cpt;
         p->staged_K = K;
-        p->staged_cps = staged_gather_cps(*p, inner, cpt, K, Fc);
+        p->staged_cps = staged_gather_cps(*p, inner, cpt, K, Fc, L);
         if (tun.gather_chunks > 0 && tun.gather_chunks <= cpt && cpt % tun.gather_chunks == 0 &&
-            8 % (cpt / tun.gather_chunks) == 0 &&
+            (L / 32) % (cpt / tun.gather_chunks) == 0 &&
             (tun.gather_chunks == std::min<int64_t>(cpt, 32) || K % (32 / tun.gather_chunks) == 0))
           p->staged_cps = tun.gather_chunks;
         p->v = V16;
@@ -1374,9 +1380,10 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       if (P != p.staged_P || F != p.staged_F || p.m[in].sd != P) return bad();
       if (p.staged_Fc * 16 < F * p.eb || p.staged_cpt * 16 != P * p.eb || 256 % p.staged_cpt) return bad();
       if (p.staged_K < 1 || p.staged_K * p.staged_Fc * 16 > 65536) return bad();
-      {  // gather grouping: cps | cpt, cps | 32, cpt / cps | 8, and whole slices of tiles
+      if ((p.block != 64 && p.block != 128 && p.block != 256) || p.block < p.staged_cpt) return bad();
+      {  // gather grouping: cps | cpt, cps | 32, cpt / cps | block / 32, and whole slices of tiles
         const int64_t cps = p.staged_cps;
-        if (cps < 1 || cps > 32 || (cps & (cps - 1)) || p.staged_cpt % cps || 8 % (p.staged_cpt / cps) ||
+        if (cps < 1 || cps > 32 || (cps & (cps - 1)) || p.staged_cpt % cps || (p.block / 32) % (p.staged_cpt / cps) ||
             (cps != std::min<int64_t>(p.staged_cpt, 32) && p.staged_K % (32 / cps)))
           return bad();
       }

@@ -1405,14 +1405,20 @@ def test_full_transpose_pipelined(dev, knobs, shape, pipe, tr):
     assert np.array_equal(d.cpu().numpy(), F.transpose(src, 8192))
 
 
+@pytest.mark.parametrize("lanes", [64, 128, 256])
 @pytest.mark.parametrize("direct", [0, 1])
-def test_staged_direct_loads(dev, knobs, direct):
+def test_staged_direct_loads(dev, knobs, direct, lanes):
     """The staged path with its footprint loaded straight into LDS (gfx950 direct
-    loads) or through registers; both streaming policies."""
-    knobs.set(direct_loads=direct)
+    loads) or through registers; both streaming policies; 64-, 128- and 256-lane
+    workgroups (raised to one lane per destination chunk of a tile), under every
+    gather grouping the plan admits."""
+    knobs.set(direct_loads=direct, workgroup_lanes=lanes)
     cases = [(W.small("padtiles").src_layout, W.small("padtiles").dst_layout, W.small("padtiles").src_elems,
               W.small("padtiles").dst_elems, 4)]
     cases += [c for c in _case_pairs()]
+    # padded rows of 2 and 4 KiB: 128 and 256 destination chunks a tile
+    cases += [("(512,30):(1,520)", "(512,30):(1,512)", 520 * 30, 512 * 30, 4),
+              ("(512,9):(1,516)", "(512,9):(1,512)", 516 * 9, 512 * 9, 8)]
     ran = 0
     for nt in ("0", "1"):
         knobs.policy(nt)
@@ -1428,11 +1434,14 @@ def test_staged_direct_loads(dev, knobs, direct):
             seen = set()
             for gc in (-1, 1, 2, 4, 8, 16, 32):  # every gather grouping the plan admits
                 knobs.set(gather_chunks=gc)
-                g = plan(ts, ns, td, nd, eb, flags)["gather_chunks"]
+                p = plan(ts, ns, td, nd, eb, flags)
+                g = p["gather_chunks"]
                 if g in seen:
                     continue
                 seen.add(g)
-                say("staged direct", direct, "nt", nt, ts, "->", td, "eb", eb, "gather chunks", g)
+                assert p["block"] >= lanes
+                say("staged direct", direct, "nt", nt, ts, "->", td, "eb", eb, "gather chunks", g,
+                    "block", p["block"], "grid", p["grid"])
                 assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb, flags), want), (ts, td, g)
                 ran += 1
             knobs.unset("gather_chunks")

@@ -1177,3 +1177,15 @@ def test_workgroup_lanes_plan():
     assert lr.copy_plan(s.src_layout, s.src_elems, s.dst_layout, s.dst_elems, 2)["block"] == 256
     perm = ("(2048,1024,64):(1,2048,2097152)", 1 << 27, "(2048,1024,64):(1,131072,2048)", 1 << 27, 2)
     assert lr.copy_plan(*perm)["block"] == 256  # three modes
+    # the staged gather: two destination chunks a lane, so tiles a workgroup scale with lanes,
+    # and at least one lane per destination chunk of a tile (2 KiB rows: 128 chunks)
+    pt = W.full("padtiles")
+    pargs = (pt.src_layout, pt.src_elems, pt.dst_layout, pt.dst_elems, 4)
+    pbase = lr.copy_plan(*pargs)
+    for lanes in (64, 128, 256):
+        p = lr.copy_plan(*pargs, tuning={"workgroup_lanes": lanes})
+        assert p["path"] == "staged" and p["block"] == lanes
+        assert p["tile_a"] * pbase["block"] == pbase["tile_a"] * lanes and p["grid"] * lanes == pbase["grid"] * pbase["block"]
+    rows = ("(512,30):(1,520)", 520 * 30, "(512,30):(1,512)", 512 * 30, 4)
+    p = lr.copy_plan(*rows, flags=lr.COPY_FORCE_PATH(lr.PATH_STAGED), tuning={"workgroup_lanes": 64})
+    assert p["block"] == 128 and p["tile_a"] == 2 and p["gather_chunks"] == 32

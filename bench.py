@@ -454,6 +454,42 @@ def layout_sweep(lr, torch, steps: int = 20):
         torch.cuda.empty_cache()
 
 
+def blocks_sweep(lr, torch, steps: int = 20):
+    """Register-loaded LDS transposes with one against two V x V blocks per lane
+    (transpose_blocks 1 and 2, the same tiles with half the lanes), each twice in
+    alternation, back to back over rotating buffers, beside a contiguous copy of the
+    same bytes: the transposes of the benchmark workloads and of LAYOUT_SWEEP, and
+    fp16 16384^2.  One JSON line per transform."""
+    import workloads as W
+    dev = torch.device("cuda:0")
+    cases = []
+    for name in ("transpose", "interleave_cm", "nhwc2nchw", "shard_pack"):
+        w = W.full(name)
+        cases.append((w.name, w.src_layout, w.dst_layout, w.elem_bytes))
+    cases.append(("fp16 transpose 16384^2", "(16384,16384):(16384,1)", "(16384,16384):(1,16384)", 2))
+    cases += [c for c in LAYOUT_SWEEP]
+    for name, ts, td, eb in cases:
+        Ls = lr.parse(ts)
+        n, ns, nd = Ls.size, Ls.cosize, lr.parse(td).cosize
+        p1 = lr.copy_plan(ts, ns, td, nd, eb, tuning={"transpose_blocks": 1})
+        p2 = lr.copy_plan(ts, ns, td, nd, eb, tuning={"transpose_blocks": 2})
+        if p2["path"] != "transpose" or p2["block"] == p1["block"]:
+            continue
+        pairs = _pairs(torch, dev, ns * eb, nd * eb)
+        res = {1: [], 2: []}
+        for rep in range(2):
+            for tb in (1, 2):
+                _, ms = _time_copies(lr, torch, pairs, ts, td, eb, steps, 3, tuning={"transpose_blocks": tb})
+                res[tb].append(round(ms * 1e3, 2))
+        cu = n * eb // 16
+        whole = [(s_[:cu * 16], d_[:cu * 16]) for s_, d_ in pairs]
+        _, cms = _time_copies(lr, torch, whole, f"{cu}:1", f"{cu}:1", 16, steps, 3)
+        print(json.dumps({"case": name, "tile": [p1["tile_a"], p1["tile_b"]], "lanes": [p1["block"], p2["block"]],
+                          "us_1": res[1], "us_2": res[2], "copy_us": round(cms * 1e3, 2)}), flush=True)
+        del pairs
+        torch.cuda.empty_cache()
+
+
 # 1-byte transposes: matrix shapes (rows x columns, row-major source, column-major
 # destination) and the tunings compared on each
 BYTE_SHAPES = ((16384, 16384), (8192, 8192), (8192, 16384), (16384, 8192), (4096, 4096), (6144, 6144),
@@ -677,6 +713,8 @@ def main():
     ap.add_argument("--batched-sweep", nargs="?", const="paths", choices=["paths", "swizzles"],
                     help="batched small-matrix transposes: the planner's path against the batched, staged and "
                          "transpose paths, or the batched path under each LDS swizzle and block order")
+    ap.add_argument("--blocks-sweep", action="store_true",
+                    help="register-loaded LDS transposes with one against two register blocks per lane")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
                     help="with --launch: also time K back-to-back launches per spec")
     args = ap.parse_args()
@@ -713,6 +751,9 @@ def main():
         return
     if args.layout_sweep:
         layout_sweep(lr, torch)
+        return
+    if args.blocks_sweep:
+        blocks_sweep(lr, torch)
         return
     if args.batched_sweep:
         batched_sweep(lr, torch, args.batched_sweep)

@@ -418,7 +418,11 @@ typedef struct {
                               directions, chunk form) and the staged gather (raised to the
                               16-byte destination chunks of one tile where that is more):
                               64, 128 or 256 lanes per workgroup */
-  int32_t reserved[1];     /* must be -1 or 0 */
+  int32_t transpose_blocks; /* LDS transpose through registers (not direct loads), 16-byte chunks
+                              (8-byte for 1-byte elements), tile shapes 0-6 (an even b side and
+                              at least a wavefront's worth of lanes):
+                              1 one V x V register block per lane, 2 two blocks per lane (half
+                              the workgroup's lanes for the same tile) */
 } lr_copy_tuning;
 
 /* Every field of *t to -1 (the planner's choices). */

@@ -121,11 +121,11 @@ class lr_copy_tuning(ctypes.Structure):
         ("batch_swizzle", ctypes.c_int32),
         ("batch_order", ctypes.c_int32),
         ("workgroup_lanes", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("transpose_blocks", ctypes.c_int32),
     ]
 
 
-TUNING_FIELDS = tuple(k for k, _ in lr_copy_tuning._fields_ if k != "reserved")
+TUNING_FIELDS = tuple(k for k, _ in lr_copy_tuning._fields_)
 
 
 def _tuning(tuning):

@@ -762,12 +762,14 @@ __device__ __forceinline__ void transpose_tile(const TransposeArgs& t, uint32_t 
 // touch distinct chunk slots of a bank window.
 // LDS == false (TA == TB == 16 only): lanes are arranged 8 x 8 per wave so each
 // load and store instruction covers eight full 128-byte lines, with no LDS.
-template <int EB, int V, bool LDS, int TA, int TB, bool NT>
-__global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
+template <int EB, int V, bool LDS, int TA, int TB, bool NT, int R = 1>
+__global__ void __launch_bounds__(TA * TB / R) k_transpose(TransposeArgs t) {
   using T = typename Raw<EB>::T;
   using C = Chunk<T, V>;
-  constexpr int NTH = TA * TB;  // threads
-  static_assert(LDS || (TA == 16 && TB == 16), "the direct variant uses 16 x 16 blocks");
+  constexpr int NTH = TA * TB / R;  // threads: R register blocks per lane
+  static_assert(LDS || (TA == 16 && TB == 16 && R == 1), "the direct variant uses 16 x 16 blocks");
+  static_assert(R == 1 || R == 2, "one or two blocks per lane");
+  static_assert(TB % R == 0, "whole rows of blocks per lane group");
   const char* __restrict__ src = (const char*)t.src;
   char* __restrict__ dst = (char*)t.dst;
 
@@ -777,7 +779,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   batch_offsets(t.batch, r2, &bs, &bd);
 
   const int tid = threadIdx.x;
-  int alpha, beta;
+  int alpha, beta;  // the lane's first block; its others lie TB / R block rows further along b
   if (LDS) {
     alpha = tid % TA;
     beta = tid / TA;
@@ -787,30 +789,37 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
     beta = (lane >> 3) + 8 * (w >> 1);
   }
   const uint32_t a0 = ta * (TA * V), b0 = tb * (TB * V);
-  const uint32_t a_blk = a0 + V * alpha, b_blk = b0 + V * beta;
-  const bool valid = a_blk < t.ext_a && b_blk < t.ext_b;
-
-  C in[V];
-  if (valid) {
+  const uint32_t a_blk = a0 + V * alpha;
+  bool valid[R];
+  C in[R][V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const uint32_t b = b_blk + j;
-      uint32_t so = swz32(a_blk + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
-      in[j] = gload<NT, C>(src + (size_t)so * EB);
+  for (int r = 0; r < R; ++r) {
+    const uint32_t b_blk = b0 + V * (beta + (TB / R) * r);
+    valid[r] = a_blk < t.ext_a && b_blk < t.ext_b;
+    if (valid[r]) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint32_t b = b_blk + j;
+        uint32_t so = swz32(a_blk + (b & t.bmask) * t.ss_b + (b >> t.bshift) * t.ss_b2 + bs, t.sws);
+        in[r][j] = gload<NT, C>(src + (size_t)so * EB);
+      }
     }
   }
-  C out[V];
+  C out[R][V];
 #pragma unroll
-  for (int i = 0; i < V; ++i)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int j = 0; j < V; ++j) out[i].e[j] = in[j].e[i];
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < V; ++j) out[r][i].e[j] = in[r][j].e[i];
 
   if (!LDS) {
-    if (valid) {
+    if (valid[0]) {
+      const uint32_t b_blk = b0 + V * beta;
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         uint32_t dof = swz32((a_blk + i) * t.sd_a + b_blk + bd, t.swd);
-        gstore<NT, C>(dst + (size_t)dof * EB, out[i]);
+        gstore<NT, C>(dst + (size_t)dof * EB, out[0][i]);
         count_store(t.wcnt, t.dst, dst + (size_t)dof * EB, sizeof(C));
       }
     }
@@ -818,9 +827,13 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
   }
 
   __shared__ C tile[TA * V][TB];
-  if (valid) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) tile[V * alpha + i][beta ^ (alpha % TB)] = out[i];
+  for (int r = 0; r < R; ++r) {
+    if (valid[r]) {
+      const int bt = beta + (TB / R) * r;
+#pragma unroll
+      for (int i = 0; i < V; ++i) tile[V * alpha + i][bt ^ (alpha % TB)] = out[r][i];
+    }
   }
   __syncthreads();
   const int c = tid % TB;
@@ -834,7 +847,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
       const uint32_t tbase = (a0 * t.sd_a + b0 + bd) & t.bufmask;
       const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst + (size_t)tbase * EB, 0, -1, kBufferWord3);
 #pragma unroll
-      for (int k = 0; k < V; ++k) {
+      for (int k = 0; k < V * R; ++k) {
         const int row = tid / TB + (NTH / TB) * k;
         const uint32_t a = a0 + row, b = b0 + V * c;
         if (a < t.ext_a && b < t.ext_b) {
@@ -849,7 +862,7 @@ __global__ void __launch_bounds__(TA * TB) k_transpose(TransposeArgs t) {
     }
   }
 #pragma unroll
-  for (int k = 0; k < V; ++k) {
+  for (int k = 0; k < V * R; ++k) {
     const int row = tid / TB + (NTH / TB) * k;
     const uint32_t a = a0 + row, b = b0 + V * c;
     if (a < t.ext_a && b < t.ext_b) {
@@ -2104,9 +2117,9 @@ static void launch_dual(const DualArgs& a, bool wide, unsigned grid, hipStream_t
     hipLaunchKernelGGL((k_dual<EB, false>), dim3(grid), dim3(256), 0, st, a);
 }
 
-template <int EB, int V, int TA, int TB, bool NT>
+template <int EB, int V, int TA, int TB, bool NT, int R = 1>
 static void launch_transpose_shape(const TransposeArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_transpose<EB, V, true, TA, TB, NT>), dim3(grid), dim3(TA * TB), 0, st, a);
+  hipLaunchKernelGGL((k_transpose<EB, V, true, TA, TB, NT, R>), dim3(grid), dim3(TA * TB / R), 0, st, a);
 }
 
 // The direct-load kernels: pipelined (a.pipe) or one tile per workgroup.
@@ -2150,10 +2163,36 @@ static bool launch_dl(const TransposeArgs& a, int shape, unsigned grid, hipStrea
 }
 
 // dl: 0 through registers, 1 direct loads, 2 direct loads read back with the gfx950
-// transpose reads
+// transpose reads, 3 through registers with two blocks per lane
 template <int EB, int V, bool NT>
 static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, int dl, unsigned grid,
                                hipStream_t st) {
+  if constexpr (V * EB == 16 || (EB == 1 && V == 8)) {
+    if (dl == 3) {
+      if (!lds) return false;
+#define LR_TSHAPE2_CASE(S)                                                               \
+  case S:                                                                                \
+    if constexpr (shape_fits(S, V) && kTileTB[S] % 2 == 0 && kTileTA[S] * kTileTB[S] >= 128) { \
+      launch_transpose_shape<EB, V, kTileTA[S], kTileTB[S], NT, 2>(a, grid, st);         \
+      return true;                                                                       \
+    }                                                                                    \
+    return false;
+      switch (shape) {
+        case 0: launch_transpose_shape<EB, V, 16, 16, NT, 2>(a, grid, st); return true;
+        LR_TSHAPE2_CASE(1)
+        LR_TSHAPE2_CASE(2)
+        LR_TSHAPE2_CASE(3)
+        LR_TSHAPE2_CASE(4)
+        LR_TSHAPE2_CASE(5)
+        LR_TSHAPE2_CASE(6)
+        LR_TSHAPE2_CASE(7)
+        default: return false;
+      }
+#undef LR_TSHAPE2_CASE
+    }
+  } else {
+    if (dl == 3) return false;
+  }
   if constexpr (V * EB == 16) {
     if (dl == 2 && lds) {
       if constexpr (EB <= 2) return launch_dl<EB, V, NT, true>(a, shape, grid, st);
@@ -2421,7 +2460,8 @@ static int run_copy(const void* src, const lr_layout* Ls, void* dst, const lr_la
         return check_launch();
       }
       bool ok = false;
-      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, p.direct ? (p.tr ? 2 : 1) : 0, grid, st));
+      const int dl = p.direct ? (p.tr ? 2 : 1) : (p.tblocks == 2 ? 3 : 0);
+      LR_DISPATCH_EB(p.eb, ok = launch_transpose<EBV>(a, p.v, lds, p.tshape, p.nt, dl, grid, st));
       if (!ok) return LR_ERR_PATH;
       return check_launch();
     }

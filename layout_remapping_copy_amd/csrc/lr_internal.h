@@ -116,6 +116,7 @@ struct Plan {
   int tshape;         // transpose tile shape index into kTileTA / kTileTB
   int pipe;           // pipelined transpose: tiles per workgroup (0: one tile, not pipelined)
   bool tr;            // LDS transpose: the tile is read with gfx950 transpose reads
+  int tblocks;        // LDS transpose through registers: V x V blocks per lane (2, else 1)
   int64_t tiles_total; // transpose: tiles over all batch indices
   // batched small matrices: whole matrices per wavefront, matrices, the LDS chunk
   // swizzle (two XOR terms of shift, mask, target shift) and the block order (0:

@@ -146,8 +146,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
   if (t.batch_swizzle != -1 && (t.batch_swizzle < 0 || t.batch_swizzle > 15)) return false;
   if (!in(t.batch_order, {0, 1})) return false;
   if (!in(t.workgroup_lanes, {64, 128, 256})) return false;
-  for (int32_t r : t.reserved)
-    if (r != -1 && r != 0) return false;
+  if (!in(t.transpose_blocks, {1, 2})) return false;
   return true;
 }
 
@@ -1049,6 +1048,14 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->tr = true;
         p->bufst = false;
       }
+      // two register blocks per lane (half the lanes for the same tile) on the
+      // register-loaded LDS transpose
+      if (tun.transpose_blocks == 2 && p->path == LR_PATH_TRANSPOSE && !p->tel && !p->direct && !p->pipe &&
+          (V * p->eb == 16 || (p->eb == 1 && V == 8)) && kTileTB[p->tshape] % 2 == 0 &&
+          kTileTA[p->tshape] * kTileTB[p->tshape] >= 128) {  // whole wavefronts
+        p->tblocks = 2;
+        p->block = kTileTA[p->tshape] * kTileTB[p->tshape] / 2;
+      }
       // Small matrices in a batch (a whole matrix at most a quarter of the tile): the
       // staged path where it applies, which moves each compact matrix as one block,
       // else (under a quarter) the batched path.  Measured on batched fp16 transposes:
@@ -1263,6 +1270,13 @@ int verify_plan(const Plan& p, int64_t src_cap, int64_t dst_cap) {
       // direct-load kernel: full 16-byte chunks, tiles 16 or 32 chunks along a, >= 16 along b
       if (p.direct && (p.path != LR_PATH_TRANSPOSE || v * p.eb != 16 || p.tshape > 3 || !shape_fits(p.tshape, (int)v)))
         return bad();
+      // two register blocks per lane: the register-loaded LDS kernel, whole block rows per lane group
+      if (p.tblocks == 2 &&
+          (p.path != LR_PATH_TRANSPOSE || p.tel || p.direct || p.pipe || kTileTB[p.tshape] % 2 ||
+           (v * p.eb != 16 && !(p.eb == 1 && v == 8)) || p.block != kTileTA[p.tshape] * kTileTB[p.tshape] / 2 ||
+           p.block < 64))
+        return bad();
+      if (p.tblocks != 0 && p.tblocks != 1 && p.tblocks != 2) return bad();
       if (p.tel) {  // element-granular tiles of 256-byte rows
         if (p.path != LR_PATH_TRANSPOSE || p.eb > 8 || v != 1 || p.direct || p.tile_a != 256 / p.eb ||
             p.tile_b != 256 / p.eb || p.block != 512)
@@ -1480,7 +1494,7 @@ void lr_copy_tuning_init(lr_copy_tuning* t) {
   t->batch_swizzle = -1;
   t->batch_order = -1;
   t->workgroup_lanes = -1;
-  for (int32_t& r : t->reserved) r = -1;
+  t->transpose_blocks = -1;
 }
 
 int lr_copy_plan(const lr_layout* Ls, int64_t src_capacity_elems, size_t src_align, const lr_layout* Ld,

@@ -800,6 +800,55 @@ def test_transpose_tile_shapes(dev, knobs, shape):
         knobs.unset("tile_order")
 
 
+@pytest.mark.parametrize("nt", ["0", "1"])
+def test_transpose_two_blocks_per_lane(dev, knobs, nt):
+    """transpose_blocks = 2: each lane of the register-loaded LDS transpose moves two
+    V x V blocks, so a tile takes half the lanes.  Every tile shape with an even b
+    side, ragged tiles on both sides, 1- to 8-byte elements, a grouped b side and a
+    swizzled destination, plain and streaming accesses (the latter with the sc1
+    buffer stores), and the 8192^2 fp16 transpose at full size."""
+    knobs.policy(nt)
+    cases = [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
+             ("(3,7,9,40):(2520,360,40,1)", "(3,7,9,40):(2520,9,1,63)", 7560, 2),
+             ("(100,72):(72,1)", "(100,72):(1,100)", 7200, 4),
+             ("(64,96,5):(96,1,6144)", "(64,96,5):(1,64,6144)", 30720, 8),
+             ("(1024,512):(512,1)", "Sw<3,3,3> o (1024,512):(1,1024)", 1024 * 512, 2),
+             ("(512,272):(272,1)", "(512,272):(1,512)", 512 * 272, 1)]
+    for name in ("transpose", "interleave_cm", "nhwc2nchw"):
+        w = W.small(name)
+        cases.append((w.src_layout, w.dst_layout, max(w.src_elems, w.dst_elems), w.elem_bytes))
+    ran = 0
+    for ci, (ts, td, n, eb) in enumerate(cases):
+        src = np.random.default_rng(300 + ci).integers(0, 256, n * eb, dtype=np.uint8)
+        dst = np.full(n * eb, 0xA5, np.uint8)
+        want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
+        for shape in range(8):
+            knobs.t.clear()
+            knobs.policy(nt)
+            knobs.set(tile_shape=shape, transpose_blocks=2)
+            p = plan(ts, n, td, n, eb)
+            if p["path"] != "transpose":
+                continue
+            two = p["block"] * 2 * p["vec_elems"] ** 2 == p["tile_a"] * p["tile_b"]
+            say("two blocks per lane", ts, "->", td, "eb", eb, "shape", shape, "block", p["block"], "two", two)
+            assert np.array_equal(gpu_copy(dev, src, ts, dst, td, eb), want), (ts, shape)
+            ran += two
+    assert ran >= 40
+    knobs.t.clear()
+    knobs.policy(nt)
+    knobs.set(transpose_blocks=2)
+    w = W.full("transpose")
+    assert plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)["block"] == 512
+    s = torch.from_numpy(W.make_src(w)).to(dev)
+    d = torch.full((w.dst_elems * 2,), 0xA5, dtype=torch.uint8, device=dev)
+    say("two blocks per lane: fp16 8192^2")
+    copy_(s, w.src_layout, d, w.dst_layout, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), F.transpose(W.make_src(w), 8192))
+    del s, d
+    torch.cuda.empty_cache()
+
+
 def test_streaming_accesses_every_path(dev, knobs):
     """Small copies default to plain accesses; a non-temporal load policy forces the
     non-temporal kernels, which must give the same bytes on every path and workload."""

@@ -706,6 +706,25 @@ def test_plan_store_policy():
     assert e.value.code == lr.binding.ERR_PATH
 
 
+def test_transpose_blocks_plan():
+    """transpose_blocks = 2 halves the lanes of the register-loaded LDS transpose for
+    the same tile; direct loads, element tiles and odd b sides keep one block a lane."""
+    w = W.full("transpose")
+    args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    base = lr.copy_plan(*args)
+    p = lr.copy_plan(*args, tuning={"transpose_blocks": 2})
+    assert base["block"] == 1024 and p["block"] == 512
+    assert (p["tile_a"], p["tile_b"], p["grid"], p["order"]) == (base["tile_a"], base["tile_b"], base["grid"], base["order"])
+    assert lr.copy_plan(*args, tuning={"transpose_blocks": 1})["block"] == 1024
+    assert lr.copy_plan(*args, tuning={"transpose_blocks": 2, "direct_loads": 1})["block"] == 1024
+    for shape in range(8):
+        p = lr.copy_plan(*args, tuning={"transpose_blocks": 2, "tile_shape": shape})
+        blocks = p["tile_a"] * p["tile_b"] // p["vec_elems"] ** 2
+        assert p["block"] == (blocks if shape == 7 else blocks // 2), shape  # 8 x 8 chunks: one wavefront
+    odd = ("(8191,8191):(8191,1)", 8191 * 8191, "(8191,8191):(1,8191)", 8191 * 8191, 2)
+    assert lr.copy_plan(*odd, tuning={"transpose_blocks": 2})["block"] == lr.copy_plan(*odd)["block"]
+
+
 def test_tuning_overrides_are_checked():
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
@@ -713,7 +732,7 @@ def test_tuning_overrides_are_checked():
                 {"units_per_lane": 2}, {"vector_order": 4}, {"gather_chunks": 3}, {"direct_loads": 2},
                 {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2},
                 {"chunk_bytes": 4}, {"chunk_bytes": 0}, {"workgroup_lanes": 32}, {"workgroup_lanes": 512},
-                {"batch_swizzle": 16}, {"batch_order": 2}):
+                {"batch_swizzle": 16}, {"batch_order": 2}, {"transpose_blocks": 0}, {"transpose_blocks": 3}):
         with pytest.raises(lr.LayoutRemapError) as e:
             lr.copy_plan(*args, tuning=bad)
         assert e.value.code == lr.binding.ERR_INVALID, bad

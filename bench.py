@@ -323,7 +323,13 @@ def launch_run(lr, torch, W, specs, reps: int = 12, back_to_back: int = 0):
     for spec in specs:
         name, _, js = spec.partition(":")
         tuning = json.loads(js) if js else None
-        w = W.full(name)
+        if name.startswith("sweep"):  # sweepK: the K-th transform of LAYOUT_SWEEP
+            case, ts, td, eb_ = LAYOUT_SWEEP[int(name[5:])]
+            Ls, Ld = lr.parse(ts), lr.parse(td)
+            w = W.Workload(name=case, elem_bytes=eb_, src_layout=ts, dst_layout=td, src_elems=Ls.cosize,
+                           dst_elems=Ld.cosize, seed=0, values="bits16", n_elems=Ls.size)
+        else:
+            w = W.full(name)
         eb = w.elem_bytes
         p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, eb, tuning=tuning)
         pairs = _pairs(torch, dev, w.src_elems * eb, w.dst_elems * eb)
@@ -450,6 +456,59 @@ def layout_sweep(lr, torch, steps: int = 20):
                           "vector_order": p["vector_order"], "us": round(ms * 1e3, 2),
                           "GBps": round(2 * n * eb / (ms * 1e-3) / 1e9), "copy_us": round(cms * 1e3, 2),
                           "frac_of_copy": round(cms / ms, 3)}), flush=True)
+        del pairs
+        torch.cuda.empty_cache()
+
+
+# transposes for the tile-shape sweep: (name, rows, columns, element bytes) of a
+# row-major source and its column-major destination, plus whole-block cases
+SHAPE_SWEEP = [(f"{8 * eb}-bit transpose {r}x{c}", r, c, eb) for eb, r, c in (
+    (1, 16384, 16384), (1, 8192, 16384), (2, 8192, 8192), (2, 16384, 16384), (2, 4096, 16384), (2, 16384, 4096),
+    (4, 8192, 8192), (4, 4096, 8192), (8, 4096, 8192), (8, 4096, 4096), (8, 8192, 8192), (16, 4096, 4096),
+    (16, 2048, 4096))]
+
+
+def shape_sweep(lr, torch, matrices=None, steps: int = 20):
+    """Transposes of 1- to 16-byte elements under every transpose tile shape but the
+    8 x 8-chunk one (tile_shape 0-6 and 8), each twice in alternation, back to back over
+    rotating buffers, beside a contiguous copy of the same bytes; then the layout
+    sweep's NCHW -> NHWC and KV-cache transposes and the NHWC -> NCHW workload the same
+    way.  `matrices` ("RxCxB": rows, columns, element bytes) replaces the whole list.
+    One JSON line per transform, microseconds per shape."""
+    import workloads as W
+    dev = torch.device("cuda:0")
+    if matrices:
+        sweep = []
+        for m in matrices:
+            r, c, eb = (int(x) for x in m.split("x"))
+            sweep.append((f"{8 * eb}-bit transpose {r}x{c}", r, c, eb))
+        cases = [(name, f"({r},{c}):({c},1)", f"({r},{c}):(1,{r})", eb) for name, r, c, eb in sweep]
+    else:
+        cases = [(name, f"({r},{c}):({c},1)", f"({r},{c}):(1,{r})", eb) for name, r, c, eb in SHAPE_SWEEP]
+        cases += [c for c in LAYOUT_SWEEP if c[0].startswith(("NCHW", "KV"))]
+        w = W.full("nhwc2nchw")
+        cases.append((w.name, w.src_layout, w.dst_layout, w.elem_bytes))
+    for name, ts, td, eb in cases:
+        Ls = lr.parse(ts)
+        n, ns, nd = Ls.size, Ls.cosize, lr.parse(td).cosize
+        pairs = _pairs(torch, dev, ns * eb, nd * eb)
+        dflt = lr.copy_plan(ts, ns, td, nd, eb)
+        shapes = {}
+        for sh in (0, 1, 2, 3, 4, 5, 6, 8):
+            p = lr.copy_plan(ts, ns, td, nd, eb, tuning={"tile_shape": sh})
+            if p["path"] == "transpose" and (p["tile_a"], p["tile_b"]) not in [v[0] for v in shapes.values()]:
+                shapes[sh] = ((p["tile_a"], p["tile_b"]), [])
+        for rep in range(2):
+            for sh, (_, res) in shapes.items():
+                _, ms = _time_copies(lr, torch, pairs, ts, td, eb, steps, 3, tuning={"tile_shape": sh})
+                res.append(round(ms * 1e3, 2))
+        cu = n * eb // 16
+        whole = [(s_[:cu * 16], d_[:cu * 16]) for s_, d_ in pairs]
+        _, cms = _time_copies(lr, torch, whole, f"{cu}:1", f"{cu}:1", 16, steps, 3)
+        print(json.dumps({"case": name, "eb": eb, "planner_tile": [dflt["tile_a"], dflt["tile_b"]],
+                          "us": {str(sh): v[1] for sh, v in shapes.items()},
+                          "tiles": {str(sh): list(v[0]) for sh, v in shapes.items()},
+                          "copy_us": round(cms * 1e3, 2)}), flush=True)
         del pairs
         torch.cuda.empty_cache()
 
@@ -700,7 +759,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--groups-of", type=int, default=0, help="with --summarize-trace: dispatches per launch group")
-    ap.add_argument("--launch", action="append", metavar="NAME[:JSON]")
+    ap.add_argument("--launch", action="append", metavar="NAME[:JSON]",
+                    help="a workload by name, or sweepK for the K-th layout-sweep transform, with lr_copy_tuning "
+                         "overrides as JSON")
     ap.add_argument("--atom-sweep", nargs="?", const="orders", choices=["orders", "lanes"],
                     help="head splits for head dims of 32-512 bytes: tiles of atoms against the source order, "
                          "or in 128- against 256-lane workgroups")
@@ -713,6 +774,9 @@ def main():
     ap.add_argument("--batched-sweep", nargs="?", const="paths", choices=["paths", "swizzles"],
                     help="batched small-matrix transposes: the planner's path against the batched, staged and "
                          "transpose paths, or the batched path under each LDS swizzle and block order")
+    ap.add_argument("--shape-sweep", nargs="*", metavar="RxCxB",
+                    help="transposes of 1- to 16-byte elements under every transpose tile shape (all listed "
+                         "matrices and layout transforms, or these rows x columns x element bytes)")
     ap.add_argument("--blocks-sweep", action="store_true",
                     help="register-loaded LDS transposes with one against two register blocks per lane")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
@@ -754,6 +818,9 @@ def main():
         return
     if args.blocks_sweep:
         blocks_sweep(lr, torch)
+        return
+    if args.shape_sweep is not None:
+        shape_sweep(lr, torch, args.shape_sweep)
         return
     if args.batched_sweep:
         batched_sweep(lr, torch, args.batched_sweep)

@@ -390,8 +390,9 @@ typedef struct {
                               lr_plan.vector_order) */
   int32_t interleave_form; /* interleave: 0 one chunk per lane per head, 1 one destination
                               chunk per lane from narrow loads, 2 the channel shuffle */
-  int32_t tile_shape;      /* transpose: 0..7, the tile shapes of lr_plan.tile_a/tile_b (16-byte
-                              chunks a x b: 16x16, 32x16, 16x32, 32x32, 32x8, 64x8, 64x16, 8x8) */
+  int32_t tile_shape;      /* transpose: 0..8, the tile shapes of lr_plan.tile_a/tile_b (16-byte
+                              chunks a x b: 16x16, 32x16, 16x32, 32x32, 32x8, 64x8, 64x16, 8x8,
+                              8x32) */
   int32_t tile_order;      /* transpose: 0..9, as lr_plan.order (5..9 not with pipeline_tiles) */
   int32_t element_tiles;   /* transpose: 0 chunk tiles, 1 element-granular tiles */
   int32_t direct_loads;    /* staged and LDS transpose: 0 through registers, 1 global -> LDS */
@@ -419,8 +420,8 @@ typedef struct {
                               16-byte destination chunks of one tile where that is more):
                               64, 128 or 256 lanes per workgroup */
   int32_t transpose_blocks; /* LDS transpose through registers (not direct loads), 16-byte chunks
-                              (8-byte for 1-byte elements), tile shapes 0-6 (an even b side and
-                              at least a wavefront's worth of lanes):
+                              (8-byte for 1-byte elements), tile shapes other than 7 (an even b
+                              side and at least a wavefront's worth of lanes):
                               1 one V x V register block per lane, 2 two blocks per lane (half
                               the workgroup's lanes for the same tile) */
 } lr_copy_tuning;

@@ -2186,6 +2186,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, int 
         LR_TSHAPE2_CASE(5)
         LR_TSHAPE2_CASE(6)
         LR_TSHAPE2_CASE(7)
+        LR_TSHAPE2_CASE(8)
         default: return false;
       }
 #undef LR_TSHAPE2_CASE
@@ -2221,6 +2222,7 @@ static bool launch_transpose_v(const TransposeArgs& a, bool lds, int shape, int 
       LR_TSHAPE_CASE(5)
       LR_TSHAPE_CASE(6)
       LR_TSHAPE_CASE(7)
+      LR_TSHAPE_CASE(8)
       default: break;
     }
 #undef LR_TSHAPE_CASE

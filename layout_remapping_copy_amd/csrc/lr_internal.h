@@ -56,9 +56,9 @@ struct Swz {
 
 // Transpose tile shapes in 16-byte chunks along a (source-contiguous) x b
 // (destination-contiguous); the workgroup has TA * TB lanes.
-constexpr int kTileShapes = 8;
-constexpr int kTileTA[kTileShapes] = {16, 32, 16, 32, 32, 64, 64, 8};
-constexpr int kTileTB[kTileShapes] = {16, 16, 32, 32, 8, 8, 16, 8};
+constexpr int kTileShapes = 9;
+constexpr int kTileTA[kTileShapes] = {16, 32, 16, 32, 32, 64, 64, 8, 8};
+constexpr int kTileTB[kTileShapes] = {16, 16, 32, 32, 8, 8, 16, 8, 32};
 // LDS bytes of a tile shape's exchange with V-element 16-byte chunks: TA*V rows of
 // TB chunks; a shape is usable when it fits the 160 KiB of a CU.
 constexpr bool shape_fits(int shape, int V) { return kTileTA[shape] * V * kTileTB[shape] * 16 <= 160 * 1024; }

@@ -137,7 +137,7 @@ static bool tuning_valid(const lr_copy_tuning& t) {
   };
   if (!in(t.load_policy, {0, 2}) || !in(t.store_policy, {0, 2, 18}) || !in(t.units_per_lane, {1, 4}) ||
       !in(t.vector_order, {0, 1, 2, 3}) || !in(t.interleave_form, {0, 1, 2}) ||
-      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6, 7}) || !in(t.tile_order, {0, 1, 2, 3, 4, 5, 6, 7, 8, 9}) ||
+      !in(t.tile_shape, {0, 1, 2, 3, 4, 5, 6, 7, 8}) || !in(t.tile_order, {0, 1, 2, 3, 4, 5, 6, 7, 8, 9}) ||
       !in(t.element_tiles, {0, 1}) || !in(t.direct_loads, {0, 1}) || !in(t.gather_chunks, {1, 2, 4, 8, 16, 32}))
     return false;
   if (t.pipeline_tiles != -1 && (t.pipeline_tiles < 0 || t.pipeline_tiles == 1 || t.pipeline_tiles > 64)) return false;
@@ -876,28 +876,41 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       // source distance between nearby b rows
       const int64_t pitch = (b2 >= 0 ? std::min(p->m[b].ss, p->m[b2].ss) : p->m[b].ss) * p->eb;
       // tile shape in 16-byte chunks (a x b): wider tiles only for full chunks on
-      // the LDS variant.  Measured with streaming (non-temporal) accesses:
+      // the LDS variant.  Measured with streaming (non-temporal) accesses, back to
+      // back against every other shape:
       //  - when one tile spans the whole a extent and consecutive b rows are
       //    adjacent in the source (each tile reads one contiguous block, e.g.
       //    NHWC -> NCHW), 32 x 8 chunks: small workgroups, many per CU;
+      //  - its mirror, one tile spanning the whole b extent of 17-32 chunks with
+      //    consecutive a rows adjacent in the destination (each tile writes one
+      //    contiguous block, e.g. NCHW -> NHWC with 256 fp16 channels), 8 x 32
+      //    chunks: 67.6 against 72.7 us for 32 x 32 over 128 images of 56 x 56;
       //  - otherwise the longest runs on both sides, 32 x 32 chunks (16 x 32 when
-      //    16 chunks already cover the a extent); with only one or two elements per
-      //    chunk (8- and 16-byte elements) a lane has few loads in flight and
-      //    smaller tiles won: 32 x 16 chunks for two (5.48 vs 5.11 TB/s on an
-      //    8192^2 transpose), 16 x 16 for one (5.35 vs 5.26).
+      //    16 chunks already cover the a extent); 16 x 32 for 8-byte elements (two a
+      //    chunk: 3.6 % faster than 32 x 16 over seven fp64 transposes from 2048 x
+      //    8192 to 4096 x 16384, 10 % at best, 3 % slower at worst); 64 x 16 for
+      //    16-byte elements (9 % faster than 16 x 16 over six transposes from 2048^2
+      //    to 8192 x 2048, 5-13 % each); 1-byte elements in 8-byte chunks 32 x 16
+      //    (level with 32 x 32 and 64 x 16 over six transposes, each ahead on some).
       const bool wide_ok = (V * p->eb == 16 || (p->eb == 1 && V == 8)) && p->path == LR_PATH_TRANSPOSE;
       const int64_t ext_a = p->m[a].ext;
       const bool block_rows = ext_a <= 32 * V && p->m[b].ss == ext_a;
+      const bool block_cols =
+          V * p->eb == 16 && b2 < 0 && ext_b > 16 * V && ext_b <= 32 * V && p->m[a].sd == ext_b;
       if (!wide_ok)
         p->tshape = 0;
       else if (block_rows)
         p->tshape = ext_a > 16 * V ? 4 : 0;
+      else if (block_cols)
+        p->tshape = 8;
       else if (p->eb == 1)
         p->tshape = ext_a > 16 * V ? 1 : 0;  // 8-byte chunks: 32 x 16 (u8 8192^2 4.78 against 4.56 with 32 x 32)
       else if (V >= 4)
         p->tshape = ext_a > 16 * V ? 3 : 2;
+      else if (V == 2)
+        p->tshape = 2;
       else
-        p->tshape = (V == 2 && ext_a > 16 * V) ? 1 : 0;
+        p->tshape = ext_a > 32 ? 6 : 0;
       // A short destination-contiguous extent: no tile taller along b than it needs,
       // else most of a tile's lanes idle.  Measured on NCHW -> NHWC fp16 (256 images of
       // 112 x 112): 32 channels 145.0 -> 69.3 us with 32 x 8 chunks instead of 32 x 32,
@@ -914,7 +927,7 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       // fp16 1024 x 8192 and 8192 x 1024, the 8-way shard pack of 1024 x 8192 and u8
       // 4096^2 in 16-byte chunks: +2 to +8 % (16 MiB copies run near a plain copy's
       // 3.2-3.6 TB/s).
-      if (wide_ok && !block_rows) {
+      if (wide_ok && !block_rows && !block_cols) {
         int64_t tiles = ((ext_a + kTileTA[p->tshape] * V - 1) / (kTileTA[p->tshape] * V)) *
                         ((ext_b + kTileTB[p->tshape] * V - 1) / (kTileTB[p->tshape] * V));
         for (int k = 0; k < p->rank; ++k)

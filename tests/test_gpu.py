@@ -507,7 +507,7 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
         want = O.copy(src, Ls, dst, Ld, eb)
         mult = _multiplicity(Ld, O.size(Ls), nd)
         knobs.t.clear()
-        knobs.set(tile_shape=rng.randint(0, 6), tile_order=rng.randint(0, 9), gather_chunks=rng.choice([-1, 8, 16]),
+        knobs.set(tile_shape=rng.choice([0, 1, 2, 3, 4, 5, 6, 8]), tile_order=rng.randint(0, 9), gather_chunks=rng.choice([-1, 8, 16]),
                   vector_order=rng.choice([-1, 0, 1, 2, 3]), element_tiles=rng.choice([-1, 0, 1]),
                   pipeline_tiles=rng.choice([-1, 2, 3]), transpose_reads=rng.choice([-1, 1]),
                   direct_loads=rng.choice([-1, 1]))
@@ -774,7 +774,7 @@ def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
 # ---------------------------------------------------------------------------
 # Tuning variants chosen at plan time (tile shapes, narrow-load interleave)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 def test_transpose_tile_shapes(dev, knobs, shape):
     knobs.set(tile_shape=shape)
     for ts, td, n, eb in [("(520,264):(264,1)", "(520,264):(1,520)", 520 * 264, 2),
@@ -822,7 +822,7 @@ def test_transpose_two_blocks_per_lane(dev, knobs, nt):
         src = np.random.default_rng(300 + ci).integers(0, 256, n * eb, dtype=np.uint8)
         dst = np.full(n * eb, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
-        for shape in range(8):
+        for shape in range(9):
             knobs.t.clear()
             knobs.policy(nt)
             knobs.set(tile_shape=shape, transpose_blocks=2)
@@ -893,7 +893,7 @@ def test_transpose_streaming_store_forms(dev, knobs, tsc1):
              ("(48,80):(80,1)", "(48,80):(1,48)", 16),
              (cm.src_layout, cm.dst_layout, 2)]
     ran = 0
-    for shape in range(8):
+    for shape in range(9):
         knobs.set(tile_shape=shape)
         for ci, (ts, td, eb) in enumerate(cases):
             n = O.size(O.parse(ts))
@@ -1312,7 +1312,7 @@ def test_byte_transpose_chunks(dev, knobs):
         dst = np.full(nd, 0xA5, np.uint8)
         want = O.copy(src, O.parse(ts), dst, O.parse(td), 1)
         for cb in (8, 16):
-            for shape in range(8):
+            for shape in range(9):
                 for direct in (0, 1):
                     knobs.t.clear()
                     knobs.set(chunk_bytes=cb, tile_shape=shape, direct_loads=direct)

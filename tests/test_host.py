@@ -626,6 +626,20 @@ def test_plan_streaming_default_and_tile_shapes():
     # u8 4096^2 in 8-byte chunks: 32 x 16-chunk tiles of 256 x 128 bytes already make 512
     p = lr.copy_plan("(4096,4096):(4096,1)", 1 << 24, "(4096,4096):(1,4096)", 1 << 24, 1)
     assert (p["vec_elems"], p["tile_a"], p["tile_b"], p["grid"]) == (8, 256, 128, 512), p
+    # 8-byte elements: 16 x 32 chunks; 16-byte elements: 64 x 16
+    p = lr.copy_plan("(4096,8192):(8192,1)", 1 << 25, "(4096,8192):(1,4096)", 1 << 25, 8)
+    assert (p["vec_elems"], p["tile_a"], p["tile_b"], p["block"]) == (2, 32, 64, 512), p
+    p = lr.copy_plan("(4096,4096):(4096,1)", 1 << 24, "(4096,4096):(1,4096)", 1 << 24, 16)
+    assert (p["vec_elems"], p["tile_a"], p["tile_b"], p["block"]) == (1, 64, 16, 1024), p
+    # a whole destination-contiguous extent of 17-32 chunks whose rows are adjacent in the
+    # destination (NCHW -> NHWC, 256 fp16 channels): 8 x 32 chunks, one contiguous
+    # destination block per tile; 64 channels keep 32 x 8, and NHWC -> NCHW its 32 x 8
+    p = lr.copy_plan("(128,3136,256):(802816,1,3136)", 128 * 3136 * 256, "(128,3136,256):(802816,256,1)",
+                     128 * 3136 * 256, 2)
+    assert (p["tile_a"], p["tile_b"], p["block"], p["grid"]) == (64, 256, 256, 128 * 49), p
+    p = lr.copy_plan("(256,12544,64):(802816,1,12544)", 256 * 12544 * 64, "(256,12544,64):(802816,64,1)",
+                     256 * 12544 * 64, 2)
+    assert (p["tile_a"], p["tile_b"]) == (256, 64), p
 
 
 def test_plan_workgroup_order():
@@ -653,7 +667,9 @@ def test_plan_workgroup_order():
             (6144, 6144, 1): 2, (11264, 11264, 1): 2, (8184, 8184, 1): 2,  # 1-byte, 8-byte chunks: order 2
             (8192, 8192, 1): 2,  # 256 x 128 tiles (8-byte chunks), 32 a-tiles <= 64 b-tiles
             (2048, 32768, 1): 4,  # 64 a-tiles > 8 b-tiles
-            (8192, 4096, 8): 2, (4096, 4096, 16): 4, (8192, 8192, 4): 4}
+            (8192, 4096, 8): 4,  # 8-byte elements: 32 x 64 tiles, not longer along a
+            (4096, 4096, 16): 2,  # 16-byte elements: 64 x 16 tiles, 64 a-tiles <= 256 b-tiles
+            (8192, 8192, 4): 4}
     for (rows, cols, eb), o in want.items():
         assert order(rows, cols, eb) == o, (rows, cols, eb)
     for name, o in (("transpose", 4), ("interleave_cm", 1), ("nhwc2nchw", 1)):
@@ -717,7 +733,7 @@ def test_transpose_blocks_plan():
     assert (p["tile_a"], p["tile_b"], p["grid"], p["order"]) == (base["tile_a"], base["tile_b"], base["grid"], base["order"])
     assert lr.copy_plan(*args, tuning={"transpose_blocks": 1})["block"] == 1024
     assert lr.copy_plan(*args, tuning={"transpose_blocks": 2, "direct_loads": 1})["block"] == 1024
-    for shape in range(8):
+    for shape in range(9):
         p = lr.copy_plan(*args, tuning={"transpose_blocks": 2, "tile_shape": shape})
         blocks = p["tile_a"] * p["tile_b"] // p["vec_elems"] ** 2
         assert p["block"] == (blocks if shape == 7 else blocks // 2), shape  # 8 x 8 chunks: one wavefront
@@ -728,7 +744,7 @@ def test_transpose_blocks_plan():
 def test_tuning_overrides_are_checked():
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
-    for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 8}, {"tile_order": 10},
+    for bad in ({"load_policy": 1}, {"store_policy": 16}, {"tile_shape": 9}, {"tile_order": 10},
                 {"units_per_lane": 2}, {"vector_order": 4}, {"gather_chunks": 3}, {"direct_loads": 2},
                 {"pipeline_tiles": 1}, {"pipeline_tiles": 65}, {"pipeline_tiles": -2}, {"transpose_reads": 2},
                 {"chunk_bytes": 4}, {"chunk_bytes": 0}, {"workgroup_lanes": 32}, {"workgroup_lanes": 512},

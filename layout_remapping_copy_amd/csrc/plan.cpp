@@ -897,12 +897,18 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
       const bool block_rows = ext_a <= 32 * V && p->m[b].ss == ext_a;
       const bool block_cols =
           V * p->eb == 16 && b2 < 0 && ext_b > 16 * V && ext_b <= 32 * V && p->m[a].sd == ext_b;
+      // the share of a tile's lanes with work in a shape, over both sides' ragged edges
+      auto lane_share = [&](int s) {
+        const int64_t ta = kTileTA[s] * V, tb = kTileTB[s] * V;
+        return (double)ext_a / (double)(((ext_a + ta - 1) / ta) * ta) * (double)ext_b /
+               (double)(((ext_b + tb - 1) / tb) * tb);
+      };
       if (!wide_ok)
         p->tshape = 0;
-      else if (block_rows)
+      else if (block_rows && !(block_cols && lane_share(8) > lane_share(ext_a > 16 * V ? 4 : 0)))
         p->tshape = ext_a > 16 * V ? 4 : 0;
-      else if (block_cols)
-        p->tshape = 8;
+      else if (block_cols)  // whole matrices both ways take the shape with more lanes at work
+        p->tshape = 8;      // (batched fp32 128 x 96: 65.5 against 70.4 us for 32 x 8)
       else if (p->eb == 1)
         p->tshape = ext_a > 16 * V ? 1 : 0;  // 8-byte chunks: 32 x 16 (u8 8192^2 4.78 against 4.56 with 32 x 32)
       else if (V >= 4)

@@ -640,6 +640,14 @@ def test_plan_streaming_default_and_tile_shapes():
     p = lr.copy_plan("(256,12544,64):(802816,1,12544)", 256 * 12544 * 64, "(256,12544,64):(802816,64,1)",
                      256 * 12544 * 64, 2)
     assert (p["tile_a"], p["tile_b"]) == (256, 64), p
+    # whole matrices both ways (fp32 128 x 96, 4096 of them): the whole-block shape with more
+    # lanes at work, 8 x 32 chunks (96 = 3 x 32 along a) over 32 x 8 (96 of 128 along a)
+    p = lr.copy_plan("(128,96,4096):(96,1,12288)", 128 * 96 * 4096, "(128,96,4096):(1,128,12288)",
+                     128 * 96 * 4096, 4)
+    assert (p["path"], p["tile_a"], p["tile_b"]) == ("transpose", 32, 128), p
+    w = W.full("nhwc2nchw")  # a whole 256-channel block each way only along a: 32 x 8
+    p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
+    assert (p["tile_a"], p["tile_b"]) == (256, 64), p
 
 
 def test_plan_workgroup_order():

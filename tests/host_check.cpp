@@ -119,7 +119,7 @@ static lr_copy_tuning rand_tuning(std::mt19937_64& rng) {
   t.units_per_lane = pick({-1, 1, 4});
   t.vector_order = pick({-1, 0, 1, 2, 3});
   t.interleave_form = pick({-1, 0, 1, 2});
-  t.tile_shape = pick({-1, 0, 1, 2, 3, 4, 5, 6});
+  t.tile_shape = pick({-1, 0, 1, 2, 3, 4, 5, 6, 7, 8});
   t.tile_order = pick({-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9});
   t.element_tiles = pick({-1, 0, 1});
   t.direct_loads = pick({-1, 0, 1});
@@ -127,6 +127,10 @@ static lr_copy_tuning rand_tuning(std::mt19937_64& rng) {
   t.pipeline_tiles = pick({-1, 0, 2, 3, 5, 64});
   t.transpose_reads = pick({-1, 0, 1});
   t.chunk_bytes = pick({-1, 8, 16});
+  t.batch_swizzle = pick({-1, 0, 3, 7, 15});
+  t.batch_order = pick({-1, 0, 1});
+  t.workgroup_lanes = pick({-1, 64, 128, 256});
+  t.transpose_blocks = pick({-1, 1, 2});
   return t;
 }
 

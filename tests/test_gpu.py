@@ -430,7 +430,8 @@ def test_copy_random_pairs(dev, knobs):
     """600 seeded random pairs (permuted, padded, swizzled, 1-16 byte elements, up to
     2^17 elements), each by the default plan, by every path that applies when
     forced, and with 64-bit indices, under randomly drawn plan-time variants
-    (access policy, direct loads, tile shape and order)."""
+    (access policy, direct loads, tile shape and order, register blocks per lane,
+    workgroup lanes, gather grouping, batched swizzles)."""
     rng = random.Random(41)
     runs = 0
     for i in range(600):
@@ -441,7 +442,8 @@ def test_copy_random_pairs(dev, knobs):
         want = O.copy(src, O.parse(ts), dst, O.parse(td), eb)
         pol = rng.choice([(0, -1), (2, -1), (2, 2), (2, 0)])  # the last: vector/generic paths only
         env = {"load_policy": pol[0], "store_policy": pol[1], "direct_loads": rng.choice([-1, 0, 1]),
-               "tile_shape": rng.randint(0, 6), "tile_order": rng.randint(0, 9),
+               "tile_shape": rng.randint(0, 6) if random.Random(5000 + i).random() > 0.15 else 8,
+               "tile_order": rng.randint(0, 9),
                "element_tiles": rng.choice([-1, 0, 1]), "interleave_form": rng.choice([0, 1, 2]),
                "vector_order": rng.choice([-1, 0, 1, 2, 3]), "units_per_lane": rng.choice([-1, 1, 4]),
                "gather_chunks": rng.choice([-1, 1, 2, 4, 8, 16, 32]), "pipeline_tiles": rng.choice([-1, -1, 2, 3, 5]),
@@ -449,7 +451,8 @@ def test_copy_random_pairs(dev, knobs):
                "chunk_bytes": random.Random(i).choice([-1, -1, 8, 16]),
                "workgroup_lanes": random.Random(1000 + i).choice([-1, 64, 128, 256]),
                "batch_swizzle": random.Random(2000 + i).choice([-1, -1] + list(range(16))),
-               "batch_order": random.Random(3000 + i).choice([-1, 0, 1])}
+               "batch_order": random.Random(3000 + i).choice([-1, 0, 1]),
+               "transpose_blocks": random.Random(4000 + i).choice([-1, 1, 2])}
         knobs.t.clear()
         knobs.set(**env)
         if i % 50 == 0:
@@ -510,7 +513,7 @@ def test_write_counts_random_pairs_and_aliased_tile(dev, knobs):
         knobs.set(tile_shape=rng.choice([0, 1, 2, 3, 4, 5, 6, 8]), tile_order=rng.randint(0, 9), gather_chunks=rng.choice([-1, 8, 16]),
                   vector_order=rng.choice([-1, 0, 1, 2, 3]), element_tiles=rng.choice([-1, 0, 1]),
                   pipeline_tiles=rng.choice([-1, 2, 3]), transpose_reads=rng.choice([-1, 1]),
-                  direct_loads=rng.choice([-1, 1]))
+                  direct_loads=rng.choice([-1, 1]), transpose_blocks=random.Random(6000 + i).choice([-1, 2]))
         for flags in [0] + [lr.COPY_FORCE_PATH(p) for p in ALL_PATHS]:
             try:
                 p = plan(ts, ns, td, nd, eb, flags)

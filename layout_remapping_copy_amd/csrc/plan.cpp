@@ -1068,8 +1068,14 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         p->bufst = false;
       }
       // two register blocks per lane (half the lanes for the same tile) on the
-      // register-loaded LDS transpose
-      if (tun.transpose_blocks == 2 && p->path == LR_PATH_TRANSPOSE && !p->tel && !p->direct && !p->pipe &&
+      // register-loaded LDS transpose.  Taken for 1024-lane tiles of 2-byte elements:
+      // back to back, the fp16 8192^2 transpose 46.2-47.2 against 47.1-47.7 us over
+      // three runs, fp16 16384^2 and the bf16 KV-cache reorder 0.5-1 % faster; 4-byte
+      // elements and smaller tiles lose 1-5 %.
+      const bool two_blocks = tun.transpose_blocks >= 0
+                                  ? tun.transpose_blocks == 2
+                                  : p->eb == 2 && kTileTA[p->tshape] * kTileTB[p->tshape] == 1024;
+      if (two_blocks && p->path == LR_PATH_TRANSPOSE && !p->tel && !p->direct && !p->pipe &&
           (V * p->eb == 16 || (p->eb == 1 && V == 8)) && kTileTB[p->tshape] % 2 == 0 &&
           kTileTA[p->tshape] * kTileTB[p->tshape] >= 128) {  // whole wavefronts
         p->tblocks = 2;

@@ -604,8 +604,9 @@ def test_plan_streaming_default_and_tile_shapes():
         p = lr.copy_plan("8:1", 8, "8:0", 1, 4, lr.COPY_ORDERED_ALIAS, tuning=t)
         assert p["path"] == "alias" and not p["streaming"]
     # transpose tiles: rows far apart -> 32 x 32 chunks (16 x 32 when 16 chunks
-    # cover the contiguous extent); a contiguous source block per tile -> 32 x 8
-    want = {"transpose": (256, 256, 1024), "interleave_cm": (128, 256, 512), "nhwc2nchw": (256, 64, 256)}
+    # cover the contiguous extent), two register blocks a lane for 2-byte elements in
+    # 32 x 32 chunks; a contiguous source block per tile -> 32 x 8
+    want = {"transpose": (256, 256, 512), "interleave_cm": (128, 256, 512), "nhwc2nchw": (256, 64, 256)}
     for name, (ta, tb, block) in want.items():
         w = W.full(name)
         p = lr.copy_plan(w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, w.elem_bytes)
@@ -732,14 +733,18 @@ def test_plan_store_policy():
 
 def test_transpose_blocks_plan():
     """transpose_blocks = 2 halves the lanes of the register-loaded LDS transpose for
-    the same tile; direct loads, element tiles and odd b sides keep one block a lane."""
+    the same tile; direct loads, element tiles and odd b sides keep one block a lane.
+    By default 1024-lane tiles of 2-byte elements take two blocks a lane, others one."""
     w = W.full("transpose")
     args = (w.src_layout, w.src_elems, w.dst_layout, w.dst_elems, 2)
-    base = lr.copy_plan(*args)
+    base = lr.copy_plan(*args, tuning={"transpose_blocks": 1})
     p = lr.copy_plan(*args, tuning={"transpose_blocks": 2})
-    assert base["block"] == 1024 and p["block"] == 512
+    assert base["block"] == 1024 and p["block"] == 512 and lr.copy_plan(*args)["block"] == 512
     assert (p["tile_a"], p["tile_b"], p["grid"], p["order"]) == (base["tile_a"], base["tile_b"], base["grid"], base["order"])
-    assert lr.copy_plan(*args, tuning={"transpose_blocks": 1})["block"] == 1024
+    f32 = ("(8192,8192):(8192,1)", 1 << 26, "(8192,8192):(1,8192)", 1 << 26, 4)
+    assert lr.copy_plan(*f32)["block"] == 1024 and lr.copy_plan(*f32, tuning={"transpose_blocks": 2})["block"] == 512
+    cm = W.full("interleave_cm")  # 512-lane tiles keep one block a lane
+    assert lr.copy_plan(cm.src_layout, cm.src_elems, cm.dst_layout, cm.dst_elems, 2)["block"] == 512
     assert lr.copy_plan(*args, tuning={"transpose_blocks": 2, "direct_loads": 1})["block"] == 1024
     for shape in range(9):
         p = lr.copy_plan(*args, tuning={"transpose_blocks": 2, "tile_shape": shape})

@@ -54,6 +54,14 @@ def nhwc2nchw(src: np.ndarray, n: int, h: int, w: int, c: int, eb: int = 2) -> n
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
 
 
+def transpose_batched(src: np.ndarray, batch: int, rows: int, cols: int, eb: int) -> np.ndarray:
+    """batch row-major rows x cols matrices, one after another -> the same matrices
+    transposed (cols x rows, row-major), elements of eb bytes moved as opaque bytes:
+    dst[m][j][i] = src[m][i][j]."""
+    x = src.reshape(batch, rows, cols, eb).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(x).reshape(-1)
+
+
 def nchw2nhwc(src: np.ndarray, n: int, h: int, w: int, c: int, eb: int = 2) -> np.ndarray:
     """(n,c,h,w) contiguous -> (n,h,w,c) contiguous, elements of eb bytes."""
     x = src.view(_UINT[eb]).reshape(n, c, h, w).transpose(0, 2, 3, 1)

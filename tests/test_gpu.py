@@ -662,6 +662,43 @@ def test_full_transpose_both_variants(dev, knobs, nt):
         assert np.array_equal(d.cpu().numpy(), want)
 
 
+# transposes whose default tiles come from the tile-shape rules for 8- and 16-byte
+# elements and for whole blocks: (source, destination, element bytes, tile, closed form)
+TILE_RULE_CASES = {
+    "fp64 4096x8192": ("(4096,8192):(8192,1)", "(4096,8192):(1,4096)", 8, (32, 64),
+                       lambda s: F.transpose_batched(s, 1, 4096, 8192, 8)),
+    "16-byte 4096^2": ("(4096,4096):(4096,1)", "(4096,4096):(1,4096)", 16, (64, 16),
+                       lambda s: F.transpose_batched(s, 1, 4096, 4096, 16)),
+    "NCHW->NHWC (128,256,56,56)": ("(128,3136,256):(802816,1,3136)", "(128,3136,256):(802816,256,1)", 2,
+                                   (64, 256), lambda s: F.nchw2nhwc(s, 128, 56, 56, 256, 2)),
+    "fp32 128x96 x 4096": ("(128,96,4096):(96,1,12288)", "(128,96,4096):(1,128,12288)", 4, (32, 128),
+                           lambda s: F.transpose_batched(s, 4096, 128, 96, 4)),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("case", list(TILE_RULE_CASES))
+def test_full_size_tile_rule_transposes(dev, case):
+    """Full-size parity of the transposes whose tiles the planner picks by element size
+    (16 x 32 chunks for 8-byte elements, 64 x 16 for 16-byte ones) and by whole blocks
+    (8 x 32 chunks where each tile writes one contiguous destination block): the whole
+    destination buffer against the oracle's closed forms."""
+    ts, td, eb, tile, form = TILE_RULE_CASES[case]
+    n = lr.parse(ts).size
+    p = plan(ts, n, td, n, eb)
+    assert p["path"] == "transpose" and (p["tile_a"], p["tile_b"]) == tile, p
+    src = np.random.default_rng(len(case)).integers(0, 256, n * eb, dtype=np.uint8)
+    s = torch.from_numpy(src).to(dev)
+    d = torch.full((n * eb,), 0xA5, dtype=torch.uint8, device=dev)
+    say("full tile-rule transpose", case, "tile", tile)
+    copy_(s, ts, d, td, eb)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    del s, d
+    torch.cuda.empty_cache()
+    assert np.array_equal(got, form(src)), case
+
+
 @pytest.mark.slow
 def test_copy_beyond_2_31_elements(dev):
     """More than 2^31 elements: by default the copy is cut into blocks that each fit

@@ -772,6 +772,15 @@ def test_forms_equal_oracle_copy():
         blank = np.zeros_like(src)
         assert np.array_equal(F.nhwc2nchw(src, n, h, wd, c, eb), O.copy(src, nhwc, blank, nchw, eb)), eb
         assert np.array_equal(F.nchw2nhwc(src, n, h, wd, c, eb), O.copy(src, nchw, blank, nhwc, eb)), eb
+    # batched transposes of 1- to 16-byte elements, square and not, one matrix or several
+    for eb, (m, r, c) in [(1, (1, 5, 7)), (2, (3, 4, 6)), (4, (2, 7, 3)), (8, (1, 6, 6)), (16, (2, 3, 5))]:
+        src = rng.integers(0, 256, m * r * c * eb, dtype=np.uint8)
+        Ls = O.parse(f"({r},{c},{m}):({c},1,{r * c})")
+        Ld = O.parse(f"({r},{c},{m}):(1,{r},{r * c})")
+        assert np.array_equal(F.transpose_batched(src, m, r, c, eb), O.copy(src, Ls, np.zeros_like(src), Ld, eb)), eb
+    # the fp16 square transpose form agrees with the batched one
+    src = rng.integers(0, 256, 9 * 9 * 2, dtype=np.uint8)
+    assert np.array_equal(F.transpose(src, 9), F.transpose_batched(src, 1, 9, 9, 2))
 
 
 def test_shard_pack_exchange_reassembles_the_transpose():

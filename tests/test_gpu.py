@@ -763,13 +763,15 @@ def test_channel_shuffle_destination_beyond_4_gib(dev):
         del got
 
 
+@pytest.mark.parametrize("blocks", [-1, 2])
 @pytest.mark.parametrize("nt", ["0", "1"])
-def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
+def test_copies_replay_in_a_hip_graph(dev, knobs, nt, blocks):
     """lr_layout_copy allocates nothing and records no memset, so captured copies
-    (eight copies on six paths in one graph, with plain or streaming accesses, the latter with the
-    sc1 buffer stores) replay correctly; each replay is checked after eager work has
-    changed the sources."""
+    (nine copies on six paths in one graph, with plain or streaming accesses, the latter with the
+    sc1 buffer stores, and the transposes with one or two register blocks a lane) replay
+    correctly; each replay is checked after eager work has changed the sources."""
     knobs.policy(nt)
+    knobs.set(transpose_blocks=blocks)
     cases = []
     for name in ("transpose", "retile", "interleave", "nhwc2nchw", "padtiles", "rgb_nhwc2nchw"):
         w = W.small(name)
@@ -777,6 +779,7 @@ def test_copies_replay_in_a_hip_graph(dev, knobs, nt):
     rgb = W.small("rgb_nhwc2nchw")  # and back: the channel-shuffle interleave
     cases.append((rgb.dst_layout, rgb.src_layout, rgb.dst_elems, rgb.src_elems, rgb.elem_bytes))
     cases.append(("(16,16,300):(16,1,256)", "(16,16,300):(1,16,256)", 76800, 76800, 2))  # batched matrices
+    cases.append(("(2,320,256):(81920,1,320)", "(2,320,256):(81920,256,1)", 163840, 163840, 2))  # 8 x 32 tiles
     paths = {plan(ts, ns, td, nd, eb)["path"] for ts, td, ns, nd, eb in cases}
     assert {"transpose", "vector", "interleave", "staged", "deinterleave", "batched"} <= paths, paths
     s_list, d_list, plans = [], [], []

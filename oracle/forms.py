@@ -54,6 +54,22 @@ def nhwc2nchw(src: np.ndarray, n: int, h: int, w: int, c: int, eb: int = 2) -> n
     return np.ascontiguousarray(x).reshape(-1).view(np.uint8)
 
 
+def strided_copy(src: np.ndarray, shape, src_strides, dst: np.ndarray, dst_strides, eb: int) -> np.ndarray:
+    """The copy between two flat (single-level, unswizzled) layouts of the same shape,
+    as NumPy strided views: for every coordinate c, the eb-byte element at
+    sum(c_i * dst_strides_i) of a copy of dst takes the one at sum(c_i * src_strides_i)
+    of src (strides in elements).  Returns the new destination bytes."""
+    item = np.dtype((np.void, eb))
+    s = src.view(item)
+    out = dst.copy()
+    d = out.view(item)
+    sv = np.lib.stride_tricks.as_strided(s, shape=tuple(shape), strides=tuple(eb * x for x in src_strides),
+                                         writeable=False)
+    dv = np.lib.stride_tricks.as_strided(d, shape=tuple(shape), strides=tuple(eb * x for x in dst_strides))
+    dv[...] = sv
+    return out
+
+
 def transpose_batched(src: np.ndarray, batch: int, rows: int, cols: int, eb: int) -> np.ndarray:
     """batch row-major rows x cols matrices, one after another -> the same matrices
     transposed (cols x rows, row-major), elements of eb bytes moved as opaque bytes:

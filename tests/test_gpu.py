@@ -699,6 +699,39 @@ def test_full_size_tile_rule_transposes(dev, case):
     assert np.array_equal(got, form(src)), case
 
 
+def _flat(text):
+    """'(a,b,...):(x,y,...)' -> shape and strides (flat layouts without swizzle)."""
+    sh, st = text.split(":")
+    return [int(v) for v in sh.strip("()").split(",")], [int(v) for v in st.strip("()").split(",")]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("k", range(16))
+def test_layout_sweep_transforms_full_size(dev, k):
+    """Every transform the layout sweep times (bench.py LAYOUT_SWEEP), at its full size in the
+    plan the planner picks: the whole destination buffer, holes included, against the
+    oracle's strided-copy form (pinned to oracle.copy)."""
+    import bench
+    name, ts, td, eb = bench.LAYOUT_SWEEP[k]
+    Ls, Ld = lr.parse(ts), lr.parse(td)
+    n, ns, nd = Ls.size, Ls.cosize, Ld.cosize
+    p = plan(ts, ns, td, nd, eb)
+    src = np.random.default_rng(900 + k).integers(0, 256, ns * eb, dtype=np.uint8)
+    dst = np.full(nd * eb, 0xA5, np.uint8)
+    s = torch.from_numpy(src).to(dev)
+    d = torch.from_numpy(dst).to(dev)
+    say("layout sweep transform", k, name, p["path"], p["tile_a"], p["tile_b"])
+    copy_(s, ts, d, td, eb)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    del s, d
+    torch.cuda.empty_cache()
+    shape, ss = _flat(ts)
+    shape_d, sd = _flat(td)
+    assert shape == shape_d
+    assert np.array_equal(got, F.strided_copy(src, shape, ss, dst, sd, eb)), name
+
+
 @pytest.mark.slow
 def test_copy_beyond_2_31_elements(dev):
     """More than 2^31 elements: by default the copy is cut into blocks that each fit

@@ -778,6 +778,18 @@ def test_forms_equal_oracle_copy():
         Ls = O.parse(f"({r},{c},{m}):({c},1,{r * c})")
         Ld = O.parse(f"({r},{c},{m}):(1,{r},{r * c})")
         assert np.array_equal(F.transpose_batched(src, m, r, c, eb), O.copy(src, Ls, np.zeros_like(src), Ld, eb)), eb
+    # strided copies between flat layouts: permutes with padding, a gather of every second row,
+    # a reversal of modes and a broadcast-free injective scatter, against the oracle's copy
+    for eb, shape, ss, sd in [(2, (4, 3, 5), (1, 4, 12), (15, 5, 1)), (4, (6, 7), (1, 8), (7, 1)),
+                              (1, (3, 4, 2), (1, 6, 3), (1, 3, 12)), (8, (5, 4), (1, 10), (1, 5)),
+                              (16, (2, 3, 4), (12, 4, 1), (1, 2, 6))]:
+        ns = 1 + sum((e - 1) * x for e, x in zip(shape, ss))
+        nd = 1 + sum((e - 1) * x for e, x in zip(shape, sd))
+        src = rng.integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = rng.integers(0, 256, nd * eb, dtype=np.uint8)
+        Ls = O.parse("(" + ",".join(map(str, shape)) + "):(" + ",".join(map(str, ss)) + ")")
+        Ld = O.parse("(" + ",".join(map(str, shape)) + "):(" + ",".join(map(str, sd)) + ")")
+        assert np.array_equal(F.strided_copy(src, shape, ss, dst, sd, eb), O.copy(src, Ls, dst, Ld, eb)), (eb, shape)
     # the fp16 square transpose form agrees with the batched one
     src = rng.integers(0, 256, 9 * 9 * 2, dtype=np.uint8)
     assert np.array_equal(F.transpose(src, 9), F.transpose_batched(src, 1, 9, 9, 2))

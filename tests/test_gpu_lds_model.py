@@ -1,6 +1,6 @@
 """The gfx950 LDS model of lr_access_check against the hardware's own count.
 
-The probe (tests/lds_bank_probe.hip, compiled by this test and linked against
+The probe (tests/lds_bank_probe.hip, built by build() into tests/bin, else here, and linked against
 the library) makes every wave of a large launch access
 LDS in one lane pattern, for 40 layouts x {read, write}, and prints what
 lr_access_check predicts for each.  Run under rocprofv3 with the
@@ -21,18 +21,20 @@ import pytest
 lr = pytest.importorskip("layout_remapping_copy_amd")
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(HERE)
 
 
-def _build_probe(out_path):
-    """Compiles the probe (host code and one gfx950 kernel) against the built library."""
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    lib_dir = os.path.dirname(lr.LIB_PATH)
-    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-Wall", "-I", os.path.join(ROOT, "include"), os.path.join(HERE, "lds_bank_probe.hip"),
-           "-L", lib_dir, "-llayout_remap", f"-Wl,-rpath,{lib_dir}", "-o", out_path]
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+def _probe(tmp_path):
+    """The probe (host code and one gfx950 kernel, linked against the built library):
+    the one build() made when it is newer than its source, else compiled here."""
+    import __graft_entry__ as G
+    exe = os.path.join(G.PROBE_DIR, "lds_bank_probe")
+    if os.path.exists(exe) and os.path.getmtime(exe) >= os.path.getmtime(os.path.join(HERE, "lds_bank_probe.hip")):
+        return exe
+    exe = str(tmp_path / "lds_bank_probe")
+    print("building the probe", flush=True)
+    r = subprocess.run(G.probe_command("lds_bank_probe", exe), capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    return exe
 
 
 @pytest.mark.gpu
@@ -42,9 +44,7 @@ def test_lds_model_equals_bank_conflict_counter(tmp_path):
     rocprof = shutil.which("rocprofv3")
     if rocprof is None:
         pytest.skip("rocprofv3 not on PATH")
-    PROBE = str(tmp_path / "lds_bank_probe")
-    print("building the probe", flush=True)
-    _build_probe(PROBE)
+    PROBE = _probe(tmp_path)
     # the probe itself (our code) must run and report every pattern
     plain = subprocess.run([PROBE, "read"], capture_output=True, text=True, timeout=120)
     assert plain.returncode == 0, plain.stderr[-2000:]

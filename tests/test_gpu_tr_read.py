@@ -2,7 +2,7 @@
 (ds_read_b64_tr_b16, ds_read_b64_tr_b8), which the direct-load transpose's
 transpose_reads form is built on.
 
-tests/tr_read_probe.hip (compiled by this test) reads 8 bytes per lane from an LDS
+tests/tr_read_probe.hip (built by build() into tests/bin, else here) reads 8 bytes per lane from an LDS
 array holding each element's own index, at five address patterns.  Within each group
 of 16 lanes, lane i must receive
   - 2-byte form: as its element k (k = 0..3), element i % 4 of the four 2-byte
@@ -13,7 +13,6 @@ of 16 lanes, lane i must receive
 
 import json
 import os
-import shutil
 import subprocess
 
 import pytest
@@ -56,13 +55,13 @@ def test_expected_layout_examples():
 
 @pytest.mark.gpu
 def test_transpose_read_lane_layout(tmp_path):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    exe = str(tmp_path / "tr_read_probe")
-    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-Wall", os.path.join(HERE, "tr_read_probe.hip"), "-o", exe]
-    print("building the probe", flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
-    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    import __graft_entry__ as G
+    exe = os.path.join(G.PROBE_DIR, "tr_read_probe")
+    if not (os.path.exists(exe) and os.path.getmtime(exe) >= os.path.getmtime(os.path.join(HERE, "tr_read_probe.hip"))):
+        exe = str(tmp_path / "tr_read_probe")  # not built by build(), or older than its source
+        print("building the probe", flush=True)
+        r = subprocess.run(G.probe_command("tr_read_probe", exe), capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     print("running the probe", flush=True)
     p = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert p.returncode == 0, p.stderr[-2000:]

@@ -732,6 +732,68 @@ def test_layout_sweep_transforms_full_size(dev, k):
     assert np.array_equal(got, F.strided_copy(src, shape, ss, dst, sd, eb)), name
 
 
+def _rand_flat_large(rng):
+    """A random pair of flat layouts over 2^21-2^25 elements: rank 2-4, a random
+    mode order on each side, rows padded at random on either side, extents ragged
+    against every tile (odd factors)."""
+    rank = rng.randint(2, 4)
+    total_log = rng.randint(21, 25)
+    ext = []
+    left = total_log
+    for k in range(rank - 1):
+        e = rng.randint(3, max(3, left - 2 * (rank - 1 - k)))
+        ext.append(e)
+        left -= e
+    ext.append(max(1, left))
+    shape = [(1 << e) + rng.choice([0, 0, 0, -1, 1, 3, -3, 7]) for e in ext]
+    shape = [max(2, s) for s in shape]
+
+    def strides(order, pad):
+        st = [0] * rank
+        acc = 1
+        for k in order:
+            st[k] = acc
+            acc *= shape[k] + (rng.choice([0, 0, 1, 8, 13]) if pad and k == order[0] else 0)
+        return st
+
+    src_order = list(range(rank))
+    dst_order = list(range(rank))
+    rng.shuffle(dst_order)
+    if rng.random() < 0.3:
+        rng.shuffle(src_order)
+    return shape, strides(src_order, True), strides(dst_order, rng.random() < 0.5)
+
+
+@pytest.mark.slow
+def test_random_large_flat_copies(dev, knobs):
+    """24 seeded random pairs of flat layouts at 2^21-2^25 elements and 1- to 16-byte
+    elements (transposes, permutes, padded rows on either side, ragged extents) under
+    the planner's default plan: whole destination buffers, holes included, against
+    the oracle's strided-copy form."""
+    rng = random.Random(2024)
+    for i in range(24):
+        shape, ss, sd = _rand_flat_large(rng)
+        eb = rng.choice([1, 2, 4, 8, 16])
+        while eb > 1 and np.prod(shape) * eb > (1 << 27):
+            eb //= 2
+        ts = "(" + ",".join(map(str, shape)) + "):(" + ",".join(map(str, ss)) + ")"
+        td = "(" + ",".join(map(str, shape)) + "):(" + ",".join(map(str, sd)) + ")"
+        ns = 1 + sum((e - 1) * x for e, x in zip(shape, ss))
+        nd = 1 + sum((e - 1) * x for e, x in zip(shape, sd))
+        p = plan(ts, ns, td, nd, eb)
+        say("random large", i, ts, "->", td, "eb", eb, p["path"], p["tile_a"], p["tile_b"])
+        src = np.random.default_rng(3000 + i).integers(0, 256, ns * eb, dtype=np.uint8)
+        dst = np.full(nd * eb, 0xA5, np.uint8)
+        s = torch.from_numpy(src).to(dev)
+        d = torch.from_numpy(dst).to(dev)
+        copy_(s, ts, d, td, eb)
+        torch.cuda.synchronize()
+        got = d.cpu().numpy()
+        del s, d
+        assert np.array_equal(got, F.strided_copy(src, shape, ss, dst, sd, eb)), (i, ts, td, eb)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.slow
 def test_copy_beyond_2_31_elements(dev):
     """More than 2^31 elements: by default the copy is cut into blocks that each fit

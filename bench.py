@@ -513,6 +513,36 @@ def shape_sweep(lr, torch, matrices=None, steps: int = 20):
         torch.cuda.empty_cache()
 
 
+# transposes for the workgroup-order sweep (rows, columns, element bytes): pitches on,
+# just short of and just past multiples of 16 KiB, and others
+ORDER_SWEEP = ((8192, 8192, 2), (16384, 16384, 2), (8184, 8184, 2), (8200, 8200, 2), (8208, 8208, 2),
+               (8224, 8224, 2), (16400, 16400, 2), (16416, 16416, 2), (4100, 4100, 4), (8200, 8200, 4),
+               (4104, 8200, 4), (12296, 12296, 2), (10240, 10240, 2), (12280, 12280, 2))
+
+
+def order_sweep(lr, torch, matrices=None, steps: int = 20):
+    """Transposes under the planner's workgroup order and under orders 0, 1, 2 and 4
+    (a-tiles fastest, b-tiles fastest, the two diagonals), each twice in alternation,
+    back to back over rotating buffers, best of the two.  One JSON line per matrix."""
+    dev = torch.device("cuda:0")
+    mats = [tuple(int(x) for x in m.split("x")) for m in matrices] if matrices else ORDER_SWEEP
+    for r, c, eb in mats:
+        ts, td = f"({r},{c}):({c},1)", f"({r},{c}):(1,{r})"
+        n = r * c
+        p = lr.copy_plan(ts, n, td, n, eb)
+        pairs = _pairs(torch, dev, n * eb, n * eb)
+        res = {}
+        for rep in range(2):
+            for o in (None, 0, 1, 2, 4):
+                t = None if o is None else {"tile_order": o}
+                _, ms = _time_copies(lr, torch, pairs, ts, td, eb, steps, 3, tuning=t)
+                res.setdefault("planner" if o is None else str(o), []).append(round(ms * 1e3, 2))
+        print(json.dumps({"matrix": [r, c, eb], "pitch_bytes": [c * eb, r * eb], "tile": [p["tile_a"], p["tile_b"]],
+                          "planner_order": p["order"], "us": {k: min(v) for k, v in res.items()}}), flush=True)
+        del pairs
+        torch.cuda.empty_cache()
+
+
 def blocks_sweep(lr, torch, steps: int = 20):
     """Register-loaded LDS transposes with one against two V x V blocks per lane
     (transpose_blocks 1 and 2, the same tiles with half the lanes), each twice in
@@ -777,6 +807,8 @@ def main():
     ap.add_argument("--shape-sweep", nargs="*", metavar="RxCxB",
                     help="transposes of 1- to 16-byte elements under every transpose tile shape (all listed "
                          "matrices and layout transforms, or these rows x columns x element bytes)")
+    ap.add_argument("--order-sweep", nargs="*", metavar="RxCxB",
+                    help="transposes under the planner's workgroup order and orders 0, 1, 2 and 4")
     ap.add_argument("--blocks-sweep", action="store_true",
                     help="register-loaded LDS transposes with one against two register blocks per lane")
     ap.add_argument("--back-to-back", type=int, default=0, metavar="K",
@@ -818,6 +850,9 @@ def main():
         return
     if args.blocks_sweep:
         blocks_sweep(lr, torch)
+        return
+    if args.order_sweep is not None:
+        order_sweep(lr, torch, args.order_sweep)
         return
     if args.shape_sweep is not None:
         shape_sweep(lr, torch, args.shape_sweep)

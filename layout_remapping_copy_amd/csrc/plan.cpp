@@ -1011,7 +1011,19 @@ static int plan_path(const lr_layout* Ls, int64_t src_cap, size_t src_align, con
         const int64_t ntb0 = (ext_b + p->tile_b - 1) / p->tile_b;
         const bool camp = pow2_heavy(pitch) || pow2_heavy(pitch_d) ||
                           (!p->tel && (near_16k(pitch) || near_16k(pitch_d)));
-        if (nta0 > 1 && camp)
+        // chunk tiles whose pitches lie just past a multiple of 16 KiB (none on or
+        // just short of one): the diagonal with a fastest, remeasured back to back
+        // on eight transposes whose pitches are 16-64 bytes past one (fp16 8200^2
+        // 67.1 against 71.5 us for the diagonal with b fastest, 16400^2 225.5 against
+        // 235.6, fp32 8200^2 113.8 against 121.1; fastest or within 0.5 % of it on
+        // seven, 1.3 % behind order 4 on fp32 4104 x 8200); on or just short of a
+        // multiple the diagonal with b fastest stays ahead (fp16 8184^2 64.4 against 68.4).
+        auto past_16k = [](int64_t q) { return q > 16384 && q % 16384 != 0 && q % 16384 <= 64; };
+        const bool past_only = !p->tel && !pow2_heavy(pitch) && !pow2_heavy(pitch_d) &&
+                               (past_16k(pitch) || !near_16k(pitch)) && (past_16k(pitch_d) || !near_16k(pitch_d));
+        if (nta0 > 1 && camp && past_only)
+          p->torder = 2u;
+        else if (nta0 > 1 && camp)
           p->torder = (p->tile_a > p->tile_b && nta0 <= ntb0) ? 2u : 4u;
         else if (nta0 > 1 && p->eb == 1 && !p->tel && p->v == 8 && p->tile_a > p->tile_b && nta0 <= ntb0)
           p->torder = 2u;  // 1-byte elements in 8-byte chunks: the diagonal at any pitch (u8 6144^2 4.07 against 3.73)

@@ -656,7 +656,8 @@ def test_plan_workgroup_order():
     heavy (a multiple of 16 KiB, or a power of two from 4 KiB); then the diagonal
     with b fastest, or with a fastest for tiles with longer source rows and no more
     a-tiles than b-tiles.  A single a-tile keeps b fastest.  Chunk tiles within 64
-    bytes of a multiple of 16 KiB count as power-of-two heavy.  Element tiles (rows
+    bytes of a multiple of 16 KiB count as power-of-two heavy, and take the diagonal
+    with a fastest when every such pitch lies just past a multiple.  Element tiles (rows
     without aligned chunks) take the diagonal with b fastest up to 64 bytes past a
     multiple of 8 KiB, else a fastest with at least as many a-tiles as b-tiles."""
 
@@ -670,7 +671,9 @@ def test_plan_workgroup_order():
             (8192, 8256, 2): 4,  # destination pitch 16 KiB
             (11264, 11264, 2): 1, (12288, 12288, 2): 1, (8191, 8191, 2): 0, (6144, 6144, 4): 1,
             (16383, 4097, 2): 1, (4097, 16383, 2): 0,  # element tiles: 33 x 128 and 128 x 33 tiles
-            (8184, 8184, 2): 4, (8224, 8224, 2): 4, (4100, 4100, 4): 4, (8256, 8256, 2): 1,  # near 16 KiB
+            (8184, 8184, 2): 4, (8256, 8256, 2): 1,  # near 16 KiB: just short of a multiple
+            (8224, 8224, 2): 2, (4100, 4100, 4): 2, (16416, 16416, 2): 2,  # just past one: a fastest
+            (16392, 8192, 2): 4,  # one pitch a multiple of 16 KiB, the other just past two
             (8193, 8193, 2): 4, (8196, 8196, 2): 4, (12289, 12289, 2): 4, (8188, 8188, 2): 0,  # past 8 KiB
             (8193, 4097, 4): 4, (4097, 2049, 2): 4,  # both pitches past 8 KiB, or one past and one small
             (6144, 6144, 1): 2, (11264, 11264, 1): 2, (8184, 8184, 1): 2,  # 1-byte, 8-byte chunks: order 2

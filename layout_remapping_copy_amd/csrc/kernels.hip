@@ -748,10 +748,11 @@ __device__ __forceinline__ void transpose_tile(const TransposeArgs& t, uint32_t 
   }
 }
 
-// Tile of (TA*V) x (TB*V) elements per workgroup of TA*TB lanes; each lane owns a
-// V x V register block: V chunk loads of V elements along a (one per b row), an
-// in-register transpose, V chunk stores of V elements along b (one per a row).
-// V*EB == 16 normally, so every global access is a 16-byte vector.
+// Tile of (TA*V) x (TB*V) elements per workgroup of TA*TB/R lanes; each lane owns R
+// V x V register blocks (the second TB/R block rows further along b): V chunk loads
+// of V elements along a per block (one per b row), an in-register transpose, V chunk
+// stores of V elements along b (one per a row).  V*EB == 16 normally, so every
+// global access is a 16-byte vector.
 //
 // LDS == true: the transposed chunks go through LDS so that a wave's stores run
 // along TB consecutive chunks of one dst row (TB*16 contiguous bytes per row for
